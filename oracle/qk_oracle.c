@@ -1,0 +1,525 @@
+/*
+ * qk_oracle.c - plain scalar CPU oracle for ggml block-quantized GEMV.
+ *
+ * TEST INFRASTRUCTURE ONLY (see qk_oracle.h): used by tests, the smoke check
+ * and the benchmark's CPU-baseline leg, never by the product path.
+ *
+ * Built with -O2 -ffp-contract=off and the default x86-64 ISA, so every float
+ * operation below is one IEEE binary32 (or binary64) operation, rounded to
+ * nearest even, in the order written.  Integer sums are exact int32.
+ */
+#include "qk_oracle.h"
+
+#include <math.h>
+#include <string.h>
+
+
+/* ------------------------------------------------------------------------- */
+/* Type table.                                                                */
+/* [candle] GgmlDType table: block elements / block bytes                    */
+/*   Q4_0 32/18, Q8_0 32/34, Q4K 256/144, Q6K 256/210, Q8K 256/292.          */
+/* [sipllm] Design, "type_nbytes(t, n) = n / block_size * type_size".        */
+/* ------------------------------------------------------------------------- */
+
+int64_t orc_block_elems(int type) {
+  switch (type) {
+    case ORC_Q4_0:
+    case ORC_Q8_0:
+      return 32;
+    case ORC_Q4_K:
+    case ORC_Q6_K:
+    case ORC_Q8_K:
+      return 256;
+    default:
+      return 0;
+  }
+}
+
+int64_t orc_block_bytes(int type) {
+  switch (type) {
+    case ORC_Q4_0: return 18;
+    case ORC_Q8_0: return 34;
+    case ORC_Q4_K: return 144;
+    case ORC_Q6_K: return 210;
+    case ORC_Q8_K: return 292;
+    default: return 0;
+  }
+}
+
+/* A row is whole blocks with nothing between them ([cl] Example 9). */
+int64_t orc_row_bytes(int type, int64_t n) {
+  int64_t be = orc_block_elems(type);
+  if (be == 0 || n < 0 || n % be != 0) return 0;
+  return n / be * orc_block_bytes(type);
+}
+
+/* Weight -> activation pairing: [candle] VecDotType table; [cl] Example 11
+ * (Q4_0 pairs with Q8_0); [rml] "Quantized dot products". */
+int orc_act_type(int weight_type) {
+  switch (weight_type) {
+    case ORC_Q4_0:
+    case ORC_Q8_0:
+      return ORC_Q8_0;
+    case ORC_Q4_K:
+    case ORC_Q6_K:
+      return ORC_Q8_K;
+    default:
+      return -1;
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* IEEE 754 binary16 <-> binary32, from the format's definition:             */
+/* 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; exponent 0 is    */
+/* zero/subnormal (fraction * 2^-24), exponent 31 is inf/NaN.  Conversion    */
+/* to binary16 rounds to nearest, ties to even, overflows to infinity.       */
+/* [cl] Example 2 uses Float.floatToFloat16 (that rounding); [candle]        */
+/* "一些边界值": a d below the smallest subnormal becomes 0, above 65504      */
+/* becomes inf.                                                              */
+/* ------------------------------------------------------------------------- */
+
+float orc_f16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int frac = h & 1023;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)frac, -24);
+  } else if (e == 31) {
+    v = frac ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + frac), e - 25);
+  }
+  return (float)(sign ? -v : v);
+}
+
+/* Round a non-negative double holding an exact binary32 value to the nearest
+ * integer, ties to even. */
+static double orc_rint_even(double v) {
+  double f = floor(v);
+  double r = v - f; /* exact: v has at most 24 significant bits */
+  if (r > 0.5) return f + 1.0;
+  if (r < 0.5) return f;
+  return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+uint16_t orc_f32_to_f16(float f) {
+  uint16_t sign = signbit(f) ? 0x8000 : 0;
+  if (isnan(f)) return sign | 0x7E00;
+  double a = fabs((double)f);
+  if (isinf(f)) return sign | 0x7C00;
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: value = m * 2^-24, m in [0, 1024]; m == 1024 is the
+     * smallest normal, whose encoding (exponent 1, fraction 0) is also 1024. */
+    double m = orc_rint_even(a * ldexp(1.0, 24));
+    return sign | (uint16_t)m;
+  }
+  int e2;
+  (void)frexp(a, &e2);           /* a = fr * 2^e2, fr in [0.5, 1) */
+  int e = e2 - 1;                /* a in [2^e, 2^(e+1)) */
+  double m = orc_rint_even(ldexp(a, 10 - e)); /* in [1024, 2048] */
+  if (m == 2048.0) {
+    m = 1024.0;
+    e += 1;
+  }
+  if (e > 15) return sign | 0x7C00;
+  return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+/* ------------------------------------------------------------------------- */
+/* Activation / weight quantizers.                                           */
+/* ------------------------------------------------------------------------- */
+
+/* C roundf (halves away from zero) of x*id, saturated to int8 the way
+ * [candle]'s `as i8` cast does; NaN becomes 0 ([candle] "一些边界值": a NaN
+ * value is ignored by amax and its own code becomes 0). */
+static int8_t orc_code_q8(float v) {
+  if (isnan(v)) return 0;
+  float r = roundf(v);
+  if (r > 127.0f) return 127;
+  if (r < -128.0f) return -128;
+  return (int8_t)r;
+}
+
+/* Largest |x| over a block, NaN ignored (fmaxf returns the other operand). */
+static float orc_amax(const float* x, int64_t len) {
+  float amax = 0.0f;
+  for (int64_t j = 0; j < len; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  return amax;
+}
+
+static void orc_put_u16(uint8_t* p, uint16_t v) {
+  p[0] = (uint8_t)(v & 0xFF);
+  p[1] = (uint8_t)(v >> 8);
+}
+static uint16_t orc_get_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static int16_t orc_get_i16(const uint8_t* p) { return (int16_t)orc_get_u16(p); }
+static float orc_get_f32(const uint8_t* p) {
+  uint32_t u = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) |
+               ((uint32_t)p[3] << 24);
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+static void orc_put_f32(uint8_t* p, float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  p[0] = (uint8_t)u;
+  p[1] = (uint8_t)(u >> 8);
+  p[2] = (uint8_t)(u >> 16);
+  p[3] = (uint8_t)(u >> 24);
+}
+
+/* quantize_row_q8_0 reference ([cl] Example 2, four steps per 32-block;
+ * [candle] BlockQ8_0::from_float): amax; d = amax / 127; id = 1/d or 0 when
+ * d is 0; store d as f16; code = roundf(x * id) with the unrounded f32 id.
+ * Block bytes: d f16 little-endian at 0, 32 int8 codes at 2 ([cl] Example 1). */
+int orc_quantize_q8_0(const float* x, uint8_t* out, int64_t n) {
+  if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float* xb = x + 32 * b;
+    uint8_t* ob = out + 34 * b;
+    float amax = orc_amax(xb, 32);
+    float d = amax / 127.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    orc_put_u16(ob, orc_f32_to_f16(d));
+    for (int j = 0; j < 32; ++j) ob[2 + j] = (uint8_t)orc_code_q8(xb[j] * id);
+  }
+  return ORC_OK;
+}
+
+/* quantize_row_q8_K: [candle] BlockQ8K layout (d f32 at 0, 256 int8 qs at 4,
+ * 16 int16 bsums at 260, each the sum of 16 consecutive qs).  The pages give
+ * no scale rule for it; the Q8_0 rule over 256 elements is taken (d = amax/127
+ * kept in f32, ties away from zero). */
+int orc_quantize_q8_K(const float* x, uint8_t* out, int64_t n) {
+  if (n < 0 || n % 256 != 0) return ORC_BAD_SHAPE;
+  for (int64_t b = 0; b < n / 256; ++b) {
+    const float* xb = x + 256 * b;
+    uint8_t* ob = out + 292 * b;
+    float amax = orc_amax(xb, 256);
+    float d = amax / 127.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    orc_put_f32(ob, d);
+    int8_t q[256];
+    for (int j = 0; j < 256; ++j) {
+      q[j] = orc_code_q8(xb[j] * id);
+      ob[4 + j] = (uint8_t)q[j];
+    }
+    for (int k = 0; k < 16; ++k) {
+      int s = 0;
+      for (int i = 0; i < 16; ++i) s += q[16 * k + i];
+      orc_put_u16(ob + 260 + 2 * k, (uint16_t)(int16_t)s);
+    }
+  }
+  return ORC_OK;
+}
+
+/* quantize_row_q4_0 reference ([rml] "A worked example: Q4_0"; [cl] Example
+ * 5): max = the first value of largest magnitude, sign kept (strict <); d =
+ * max / -8; id = 1/d or 0; code = min(15, (int8)(x*id + 8.5)); byte j holds
+ * element j in its low nibble and element j+16 in its high nibble. */
+int orc_quantize_q4_0(const float* x, uint8_t* out, int64_t n) {
+  if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float* xb = x + 32 * b;
+    uint8_t* ob = out + 18 * b;
+    float amax = 0.0f, max = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+      if (amax < fabsf(xb[j])) {
+        amax = fabsf(xb[j]);
+        max = xb[j];
+      }
+    }
+    float d = max / -8.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    orc_put_u16(ob, orc_f32_to_f16(d));
+    for (int j = 0; j < 16; ++j) {
+      float v0 = xb[j] * id + 8.5f;
+      float v1 = xb[j + 16] * id + 8.5f;
+      int c0 = (int)(int8_t)v0;
+      int c1 = (int)(int8_t)v1;
+      if (c0 > 15) c0 = 15;
+      if (c1 > 15) c1 = 15;
+      ob[2 + j] = (uint8_t)(c0 | (c1 << 4));
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Element decoders: the code q of element e of one block, and its scales.   */
+/* ------------------------------------------------------------------------- */
+
+/* Q4_0 ([cl] Example 5 picture and Example 6): byte j low nibble is element
+ * j, high nibble is element j+16; the stored nibble means code - 8. */
+static int orc_q4_0_code(const uint8_t* blk, int e) {
+  const uint8_t* qs = blk + 2;
+  int nib = (e < 16) ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);
+  return nib - 8;
+}
+
+/* Q4_K sub-block (scale, min) pair, get_scale_min_k4:
+ * [candle] 块结构: "the first 4 sub-blocks' scale and min are the low 6 bits of
+ * the first 8 bytes; the last 4 keep their low 4 bits in the last 4 bytes and
+ * borrow their high 2 bits from the top 2 bits of the first 8 bytes".
+ * [rml] "Unpacking the packed fields", element-200 trace, fixes j = 6:
+ * scale = (s[10] & 0xF) | ((s[2] >> 6) << 4), min = (s[10] >> 4) | ((s[6] >> 6) << 4).
+ * So scale j<4 = s[j] & 63 and min j<4 = s[j+4] & 63; for j>=4 the scale
+ * takes the low nibble of s[j+4] and the top bits of s[j-4], the min the high
+ * nibble of s[j+4] and the top bits of s[j]. */
+static void orc_q4_K_scale_min(const uint8_t* s, int j, int* sc, int* m) {
+  if (j < 4) {
+    *sc = s[j] & 63;
+    *m = s[j + 4] & 63;
+  } else {
+    *sc = (s[j + 4] & 0x0F) | ((s[j - 4] >> 6) << 4);
+    *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+  }
+}
+
+/* Q4_K code of element e ([rml] element-200 trace): chunk c = e / 64, position
+ * p = e % 64; p < 32 -> low nibble of qs[32c + p]; otherwise the high nibble of
+ * qs[32c + p - 32].  Field offsets follow [candle]'s BlockQ4K field order:
+ * d f16 @0, dmin f16 @2, scales[12] @4, qs[128] @16. */
+static int orc_q4_K_code(const uint8_t* blk, int e) {
+  const uint8_t* qs = blk + 16;
+  int c = e / 64, p = e % 64;
+  return (p < 32) ? (qs[32 * c + p] & 0x0F) : (qs[32 * c + p - 32] >> 4);
+}
+
+/* Q6_K ([candle] BlockQ6K: ql[128] @0 low 4 bits, qh[64] @128 high 2 bits,
+ * scales int8[16] @192, d f16 @208; 16-element sub-block j has value
+ * d * sc[j] * (q - 32)).  The pages do not give which ql nibble and which qh
+ * bit pair belong to element e; this takes the GGUF arrangement (parity
+ * unpinned): half h = e / 128, r = e % 128, group g = r / 32, l = r % 32;
+ * low4 = nibble (g < 2 ? low : high) of ql[64h + l + 32 (g & 1)];
+ * high2 = (qh[32h + l] >> 2g) & 3. */
+static int orc_q6_K_code(const uint8_t* blk, int e) {
+  const uint8_t* ql = blk;
+  const uint8_t* qh = blk + 128;
+  int h = e / 128, r = e % 128, g = r / 32, l = r % 32;
+  uint8_t lb = ql[64 * h + l + 32 * (g & 1)];
+  int low4 = (g < 2) ? (lb & 0x0F) : (lb >> 4);
+  int high2 = (qh[32 * h + l] >> (2 * g)) & 3;
+  return low4 | (high2 << 4);
+}
+
+/* ------------------------------------------------------------------------- */
+/* DequantizeRow ([rml] "Dequantization": one block at a time, shaped like    */
+/* the format; [sipllm] dequantize_row(t, src, dst, n)).                     */
+/* ------------------------------------------------------------------------- */
+
+int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
+  int64_t be = orc_block_elems(type), bb = orc_block_bytes(type);
+  if (be == 0) return ORC_BAD_TYPE;
+  if (n < 0 || n % be != 0) return ORC_BAD_SHAPE;
+  for (int64_t b = 0; b < n / be; ++b) {
+    const uint8_t* blk = src + bb * b;
+    float* y = dst + be * b;
+    switch (type) {
+      case ORC_Q8_0: { /* [cl] Example 1: value = qs[j] * d */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        for (int j = 0; j < 32; ++j) y[j] = (float)(int8_t)blk[2 + j] * d;
+        break;
+      }
+      case ORC_Q4_0: { /* [cl] Example 6: value = (nibble - 8) * d */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        for (int e = 0; e < 32; ++e) y[e] = (float)orc_q4_0_code(blk, e) * d;
+        break;
+      }
+      case ORC_Q4_K: { /* [rml] trace: x = d * scale * q - dmin * min */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        float dmin = orc_f16_to_f32(orc_get_u16(blk + 2));
+        for (int e = 0; e < 256; ++e) {
+          int sc, m;
+          orc_q4_K_scale_min(blk + 4, e / 32, &sc, &m);
+          int q = orc_q4_K_code(blk, e);
+          y[e] = d * (float)sc * (float)q - dmin * (float)m;
+        }
+        break;
+      }
+      case ORC_Q6_K: { /* [candle] BlockQ6K: d * sc[j] * (q - 32) */
+        float d = orc_f16_to_f32(orc_get_u16(blk + 208));
+        const int8_t* sc = (const int8_t*)(blk + 192);
+        for (int e = 0; e < 256; ++e) {
+          int q = orc_q6_K_code(blk, e);
+          y[e] = d * (float)sc[e / 16] * (float)(q - 32);
+        }
+        break;
+      }
+      case ORC_Q8_K: { /* [candle] BlockQ8K: d * q (test helper: activations) */
+        float d = orc_get_f32(blk);
+        for (int j = 0; j < 256; ++j) y[j] = d * (float)(int8_t)blk[4 + j];
+        break;
+      }
+      default:
+        return ORC_BAD_TYPE;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* VecDot ([rml] "Quantized dot products", "Kernels and references": every    */
+/* product inside a block is an exact int32 sum, computed here element by     */
+/* element as VecDotRef does; only the block scales are float).              */
+/* ------------------------------------------------------------------------- */
+
+/* Integer quantities kept per weight block: one s for Q8_0, Q4_0, Q6_K; the
+ * pair (S_q, S_m) for Q4_K (scale sum and min sum). */
+int64_t orc_sums_per_block(int weight_type) {
+  switch (weight_type) {
+    case ORC_Q8_0:
+    case ORC_Q4_0:
+    case ORC_Q6_K:
+      return 1;
+    case ORC_Q4_K:
+      return 2;
+    default:
+      return 0;
+  }
+}
+
+/* Exact per-block integer sums of one weight row against its paired act row. */
+static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t* out) {
+  switch (wt) {
+    case ORC_Q8_0: { /* [cl] Example 10 step 1: s = sum of the 32 code products */
+      int32_t s = 0;
+      for (int j = 0; j < 32; ++j) s += (int32_t)(int8_t)wb[2 + j] * (int32_t)(int8_t)xb[2 + j];
+      out[0] = s;
+      return ORC_OK;
+    }
+    case ORC_Q4_0: { /* [cl] Example 11: low nibble x a_j, high nibble x a_{j+16} */
+      int32_t s = 0;
+      for (int e = 0; e < 32; ++e) s += (int32_t)orc_q4_0_code(wb, e) * (int32_t)(int8_t)xb[2 + e];
+      out[0] = s;
+      return ORC_OK;
+    }
+    case ORC_Q4_K: {
+      /* S_q = sum_j sc_j * (sum_{e in j} q_e a_e);  S_m = sum_j m_j * (sum_{e in j} a_e).
+       * [rml]: the sub-block min term is min * sum(a); the reference sums it
+       * element by element, the kernels take sum(a) over 32 activations as two
+       * stored 16-sums (bsums).  Both routes are computed and must agree. */
+      const uint8_t* a = xb + 4;
+      int32_t sq = 0, sm = 0, sm_bsums = 0;
+      for (int j = 0; j < 8; ++j) {
+        int sc, m;
+        orc_q4_K_scale_min(wb + 4, j, &sc, &m);
+        int32_t s = 0, sa = 0;
+        for (int e = 32 * j; e < 32 * j + 32; ++e) {
+          s += (int32_t)orc_q4_K_code(wb, e) * (int32_t)(int8_t)a[e];
+          sa += (int32_t)(int8_t)a[e];
+        }
+        sq += sc * s;
+        sm += m * sa;
+        int32_t bs = (int32_t)orc_get_i16(xb + 260 + 2 * (2 * j)) +
+                     (int32_t)orc_get_i16(xb + 260 + 2 * (2 * j + 1));
+        sm_bsums += m * bs;
+      }
+      if (sm != sm_bsums) return ORC_INCONSISTENT;
+      out[0] = sq;
+      out[1] = sm;
+      return ORC_OK;
+    }
+    case ORC_Q6_K: { /* S = sum_j sc_j * sum_{e in j} (q_e - 32) a_e, 16-element j */
+      const uint8_t* a = xb + 4;
+      const int8_t* sc = (const int8_t*)(wb + 192);
+      int32_t S = 0;
+      for (int j = 0; j < 16; ++j) {
+        int32_t s = 0;
+        for (int e = 16 * j; e < 16 * j + 16; ++e)
+          s += (int32_t)(orc_q6_K_code(wb, e) - 32) * (int32_t)(int8_t)a[e];
+        S += (int32_t)sc[j] * s;
+      }
+      out[0] = S;
+      return ORC_OK;
+    }
+    default:
+      return ORC_BAD_TYPE;
+  }
+}
+
+/* The one float step per block ([rml] "Kernels and references": kernels and
+ * references share it).  Q8_0/Q4_0: c = s * (dw * dx) with both f16 scales
+ * ([cl] Example 10 step 2).  Q4_K: c = (dx*d) * S_q - (dx*dmin) * S_m.
+ * Q6_K: c = (dx*d) * S.  dx of Q8_K is f32 ([candle] BlockQ8K). */
+static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s) {
+  switch (wt) {
+    case ORC_Q8_0:
+    case ORC_Q4_0: {
+      float dw = orc_f16_to_f32(orc_get_u16(wb));
+      float dx = orc_f16_to_f32(orc_get_u16(xb));
+      return (float)s[0] * (dw * dx);
+    }
+    case ORC_Q4_K: {
+      float dx = orc_get_f32(xb);
+      float d = orc_f16_to_f32(orc_get_u16(wb));
+      float dmin = orc_f16_to_f32(orc_get_u16(wb + 2));
+      return (dx * d) * (float)s[0] - (dx * dmin) * (float)s[1];
+    }
+    case ORC_Q6_K: {
+      float dx = orc_get_f32(xb);
+      float d = orc_f16_to_f32(orc_get_u16(wb + 208));
+      return (dx * d) * (float)s[0];
+    }
+    default:
+      return NAN;
+  }
+}
+
+int orc_block_sums(int wt, const uint8_t* w, const uint8_t* xq, int64_t n, int32_t* sums) {
+  int at = orc_act_type(wt);
+  if (at < 0) return ORC_BAD_PAIR;
+  int64_t be = orc_block_elems(wt), bw = orc_block_bytes(wt), bx = orc_block_bytes(at);
+  if (n < 0 || n % be != 0) return ORC_BAD_SHAPE;
+  int64_t k = orc_sums_per_block(wt);
+  for (int64_t b = 0; b < n / be; ++b) {
+    int rc = orc_block_ints(wt, w + bw * b, xq + bx * b, sums + k * b);
+    if (rc != ORC_OK) return rc;
+  }
+  return ORC_OK;
+}
+
+/* VecDot(weight, w, x, n): y = sum over blocks of the float step, accumulated
+ * in f32 in block order ([cl] Example 10: `sumf += ...`).  l1 (optional)
+ * receives sum |c_b| in f64, the scale the output tolerance is taken against
+ * ([cl] Example 10 reports error against the sum of |a*b|). */
+int orc_vec_dot(int wt, const uint8_t* w, const uint8_t* xq, int64_t n, float* out, double* l1) {
+  int at = orc_act_type(wt);
+  if (at < 0) return ORC_BAD_PAIR;
+  int64_t be = orc_block_elems(wt), bw = orc_block_bytes(wt), bx = orc_block_bytes(at);
+  if (n < 0 || n % be != 0) return ORC_BAD_SHAPE;
+  float sumf = 0.0f;
+  double sabs = 0.0;
+  int32_t s[2];
+  for (int64_t b = 0; b < n / be; ++b) {
+    int rc = orc_block_ints(wt, w + bw * b, xq + bx * b, s);
+    if (rc != ORC_OK) return rc;
+    float c = orc_block_float(wt, w + bw * b, xq + bx * b, s);
+    sumf += c;
+    sabs += fabs((double)c);
+  }
+  *out = sumf;
+  if (l1) *l1 = sabs;
+  return ORC_OK;
+}
+
+/* GEMV ([sipllm] matmul_quant: W is [n_out, n_in] row-major, whole blocks per
+ * row; the activation is quantized once and reused by every row).  xq holds
+ * ncols activation rows of n_in elements each; y is [ncols][n_out]. */
+int orc_gemv(int wt, const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_t* xq,
+             int64_t ncols, float* y, double* l1) {
+  int at = orc_act_type(wt);
+  if (at < 0) return ORC_BAD_PAIR;
+  int64_t rw = orc_row_bytes(wt, n_in), rx = orc_row_bytes(at, n_in);
+  if (rw == 0 || n_out < 0 || ncols < 0) return ORC_BAD_SHAPE;
+  for (int64_t c = 0; c < ncols; ++c) {
+    for (int64_t r = 0; r < n_out; ++r) {
+      int rc = orc_vec_dot(wt, W + rw * r, xq + rx * c, n_in, y + c * n_out + r,
+                           l1 ? l1 + c * n_out + r : NULL);
+      if (rc != ORC_OK) return rc;
+    }
+  }
+  return ORC_OK;
+}

@@ -1,0 +1,77 @@
+/*
+ * qk_oracle.h - plain scalar CPU oracle for ggml block-quantized GEMV.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this code: only tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header or constant with the HIP library; it keeps
+ * its own copy of the block layouts on purpose.
+ *
+ * Every routine is written element by element, in the order the pages define
+ * the formats, not for speed.  Sources (page title, then section):
+ *   [rml]     "Quantization" (rayaq.ca/rml/quantization)
+ *   [sipllm]  "Quantization" (ankit1057.github.io/sipllm-docs)
+ *   [cl]      "Building Q8_0 and Q4_0 Like ggml" (codeloopback.dev), Examples 1-14
+ *   [candle]  "量化格式" (rustineverything.app/docs/candle/06-quantized/formats)
+ *
+ * Parity status per function (what pins it is listed in tests/test_oracle_pins.py):
+ *   f16 conversion, quantize_q8_0, quantize_q4_0, dequantize Q8_0/Q4_0,
+ *   vec_dot Q8_0xQ8_0 and Q4_0xQ8_0: pinned by printed bytes and values.
+ *   dequantize Q4_K: pinned by the [rml] element-200 trace and [candle]
+ *   get_scale_min_k4 prose, plus brute force.
+ *   vec_dot Q4_KxQ8_K / Q6_KxQ8_K: pinned by brute force against the dequant
+ *   definitions and by the bsums identity.
+ *   quantize_q8_K: invariants only (the pages give its layout, not its scale
+ *   rule); the scale rule taken is the Q8_0 one over 256 elements.
+ *   Q6_K ql/qh bit arrangement: parity unpinned (the pages give only the field
+ *   roles); the GGUF arrangement is assumed.
+ */
+#ifndef QK_ORACLE_H
+#define QK_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGUF type ids (ggml's numbering, which is what a GGUF tensor record stores). */
+#define ORC_Q4_0 2
+#define ORC_Q8_0 8
+#define ORC_Q4_K 12
+#define ORC_Q6_K 14
+#define ORC_Q8_K 15
+
+/* Return codes. */
+#define ORC_OK 0
+#define ORC_BAD_TYPE (-1)
+#define ORC_BAD_SHAPE (-2)
+#define ORC_BAD_PAIR (-3)
+#define ORC_INCONSISTENT (-4) /* two independent routes to one integer disagreed */
+
+int64_t orc_block_elems(int type);
+int64_t orc_block_bytes(int type);
+int64_t orc_row_bytes(int type, int64_t n);
+int orc_act_type(int weight_type);
+
+float orc_f16_to_f32(uint16_t h);
+uint16_t orc_f32_to_f16(float f);
+
+int orc_quantize_q8_0(const float* x, uint8_t* out, int64_t n);
+int orc_quantize_q8_K(const float* x, uint8_t* out, int64_t n);
+int orc_quantize_q4_0(const float* x, uint8_t* out, int64_t n);
+
+int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n);
+
+int64_t orc_sums_per_block(int weight_type);
+int orc_block_sums(int weight_type, const uint8_t* w, const uint8_t* xq, int64_t n,
+                   int32_t* sums);
+int orc_vec_dot(int weight_type, const uint8_t* w, const uint8_t* xq, int64_t n,
+                float* out, double* l1);
+int orc_gemv(int weight_type, const uint8_t* W, int64_t n_out, int64_t n_in,
+             const uint8_t* xq, int64_t ncols, float* y, double* l1);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

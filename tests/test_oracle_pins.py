@@ -1,0 +1,587 @@
+"""Pins of the CPU oracle against what the pages fix (no GPU needed).
+
+Every check here compares the oracle with something other than itself: values
+printed on the pages (tests/golden/, each file citing its page and section),
+a library routine for a textbook case (numpy's IEEE binary16 conversion),
+structural properties the pages state in prose, and f64 brute force on tiny
+rows.  Sources are cited by page title and section.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from golden_io import keyvals, rows
+from jrandom import JavaRandom
+from oracle import oracle as o
+
+F32 = np.float32
+
+
+# --------------------------------------------------------------------------
+# Type table and row geometry
+# --------------------------------------------------------------------------
+
+def test_type_table_matches_printed_geometry():
+    # candle "量化格式" GgmlDType table; codeloopback lesson format table.
+    ids = {"Q4_0": o.Q4_0, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
+    for name, gid, elems, nbytes, bpw in rows("type_table.txt"):
+        t = ids[name]
+        assert t == int(gid)
+        assert o.block_elems(t) == int(elems)
+        assert o.block_bytes(t) == int(nbytes)
+        assert f"{o.block_bytes(t) * 8 / o.block_elems(t):.4f}" == bpw
+
+
+def test_row_bytes_whole_blocks_no_padding():
+    # codeloopback Example 9: 64 x 4096 tensor is 278,528 B in Q8_0 and 147,456 B in
+    # Q4_0; row strides 4352 and 2304.  Example 15: a 100-element row is rejected.
+    assert 64 * o.row_bytes(o.Q8_0, 4096) == 278528
+    assert 64 * o.row_bytes(o.Q4_0, 4096) == 147456
+    assert o.row_bytes(o.Q8_0, 4096) == 4352
+    assert o.row_bytes(o.Q4_0, 4096) == 2304
+    assert o.row_bytes(o.Q4_0, 100) == 0
+    assert o.row_bytes(o.Q4_K, 11008) == 43 * 144
+    assert o.row_bytes(o.Q6_K, 11008) == 43 * 210
+    assert o.row_bytes(o.Q4_K, 4096 + 32) == 0
+    assert o.row_bytes(99, 256) == 0
+
+
+def test_pairing_table():
+    # candle VecDotType table; codeloopback Example 11 (Q4_0 -> Q8_0).
+    assert o.act_type(o.Q4_0) == o.Q8_0
+    assert o.act_type(o.Q8_0) == o.Q8_0
+    assert o.act_type(o.Q4_K) == o.Q8_K
+    assert o.act_type(o.Q6_K) == o.Q8_K
+    assert o.act_type(o.Q8_K) == -1
+    assert o.act_type(3) == -1
+
+
+# --------------------------------------------------------------------------
+# binary16 conversion
+# --------------------------------------------------------------------------
+
+def test_f16_decode_all_patterns_against_numpy():
+    # IEEE 754 binary16 decode is a textbook routine; numpy implements it.
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([o.f16_to_f32(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_encode_against_numpy_rne():
+    rng = np.random.default_rng(1234)
+    # random f32 bit patterns over the whole range, plus every f16 boundary and
+    # midpoint (ties), subnormals and overflow edges.
+    vals = [rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32).view(np.float32)]
+    h = np.arange(0, 0x7C01, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = (h[:-1] + h[1:]) / 2  # exact in f64; the f32 casts below hit ties and neighbours
+    m32 = mids.astype(np.float32)
+    vals += [h.astype(np.float32), m32, np.nextafter(m32, np.float32(np.inf)),
+             np.nextafter(m32, np.float32(0)),
+             np.array([65504, 65519.996, 65520, 65536, 1e-8, 2.98e-8, 2.9802322e-8,
+                       5.96e-8, 6.1e-5], dtype=np.float32)]
+    v = np.concatenate(vals)
+    v = np.concatenate([v, -v])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = np.array([o.f32_to_f16(float(x)) for x in v], dtype=np.uint16)
+    nan = np.isnan(v)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7C00) == 0x7C00) and np.all((got[nan] & 0x3FF) != 0)
+
+
+def test_f16_printed_scales():
+    kv = keyvals("q8_0_blocks.txt")
+    # codeloopback Example 2: d = 0.011682516 -> f16 0x21FB = 0.011680603.
+    assert o.f32_to_f16(float(F32(kv["cl_ex2.d_f32"]))) == int(kv["cl_ex2.d_f16_bits"], 16)
+    assert f"{o.f16_to_f32(0x21FB):.9f}" == kv["cl_ex2.d_f16"]
+    # candle: [40, 22] -> 0x2240 = 0.012207031.
+    assert f"{o.f16_to_f32(0x2240):.9f}" == kv["candle.d"]
+    # rml Q4_0 example: 0.25 -> 0x3400; codeloopback Example 14: 9.5 / -8 -> 0xBCC0.
+    kq = keyvals("q4_0_blocks.txt")
+    assert o.f32_to_f16(0.25) == int(kq["rml.d_f16_bits"], 16)
+    assert o.f32_to_f16(float(F32(9.5) / F32(-8))) == int(kq["cl_ex14_read.d_f16_bits"], 16)
+
+
+# --------------------------------------------------------------------------
+# quantize_row_q8_0 / q4_0 against printed bytes
+# --------------------------------------------------------------------------
+
+def _cl_inputs(n):
+    i = np.arange(n)
+    return (((i * 7919) % 1001) - 500).astype(np.float32) / np.float32(337)
+
+
+def test_q8_0_candle_block():
+    kv = keyvals("q8_0_blocks.txt")
+    x = (np.arange(32, dtype=np.float32) - F32(15.5)) / F32(10)
+    b = o.quantize(o.Q8_0, x)
+    assert b[:2].tobytes().hex() == kv["candle.d_bytes_hex"]
+    assert [int(c) for c in b[2:].view(np.int8)] == [int(c) for c in kv["candle.qs"].split()]
+    back = o.dequantize(o.Q8_0, b, 32)
+    assert np.array_equal(back[:4], np.array(kv["candle.back4"].split(), dtype=np.float32))
+    assert f"{o.f16_to_f32(int(b[0]) | int(b[1]) << 8):.9f}" == kv["candle.d"]
+
+
+def test_q8_0_codeloopback_examples_2_3_4():
+    kv = keyvals("q8_0_blocks.txt")
+    x = _cl_inputs(32)
+    b = o.quantize(o.Q8_0, x)
+    assert [int(c) for c in b[2:].view(np.int8)] == [int(c) for c in kv["cl_ex2.qs"].split()]
+    assert b.tobytes().hex() == kv["cl_ex2.hex"]
+    assert f"{np.abs(x).max() / F32(127):.9f}" == kv["cl_ex2.d_f32"]
+    y = o.dequantize(o.Q8_0, b, 32)
+    assert y[0] == F32(kv["cl_ex2.y0"])  # printed as the shortest f32 repr
+    # Example 3: error with the f32 scale and with the stored f16 scale.
+    d = np.abs(x).max() / F32(127)
+    codes = b[2:].view(np.int8).astype(np.float32)
+    err_f32 = np.max(np.abs(codes * d - x).astype(np.float64))
+    err_f16 = np.max(np.abs((y - x).astype(np.float64)))
+    rmse = 100 * math.sqrt(np.sum((y - x).astype(np.float64) ** 2) / np.sum((x * x).astype(np.float64)))
+    assert f"{err_f32:.6f}" == kv["cl_ex3.max_err_f32_d"]
+    assert f"{err_f16:.6f}" == kv["cl_ex3.max_err_f16_d"]
+    assert f"{rmse:.4f}" == kv["cl_ex3.rel_rmse_pct"]
+
+
+def test_hex_crosscheck_example_14():
+    x = _cl_inputs(64)
+    x[40] = F32(9.5)
+    types = {"Q8_0": o.Q8_0, "Q4_0": o.Q4_0}
+    for blk, name, hexs in rows("hex_crosscheck.txt"):
+        blk = int(blk)
+        assert o.quantize(types[name], x[32 * blk:32 * blk + 32]).tobytes().hex() == hexs
+
+
+def test_q4_0_rml_worked_example():
+    kv = keyvals("q4_0_blocks.txt")
+    x = np.zeros(32, dtype=np.float32)
+    x[:4] = np.array(kv["rml.x4"].split(), dtype=np.float32)
+    b = o.quantize(o.Q4_0, x)
+    assert b[:6].tobytes().hex() == kv["rml.head_hex"]
+    y = o.dequantize(o.Q4_0, b, 32)
+    assert y[0] == F32(-2.0)          # the extreme value is exact
+    assert y[2] == F32(kv["rml.decoded_2_0"])  # 2.0 comes back as 1.75
+
+
+def test_q4_0_nibble_reading_example_14():
+    # Second Q4_0 block of Example 14: byte 0x79 holds code 9 for value 32 (low
+    # nibble) and code 7 for value 48 (high nibble); d = 0xBCC0.
+    kv = keyvals("q4_0_blocks.txt")
+    x = _cl_inputs(64)
+    x[40] = F32(9.5)
+    b = o.quantize(o.Q4_0, x[32:64])
+    assert b[2] == int(kv["cl_ex14_read.byte0"], 16)
+    d = o.f16_to_f32(int(kv["cl_ex14_read.d_f16_bits"], 16))
+    y = o.dequantize(o.Q4_0, b, 32)
+    assert y[0] == F32(9 - 8) * F32(d)
+    assert y[16] == F32(7 - 8) * F32(d)
+
+
+def test_q4_0_example_6_errors():
+    kv = keyvals("q4_0_blocks.txt")
+    x = _cl_inputs(32)
+    for t, key in ((o.Q4_0, "q4_0"), (o.Q8_0, "q8_0")):
+        y = o.dequantize(t, o.quantize(t, x), 32)
+        assert " ".join(f"{v:.4f}" for v in y[:4]) == kv[f"cl_ex6.{key}_first4"]
+        diff = (y - x).astype(np.float64)
+        assert f"{np.max(np.abs(diff)):.4f}" == kv[f"cl_ex6.{key}_max_err"]
+        rmse = 100 * math.sqrt(np.sum(diff ** 2) / np.sum((x * x).astype(np.float64)))
+        assert f"{rmse:.3f}" == kv[f"cl_ex6.{key}_rel_rmse_pct"]
+
+
+def _fmt_out(v):
+    if np.isnan(v):
+        return "nan"
+    if np.isinf(v):
+        return "inf" if v > 0 else "-inf"
+    return repr(float(v)) if v != 0 else "0.0"
+
+
+def test_q8_0_edge_table():
+    # candle "一些边界值": NaN ignored by amax and coded 0; inf amax -> d = inf ->
+    # NaN block; d below the f16 subnormal range -> 0; d above 65504 -> inf.
+    for label, A, special, outs in rows("q8_edge.txt", sep="|"):
+        A = F32(A)
+        x = (A * np.arange(32, dtype=np.float32) / F32(31)).astype(np.float32)
+        if special == "x1=nan":
+            x[1] = np.nan
+        elif special == "x1=inf":
+            x[1] = np.inf
+        y = o.dequantize(o.Q8_0, o.quantize(o.Q8_0, x), 32)
+        expect = outs.split()
+        for got, want in zip(y[:3], expect):
+            if want in ("nan", "inf"):
+                assert _fmt_out(got) == want, label
+            else:
+                assert got == F32(want), (label, got, want)
+
+
+def test_q8_0_fixed_point_and_bound():
+    # codeloopback Example 4: requantizing dequantized values gives the same bytes;
+    # rontolisp quantize: a value moves by at most half a step (amax / 254 before
+    # the scale is rounded to f16).
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(32 * 500) * rng.choice([0.02, 1, 30], 32 * 500)).astype(np.float32)
+    b = o.quantize(o.Q8_0, x)
+    y = o.dequantize(o.Q8_0, b, x.size)
+    assert np.array_equal(o.quantize(o.Q8_0, y), b)
+    xb = x.reshape(-1, 32)
+    d = np.abs(xb).max(axis=1, keepdims=True) / F32(127)
+    codes = b.reshape(-1, 34)[:, 2:].view(np.int8).astype(np.float32)
+    assert np.all(np.abs(codes * d - xb) <= np.abs(xb).max(axis=1, keepdims=True) / 254 * (1 + 1e-6))
+    bq = o.quantize(o.Q4_0, x)
+    assert np.array_equal(o.quantize(o.Q4_0, o.dequantize(o.Q4_0, bq, x.size)), bq)
+
+
+def test_zero_block_gives_zero():
+    # rml ZeroActivationsGiveZero; codeloopback Example 2 (d = 0 -> id = 0).
+    z = np.zeros(512, dtype=np.float32)
+    b8 = o.quantize(o.Q8_0, z)
+    assert not b8.any()
+    bk = o.quantize(o.Q8_K, z)
+    assert not bk.any()
+    rng = np.random.default_rng(3)
+    w = rng.integers(0, 256, o.row_bytes(o.Q4_K, 512), dtype=np.uint8)
+    w.reshape(-1, 144)[:, 0:2] = np.frombuffer(np.float16(0.01).tobytes(), np.uint8)
+    w.reshape(-1, 144)[:, 2:4] = np.frombuffer(np.float16(0.02).tobytes(), np.uint8)
+    y, l1 = o.vec_dot(o.Q4_K, w, bk, 512)
+    assert y == 0.0 and l1 == 0.0
+
+
+# --------------------------------------------------------------------------
+# Q8_K invariants (its scale rule is not on the pages; these hold for any rule)
+# --------------------------------------------------------------------------
+
+def test_q8_K_layout_invariants():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(256 * 64).astype(np.float32) * rng.choice([1e-3, 1, 50], 256 * 64).astype(np.float32)
+    b = o.quantize(o.Q8_K, x).reshape(-1, 292)
+    d = b[:, 0:4].copy().view(np.float32)[:, 0]
+    qs = b[:, 4:260].view(np.int8).astype(np.int32)
+    bsums = b[:, 260:292].copy().view(np.int16).astype(np.int32)
+    assert np.array_equal(bsums, qs.reshape(-1, 16, 16).sum(axis=2))  # candle BlockQ8K
+    assert np.all(np.abs(qs) <= 127)
+    amax = np.abs(x.reshape(-1, 256)).max(axis=1)
+    # every block uses its full code range and codes are within half a step
+    assert np.all(np.abs(qs).max(axis=1) == 127)
+    err = np.abs(qs * d[:, None].astype(np.float64) - x.reshape(-1, 256))
+    assert np.all(err <= (amax / 254 * (1 + 1e-5))[:, None])
+    y = o.dequantize(o.Q8_K, b, x.size).reshape(-1, 256)
+    assert np.array_equal(y, (qs.astype(np.float32) * d[:, None]).astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# Q4_K: rml element-200 trace and candle get_scale_min_k4 prose
+# --------------------------------------------------------------------------
+
+def _q4k_block(rng):
+    b = rng.integers(0, 256, 144, dtype=np.uint8)
+    b[0:2] = np.frombuffer(np.float16(rng.uniform(0.01, 0.1)).tobytes(), np.uint8)
+    b[2:4] = np.frombuffer(np.float16(rng.uniform(0.01, 0.1)).tobytes(), np.uint8)
+    return b
+
+
+def test_q4_K_element_200_trace():
+    # rml "Unpacking the packed fields": element 200 is in sub-block 6, chunk 3,
+    # position 8 -> low nibble of qs[104]; scale = (s[10] & 0xF) | ((s[2] >> 6) << 4),
+    # min = (s[10] >> 4) | ((s[6] >> 6) << 4); x = d * scale * q - dmin * min.
+    rng = np.random.default_rng(200)
+    for _ in range(50):
+        b = np.zeros(144, dtype=np.uint8)
+        d, dmin = np.float16(rng.uniform(0.01, 0.2)), np.float16(rng.uniform(0.01, 0.2))
+        b[0:2] = np.frombuffer(d.tobytes(), np.uint8)
+        b[2:4] = np.frombuffer(dmin.tobytes(), np.uint8)
+        s = b[4:16]
+        s[2], s[6], s[10] = rng.integers(0, 256, 3)
+        b[16 + 104] = rng.integers(0, 256)
+        scale = (int(s[10]) & 0xF) | ((int(s[2]) >> 6) << 4)
+        mn = (int(s[10]) >> 4) | ((int(s[6]) >> 6) << 4)
+        q = int(b[16 + 104]) & 0xF
+        want = F32(d) * F32(scale) * F32(q) - F32(dmin) * F32(mn)
+        y = o.dequantize(o.Q4_K, b, 256)
+        assert y[200] == want
+        # every other byte (besides d, dmin and the four above) leaves y[200] alone
+        for k in range(4, 144):
+            if k in (4 + 2, 4 + 6, 4 + 10, 16 + 104):
+                continue
+            b2 = b.copy()
+            b2[k] ^= rng.integers(1, 256)
+            assert o.dequantize(o.Q4_K, b2, 256)[200] == y[200], k
+
+
+def _sub_block_effect(b, k, mask):
+    """Which (sub-block, kind) values change when byte k of a Q4_K block is
+    XORed with mask.  kind 'sc' is seen through dmin = 0, 'm' through d = 0."""
+    out = set()
+    for kind in ("sc", "m"):
+        bb = b.copy()
+        if kind == "sc":
+            bb[2:4] = 0
+        else:
+            bb[0:2] = 0
+        y0 = o.dequantize(o.Q4_K, bb, 256)
+        bb[k] ^= mask
+        y1 = o.dequantize(o.Q4_K, bb, 256)
+        for j in range(8):
+            if not np.array_equal(y0[32 * j:32 * j + 32], y1[32 * j:32 * j + 32]):
+                out.add((j, kind))
+    return out
+
+
+def test_q4_K_scale_min_bit_positions():
+    # candle 块结构 (get_scale_min_k4): sub-blocks 0-3 keep scale and min in the low
+    # 6 bits of bytes 0-7; sub-blocks 4-7 keep their low 4 bits in bytes 8-11 and
+    # borrow the high 2 bits from the top 2 bits of bytes 0-7.  rml's trace fixes
+    # which of those belong to the scale (low nibble / bytes 0-3) and which to the
+    # min (high nibble / bytes 4-7).
+    rng = np.random.default_rng(5)
+    b = _q4k_block(rng)
+    b[16:] = 0x11  # q = 1 everywhere so a scale change shows in every element
+    for t in range(4):
+        assert _sub_block_effect(b, 4 + t, 0x3F) == {(t, "sc")}
+        assert _sub_block_effect(b, 4 + t, 0xC0) == {(t + 4, "sc")}
+        assert _sub_block_effect(b, 8 + t, 0x3F) == {(t, "m")}
+        assert _sub_block_effect(b, 8 + t, 0xC0) == {(t + 4, "m")}
+        assert _sub_block_effect(b, 12 + t, 0x0F) == {(t + 4, "sc")}
+        assert _sub_block_effect(b, 12 + t, 0xF0) == {(t + 4, "m")}
+
+
+def test_q4_K_each_nibble_is_one_element():
+    # rml trace: element e of chunk c = e/64 at p = e%64 is the low nibble of
+    # qs[32c + p] when p < 32, else (the complement) the high nibble of qs[32c+p-32].
+    rng = np.random.default_rng(9)
+    b = _q4k_block(rng)
+    b[4:16] = 0x21  # nonzero scales in every sub-block
+    y0 = o.dequantize(o.Q4_K, b, 256)
+    for k in range(128):
+        c, p = divmod(k, 32)
+        for nib, e in ((0x0F, 64 * c + p), (0xF0, 64 * c + p + 32)):
+            bb = b.copy()
+            bb[16 + k] ^= nib
+            changed = np.nonzero(o.dequantize(o.Q4_K, bb, 256) != y0)[0]
+            assert list(changed) == [e], (k, nib)
+
+
+# --------------------------------------------------------------------------
+# Q6_K: only invariants (bit arrangement is not on the pages: parity unpinned)
+# --------------------------------------------------------------------------
+
+def test_q6_K_structure_invariants():
+    # candle 块结构: ql = low 4 bits, qh = high 2 bits, 16 int8 scales for 16-element
+    # sub-blocks, value d * sc[j] * (q - 32).  Properties any arrangement satisfies:
+    # every ql nibble and every qh bit pair controls exactly one element, each element
+    # is controlled by exactly one of each, and the scale of element e is sc[e / 16].
+    rng = np.random.default_rng(6)
+    b = rng.integers(0, 256, 210, dtype=np.uint8)
+    b[192:208] = rng.integers(1, 100, 16).astype(np.int8).view(np.uint8)
+    b[208:210] = np.frombuffer(np.float16(0.5).tobytes(), np.uint8)
+    y0 = o.dequantize(o.Q6_K, b, 256)
+    owner_low, owner_high = {}, {}
+    for k in range(128):
+        for nib in (0x0F, 0xF0):
+            bb = b.copy()
+            bb[k] ^= nib
+            ch = np.nonzero(o.dequantize(o.Q6_K, bb, 256) != y0)[0]
+            assert len(ch) == 1
+            assert int(ch[0]) not in owner_low
+            owner_low[int(ch[0])] = (k, nib)
+    for k in range(64):
+        for sh in range(4):
+            bb = b.copy()
+            bb[128 + k] ^= 3 << (2 * sh)
+            ch = np.nonzero(o.dequantize(o.Q6_K, bb, 256) != y0)[0]
+            assert len(ch) == 1
+            assert int(ch[0]) not in owner_high
+            owner_high[int(ch[0])] = (k, sh)
+    assert len(owner_low) == 256 and len(owner_high) == 256
+    d = F32(0.5)
+    for j in range(16):
+        bb = b.copy()
+        bb[192 + j] = np.uint8(np.int8(-1).view(np.uint8))  # sc = -1
+        y = o.dequantize(o.Q6_K, bb, 256)
+        ch = np.nonzero(y != y0)[0]
+        assert set(ch) <= set(range(16 * j, 16 * j + 16))
+        # value = d * sc * (q - 32) -> with sc = -1, y = -d * (q - 32); q = 32 +- 32 range
+        q = -y[16 * j:16 * j + 16] / d + 32
+        assert np.all(q == np.round(q)) and np.all((q >= 0) & (q <= 63))
+    bb = b.copy()
+    bb[:192] = 0
+    # q = 0 everywhere: value = -32 * d * sc
+    sc = bb[192:208].view(np.int8).astype(np.float32)
+    assert np.array_equal(o.dequantize(o.Q6_K, bb, 256), np.repeat(F32(-32) * d * sc, 16))
+
+
+# --------------------------------------------------------------------------
+# VecDot: brute force against the dequantized values, and the seeded examples
+# --------------------------------------------------------------------------
+
+def _random_weights(t, nblocks, rng):
+    nb = o.block_bytes(t)
+    w = rng.integers(0, 256, nb * nblocks, dtype=np.uint8).reshape(nblocks, nb)
+    h = lambda lo, hi: np.frombuffer(rng.uniform(lo, hi, nblocks).astype(np.float16).tobytes(), np.uint8).reshape(nblocks, 2)
+    if t in (o.Q8_0, o.Q4_0):
+        w[:, 0:2] = h(0.001, 0.05)
+    elif t == o.Q4_K:
+        w[:, 0:2] = h(1e-3, 1e-2)
+        w[:, 2:4] = h(1e-3, 1e-2)
+    elif t == o.Q6_K:
+        w[:, 192:208] = rng.integers(-64, 64, (nblocks, 16)).astype(np.int8).view(np.uint8)
+        w[:, 208:210] = h(1e-3, 1e-2)
+    return w.reshape(-1)
+
+
+def _act_parts(at, xq, n):
+    """(per-element f64 scale, per-element int code) of an activation row."""
+    if at == o.Q8_0:
+        blk = xq.reshape(-1, 34)
+        d = blk[:, 0:2].copy().view(np.float16).astype(np.float64)[:, 0]
+        return np.repeat(d, 32), blk[:, 2:].view(np.int8).astype(np.int64).reshape(-1)
+    blk = xq.reshape(-1, 292)
+    d = blk[:, 0:4].copy().view(np.float32).astype(np.float64)[:, 0]
+    return np.repeat(d, 256), blk[:, 4:260].view(np.int8).astype(np.int64).reshape(-1)
+
+
+@pytest.mark.parametrize("t", [o.Q8_0, o.Q4_0, o.Q4_K, o.Q6_K])
+def test_vec_dot_brute_force(t):
+    rng = np.random.default_rng(100 + t)
+    at = o.act_type(t)
+    for nblocks_k in (1, 2, 3):
+        n = nblocks_k * 256
+        w = _random_weights(t, n // o.block_elems(t), rng)
+        x = rng.standard_normal(n).astype(np.float32)
+        xq = o.quantize(at, x)
+        wdeq = o.dequantize(t, w, n).astype(np.float64)
+        dx, qx = _act_parts(at, xq, n)
+        terms = wdeq * (dx * qx)
+        brute = terms.sum()
+        # f64 evaluation of the oracle's exact block integers with the block scales
+        sums = o.block_sums(t, w, xq, n).astype(np.float64)
+        wb = w.reshape(n // o.block_elems(t), -1)
+        f16 = lambda a, off: a[:, off:off + 2].copy().view(np.float16).astype(np.float64)[:, 0]
+        if t in (o.Q8_0, o.Q4_0):
+            exact = np.sum(sums[:, 0] * f16(wb, 0) * dx[::32])
+        elif t == o.Q4_K:
+            exact = np.sum(dx[::256] * (f16(wb, 0) * sums[:, 0] - f16(wb, 2) * sums[:, 1]))
+        else:
+            exact = np.sum(dx[::256] * f16(wb, 208) * sums[:, 0])
+        scale = np.abs(terms).sum()
+        # Q8_0, Q4_0, Q6_K decoded values are exact in f32; Q4_K's d*sc*q - dmin*m
+        # rounds once per element.
+        tol = 1e-12 if t != o.Q4_K else 1e-7
+        assert abs(exact - brute) <= tol * scale, (t, n, exact, brute)
+        y, l1 = o.vec_dot(t, w, xq, n)
+        nbk = n // o.block_elems(t)
+        assert abs(y - exact) <= nbk * 2.0 ** -23 * l1 + 1e-30
+
+
+def _examples_10_11():
+    kv = keyvals("seeded_examples.txt")
+    n = 4096
+    r = JavaRandom(22)
+    a = np.empty(n, np.float32)
+    b = np.empty(n, np.float32)
+    for i in range(n):
+        a[i] = F32(r.next_gaussian()) * F32(0.02)
+        b[i] = F32(r.next_gaussian())
+    y10, _ = o.vec_dot(o.Q8_0, o.quantize(o.Q8_0, a), o.quantize(o.Q8_0, b), n)
+    exact10 = float(np.dot(a.astype(np.float64), b.astype(np.float64)))
+    r = JavaRandom(23)
+    w = np.empty(n, np.float32)
+    x = np.empty(n, np.float32)
+    for i in range(n):
+        w[i] = F32(r.next_gaussian()) * F32(0.02)
+        x[i] = F32(r.next_gaussian())
+    qw = o.quantize(o.Q4_0, w)
+    y11, _ = o.vec_dot(o.Q4_0, qw, o.quantize(o.Q8_0, x), n)
+    wo11 = float(np.dot(o.dequantize(o.Q4_0, qw, n).astype(np.float64), x.astype(np.float64)))
+    exact11 = float(np.dot(w.astype(np.float64), x.astype(np.float64)))
+    return kv, (y10, exact10, y11, wo11, exact11)
+
+
+def test_codeloopback_examples_10_11_vec_dot():
+    kv, (y10, exact10, y11, wo11, exact11) = _examples_10_11()
+    assert f"{y10:.6f}" == kv["ex10.q8_0_dot"]
+    assert f"{exact10:.6f}" == kv["ex10.exact"]
+    assert f"{y11:.6f}" == kv["ex11.q4_0_q8_0_kernel"]
+    assert f"{wo11:.6f}" == kv["ex11.q4_0_weights_f32_x"]
+    assert f"{exact11:.6f}" == kv["ex11.exact"]
+
+
+def _outlier_weights(r, count):
+    w = np.empty(count, np.float32)
+    for i in range(count):
+        g = F32(r.next_gaussian()) * F32(0.02)
+        w[i] = g * (F32(10) if r.next_int(500) == 0 else F32(1))
+    return w
+
+
+def _fake(t, x):
+    if t == "F16":
+        return x.astype(np.float16).astype(np.float32)
+    tt = {"Q8_0": o.Q8_0, "Q4_0": o.Q4_0}[t]
+    return o.dequantize(tt, o.quantize(tt, x), x.size)
+
+
+def test_codeloopback_example_12_error_table():
+    kv = keyvals("seeded_examples.txt")
+    x = _outlier_weights(JavaRandom(24), 65536)
+    p = np.sum((x * x).astype(np.float64))
+    for t in ("F16", "Q8_0", "Q4_0"):
+        y = _fake(t, x)
+        e = np.sum(((y - x).astype(np.float64)) ** 2)
+        assert f"{100 * math.sqrt(e / p):.4f}" == kv[f"ex12.{t}"], t
+
+
+def test_codeloopback_example_13_output_error():
+    kv = keyvals("seeded_examples.txt")
+    rows_, cols = 256, 4096
+    r = JavaRandom(25)
+    w = _outlier_weights(r, rows_ * cols).reshape(rows_, cols)
+    x = np.array([F32(r.next_gaussian()) for _ in range(cols)], dtype=np.float32)
+    xq = _fake("Q8_0", x)
+    ref = w.astype(np.float64) @ x.astype(np.float64)
+    for t in ("F16", "Q8_0", "Q4_0"):
+        wq = _fake(t, w.reshape(-1)).reshape(rows_, cols)
+        act = x if t == "F16" else xq
+        y = wq.astype(np.float64) @ act.astype(np.float64)
+        err = 100 * math.sqrt(np.sum((y - ref) ** 2) / np.sum(ref ** 2))
+        assert f"{err:.4f}" == kv[f"ex13.{t}"], t
+
+
+def test_codeloopback_example_15_project_report():
+    kv = keyvals("seeded_examples.txt")
+    rows_, cols = 512, 2048
+    r = JavaRandom(26)
+    w = _outlier_weights(r, rows_ * cols)
+    x = np.array([F32(r.next_gaussian()) for _ in range(cols)], dtype=np.float32)
+    for name, t in (("Q8_0", o.Q8_0), ("Q4_0", o.Q4_0)):
+        q = o.quantize(t, w.reshape(rows_, cols))
+        wq = o.dequantize(t, q, w.size)
+        e = np.sum(((wq - w).astype(np.float64)) ** 2)
+        p = np.sum((w * w).astype(np.float64))
+        assert f"{100 * math.sqrt(e / p):.3f}" == kv[f"ex15.{name}.weight_rmse"]
+        y = w.reshape(rows_, cols).astype(np.float64) @ x.astype(np.float64)
+        yq = wq.reshape(rows_, cols).astype(np.float64) @ x.astype(np.float64)
+        oe = 100 * math.sqrt(np.sum((yq - y) ** 2) / np.sum(y ** 2))
+        assert f"{oe:.3f}" == kv[f"ex15.{name}.output_err"]
+        assert np.array_equal(o.quantize(t, wq.reshape(rows_, cols)), q)  # stable
+
+
+def test_gemv_is_vec_dot_per_row_and_column():
+    # sipllm matmul_quant: y[o] = VecDot(row o, x) for each output row; every
+    # activation column is independent.
+    rng = np.random.default_rng(21)
+    for t in (o.Q8_0, o.Q4_0, o.Q4_K, o.Q6_K):
+        n_out, n_in, ncols = 5, 512, 3
+        W = _random_weights(t, n_out * n_in // o.block_elems(t), rng)
+        X = rng.standard_normal((ncols, n_in)).astype(np.float32)
+        xq = o.quantize(o.act_type(t), X)
+        y, l1 = o.gemv(t, W, n_out, n_in, xq, ncols)
+        rb = o.row_bytes(t, n_in)
+        for c in range(ncols):
+            for r_ in range(n_out):
+                v, s = o.vec_dot(t, W[rb * r_:rb * (r_ + 1)], xq[c], n_in)
+                assert y[c, r_] == F32(v) and l1[c, r_] == s
