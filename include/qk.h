@@ -1,0 +1,147 @@
+/*
+ * qk.h - C ABI of libqk.so, the MI355X (gfx950) block-quantized GEMV library.
+ *
+ * The library computes y = W x where W is stored row-major as whole ggml blocks
+ * (Q8_0, Q4_0, Q4_K or Q6_K, byte-exact GGUF layouts) and x is quantized once per
+ * call into int8 activation blocks (Q8_0 or Q8_K) aligned with W's blocks.  Every
+ * product inside a block is an exact int32 sum; only the block scales are float.
+ * Sources (page title, section):
+ *   "Quantization" (rml): type table, DequantizeRow, VecDot and its pairing.
+ *   "Quantization" (sipllm): dequantize_row(t, src, dst, n), matmul_quant layout.
+ *   "Building Q8_0 and Q4_0 Like ggml" (codeloopback): Q8_0/Q4_0 bytes, Examples 1-11.
+ *   "量化格式" (candle formats): type table, BlockQ4K/Q6K/Q8K fields, VecDotType.
+ *
+ * Conventions shared by every call:
+ *  - Types are ggml's ids, as a GGUF tensor record stores them.
+ *  - All buffers are device memory owned by the caller (for example torch tensors);
+ *    the library allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously on it; a QK_OK return means it was enqueued.
+ *  - Arguments are checked on the host before anything is enqueued; on any error
+ *    nothing is launched and no buffer is touched.
+ *  - Base pointers must be 16-byte aligned (QK_E_ALIGN otherwise).  Rows inside W
+ *    need not be: a Q6_K row of 11008 elements is 9030 bytes.
+ */
+#ifndef QK_H
+#define QK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ggml type ids of the formats on the path. */
+#define QK_TYPE_Q4_0 2
+#define QK_TYPE_Q8_0 8
+#define QK_TYPE_Q4_K 12
+#define QK_TYPE_Q6_K 14
+#define QK_TYPE_Q8_K 15
+
+/* Status codes returned by every call that can fail. */
+#define QK_OK 0
+#define QK_E_TYPE 1   /* unknown type id, or an activation type used as a weight */
+#define QK_E_SHAPE 3  /* n not a positive multiple of the block size, or a negative count */
+#define QK_E_ALIGN 4  /* a base pointer is not 16-byte aligned */
+#define QK_E_NULL 5   /* a required pointer is NULL */
+#define QK_E_DEVICE 6 /* the HIP runtime reported an error while enqueueing */
+#define QK_E_LIMIT 7  /* the activation row does not fit the kernels' LDS budget */
+
+/* Elements per block (32 or 256) and bytes per block (18, 34, 144, 210, 292) of a
+ * type, 0 for an unknown id.  Geometry from the candle formats page, "GgmlDType" table. */
+int64_t qk_block_elems(int type);
+int64_t qk_block_bytes(int type);
+
+/* Bytes of n elements of a type: n / block_elems * block_bytes, rows being whole
+ * blocks with nothing between them (codeloopback Example 9; sipllm type_nbytes).
+ * 0 when the type is unknown or n is negative or not a multiple of the block size. */
+int64_t qk_row_bytes(int type, int64_t n);
+
+/* Activation type a weight type is multiplied against (candle "VecDotType" table;
+ * codeloopback Example 11): Q4_0, Q8_0 -> Q8_0; Q4_K, Q6_K -> Q8_K; -1 otherwise. */
+int qk_act_type(int weight_type);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* qk_status_str(int status);
+
+/* Largest n_in a GEMV accepts for a weight type (the paired activation row is held
+ * in LDS); 0 for an unknown or non-weight type. */
+int64_t qk_max_n_in(int weight_type);
+
+/*
+ * qk_quantize_act - quantize float activations into int8 blocks, once per call.
+ *   act_type  QK_TYPE_Q8_0 or QK_TYPE_Q8_K (else QK_E_TYPE).
+ *   x         f32 [ncols][n], row-major, device.
+ *   xq        out: [ncols][n / block] blocks, ncols * qk_row_bytes(act_type, n) bytes.
+ *   n         elements per column, a positive multiple of the block size.
+ *   ncols     number of columns (tokens), >= 0; 0 enqueues nothing.
+ * Per block (codeloopback Example 2; candle BlockQ8_0::from_float): amax = largest
+ * |x| (NaN ignored); d = amax / 127 (correctly rounded f32); id = 1/d, or 0 when d
+ * is 0; code = roundf(x * id), halves away from zero, NaN -> 0, saturated to int8.
+ * Q8_0 stores d as f16 (round to nearest even, subnormals kept, overflow -> inf)
+ * then 32 codes (34 bytes).  Q8_K stores d as f32, 256 codes and 16 int16 bsums,
+ * each the sum of 16 consecutive codes (292 bytes; candle BlockQ8K).
+ * Results are bit-exact to that definition.
+ */
+int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
+                    void* stream);
+
+/*
+ * qk_gemv - y = W x for quantized W and already-quantized activations.
+ *   w_type    QK_TYPE_Q8_0, Q4_0, Q4_K or Q6_K (else QK_E_TYPE).
+ *   W         n_out rows of qk_row_bytes(w_type, n_in) bytes, contiguous, row-major
+ *             (sipllm matmul_quant layout), device.
+ *   n_out     output rows, >= 0.
+ *   n_in      elements per row, a positive multiple of the block size,
+ *             <= qk_max_n_in(w_type) (else QK_E_LIMIT).
+ *   xq        ncols activation rows from qk_quantize_act(qk_act_type(w_type), ...).
+ *   ncols     number of activation columns (tokens), >= 0.
+ *   y         out: f32 [ncols][n_out], device.
+ * For every (row, block): the exact int32 sums of code products (VecDot, rml
+ * "Quantized dot products"; Q4_K's min term taken from the activation bsums), then
+ * one f32 step with the block scales; y is the f32 sum of those steps.  The
+ * summation order differs from a sequential loop, so y matches a sequential f32
+ * evaluation to within rounding, not bit for bit.
+ */
+int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
+            int64_t ncols, float* y, void* stream);
+
+/*
+ * qk_dequantize_row - expand n elements (whole blocks) of a weight type to f32.
+ *   type      QK_TYPE_Q8_0, Q4_0, Q4_K or Q6_K (Q8_K is an activation-only format
+ *             and is refused with QK_E_TYPE, as sipllm's dequantize_row refuses it).
+ *   src       n / block blocks, device.  A whole matrix is n = n_out * n_in.
+ *   dst       out: f32 [n], device.
+ *   n         >= 0, a multiple of the block size; 0 enqueues nothing.
+ * Values (rml DequantizeRow; candle block table): Q8_0 d*q; Q4_0 d*(q-8); Q4_K
+ * d*sc_j*q - dmin*m_j; Q6_K d*sc_j*(q-32).  Each product is exact in f32, so the
+ * result is bit-exact.
+ */
+int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* stream);
+
+/*
+ * qk_gemv_block_sums - the same GEMV kernels, storing the per-block integers they
+ * compute instead of y.  For checking exactness; not needed to use the library.
+ *   sums      out: int32 [ncols][n_out][n_in / block][k]; k = 2 for Q4_K (the scale
+ *             sum S_q = sum_j sc_j s_j and the min sum S_m = sum_j m_j sum(a_j)),
+ *             k = 1 otherwise (Q8_0, Q4_0: the block's code-product sum; Q6_K:
+ *             S = sum_j sc_j sum (q - 32) a).
+ * Other arguments and errors as qk_gemv.
+ */
+int qk_gemv_block_sums(int w_type, const void* W, int64_t n_out, int64_t n_in,
+                       const void* xq, int64_t ncols, int32_t* sums, void* stream);
+
+/*
+ * qk_gemv_timed - qk_gemv whose kernel launches carry two hipEvent_t that record
+ * the start of the first and the end of the last GEMV kernel themselves (HIP's
+ * extended launch), for measuring kernel duration without enqueue gaps.  Either
+ * event may be NULL.  Arguments and errors otherwise as qk_gemv.
+ */
+int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
+                  int64_t ncols, float* y, void* stream, void* ev_start, void* ev_stop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,160 @@
+"""MI355X block-quantized GEMV (ggml Q8_0 / Q4_0 / Q4_K / Q6_K) - Python binding.
+
+A thin ctypes binding over libqk.so (C ABI in include/qk.h).  Functions carry
+the C names and only marshal arguments: torch tensors supply device pointers
+and the current stream; every step of the computation runs in the HIP kernels.
+There is no fallback: if libqk.so is missing or cannot be loaded, calls raise.
+"""
+import ctypes
+import os
+
+QK_TYPE_Q4_0 = 2
+QK_TYPE_Q8_0 = 8
+QK_TYPE_Q4_K = 12
+QK_TYPE_Q6_K = 14
+QK_TYPE_Q8_K = 15
+WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q4_K, QK_TYPE_Q6_K)
+TYPE_NAMES = {QK_TYPE_Q4_0: "Q4_0", QK_TYPE_Q8_0: "Q8_0", QK_TYPE_Q4_K: "Q4_K",
+              QK_TYPE_Q6_K: "Q6_K", QK_TYPE_Q8_K: "Q8_K"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqk.so")
+
+_lib = None
+
+
+class QKError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_str(status)})")
+
+
+def lib():
+    """Load libqk.so once.  torch is imported first so that the library binds to
+    the HIP runtime torch already mapped (they share the soname)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401  (HIP runtime must be torch's)
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "or python quantized_gemv_quantize_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        L.qk_block_elems.restype = i64
+        L.qk_block_elems.argtypes = [i32]
+        L.qk_block_bytes.restype = i64
+        L.qk_block_bytes.argtypes = [i32]
+        L.qk_row_bytes.restype = i64
+        L.qk_row_bytes.argtypes = [i32, i64]
+        L.qk_act_type.restype = i32
+        L.qk_act_type.argtypes = [i32]
+        L.qk_status_str.restype = ctypes.c_char_p
+        L.qk_status_str.argtypes = [i32]
+        L.qk_max_n_in.restype = i64
+        L.qk_max_n_in.argtypes = [i32]
+        L.qk_quantize_act.restype = i32
+        L.qk_quantize_act.argtypes = [i32, p, p, i64, i64, p]
+        L.qk_gemv.restype = i32
+        L.qk_gemv.argtypes = [i32, p, i64, i64, p, i64, p, p]
+        L.qk_gemv_timed.restype = i32
+        L.qk_gemv_timed.argtypes = [i32, p, i64, i64, p, i64, p, p, p, p]
+        L.qk_gemv_block_sums.restype = i32
+        L.qk_gemv_block_sums.argtypes = [i32, p, i64, i64, p, i64, p, p]
+        L.qk_dequantize_row.restype = i32
+        L.qk_dequantize_row.argtypes = [i32, p, p, i64, p]
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().qk_status_str(int(status)).decode()
+
+
+def qk_block_elems(t):
+    return int(lib().qk_block_elems(t))
+
+
+def qk_block_bytes(t):
+    return int(lib().qk_block_bytes(t))
+
+
+def qk_row_bytes(t, n):
+    return int(lib().qk_row_bytes(t, n))
+
+
+def qk_act_type(t):
+    return int(lib().qk_act_type(t))
+
+
+def qk_max_n_in(t):
+    return int(lib().qk_max_n_in(t))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise QKError(rc, what)
+
+
+def qk_quantize_act(act_type, x, xq=None, stream=None):
+    """Quantize x (f32 [ncols, n] or [n], device) into act blocks; returns xq
+    (uint8 [ncols, row_bytes])."""
+    import torch
+    n = x.shape[-1]
+    ncols = x.numel() // n if n else 0
+    if xq is None:
+        xq = torch.empty((ncols, max(qk_row_bytes(act_type, n), 0)), dtype=torch.uint8,
+                         device=x.device)
+    _check(lib().qk_quantize_act(act_type, _ptr(x), _ptr(xq), n, ncols, _stream(stream)),
+           "qk_quantize_act")
+    return xq
+
+
+def qk_gemv(w_type, W, n_out, n_in, xq, ncols=1, y=None, stream=None):
+    """y [ncols, n_out] f32 = W x for quantized W (device uint8) and act blocks xq."""
+    import torch
+    if y is None:
+        y = torch.empty((ncols, n_out), dtype=torch.float32, device=W.device)
+    _check(lib().qk_gemv(w_type, _ptr(W), n_out, n_in, _ptr(xq), ncols, _ptr(y),
+                         _stream(stream)), "qk_gemv")
+    return y
+
+
+def qk_gemv_timed(w_type, W, n_out, n_in, xq, ncols, y, ev_start, ev_stop, stream=None):
+    """qk_gemv with torch.cuda.Event(enable_timing=True) pair recorded by the
+    kernel launch itself (start of the first / end of the last GEMV kernel)."""
+    e0 = ctypes.c_void_p(ev_start.cuda_event) if ev_start is not None else None
+    e1 = ctypes.c_void_p(ev_stop.cuda_event) if ev_stop is not None else None
+    _check(lib().qk_gemv_timed(w_type, _ptr(W), n_out, n_in, _ptr(xq), ncols, _ptr(y),
+                               _stream(stream), e0, e1), "qk_gemv_timed")
+    return y
+
+
+def qk_gemv_block_sums(w_type, W, n_out, n_in, xq, ncols=1, sums=None, stream=None):
+    """Per-block int32 sums [ncols, n_out, n_in/block, k] of the GEMV kernels."""
+    import torch
+    k = 2 if w_type == QK_TYPE_Q4_K else 1
+    nb = n_in // qk_block_elems(w_type) if qk_block_elems(w_type) else 0
+    if sums is None:
+        sums = torch.empty((ncols, n_out, nb, k), dtype=torch.int32, device=W.device)
+    _check(lib().qk_gemv_block_sums(w_type, _ptr(W), n_out, n_in, _ptr(xq), ncols, _ptr(sums),
+                                    _stream(stream)), "qk_gemv_block_sums")
+    return sums
+
+
+def qk_dequantize_row(t, src, n, dst=None, stream=None):
+    """f32 [n] values of n elements (whole blocks) of type t."""
+    import torch
+    if dst is None:
+        dst = torch.empty((n,), dtype=torch.float32, device=src.device)
+    _check(lib().qk_dequantize_row(t, _ptr(src), _ptr(dst), n, _stream(stream)),
+           "qk_dequantize_row")
+    return dst

@@ -1,0 +1,171 @@
+// qk_capi.hip - the C ABI of libqk.so (declared in include/qk.h).
+//
+// Host-side validation of types, pairing, shapes, pointers and alignment, then
+// asynchronous launches on the caller's stream.  No allocation, no state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qk.h"
+#include "qk_internal.h"
+
+namespace {
+
+bool is_weight(int t) {
+  return t == QK_TYPE_Q4_0 || t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_K || t == QK_TYPE_Q6_K;
+}
+bool is_act(int t) { return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q8_K; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? QK_OK : QK_E_DEVICE; }
+
+// Common checks of a GEMV call; `out` is y or sums.
+int check_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
+               int64_t ncols, const void* out) {
+  if (!is_weight(w_type)) return QK_E_TYPE;
+  if (n_out < 0 || ncols < 0 || n_in <= 0 || n_in % qk_block_elems(w_type) != 0) return QK_E_SHAPE;
+  if (n_out > INT32_MAX) return QK_E_SHAPE;
+  if (n_in > qk_max_n_in(w_type)) return QK_E_LIMIT;
+  if (n_out == 0 || ncols == 0) return QK_OK;
+  if (W == nullptr || xq == nullptr || out == nullptr) return QK_E_NULL;
+  if (!aligned16(W) || !aligned16(xq) || !aligned16(out)) return QK_E_ALIGN;
+  return QK_OK;
+}
+
+int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
+              int64_t ncols, float* y, int32_t* sums, void* stream, void* ev0, void* ev1) {
+  const void* out = y ? static_cast<const void*>(y) : static_cast<const void*>(sums);
+  const int rc = check_gemv(w_type, W, n_out, n_in, xq, ncols, out);
+  if (rc != QK_OK || n_out == 0 || ncols == 0) return rc;
+  const int at = qk_act_type(w_type);
+  const int64_t xrow = qk_row_bytes(at, n_in);
+  const int64_t nb = n_in / qk_block_elems(w_type);
+  const int k = (w_type == QK_TYPE_Q4_K) ? 2 : 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t c = 0; c < ncols; ++c) {
+    const uint8_t* xc = static_cast<const uint8_t*>(xq) + c * xrow;
+    float* yc = y ? y + c * n_out : nullptr;
+    int32_t* sc = sums ? sums + c * n_out * nb * k : nullptr;
+    hipEvent_t e0 = (c == 0) ? static_cast<hipEvent_t>(ev0) : nullptr;
+    hipEvent_t e1 = (c == ncols - 1) ? static_cast<hipEvent_t>(ev1) : nullptr;
+    const hipError_t e = qk::launch_gemv(w_type, static_cast<const uint8_t*>(W), n_out, n_in, xc,
+                                         yc, sc, s, e0, e1);
+    if (e != hipSuccess) return QK_E_DEVICE;
+  }
+  return QK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t qk_block_elems(int type) {
+  switch (type) {
+    case QK_TYPE_Q4_0:
+    case QK_TYPE_Q8_0: return 32;
+    case QK_TYPE_Q4_K:
+    case QK_TYPE_Q6_K:
+    case QK_TYPE_Q8_K: return 256;
+    default: return 0;
+  }
+}
+
+int64_t qk_block_bytes(int type) {
+  switch (type) {
+    case QK_TYPE_Q4_0: return 18;
+    case QK_TYPE_Q8_0: return 34;
+    case QK_TYPE_Q4_K: return 144;
+    case QK_TYPE_Q6_K: return 210;
+    case QK_TYPE_Q8_K: return 292;
+    default: return 0;
+  }
+}
+
+int64_t qk_row_bytes(int type, int64_t n) {
+  const int64_t be = qk_block_elems(type);
+  if (be == 0 || n < 0 || n % be != 0) return 0;
+  return n / be * qk_block_bytes(type);
+}
+
+int qk_act_type(int weight_type) {
+  switch (weight_type) {
+    case QK_TYPE_Q4_0:
+    case QK_TYPE_Q8_0: return QK_TYPE_Q8_0;
+    case QK_TYPE_Q4_K:
+    case QK_TYPE_Q6_K: return QK_TYPE_Q8_K;
+    default: return -1;
+  }
+}
+
+const char* qk_status_str(int status) {
+  switch (status) {
+    case QK_OK: return "ok";
+    case QK_E_TYPE: return "unknown type, or activation type used as a weight";
+    case QK_E_SHAPE: return "shape is not whole blocks, or a count is negative";
+    case QK_E_ALIGN: return "a base pointer is not 16-byte aligned";
+    case QK_E_NULL: return "a required pointer is NULL";
+    case QK_E_DEVICE: return "HIP runtime error while enqueueing";
+    case QK_E_LIMIT: return "activation row exceeds the GEMV LDS budget";
+    default: return "unknown status";
+  }
+}
+
+int64_t qk_max_n_in(int weight_type) {
+  if (!is_weight(weight_type)) return 0;
+  const int64_t be = qk_block_elems(weight_type);
+  int64_t best = 0;
+  // largest whole-block n_in whose LDS layout fits (monotone in n_in)
+  int64_t lo = 1, hi = (int64_t(1) << 20) / be;
+  while (lo <= hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (qk::gemv_lds_bytes(weight_type, mid * be) <= qk::kMaxLdsBytes) {
+      best = mid * be;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return best;
+}
+
+int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
+                    void* stream) {
+  if (!is_act(act_type)) return QK_E_TYPE;
+  const int64_t be = qk_block_elems(act_type);
+  if (n <= 0 || n % be != 0 || ncols < 0) return QK_E_SHAPE;
+  if (ncols == 0) return QK_OK;
+  if (x == nullptr || xq == nullptr) return QK_E_NULL;
+  if (!aligned16(x) || !aligned16(xq)) return QK_E_ALIGN;
+  const int64_t nblocks = n / be * ncols;
+  return status_of(qk::launch_quantize(act_type, x, static_cast<uint8_t*>(xq), nblocks,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
+            int64_t ncols, float* y, void* stream) {
+  return gemv_impl(w_type, W, n_out, n_in, xq, ncols, y, nullptr, stream, nullptr, nullptr);
+}
+
+int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
+                  int64_t ncols, float* y, void* stream, void* ev_start, void* ev_stop) {
+  return gemv_impl(w_type, W, n_out, n_in, xq, ncols, y, nullptr, stream, ev_start, ev_stop);
+}
+
+int qk_gemv_block_sums(int w_type, const void* W, int64_t n_out, int64_t n_in,
+                       const void* xq, int64_t ncols, int32_t* sums, void* stream) {
+  if (sums == nullptr && is_weight(w_type) && n_out > 0 && ncols > 0) return QK_E_NULL;
+  return gemv_impl(w_type, W, n_out, n_in, xq, ncols, nullptr, sums, stream, nullptr, nullptr);
+}
+
+int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* stream) {
+  if (!is_weight(type)) return QK_E_TYPE;
+  const int64_t be = qk_block_elems(type);
+  if (n < 0 || n % be != 0) return QK_E_SHAPE;
+  if (n == 0) return QK_OK;
+  if (src == nullptr || dst == nullptr) return QK_E_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return QK_E_ALIGN;
+  return status_of(qk::launch_dequantize(type, static_cast<const uint8_t*>(src), dst, n / be,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

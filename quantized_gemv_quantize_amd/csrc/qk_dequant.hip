@@ -1,0 +1,155 @@
+// qk_dequant.hip - DequantizeRow kernels (block -> f32) for gfx950.
+//
+// Values (rml "Dequantization"; candle formats page, block table; codeloopback
+// Example 6 for Q4_0's nibble order):
+//   Q8_0  d * q
+//   Q4_0  d * (q - 8); byte j: element j in the low nibble, element j+16 in the high
+//   Q4_K  d * sc_j * q - dmin * m_j for 32-element sub-block j (scales per
+//         get_scale_min_k4, rml element-200 trace)
+//   Q6_K  d * sc_j * (q - 32) for 16-element sub-block j; q = 4 bits from ql and
+//         2 bits from qh in the GGUF arrangement (the pages give only the roles)
+// Each product is exact in f32 (at most 23 significant bits), so the order of
+// multiplication and any FMA contraction leave the result unchanged.
+//
+// Each lane produces 4 consecutive floats and stores them as one float4, so a
+// wavefront writes contiguous spans (the f32 output is 4-7x the bytes read).
+#include "qk_device.h"
+#include "qk_internal.h"
+
+namespace qk {
+namespace {
+
+constexpr uint32_t kLo4 = 0x0F0F0F0Fu;
+
+__device__ __forceinline__ float4 scale_bytes_signed(uint32_t q, float scale, int offset) {
+  return make_float4(scale * static_cast<float>(static_cast<int>(q & 0xFF) - offset),
+                     scale * static_cast<float>(static_cast<int>((q >> 8) & 0xFF) - offset),
+                     scale * static_cast<float>(static_cast<int>((q >> 16) & 0xFF) - offset),
+                     scale * static_cast<float>(static_cast<int>(q >> 24) - offset));
+}
+
+// Q8_0: 8 lanes per block.
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __restrict__ src,
+                                                           float* __restrict__ dst,
+                                                           int64_t nblocks) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t b = t >> 3;
+  if (b >= nblocks) return;
+  const int part = threadIdx.x & 7;
+  const uint8_t* blk = src + b * kQ8_0Bytes;
+  const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+  const uint32_t q = load_u2<uint32_t>(blk + 2 + 4 * part);
+  float4 o;
+  o.x = d * static_cast<float>(static_cast<int8_t>(q & 0xFF));
+  o.y = d * static_cast<float>(static_cast<int8_t>((q >> 8) & 0xFF));
+  o.z = d * static_cast<float>(static_cast<int8_t>((q >> 16) & 0xFF));
+  o.w = d * static_cast<float>(static_cast<int8_t>(q >> 24));
+  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = o;
+}
+
+// Q4_0: 8 lanes per block; lanes 0-3 take low nibbles (elements 0-15), lanes 4-7
+// the high nibbles (elements 16-31) of the same 16 bytes.
+__global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* __restrict__ src,
+                                                           float* __restrict__ dst,
+                                                           int64_t nblocks) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t b = t >> 3;
+  if (b >= nblocks) return;
+  const int part = threadIdx.x & 7;
+  const uint8_t* blk = src + b * kQ4_0Bytes;
+  const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+  const uint32_t w = load_u2<uint32_t>(blk + 2 + 4 * (part & 3));
+  const uint32_t q = (part < 4) ? (w & kLo4) : ((w >> 4) & kLo4);
+  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(q, d, 8);
+}
+
+// Q4_K: one wavefront per superblock, lane l -> elements 4l..4l+3.
+__global__ __launch_bounds__(256) void dequant_q4_K_kernel(const uint8_t* __restrict__ src,
+                                                           float* __restrict__ dst,
+                                                           int64_t nblocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (b >= nblocks) return;
+  const uint8_t* blk = src + b * kQ4_KBytes;
+  const uint4 h = *reinterpret_cast<const uint4*>(blk);  // d, dmin, scales[12]
+  const float d = f16_to_f32(h.x & 0xFFFF);
+  const float dmin = f16_to_f32(h.x >> 16);
+  const int e0 = 4 * lane;
+  const int j = e0 >> 5;   // sub-block
+  const int c = e0 >> 6;   // 64-element chunk
+  const int p = e0 & 63;   // position in the chunk
+  // get_scale_min_k4: sub-blocks 0-3 use the low 6 bits of bytes j and j+4; 4-7
+  // take the low / high nibble of byte j+4 and the top 2 bits of bytes j-4 / j.
+  const uint32_t s0 = h.y, s1 = h.z, s2 = h.w;
+  const uint32_t scw = (j < 4) ? (s0 & 0x3F3F3F3Fu) : ((s2 & kLo4) | ((s0 >> 2) & 0x30303030u));
+  const uint32_t mw = (j < 4) ? (s1 & 0x3F3F3F3Fu) : (((s2 >> 4) & kLo4) | ((s1 >> 2) & 0x30303030u));
+  const int sh = 8 * (j & 3);
+  const float sc = static_cast<float>((scw >> sh) & 0xFF);
+  const float mn = static_cast<float>((mw >> sh) & 0xFF);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * c + (p & 31));
+  const uint32_t q = (p < 32) ? (w & kLo4) : ((w >> 4) & kLo4);
+  const float dsc = d * sc;
+  const float dm = dmin * mn;
+  float4 o;
+  o.x = dsc * static_cast<float>(q & 0xFF) - dm;
+  o.y = dsc * static_cast<float>((q >> 8) & 0xFF) - dm;
+  o.z = dsc * static_cast<float>((q >> 16) & 0xFF) - dm;
+  o.w = dsc * static_cast<float>(q >> 24) - dm;
+  *reinterpret_cast<float4*>(dst + b * 256 + e0) = o;
+}
+
+// Q6_K: one wavefront per superblock, lane l -> elements 4l..4l+3.
+// Element e: half h = e/128, r = e%128, group g = r/32, l = r%32; low 4 bits are
+// nibble (g < 2 ? low : high) of ql[64h + l + 32(g&1)], high 2 bits are
+// (qh[32h + l] >> 2g) & 3.
+__global__ __launch_bounds__(256) void dequant_q6_K_kernel(const uint8_t* __restrict__ src,
+                                                           float* __restrict__ dst,
+                                                           int64_t nblocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (b >= nblocks) return;
+  const uint8_t* blk = src + b * kQ6_KBytes;
+  const int e0 = 4 * lane;
+  const int h = e0 >> 7, r = e0 & 127, g = r >> 5, l = r & 31;
+  const uint32_t wl = load_u2<uint32_t>(blk + 64 * h + l + 32 * (g & 1));
+  const uint32_t wh = load_u2<uint32_t>(blk + 128 + 32 * h + l);
+  const uint32_t lo = (g < 2) ? (wl & kLo4) : ((wl >> 4) & kLo4);
+  const uint32_t q = lo | (((wh >> (2 * g)) & 0x03030303u) << 4);
+  const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk + 208));
+  const float sc = static_cast<float>(static_cast<int8_t>(blk[192 + (e0 >> 4)]));
+  *reinterpret_cast<float4*>(dst + b * 256 + e0) = scale_bytes_signed(q, d * sc, 32);
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t nblocks,
+                             hipStream_t s) {
+  if (nblocks <= 0) return hipSuccess;
+  switch (type) {
+    case kQ8_0: {
+      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
+      dequant_q8_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
+      break;
+    }
+    case kQ4_0: {
+      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
+      dequant_q4_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
+      break;
+    }
+    case kQ4_K: {
+      const unsigned grid = static_cast<unsigned>((nblocks + 3) / 4);
+      dequant_q4_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
+      break;
+    }
+    case kQ6_K: {
+      const unsigned grid = static_cast<unsigned>((nblocks + 3) / 4);
+      dequant_q6_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qk

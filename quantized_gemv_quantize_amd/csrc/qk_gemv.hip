@@ -1,0 +1,634 @@
+// qk_gemv.hip - batch-1 GEMV kernels y = W x for gfx950, one per weight format.
+//
+// Method (rml "Quantized dot products" and "Kernels and references"; codeloopback
+// Examples 10 and 11; candle formats page, VecDotType and BlockQ8K): x has been
+// quantized once into int8 blocks aligned with W's blocks; for each (row, block)
+// the products of codes are summed exactly in int32 (v_dot4 over packed bytes),
+// the K-quant sub-block scales are applied as int32 multiply-adds, and only the
+// block step uses floats:
+//   Q8_0, Q4_0  c = s * (d_w * d_x)
+//   Q4_K        c = (d_x * d) * S_q - (d_x * dmin) * S_m,
+//               S_q = sum_j sc_j s_j, S_m = sum_j m_j (bsum_2j + bsum_2j+1)
+//   Q6_K        c = (d_x * d) * S,  S = sum_j sc_j sum_e (q_e - 32) a_e
+// y[row] is the f32 sum of c over the row's blocks.
+//
+// Mapping on the GPU (all kernels):
+//  - one wavefront per output row; its lanes cover a span of consecutive blocks
+//    (Q4_K, Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
+//    Q8_0, Q4_0: 1 lane per 32-element block, 64 blocks per pass);
+//  - every lane issues the global loads of up to UNR passes of its row before the
+//    workgroup stages the paired activation row into LDS, so the HBM stream is in
+//    flight while the activations are copied;
+//  - activations sit in LDS in a per-format layout (padded / permuted so the 16-byte
+//    reads of the lanes of a pass fall in different banks) with the scales already
+//    converted to f32 and the bsums regrouped;
+//  - lanes of one superblock combine their int32 partial sums with DPP (exact),
+//    then one lane applies the float step; the row total is a wavefront sum.
+#include <hip/hip_ext.h>
+
+#include "qk_device.h"
+#include "qk_internal.h"
+
+namespace qk {
+namespace {
+
+constexpr uint32_t kLo4 = 0x0F0F0F0Fu;
+constexpr uint32_t kHi2 = 0x30303030u;
+constexpr uint32_t kOnes = 0x01010101u;
+
+constexpr int kWaves = 4;  // wavefronts (rows) per workgroup
+constexpr int kThreads = kWaves * 64;
+
+__host__ __device__ constexpr int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
+
+// ---------------------------------------------------------------------------
+// LDS activation layouts.
+//
+// Q8_K for Q4_K weights: per superblock 272 bytes of codes; the 16-byte piece i
+// (elements 16i..16i+15) of 64-element chunk c is stored at 64c + 16 (i ^ 2*(c>>1)).
+// A pass reads, at step i, piece i of chunk c = lane & 3 of superblock lane >> 2:
+// the stride 272 (17 pieces) and the XOR put the 8 lanes of a 128-byte bank sweep
+// on 8 different pieces.  Then d (f32) per superblock, then the 8 sums of 32 codes
+// (bsum_2j + bsum_2j+1) per superblock.
+struct LayoutQ4K {
+  static constexpr int kStride = 272;
+  int64_t off_d, off_s, bytes;
+  __host__ __device__ explicit LayoutQ4K(int64_t nb) {
+    off_d = nb * kStride;
+    off_s = align16(off_d + 4 * nb);
+    bytes = off_s + 32 * nb;
+  }
+};
+
+// Q8_K for Q6_K weights: piece P = e/16 = 8h + 2g + k (half h, group g, lane k) is
+// stored at slot 8h + ((2g + k) ^ 4h) of a 288-byte superblock; lane (h, k) reads
+// piece 8h + 2g + k at step g.  Then d (f32), then 32 * bsum_t as int32 stored at
+// index 8h + 4k + g so a lane's four values are one 16-byte read.
+struct LayoutQ6K {
+  static constexpr int kStride = 288;
+  int64_t off_d, off_s, bytes;
+  __host__ __device__ explicit LayoutQ6K(int64_t nb) {
+    off_d = nb * kStride;
+    off_s = align16(off_d + 4 * nb);
+    bytes = off_s + 64 * nb;
+  }
+};
+
+// Q8_0 for Q8_0 and Q4_0 weights: 32 codes per block at a 48-byte stride (lanes of
+// a pass read consecutive blocks), then d (f32) per block.
+struct LayoutQ80 {
+  static constexpr int kStride = 48;
+  int64_t off_d, bytes;
+  __host__ __device__ explicit LayoutQ80(int64_t nb) {
+    off_d = nb * kStride;
+    bytes = align16(off_d + 4 * nb);
+  }
+};
+
+// Staging of one activation row into LDS.
+//
+// The row is split into 16-byte pieces of codes (one dwordx4 load and one
+// ds_write_b128 each) and small units (the block scale and the bsums).  Staging
+// runs in two phases so that its global loads are issued before the weight loads:
+// `load` fills registers, `place` writes LDS after the weight loads are in
+// flight; because the load counter retires in order, `place` then waits for the
+// older activation loads only.  Every index is clamped to the last unit, so all
+// lanes issue the same loads without branches (a clamped lane rewrites the value
+// the last unit already holds).  Units beyond kPieces / kSmall per thread (rows
+// longer than 16 K elements) are copied by a plain loop afterwards.
+constexpr int kPieces = 4;
+constexpr int kSmall = 2;
+
+struct StagedQ8K {
+  uint4 piece[kPieces];
+  uint32_t small[kSmall];
+};
+struct StagedQ80 {
+  uint4 piece[kPieces];
+  uint16_t small[kSmall];
+};
+
+// Q8_K block i (292 bytes): piece p (p < 16) = codes 16p..16p+15 at 4 + 16p;
+// small unit r (r < 9) = dword r of {d, bsum pairs 0-7} at 0 and 260 + 4(r-1).
+__device__ __forceinline__ const uint8_t* q8K_piece_src(const uint8_t* xq, int u) {
+  return xq + (u >> 4) * kQ8_KBytes + 4 + 16 * (u & 15);
+}
+__device__ __forceinline__ const uint8_t* q8K_small_src(const uint8_t* xq, int u) {
+  const int i = u / 9, r = u - 9 * i;
+  return xq + i * kQ8_KBytes + (r == 0 ? 0 : 256 + 4 * r);
+}
+
+__device__ __forceinline__ void stage_load_q8K(StagedQ8K& st, const uint8_t* __restrict__ xq, int nb) {
+  const int np = nb * 16, ns = nb * 9;
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1);
+    st.piece[i] = load_u2<uint4>(q8K_piece_src(xq, u));
+  }
+#pragma unroll
+  for (int i = 0; i < kSmall; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, ns - 1);
+    st.small[i] = *reinterpret_cast<const uint32_t*>(q8K_small_src(xq, u));
+  }
+}
+
+__device__ __forceinline__ int sext16_lo(uint32_t v) { return static_cast<int16_t>(v & 0xFFFF); }
+__device__ __forceinline__ int sext16_hi(uint32_t v) { return static_cast<int16_t>(v >> 16); }
+
+// Q4_K layout: piece p of block i -> 272 i + 64 c + 16 (pi ^ 2 (c >> 1)), c = p / 4,
+// pi = p % 4; d -> off_d + 4 i; bsum pair j -> off_s + 32 i + 4 j as one int32 sum.
+__device__ __forceinline__ void place_piece_q4K(uint8_t* lds, int u, const uint4& v) {
+  const int i = u >> 4, p = u & 15, c = p >> 2, pi = p & 3;
+  *reinterpret_cast<uint4*>(lds + i * LayoutQ4K::kStride + 64 * c + 16 * (pi ^ ((c >> 1) << 1))) = v;
+}
+__device__ __forceinline__ void place_small_q4K(uint8_t* lds, const LayoutQ4K& L, int u, uint32_t v) {
+  const int i = u / 9, r = u - 9 * i;
+  const int addr = (r == 0) ? static_cast<int>(L.off_d) + 4 * i : static_cast<int>(L.off_s) + 32 * i + 4 * (r - 1);
+  const uint32_t val = (r == 0) ? v : static_cast<uint32_t>(sext16_lo(v) + sext16_hi(v));
+  *reinterpret_cast<uint32_t*>(lds + addr) = val;
+}
+
+// Q6_K layout: piece P of block i -> 288 i + 16 (8h + ((P & 7) ^ 4h)), h = P / 8;
+// d -> off_d + 4 i; bsum t -> off_s + 64 i + 4 (8h + 4k + g) as 32 * bsum, where
+// t = 8h + 2g + k.  Small unit r >= 1 holds bsums t = 2(r-1) (k = 0) and 2(r-1)+1.
+__device__ __forceinline__ void place_piece_q6K(uint8_t* lds, int u, const uint4& v) {
+  const int i = u >> 4, P = u & 15, h = P >> 3;
+  *reinterpret_cast<uint4*>(lds + i * LayoutQ6K::kStride + 16 * (8 * h + ((P & 7) ^ (4 * h)))) = v;
+}
+__device__ __forceinline__ void place_small_q6K(uint8_t* lds, const LayoutQ6K& L, int u, uint32_t v) {
+  const int i = u / 9, r = u - 9 * i;
+  const int j = max(r - 1, 0), h = j >> 2, g = j & 3;
+  const int base = static_cast<int>(L.off_s) + 64 * i + 4 * (8 * h + g);
+  const int a0 = (r == 0) ? static_cast<int>(L.off_d) + 4 * i : base;
+  const uint32_t v0 = (r == 0) ? v : static_cast<uint32_t>(32 * sext16_lo(v));
+  *reinterpret_cast<uint32_t*>(lds + a0) = v0;
+  // second bsum of the pair (k = 1); the d unit rewrites its own value instead
+  const int a1 = (r == 0) ? a0 : base + 16;
+  const uint32_t v1 = (r == 0) ? v : static_cast<uint32_t>(32 * sext16_hi(v));
+  *reinterpret_cast<uint32_t*>(lds + a1) = v1;
+}
+
+template <typename LayoutT, typename PieceF, typename SmallF>
+__device__ __forceinline__ void stage_place_q8K(uint8_t* lds, const LayoutT& L, const StagedQ8K& st,
+                                                const uint8_t* __restrict__ xq, int nb, PieceF piece,
+                                                SmallF small) {
+  const int np = nb * 16, ns = nb * 9;
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    piece(lds, min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1), st.piece[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < kSmall; ++i) {
+    small(lds, L, min(static_cast<int>(threadIdx.x) + i * kThreads, ns - 1), st.small[i]);
+  }
+  for (int u = static_cast<int>(threadIdx.x) + kPieces * kThreads; u < np; u += kThreads) {
+    piece(lds, u, load_u2<uint4>(q8K_piece_src(xq, u)));
+  }
+  for (int u = static_cast<int>(threadIdx.x) + kSmall * kThreads; u < ns; u += kThreads) {
+    small(lds, L, u, *reinterpret_cast<const uint32_t*>(q8K_small_src(xq, u)));
+  }
+}
+
+// Q8_0 block i (34 bytes): pieces 0, 1 = codes at 2 and 18; small unit = f16 d at 0.
+// LDS: piece p -> 48 i + 16 p; d -> off_d + 4 i as f32.
+__device__ __forceinline__ void stage_load_q80(StagedQ80& st, const uint8_t* __restrict__ xq, int nb) {
+  const int np = nb * 2;
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1);
+    st.piece[i] = load_u2<uint4>(xq + (u >> 1) * kQ8_0Bytes + 2 + 16 * (u & 1));
+  }
+#pragma unroll
+  for (int i = 0; i < kSmall; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, nb - 1);
+    st.small[i] = *reinterpret_cast<const uint16_t*>(xq + u * kQ8_0Bytes);
+  }
+}
+
+__device__ __forceinline__ void stage_place_q80(uint8_t* lds, const LayoutQ80& L, const StagedQ80& st,
+                                                const uint8_t* __restrict__ xq, int nb) {
+  const int np = nb * 2;
+  float* dA = reinterpret_cast<float*>(lds + L.off_d);
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1);
+    *reinterpret_cast<uint4*>(lds + (u >> 1) * LayoutQ80::kStride + 16 * (u & 1)) = st.piece[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kSmall; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, nb - 1);
+    dA[u] = f16_to_f32(st.small[i]);
+  }
+  for (int u = static_cast<int>(threadIdx.x) + kPieces * kThreads; u < np; u += kThreads) {
+    *reinterpret_cast<uint4*>(lds + (u >> 1) * LayoutQ80::kStride + 16 * (u & 1)) =
+        load_u2<uint4>(xq + (u >> 1) * kQ8_0Bytes + 2 + 16 * (u & 1));
+  }
+  for (int u = static_cast<int>(threadIdx.x) + kSmall * kThreads; u < nb; u += kThreads) {
+    dA[u] = f16_to_f32(*reinterpret_cast<const uint16_t*>(xq + u * kQ8_0Bytes));
+  }
+}
+
+// Keeps the backend scheduler from interleaving the activation and weight loads.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// ---------------------------------------------------------------------------
+// Q4_K x Q8_K.  Lane (u = lane >> 2, c = lane & 3) of pass `it` handles 64-element
+// chunk c of superblock it*16 + u: qs[32c .. 32c+31] hold sub-block 2c in their low
+// nibbles and sub-block 2c+1 in their high nibbles.
+template <int UNR, bool SUMS>
+__global__ __launch_bounds__(kWaves * 64) void gemv_q4_K_kernel(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int c = lane & 3, u = lane >> 2;
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 15) >> 4;
+
+  uint4 H[UNR], Q0[UNR], Q1[UNR];
+  // Unconditional loads (superblock index clamped): the same number of loads in
+  // every lane lets the compiler wait for pass j's data only.
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = min((p0 + j) * 16 + u, nb - 1);
+      const uint8_t* p = wrow + static_cast<size_t>(sb) * kQ4_KBytes;
+      H[j] = *reinterpret_cast<const uint4*>(p);
+      Q0[j] = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
+      Q1[j] = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
+    }
+  };
+  const LayoutQ4K L(nb);
+  StagedQ8K st;
+  stage_load_q8K(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  stage_place_q8K(lds, L, st, xq, nb, place_piece_q4K, place_small_q4K);
+  __syncthreads();
+
+  const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
+  const int32_t* sA = reinterpret_cast<const int32_t*>(lds + L.off_s);
+  const int sw = (c >> 1) << 1;  // piece XOR of chunk c
+  const int sh = (c & 1) * 16;   // byte pair of this chunk's two sub-blocks
+  float acc = 0.0f;
+
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = (p0 + j) * 16 + u;
+      if (!row_ok || sb >= nb) continue;  // uniform over the 4 lanes of a superblock
+      const uint8_t* ap = lds + sb * LayoutQ4K::kStride + 64 * c;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(ap + 16 * (0 ^ sw));
+      const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16 * (1 ^ sw));
+      const uint4 a2 = *reinterpret_cast<const uint4*>(ap + 16 * (2 ^ sw));
+      const uint4 a3 = *reinterpret_cast<const uint4*>(ap + 16 * (3 ^ sw));
+      const int2 asum = *reinterpret_cast<const int2*>(sA + sb * 8 + 2 * c);
+      const float dx = dA[sb];
+      const uint4 q0 = Q0[j], q1 = Q1[j], h = H[j];
+
+      int slo = 0, shi = 0;
+      slo = dot4(q0.x & kLo4, a0.x, slo);
+      slo = dot4(q0.y & kLo4, a0.y, slo);
+      slo = dot4(q0.z & kLo4, a0.z, slo);
+      slo = dot4(q0.w & kLo4, a0.w, slo);
+      slo = dot4(q1.x & kLo4, a1.x, slo);
+      slo = dot4(q1.y & kLo4, a1.y, slo);
+      slo = dot4(q1.z & kLo4, a1.z, slo);
+      slo = dot4(q1.w & kLo4, a1.w, slo);
+      shi = dot4((q0.x >> 4) & kLo4, a2.x, shi);
+      shi = dot4((q0.y >> 4) & kLo4, a2.y, shi);
+      shi = dot4((q0.z >> 4) & kLo4, a2.z, shi);
+      shi = dot4((q0.w >> 4) & kLo4, a2.w, shi);
+      shi = dot4((q1.x >> 4) & kLo4, a3.x, shi);
+      shi = dot4((q1.y >> 4) & kLo4, a3.y, shi);
+      shi = dot4((q1.z >> 4) & kLo4, a3.z, shi);
+      shi = dot4((q1.w >> 4) & kLo4, a3.w, shi);
+
+      // get_scale_min_k4 for sub-blocks 2c and 2c+1, all four bytes of a group at once:
+      // sub-blocks 0-3: low 6 bits of bytes 0-3 (scale) and 4-7 (min); 4-7: low / high
+      // nibble of bytes 8-11 plus the top 2 bits of bytes 0-3 / 4-7.
+      const uint32_t scw = (c & 2) ? ((h.w & kLo4) | ((h.y >> 2) & kHi2)) : (h.y & 0x3F3F3F3Fu);
+      const uint32_t mw = (c & 2) ? (((h.w >> 4) & kLo4) | ((h.z >> 2) & kHi2)) : (h.z & 0x3F3F3F3Fu);
+      const int sc_lo = (scw >> sh) & 0xFF, sc_hi = (scw >> (sh + 8)) & 0xFF;
+      const int m_lo = (mw >> sh) & 0xFF, m_hi = (mw >> (sh + 8)) & 0xFF;
+
+      const int sq = quad_sum(sc_lo * slo + sc_hi * shi);
+      const int sm = quad_sum(m_lo * asum.x + m_hi * asum.y);
+      if (c == 0) {
+        const float d = f16_to_f32(h.x & 0xFFFF);
+        const float dmin = f16_to_f32(h.x >> 16);
+        acc += (dx * d) * static_cast<float>(sq) - (dx * dmin) * static_cast<float>(sm);
+        if constexpr (SUMS) {
+          int32_t* o = sums + (static_cast<size_t>(row) * nb + sb) * 2;
+          o[0] = sq;
+          o[1] = sm;
+        }
+      }
+    }
+  }
+  if (row_ok) {
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q6_K x Q8_K.  Lane (u = lane >> 2, p = lane & 3 -> half h = p >> 1, k = p & 1) of
+// pass `it` handles, in superblock it*16 + u, positions l in [16k, 16k+16) of half
+// h for all four groups g: elements 128h + 32g + l, sub-blocks 8h + 2g + k.
+template <int UNR, bool SUMS>
+__global__ __launch_bounds__(kWaves * 64) void gemv_q6_K_kernel(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int pos = lane & 3, u = lane >> 2;
+  const int hh = pos >> 1, kk = pos & 1;
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kQ6_KBytes;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 15) >> 4;
+
+  uint4 A[UNR], B[UNR], QH[UNR];
+  uint2 SC[UNR];
+  uint32_t D[UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = min((p0 + j) * 16 + u, nb - 1);
+      const uint8_t* p = wrow + static_cast<size_t>(sb) * kQ6_KBytes;
+      A[j] = load_u2<uint4>(p + 64 * hh + 16 * kk);
+      B[j] = load_u2<uint4>(p + 64 * hh + 32 + 16 * kk);
+      QH[j] = load_u2<uint4>(p + 128 + 32 * hh + 16 * kk);
+      SC[j] = load_u2<uint2>(p + 192 + 8 * hh);
+      D[j] = *reinterpret_cast<const uint16_t*>(p + 208);
+    }
+  };
+  const LayoutQ6K L(nb);
+  StagedQ8K st;
+  stage_load_q8K(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  stage_place_q8K(lds, L, st, xq, nb, place_piece_q6K, place_small_q6K);
+  __syncthreads();
+
+  const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
+  const int32_t* sA = reinterpret_cast<const int32_t*>(lds + L.off_s);
+  float acc = 0.0f;
+
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = (p0 + j) * 16 + u;
+      if (!row_ok || sb >= nb) continue;
+      const uint8_t* ap = lds + sb * LayoutQ6K::kStride + 128 * hh;
+      uint4 a[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        a[g] = *reinterpret_cast<const uint4*>(ap + 16 * ((2 * g + kk) ^ (4 * hh)));
+      }
+      const int4 bs = *reinterpret_cast<const int4*>(sA + sb * 16 + 8 * hh + 4 * kk);
+      const float dx = dA[sb];
+      const uint32_t al[4] = {A[j].x, A[j].y, A[j].z, A[j].w};
+      const uint32_t bl[4] = {B[j].x, B[j].y, B[j].z, B[j].w};
+      const uint32_t hl[4] = {QH[j].x, QH[j].y, QH[j].z, QH[j].w};
+      const uint32_t a0[4] = {a[0].x, a[0].y, a[0].z, a[0].w};
+      const uint32_t a1[4] = {a[1].x, a[1].y, a[1].z, a[1].w};
+      const uint32_t a2[4] = {a[2].x, a[2].y, a[2].z, a[2].w};
+      const uint32_t a3[4] = {a[3].x, a[3].y, a[3].z, a[3].w};
+      int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t q0 = (al[i] & kLo4) | ((hl[i] << 4) & kHi2);
+        const uint32_t q1 = (bl[i] & kLo4) | ((hl[i] << 2) & kHi2);
+        const uint32_t q2 = ((al[i] >> 4) & kLo4) | (hl[i] & kHi2);
+        const uint32_t q3 = ((bl[i] >> 4) & kLo4) | ((hl[i] >> 2) & kHi2);
+        s0 = dot4(q0, a0[i], s0);
+        s1 = dot4(q1, a1[i], s1);
+        s2 = dot4(q2, a2[i], s2);
+        s3 = dot4(q3, a3[i], s3);
+      }
+      // sub-block scales sc[8h + 2g + k] = byte (2g + k) of the 8 bytes at 192 + 8h
+      const int sc0 = static_cast<int8_t>((SC[j].x >> (8 * kk)) & 0xFF);
+      const int sc1 = static_cast<int8_t>((SC[j].x >> (16 + 8 * kk)) & 0xFF);
+      const int sc2 = static_cast<int8_t>((SC[j].y >> (8 * kk)) & 0xFF);
+      const int sc3 = static_cast<int8_t>((SC[j].y >> (16 + 8 * kk)) & 0xFF);
+      // q is stored as 0..63; sum (q - 32) a = sum q a - 32 * bsum
+      const int part = sc0 * (s0 - bs.x) + sc1 * (s1 - bs.y) + sc2 * (s2 - bs.z) + sc3 * (s3 - bs.w);
+      const int S = quad_sum(part);
+      if (pos == 0) {
+        const float d = f16_to_f32(D[j]);
+        acc += (dx * d) * static_cast<float>(S);
+        if constexpr (SUMS) sums[static_cast<size_t>(row) * nb + sb] = S;
+      }
+    }
+  }
+  if (row_ok) {
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0 x Q8_0 and Q4_0 x Q8_0: lane b of pass `it` handles block it*64 + lane.
+template <int UNR, bool SUMS>
+__global__ __launch_bounds__(kWaves * 64) void gemv_q8_0_kernel(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kQ8_0Bytes;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 63) >> 6;
+
+  uint4 Q0[UNR], Q1[UNR];
+  uint32_t D[UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = min((p0 + j) * 64 + lane, nb - 1);
+      const uint8_t* p = wrow + static_cast<size_t>(b) * kQ8_0Bytes;
+      D[j] = *reinterpret_cast<const uint16_t*>(p);
+      Q0[j] = load_u2<uint4>(p + 2);
+      Q1[j] = load_u2<uint4>(p + 18);
+    }
+  };
+  const LayoutQ80 L(nb);
+  StagedQ80 st;
+  stage_load_q80(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  stage_place_q80(lds, L, st, xq, nb);
+  __syncthreads();
+
+  const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
+  float acc = 0.0f;
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = (p0 + j) * 64 + lane;
+      if (!row_ok || b >= nb) continue;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ80::kStride);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ80::kStride + 16);
+      int s = 0;
+      s = dot4(Q0[j].x, a0.x, s);
+      s = dot4(Q0[j].y, a0.y, s);
+      s = dot4(Q0[j].z, a0.z, s);
+      s = dot4(Q0[j].w, a0.w, s);
+      s = dot4(Q1[j].x, a1.x, s);
+      s = dot4(Q1[j].y, a1.y, s);
+      s = dot4(Q1[j].z, a1.z, s);
+      s = dot4(Q1[j].w, a1.w, s);
+      acc += static_cast<float>(s) * (f16_to_f32(D[j]) * dA[b]);
+      if constexpr (SUMS) sums[static_cast<size_t>(row) * nb + b] = s;
+    }
+  }
+  if (row_ok) {
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+template <int UNR, bool SUMS>
+__global__ __launch_bounds__(kWaves * 64) void gemv_q4_0_kernel(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kQ4_0Bytes;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 63) >> 6;
+
+  uint4 Q[UNR];
+  uint32_t D[UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = min((p0 + j) * 64 + lane, nb - 1);
+      const uint8_t* p = wrow + static_cast<size_t>(b) * kQ4_0Bytes;
+      D[j] = *reinterpret_cast<const uint16_t*>(p);
+      Q[j] = load_u2<uint4>(p + 2);
+    }
+  };
+  const LayoutQ80 L(nb);
+  StagedQ80 st;
+  stage_load_q80(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  stage_place_q80(lds, L, st, xq, nb);
+  __syncthreads();
+
+  const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
+  float acc = 0.0f;
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = (p0 + j) * 64 + lane;
+      if (!row_ok || b >= nb) continue;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ80::kStride);       // elements 0-15
+      const uint4 a1 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ80::kStride + 16);  // 16-31
+      const uint4 q = Q[j];
+      int s = 0, sa = 0;
+      s = dot4(q.x & kLo4, a0.x, s);
+      s = dot4(q.y & kLo4, a0.y, s);
+      s = dot4(q.z & kLo4, a0.z, s);
+      s = dot4(q.w & kLo4, a0.w, s);
+      s = dot4((q.x >> 4) & kLo4, a1.x, s);
+      s = dot4((q.y >> 4) & kLo4, a1.y, s);
+      s = dot4((q.z >> 4) & kLo4, a1.z, s);
+      s = dot4((q.w >> 4) & kLo4, a1.w, s);
+      sa = dot4(kOnes, a0.x, sa);
+      sa = dot4(kOnes, a0.y, sa);
+      sa = dot4(kOnes, a0.z, sa);
+      sa = dot4(kOnes, a0.w, sa);
+      sa = dot4(kOnes, a1.x, sa);
+      sa = dot4(kOnes, a1.y, sa);
+      sa = dot4(kOnes, a1.z, sa);
+      sa = dot4(kOnes, a1.w, sa);
+      s -= 8 * sa;  // nibbles are stored as q + 8
+      acc += static_cast<float>(s) * (f16_to_f32(D[j]) * dA[b]);
+      if constexpr (SUMS) sums[static_cast<size_t>(row) * nb + b] = s;
+    }
+  }
+  if (row_ok) {
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+template <typename K>
+hipError_t launch(K kernel, int64_t n_out, int64_t lds_bytes, hipStream_t s, hipEvent_t e0,
+                  hipEvent_t e1, const uint8_t* W, int nb, const uint8_t* xq, float* y,
+                  int32_t* sums) {
+  const unsigned grid = static_cast<unsigned>((n_out + kWaves - 1) / kWaves);
+  const int n = static_cast<int>(n_out);
+  if (e0 != nullptr || e1 != nullptr) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), static_cast<uint32_t>(lds_bytes),
+                          s, e0, e1, 0, W, n, nb, xq, y, sums);
+  } else {
+    kernel<<<grid, kWaves * 64, lds_bytes, s>>>(W, n, nb, xq, y, sums);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
+  switch (w_type) {
+    case kQ4_K: return LayoutQ4K(n_in / 256).bytes;
+    case kQ6_K: return LayoutQ6K(n_in / 256).bytes;
+    case kQ8_0:
+    case kQ4_0: return LayoutQ80(n_in / 32).bytes;
+    default: return -1;
+  }
+}
+
+hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in,
+                       const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,
+                       hipEvent_t e0, hipEvent_t e1) {
+  if (n_out <= 0) return hipSuccess;
+  const int64_t lds = gemv_lds_bytes(w_type, n_in);
+  const bool with_sums = sums != nullptr;
+  switch (w_type) {
+    case kQ4_K: {
+      const int nb = static_cast<int>(n_in / 256);
+      return with_sums ? launch(gemv_q4_K_kernel<3, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
+                       : launch(gemv_q4_K_kernel<3, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    }
+    case kQ6_K: {
+      const int nb = static_cast<int>(n_in / 256);
+      return with_sums ? launch(gemv_q6_K_kernel<3, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
+                       : launch(gemv_q6_K_kernel<3, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    }
+    case kQ8_0: {
+      const int nb = static_cast<int>(n_in / 32);
+      return with_sums ? launch(gemv_q8_0_kernel<2, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
+                       : launch(gemv_q8_0_kernel<2, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    }
+    case kQ4_0: {
+      const int nb = static_cast<int>(n_in / 32);
+      return with_sums ? launch(gemv_q4_0_kernel<2, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
+                       : launch(gemv_q4_0_kernel<2, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qk

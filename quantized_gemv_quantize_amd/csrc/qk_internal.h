@@ -1,0 +1,31 @@
+// qk_internal.h - launchers between the C ABI (qk_capi.hip) and the kernels.
+// Arguments reaching a launcher have been validated by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qk {
+
+enum WType : int { kQ4_0 = 2, kQ8_0 = 8, kQ4_K = 12, kQ6_K = 14, kQ8_K = 15 };
+
+// Activation quantization of `nblocks` consecutive blocks (any number of columns
+// laid end to end: blocks of consecutive columns are contiguous).
+hipError_t launch_quantize(int act_type, const float* x, uint8_t* xq, int64_t nblocks,
+                           hipStream_t s);
+
+// One GEMV over one activation column.  `sums` non-null selects the variant that
+// stores the per-block integers (and `y` may be null).  ev_start / ev_stop, when
+// non-null, are recorded by the kernel launch itself.
+hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in,
+                       const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,
+                       hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// Bytes of dynamic LDS a GEMV over rows of n_in elements needs.
+int64_t gemv_lds_bytes(int w_type, int64_t n_in);
+constexpr int64_t kMaxLdsBytes = 65536;
+
+hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t nblocks,
+                             hipStream_t s);
+
+}  // namespace qk

@@ -1,0 +1,122 @@
+"""Seeded synthetic inputs (numpy) for the GEMV workloads.
+
+This module only draws random numbers and lays them into the GGUF block byte
+layouts; it holds none of the method's arithmetic (no quantization, no
+dequantization, no dot products).  Tests feed the same arrays to the CPU oracle
+and to the HIP library; the benchmark uses them for its weight copies.
+
+Recipes (one numpy default_rng(seed) per workload, drawn in the order listed):
+  f16 fields "U[a, b]": f64 uniform draw, rounded to f16 (numpy, RNE).
+  "uniform bytes": every byte iid U{0..255}, so Q4_K's 6-bit scales/mins and the
+  nibbles are uniform; Q6_K scales int8 U{-64..63} inclusive.
+"""
+import numpy as np
+
+Q4_0, Q8_0, Q4_K, Q6_K, Q8_K = 2, 8, 12, 14, 15
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q8_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q8_K: 292}
+
+
+def uniform_bytes(rng, shape):
+    """iid U{0..255} bytes, cut from full-range uint32 draws (exactly uniform)."""
+    count = int(np.prod(shape))
+    words = rng.integers(0, 2**32, size=(count + 3) // 4, dtype=np.uint32)
+    return words.view(np.uint8)[:count].reshape(shape).copy()
+
+
+def uniform_int8(rng, shape, lo, hi):
+    """iid integers U{lo..hi} with hi - lo + 1 a power of two dividing 2^32."""
+    span = hi - lo + 1
+    words = rng.integers(0, 2**32, size=shape, dtype=np.uint32)
+    return ((words % np.uint32(span)).astype(np.int32) + lo).astype(np.int8)
+
+
+def _f16_bytes(vals):
+    return np.ascontiguousarray(vals.astype(np.float16)).view(np.uint8).reshape(*vals.shape, 2)
+
+
+def q4_0_blocks(rng, n_out, n_in, d_range=(1e-3, 4e-3)):
+    """Q4_0 rows: f16 d ~ U[d_range], 16 uniform qs bytes per block."""
+    nb = n_in // 32
+    b = uniform_bytes(rng, (n_out, nb, 18))
+    b[:, :, 0:2] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 18)
+
+
+def q4_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
+    """Q4_K rows: f16 d, dmin ~ U[d_range]; 12 scale bytes and 128 qs bytes uniform."""
+    nb = n_in // 256
+    b = uniform_bytes(rng, (n_out, nb, 144))
+    b[:, :, 0:2] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    b[:, :, 2:4] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 144)
+
+
+def q6_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
+    """Q6_K rows: ql/qh bytes uniform, int8 scales ~ U{-64..63}, f16 d ~ U[d_range]."""
+    nb = n_in // 256
+    b = uniform_bytes(rng, (n_out, nb, 210))
+    b[:, :, 192:208] = uniform_int8(rng, (n_out, nb, 16), -64, 63).view(np.uint8)
+    b[:, :, 208:210] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 210)
+
+
+def weight_blocks(rng, t, n_out, n_in):
+    return {Q4_0: q4_0_blocks, Q4_K: q4_K_blocks, Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
+
+
+def gaussian(rng, shape, std=1.0):
+    return (rng.standard_normal(size=shape) * std).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Named workloads.  Each returns a dict of numpy arrays; "W_f32" entries are f32
+# weights still to be quantized (Q8_0), "W" entries are finished block bytes.
+# ---------------------------------------------------------------------------
+
+def q8_0_gemv_256x1024():
+    """Q8_0 GEMV 256x1024: W f32 ~N(0, 0.02) to be quantized to Q8_0; x ~N(0,1)."""
+    rng = np.random.default_rng(0)
+    return {"W_f32": gaussian(rng, (256, 1024), 0.02), "x": gaussian(rng, (1024,))}
+
+
+def q4_gemv_4096x4096():
+    """Q4_0 and Q4_K GEMV 4096x4096; x ~N(0,1)[4096]."""
+    rng = np.random.default_rng(1)
+    w40 = q4_0_blocks(rng, 4096, 4096)
+    w4k = q4_K_blocks(rng, 4096, 4096)
+    return {"W_q4_0": w40, "W_q4_K": w4k, "x": gaussian(rng, (4096,))}
+
+
+def ffn_7b():
+    """7B-shape FFN: gate, up Q4_K 11008x4096; down Q6_K 4096x11008; x[4096], x2[11008]."""
+    rng = np.random.default_rng(2)
+    gate = q4_K_blocks(rng, 11008, 4096)
+    up = q4_K_blocks(rng, 11008, 4096)
+    down = q6_K_blocks(rng, 4096, 11008)
+    return {"gate": gate, "up": up, "down": down, "x": gaussian(rng, (4096,)),
+            "x2": gaussian(rng, (11008,))}
+
+
+def q6_K_head_32000x4096():
+    """Q6_K output head 32000x4096; x[4096]."""
+    rng = np.random.default_rng(3)
+    return {"W": q6_K_blocks(rng, 32000, 4096), "x": gaussian(rng, (4096,))}
+
+
+def q4_K_batched_14336x4096():
+    """Q4_K 14336x4096 with 64 token columns X[64, 4096] (16-column case = first 16)."""
+    rng = np.random.default_rng(4)
+    return {"W": q4_K_blocks(rng, 14336, 4096), "X": gaussian(rng, (64, 4096))}
+
+
+def q4_K_decode_4096x11008(seed=5):
+    """Q4_K decode GEMV, 4096 rows x 11008 columns (43 superblocks per row); x[11008]."""
+    rng = np.random.default_rng(seed)
+    return {"W": q4_K_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
+
+
+def random_copies(t, n_out, n_in, count, seed):
+    """`count` independent weight matrices of one shape (for cache rotation)."""
+    rng = np.random.default_rng(seed)
+    return [weight_blocks(rng, t, n_out, n_in) for _ in range(count)]

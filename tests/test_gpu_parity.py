@@ -1,0 +1,327 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (per the method's definition):
+  - activation blocks (qk_quantize_act): bit-exact;
+  - per-block int32 sums of the GEMV kernels: bit-exact;
+  - dequantized values: bit-exact (every product is exact in f32);
+  - y: |y_gpu - y_oracle| <= 1e-5 * sum_b |c_b| per output, where c_b are the
+    oracle's per-block float steps (a relative bound that stays meaningful when a
+    random dot product lands near zero; codeloopback Example 10 reports its error
+    against the sum of |a*b| for the same reason).  The GPU sums the same c_b in
+    a different order (and may fuse multiply-adds), which stays far inside it.
+Inputs are seeded (numpy) and synthetic; see quantized_gemv_quantize_amd/synth.py.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import quantized_gemv_quantize_amd as qk
+from quantized_gemv_quantize_amd import synth
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+T8_0, T4_0, T4K, T6K, T8K = (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q4_K,
+                             qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q8_K)
+Y_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    qk.lib()
+    return torch
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def assert_y(y_gpu, y_orc, l1, what):
+    err = np.abs(y_gpu.astype(np.float64) - y_orc.astype(np.float64))
+    bound = Y_TOL * l1
+    bad = err > bound
+    ratio = np.max(err / np.maximum(l1, 1e-300))
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond 1e-5*sum|c_b| (worst {ratio:.3g})"
+
+
+def weights(rng, t, n_out, n_in):
+    if t == T8_0:
+        return orc.quantize(orc.Q8_0, synth.gaussian(rng, (n_out, n_in), 0.02))
+    return synth.weight_blocks(rng, t, n_out, n_in)
+
+
+# ---------------------------------------------------------------------------
+# qk_quantize_act
+# ---------------------------------------------------------------------------
+
+def _special_rows(n, rng):
+    """Activation rows that exercise the edge semantics of the quantizer."""
+    rows = []
+    rows.append(rng.standard_normal(n).astype(np.float32))
+    rows.append((rng.standard_normal(n) * 1e3).astype(np.float32))
+    rows.append(np.zeros(n, np.float32))                          # d = 0 -> codes 0
+    z = rng.standard_normal(n).astype(np.float32)
+    z[::7] = np.nan                                               # NaN ignored / coded 0
+    rows.append(z)
+    w = rng.standard_normal(n).astype(np.float32)
+    w[5] = np.inf                                                 # inf amax -> d = inf
+    w[n // 2 + 3] = -np.inf
+    rows.append(w)
+    rows.append((rng.standard_normal(n) * 1e-39).astype(np.float32))   # subnormal f32
+    rows.append((rng.standard_normal(n) * 1e-42).astype(np.float32))   # 1/d overflows
+    rows.append((rng.standard_normal(n) * 2e-6).astype(np.float32))    # f16 subnormal d
+    rows.append((rng.standard_normal(n) * 9e6).astype(np.float32))     # f16 d -> inf
+    # exact ties: values (k + 0.5) * d with d = 1 -> amax 127 so id = 1/ (127/127)
+    t = (rng.integers(-126, 126, n) + 0.5).astype(np.float32)
+    t[::32] = 127.0
+    rows.append(t)
+    rows.append(np.full(n, -3.25, np.float32))
+    rows.append(np.float32(1.0) * (np.arange(n) % 256 - 128).astype(np.float32))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("act", [T8_0, T8K])
+@pytest.mark.parametrize("n", [256, 4096, 11008])
+def test_quantize_act_bit_exact(torch_cuda, act, n):
+    say("quantize", act, n)
+    rng = np.random.default_rng(1000 + n + act)
+    X = _special_rows(n, rng)
+    got = host(qk.qk_quantize_act(act, dev(torch_cuda, X)))
+    want = orc.quantize(act, X)
+    torch_cuda.cuda.synchronize()
+    assert got.shape == want.shape
+    mism = np.nonzero((got != want).any(axis=1))[0]
+    assert mism.size == 0, f"rows {mism.tolist()} differ"
+
+
+def test_quantize_act_many_columns(torch_cuda):
+    say("quantize many columns")
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((64, 4096)).astype(np.float32)
+    for act in (T8_0, T8K):
+        assert np.array_equal(host(qk.qk_quantize_act(act, dev(torch_cuda, X))),
+                              orc.quantize(act, X))
+
+
+# ---------------------------------------------------------------------------
+# qk_dequantize_row
+# ---------------------------------------------------------------------------
+
+def _edge_scale_blocks(t, rng, nblocks):
+    """Blocks with unusual f16 scales: subnormal, negative, largest finite."""
+    n = nblocks * synth.BLOCK_ELEMS[t]
+    b = weights(rng, t, 1, n).reshape(nblocks, -1).copy()
+    specials = np.array([0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF, 0x3C00, 0xBC00, 0x0000],
+                        dtype=np.uint16).view(np.uint8).reshape(-1, 2)
+    offs = {T8_0: [0], T4_0: [0], T4K: [0, 2], T6K: [208]}[t]
+    for i in range(nblocks):
+        for o in offs:
+            b[i, o:o + 2] = specials[(i + o) % len(specials)]
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("t", [T8_0, T4_0, T4K, T6K])
+def test_dequantize_bit_exact(torch_cuda, t):
+    rng = np.random.default_rng(200 + t)
+    for nblocks in (1, 3, 17, 1000):
+        say("dequantize", t, nblocks)
+        n = nblocks * synth.BLOCK_ELEMS[t]
+        for src in (weights(rng, t, 1, n).reshape(-1), _edge_scale_blocks(t, rng, nblocks)):
+            got = host(qk.qk_dequantize_row(t, dev(torch_cuda, src), n))
+            want = orc.dequantize(t, src, n)
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (t, nblocks)
+
+
+# ---------------------------------------------------------------------------
+# qk_gemv: per-block integer sums and y
+# ---------------------------------------------------------------------------
+
+SHAPES = {
+    T4K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
+    T6K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
+    T8_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (6, 28672)],
+    T4_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (6, 28672)],
+}
+
+
+def _oracle_sums(t, W, xq, n_out, n_in, ncols):
+    at = orc.act_type(t)
+    rb, xb = orc.row_bytes(t, n_in), orc.row_bytes(at, n_in)
+    Wf, xf = W.reshape(-1), xq.reshape(-1)
+    out = []
+    for c in range(ncols):
+        out.append(np.stack([orc.block_sums(t, Wf[r * rb:(r + 1) * rb], xf[c * xb:(c + 1) * xb], n_in)
+                             for r in range(n_out)]))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("t", [T8_0, T4_0, T4K, T6K])
+def test_gemv_block_sums_and_y(torch_cuda, t):
+    rng = np.random.default_rng(300 + t)
+    at = orc.act_type(t)
+    for n_out, n_in in SHAPES[t]:
+        for ncols in (1, 3):
+            say("gemv", t, n_out, n_in, ncols)
+            W = weights(rng, t, n_out, n_in)
+            X = rng.standard_normal((ncols, n_in)).astype(np.float32)
+            xq = orc.quantize(at, X)
+            Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+            # activation blocks from the GPU quantizer equal the oracle's
+            assert np.array_equal(host(qk.qk_quantize_act(at, dev(torch_cuda, X))), xq)
+            sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xd, ncols))
+            want = _oracle_sums(t, W, xq, n_out, n_in, ncols)
+            assert np.array_equal(sums, want.reshape(sums.shape)), (t, n_out, n_in, ncols)
+            y = host(qk.qk_gemv(t, Wd, n_out, n_in, xd, ncols))
+            y_o, l1 = orc.gemv(t, W, n_out, n_in, xq, ncols)
+            assert_y(y, y_o, l1, f"type {t} {n_out}x{n_in} ncols {ncols}")
+
+
+def test_gemv_max_row_length(torch_cuda):
+    rng = np.random.default_rng(31)
+    for t in (T4K, T6K, T8_0, T4_0):
+        n_in = qk.qk_max_n_in(t)
+        say("gemv max n_in", t, n_in)
+        W = weights(rng, t, 3, n_in)
+        X = rng.standard_normal((1, n_in)).astype(np.float32)
+        xq = orc.quantize(orc.act_type(t), X)
+        y = host(qk.qk_gemv(t, dev(torch_cuda, W), 3, n_in, dev(torch_cuda, xq), 1))
+        y_o, l1 = orc.gemv(t, W, 3, n_in, xq, 1)
+        assert_y(y, y_o, l1, f"type {t} max n_in {n_in}")
+
+
+def test_gemv_zero_activation_gives_zero(torch_cuda):
+    # rml ZeroActivationsGiveZero
+    rng = np.random.default_rng(5)
+    for t in (T4K, T6K, T8_0, T4_0):
+        W = weights(rng, t, 8, 1024)
+        xq = qk.qk_quantize_act(orc.act_type(t), torch_cuda.zeros((1, 1024), device="cuda"))
+        y = host(qk.qk_gemv(t, dev(torch_cuda, W), 8, 1024, xq, 1))
+        assert not y.any()
+
+
+def test_gemv_rejects_misaligned_view(torch_cuda):
+    rng = np.random.default_rng(6)
+    W = dev(torch_cuda, weights(rng, T4K, 4, 512))
+    xq = qk.qk_quantize_act(T8K, dev(torch_cuda, rng.standard_normal((1, 512)).astype(np.float32)))
+    with pytest.raises(qk.QKError) as e:
+        qk.qk_gemv(T4K, W.reshape(-1)[8:], 3, 512, xq, 1)
+    assert e.value.status == 4
+    with pytest.raises(qk.QKError) as e:
+        qk.qk_gemv(T8K, W, 4, 512, xq, 1)
+    assert e.value.status == 1
+
+
+def test_gemv_timed_matches_untimed(torch_cuda):
+    rng = np.random.default_rng(8)
+    W = dev(torch_cuda, weights(rng, T4K, 256, 4096))
+    xq = qk.qk_quantize_act(T8K, dev(torch_cuda, rng.standard_normal((2, 4096)).astype(np.float32)))
+    y0 = qk.qk_gemv(T4K, W, 256, 4096, xq, 2)
+    e0 = torch_cuda.cuda.Event(enable_timing=True)
+    e1 = torch_cuda.cuda.Event(enable_timing=True)
+    e0.record()  # torch creates the underlying hipEvent_t on first record
+    e1.record()
+    y1 = torch_cuda.empty_like(y0)
+    qk.qk_gemv_timed(T4K, W, 256, 4096, xq, 2, y1, e0, e1)
+    e1.synchronize()
+    assert e0.elapsed_time(e1) > 0
+    assert torch_cuda.equal(y0, y1)
+
+
+def test_native_library_is_the_one_loaded(torch_cuda):
+    maps = open("/proc/self/maps").read()
+    assert os.path.realpath(qk.LIB_PATH) in maps
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times.
+# ---------------------------------------------------------------------------
+
+def _check_full(torch, t, W, n_out, n_in, X, rows=None, what=""):
+    """GEMV over the full matrix on the GPU; oracle on `rows` (all if None)."""
+    at = orc.act_type(t)
+    ncols = X.shape[0]
+    xq_gpu = qk.qk_quantize_act(at, dev(torch, X))
+    xq = orc.quantize(at, X)
+    assert np.array_equal(host(xq_gpu), xq), what
+    Wd = dev(torch, W)
+    y = host(qk.qk_gemv(t, Wd, n_out, n_in, xq_gpu, ncols))
+    sel = np.arange(n_out) if rows is None else np.asarray(rows)
+    Wsel = W.reshape(n_out, -1)[sel]
+    y_o, l1 = orc.gemv(t, Wsel, len(sel), n_in, xq, ncols)
+    assert_y(y[:, sel], y_o, l1, what)
+    sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xq_gpu, ncols))
+    pick = sel[:: max(1, len(sel) // 64)]
+    want = _oracle_sums(t, W.reshape(n_out, -1)[pick], xq, len(pick), n_in, ncols)
+    assert np.array_equal(sums[:, pick], want.reshape(sums[:, pick].shape)), what
+    return y
+
+
+def test_full_q8_0_256x1024(torch_cuda):
+    say("full Q8_0 256x1024")
+    d = synth.q8_0_gemv_256x1024()
+    # the weights are quantized on each side by its own quantizer
+    Wg = host(qk.qk_quantize_act(T8_0, dev(torch_cuda, d["W_f32"])))
+    W = orc.quantize(orc.Q8_0, d["W_f32"])
+    assert np.array_equal(Wg, W)
+    _check_full(torch_cuda, T8_0, W, 256, 1024, d["x"][None, :], what="Q8_0 256x1024")
+
+
+def test_full_q4_0_and_q4_K_4096x4096(torch_cuda):
+    d = synth.q4_gemv_4096x4096()
+    say("full Q4_0 4096x4096")
+    _check_full(torch_cuda, T4_0, d["W_q4_0"], 4096, 4096, d["x"][None, :], what="Q4_0 4096^2")
+    say("full Q4_K 4096x4096")
+    _check_full(torch_cuda, T4K, d["W_q4_K"], 4096, 4096, d["x"][None, :], what="Q4_K 4096^2")
+
+
+def test_full_ffn_7b(torch_cuda):
+    d = synth.ffn_7b()
+    say("full FFN gate/up Q4_K 11008x4096")
+    _check_full(torch_cuda, T4K, d["gate"], 11008, 4096, d["x"][None, :], what="gate")
+    _check_full(torch_cuda, T4K, d["up"], 11008, 4096, d["x"][None, :], what="up")
+    say("full FFN down Q6_K 4096x11008")
+    _check_full(torch_cuda, T6K, d["down"], 4096, 11008, d["x2"][None, :], what="down")
+
+
+def test_full_q6_K_head_and_dequantize(torch_cuda):
+    d = synth.q6_K_head_32000x4096()
+    say("full Q6_K head 32000x4096")
+    _check_full(torch_cuda, T6K, d["W"], 32000, 4096, d["x"][None, :], what="Q6_K head")
+    say("full Q6_K dequantize 32000x4096")
+    Wd = dev(torch_cuda, d["W"])
+    out = qk.qk_dequantize_row(T6K, Wd, 32000 * 4096)
+    rb = orc.row_bytes(orc.Q6_K, 4096)
+    for r0 in range(0, 32000, 4000):
+        want = orc.dequantize(orc.Q6_K, d["W"][r0:r0 + 4000].reshape(-1), 4000 * 4096)
+        got = host(out[r0 * 4096:(r0 + 4000) * 4096])
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), r0
+    del rb
+
+
+@pytest.mark.parametrize("ncols", [16, 64])
+def test_full_q4_K_batched_14336x4096(torch_cuda, ncols):
+    d = synth.q4_K_batched_14336x4096()
+    say("full Q4_K batched 14336x4096", ncols)
+    rng = np.random.default_rng(44)
+    rows = np.unique(np.concatenate([np.arange(64), rng.integers(0, 14336, 192), [14335]]))
+    _check_full(torch_cuda, T4K, d["W"], 14336, 4096, d["X"][:ncols], rows=rows,
+                what=f"Q4_K batched {ncols}")
+
+
+def test_full_q4_K_decode_4096x11008(torch_cuda):
+    d = synth.q4_K_decode_4096x11008()
+    say("full Q4_K 4096x11008")
+    _check_full(torch_cuda, T4K, d["W"], 4096, 11008, d["x"][None, :], what="Q4_K 4096x11008")
