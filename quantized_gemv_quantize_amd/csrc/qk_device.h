@@ -58,6 +58,12 @@ __device__ __forceinline__ void store_u2(uint8_t* p, const T& v) {
   __builtin_memcpy(p2, &v, sizeof(T));
 }
 
+// Index of the wavefront inside its workgroup, as a wave-uniform (scalar) value so
+// that row base addresses live in SGPRs and loads take a 32-bit lane offset.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 // Cross-lane sums inside groups of 4 lanes (DPP quad_perm, exact int32 adds).
 __device__ __forceinline__ int quad_sum(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
@@ -65,17 +71,43 @@ __device__ __forceinline__ int quad_sum(int v) {
   return v;
 }
 
-// Sum over the 64 lanes of a wavefront (every lane receives the total).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// a * b + c for |a|, |b| < 2^23 (v_mad_i32_i24, full rate).
+__device__ __forceinline__ int mad24(int a, int b, int c) { return __mul24(a, b) + c; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Sum over the 64 lanes of a wavefront, returned in every lane: DPP sums inside
+// each row of 16 lanes (quad swaps, half-row and row mirrors), then the four row
+// totals are read from lanes 15, 31, 47 and 63.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror: sum of 8
+  v += dpp_f<0x140>(v);  // row_mirror: sum of 16 in every lane of the row
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Largest value over groups of 8 lanes (returned in every lane of the group).
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  return fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+}
+
+// Largest value over the 64 lanes of a wavefront, returned in every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v = max8(v);
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror: max of 16
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63))));
 }
 
 }  // namespace qk

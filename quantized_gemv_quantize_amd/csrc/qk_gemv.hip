@@ -29,6 +29,13 @@
 #include "qk_device.h"
 #include "qk_internal.h"
 
+#ifndef QK_GEMV_WAVES
+#define QK_GEMV_WAVES 4
+#endif
+#ifndef QK_MAX_WAVES
+#define QK_MAX_WAVES 4096
+#endif
+
 namespace qk {
 namespace {
 
@@ -36,8 +43,6 @@ constexpr uint32_t kLo4 = 0x0F0F0F0Fu;
 constexpr uint32_t kHi2 = 0x30303030u;
 constexpr uint32_t kOnes = 0x01010101u;
 
-constexpr int kWaves = 4;  // wavefronts (rows) per workgroup
-constexpr int kThreads = kWaves * 64;
 
 __host__ __device__ constexpr int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
 
@@ -111,23 +116,24 @@ struct StagedQ80 {
 // Q8_K block i (292 bytes): piece p (p < 16) = codes 16p..16p+15 at 4 + 16p;
 // small unit r (r < 9) = dword r of {d, bsum pairs 0-7} at 0 and 260 + 4(r-1).
 __device__ __forceinline__ const uint8_t* q8K_piece_src(const uint8_t* xq, int u) {
-  return xq + (u >> 4) * kQ8_KBytes + 4 + 16 * (u & 15);
+  return xq + static_cast<uint32_t>((u >> 4) * kQ8_KBytes + 4 + 16 * (u & 15));
 }
 __device__ __forceinline__ const uint8_t* q8K_small_src(const uint8_t* xq, int u) {
   const int i = u / 9, r = u - 9 * i;
-  return xq + i * kQ8_KBytes + (r == 0 ? 0 : 256 + 4 * r);
+  return xq + static_cast<uint32_t>(i * kQ8_KBytes + (r == 0 ? 0 : 256 + 4 * r));
 }
 
+template <int NT>
 __device__ __forceinline__ void stage_load_q8K(StagedQ8K& st, const uint8_t* __restrict__ xq, int nb) {
   const int np = nb * 16, ns = nb * 9;
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1);
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, np - 1);
     st.piece[i] = load_u2<uint4>(q8K_piece_src(xq, u));
   }
 #pragma unroll
   for (int i = 0; i < kSmall; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, ns - 1);
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, ns - 1);
     st.small[i] = *reinterpret_cast<const uint32_t*>(q8K_small_src(xq, u));
   }
 }
@@ -168,62 +174,64 @@ __device__ __forceinline__ void place_small_q6K(uint8_t* lds, const LayoutQ6K& L
   *reinterpret_cast<uint32_t*>(lds + a1) = v1;
 }
 
-template <typename LayoutT, typename PieceF, typename SmallF>
+template <int NT, typename LayoutT, typename PieceF, typename SmallF>
 __device__ __forceinline__ void stage_place_q8K(uint8_t* lds, const LayoutT& L, const StagedQ8K& st,
                                                 const uint8_t* __restrict__ xq, int nb, PieceF piece,
                                                 SmallF small) {
   const int np = nb * 16, ns = nb * 9;
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
-    piece(lds, min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1), st.piece[i]);
+    piece(lds, min(static_cast<int>(threadIdx.x) + i * NT, np - 1), st.piece[i]);
   }
 #pragma unroll
   for (int i = 0; i < kSmall; ++i) {
-    small(lds, L, min(static_cast<int>(threadIdx.x) + i * kThreads, ns - 1), st.small[i]);
+    small(lds, L, min(static_cast<int>(threadIdx.x) + i * NT, ns - 1), st.small[i]);
   }
-  for (int u = static_cast<int>(threadIdx.x) + kPieces * kThreads; u < np; u += kThreads) {
+  for (int u = static_cast<int>(threadIdx.x) + kPieces * NT; u < np; u += NT) {
     piece(lds, u, load_u2<uint4>(q8K_piece_src(xq, u)));
   }
-  for (int u = static_cast<int>(threadIdx.x) + kSmall * kThreads; u < ns; u += kThreads) {
+  for (int u = static_cast<int>(threadIdx.x) + kSmall * NT; u < ns; u += NT) {
     small(lds, L, u, *reinterpret_cast<const uint32_t*>(q8K_small_src(xq, u)));
   }
 }
 
 // Q8_0 block i (34 bytes): pieces 0, 1 = codes at 2 and 18; small unit = f16 d at 0.
 // LDS: piece p -> 48 i + 16 p; d -> off_d + 4 i as f32.
+template <int NT>
 __device__ __forceinline__ void stage_load_q80(StagedQ80& st, const uint8_t* __restrict__ xq, int nb) {
   const int np = nb * 2;
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1);
-    st.piece[i] = load_u2<uint4>(xq + (u >> 1) * kQ8_0Bytes + 2 + 16 * (u & 1));
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, np - 1);
+    st.piece[i] = load_u2<uint4>(xq + static_cast<uint32_t>((u >> 1) * kQ8_0Bytes + 2 + 16 * (u & 1)));
   }
 #pragma unroll
   for (int i = 0; i < kSmall; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, nb - 1);
-    st.small[i] = *reinterpret_cast<const uint16_t*>(xq + u * kQ8_0Bytes);
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, nb - 1);
+    st.small[i] = *reinterpret_cast<const uint16_t*>(xq + static_cast<uint32_t>(u * kQ8_0Bytes));
   }
 }
 
+template <int NT>
 __device__ __forceinline__ void stage_place_q80(uint8_t* lds, const LayoutQ80& L, const StagedQ80& st,
                                                 const uint8_t* __restrict__ xq, int nb) {
   const int np = nb * 2;
   float* dA = reinterpret_cast<float*>(lds + L.off_d);
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, np - 1);
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, np - 1);
     *reinterpret_cast<uint4*>(lds + (u >> 1) * LayoutQ80::kStride + 16 * (u & 1)) = st.piece[i];
   }
 #pragma unroll
   for (int i = 0; i < kSmall; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * kThreads, nb - 1);
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, nb - 1);
     dA[u] = f16_to_f32(st.small[i]);
   }
-  for (int u = static_cast<int>(threadIdx.x) + kPieces * kThreads; u < np; u += kThreads) {
+  for (int u = static_cast<int>(threadIdx.x) + kPieces * NT; u < np; u += NT) {
     *reinterpret_cast<uint4*>(lds + (u >> 1) * LayoutQ80::kStride + 16 * (u & 1)) =
         load_u2<uint4>(xq + (u >> 1) * kQ8_0Bytes + 2 + 16 * (u & 1));
   }
-  for (int u = static_cast<int>(threadIdx.x) + kSmall * kThreads; u < nb; u += kThreads) {
+  for (int u = static_cast<int>(threadIdx.x) + kSmall * NT; u < nb; u += NT) {
     dA[u] = f16_to_f32(*reinterpret_cast<const uint16_t*>(xq + u * kQ8_0Bytes));
   }
 }
@@ -231,17 +239,63 @@ __device__ __forceinline__ void stage_place_q80(uint8_t* lds, const LayoutQ80& L
 // Keeps the backend scheduler from interleaving the activation and weight loads.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+template <typename T>
+__device__ __forceinline__ T load_a4(const uint8_t* p) {  // 4-byte aligned field
+  const uint32_t* p4 = reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));
+  T v;
+  __builtin_memcpy(&v, p4, sizeof(T));
+  return v;
+}
+
+// Exact integer part of one Q4_K superblock for chunk c (sub-blocks 2c, 2c+1):
+// returns this lane's S_q and S_m partial sums (before the quad reduction).
+// hi_mask is all ones for chunks 2 and 3 (sub-blocks 4-7), zero otherwise, so the
+// scale words are selected with bit operations instead of a divergent branch.
+__device__ __forceinline__ int2 q4K_chunk(const uint4& q0, const uint4& q1, const uint4& h,
+                                          const uint4& a0, const uint4& a1, const uint4& a2,
+                                          const uint4& a3, int2 asum, uint32_t hi_mask, int sh) {
+  int slo = 0, shi = 0;
+  slo = dot4(q0.x & kLo4, a0.x, slo);
+  slo = dot4(q0.y & kLo4, a0.y, slo);
+  slo = dot4(q0.z & kLo4, a0.z, slo);
+  slo = dot4(q0.w & kLo4, a0.w, slo);
+  slo = dot4(q1.x & kLo4, a1.x, slo);
+  slo = dot4(q1.y & kLo4, a1.y, slo);
+  slo = dot4(q1.z & kLo4, a1.z, slo);
+  slo = dot4(q1.w & kLo4, a1.w, slo);
+  shi = dot4((q0.x >> 4) & kLo4, a2.x, shi);
+  shi = dot4((q0.y >> 4) & kLo4, a2.y, shi);
+  shi = dot4((q0.z >> 4) & kLo4, a2.z, shi);
+  shi = dot4((q0.w >> 4) & kLo4, a2.w, shi);
+  shi = dot4((q1.x >> 4) & kLo4, a3.x, shi);
+  shi = dot4((q1.y >> 4) & kLo4, a3.y, shi);
+  shi = dot4((q1.z >> 4) & kLo4, a3.z, shi);
+  shi = dot4((q1.w >> 4) & kLo4, a3.w, shi);
+  // get_scale_min_k4 for all four sub-blocks of a group at once: sub-blocks 0-3
+  // take the low 6 bits of scale bytes 0-3 / 4-7; sub-blocks 4-7 take the low /
+  // high nibble of bytes 8-11 and the top 2 bits of bytes 0-3 / 4-7.
+  const uint32_t sc_a = h.y & 0x3F3F3F3Fu;
+  const uint32_t m_a = h.z & 0x3F3F3F3Fu;
+  const uint32_t sc_b = (h.w & kLo4) | ((h.y >> 2) & kHi2);
+  const uint32_t m_b = ((h.w >> 4) & kLo4) | ((h.z >> 2) & kHi2);
+  const uint32_t scw = (sc_b & hi_mask) | (sc_a & ~hi_mask);
+  const uint32_t mw = (m_b & hi_mask) | (m_a & ~hi_mask);
+  const int sc_lo = __builtin_amdgcn_ubfe(scw, sh, 8), sc_hi = __builtin_amdgcn_ubfe(scw, sh + 8, 8);
+  const int m_lo = __builtin_amdgcn_ubfe(mw, sh, 8), m_hi = __builtin_amdgcn_ubfe(mw, sh + 8, 8);
+  return make_int2(mad24(sc_lo, slo, __mul24(sc_hi, shi)), mad24(m_lo, asum.x, __mul24(m_hi, asum.y)));
+}
+
 // ---------------------------------------------------------------------------
 // Q4_K x Q8_K.  Lane (u = lane >> 2, c = lane & 3) of pass `it` handles 64-element
 // chunk c of superblock it*16 + u: qs[32c .. 32c+31] hold sub-block 2c in their low
 // nibbles and sub-block 2c+1 in their high nibbles.
-template <int UNR, bool SUMS>
-__global__ __launch_bounds__(kWaves * 64) void gemv_q4_K_kernel(
+template <int NW, int UNR, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * NW + wave_id();
   const int c = lane & 3, u = lane >> 2;
   const bool row_ok = row < n_out;
   const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
@@ -255,7 +309,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q4_K_kernel(
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       const int sb = min((p0 + j) * 16 + u, nb - 1);
-      const uint8_t* p = wrow + static_cast<size_t>(sb) * kQ4_KBytes;
+      const uint8_t* p = wrow + static_cast<uint32_t>(sb * kQ4_KBytes);
       H[j] = *reinterpret_cast<const uint4*>(p);
       Q0[j] = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
       Q1[j] = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
@@ -263,17 +317,25 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q4_K_kernel(
   };
   const LayoutQ4K L(nb);
   StagedQ8K st;
-  stage_load_q8K(st, xq, nb);
+  stage_load_q8K<NW * 64>(st, xq, nb);
+  sched_fence();
+#ifdef QK_ACT_FIRST
+  stage_place_q8K<NW * 64>(lds, L, st, xq, nb, place_piece_q4K, place_small_q4K);
   sched_fence();
   issue(0);
-  sched_fence();
-  stage_place_q8K(lds, L, st, xq, nb, place_piece_q4K, place_small_q4K);
   __syncthreads();
+#else
+  issue(0);
+  sched_fence();
+  stage_place_q8K<NW * 64>(lds, L, st, xq, nb, place_piece_q4K, place_small_q4K);
+  __syncthreads();
+#endif
 
   const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
   const int32_t* sA = reinterpret_cast<const int32_t*>(lds + L.off_s);
   const int sw = (c >> 1) << 1;  // piece XOR of chunk c
   const int sh = (c & 1) * 16;   // byte pair of this chunk's two sub-blocks
+  const uint32_t hi_mask = (c & 2) ? 0xFFFFFFFFu : 0u;
   float acc = 0.0f;
 
   for (int p0 = 0; p0 < passes; p0 += UNR) {
@@ -289,40 +351,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q4_K_kernel(
       const uint4 a3 = *reinterpret_cast<const uint4*>(ap + 16 * (3 ^ sw));
       const int2 asum = *reinterpret_cast<const int2*>(sA + sb * 8 + 2 * c);
       const float dx = dA[sb];
-      const uint4 q0 = Q0[j], q1 = Q1[j], h = H[j];
-
-      int slo = 0, shi = 0;
-      slo = dot4(q0.x & kLo4, a0.x, slo);
-      slo = dot4(q0.y & kLo4, a0.y, slo);
-      slo = dot4(q0.z & kLo4, a0.z, slo);
-      slo = dot4(q0.w & kLo4, a0.w, slo);
-      slo = dot4(q1.x & kLo4, a1.x, slo);
-      slo = dot4(q1.y & kLo4, a1.y, slo);
-      slo = dot4(q1.z & kLo4, a1.z, slo);
-      slo = dot4(q1.w & kLo4, a1.w, slo);
-      shi = dot4((q0.x >> 4) & kLo4, a2.x, shi);
-      shi = dot4((q0.y >> 4) & kLo4, a2.y, shi);
-      shi = dot4((q0.z >> 4) & kLo4, a2.z, shi);
-      shi = dot4((q0.w >> 4) & kLo4, a2.w, shi);
-      shi = dot4((q1.x >> 4) & kLo4, a3.x, shi);
-      shi = dot4((q1.y >> 4) & kLo4, a3.y, shi);
-      shi = dot4((q1.z >> 4) & kLo4, a3.z, shi);
-      shi = dot4((q1.w >> 4) & kLo4, a3.w, shi);
-
-      // get_scale_min_k4 for sub-blocks 2c and 2c+1, all four bytes of a group at once:
-      // sub-blocks 0-3: low 6 bits of bytes 0-3 (scale) and 4-7 (min); 4-7: low / high
-      // nibble of bytes 8-11 plus the top 2 bits of bytes 0-3 / 4-7.
-      const uint32_t scw = (c & 2) ? ((h.w & kLo4) | ((h.y >> 2) & kHi2)) : (h.y & 0x3F3F3F3Fu);
-      const uint32_t mw = (c & 2) ? (((h.w >> 4) & kLo4) | ((h.z >> 2) & kHi2)) : (h.z & 0x3F3F3F3Fu);
-      const int sc_lo = (scw >> sh) & 0xFF, sc_hi = (scw >> (sh + 8)) & 0xFF;
-      const int m_lo = (mw >> sh) & 0xFF, m_hi = (mw >> (sh + 8)) & 0xFF;
-
-      const int sq = quad_sum(sc_lo * slo + sc_hi * shi);
-      const int sm = quad_sum(m_lo * asum.x + m_hi * asum.y);
+      const uint4 h = H[j];
+      const int2 part = q4K_chunk(Q0[j], Q1[j], h, a0, a1, a2, a3, asum, hi_mask, sh);
+      const int sq = quad_sum(part.x);
+      const int sm = quad_sum(part.y);
+      const float cb = (dx * f16_to_f32(h.x & 0xFFFF)) * static_cast<float>(sq) -
+                       (dx * f16_to_f32(h.x >> 16)) * static_cast<float>(sm);
+      acc += (c == 0) ? cb : 0.0f;
       if (c == 0) {
-        const float d = f16_to_f32(h.x & 0xFFFF);
-        const float dmin = f16_to_f32(h.x >> 16);
-        acc += (dx * d) * static_cast<float>(sq) - (dx * dmin) * static_cast<float>(sm);
         if constexpr (SUMS) {
           int32_t* o = sums + (static_cast<size_t>(row) * nb + sb) * 2;
           o[0] = sq;
@@ -341,13 +377,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q4_K_kernel(
 // Q6_K x Q8_K.  Lane (u = lane >> 2, p = lane & 3 -> half h = p >> 1, k = p & 1) of
 // pass `it` handles, in superblock it*16 + u, positions l in [16k, 16k+16) of half
 // h for all four groups g: elements 128h + 32g + l, sub-blocks 8h + 2g + k.
-template <int UNR, bool SUMS>
-__global__ __launch_bounds__(kWaves * 64) void gemv_q6_K_kernel(
+template <int NW, int UNR, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * NW + wave_id();
   const int pos = lane & 3, u = lane >> 2;
   const int hh = pos >> 1, kk = pos & 1;
   const bool row_ok = row < n_out;
@@ -362,7 +398,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q6_K_kernel(
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       const int sb = min((p0 + j) * 16 + u, nb - 1);
-      const uint8_t* p = wrow + static_cast<size_t>(sb) * kQ6_KBytes;
+      const uint8_t* p = wrow + static_cast<uint32_t>(sb * kQ6_KBytes);
       A[j] = load_u2<uint4>(p + 64 * hh + 16 * kk);
       B[j] = load_u2<uint4>(p + 64 * hh + 32 + 16 * kk);
       QH[j] = load_u2<uint4>(p + 128 + 32 * hh + 16 * kk);
@@ -372,11 +408,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q6_K_kernel(
   };
   const LayoutQ6K L(nb);
   StagedQ8K st;
-  stage_load_q8K(st, xq, nb);
+  stage_load_q8K<NW * 64>(st, xq, nb);
   sched_fence();
   issue(0);
   sched_fence();
-  stage_place_q8K(lds, L, st, xq, nb, place_piece_q6K, place_small_q6K);
+  stage_place_q8K<NW * 64>(lds, L, st, xq, nb, place_piece_q6K, place_small_q6K);
   __syncthreads();
 
   const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
@@ -422,7 +458,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q6_K_kernel(
       const int sc2 = static_cast<int8_t>((SC[j].y >> (8 * kk)) & 0xFF);
       const int sc3 = static_cast<int8_t>((SC[j].y >> (16 + 8 * kk)) & 0xFF);
       // q is stored as 0..63; sum (q - 32) a = sum q a - 32 * bsum
-      const int part = sc0 * (s0 - bs.x) + sc1 * (s1 - bs.y) + sc2 * (s2 - bs.z) + sc3 * (s3 - bs.w);
+      const int part = mad24(sc0, s0 - bs.x, mad24(sc1, s1 - bs.y, mad24(sc2, s2 - bs.z, __mul24(sc3, s3 - bs.w))));
       const int S = quad_sum(part);
       if (pos == 0) {
         const float d = f16_to_f32(D[j]);
@@ -439,13 +475,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q6_K_kernel(
 
 // ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 and Q4_0 x Q8_0: lane b of pass `it` handles block it*64 + lane.
-template <int UNR, bool SUMS>
-__global__ __launch_bounds__(kWaves * 64) void gemv_q8_0_kernel(
+template <int NW, int UNR, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q8_0_kernel(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * NW + wave_id();
   const bool row_ok = row < n_out;
   const size_t rb = static_cast<size_t>(nb) * kQ8_0Bytes;
   const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
@@ -457,7 +493,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q8_0_kernel(
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       const int b = min((p0 + j) * 64 + lane, nb - 1);
-      const uint8_t* p = wrow + static_cast<size_t>(b) * kQ8_0Bytes;
+      const uint8_t* p = wrow + static_cast<uint32_t>(b * kQ8_0Bytes);
       D[j] = *reinterpret_cast<const uint16_t*>(p);
       Q0[j] = load_u2<uint4>(p + 2);
       Q1[j] = load_u2<uint4>(p + 18);
@@ -465,11 +501,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q8_0_kernel(
   };
   const LayoutQ80 L(nb);
   StagedQ80 st;
-  stage_load_q80(st, xq, nb);
+  stage_load_q80<NW * 64>(st, xq, nb);
   sched_fence();
   issue(0);
   sched_fence();
-  stage_place_q80(lds, L, st, xq, nb);
+  stage_place_q80<NW * 64>(lds, L, st, xq, nb);
   __syncthreads();
 
   const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
@@ -501,13 +537,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q8_0_kernel(
   }
 }
 
-template <int UNR, bool SUMS>
-__global__ __launch_bounds__(kWaves * 64) void gemv_q4_0_kernel(
+template <int NW, int UNR, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q4_0_kernel(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int row = blockIdx.x * NW + wave_id();
   const bool row_ok = row < n_out;
   const size_t rb = static_cast<size_t>(nb) * kQ4_0Bytes;
   const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
@@ -519,18 +555,18 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q4_0_kernel(
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       const int b = min((p0 + j) * 64 + lane, nb - 1);
-      const uint8_t* p = wrow + static_cast<size_t>(b) * kQ4_0Bytes;
+      const uint8_t* p = wrow + static_cast<uint32_t>(b * kQ4_0Bytes);
       D[j] = *reinterpret_cast<const uint16_t*>(p);
       Q[j] = load_u2<uint4>(p + 2);
     }
   };
   const LayoutQ80 L(nb);
   StagedQ80 st;
-  stage_load_q80(st, xq, nb);
+  stage_load_q80<NW * 64>(st, xq, nb);
   sched_fence();
   issue(0);
   sched_fence();
-  stage_place_q80(lds, L, st, xq, nb);
+  stage_place_q80<NW * 64>(lds, L, st, xq, nb);
   __syncthreads();
 
   const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
@@ -572,17 +608,279 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_q4_0_kernel(
   }
 }
 
-template <typename K>
+// ---------------------------------------------------------------------------
+// Register-resident activations.  Each lane loads, once per wavefront, the
+// activation codes, sums and scale of the blocks it covers in every pass of a
+// row, then the wavefront walks its rows (RPW at a time, strided by the grid)
+// reusing those registers: no LDS, no workgroup barrier.
+template <int NW, int NP, int RPW, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 3, u = lane >> 2;
+  const uint32_t hi_mask = (c & 2) ? 0xFFFFFFFFu : 0u;
+  const int sh = (c & 1) * 16;
+  const int wave = blockIdx.x * NW + wave_id();
+  const int nwaves = gridDim.x * NW;
+  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+
+  uint4 A[NP][4];
+  int2 S2[NP];
+  float DX[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint8_t* a = xq + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ8_KBytes);
+    DX[p] = *reinterpret_cast<const float*>(a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[p][i] = load_a4<uint4>(a + 4 + 64 * c + 16 * i);
+    const uint2 bs = load_a4<uint2>(a + 260 + 8 * c);
+    S2[p] = make_int2(sext16_lo(bs.x) + sext16_hi(bs.x), sext16_lo(bs.y) + sext16_hi(bs.y));
+  }
+#ifdef QK_ACT_FIRST
+  __builtin_amdgcn_s_waitcnt(0);
+  sched_fence();
+#endif
+
+  for (int r0 = wave * RPW; r0 < n_out; r0 += nwaves * RPW) {
+    uint4 H[RPW][NP], Q0[RPW][NP], Q1[RPW][NP];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const uint8_t* wrow = W + static_cast<size_t>(min(r0 + r, n_out - 1)) * rb;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ4_KBytes);
+        H[r][p] = *reinterpret_cast<const uint4*>(q);
+        Q0[r][p] = *reinterpret_cast<const uint4*>(q + 16 + 32 * c);
+        Q1[r][p] = *reinterpret_cast<const uint4*>(q + 32 + 32 * c);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = r0 + r;
+      if (row >= n_out) break;  // uniform over the wavefront
+      float acc = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int sb = p * 16 + u;
+        if (sb >= nb) continue;  // uniform over the 4 lanes of a superblock
+        const int2 part = q4K_chunk(Q0[r][p], Q1[r][p], H[r][p], A[p][0], A[p][1], A[p][2], A[p][3],
+                                    S2[p], hi_mask, sh);
+        const int sq = quad_sum(part.x);
+        const int sm = quad_sum(part.y);
+        const uint32_t dd = H[r][p].x;
+        const float cb = (DX[p] * f16_to_f32(dd & 0xFFFF)) * static_cast<float>(sq) -
+                         (DX[p] * f16_to_f32(dd >> 16)) * static_cast<float>(sm);
+        acc += (c == 0) ? cb : 0.0f;
+        if (c == 0) {
+          if constexpr (SUMS) {
+            int32_t* o = sums + (static_cast<size_t>(row) * nb + sb) * 2;
+            o[0] = sq;
+            o[1] = sm;
+          }
+        }
+      }
+      const float total = wave_sum(acc);
+      if (lane == 0 && y != nullptr) y[row] = total;
+    }
+  }
+}
+
+// Q6_K x Q8_K, register-resident activations.  Lane (u, p = h*2 + k) of pass P
+// covers l in [16k, 16k+16) of half h of superblock P*16 + u for the four groups
+// g: activation pieces 8h + 2g + k, 16-element sub-blocks 8h + 2g + k.
+template <int NW, int NP, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q6_K_reg(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  const int lane = threadIdx.x & 63;
+  const int pos = lane & 3, u = lane >> 2;
+  const int hh = pos >> 1, kk = pos & 1;
+  const int wave = blockIdx.x * NW + wave_id();
+  const int nwaves = gridDim.x * NW;
+  const size_t rb = static_cast<size_t>(nb) * kQ6_KBytes;
+
+  uint4 A[NP][4];
+  int4 BS[NP];  // 32 * bsum of sub-blocks 8h + 2g + k, g = 0..3
+  float DX[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint8_t* a = xq + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ8_KBytes);
+    DX[p] = *reinterpret_cast<const float*>(a);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) A[p][g] = load_a4<uint4>(a + 4 + 128 * hh + 32 * g + 16 * kk);
+    const uint4 b = load_a4<uint4>(a + 260 + 16 * hh);  // bsums 8h .. 8h+7
+    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+    int v[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) v[g] = 32 * (kk ? sext16_hi(w[g]) : sext16_lo(w[g]));
+    BS[p] = make_int4(v[0], v[1], v[2], v[3]);
+  }
+#ifdef QK_ACT_FIRST
+  __builtin_amdgcn_s_waitcnt(0);
+  sched_fence();
+#endif
+
+  for (int row = wave; row < n_out; row += nwaves) {
+    const uint8_t* wrow = W + static_cast<size_t>(row) * rb;
+    uint4 QA[NP], QB[NP], QH[NP];
+    uint2 SC[NP];
+    uint32_t D[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ6_KBytes);
+      QA[p] = load_u2<uint4>(q + 64 * hh + 16 * kk);
+      QB[p] = load_u2<uint4>(q + 64 * hh + 32 + 16 * kk);
+      QH[p] = load_u2<uint4>(q + 128 + 32 * hh + 16 * kk);
+      SC[p] = load_u2<uint2>(q + 192 + 8 * hh);
+      D[p] = *reinterpret_cast<const uint16_t*>(q + 208);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int sb = p * 16 + u;
+      if (sb >= nb) continue;
+      const uint32_t al[4] = {QA[p].x, QA[p].y, QA[p].z, QA[p].w};
+      const uint32_t bl[4] = {QB[p].x, QB[p].y, QB[p].z, QB[p].w};
+      const uint32_t hl[4] = {QH[p].x, QH[p].y, QH[p].z, QH[p].w};
+      int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a0 = i == 0 ? A[p][0].x : i == 1 ? A[p][0].y : i == 2 ? A[p][0].z : A[p][0].w;
+        const uint32_t a1 = i == 0 ? A[p][1].x : i == 1 ? A[p][1].y : i == 2 ? A[p][1].z : A[p][1].w;
+        const uint32_t a2 = i == 0 ? A[p][2].x : i == 1 ? A[p][2].y : i == 2 ? A[p][2].z : A[p][2].w;
+        const uint32_t a3 = i == 0 ? A[p][3].x : i == 1 ? A[p][3].y : i == 2 ? A[p][3].z : A[p][3].w;
+        s0 = dot4((al[i] & kLo4) | ((hl[i] << 4) & kHi2), a0, s0);
+        s1 = dot4((bl[i] & kLo4) | ((hl[i] << 2) & kHi2), a1, s1);
+        s2 = dot4(((al[i] >> 4) & kLo4) | (hl[i] & kHi2), a2, s2);
+        s3 = dot4(((bl[i] >> 4) & kLo4) | ((hl[i] >> 2) & kHi2), a3, s3);
+      }
+      const int sc0 = static_cast<int8_t>((SC[p].x >> (8 * kk)) & 0xFF);
+      const int sc1 = static_cast<int8_t>((SC[p].x >> (16 + 8 * kk)) & 0xFF);
+      const int sc2 = static_cast<int8_t>((SC[p].y >> (8 * kk)) & 0xFF);
+      const int sc3 = static_cast<int8_t>((SC[p].y >> (16 + 8 * kk)) & 0xFF);
+      const int part = mad24(sc0, s0 - BS[p].x, mad24(sc1, s1 - BS[p].y,
+                             mad24(sc2, s2 - BS[p].z, __mul24(sc3, s3 - BS[p].w))));
+      const int S = quad_sum(part);
+      const float cb = (DX[p] * f16_to_f32(D[p])) * static_cast<float>(S);
+      acc += (pos == 0) ? cb : 0.0f;
+      if constexpr (SUMS) {
+        if (pos == 0) sums[static_cast<size_t>(row) * nb + sb] = S;
+      }
+    }
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+// Q8_0 x Q8_0 and Q4_0 x Q8_0, register-resident activations: lane b of pass P
+// holds the 32 codes, d and (for Q4_0) the code sum of activation block P*64 + b.
+template <int NW, int NP, bool Q4, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q80_reg(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  constexpr int kWB = Q4 ? kQ4_0Bytes : kQ8_0Bytes;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * NW + wave_id();
+  const int nwaves = gridDim.x * NW;
+  const size_t rb = static_cast<size_t>(nb) * kWB;
+
+  uint4 A0[NP], A1[NP];
+  float DX[NP];
+  int ASUM[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint8_t* a = xq + static_cast<uint32_t>(min(p * 64 + lane, nb - 1) * kQ8_0Bytes);
+    DX[p] = f16_to_f32(*reinterpret_cast<const uint16_t*>(a));
+    A0[p] = load_u2<uint4>(a + 2);
+    A1[p] = load_u2<uint4>(a + 18);
+    int sa = 0;
+    if constexpr (Q4) {
+      sa = dot4(kOnes, A0[p].x, sa);
+      sa = dot4(kOnes, A0[p].y, sa);
+      sa = dot4(kOnes, A0[p].z, sa);
+      sa = dot4(kOnes, A0[p].w, sa);
+      sa = dot4(kOnes, A1[p].x, sa);
+      sa = dot4(kOnes, A1[p].y, sa);
+      sa = dot4(kOnes, A1[p].z, sa);
+      sa = dot4(kOnes, A1[p].w, sa);
+    }
+    ASUM[p] = 8 * sa;
+  }
+
+  for (int row = wave; row < n_out; row += nwaves) {
+    const uint8_t* wrow = W + static_cast<size_t>(row) * rb;
+    uint4 Q0[NP], Q1[NP];
+    uint32_t D[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 64 + lane, nb - 1) * kWB);
+      D[p] = *reinterpret_cast<const uint16_t*>(q);
+      Q0[p] = load_u2<uint4>(q + 2);
+      if constexpr (!Q4) Q1[p] = load_u2<uint4>(q + 18);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int b = p * 64 + lane;
+      if (b >= nb) continue;
+      int s = 0;
+      if constexpr (Q4) {
+        const uint4 q = Q0[p];
+        s = dot4(q.x & kLo4, A0[p].x, s);
+        s = dot4(q.y & kLo4, A0[p].y, s);
+        s = dot4(q.z & kLo4, A0[p].z, s);
+        s = dot4(q.w & kLo4, A0[p].w, s);
+        s = dot4((q.x >> 4) & kLo4, A1[p].x, s);
+        s = dot4((q.y >> 4) & kLo4, A1[p].y, s);
+        s = dot4((q.z >> 4) & kLo4, A1[p].z, s);
+        s = dot4((q.w >> 4) & kLo4, A1[p].w, s);
+        s -= ASUM[p];  // nibbles are stored as q + 8
+      } else {
+        s = dot4(Q0[p].x, A0[p].x, s);
+        s = dot4(Q0[p].y, A0[p].y, s);
+        s = dot4(Q0[p].z, A0[p].z, s);
+        s = dot4(Q0[p].w, A0[p].w, s);
+        s = dot4(Q1[p].x, A1[p].x, s);
+        s = dot4(Q1[p].y, A1[p].y, s);
+        s = dot4(Q1[p].z, A1[p].z, s);
+        s = dot4(Q1[p].w, A1[p].w, s);
+      }
+      acc += static_cast<float>(s) * (f16_to_f32(D[p]) * DX[p]);
+      if constexpr (SUMS) sums[static_cast<size_t>(row) * nb + b] = s;
+    }
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+template <int NW, typename K>
 hipError_t launch(K kernel, int64_t n_out, int64_t lds_bytes, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1, const uint8_t* W, int nb, const uint8_t* xq, float* y,
                   int32_t* sums) {
-  const unsigned grid = static_cast<unsigned>((n_out + kWaves - 1) / kWaves);
+  const unsigned grid = static_cast<unsigned>((n_out + NW - 1) / NW);
   const int n = static_cast<int>(n_out);
   if (e0 != nullptr || e1 != nullptr) {
-    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), static_cast<uint32_t>(lds_bytes),
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), static_cast<uint32_t>(lds_bytes),
                           s, e0, e1, 0, W, n, nb, xq, y, sums);
   } else {
-    kernel<<<grid, kWaves * 64, lds_bytes, s>>>(W, n, nb, xq, y, sums);
+    kernel<<<grid, NW * 64, lds_bytes, s>>>(W, n, nb, xq, y, sums);
+  }
+  return hipGetLastError();
+}
+
+template <int NW, typename K>
+hipError_t launch_rows(K kernel, int64_t n_out, int rpw, int max_waves, hipStream_t s,
+                       hipEvent_t e0, hipEvent_t e1, const uint8_t* W, int nb, const uint8_t* xq,
+                       float* y, int32_t* sums) {
+  const int64_t groups = (n_out + rpw - 1) / rpw;
+  const int64_t waves = groups < max_waves ? groups : max_waves;
+  const unsigned grid = static_cast<unsigned>((waves + NW - 1) / NW);
+  const int n = static_cast<int>(n_out);
+  if (e0 != nullptr || e1 != nullptr) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), 0, s, e0, e1, 0, W, n, nb, xq, y, sums);
+  } else {
+    kernel<<<grid, NW * 64, 0, s>>>(W, n, nb, xq, y, sums);
   }
   return hipGetLastError();
 }
@@ -599,36 +897,52 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
   }
 }
 
+// Wavefronts (rows) per workgroup of the GEMV launches.
+constexpr int kWaves = QK_GEMV_WAVES;
+
 hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in,
                        const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,
                        hipEvent_t e0, hipEvent_t e1) {
   if (n_out <= 0) return hipSuccess;
   const int64_t lds = gemv_lds_bytes(w_type, n_in);
-  const bool with_sums = sums != nullptr;
+  const bool S = sums != nullptr;
+  constexpr int MW = QK_MAX_WAVES;
+#define QK_ROWS(kern) launch_rows<4>(kern, n_out, 1, MW, s, e0, e1, W, nb, xq, y, sums)
+#define QK_LDS(kern) launch<kWaves>(kern, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
   switch (w_type) {
     case kQ4_K: {
       const int nb = static_cast<int>(n_in / 256);
-      return with_sums ? launch(gemv_q4_K_kernel<3, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
-                       : launch(gemv_q4_K_kernel<3, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+      const int passes = (nb + 15) / 16;
+      if (passes == 1) return S ? QK_ROWS((gemv_q4_K_reg<4, 1, 1, true>)) : QK_ROWS((gemv_q4_K_reg<4, 1, 1, false>));
+      if (passes == 2) return S ? QK_ROWS((gemv_q4_K_reg<4, 2, 1, true>)) : QK_ROWS((gemv_q4_K_reg<4, 2, 1, false>));
+      return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 3, true>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 3, false>));
     }
     case kQ6_K: {
       const int nb = static_cast<int>(n_in / 256);
-      return with_sums ? launch(gemv_q6_K_kernel<3, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
-                       : launch(gemv_q6_K_kernel<3, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+      const int passes = (nb + 15) / 16;
+      if (passes == 1) return S ? QK_ROWS((gemv_q6_K_reg<4, 1, true>)) : QK_ROWS((gemv_q6_K_reg<4, 1, false>));
+      if (passes == 2) return S ? QK_ROWS((gemv_q6_K_reg<4, 2, true>)) : QK_ROWS((gemv_q6_K_reg<4, 2, false>));
+      return S ? QK_LDS((gemv_q6_K_kernel<kWaves, 3, true>)) : QK_LDS((gemv_q6_K_kernel<kWaves, 3, false>));
     }
     case kQ8_0: {
       const int nb = static_cast<int>(n_in / 32);
-      return with_sums ? launch(gemv_q8_0_kernel<2, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
-                       : launch(gemv_q8_0_kernel<2, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+      const int passes = (nb + 63) / 64;
+      if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, false, true>)) : QK_ROWS((gemv_q80_reg<4, 1, false, false>));
+      if (passes == 2) return S ? QK_ROWS((gemv_q80_reg<4, 2, false, true>)) : QK_ROWS((gemv_q80_reg<4, 2, false, false>));
+      return S ? QK_LDS((gemv_q8_0_kernel<kWaves, 2, true>)) : QK_LDS((gemv_q8_0_kernel<kWaves, 2, false>));
     }
     case kQ4_0: {
       const int nb = static_cast<int>(n_in / 32);
-      return with_sums ? launch(gemv_q4_0_kernel<2, true>, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
-                       : launch(gemv_q4_0_kernel<2, false>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+      const int passes = (nb + 63) / 64;
+      if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, true, true>)) : QK_ROWS((gemv_q80_reg<4, 1, true, false>));
+      if (passes == 2) return S ? QK_ROWS((gemv_q80_reg<4, 2, true, true>)) : QK_ROWS((gemv_q80_reg<4, 2, true, false>));
+      return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, false>));
     }
     default:
       return hipErrorInvalidValue;
   }
+#undef QK_ROWS
+#undef QK_LDS
 }
 
 }  // namespace qk

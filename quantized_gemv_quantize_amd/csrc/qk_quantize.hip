@@ -31,8 +31,10 @@ __device__ __forceinline__ uint32_t pack4(int c0, int c1, int c2, int c3) {
          ((static_cast<uint32_t>(c2) & 0xFFu) << 16) | ((static_cast<uint32_t>(c3) & 0xFFu) << 24);
 }
 
+// Largest |x| of 4 values folded from 0, so NaN never wins (fmaxf returns the
+// other operand) and an all-NaN block gives 0, as the sequential definition does.
 __device__ __forceinline__ float abs_max4(float4 v) {
-  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  return fmaxf(fmaxf(fmaxf(fmaxf(0.0f, fabsf(v.x)), fabsf(v.y)), fabsf(v.z)), fabsf(v.w));
 }
 
 // 8 lanes per 32-element block, 4 consecutive elements per lane.
@@ -45,9 +47,7 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
   const bool valid = b < nblocks;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (valid) v = *reinterpret_cast<const float4*>(x + b * 32 + part * 4);
-  float amax = abs_max4(v);
-#pragma unroll
-  for (int off = 4; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
+  const float amax = max8(abs_max4(v));  // the 8 lanes of this block
   const float d = amax / 127.0f;
   const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
   if (!valid) return;

@@ -87,6 +87,9 @@ def _special_rows(n, rng):
     t[::32] = 127.0
     rows.append(t)
     rows.append(np.full(n, -3.25, np.float32))
+    allnan = rng.standard_normal(n).astype(np.float32)
+    allnan[:256] = np.nan                                         # whole blocks of NaN -> d = 0
+    rows.append(allnan)
     rows.append(np.float32(1.0) * (np.arange(n) % 256 - 128).astype(np.float32))
     return np.stack(rows)
 
@@ -236,6 +239,40 @@ def test_gemv_timed_matches_untimed(torch_cuda):
     e1.synchronize()
     assert e0.elapsed_time(e1) > 0
     assert torch_cuda.equal(y0, y1)
+
+
+def test_graph_capture_replays_match_eager(torch_cuda):
+    # quantize + GEMV captured into a HIP graph; several replays, with eager work
+    # and synchronizations between them, must each equal the eager result.
+    torch = torch_cuda
+    rng = np.random.default_rng(9)
+    cases = [(T4K, 64, 11008), (T4K, 300, 4096), (T6K, 70, 4096), (T8_0, 50, 4096), (T4_0, 33, 1024)]
+    bufs = []
+    for t, n_out, n_in in cases:
+        W = dev(torch, weights(rng, t, n_out, n_in))
+        x = dev(torch, rng.standard_normal((1, n_in)).astype(np.float32))
+        at = qk.qk_act_type(t)
+        xq = torch.empty((1, qk.qk_row_bytes(at, n_in)), dtype=torch.uint8, device="cuda")
+        y = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
+        bufs.append((t, n_out, n_in, W, x, at, xq, y))
+    want = []
+    for t, n_out, n_in, W, x, at, xq, y in bufs:
+        qk.qk_quantize_act(at, x, xq)
+        want.append(qk.qk_gemv(t, W, n_out, n_in, xq, 1).clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t, n_out, n_in, W, x, at, xq, y in bufs:
+            qk.qk_quantize_act(at, x, xq)
+            qk.qk_gemv(t, W, n_out, n_in, xq, 1, y)
+    for rep in range(4):
+        for b in bufs:
+            b[7].fill_(float("nan"))
+            b[6].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (t, n_out, n_in, W, x, at, xq, y), w in zip(bufs, want):
+            assert torch.equal(y, w), (rep, t, n_out, n_in)
 
 
 def test_native_library_is_the_one_loaded(torch_cuda):
