@@ -285,6 +285,61 @@ __device__ __forceinline__ int2 q4K_chunk(const uint4& q0, const uint4& q1, cons
   return make_int2(mad24(sc_lo, slo, __mul24(sc_hi, shi)), mad24(m_lo, asum.x, __mul24(m_hi, asum.y)));
 }
 
+// Image staging of a Q8_K activation row: the row's bytes are copied to LDS
+// unchanged (16-byte chunks: one dwordx4 load and one ds_write_b128 each), so the
+// copy needs almost no index arithmetic; readers address the image directly
+// (block b at 292 b: d at +0, codes at +4, bsums at +260; 4-byte aligned fields).
+// As with the other staging, loads go out before the weight loads, and chunk
+// indices are clamped so every lane issues the same loads.
+constexpr int kImgChunks = 4;
+
+struct ImageQ8K {
+  uint4 v[kImgChunks];
+  uint32_t tail;
+};
+
+template <int NT>
+__device__ __forceinline__ void image_load_q8K(ImageQ8K& st, const uint8_t* __restrict__ xq, int nb) {
+  const int bytes = nb * kQ8_KBytes;
+  const int nch = bytes >> 4;
+#pragma unroll
+  for (int i = 0; i < kImgChunks; ++i) {
+    const int k = min(static_cast<int>(threadIdx.x) + i * NT, nch - 1);
+    st.v[i] = load_a4<uint4>(xq + static_cast<uint32_t>(16 * k));
+  }
+  // the last (bytes mod 16) / 4 dwords
+  const int ntail = (bytes & 15) >> 2;
+  const int t = min(static_cast<int>(threadIdx.x), max(ntail - 1, 0));
+  st.tail = ntail ? *reinterpret_cast<const uint32_t*>(xq + static_cast<uint32_t>(16 * nch + 4 * t)) : 0u;
+}
+
+template <int NT>
+__device__ __forceinline__ void image_place_q8K(uint8_t* lds, const ImageQ8K& st,
+                                                const uint8_t* __restrict__ xq, int nb) {
+  const int bytes = nb * kQ8_KBytes;
+  const int nch = bytes >> 4;
+#pragma unroll
+  for (int i = 0; i < kImgChunks; ++i) {
+    const int k = min(static_cast<int>(threadIdx.x) + i * NT, nch - 1);
+    *reinterpret_cast<uint4*>(lds + 16 * k) = st.v[i];
+  }
+  const int ntail = (bytes & 15) >> 2;
+  if (static_cast<int>(threadIdx.x) < ntail) {
+    *reinterpret_cast<uint32_t*>(lds + 16 * nch + 4 * threadIdx.x) = st.tail;
+  }
+  for (int k = static_cast<int>(threadIdx.x) + kImgChunks * NT; k < nch; k += NT) {
+    *reinterpret_cast<uint4*>(lds + 16 * k) = load_a4<uint4>(xq + static_cast<uint32_t>(16 * k));
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_a4(const uint8_t* p) {  // 4-byte aligned LDS field
+  const uint32_t* p4 = reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));
+  T v;
+  __builtin_memcpy(&v, p4, sizeof(T));
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Q4_K x Q8_K.  Lane (u = lane >> 2, c = lane & 3) of pass `it` handles 64-element
 // chunk c of superblock it*16 + u: qs[32c .. 32c+31] hold sub-block 2c in their low
@@ -315,25 +370,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
       Q1[j] = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
     }
   };
-  const LayoutQ4K L(nb);
-  StagedQ8K st;
-  stage_load_q8K<NW * 64>(st, xq, nb);
-  sched_fence();
-#ifdef QK_ACT_FIRST
-  stage_place_q8K<NW * 64>(lds, L, st, xq, nb, place_piece_q4K, place_small_q4K);
+  ImageQ8K st;
+  image_load_q8K<NW * 64>(st, xq, nb);
   sched_fence();
   issue(0);
-  __syncthreads();
-#else
-  issue(0);
   sched_fence();
-  stage_place_q8K<NW * 64>(lds, L, st, xq, nb, place_piece_q4K, place_small_q4K);
+  image_place_q8K<NW * 64>(lds, st, xq, nb);
   __syncthreads();
-#endif
 
-  const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
-  const int32_t* sA = reinterpret_cast<const int32_t*>(lds + L.off_s);
-  const int sw = (c >> 1) << 1;  // piece XOR of chunk c
   const int sh = (c & 1) * 16;   // byte pair of this chunk's two sub-blocks
   const uint32_t hi_mask = (c & 2) ? 0xFFFFFFFFu : 0u;
   float acc = 0.0f;
@@ -344,13 +388,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
     for (int j = 0; j < UNR; ++j) {
       const int sb = (p0 + j) * 16 + u;
       if (!row_ok || sb >= nb) continue;  // uniform over the 4 lanes of a superblock
-      const uint8_t* ap = lds + sb * LayoutQ4K::kStride + 64 * c;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(ap + 16 * (0 ^ sw));
-      const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 16 * (1 ^ sw));
-      const uint4 a2 = *reinterpret_cast<const uint4*>(ap + 16 * (2 ^ sw));
-      const uint4 a3 = *reinterpret_cast<const uint4*>(ap + 16 * (3 ^ sw));
-      const int2 asum = *reinterpret_cast<const int2*>(sA + sb * 8 + 2 * c);
-      const float dx = dA[sb];
+      const uint8_t* blk = lds + sb * kQ8_KBytes;
+      const uint8_t* ap = blk + 4 + 64 * c;
+      const uint4 a0 = lds_a4<uint4>(ap);
+      const uint4 a1 = lds_a4<uint4>(ap + 16);
+      const uint4 a2 = lds_a4<uint4>(ap + 32);
+      const uint4 a3 = lds_a4<uint4>(ap + 48);
+      const uint2 bsw = lds_a4<uint2>(blk + 260 + 8 * c);  // bsums 4c .. 4c+3
+      const int2 asum = make_int2(sext16_lo(bsw.x) + sext16_hi(bsw.x), sext16_lo(bsw.y) + sext16_hi(bsw.y));
+      const float dx = lds_a4<float>(blk);
       const uint4 h = H[j];
       const int2 part = q4K_chunk(Q0[j], Q1[j], h, a0, a1, a2, a3, asum, hi_mask, sh);
       const int sq = quad_sum(part.x);
@@ -406,17 +452,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
       D[j] = *reinterpret_cast<const uint16_t*>(p + 208);
     }
   };
-  const LayoutQ6K L(nb);
-  StagedQ8K st;
-  stage_load_q8K<NW * 64>(st, xq, nb);
+  ImageQ8K st;
+  image_load_q8K<NW * 64>(st, xq, nb);
   sched_fence();
   issue(0);
   sched_fence();
-  stage_place_q8K<NW * 64>(lds, L, st, xq, nb, place_piece_q6K, place_small_q6K);
+  image_place_q8K<NW * 64>(lds, st, xq, nb);
   __syncthreads();
 
-  const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
-  const int32_t* sA = reinterpret_cast<const int32_t*>(lds + L.off_s);
   float acc = 0.0f;
 
   for (int p0 = 0; p0 < passes; p0 += UNR) {
@@ -425,14 +468,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
     for (int j = 0; j < UNR; ++j) {
       const int sb = (p0 + j) * 16 + u;
       if (!row_ok || sb >= nb) continue;
-      const uint8_t* ap = lds + sb * LayoutQ6K::kStride + 128 * hh;
+      const uint8_t* blk = lds + sb * kQ8_KBytes;
       uint4 a[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        a[g] = *reinterpret_cast<const uint4*>(ap + 16 * ((2 * g + kk) ^ (4 * hh)));
-      }
-      const int4 bs = *reinterpret_cast<const int4*>(sA + sb * 16 + 8 * hh + 4 * kk);
-      const float dx = dA[sb];
+      for (int g = 0; g < 4; ++g) a[g] = lds_a4<uint4>(blk + 4 + 128 * hh + 32 * g + 16 * kk);
+      const uint4 bw = lds_a4<uint4>(blk + 260 + 16 * hh);  // bsums 8h .. 8h+7
+      const int4 bs = make_int4(32 * (kk ? sext16_hi(bw.x) : sext16_lo(bw.x)),
+                                32 * (kk ? sext16_hi(bw.y) : sext16_lo(bw.y)),
+                                32 * (kk ? sext16_hi(bw.z) : sext16_lo(bw.z)),
+                                32 * (kk ? sext16_hi(bw.w) : sext16_lo(bw.w)));
+      const float dx = lds_a4<float>(blk);
       const uint32_t al[4] = {A[j].x, A[j].y, A[j].z, A[j].w};
       const uint32_t bl[4] = {B[j].x, B[j].y, B[j].z, B[j].w};
       const uint32_t hl[4] = {QH[j].x, QH[j].y, QH[j].z, QH[j].w};
@@ -889,8 +934,8 @@ hipError_t launch_rows(K kernel, int64_t n_out, int rpw, int max_waves, hipStrea
 
 int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
   switch (w_type) {
-    case kQ4_K: return LayoutQ4K(n_in / 256).bytes;
-    case kQ6_K: return LayoutQ6K(n_in / 256).bytes;
+    case kQ4_K:
+    case kQ6_K: return align16(n_in / 256 * kQ8_KBytes);
     case kQ8_0:
     case kQ4_0: return LayoutQ80(n_in / 32).bytes;
     default: return -1;
@@ -928,14 +973,12 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
       const int nb = static_cast<int>(n_in / 32);
       const int passes = (nb + 63) / 64;
       if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, false, true>)) : QK_ROWS((gemv_q80_reg<4, 1, false, false>));
-      if (passes == 2) return S ? QK_ROWS((gemv_q80_reg<4, 2, false, true>)) : QK_ROWS((gemv_q80_reg<4, 2, false, false>));
       return S ? QK_LDS((gemv_q8_0_kernel<kWaves, 2, true>)) : QK_LDS((gemv_q8_0_kernel<kWaves, 2, false>));
     }
     case kQ4_0: {
       const int nb = static_cast<int>(n_in / 32);
       const int passes = (nb + 63) / 64;
       if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, true, true>)) : QK_ROWS((gemv_q80_reg<4, 1, true, false>));
-      if (passes == 2) return S ? QK_ROWS((gemv_q80_reg<4, 2, true, true>)) : QK_ROWS((gemv_q80_reg<4, 2, true, false>));
       return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, false>));
     }
     default:
