@@ -42,6 +42,21 @@ int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void
   const int64_t nb = n_in / qk_block_elems(w_type);
   const int k = (w_type == QK_TYPE_Q4_K) ? 2 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w_type == QK_TYPE_Q4_K && ncols > 1) {
+    // several columns: one pass over W per group of up to 64 columns (matrix cores)
+    for (int64_t c = 0; c < ncols; c += qk::kGemmMaxCols) {
+      const int64_t nc = (ncols - c < qk::kGemmMaxCols) ? ncols - c : qk::kGemmMaxCols;
+      const uint8_t* xc = static_cast<const uint8_t*>(xq) + c * xrow;
+      float* yc = y ? y + c * n_out : nullptr;
+      int32_t* sc = sums ? sums + c * n_out * nb * k : nullptr;
+      hipEvent_t e0 = (c == 0) ? static_cast<hipEvent_t>(ev0) : nullptr;
+      hipEvent_t e1 = (c + nc == ncols) ? static_cast<hipEvent_t>(ev1) : nullptr;
+      const hipError_t e = qk::launch_gemm_q4K(static_cast<const uint8_t*>(W), n_out, n_in, xc, nc,
+                                               yc, sc, s, e0, e1);
+      if (e != hipSuccess) return QK_E_DEVICE;
+    }
+    return QK_OK;
+  }
   for (int64_t c = 0; c < ncols; ++c) {
     const uint8_t* xc = static_cast<const uint8_t*>(xq) + c * xrow;
     float* yc = y ? y + c * n_out : nullptr;

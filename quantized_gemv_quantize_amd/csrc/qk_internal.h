@@ -21,6 +21,14 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
                        const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,
                        hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// Q4_K x Q8_K over 2..64 activation columns at once (int8 MFMA).  xq holds ncols
+// consecutive Q8_K rows, y is [ncols][n_out], sums (when non-null) is
+// [ncols][n_out][n_in / 256][2].
+hipError_t launch_gemm_q4K(const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_t* xq,
+                           int64_t ncols, float* y, int32_t* sums, hipStream_t s,
+                           hipEvent_t ev_start, hipEvent_t ev_stop);
+constexpr int64_t kGemmMaxCols = 64;
+
 // Bytes of dynamic LDS a GEMV over rows of n_in elements needs.
 int64_t gemv_lds_bytes(int w_type, int64_t n_in);
 constexpr int64_t kMaxLdsBytes = 65536;

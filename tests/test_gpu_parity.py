@@ -190,6 +190,54 @@ def test_gemv_block_sums_and_y(torch_cuda, t):
             assert_y(y, y_o, l1, f"type {t} {n_out}x{n_in} ncols {ncols}")
 
 
+# Q4_K with several activation columns runs on the matrix cores (16-token tiles,
+# up to 64 columns per pass): ragged row counts, every tile count and the
+# column counts around each tile and pass boundary.
+BATCHED = [(1, 256, 2), (17, 512, 16), (33, 1024, 17), (45, 4096, 33), (70, 2304, 48),
+           (31, 11008, 64), (50, 768, 65), (21, 4352, 130), (129, 256, 7)]
+
+
+@pytest.mark.parametrize("n_out,n_in,ncols", BATCHED)
+def test_batched_q4_K_block_sums_and_y(torch_cuda, n_out, n_in, ncols):
+    say("batched Q4_K", n_out, n_in, ncols)
+    rng = np.random.default_rng(n_out * 7 + ncols)
+    W = synth.q4_K_blocks(rng, n_out, n_in)
+    X = rng.standard_normal((ncols, n_in)).astype(np.float32)
+    X[ncols // 2] = 0.0                      # an all-zero column: d = 0, codes 0
+    xq = orc.quantize(T8K, X)
+    Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+    sums = host(qk.qk_gemv_block_sums(T4K, Wd, n_out, n_in, xd, ncols))
+    want = _oracle_sums(T4K, W, xq, n_out, n_in, ncols)
+    assert np.array_equal(sums, want.reshape(sums.shape))
+    y = host(qk.qk_gemv(T4K, Wd, n_out, n_in, xd, ncols))
+    y_o, l1 = orc.gemv(T4K, W, n_out, n_in, xq, ncols)
+    assert_y(y, y_o, l1, f"batched Q4_K {n_out}x{n_in} ncols {ncols}")
+    assert not y[ncols // 2].any()
+
+
+def test_batched_q4_K_extreme_codes(torch_cuda):
+    # every nibble 15, every 6-bit scale and min 63, activations at +-127: the
+    # largest integer sums the format allows, on both MFMA products
+    say("batched Q4_K extreme codes")
+    rng = np.random.default_rng(77)
+    n_out, n_in, ncols = 40, 1024, 20
+    W = synth.q4_K_blocks(rng, n_out, n_in).reshape(n_out, n_in // 256, 144)
+    W[:, :, 4:] = 0xFF
+    W = W.reshape(n_out, -1)
+    X = np.where(rng.integers(0, 2, (ncols, n_in)) == 1, 1.0, -1.0).astype(np.float32)
+    X[1] = 1.0
+    X[2] = -1.0
+    xq = orc.quantize(T8K, X)
+    Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+    sums = host(qk.qk_gemv_block_sums(T4K, Wd, n_out, n_in, xd, ncols))
+    want = _oracle_sums(T4K, W, xq, n_out, n_in, ncols)
+    assert np.array_equal(sums, want.reshape(sums.shape))
+    assert np.abs(want).max() == 256 * 15 * 63 * 127
+    y = host(qk.qk_gemv(T4K, Wd, n_out, n_in, xd, ncols))
+    y_o, l1 = orc.gemv(T4K, W, n_out, n_in, xq, ncols)
+    assert_y(y, y_o, l1, "batched Q4_K extreme codes")
+
+
 def test_gemv_max_row_length(torch_cuda):
     rng = np.random.default_rng(31)
     for t in (T4K, T6K, T8_0, T4_0):
@@ -246,33 +294,34 @@ def test_graph_capture_replays_match_eager(torch_cuda):
     # and synchronizations between them, must each equal the eager result.
     torch = torch_cuda
     rng = np.random.default_rng(9)
-    cases = [(T4K, 64, 11008), (T4K, 300, 4096), (T6K, 70, 4096), (T8_0, 50, 4096), (T4_0, 33, 1024)]
+    cases = [(T4K, 64, 11008, 1), (T4K, 300, 4096, 1), (T6K, 70, 4096, 1), (T8_0, 50, 4096, 1),
+             (T4_0, 33, 1024, 1), (T4K, 200, 4096, 16), (T4K, 90, 2048, 64)]
     bufs = []
-    for t, n_out, n_in in cases:
+    for t, n_out, n_in, nc in cases:
         W = dev(torch, weights(rng, t, n_out, n_in))
-        x = dev(torch, rng.standard_normal((1, n_in)).astype(np.float32))
+        x = dev(torch, rng.standard_normal((nc, n_in)).astype(np.float32))
         at = qk.qk_act_type(t)
-        xq = torch.empty((1, qk.qk_row_bytes(at, n_in)), dtype=torch.uint8, device="cuda")
-        y = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
-        bufs.append((t, n_out, n_in, W, x, at, xq, y))
+        xq = torch.empty((nc, qk.qk_row_bytes(at, n_in)), dtype=torch.uint8, device="cuda")
+        y = torch.empty((nc, n_out), dtype=torch.float32, device="cuda")
+        bufs.append((t, n_out, n_in, nc, W, x, at, xq, y))
     want = []
-    for t, n_out, n_in, W, x, at, xq, y in bufs:
+    for t, n_out, n_in, nc, W, x, at, xq, y in bufs:
         qk.qk_quantize_act(at, x, xq)
-        want.append(qk.qk_gemv(t, W, n_out, n_in, xq, 1).clone())
+        want.append(qk.qk_gemv(t, W, n_out, n_in, xq, nc).clone())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for t, n_out, n_in, W, x, at, xq, y in bufs:
+        for t, n_out, n_in, nc, W, x, at, xq, y in bufs:
             qk.qk_quantize_act(at, x, xq)
-            qk.qk_gemv(t, W, n_out, n_in, xq, 1, y)
+            qk.qk_gemv(t, W, n_out, n_in, xq, nc, y)
     for rep in range(4):
         for b in bufs:
-            b[7].fill_(float("nan"))
-            b[6].zero_()
+            b[8].fill_(float("nan"))
+            b[7].zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for (t, n_out, n_in, W, x, at, xq, y), w in zip(bufs, want):
-            assert torch.equal(y, w), (rep, t, n_out, n_in)
+        for (t, n_out, n_in, nc, W, x, at, xq, y), w in zip(bufs, want):
+            assert torch.equal(y, w), (rep, t, n_out, n_in, nc)
 
 
 def test_native_library_is_the_one_loaded(torch_cuda):
