@@ -14,8 +14,17 @@ Prints ONE JSON line on stdout (details on stderr):
   cpu_baseline  the scalar C oracle on the host, single thread, on a bounded
              sample of the same workload
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Profiling helpers (no GPU use; they read rocprofv3 CSV output):
+  --summarize-trace DIR         per-kernel durations of a --kernel-trace --stats run
+  --summarize-pmc FDIR WDIR     HBM bytes per step from a FETCH_SIZE run and a
+                                WRITE_SIZE run, scaled by the copy kernel that
+                                --calibrate-copy adds to the profiled run
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +38,12 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 * 1024 * 1024
+CALIB_BYTES = 256 * 1024 * 1024  # the copy kernel reads and writes this much per dispatch
+CSRC = os.path.join(ROOT, "quantized_gemv_quantize_amd", "csrc")
+# sources of each kernel family; a recorded HBM traffic figure is used only while
+# these files are unchanged since the counters were taken
+KERNEL_SOURCES = {"gemv": ["qk_gemv.hip", "qk_device.h", "qk_internal.h"],
+                  "gemm": ["qk_gemm.hip", "qk_device.h", "qk_internal.h"]}
 METRIC = "quantized GEMV weight GB/s and % of HBM peak (Q4_K/Q6_K/Q8_0, batch 1)"
 
 
@@ -142,6 +157,144 @@ def cpu_baseline(name, wl, inputs, seconds):
             "sample": f"{desc}; quantize + GEMV repeated {reps}x in {dt:.1f} s, single thread"}
 
 
+def kernel_family(workload):
+    return "gemm" if workload.startswith("q4_K_batched") else "gemv"
+
+
+def source_hash(family):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"{kernel_family(workload)}_{workload}_pmc_traffic.txt")
+
+
+def recorded_traffic(workload):
+    """HBM bytes per step of the GEMV kernels from the committed counter summary,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash(kernel_family(workload)):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_step"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(wl, qk):
+    """Weights + activation blocks + f32 outputs of the GEMV launches of one step."""
+    total = 0
+    for _, wt, n_out, n_in, akey in wl["gemvs"]:
+        at, n, ncols = wl["acts"][akey]
+        total += qk.qk_row_bytes(wt, n_in) * n_out + qk.qk_row_bytes(at, n) * ncols + 4 * n_out * ncols
+    return total
+
+
+def _short(name):
+    name = name.replace("qk::(anonymous namespace)::", "")
+    return name.split("(")[0] if name.startswith(("void gemv", "void gemm", "gemv", "gemm", "quantize",
+                                                      "void quantize", "dequant", "void dequant")) else name[:90]
+
+
+def _is_gemv(name):
+    return "qk::" in name and ("gemv_" in name or "gemm_" in name)
+
+
+def summarize_trace(d):
+    """Per-kernel durations from a rocprofv3 --kernel-trace --stats output directory."""
+    stats = glob.glob(os.path.join(d, "*kernel_stats.csv"))
+    trace = glob.glob(os.path.join(d, "*kernel_trace.csv"))
+    if stats:
+        print("rocprofv3 --stats (library kernels):")
+        print(f"  {'kernel':60s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}")
+        for r in csv.DictReader(open(stats[0])):
+            if "qk::" in r["Name"]:
+                print(f"  {_short(r['Name']):60s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.3f} "
+                      f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
+    if trace:
+        rows = [r for r in csv.DictReader(open(trace[0])) if "qk::" in r["Kernel_Name"]]
+        names = sorted({r["Kernel_Name"] for r in rows})
+        print("per-dispatch trace, split into back-to-back runs (gaps > 1 ms):")
+        for nm in names:
+            rr = sorted((r for r in rows if r["Kernel_Name"] == nm), key=lambda r: int(r["Start_Timestamp"]))
+            dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rr]
+            runs, cur = [], [dur[0]]
+            for i in range(1, len(rr)):
+                if int(rr[i]["Start_Timestamp"]) - int(rr[i - 1]["End_Timestamp"]) > 1_000_000:
+                    runs.append(cur)
+                    cur = []
+                cur.append(dur[i])
+            runs.append(cur)
+            print(f"  {_short(nm)}")
+            for r in runs:
+                print(f"    {len(r):5d} dispatches: mean {np.mean(r):8.3f} us  median {np.median(r):8.3f}"
+                      f"  p10 {np.percentile(r, 10):8.3f}  p90 {np.percentile(r, 90):8.3f}")
+
+
+def _counter_means(d):
+    """Kernel name -> (dispatches, mean counter value per dispatch) of a --pmc run."""
+    files = glob.glob(os.path.join(d, "*counter_collection.csv"))
+    if not files:
+        sys.exit(f"no counter_collection.csv under {d}")
+    acc = {}
+    for r in csv.DictReader(open(files[0])):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    per = {}
+    for (nm, _), v in acc.items():
+        per.setdefault(nm, []).append(v)
+    return {nm: (len(v), float(np.mean(v)), float(np.sum(v))) for nm, v in per.items()}
+
+
+def summarize_pmc(fdir, wdir, workload):
+    """HBM bytes per step of the workload's GEMV kernels, from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for
+    the calibration copy kernel (CALIB_BYTES read + CALIB_BYTES written)."""
+    import quantized_gemv_quantize_amd as qk  # constants only; the library is not loaded
+    wl = workloads(qk)[workload]
+    n_g = len(wl["gemvs"])
+    out = {}
+    for tag, d in (("FETCH_SIZE", fdir), ("WRITE_SIZE", wdir)):
+        m = _counter_means(d)
+        calib = [v for nm, v in m.items() if "neg" in nm.lower() and "qk::" not in nm]
+        if not calib:
+            sys.exit(f"{tag}: no calibration copy kernel in {d} (run bench.py with --calibrate-copy)")
+        c_n, c_mean, _ = calib[0]
+        factor = CALIB_BYTES / (c_mean * 1024.0)
+        g = {nm: v for nm, v in m.items() if _is_gemv(nm)}
+        disp = sum(v[0] for v in g.values())
+        steps = disp / n_g
+        per_step_kib = sum(v[2] for v in g.values()) / steps
+        out[tag] = (factor, per_step_kib, c_mean, c_n, g)
+    alg = algorithmic_bytes(wl, qk)
+    fetch = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][1] * 1024.0
+    write = out["WRITE_SIZE"][0] * out["WRITE_SIZE"][1] * 1024.0
+    print(f"workload: {workload}")
+    print(f"kernel_family: {kernel_family(workload)}")
+    print(f"source_sha256: {source_hash(kernel_family(workload))}")
+    for tag in ("FETCH_SIZE", "WRITE_SIZE"):
+        factor, per_step, c_mean, c_n, g = out[tag]
+        print(f"{tag.lower()}_calibration: copy kernel {c_mean:.1f} KiB per dispatch over {c_n} dispatches "
+              f"for {CALIB_BYTES} bytes -> factor {factor:.4f}")
+        for nm, (n, mean, _) in sorted(g.items()):
+            print(f"  {_short(nm)}: {n} dispatches, mean {mean:.1f} KiB (raw)")
+        print(f"{tag.lower()}_bytes_per_step: {int(round(factor * per_step * 1024.0))}")
+    print(f"traffic_bytes_per_step: {int(round(fetch + write))}")
+    print(f"algorithmic_bytes_per_step: {alg}")
+    print(f"traffic_over_algorithmic: {(fetch + write) / alg:.4f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,7 +303,17 @@ def main():
     ap.add_argument("--workload", default="q4_K_decode_4096x11008")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB read + write kernel (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the GEMV library runs on a single MI355X, "
@@ -214,8 +377,10 @@ def main():
                 e0, e1 = evs[g]
                 qk.qk_gemv_timed(wt, mats[g], n_out, n_in, xq, ncols, ys[g], e0, e1)
 
+    tw = time.perf_counter()
     for k in range(args.warmup):
         step(k)
+    enqueue_ms_per_step = (time.perf_counter() - tw) * 1e3 / max(args.warmup, 1)
     torch.cuda.synchronize()
 
     # Region A - whole job.  The K steps are captured once into a HIP graph and
@@ -250,24 +415,36 @@ def main():
             e0.record(stream)
             e1.record(stream)
     torch.cuda.synchronize()
+    # A bounded spin kernel holds the stream while the host enqueues all K steps,
+    # so the GPU then runs them back to back as in the graph replay (an idle GPU
+    # between host launches would add a start-up cost to every kernel).
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(s0.elapsed_time(s1), 1e-3)
+    hold_ms = 4.0 * enqueue_ms_per_step * args.steps + 10.0  # profilers slow the enqueue
     e_start = torch.cuda.Event(enable_timing=True)
     e_stop = torch.cuda.Event(enable_timing=True)
+    hold_done = torch.cuda.Event()
+    torch.cuda._sleep(int(cycles_per_ms * hold_ms))
+    hold_done.record(stream)
     e_start.record(stream)
     for k in range(args.steps):
         step(args.warmup + k, ev[k])
     e_stop.record(stream)
+    backlog = not hold_done.query()  # still spinning: every step was queued in time
     torch.cuda.synchronize()
     eager_ms = e_start.elapsed_time(e_stop)
+    if not backlog:
+        log("[bench] warning: the stream hold ended before all steps were enqueued")
 
     kern_ms = np.array([[e0.elapsed_time(e1) for e0, e1 in per] for per in ev])  # [steps, n_g]
     gemv_ms_mean = kern_ms.sum(axis=1).mean()
 
-    # algorithmic bytes per GEMV launch: weights + activation blocks + f32 outputs
-    alg_bytes = 0
-    for _, wt, n_out, n_in, akey in wl["gemvs"]:
-        at, xf, xq = acts[akey]
-        ncols = xf.shape[0]
-        alg_bytes += qk.qk_row_bytes(wt, n_in) * n_out + xq.numel() + 4 * n_out * ncols
+    alg_bytes = algorithmic_bytes(wl, qk)
     achieved = alg_bytes / (gemv_ms_mean / 1e3) / 1e9
     per_kernel_us = {wl["gemvs"][g][0]: {"mean": round(float(kern_ms[:, g].mean() * 1e3), 3),
                                           "p10": round(float(np.percentile(kern_ms[:, g], 10) * 1e3), 3),
@@ -278,6 +455,14 @@ def main():
         f"({elapsed_ms / args.steps * 1e3:.2f} us/step, host wall {wall * 1e3:.1f} ms); "
         f"eager {eager_ms / args.steps * 1e3:.2f} us/step; GEMV kernel time per step "
         f"{gemv_ms_mean * 1e3:.2f} us; per kernel {per_kernel_us}")
+
+    if args.calibrate_copy:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -312,10 +497,13 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(args.workload),
         },
         "cpu_baseline": cpu,
         "detail": {"gemv_kernel_us_per_step": round(float(gemv_ms_mean * 1e3), 3),
+                   "kernel_timing": "HIP events of the kernel launches, steps run back to back "
+                                    "behind a stream hold" + ("" if backlog else " (hold ended early)"),
+                   "traffic_unit": "bytes per step (FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
                    "eager_us_per_step": round(eager_ms / args.steps * 1e3, 3),
                    "gemv_kernel_us": per_kernel_us,
                    "algorithmic_bytes_per_step_gemv": alg_bytes},
