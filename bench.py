@@ -43,7 +43,8 @@ CSRC = os.path.join(ROOT, "quantized_gemv_quantize_amd", "csrc")
 # sources of each kernel family; a recorded HBM traffic figure is used only while
 # these files are unchanged since the counters were taken
 KERNEL_SOURCES = {"gemv": ["qk_gemv.hip", "qk_device.h", "qk_internal.h"],
-                  "gemm": ["qk_gemm.hip", "qk_device.h", "qk_internal.h"]}
+                  "gemm": ["qk_gemm.hip", "qk_device.h", "qk_internal.h"],
+                  "dequant": ["qk_dequant.hip", "qk_device.h", "qk_internal.h"]}
 METRIC = "quantized GEMV weight GB/s and % of HBM peak (Q4_K/Q6_K/Q8_0, batch 1)"
 
 
@@ -78,6 +79,9 @@ def workloads(qk):
             "gemvs": [("W", T4K, 14336, 4096, "X")], "acts": {"X": (T8K, 4096, 16)}},
         "q4_K_batched_14336x4096_n64": {
             "gemvs": [("W", T4K, 14336, 4096, "X")], "acts": {"X": (T8K, 4096, 64)}},
+        # qk_dequantize_row of the whole Q6_K head matrix to f32 (no activations)
+        "q6_K_dequantize_32000x4096": {
+            "gemvs": [("W", T6K, 32000, 4096, None)], "acts": {}, "dequant": True},
     }
 
 
@@ -90,7 +94,7 @@ def host_inputs(name, qk):
         return synth.q4_gemv_4096x4096()
     if name == "ffn_7b_q4_K_q6_K":
         return synth.ffn_7b()
-    if name == "q6_K_head_32000x4096":
+    if name in ("q6_K_head_32000x4096", "q6_K_dequantize_32000x4096"):
         return synth.q6_K_head_32000x4096()
     if name.startswith("q4_K_batched"):
         d = synth.q4_K_batched_14336x4096()
@@ -137,6 +141,13 @@ def cpu_baseline(name, wl, inputs, seconds):
     sample_rows = {}
     t0 = time.perf_counter()
     while True:
+        if wl.get("dequant"):
+            for wname, wt, n_out, n_in, _ in wl["gemvs"]:
+                W = inputs[wname]
+                rows = min(n_out, max(1, int(4e6 // n_in)))
+                sample_rows[wname] = rows
+                orc.dequantize(wt, W[:rows], rows * n_in)
+                done_bytes += rows * W.shape[1] + 4 * rows * n_in
         for key, (at, n, ncols) in wl["acts"].items():
             x = inputs[key] if inputs[key].ndim == 2 else inputs[key][None, :]
             xq = orc.quantize(at, x[:ncols])
@@ -154,11 +165,14 @@ def cpu_baseline(name, wl, inputs, seconds):
     dt = time.perf_counter() - t0
     desc = ", ".join(f"{k}: first {r} rows" for k, r in sample_rows.items())
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{desc}; quantize + GEMV repeated {reps}x in {dt:.1f} s, single thread"}
+            "sample": f"{desc}; {'dequantize' if wl.get('dequant') else 'quantize + GEMV'} repeated "
+                      f"{reps}x in {dt:.1f} s, single thread"}
 
 
 def kernel_family(workload):
-    return "gemm" if workload.startswith("q4_K_batched") else "gemv"
+    if workload.startswith("q4_K_batched"):
+        return "gemm"
+    return "dequant" if "dequantize" in workload else "gemv"
 
 
 def source_hash(family):
@@ -193,22 +207,34 @@ def recorded_traffic(workload):
 
 
 def algorithmic_bytes(wl, qk):
-    """Weights + activation blocks + f32 outputs of the GEMV launches of one step."""
+    """Weights + activation blocks + f32 outputs of the GEMV launches of one step
+    (for a dequantize workload: the blocks read plus the f32 values written)."""
     total = 0
     for _, wt, n_out, n_in, akey in wl["gemvs"]:
+        if wl.get("dequant"):
+            total += qk.qk_row_bytes(wt, n_in) * n_out + 4 * n_out * n_in  # read blocks, write f32
+            continue
         at, n, ncols = wl["acts"][akey]
         total += qk.qk_row_bytes(wt, n_in) * n_out + qk.qk_row_bytes(at, n) * ncols + 4 * n_out * ncols
     return total
 
 
 def _short(name):
+    if _is_calib(name):
+        return f"copy kernel (torch.neg, {CALIB_BYTES >> 20} MiB read + write)"
     name = name.replace("qk::(anonymous namespace)::", "")
     return name.split("(")[0] if name.startswith(("void gemv", "void gemm", "gemv", "gemm", "quantize",
                                                       "void quantize", "dequant", "void dequant")) else name[:90]
 
 
-def _is_gemv(name):
-    return "qk::" in name and ("gemv_" in name or "gemm_" in name)
+def _is_calib(name):
+    """The --calibrate-copy kernel (torch.neg over CALIB_BYTES of f32)."""
+    return "qk::" not in name and "neg" in name.lower()
+
+
+def _is_family(name, family):
+    """Library kernels of one family: gemv_*, gemm_* or dequant_* (not quantize)."""
+    return "qk::" in name and f"{family}_" in name
 
 
 def summarize_trace(d):
@@ -219,11 +245,12 @@ def summarize_trace(d):
         print("rocprofv3 --stats (library kernels):")
         print(f"  {'kernel':60s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}")
         for r in csv.DictReader(open(stats[0])):
-            if "qk::" in r["Name"]:
+            if "qk::" in r["Name"] or _is_calib(r["Name"]):
                 print(f"  {_short(r['Name']):60s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:9.3f} "
                       f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f}")
     if trace:
-        rows = [r for r in csv.DictReader(open(trace[0])) if "qk::" in r["Kernel_Name"]]
+        rows = [r for r in csv.DictReader(open(trace[0]))
+                if "qk::" in r["Kernel_Name"] or _is_calib(r["Kernel_Name"])]
         names = sorted({r["Kernel_Name"] for r in rows})
         print("per-dispatch trace, split into back-to-back runs (gaps > 1 ms):")
         for nm in names:
@@ -267,12 +294,12 @@ def summarize_pmc(fdir, wdir, workload):
     out = {}
     for tag, d in (("FETCH_SIZE", fdir), ("WRITE_SIZE", wdir)):
         m = _counter_means(d)
-        calib = [v for nm, v in m.items() if "neg" in nm.lower() and "qk::" not in nm]
+        calib = [v for nm, v in m.items() if _is_calib(nm)]
         if not calib:
             sys.exit(f"{tag}: no calibration copy kernel in {d} (run bench.py with --calibrate-copy)")
         c_n, c_mean, _ = calib[0]
         factor = CALIB_BYTES / (c_mean * 1024.0)
-        g = {nm: v for nm, v in m.items() if _is_gemv(nm)}
+        g = {nm: v for nm, v in m.items() if _is_family(nm, kernel_family(workload))}
         disp = sum(v[0] for v in g.values())
         steps = disp / n_g
         per_step_kib = sum(v[2] for v in g.values()) / steps
@@ -356,8 +383,12 @@ def main():
         xf = torch.from_numpy(np.ascontiguousarray(x[:ncols])).cuda()
         xq = torch.empty((ncols, qk.qk_row_bytes(at, n)), dtype=torch.uint8, device="cuda")
         acts[key] = (at, xf, xq)
-    ys = [torch.empty((ncols_of(wl, akey), n_out), dtype=torch.float32, device="cuda")
-          for _, _, n_out, _, akey in wl["gemvs"]]
+    if wl.get("dequant"):
+        ys = [torch.empty((n_out * n_in,), dtype=torch.float32, device="cuda")
+              for _, _, n_out, n_in, _ in wl["gemvs"]]
+    else:
+        ys = [torch.empty((ncols_of(wl, akey), n_out), dtype=torch.float32, device="cuda")
+              for _, _, n_out, _, akey in wl["gemvs"]]
     torch.cuda.synchronize()
     log(f"[bench] {copies} weight copies x {step_w_bytes / 1e6:.2f} MB resident; "
         f"warmup {args.warmup}, steps {args.steps}")
@@ -369,6 +400,13 @@ def main():
         for key, (at, xf, xq) in acts.items():
             qk.qk_quantize_act(at, xf, xq)
         for g, (wname, wt, n_out, n_in, akey) in enumerate(wl["gemvs"]):
+            if wl.get("dequant"):
+                if evs is not None:
+                    evs[g][0].record(stream)
+                qk.qk_dequantize_row(wt, mats[g], n_out * n_in, ys[g])
+                if evs is not None:
+                    evs[g][1].record(stream)
+                continue
             xq = acts[akey][2]
             ncols = acts[akey][1].shape[0]
             if evs is None:
@@ -402,7 +440,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed_ms = t_start.elapsed_time(t_stop)
-    value = step_w_bytes * args.steps / (elapsed_ms / 1e3) / 1e9
+    # weight bytes per step; a dequantize workload counts the blocks read plus the f32 written
+    value_bytes = algorithmic_bytes(wl, qk) if wl.get("dequant") else step_w_bytes
+    value = value_bytes * args.steps / (elapsed_ms / 1e3) / 1e9
 
     # Region B - the same K steps launched one by one; each GEMV launch records
     # a start / stop event pair with its own kernel timestamps (HIP extended
@@ -486,8 +526,9 @@ def main():
         "config": {
             "workload": args.workload,
             "gemvs": [f"{qk.TYPE_NAMES[t]} {n_out}x{n_in}" for _, t, n_out, n_in, _ in wl["gemvs"]],
-            "batch": acts[first[4]][1].shape[0],
+            "batch": acts[first[4]][1].shape[0] if first[4] is not None else None,
             "weight_bytes_per_step": step_w_bytes,
+            "value_bytes_per_step": value_bytes,
             "weight_copies_rotated": copies,
             "parallelism": "single GPU",
         },

@@ -63,61 +63,94 @@ __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* __rest
   *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(q, d, 8);
 }
 
-// Q4_K: one wavefront per superblock, lane l -> elements 4l..4l+3.
+// Q4_K and Q6_K: one wavefront per kSB consecutive superblocks, lane l -> elements
+// 4l..4l+3 of each; every load of the kSB superblocks is issued before the first
+// store, and fewer, longer wavefronts keep the dispatcher out of the way.
+constexpr int kSB = 4;
+
+struct Q4KPart {
+  uint4 h;      // d, dmin, scales[12]
+  uint32_t w;   // the 4 qs bytes holding this lane's 4 nibbles
+};
+
 __global__ __launch_bounds__(256) void dequant_q4_K_kernel(const uint8_t* __restrict__ src,
                                                            float* __restrict__ dst,
                                                            int64_t nblocks) {
   const int lane = threadIdx.x & 63;
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (b >= nblocks) return;
-  const uint8_t* blk = src + b * kQ4_KBytes;
-  const uint4 h = *reinterpret_cast<const uint4*>(blk);  // d, dmin, scales[12]
-  const float d = f16_to_f32(h.x & 0xFFFF);
-  const float dmin = f16_to_f32(h.x >> 16);
+  const int64_t b0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kSB;
+  if (b0 >= nblocks) return;
   const int e0 = 4 * lane;
   const int j = e0 >> 5;   // sub-block
   const int c = e0 >> 6;   // 64-element chunk
   const int p = e0 & 63;   // position in the chunk
-  // get_scale_min_k4: sub-blocks 0-3 use the low 6 bits of bytes j and j+4; 4-7
-  // take the low / high nibble of byte j+4 and the top 2 bits of bytes j-4 / j.
-  const uint32_t s0 = h.y, s1 = h.z, s2 = h.w;
-  const uint32_t scw = (j < 4) ? (s0 & 0x3F3F3F3Fu) : ((s2 & kLo4) | ((s0 >> 2) & 0x30303030u));
-  const uint32_t mw = (j < 4) ? (s1 & 0x3F3F3F3Fu) : (((s2 >> 4) & kLo4) | ((s1 >> 2) & 0x30303030u));
-  const int sh = 8 * (j & 3);
-  const float sc = static_cast<float>((scw >> sh) & 0xFF);
-  const float mn = static_cast<float>((mw >> sh) & 0xFF);
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * c + (p & 31));
-  const uint32_t q = (p < 32) ? (w & kLo4) : ((w >> 4) & kLo4);
-  const float dsc = d * sc;
-  const float dm = dmin * mn;
-  float4 o;
-  o.x = dsc * static_cast<float>(q & 0xFF) - dm;
-  o.y = dsc * static_cast<float>((q >> 8) & 0xFF) - dm;
-  o.z = dsc * static_cast<float>((q >> 16) & 0xFF) - dm;
-  o.w = dsc * static_cast<float>(q >> 24) - dm;
-  *reinterpret_cast<float4*>(dst + b * 256 + e0) = o;
+  Q4KPart v[kSB];
+#pragma unroll
+  for (int k = 0; k < kSB; ++k) {
+    const uint8_t* blk = src + min(b0 + k, nblocks - 1) * kQ4_KBytes;
+    v[k].h = *reinterpret_cast<const uint4*>(blk);
+    v[k].w = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * c + (p & 31));
+  }
+#pragma unroll
+  for (int k = 0; k < kSB; ++k) {
+    if (b0 + k >= nblocks) break;  // uniform over the wavefront
+    const uint4 h = v[k].h;
+    const float d = f16_to_f32(h.x & 0xFFFF);
+    const float dmin = f16_to_f32(h.x >> 16);
+    // get_scale_min_k4: sub-blocks 0-3 use the low 6 bits of bytes j and j+4; 4-7
+    // take the low / high nibble of byte j+4 and the top 2 bits of bytes j-4 / j.
+    const uint32_t s0 = h.y, s1 = h.z, s2 = h.w;
+    const uint32_t scw = (j < 4) ? (s0 & 0x3F3F3F3Fu) : ((s2 & kLo4) | ((s0 >> 2) & 0x30303030u));
+    const uint32_t mw = (j < 4) ? (s1 & 0x3F3F3F3Fu) : (((s2 >> 4) & kLo4) | ((s1 >> 2) & 0x30303030u));
+    const int sh = 8 * (j & 3);
+    const float sc = static_cast<float>((scw >> sh) & 0xFF);
+    const float mn = static_cast<float>((mw >> sh) & 0xFF);
+    const uint32_t q = (p < 32) ? (v[k].w & kLo4) : ((v[k].w >> 4) & kLo4);
+    const float dsc = d * sc;
+    const float dm = dmin * mn;
+    float4 o;
+    o.x = dsc * static_cast<float>(q & 0xFF) - dm;
+    o.y = dsc * static_cast<float>((q >> 8) & 0xFF) - dm;
+    o.z = dsc * static_cast<float>((q >> 16) & 0xFF) - dm;
+    o.w = dsc * static_cast<float>(q >> 24) - dm;
+    *reinterpret_cast<float4*>(dst + (b0 + k) * 256 + e0) = o;
+  }
 }
 
-// Q6_K: one wavefront per superblock, lane l -> elements 4l..4l+3.
-// Element e: half h = e/128, r = e%128, group g = r/32, l = r%32; low 4 bits are
-// nibble (g < 2 ? low : high) of ql[64h + l + 32(g&1)], high 2 bits are
+// Q6_K: element e: half h = e/128, r = e%128, group g = r/32, l = r%32; low 4 bits
+// are nibble (g < 2 ? low : high) of ql[64h + l + 32(g&1)], high 2 bits are
 // (qh[32h + l] >> 2g) & 3.
+struct Q6KPart {
+  uint32_t wl, wh;  // ql and qh bytes of this lane's 4 elements
+  uint32_t dw;      // the f16 d (bytes 208-209)
+  int sc;           // the int8 scale of this lane's 16-element sub-block
+};
+
 __global__ __launch_bounds__(256) void dequant_q6_K_kernel(const uint8_t* __restrict__ src,
                                                            float* __restrict__ dst,
                                                            int64_t nblocks) {
   const int lane = threadIdx.x & 63;
-  const int64_t b = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (b >= nblocks) return;
-  const uint8_t* blk = src + b * kQ6_KBytes;
+  const int64_t b0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kSB;
+  if (b0 >= nblocks) return;
   const int e0 = 4 * lane;
   const int h = e0 >> 7, r = e0 & 127, g = r >> 5, l = r & 31;
-  const uint32_t wl = load_u2<uint32_t>(blk + 64 * h + l + 32 * (g & 1));
-  const uint32_t wh = load_u2<uint32_t>(blk + 128 + 32 * h + l);
-  const uint32_t lo = (g < 2) ? (wl & kLo4) : ((wl >> 4) & kLo4);
-  const uint32_t q = lo | (((wh >> (2 * g)) & 0x03030303u) << 4);
-  const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk + 208));
-  const float sc = static_cast<float>(static_cast<int8_t>(blk[192 + (e0 >> 4)]));
-  *reinterpret_cast<float4*>(dst + b * 256 + e0) = scale_bytes_signed(q, d * sc, 32);
+  Q6KPart v[kSB];
+#pragma unroll
+  for (int k = 0; k < kSB; ++k) {
+    const uint8_t* blk = src + min(b0 + k, nblocks - 1) * kQ6_KBytes;
+    v[k].wl = load_u2<uint32_t>(blk + 64 * h + l + 32 * (g & 1));
+    v[k].wh = load_u2<uint32_t>(blk + 128 + 32 * h + l);
+    v[k].dw = *reinterpret_cast<const uint16_t*>(blk + 208);
+    v[k].sc = static_cast<int8_t>(blk[192 + (e0 >> 4)]);
+  }
+#pragma unroll
+  for (int k = 0; k < kSB; ++k) {
+    if (b0 + k >= nblocks) break;  // uniform over the wavefront
+    const uint32_t lo = (g < 2) ? (v[k].wl & kLo4) : ((v[k].wl >> 4) & kLo4);
+    const uint32_t q = lo | (((v[k].wh >> (2 * g)) & 0x03030303u) << 4);
+    const float d = f16_to_f32(v[k].dw);
+    *reinterpret_cast<float4*>(dst + (b0 + k) * 256 + e0) =
+        scale_bytes_signed(q, d * static_cast<float>(v[k].sc), 32);
+  }
 }
 
 }  // namespace
@@ -137,12 +170,12 @@ hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t n
       break;
     }
     case kQ4_K: {
-      const unsigned grid = static_cast<unsigned>((nblocks + 3) / 4);
+      const unsigned grid = static_cast<unsigned>((nblocks + 4 * kSB - 1) / (4 * kSB));
       dequant_q4_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
       break;
     }
     case kQ6_K: {
-      const unsigned grid = static_cast<unsigned>((nblocks + 3) / 4);
+      const unsigned grid = static_cast<unsigned>((nblocks + 4 * kSB - 1) / (4 * kSB));
       dequant_q6_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
       break;
     }
