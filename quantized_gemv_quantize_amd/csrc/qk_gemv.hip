@@ -16,12 +16,13 @@
 //  - one wavefront per output row; its lanes cover a span of consecutive blocks
 //    (Q4_K, Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
 //    Q8_0, Q4_0: 1 lane per 32-element block, 64 blocks per pass);
-//  - every lane issues the global loads of up to UNR passes of its row before the
-//    workgroup stages the paired activation row into LDS, so the HBM stream is in
-//    flight while the activations are copied;
-//  - activations sit in LDS in a per-format layout (padded / permuted so the 16-byte
-//    reads of the lanes of a pass fall in different banks) with the scales already
-//    converted to f32 and the bsums regrouped;
+//  - rows of one or two passes keep the activation blocks a lane needs in
+//    registers, loaded once per wavefront and reused over grid-strided rows;
+//  - longer rows share the activation row through LDS: every lane issues the
+//    global loads of up to UNR passes of its row first, then the workgroup copies
+//    the paired activation row into LDS (Q8_K: the 292-byte blocks as they are;
+//    Q8_0: codes at a padded 48-byte stride, scales converted to f32), so the HBM
+//    stream is in flight while the activations are copied;
 //  - lanes of one superblock combine their int32 partial sums with DPP (exact),
 //    then one lane applies the float step; the row total is a wavefront sum.
 #include <hip/hip_ext.h>
@@ -29,12 +30,6 @@
 #include "qk_device.h"
 #include "qk_internal.h"
 
-#ifndef QK_GEMV_WAVES
-#define QK_GEMV_WAVES 4
-#endif
-#ifndef QK_MAX_WAVES
-#define QK_MAX_WAVES 4096
-#endif
 
 namespace qk {
 namespace {
@@ -47,40 +42,9 @@ constexpr uint32_t kOnes = 0x01010101u;
 __host__ __device__ constexpr int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
 
 // ---------------------------------------------------------------------------
-// LDS activation layouts.
-//
-// Q8_K for Q4_K weights: per superblock 272 bytes of codes; the 16-byte piece i
-// (elements 16i..16i+15) of 64-element chunk c is stored at 64c + 16 (i ^ 2*(c>>1)).
-// A pass reads, at step i, piece i of chunk c = lane & 3 of superblock lane >> 2:
-// the stride 272 (17 pieces) and the XOR put the 8 lanes of a 128-byte bank sweep
-// on 8 different pieces.  Then d (f32) per superblock, then the 8 sums of 32 codes
-// (bsum_2j + bsum_2j+1) per superblock.
-struct LayoutQ4K {
-  static constexpr int kStride = 272;
-  int64_t off_d, off_s, bytes;
-  __host__ __device__ explicit LayoutQ4K(int64_t nb) {
-    off_d = nb * kStride;
-    off_s = align16(off_d + 4 * nb);
-    bytes = off_s + 32 * nb;
-  }
-};
-
-// Q8_K for Q6_K weights: piece P = e/16 = 8h + 2g + k (half h, group g, lane k) is
-// stored at slot 8h + ((2g + k) ^ 4h) of a 288-byte superblock; lane (h, k) reads
-// piece 8h + 2g + k at step g.  Then d (f32), then 32 * bsum_t as int32 stored at
-// index 8h + 4k + g so a lane's four values are one 16-byte read.
-struct LayoutQ6K {
-  static constexpr int kStride = 288;
-  int64_t off_d, off_s, bytes;
-  __host__ __device__ explicit LayoutQ6K(int64_t nb) {
-    off_d = nb * kStride;
-    off_s = align16(off_d + 4 * nb);
-    bytes = off_s + 64 * nb;
-  }
-};
-
-// Q8_0 for Q8_0 and Q4_0 weights: 32 codes per block at a 48-byte stride (lanes of
-// a pass read consecutive blocks), then d (f32) per block.
+// LDS layout of a Q8_0 activation row (for Q8_0 and Q4_0 weights): 32 codes per
+// block at a 48-byte stride (lanes of a pass read consecutive blocks), then d
+// (f32) per block.
 struct LayoutQ80 {
   static constexpr int kStride = 48;
   int64_t off_d, bytes;
@@ -90,7 +54,7 @@ struct LayoutQ80 {
   }
 };
 
-// Staging of one activation row into LDS.
+// Staging of one Q8_0 activation row into LDS.
 //
 // The row is split into 16-byte pieces of codes (one dwordx4 load and one
 // ds_write_b128 each) and small units (the block scale and the bsums).  Staging
@@ -104,96 +68,13 @@ struct LayoutQ80 {
 constexpr int kPieces = 4;
 constexpr int kSmall = 2;
 
-struct StagedQ8K {
-  uint4 piece[kPieces];
-  uint32_t small[kSmall];
-};
 struct StagedQ80 {
   uint4 piece[kPieces];
   uint16_t small[kSmall];
 };
 
-// Q8_K block i (292 bytes): piece p (p < 16) = codes 16p..16p+15 at 4 + 16p;
-// small unit r (r < 9) = dword r of {d, bsum pairs 0-7} at 0 and 260 + 4(r-1).
-__device__ __forceinline__ const uint8_t* q8K_piece_src(const uint8_t* xq, int u) {
-  return xq + static_cast<uint32_t>((u >> 4) * kQ8_KBytes + 4 + 16 * (u & 15));
-}
-__device__ __forceinline__ const uint8_t* q8K_small_src(const uint8_t* xq, int u) {
-  const int i = u / 9, r = u - 9 * i;
-  return xq + static_cast<uint32_t>(i * kQ8_KBytes + (r == 0 ? 0 : 256 + 4 * r));
-}
-
-template <int NT>
-__device__ __forceinline__ void stage_load_q8K(StagedQ8K& st, const uint8_t* __restrict__ xq, int nb) {
-  const int np = nb * 16, ns = nb * 9;
-#pragma unroll
-  for (int i = 0; i < kPieces; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * NT, np - 1);
-    st.piece[i] = load_u2<uint4>(q8K_piece_src(xq, u));
-  }
-#pragma unroll
-  for (int i = 0; i < kSmall; ++i) {
-    const int u = min(static_cast<int>(threadIdx.x) + i * NT, ns - 1);
-    st.small[i] = *reinterpret_cast<const uint32_t*>(q8K_small_src(xq, u));
-  }
-}
-
 __device__ __forceinline__ int sext16_lo(uint32_t v) { return static_cast<int16_t>(v & 0xFFFF); }
 __device__ __forceinline__ int sext16_hi(uint32_t v) { return static_cast<int16_t>(v >> 16); }
-
-// Q4_K layout: piece p of block i -> 272 i + 64 c + 16 (pi ^ 2 (c >> 1)), c = p / 4,
-// pi = p % 4; d -> off_d + 4 i; bsum pair j -> off_s + 32 i + 4 j as one int32 sum.
-__device__ __forceinline__ void place_piece_q4K(uint8_t* lds, int u, const uint4& v) {
-  const int i = u >> 4, p = u & 15, c = p >> 2, pi = p & 3;
-  *reinterpret_cast<uint4*>(lds + i * LayoutQ4K::kStride + 64 * c + 16 * (pi ^ ((c >> 1) << 1))) = v;
-}
-__device__ __forceinline__ void place_small_q4K(uint8_t* lds, const LayoutQ4K& L, int u, uint32_t v) {
-  const int i = u / 9, r = u - 9 * i;
-  const int addr = (r == 0) ? static_cast<int>(L.off_d) + 4 * i : static_cast<int>(L.off_s) + 32 * i + 4 * (r - 1);
-  const uint32_t val = (r == 0) ? v : static_cast<uint32_t>(sext16_lo(v) + sext16_hi(v));
-  *reinterpret_cast<uint32_t*>(lds + addr) = val;
-}
-
-// Q6_K layout: piece P of block i -> 288 i + 16 (8h + ((P & 7) ^ 4h)), h = P / 8;
-// d -> off_d + 4 i; bsum t -> off_s + 64 i + 4 (8h + 4k + g) as 32 * bsum, where
-// t = 8h + 2g + k.  Small unit r >= 1 holds bsums t = 2(r-1) (k = 0) and 2(r-1)+1.
-__device__ __forceinline__ void place_piece_q6K(uint8_t* lds, int u, const uint4& v) {
-  const int i = u >> 4, P = u & 15, h = P >> 3;
-  *reinterpret_cast<uint4*>(lds + i * LayoutQ6K::kStride + 16 * (8 * h + ((P & 7) ^ (4 * h)))) = v;
-}
-__device__ __forceinline__ void place_small_q6K(uint8_t* lds, const LayoutQ6K& L, int u, uint32_t v) {
-  const int i = u / 9, r = u - 9 * i;
-  const int j = max(r - 1, 0), h = j >> 2, g = j & 3;
-  const int base = static_cast<int>(L.off_s) + 64 * i + 4 * (8 * h + g);
-  const int a0 = (r == 0) ? static_cast<int>(L.off_d) + 4 * i : base;
-  const uint32_t v0 = (r == 0) ? v : static_cast<uint32_t>(32 * sext16_lo(v));
-  *reinterpret_cast<uint32_t*>(lds + a0) = v0;
-  // second bsum of the pair (k = 1); the d unit rewrites its own value instead
-  const int a1 = (r == 0) ? a0 : base + 16;
-  const uint32_t v1 = (r == 0) ? v : static_cast<uint32_t>(32 * sext16_hi(v));
-  *reinterpret_cast<uint32_t*>(lds + a1) = v1;
-}
-
-template <int NT, typename LayoutT, typename PieceF, typename SmallF>
-__device__ __forceinline__ void stage_place_q8K(uint8_t* lds, const LayoutT& L, const StagedQ8K& st,
-                                                const uint8_t* __restrict__ xq, int nb, PieceF piece,
-                                                SmallF small) {
-  const int np = nb * 16, ns = nb * 9;
-#pragma unroll
-  for (int i = 0; i < kPieces; ++i) {
-    piece(lds, min(static_cast<int>(threadIdx.x) + i * NT, np - 1), st.piece[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < kSmall; ++i) {
-    small(lds, L, min(static_cast<int>(threadIdx.x) + i * NT, ns - 1), st.small[i]);
-  }
-  for (int u = static_cast<int>(threadIdx.x) + kPieces * NT; u < np; u += NT) {
-    piece(lds, u, load_u2<uint4>(q8K_piece_src(xq, u)));
-  }
-  for (int u = static_cast<int>(threadIdx.x) + kSmall * NT; u < ns; u += NT) {
-    small(lds, L, u, *reinterpret_cast<const uint32_t*>(q8K_small_src(xq, u)));
-  }
-}
 
 // Q8_0 block i (34 bytes): pieces 0, 1 = codes at 2 and 18; small unit = f16 d at 0.
 // LDS: piece p -> 48 i + 16 p; d -> off_d + 4 i as f32.
@@ -682,10 +563,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
     const uint2 bs = load_a4<uint2>(a + 260 + 8 * c);
     S2[p] = make_int2(sext16_lo(bs.x) + sext16_hi(bs.x), sext16_lo(bs.y) + sext16_hi(bs.y));
   }
-#ifdef QK_ACT_FIRST
-  __builtin_amdgcn_s_waitcnt(0);
-  sched_fence();
-#endif
 
   for (int r0 = wave * RPW; r0 < n_out; r0 += nwaves * RPW) {
     uint4 H[RPW][NP], Q0[RPW][NP], Q1[RPW][NP];
@@ -761,10 +638,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_reg(
     for (int g = 0; g < 4; ++g) v[g] = 32 * (kk ? sext16_hi(w[g]) : sext16_lo(w[g]));
     BS[p] = make_int4(v[0], v[1], v[2], v[3]);
   }
-#ifdef QK_ACT_FIRST
-  __builtin_amdgcn_s_waitcnt(0);
-  sched_fence();
-#endif
 
   for (int row = wave; row < n_out; row += nwaves) {
     const uint8_t* wrow = W + static_cast<size_t>(row) * rb;
@@ -942,8 +815,11 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
   }
 }
 
-// Wavefronts (rows) per workgroup of the GEMV launches.
-constexpr int kWaves = QK_GEMV_WAVES;
+// Wavefronts (rows) per workgroup of the LDS-staged GEMV launches (4 measured
+// best: 8 and 2 were slower on the 4096 x 11008 Q4_K decode shape), and the most
+// wavefronts the register-resident kernels launch (grid-strided over rows).
+constexpr int kWaves = 4;
+constexpr int kMaxWaves = 4096;
 
 hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in,
                        const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,
@@ -951,8 +827,7 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
   if (n_out <= 0) return hipSuccess;
   const int64_t lds = gemv_lds_bytes(w_type, n_in);
   const bool S = sums != nullptr;
-  constexpr int MW = QK_MAX_WAVES;
-#define QK_ROWS(kern) launch_rows<4>(kern, n_out, 1, MW, s, e0, e1, W, nb, xq, y, sums)
+#define QK_ROWS(kern) launch_rows<4>(kern, n_out, 1, kMaxWaves, s, e0, e1, W, nb, xq, y, sums)
 #define QK_LDS(kern) launch<kWaves>(kern, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
   switch (w_type) {
     case kQ4_K: {
