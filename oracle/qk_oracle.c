@@ -10,6 +10,7 @@
  */
 #include "qk_oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <string.h>
 
@@ -17,13 +18,16 @@
 /* ------------------------------------------------------------------------- */
 /* Type table.                                                                */
 /* [candle] GgmlDType table: block elements / block bytes                    */
-/*   Q4_0 32/18, Q8_0 32/34, Q4K 256/144, Q6K 256/210, Q8K 256/292.          */
+/*   Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q8_0 32/34, Q4K 256/144,            */
+/*   Q6K 256/210, Q8K 256/292.                                                */
 /* [sipllm] Design, "type_nbytes(t, n) = n / block_size * type_size".        */
 /* ------------------------------------------------------------------------- */
 
 int64_t orc_block_elems(int type) {
   switch (type) {
     case ORC_Q4_0:
+    case ORC_Q4_1:
+    case ORC_Q5_0:
     case ORC_Q8_0:
       return 32;
     case ORC_Q4_K:
@@ -38,6 +42,8 @@ int64_t orc_block_elems(int type) {
 int64_t orc_block_bytes(int type) {
   switch (type) {
     case ORC_Q4_0: return 18;
+    case ORC_Q4_1: return 20;
+    case ORC_Q5_0: return 22;
     case ORC_Q8_0: return 34;
     case ORC_Q4_K: return 144;
     case ORC_Q6_K: return 210;
@@ -53,11 +59,14 @@ int64_t orc_row_bytes(int type, int64_t n) {
   return n / be * orc_block_bytes(type);
 }
 
-/* Weight -> activation pairing: [candle] VecDotType table; [cl] Example 11
- * (Q4_0 pairs with Q8_0); [rml] "Quantized dot products". */
+/* Weight -> activation pairing: [candle] VecDotType table (Q4_0, Q5_0, Q8_0
+ * pair with Q8_0; the K-quants with Q8K); [cl] Example 11; [rml] "Quantized
+ * dot products".  Q4_1 pairs with Q8_1, which the pages only name: no pairing
+ * here. */
 int orc_act_type(int weight_type) {
   switch (weight_type) {
     case ORC_Q4_0:
+    case ORC_Q5_0:
     case ORC_Q8_0:
       return ORC_Q8_0;
     case ORC_Q4_K:
@@ -247,6 +256,72 @@ int orc_quantize_q4_0(const float* x, uint8_t* out, int64_t n) {
   return ORC_OK;
 }
 
+/* quantize_row_q4_1 ([cl] Example 7): d = (max - min) / 15, id = 1/d (0 when
+ * d is 0), both d and m = min stored as f16; code = min(15, (int8)((x - min) *
+ * id + 0.5)) from the unrounded f32 d and min; nibbles ordered as Q4_0. */
+int orc_quantize_q4_1(const float* x, uint8_t* out, int64_t n) {
+  if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float* xb = x + 32 * b;
+    uint8_t* ob = out + 20 * b;
+    float mn = FLT_MAX, mx = -FLT_MAX;
+    for (int j = 0; j < 32; ++j) {
+      if (xb[j] < mn) mn = xb[j];
+      if (xb[j] > mx) mx = xb[j];
+    }
+    float d = (mx - mn) / 15.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    orc_put_u16(ob, orc_f32_to_f16(d));
+    orc_put_u16(ob + 2, orc_f32_to_f16(mn));
+    for (int j = 0; j < 16; ++j) {
+      float v0 = (xb[j] - mn) * id + 0.5f;
+      float v1 = (xb[j + 16] - mn) * id + 0.5f;
+      int c0 = (int)(int8_t)v0;
+      int c1 = (int)(int8_t)v1;
+      if (c0 > 15) c0 = 15;
+      if (c1 > 15) c1 = 15;
+      ob[4 + j] = (uint8_t)(c0 | (c1 << 4));
+    }
+  }
+  return ORC_OK;
+}
+
+/* quantize_row_q5_0 ([cl] Example 8): max = the first element of largest
+ * magnitude (as Q4_0), d = max / -16, code = min(31, (int8)(x * id + 16.5));
+ * the low 4 bits go to nibbles ordered as Q4_0, bit 4 of code e to bit e of
+ * the 32-bit word qh (little-endian at byte 2). */
+int orc_quantize_q5_0(const float* x, uint8_t* out, int64_t n) {
+  if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float* xb = x + 32 * b;
+    uint8_t* ob = out + 22 * b;
+    float amax = 0.0f, max = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+      if (amax < fabsf(xb[j])) {
+        amax = fabsf(xb[j]);
+        max = xb[j];
+      }
+    }
+    float d = max / -16.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    uint32_t qh = 0;
+    for (int e = 0; e < 32; ++e) {
+      float v = xb[e] * id + 16.5f;
+      int c = (int)(int8_t)v;
+      if (c > 31) c = 31;
+      qh |= (uint32_t)((c >> 4) & 1) << e;
+      if (e < 16) {
+        ob[6 + e] = (uint8_t)(c & 0x0F);
+      } else {
+        ob[6 + e - 16] |= (uint8_t)((c & 0x0F) << 4);
+      }
+    }
+    orc_put_u16(ob, orc_f32_to_f16(d));
+    for (int k = 0; k < 4; ++k) ob[2 + k] = (uint8_t)(qh >> (8 * k));
+  }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Element decoders: the code q of element e of one block, and its scales.   */
 /* ------------------------------------------------------------------------- */
@@ -257,6 +332,24 @@ static int orc_q4_0_code(const uint8_t* blk, int e) {
   const uint8_t* qs = blk + 2;
   int nib = (e < 16) ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);
   return nib - 8;
+}
+
+/* Q4_1 ([cl] Example 7): nibbles ordered as Q4_0 (qs at byte 4), code 0..15,
+ * value code * d + m. */
+static int orc_q4_1_code(const uint8_t* blk, int e) {
+  const uint8_t* qs = blk + 4;
+  return (e < 16) ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);
+}
+
+/* Q5_0 ([cl] Example 8): low 4 bits as Q4_0 (qs at byte 6), bit 4 is bit e of
+ * qh (bytes 2-5, little-endian); the 5-bit code means code - 16. */
+static int orc_q5_0_code(const uint8_t* blk, int e) {
+  const uint8_t* qs = blk + 6;
+  uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) |
+                ((uint32_t)blk[5] << 24);
+  int low4 = (e < 16) ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);
+  int bit4 = (int)((qh >> e) & 1u);
+  return (low4 | (bit4 << 4)) - 16;
 }
 
 /* Q4_K sub-block (scale, min) pair, get_scale_min_k4:
@@ -328,6 +421,17 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
         for (int e = 0; e < 32; ++e) y[e] = (float)orc_q4_0_code(blk, e) * d;
         break;
       }
+      case ORC_Q4_1: { /* [cl] Example 7: value = code * d + m */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        float m = orc_f16_to_f32(orc_get_u16(blk + 2));
+        for (int e = 0; e < 32; ++e) y[e] = (float)orc_q4_1_code(blk, e) * d + m;
+        break;
+      }
+      case ORC_Q5_0: { /* [cl] Example 8: value = (code - 16) * d */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        for (int e = 0; e < 32; ++e) y[e] = (float)orc_q5_0_code(blk, e) * d;
+        break;
+      }
       case ORC_Q4_K: { /* [rml] trace: x = d * scale * q - dmin * min */
         float d = orc_f16_to_f32(orc_get_u16(blk));
         float dmin = orc_f16_to_f32(orc_get_u16(blk + 2));
@@ -372,6 +476,7 @@ int64_t orc_sums_per_block(int weight_type) {
   switch (weight_type) {
     case ORC_Q8_0:
     case ORC_Q4_0:
+    case ORC_Q5_0:
     case ORC_Q6_K:
       return 1;
     case ORC_Q4_K:
@@ -393,6 +498,12 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
     case ORC_Q4_0: { /* [cl] Example 11: low nibble x a_j, high nibble x a_{j+16} */
       int32_t s = 0;
       for (int e = 0; e < 32; ++e) s += (int32_t)orc_q4_0_code(wb, e) * (int32_t)(int8_t)xb[2 + e];
+      out[0] = s;
+      return ORC_OK;
+    }
+    case ORC_Q5_0: { /* as Q4_0, with the 5-bit code (minus 16) of each element */
+      int32_t s = 0;
+      for (int e = 0; e < 32; ++e) s += (int32_t)orc_q5_0_code(wb, e) * (int32_t)(int8_t)xb[2 + e];
       out[0] = s;
       return ORC_OK;
     }
@@ -447,7 +558,8 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
 static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s) {
   switch (wt) {
     case ORC_Q8_0:
-    case ORC_Q4_0: {
+    case ORC_Q4_0:
+    case ORC_Q5_0: {
       float dw = orc_f16_to_f32(orc_get_u16(wb));
       float dx = orc_f16_to_f32(orc_get_u16(xb));
       return (float)s[0] * (dw * dx);

@@ -24,6 +24,10 @@
  *   rule); the scale rule taken is the Q8_0 one over 256 elements.
  *   Q6_K ql/qh bit arrangement: parity unpinned (the pages give only the field
  *   roles); the GGUF arrangement is assumed.
+ *   quantize / dequantize Q4_1 and Q5_0, vec_dot Q5_0xQ8_0: pinned by the [cl]
+ *   Example 7, 8, 12 and 14 printed values and bytes, plus brute force.  Q4_1
+ *   has no dot product here: its activation format (Q8_1) is only named on the
+ *   pages, so it is a dequantize / quantize format only.
  */
 #ifndef QK_ORACLE_H
 #define QK_ORACLE_H
@@ -37,6 +41,8 @@ extern "C" {
 
 /* GGUF type ids (ggml's numbering, which is what a GGUF tensor record stores). */
 #define ORC_Q4_0 2
+#define ORC_Q4_1 3
+#define ORC_Q5_0 6
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
 #define ORC_Q6_K 14
@@ -60,6 +66,8 @@ uint16_t orc_f32_to_f16(float f);
 int orc_quantize_q8_0(const float* x, uint8_t* out, int64_t n);
 int orc_quantize_q8_K(const float* x, uint8_t* out, int64_t n);
 int orc_quantize_q4_0(const float* x, uint8_t* out, int64_t n);
+int orc_quantize_q4_1(const float* x, uint8_t* out, int64_t n);
+int orc_quantize_q5_0(const float* x, uint8_t* out, int64_t n);
 
 int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n);
 

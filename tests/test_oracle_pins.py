@@ -24,7 +24,8 @@ F32 = np.float32
 
 def test_type_table_matches_printed_geometry():
     # candle "量化格式" GgmlDType table; codeloopback lesson format table.
-    ids = {"Q4_0": o.Q4_0, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
+    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
+           "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
     for name, gid, elems, nbytes, bpw in rows("type_table.txt"):
         t = ids[name]
         assert t == int(gid)
@@ -149,10 +150,80 @@ def test_q8_0_codeloopback_examples_2_3_4():
 def test_hex_crosscheck_example_14():
     x = _cl_inputs(64)
     x[40] = F32(9.5)
-    types = {"Q8_0": o.Q8_0, "Q4_0": o.Q4_0}
+    types = {"Q8_0": o.Q8_0, "Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0}
     for blk, name, hexs in rows("hex_crosscheck.txt"):
         blk = int(blk)
         assert o.quantize(types[name], x[32 * blk:32 * blk + 32]).tobytes().hex() == hexs
+
+
+def _rel_rmse_pct(x, y):
+    x64, y64 = x.astype(np.float64), y.astype(np.float64)
+    return 100 * math.sqrt(np.sum((y64 - x64) ** 2) / np.sum(x64 * x64))
+
+
+def test_q4_1_codeloopback_example_7():
+    kv = keyvals("q4_1_q5_0_examples.txt")
+    centered = _cl_inputs(32)
+    shifted = F32(2) + np.abs(centered)
+    for name, x in (("centered", centered), ("shifted", shifted)):
+        b = o.quantize(o.Q4_1, x)
+        assert b.size == 20
+        mn, mx = x.min(), x.max()
+        assert f"{mn:.3f}" == kv[f"ex7.{name}.min"] and f"{mx:.3f}" == kv[f"ex7.{name}.max"]
+        assert f"{(mx - mn) / F32(15):.4f}" == kv[f"ex7.{name}.d"]
+        # stored m is the f16 of min; the page prints min itself
+        assert f"{mn:.4f}" == kv[f"ex7.{name}.m"]
+        assert o.f16_to_f32(int(b[2]) | int(b[3]) << 8) == float(np.float16(mn))
+        y = o.dequantize(o.Q4_1, b, 32)
+        assert f"{_rel_rmse_pct(x, y):.3f}" == kv[f"ex7.{name}.rmse"]
+    assert f"{20 * 8 / 32.0}" == kv["ex7.bpw"]
+
+
+def test_q5_0_codeloopback_example_8():
+    kv = keyvals("q4_1_q5_0_examples.txt")
+    x = _cl_inputs(32)
+    b = o.quantize(o.Q5_0, x)
+    assert b.tobytes().hex() == kv["ex8.block"]
+    qh = int.from_bytes(b[2:6].tobytes(), "little")
+    assert format(qh, "032b") == kv["ex8.qh_bits"]
+    amax_i = int(np.argmax(np.abs(x)))  # first index of the largest magnitude
+    assert f"{x[amax_i]:.4f}" == kv["ex8.max"]
+    assert f"{x[amax_i] / F32(-16):.5f}" == kv["ex8.d"]
+    y = o.dequantize(o.Q5_0, b, 32)
+    assert f"{_rel_rmse_pct(x, y):.3f}" == kv["ex8.rmse"]
+
+
+def test_q5_0_and_q4_1_each_code_bit_is_one_element():
+    # codeloopback Example 8: bit e of qh is the fifth bit of element e; a nibble of
+    # byte j holds element j (low) or j + 16 (high), as Q4_0.  Flipping any one code
+    # bit must move exactly one element, by d * 2^k (Q5_0) or d * 2^k (Q4_1).
+    rng = np.random.default_rng(9)
+    for t, qs_off, hdr in ((o.Q5_0, 6, 22), (o.Q4_1, 4, 20)):
+        b = rng.integers(0, 256, hdr, dtype=np.uint8)
+        b[0:2] = np.frombuffer(np.float16(0.25).tobytes(), np.uint8)
+        if t == o.Q4_1:
+            b[2:4] = np.frombuffer(np.float16(-1.0).tobytes(), np.uint8)
+        base = o.dequantize(t, b, 32).astype(np.float64)
+        seen = set()
+        bits = [(j, k) for j in range(qs_off, hdr) for k in range(8)]
+        if t == o.Q5_0:
+            bits += [(j, k) for j in range(2, 6) for k in range(8)]
+        for j, k in bits:
+            c = b.copy()
+            c[j] ^= np.uint8(1 << k)
+            d = o.dequantize(t, c, 32).astype(np.float64) - base
+            moved = np.nonzero(d)[0]
+            assert moved.size == 1, (t, j, k)
+            e = int(moved[0])
+            if j >= qs_off:  # nibble bit: element j' (low) or j' + 16 (high)
+                jj = j - qs_off
+                assert e == (jj if k < 4 else jj + 16)
+                assert abs(d[e]) == 0.25 * 2 ** (k % 4)
+            else:  # qh bit: element 8 * (j - 2) + k, weight 16
+                assert e == 8 * (j - 2) + k
+                assert abs(d[e]) == 0.25 * 16
+            seen.add((e, (k % 4) if j >= qs_off else 4))
+        assert len(seen) == (32 * 5 if t == o.Q5_0 else 32 * 4)
 
 
 def test_q4_0_rml_worked_example():
@@ -422,7 +493,7 @@ def _random_weights(t, nblocks, rng):
     nb = o.block_bytes(t)
     w = rng.integers(0, 256, nb * nblocks, dtype=np.uint8).reshape(nblocks, nb)
     h = lambda lo, hi: np.frombuffer(rng.uniform(lo, hi, nblocks).astype(np.float16).tobytes(), np.uint8).reshape(nblocks, 2)
-    if t in (o.Q8_0, o.Q4_0):
+    if t in (o.Q8_0, o.Q4_0, o.Q5_0):
         w[:, 0:2] = h(0.001, 0.05)
     elif t == o.Q4_K:
         w[:, 0:2] = h(1e-3, 1e-2)
@@ -444,7 +515,7 @@ def _act_parts(at, xq, n):
     return np.repeat(d, 256), blk[:, 4:260].view(np.int8).astype(np.int64).reshape(-1)
 
 
-@pytest.mark.parametrize("t", [o.Q8_0, o.Q4_0, o.Q4_K, o.Q6_K])
+@pytest.mark.parametrize("t", [o.Q8_0, o.Q4_0, o.Q5_0, o.Q4_K, o.Q6_K])
 def test_vec_dot_brute_force(t):
     rng = np.random.default_rng(100 + t)
     at = o.act_type(t)
@@ -461,14 +532,14 @@ def test_vec_dot_brute_force(t):
         sums = o.block_sums(t, w, xq, n).astype(np.float64)
         wb = w.reshape(n // o.block_elems(t), -1)
         f16 = lambda a, off: a[:, off:off + 2].copy().view(np.float16).astype(np.float64)[:, 0]
-        if t in (o.Q8_0, o.Q4_0):
+        if t in (o.Q8_0, o.Q4_0, o.Q5_0):
             exact = np.sum(sums[:, 0] * f16(wb, 0) * dx[::32])
         elif t == o.Q4_K:
             exact = np.sum(dx[::256] * (f16(wb, 0) * sums[:, 0] - f16(wb, 2) * sums[:, 1]))
         else:
             exact = np.sum(dx[::256] * f16(wb, 208) * sums[:, 0])
         scale = np.abs(terms).sum()
-        # Q8_0, Q4_0, Q6_K decoded values are exact in f32; Q4_K's d*sc*q - dmin*m
+        # Q8_0, Q4_0, Q5_0, Q6_K decoded values are exact in f32; Q4_K's d*sc*q - dmin*m
         # rounds once per element.
         tol = 1e-12 if t != o.Q4_K else 1e-7
         assert abs(exact - brute) <= tol * scale, (t, n, exact, brute)
@@ -521,7 +592,7 @@ def _outlier_weights(r, count):
 def _fake(t, x):
     if t == "F16":
         return x.astype(np.float16).astype(np.float32)
-    tt = {"Q8_0": o.Q8_0, "Q4_0": o.Q4_0}[t]
+    tt = {"Q8_0": o.Q8_0, "Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0}[t]
     return o.dequantize(tt, o.quantize(tt, x), x.size)
 
 
@@ -529,7 +600,7 @@ def test_codeloopback_example_12_error_table():
     kv = keyvals("seeded_examples.txt")
     x = _outlier_weights(JavaRandom(24), 65536)
     p = np.sum((x * x).astype(np.float64))
-    for t in ("F16", "Q8_0", "Q4_0"):
+    for t in ("F16", "Q8_0", "Q5_0", "Q4_1", "Q4_0"):
         y = _fake(t, x)
         e = np.sum(((y - x).astype(np.float64)) ** 2)
         assert f"{100 * math.sqrt(e / p):.4f}" == kv[f"ex12.{t}"], t
