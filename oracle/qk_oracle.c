@@ -150,6 +150,17 @@ static int8_t orc_code_q8(float v) {
   return (int8_t)r;
 }
 
+/* The truncating conversion of the Q4_0 / Q4_1 / Q5_0 codes: the (int) cast of
+ * [cl] Examples 5, 7 and 8's listings, which truncates toward zero, saturates at
+ * the int32 limits and turns NaN into 0.  A value outside 0..16.5 reaches it only
+ * when 1/d overflows to infinity (a block whose scale is below 2^-128). */
+static int32_t orc_trunc_sat(float v) {
+  if (isnan(v)) return 0;
+  if (v >= 2147483648.0f) return INT32_MAX;
+  if (v <= -2147483648.0f) return INT32_MIN;
+  return (int32_t)v;
+}
+
 /* Largest |x| over a block, NaN ignored (fmaxf returns the other operand). */
 static float orc_amax(const float* x, int64_t len) {
   float amax = 0.0f;
@@ -226,7 +237,7 @@ int orc_quantize_q8_K(const float* x, uint8_t* out, int64_t n) {
 
 /* quantize_row_q4_0 reference ([rml] "A worked example: Q4_0"; [cl] Example
  * 5): max = the first value of largest magnitude, sign kept (strict <); d =
- * max / -8; id = 1/d or 0; code = min(15, (int8)(x*id + 8.5)); byte j holds
+ * max / -8; id = 1/d or 0; code = min(15, trunc_sat(x*id + 8.5)); byte j holds
  * element j in its low nibble and element j+16 in its high nibble. */
 int orc_quantize_q4_0(const float* x, uint8_t* out, int64_t n) {
   if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
@@ -246,19 +257,19 @@ int orc_quantize_q4_0(const float* x, uint8_t* out, int64_t n) {
     for (int j = 0; j < 16; ++j) {
       float v0 = xb[j] * id + 8.5f;
       float v1 = xb[j + 16] * id + 8.5f;
-      int c0 = (int)(int8_t)v0;
-      int c1 = (int)(int8_t)v1;
+      int32_t c0 = orc_trunc_sat(v0);
+      int32_t c1 = orc_trunc_sat(v1);
       if (c0 > 15) c0 = 15;
       if (c1 > 15) c1 = 15;
-      ob[2 + j] = (uint8_t)(c0 | (c1 << 4));
+      ob[2 + j] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
     }
   }
   return ORC_OK;
 }
 
 /* quantize_row_q4_1 ([cl] Example 7): d = (max - min) / 15, id = 1/d (0 when
- * d is 0), both d and m = min stored as f16; code = min(15, (int8)((x - min) *
- * id + 0.5)) from the unrounded f32 d and min; nibbles ordered as Q4_0. */
+ * d is 0), both d and m = min stored as f16; code = min(15, trunc_sat((x - min)
+ * * id + 0.5)) from the unrounded f32 d and min; nibbles ordered as Q4_0. */
 int orc_quantize_q4_1(const float* x, uint8_t* out, int64_t n) {
   if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
   for (int64_t b = 0; b < n / 32; ++b) {
@@ -276,18 +287,18 @@ int orc_quantize_q4_1(const float* x, uint8_t* out, int64_t n) {
     for (int j = 0; j < 16; ++j) {
       float v0 = (xb[j] - mn) * id + 0.5f;
       float v1 = (xb[j + 16] - mn) * id + 0.5f;
-      int c0 = (int)(int8_t)v0;
-      int c1 = (int)(int8_t)v1;
+      int32_t c0 = orc_trunc_sat(v0);
+      int32_t c1 = orc_trunc_sat(v1);
       if (c0 > 15) c0 = 15;
       if (c1 > 15) c1 = 15;
-      ob[4 + j] = (uint8_t)(c0 | (c1 << 4));
+      ob[4 + j] = (uint8_t)((c0 & 15) | ((c1 & 15) << 4));
     }
   }
   return ORC_OK;
 }
 
 /* quantize_row_q5_0 ([cl] Example 8): max = the first element of largest
- * magnitude (as Q4_0), d = max / -16, code = min(31, (int8)(x * id + 16.5));
+ * magnitude (as Q4_0), d = max / -16, code = min(31, trunc_sat(x * id + 16.5));
  * the low 4 bits go to nibbles ordered as Q4_0, bit 4 of code e to bit e of
  * the 32-bit word qh (little-endian at byte 2). */
 int orc_quantize_q5_0(const float* x, uint8_t* out, int64_t n) {
@@ -307,9 +318,9 @@ int orc_quantize_q5_0(const float* x, uint8_t* out, int64_t n) {
     uint32_t qh = 0;
     for (int e = 0; e < 32; ++e) {
       float v = xb[e] * id + 16.5f;
-      int c = (int)(int8_t)v;
+      int32_t c = orc_trunc_sat(v);
       if (c > 31) c = 31;
-      qh |= (uint32_t)((c >> 4) & 1) << e;
+      qh |= (((uint32_t)c >> 4) & 1u) << e;
       if (e < 16) {
         ob[6 + e] = (uint8_t)(c & 0x0F);
       } else {

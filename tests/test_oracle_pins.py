@@ -193,6 +193,22 @@ def test_q5_0_codeloopback_example_8():
     assert f"{_rel_rmse_pct(x, y):.3f}" == kv["ex8.rmse"]
 
 
+def test_weight_codes_when_the_inverse_scale_overflows():
+    # codeloopback Examples 5, 7, 8 convert codes with the listings' (int) cast:
+    # toward zero, saturating, NaN -> 0.  A block of f32 subnormals has a scale
+    # below 2^-128, so 1/d is +inf; the bytes below are worked out by hand from
+    # that rule: x * inf is +-inf (NaN for x = 0), +inf saturates to the top
+    # code, -inf to INT_MIN whose low bits are 0, NaN to 0.
+    x = np.zeros(32, np.float32)
+    x[0], x[1], x[17] = F32(-1e-39), F32(5e-40), F32(-2e-40)
+    q40 = "0000" + "000f" + "00" * 14                 # d -> f16 +0; only x[1] -> 15
+    q50 = "0000" + "02000000" + "000f" + "00" * 14    # code 31 for x[1]: qh bit 1
+    q41 = "00000080" + "f0" + "ff" * 15               # m = -0; x[0] -> NaN -> 0
+    assert o.quantize(o.Q4_0, x).tobytes().hex() == q40
+    assert o.quantize(o.Q5_0, x).tobytes().hex() == q50
+    assert o.quantize(o.Q4_1, x).tobytes().hex() == q41
+
+
 def test_q5_0_and_q4_1_each_code_bit_is_one_element():
     # codeloopback Example 8: bit e of qh is the fifth bit of element e; a nibble of
     # byte j holds element j (low) or j + 16 (high), as Q4_0.  Flipping any one code
