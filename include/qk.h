@@ -34,6 +34,8 @@ extern "C" {
 
 /* ggml type ids of the formats on the path. */
 #define QK_TYPE_Q4_0 2
+#define QK_TYPE_Q4_1 3
+#define QK_TYPE_Q5_0 6
 #define QK_TYPE_Q8_0 8
 #define QK_TYPE_Q4_K 12
 #define QK_TYPE_Q6_K 14
@@ -41,15 +43,16 @@ extern "C" {
 
 /* Status codes returned by every call that can fail. */
 #define QK_OK 0
-#define QK_E_TYPE 1   /* unknown type id, or an activation type used as a weight */
+#define QK_E_TYPE 1   /* unknown type id, or a type the call does not take */
 #define QK_E_SHAPE 3  /* n not a positive multiple of the block size, or a negative count */
 #define QK_E_ALIGN 4  /* a base pointer is not 16-byte aligned */
 #define QK_E_NULL 5   /* a required pointer is NULL */
 #define QK_E_DEVICE 6 /* the HIP runtime reported an error while enqueueing */
 #define QK_E_LIMIT 7  /* the activation row does not fit the kernels' LDS budget */
 
-/* Elements per block (32 or 256) and bytes per block (18, 34, 144, 210, 292) of a
- * type, 0 for an unknown id.  Geometry from the candle formats page, "GgmlDType" table. */
+/* Elements per block (32 or 256) and bytes per block (Q4_0 18, Q4_1 20, Q5_0 22,
+ * Q8_0 34, Q4_K 144, Q6_K 210, Q8_K 292) of a type, 0 for an unknown id.  Geometry
+ * from the candle formats page, "GgmlDType" table. */
 int64_t qk_block_elems(int type);
 int64_t qk_block_bytes(int type);
 
@@ -59,7 +62,9 @@ int64_t qk_block_bytes(int type);
 int64_t qk_row_bytes(int type, int64_t n);
 
 /* Activation type a weight type is multiplied against (candle "VecDotType" table;
- * codeloopback Example 11): Q4_0, Q8_0 -> Q8_0; Q4_K, Q6_K -> Q8_K; -1 otherwise. */
+ * codeloopback Example 11): Q4_0, Q5_0, Q8_0 -> Q8_0; Q4_K, Q6_K -> Q8_K; -1
+ * otherwise (Q4_1 pairs with Q8_1, a format the sources only name, so Q4_1 is a
+ * quantize / dequantize type here and has no GEMV). */
 int qk_act_type(int weight_type);
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -88,8 +93,32 @@ int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t n
                     void* stream);
 
 /*
+ * qk_quantize_row - quantize f32 weights into GGUF blocks (quantize_row_*_ref).
+ *   type      QK_TYPE_Q8_0, Q4_0, Q4_1 or Q5_0 (else QK_E_TYPE).
+ *   x         f32 [n], device, 16-byte aligned.
+ *   dst       out: n / 32 blocks (qk_row_bytes(type, n) bytes), device.
+ *   n         >= 0, a multiple of 32; 0 enqueues nothing.
+ * Per 32-element block (codeloopback Examples 2, 5, 7, 8; every float operation
+ * rounded on its own, never fused):
+ *   Q8_0  as qk_quantize_act.
+ *   Q4_0  max = the first element of largest |x|; d = max / -8; id = 1/d (0 when
+ *         d is 0); code = min(15, trunc(x * id + 8.5)); f16 d, then 16 bytes whose
+ *         low nibble is element j and high nibble element j + 16.
+ *   Q4_1  d = (max - min) / 15; code = min(15, trunc((x - min) * id + 0.5)); f16 d,
+ *         f16 min, then the nibbles as Q4_0 (codes use the unrounded d and min).
+ *   Q5_0  max as Q4_0; d = max / -16; code = min(31, trunc(x * id + 16.5)); f16 d,
+ *         a 32-bit word whose bit e is bit 4 of code e, then the low 4 bits as Q4_0.
+ * trunc is the (int) cast of the listings in those examples: toward zero,
+ * saturating at the int32 limits, NaN -> 0; the stored bits are its low 4 (or 5).
+ * It departs from plain truncation only when 1/d overflows to infinity, which
+ * happens for blocks whose scale is below 2^-128.  Inputs must be finite; the
+ * bytes are identical to that definition.
+ */
+int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream);
+
+/*
  * qk_gemv - y = W x for quantized W and already-quantized activations.
- *   w_type    QK_TYPE_Q8_0, Q4_0, Q4_K or Q6_K (else QK_E_TYPE).
+ *   w_type    QK_TYPE_Q8_0, Q4_0, Q5_0, Q4_K or Q6_K (else QK_E_TYPE).
  *   W         n_out rows of qk_row_bytes(w_type, n_in) bytes, contiguous, row-major
  *             (sipllm matmul_quant layout), device.
  *   n_out     output rows, >= 0.
@@ -109,14 +138,16 @@ int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* 
 
 /*
  * qk_dequantize_row - expand n elements (whole blocks) of a weight type to f32.
- *   type      QK_TYPE_Q8_0, Q4_0, Q4_K or Q6_K (Q8_K is an activation-only format
- *             and is refused with QK_E_TYPE, as sipllm's dequantize_row refuses it).
+ *   type      QK_TYPE_Q8_0, Q4_0, Q4_1, Q5_0, Q4_K or Q6_K (Q8_K is an
+ *             activation-only format and is refused with QK_E_TYPE, as sipllm's
+ *             dequantize_row refuses it).
  *   src       n / block blocks, device.  A whole matrix is n = n_out * n_in.
  *   dst       out: f32 [n], device.
  *   n         >= 0, a multiple of the block size; 0 enqueues nothing.
- * Values (rml DequantizeRow; candle block table): Q8_0 d*q; Q4_0 d*(q-8); Q4_K
- * d*sc_j*q - dmin*m_j; Q6_K d*sc_j*(q-32).  Each product is exact in f32, so the
- * result is bit-exact.
+ * Values (rml DequantizeRow; candle block table; codeloopback Examples 7, 8): Q8_0
+ * d*q; Q4_0 d*(q-8); Q4_1 q*d + m; Q5_0 d*(q-16); Q4_K d*sc_j*q - dmin*m_j; Q6_K
+ * d*sc_j*(q-32).  Each product is exact in f32 (at most one rounding, in Q4_1's
+ * and Q4_K's final addition), so the result is bit-exact.
  */
 int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* stream);
 
@@ -125,7 +156,7 @@ int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* st
  * compute instead of y.  For checking exactness; not needed to use the library.
  *   sums      out: int32 [ncols][n_out][n_in / block][k]; k = 2 for Q4_K (the scale
  *             sum S_q = sum_j sc_j s_j and the min sum S_m = sum_j m_j sum(a_j)),
- *             k = 1 otherwise (Q8_0, Q4_0: the block's code-product sum; Q6_K:
+ *             k = 1 otherwise (Q8_0, Q4_0, Q5_0: the block's code-product sum; Q6_K:
  *             S = sum_j sc_j sum (q - 32) a).
  * Other arguments and errors as qk_gemv.
  */

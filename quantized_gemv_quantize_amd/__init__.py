@@ -1,4 +1,4 @@
-"""MI355X block-quantized GEMV (ggml Q8_0 / Q4_0 / Q4_K / Q6_K) - Python binding.
+"""MI355X block-quantized GEMV (ggml Q8_0 / Q4_0 / Q5_0 / Q4_K / Q6_K) - Python binding.
 
 A thin ctypes binding over libqk.so (C ABI in include/qk.h).  Functions carry
 the C names and only marshal arguments: torch tensors supply device pointers
@@ -9,13 +9,18 @@ import ctypes
 import os
 
 QK_TYPE_Q4_0 = 2
+QK_TYPE_Q4_1 = 3
+QK_TYPE_Q5_0 = 6
 QK_TYPE_Q8_0 = 8
 QK_TYPE_Q4_K = 12
 QK_TYPE_Q6_K = 14
 QK_TYPE_Q8_K = 15
-WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q4_K, QK_TYPE_Q6_K)
-TYPE_NAMES = {QK_TYPE_Q4_0: "Q4_0", QK_TYPE_Q8_0: "Q8_0", QK_TYPE_Q4_K: "Q4_K",
-              QK_TYPE_Q6_K: "Q6_K", QK_TYPE_Q8_K: "Q8_K"}
+WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_K, QK_TYPE_Q6_K)
+DEQUANT_TYPES = WEIGHT_TYPES + (QK_TYPE_Q4_1,)
+QUANT_ROW_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q4_1, QK_TYPE_Q5_0)
+TYPE_NAMES = {QK_TYPE_Q4_0: "Q4_0", QK_TYPE_Q4_1: "Q4_1", QK_TYPE_Q5_0: "Q5_0",
+              QK_TYPE_Q8_0: "Q8_0", QK_TYPE_Q4_K: "Q4_K", QK_TYPE_Q6_K: "Q6_K",
+              QK_TYPE_Q8_K: "Q8_K"}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqk.so")
 
@@ -53,6 +58,8 @@ def lib():
         L.qk_max_n_in.argtypes = [i32]
         L.qk_quantize_act.restype = i32
         L.qk_quantize_act.argtypes = [i32, p, p, i64, i64, p]
+        L.qk_quantize_row.restype = i32
+        L.qk_quantize_row.argtypes = [i32, p, p, i64, p]
         L.qk_gemv.restype = i32
         L.qk_gemv.argtypes = [i32, p, i64, i64, p, i64, p, p]
         L.qk_gemv_timed.restype = i32
@@ -116,6 +123,18 @@ def qk_quantize_act(act_type, x, xq=None, stream=None):
     _check(lib().qk_quantize_act(act_type, _ptr(x), _ptr(xq), n, ncols, _stream(stream)),
            "qk_quantize_act")
     return xq
+
+
+def qk_quantize_row(t, x, dst=None, stream=None):
+    """Quantize f32 weights x (device, numel a multiple of 32) into GGUF blocks of
+    type t; returns dst (uint8 [row_bytes])."""
+    import torch
+    n = x.numel()
+    if dst is None:
+        dst = torch.empty((max(qk_row_bytes(t, n), 0),), dtype=torch.uint8, device=x.device)
+    _check(lib().qk_quantize_row(t, _ptr(x), _ptr(dst), n, _stream(stream)),
+           "qk_quantize_row")
+    return dst
 
 
 def qk_gemv(w_type, W, n_out, n_in, xq, ncols=1, y=None, stream=None):

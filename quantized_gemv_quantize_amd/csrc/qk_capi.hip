@@ -10,8 +10,16 @@
 
 namespace {
 
+// Weight formats with a GEMV (a paired activation type).
 bool is_weight(int t) {
-  return t == QK_TYPE_Q4_0 || t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_K || t == QK_TYPE_Q6_K;
+  return t == QK_TYPE_Q4_0 || t == QK_TYPE_Q5_0 || t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_K ||
+         t == QK_TYPE_Q6_K;
+}
+// Weight formats qk_dequantize_row expands.
+bool is_dequant(int t) { return is_weight(t) || t == QK_TYPE_Q4_1; }
+// Weight formats qk_quantize_row writes.
+bool is_quant_row(int t) {
+  return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_0 || t == QK_TYPE_Q4_1 || t == QK_TYPE_Q5_0;
 }
 bool is_act(int t) { return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q8_K; }
 
@@ -77,6 +85,8 @@ extern "C" {
 int64_t qk_block_elems(int type) {
   switch (type) {
     case QK_TYPE_Q4_0:
+    case QK_TYPE_Q4_1:
+    case QK_TYPE_Q5_0:
     case QK_TYPE_Q8_0: return 32;
     case QK_TYPE_Q4_K:
     case QK_TYPE_Q6_K:
@@ -88,6 +98,8 @@ int64_t qk_block_elems(int type) {
 int64_t qk_block_bytes(int type) {
   switch (type) {
     case QK_TYPE_Q4_0: return 18;
+    case QK_TYPE_Q4_1: return 20;
+    case QK_TYPE_Q5_0: return 22;
     case QK_TYPE_Q8_0: return 34;
     case QK_TYPE_Q4_K: return 144;
     case QK_TYPE_Q6_K: return 210;
@@ -105,6 +117,7 @@ int64_t qk_row_bytes(int type, int64_t n) {
 int qk_act_type(int weight_type) {
   switch (weight_type) {
     case QK_TYPE_Q4_0:
+    case QK_TYPE_Q5_0:
     case QK_TYPE_Q8_0: return QK_TYPE_Q8_0;
     case QK_TYPE_Q4_K:
     case QK_TYPE_Q6_K: return QK_TYPE_Q8_K;
@@ -115,7 +128,7 @@ int qk_act_type(int weight_type) {
 const char* qk_status_str(int status) {
   switch (status) {
     case QK_OK: return "ok";
-    case QK_E_TYPE: return "unknown type, or activation type used as a weight";
+    case QK_E_TYPE: return "unknown type, or a type this call does not take";
     case QK_E_SHAPE: return "shape is not whole blocks, or a count is negative";
     case QK_E_ALIGN: return "a base pointer is not 16-byte aligned";
     case QK_E_NULL: return "a required pointer is NULL";
@@ -156,6 +169,16 @@ int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t n
                                        static_cast<hipStream_t>(stream)));
 }
 
+int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream) {
+  if (!is_quant_row(type)) return QK_E_TYPE;
+  if (n < 0 || n % 32 != 0) return QK_E_SHAPE;
+  if (n == 0) return QK_OK;
+  if (x == nullptr || dst == nullptr) return QK_E_NULL;
+  if (!aligned16(x) || !aligned16(dst)) return QK_E_ALIGN;
+  return status_of(qk::launch_quantize_row(type, x, static_cast<uint8_t*>(dst), n / 32,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
             int64_t ncols, float* y, void* stream) {
   return gemv_impl(w_type, W, n_out, n_in, xq, ncols, y, nullptr, stream, nullptr, nullptr);
@@ -173,7 +196,7 @@ int qk_gemv_block_sums(int w_type, const void* W, int64_t n_out, int64_t n_in,
 }
 
 int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* stream) {
-  if (!is_weight(type)) return QK_E_TYPE;
+  if (!is_dequant(type)) return QK_E_TYPE;
   const int64_t be = qk_block_elems(type);
   if (n < 0 || n % be != 0) return QK_E_SHAPE;
   if (n == 0) return QK_OK;

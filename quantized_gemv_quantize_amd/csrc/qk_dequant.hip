@@ -4,6 +4,8 @@
 // Example 6 for Q4_0's nibble order):
 //   Q8_0  d * q
 //   Q4_0  d * (q - 8); byte j: element j in the low nibble, element j+16 in the high
+//   Q4_1  q * d + m, nibbles as Q4_0 (codeloopback Example 7)
+//   Q5_0  d * (q - 16), low nibbles as Q4_0, bit 4 from qh (codeloopback Example 8)
 //   Q4_K  d * sc_j * q - dmin * m_j for 32-element sub-block j (scales per
 //         get_scale_min_k4, rml element-200 trace)
 //   Q6_K  d * sc_j * (q - 32) for 16-element sub-block j; q = 4 bits from ql and
@@ -61,6 +63,48 @@ __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* __rest
   const uint32_t w = load_u2<uint32_t>(blk + 2 + 4 * (part & 3));
   const uint32_t q = (part < 4) ? (w & kLo4) : ((w >> 4) & kLo4);
   *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(q, d, 8);
+}
+
+// Q4_1: as Q4_0 with the codes unsigned and a min added: value = q * d + m (the
+// product is exact, so fused or not the one rounding is the addition).
+__global__ __launch_bounds__(256) void dequant_q4_1_kernel(const uint8_t* __restrict__ src,
+                                                           float* __restrict__ dst,
+                                                           int64_t nblocks) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t b = t >> 3;
+  if (b >= nblocks) return;
+  const int part = threadIdx.x & 7;
+  const uint8_t* blk = src + b * kQ4_1Bytes;
+  const uint32_t dm = *reinterpret_cast<const uint32_t*>(blk);  // 4-byte aligned: d, m
+  const float d = f16_to_f32(dm & 0xFFFF), m = f16_to_f32(dm >> 16);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(blk + 4 + 4 * (part & 3));
+  const uint32_t q = (part < 4) ? (w & kLo4) : ((w >> 4) & kLo4);
+  float4 o;
+  o.x = static_cast<float>(q & 0xFF) * d + m;
+  o.y = static_cast<float>((q >> 8) & 0xFF) * d + m;
+  o.z = static_cast<float>((q >> 16) & 0xFF) * d + m;
+  o.w = static_cast<float>(q >> 24) * d + m;
+  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = o;
+}
+
+// Q5_0: the Q4_0 nibbles plus bit e of qh as bit 4 of element e; value d * (q - 16).
+// Lane part holds elements 4 part .. 4 part + 3 (nibbles of bytes 4 (part & 3) ..,
+// low for part < 4, high otherwise), whose fifth bits are qh bits 4 part .. + 3.
+__global__ __launch_bounds__(256) void dequant_q5_0_kernel(const uint8_t* __restrict__ src,
+                                                           float* __restrict__ dst,
+                                                           int64_t nblocks) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t b = t >> 3;
+  if (b >= nblocks) return;
+  const int part = threadIdx.x & 7;
+  const uint8_t* blk = src + b * kQ5_0Bytes;
+  const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+  const uint32_t qh = load_u2<uint32_t>(blk + 2);
+  const uint32_t w = load_u2<uint32_t>(blk + 6 + 4 * (part & 3));
+  const uint32_t lo = (part < 4) ? (w & kLo4) : ((w >> 4) & kLo4);
+  // four bits -> bit 4 of four bytes: multiplying by 0x204081 copies bit i to bit 8i
+  const uint32_t fifth = ((((qh >> (4 * part)) & 0xF) * 0x00204081u) & 0x01010101u) << 4;
+  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(lo | fifth, d, 16);
 }
 
 // Q4_K and Q6_K: one wavefront per kSB consecutive superblocks, lane l -> elements
@@ -167,6 +211,16 @@ hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t n
     case kQ4_0: {
       const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
       dequant_q4_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
+      break;
+    }
+    case kQ4_1: {
+      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
+      dequant_q4_1_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
+      break;
+    }
+    case kQ5_0: {
+      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
+      dequant_q5_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
       break;
     }
     case kQ4_K: {

@@ -6,7 +6,8 @@
 // the products of codes are summed exactly in int32 (v_dot4 over packed bytes),
 // the K-quant sub-block scales are applied as int32 multiply-adds, and only the
 // block step uses floats:
-//   Q8_0, Q4_0  c = s * (d_w * d_x)
+//   Q8_0, Q4_0, Q5_0  c = s * (d_w * d_x)  (Q5_0: codeloopback Example 8's 5-bit
+//               codes, bit 4 from qh, paired with Q8_0 per candle's VecDotType)
 //   Q4_K        c = (d_x * d) * S_q - (d_x * dmin) * S_m,
 //               S_q = sum_j sc_j s_j, S_m = sum_j m_j (bsum_2j + bsum_2j+1)
 //   Q6_K        c = (d_x * d) * S,  S = sum_j sc_j sum_e (q_e - 32) a_e
@@ -15,7 +16,7 @@
 // Mapping on the GPU (all kernels):
 //  - one wavefront per output row; its lanes cover a span of consecutive blocks
 //    (Q4_K, Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
-//    Q8_0, Q4_0: 1 lane per 32-element block, 64 blocks per pass);
+//    Q8_0, Q4_0, Q5_0: 1 lane per 32-element block, 64 blocks per pass);
 //  - rows of one or two passes keep the activation blocks a lane needs in
 //    registers, loaded once per wavefront and reused over grid-strided rows;
 //  - longer rows share the activation row through LDS: every lane issues the
@@ -37,6 +38,13 @@ namespace {
 constexpr uint32_t kLo4 = 0x0F0F0F0Fu;
 constexpr uint32_t kHi2 = 0x30303030u;
 constexpr uint32_t kOnes = 0x01010101u;
+
+// Q5_0 codes of four elements: their low nibbles (one per byte) plus bit 4 taken
+// from four consecutive qh bits starting at `shift` (multiplying the 4-bit field by
+// 0x204081 copies bit i to bit 8i).
+__device__ __forceinline__ uint32_t q5_codes(uint32_t nibbles, uint32_t qh, int shift) {
+  return nibbles | (((((qh >> shift) & 0xFu) * 0x00204081u) & kOnes) << 4);
+}
 
 
 __host__ __device__ constexpr int64_t align16(int64_t v) { return (v + 15) & ~int64_t(15); }
@@ -463,27 +471,31 @@ __global__ __launch_bounds__(NW * 64) void gemv_q8_0_kernel(
   }
 }
 
-template <int NW, int UNR, bool SUMS>
+template <int NW, int UNR, bool Q5, bool SUMS>
 __global__ __launch_bounds__(NW * 64) void gemv_q4_0_kernel(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
+  constexpr int kWB = Q5 ? kQ5_0Bytes : kQ4_0Bytes;
+  constexpr int kQs = Q5 ? 6 : 2;         // offset of the 16 nibble bytes
+  constexpr int kBias = Q5 ? 16 : 8;      // stored code = value + bias
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * NW + wave_id();
   const bool row_ok = row < n_out;
-  const size_t rb = static_cast<size_t>(nb) * kQ4_0Bytes;
+  const size_t rb = static_cast<size_t>(nb) * kWB;
   const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
   const int passes = (nb + 63) >> 6;
 
   uint4 Q[UNR];
-  uint32_t D[UNR];
+  uint32_t D[UNR], QH[UNR];
   auto issue = [&](int p0) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       const int b = min((p0 + j) * 64 + lane, nb - 1);
-      const uint8_t* p = wrow + static_cast<uint32_t>(b * kQ4_0Bytes);
+      const uint8_t* p = wrow + static_cast<uint32_t>(b * kWB);
       D[j] = *reinterpret_cast<const uint16_t*>(p);
-      Q[j] = load_u2<uint4>(p + 2);
+      if constexpr (Q5) QH[j] = load_u2<uint32_t>(p + 2);
+      Q[j] = load_u2<uint4>(p + kQs);
     }
   };
   const LayoutQ80 L(nb);
@@ -506,15 +518,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_0_kernel(
       const uint4 a0 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ80::kStride);       // elements 0-15
       const uint4 a1 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ80::kStride + 16);  // 16-31
       const uint4 q = Q[j];
+      uint32_t lo[4] = {q.x & kLo4, q.y & kLo4, q.z & kLo4, q.w & kLo4};
+      uint32_t hi[4] = {(q.x >> 4) & kLo4, (q.y >> 4) & kLo4, (q.z >> 4) & kLo4, (q.w >> 4) & kLo4};
+      if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lo[k] = q5_codes(lo[k], QH[j], 4 * k);
+          hi[k] = q5_codes(hi[k], QH[j], 16 + 4 * k);
+        }
+      }
       int s = 0, sa = 0;
-      s = dot4(q.x & kLo4, a0.x, s);
-      s = dot4(q.y & kLo4, a0.y, s);
-      s = dot4(q.z & kLo4, a0.z, s);
-      s = dot4(q.w & kLo4, a0.w, s);
-      s = dot4((q.x >> 4) & kLo4, a1.x, s);
-      s = dot4((q.y >> 4) & kLo4, a1.y, s);
-      s = dot4((q.z >> 4) & kLo4, a1.z, s);
-      s = dot4((q.w >> 4) & kLo4, a1.w, s);
+      s = dot4(lo[0], a0.x, s);
+      s = dot4(lo[1], a0.y, s);
+      s = dot4(lo[2], a0.z, s);
+      s = dot4(lo[3], a0.w, s);
+      s = dot4(hi[0], a1.x, s);
+      s = dot4(hi[1], a1.y, s);
+      s = dot4(hi[2], a1.z, s);
+      s = dot4(hi[3], a1.w, s);
       sa = dot4(kOnes, a0.x, sa);
       sa = dot4(kOnes, a0.y, sa);
       sa = dot4(kOnes, a0.z, sa);
@@ -523,7 +544,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_0_kernel(
       sa = dot4(kOnes, a1.y, sa);
       sa = dot4(kOnes, a1.z, sa);
       sa = dot4(kOnes, a1.w, sa);
-      s -= 8 * sa;  // nibbles are stored as q + 8
+      s -= kBias * sa;  // codes are stored as value + bias
       acc += static_cast<float>(s) * (f16_to_f32(D[j]) * dA[b]);
       if constexpr (SUMS) sums[static_cast<size_t>(row) * nb + b] = s;
     }
@@ -693,11 +714,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_reg(
 
 // Q8_0 x Q8_0 and Q4_0 x Q8_0, register-resident activations: lane b of pass P
 // holds the 32 codes, d and (for Q4_0) the code sum of activation block P*64 + b.
-template <int NW, int NP, bool Q4, bool SUMS>
+constexpr int kFmtQ8_0 = 0, kFmtQ4_0 = 1, kFmtQ5_0 = 2;
+
+template <int NW, int NP, int FMT, bool SUMS>
 __global__ __launch_bounds__(NW * 64) void gemv_q80_reg(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
-  constexpr int kWB = Q4 ? kQ4_0Bytes : kQ8_0Bytes;
+  constexpr bool Q4 = FMT != kFmtQ8_0;  // nibble formats (Q4_0, Q5_0)
+  constexpr bool Q5 = FMT == kFmtQ5_0;
+  constexpr int kWB = (FMT == kFmtQ4_0) ? kQ4_0Bytes : Q5 ? kQ5_0Bytes : kQ8_0Bytes;
+  constexpr int kQs = Q5 ? 6 : 2;
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * NW + wave_id();
   const int nwaves = gridDim.x * NW;
@@ -723,18 +749,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_q80_reg(
       sa = dot4(kOnes, A1[p].z, sa);
       sa = dot4(kOnes, A1[p].w, sa);
     }
-    ASUM[p] = 8 * sa;
+    ASUM[p] = (Q5 ? 16 : 8) * sa;  // codes are stored as value + bias
   }
 
   for (int row = wave; row < n_out; row += nwaves) {
     const uint8_t* wrow = W + static_cast<size_t>(row) * rb;
     uint4 Q0[NP], Q1[NP];
-    uint32_t D[NP];
+    uint32_t D[NP], QH[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 64 + lane, nb - 1) * kWB);
       D[p] = *reinterpret_cast<const uint16_t*>(q);
-      Q0[p] = load_u2<uint4>(q + 2);
+      if constexpr (Q5) QH[p] = load_u2<uint32_t>(q + 2);
+      Q0[p] = load_u2<uint4>(q + kQs);
       if constexpr (!Q4) Q1[p] = load_u2<uint4>(q + 18);
     }
     float acc = 0.0f;
@@ -745,15 +772,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_q80_reg(
       int s = 0;
       if constexpr (Q4) {
         const uint4 q = Q0[p];
-        s = dot4(q.x & kLo4, A0[p].x, s);
-        s = dot4(q.y & kLo4, A0[p].y, s);
-        s = dot4(q.z & kLo4, A0[p].z, s);
-        s = dot4(q.w & kLo4, A0[p].w, s);
-        s = dot4((q.x >> 4) & kLo4, A1[p].x, s);
-        s = dot4((q.y >> 4) & kLo4, A1[p].y, s);
-        s = dot4((q.z >> 4) & kLo4, A1[p].z, s);
-        s = dot4((q.w >> 4) & kLo4, A1[p].w, s);
-        s -= ASUM[p];  // nibbles are stored as q + 8
+        uint32_t lo[4] = {q.x & kLo4, q.y & kLo4, q.z & kLo4, q.w & kLo4};
+        uint32_t hi[4] = {(q.x >> 4) & kLo4, (q.y >> 4) & kLo4, (q.z >> 4) & kLo4, (q.w >> 4) & kLo4};
+        if constexpr (Q5) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            lo[k] = q5_codes(lo[k], QH[p], 4 * k);
+            hi[k] = q5_codes(hi[k], QH[p], 16 + 4 * k);
+          }
+        }
+        s = dot4(lo[0], A0[p].x, s);
+        s = dot4(lo[1], A0[p].y, s);
+        s = dot4(lo[2], A0[p].z, s);
+        s = dot4(lo[3], A0[p].w, s);
+        s = dot4(hi[0], A1[p].x, s);
+        s = dot4(hi[1], A1[p].y, s);
+        s = dot4(hi[2], A1[p].z, s);
+        s = dot4(hi[3], A1[p].w, s);
+        s -= ASUM[p];  // codes are stored as value + bias
       } else {
         s = dot4(Q0[p].x, A0[p].x, s);
         s = dot4(Q0[p].y, A0[p].y, s);
@@ -810,7 +846,8 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
     case kQ4_K:
     case kQ6_K: return align16(n_in / 256 * kQ8_KBytes);
     case kQ8_0:
-    case kQ4_0: return LayoutQ80(n_in / 32).bytes;
+    case kQ4_0:
+    case kQ5_0: return LayoutQ80(n_in / 32).bytes;
     default: return -1;
   }
 }
@@ -847,14 +884,20 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
     case kQ8_0: {
       const int nb = static_cast<int>(n_in / 32);
       const int passes = (nb + 63) / 64;
-      if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, false, true>)) : QK_ROWS((gemv_q80_reg<4, 1, false, false>));
+      if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, kFmtQ8_0, true>)) : QK_ROWS((gemv_q80_reg<4, 1, kFmtQ8_0, false>));
       return S ? QK_LDS((gemv_q8_0_kernel<kWaves, 2, true>)) : QK_LDS((gemv_q8_0_kernel<kWaves, 2, false>));
     }
     case kQ4_0: {
       const int nb = static_cast<int>(n_in / 32);
       const int passes = (nb + 63) / 64;
-      if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, true, true>)) : QK_ROWS((gemv_q80_reg<4, 1, true, false>));
-      return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, false>));
+      if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, kFmtQ4_0, true>)) : QK_ROWS((gemv_q80_reg<4, 1, kFmtQ4_0, false>));
+      return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, false, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, false, false>));
+    }
+    case kQ5_0: {
+      const int nb = static_cast<int>(n_in / 32);
+      const int passes = (nb + 63) / 64;
+      if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, kFmtQ5_0, true>)) : QK_ROWS((gemv_q80_reg<4, 1, kFmtQ5_0, false>));
+      return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, false>));
     }
     default:
       return hipErrorInvalidValue;

@@ -7,12 +7,17 @@
 
 namespace qk {
 
-enum WType : int { kQ4_0 = 2, kQ8_0 = 8, kQ4_K = 12, kQ6_K = 14, kQ8_K = 15 };
+enum WType : int { kQ4_0 = 2, kQ4_1 = 3, kQ5_0 = 6, kQ8_0 = 8, kQ4_K = 12, kQ6_K = 14, kQ8_K = 15 };
 
 // Activation quantization of `nblocks` consecutive blocks (any number of columns
 // laid end to end: blocks of consecutive columns are contiguous).
 hipError_t launch_quantize(int act_type, const float* x, uint8_t* xq, int64_t nblocks,
                            hipStream_t s);
+
+// Weight quantization (quantize_row_*_ref) of `nblocks` 32-element blocks of
+// type Q8_0, Q4_0, Q4_1 or Q5_0.
+hipError_t launch_quantize_row(int type, const float* x, uint8_t* dst, int64_t nblocks,
+                               hipStream_t s);
 
 // One GEMV over one activation column.  `sums` non-null selects the variant that
 // stores the per-block integers (and `y` may be null).  ev_start / ev_stop, when

@@ -12,9 +12,9 @@ Recipes (one numpy default_rng(seed) per workload, drawn in the order listed):
 """
 import numpy as np
 
-Q4_0, Q8_0, Q4_K, Q6_K, Q8_K = 2, 8, 12, 14, 15
-BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q8_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q8_K: 292}
+Q4_0, Q4_1, Q5_0, Q8_0, Q4_K, Q6_K, Q8_K = 2, 3, 6, 8, 12, 14, 15
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q8_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q8_K: 292}
 
 
 def uniform_bytes(rng, shape):
@@ -43,6 +43,23 @@ def q4_0_blocks(rng, n_out, n_in, d_range=(1e-3, 4e-3)):
     return b.reshape(n_out, nb * 18)
 
 
+def q4_1_blocks(rng, n_out, n_in, d_range=(1e-3, 4e-3), m_range=(-0.03, -0.005)):
+    """Q4_1 rows: f16 d ~ U[d_range], f16 m ~ U[m_range], 16 uniform qs bytes."""
+    nb = n_in // 32
+    b = uniform_bytes(rng, (n_out, nb, 20))
+    b[:, :, 0:2] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    b[:, :, 2:4] = _f16_bytes(rng.uniform(*m_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 20)
+
+
+def q5_0_blocks(rng, n_out, n_in, d_range=(5e-4, 2e-3)):
+    """Q5_0 rows: f16 d ~ U[d_range]; the 4 qh bytes and 16 qs bytes uniform."""
+    nb = n_in // 32
+    b = uniform_bytes(rng, (n_out, nb, 22))
+    b[:, :, 0:2] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 22)
+
+
 def q4_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
     """Q4_K rows: f16 d, dmin ~ U[d_range]; 12 scale bytes and 128 qs bytes uniform."""
     nb = n_in // 256
@@ -62,7 +79,8 @@ def q6_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
 
 
 def weight_blocks(rng, t, n_out, n_in):
-    return {Q4_0: q4_0_blocks, Q4_K: q4_K_blocks, Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
+    return {Q4_0: q4_0_blocks, Q4_1: q4_1_blocks, Q5_0: q5_0_blocks, Q4_K: q4_K_blocks,
+            Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
 
 
 def gaussian(rng, shape, std=1.0):
@@ -102,6 +120,12 @@ def q6_K_head_32000x4096():
     """Q6_K output head 32000x4096; x[4096]."""
     rng = np.random.default_rng(3)
     return {"W": q6_K_blocks(rng, 32000, 4096), "x": gaussian(rng, (4096,))}
+
+
+def q5_0_gemv_4096x4096():
+    """Q5_0 GEMV 4096x4096 (Q8_0 activations); x ~N(0,1)[4096]."""
+    rng = np.random.default_rng(6)
+    return {"W": q5_0_blocks(rng, 4096, 4096), "x": gaussian(rng, (4096,))}
 
 
 def q4_K_batched_14336x4096():

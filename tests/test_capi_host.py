@@ -43,8 +43,9 @@ def test_library_is_built_for_gfx950_only():
 
 
 def test_geometry_matches_type_table():
-    ids = {"Q4_0": qk.QK_TYPE_Q4_0, "Q8_0": qk.QK_TYPE_Q8_0, "Q4_K": qk.QK_TYPE_Q4_K,
-           "Q6_K": qk.QK_TYPE_Q6_K, "Q8_K": qk.QK_TYPE_Q8_K}
+    ids = {"Q4_0": qk.QK_TYPE_Q4_0, "Q4_1": qk.QK_TYPE_Q4_1, "Q5_0": qk.QK_TYPE_Q5_0,
+           "Q8_0": qk.QK_TYPE_Q8_0, "Q4_K": qk.QK_TYPE_Q4_K, "Q6_K": qk.QK_TYPE_Q6_K,
+           "Q8_K": qk.QK_TYPE_Q8_K}
     for name, gid, elems, nbytes, _ in rows("type_table.txt"):
         assert ids[name] == int(gid)
         assert qk.qk_block_elems(ids[name]) == int(elems)
@@ -54,7 +55,9 @@ def test_geometry_matches_type_table():
     assert qk.qk_row_bytes(qk.QK_TYPE_Q6_K, 11008) == 9030
     assert qk.qk_row_bytes(qk.QK_TYPE_Q4_0, 100) == 0
     assert qk.qk_row_bytes(99, 256) == 0
-    assert qk.qk_block_elems(3) == 0
+    assert qk.qk_row_bytes(qk.QK_TYPE_Q5_0, 4096) == 2816
+    assert qk.qk_row_bytes(qk.QK_TYPE_Q4_1, 4096) == 2560
+    assert qk.qk_block_elems(7) == 0
 
 
 def test_pairing():
@@ -62,7 +65,9 @@ def test_pairing():
     assert qk.qk_act_type(qk.QK_TYPE_Q8_0) == qk.QK_TYPE_Q8_0
     assert qk.qk_act_type(qk.QK_TYPE_Q4_K) == qk.QK_TYPE_Q8_K
     assert qk.qk_act_type(qk.QK_TYPE_Q6_K) == qk.QK_TYPE_Q8_K
+    assert qk.qk_act_type(qk.QK_TYPE_Q5_0) == qk.QK_TYPE_Q8_0
     assert qk.qk_act_type(qk.QK_TYPE_Q8_K) == -1
+    assert qk.qk_act_type(qk.QK_TYPE_Q4_1) == -1   # its partner Q8_1 is only named
 
 
 def test_max_n_in_covers_llm_shapes():
@@ -70,6 +75,7 @@ def test_max_n_in_covers_llm_shapes():
         m = qk.qk_max_n_in(t)
         assert m >= 28672 and m % qk.qk_block_elems(t) == 0
     assert qk.qk_max_n_in(qk.QK_TYPE_Q8_K) == 0
+    assert qk.qk_max_n_in(qk.QK_TYPE_Q4_1) == 0
 
 
 P = ctypes.c_void_p
@@ -92,9 +98,24 @@ def test_quantize_validation():
     assert _status("qk_quantize_act", qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, 0, None) == 0  # no-op
 
 
+def test_quantize_row_validation():
+    f = "qk_quantize_row"
+    assert _status(f, qk.QK_TYPE_Q4_K, GOOD, GOOD, 256, None) == 1   # only 32-element types
+    assert _status(f, qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, None) == 1
+    assert _status(f, 99, GOOD, GOOD, 32, None) == 1
+    assert _status(f, qk.QK_TYPE_Q4_1, GOOD, GOOD, 48, None) == 3
+    assert _status(f, qk.QK_TYPE_Q5_0, GOOD, GOOD, -32, None) == 3
+    assert _status(f, qk.QK_TYPE_Q4_0, None, GOOD, 32, None) == 5
+    assert _status(f, qk.QK_TYPE_Q4_0, GOOD, None, 32, None) == 5
+    assert _status(f, qk.QK_TYPE_Q8_0, ODD, GOOD, 32, None) == 4
+    assert _status(f, qk.QK_TYPE_Q8_0, GOOD, ODD, 32, None) == 4
+    assert _status(f, qk.QK_TYPE_Q5_0, None, None, 0, None) == 0     # no-op
+
+
 def test_gemv_validation():
     f = "qk_gemv"
     assert _status(f, qk.QK_TYPE_Q8_K, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
+    assert _status(f, qk.QK_TYPE_Q4_1, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
     assert _status(f, 5, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
     assert _status(f, qk.QK_TYPE_Q4_K, GOOD, 4, 255, GOOD, 1, GOOD, None) == 3
     assert _status(f, qk.QK_TYPE_Q4_K, GOOD, 4, 0, GOOD, 1, GOOD, None) == 3

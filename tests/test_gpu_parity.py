@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 T8_0, T4_0, T4K, T6K, T8K = (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q4_K,
                              qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q8_K)
+T4_1, T5_0 = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_0
 Y_TOL = 1e-5
 
 
@@ -118,6 +119,90 @@ def test_quantize_act_many_columns(torch_cuda):
 
 
 # ---------------------------------------------------------------------------
+# qk_quantize_row (weight quantizers)
+# ---------------------------------------------------------------------------
+
+def _cl_inputs(n):
+    # codeloopback Example 14's inputs: ((i * 7919) mod 1001 - 500) / 337 in f32
+    i = np.arange(n)
+    return (((i * 7919) % 1001) - 500).astype(np.float32) / np.float32(337)
+
+
+def _weight_rows(rng, n):
+    """Finite weight rows (n a multiple of 32) that exercise the quantizers' edges:
+    ties for the largest magnitude, signed zeros, constant and all-zero blocks,
+    f16-subnormal and f16-overflowing scales, f32 subnormals."""
+    rows = [rng.standard_normal(n).astype(np.float32) * np.float32(0.02),
+            (rng.standard_normal(n) * 50).astype(np.float32),
+            np.zeros(n, np.float32),
+            np.full(n, -0.0, np.float32),
+            np.full(n, 0.75, np.float32),
+            (rng.standard_normal(n) * 1e-39).astype(np.float32),     # 1/d overflows
+            (rng.standard_normal(n) * 3e-37).astype(np.float32),     # 1/d near FLT_MAX
+            (rng.standard_normal(n) * 1e-6).astype(np.float32),
+            (rng.standard_normal(n) * 3e5).astype(np.float32),
+            (rng.standard_normal(n) * 1e37).astype(np.float32),
+            rng.integers(-16, 16, n).astype(np.float32)]
+    t = rng.standard_normal(n).astype(np.float32)
+    blocks = t.reshape(-1, 32)
+    for b in range(blocks.shape[0]):
+        i, j = rng.choice(32, 2, replace=False)
+        a = np.float32(3.0 + b % 5)
+        blocks[b, i], blocks[b, j] = a, -a          # equal magnitudes, opposite signs
+    rows.append(t)
+    z = rng.standard_normal(n).astype(np.float32)
+    z[rng.integers(0, 2, n) == 1] = 0.0
+    z[::3] = -0.0
+    zb = z.reshape(-1, 32)
+    zb[::2] = np.where(rng.integers(0, 2, zb[::2].shape) == 1, -0.0, 0.0)  # all-zero blocks
+    rows.append(z)
+    s = np.abs(rng.standard_normal(n)).astype(np.float32) + np.float32(2)   # min > 0
+    rows.append(s)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0])
+def test_quantize_row_bit_exact(torch_cuda, t):
+    rng = np.random.default_rng(500 + t)
+    for n in (32, 96, 4096, 32 * 1001):
+        say("quantize_row", t, n)
+        X = _weight_rows(rng, n)
+        for r in range(X.shape[0]):
+            got = host(qk.qk_quantize_row(t, dev(torch_cuda, X[r])))
+            want = orc.quantize(t, X[r])
+            bad = np.nonzero((got.reshape(-1, orc.block_bytes(t)) !=
+                              want.reshape(-1, orc.block_bytes(t))).any(axis=1))[0]
+            assert bad.size == 0, f"type {t} n {n} row {r}: blocks {bad[:8].tolist()} differ"
+
+
+def test_quantize_row_page_hex_example_14(torch_cuda):
+    # the printed block bytes of codeloopback Example 14, straight from the GPU
+    from golden_io import rows
+    say("quantize_row Example 14")
+    x = _cl_inputs(64)
+    x[40] = np.float32(9.5)
+    types = {"Q8_0": T8_0, "Q4_0": T4_0, "Q4_1": T4_1, "Q5_0": T5_0}
+    xd = dev(torch_cuda, x)
+    for blk, name, hexs in rows("hex_crosscheck.txt"):
+        got = host(qk.qk_quantize_row(types[name], xd))
+        bb = len(hexs) // 2
+        assert got[int(blk) * bb:(int(blk) + 1) * bb].tobytes().hex() == hexs, (blk, name)
+
+
+def test_quantize_row_full_4096x11008(torch_cuda):
+    # a whole weight matrix quantized in one call, as a model loader would
+    rng = np.random.default_rng(512)
+    Wf = synth.gaussian(rng, (4096, 11008), 0.02)
+    Wd = dev(torch_cuda, Wf)
+    for t in (T4_0, T4_1, T5_0, T8_0):
+        say("quantize_row full", t)
+        got = host(qk.qk_quantize_row(t, Wd)).reshape(4096, -1)
+        pick = np.unique(np.concatenate([np.arange(8), rng.integers(0, 4096, 24), [4095]]))
+        want = orc.quantize(t, Wf[pick])
+        assert np.array_equal(got[pick], want.reshape(len(pick), -1)), t
+
+
+# ---------------------------------------------------------------------------
 # qk_dequantize_row
 # ---------------------------------------------------------------------------
 
@@ -127,14 +212,14 @@ def _edge_scale_blocks(t, rng, nblocks):
     b = weights(rng, t, 1, n).reshape(nblocks, -1).copy()
     specials = np.array([0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF, 0x3C00, 0xBC00, 0x0000],
                         dtype=np.uint16).view(np.uint8).reshape(-1, 2)
-    offs = {T8_0: [0], T4_0: [0], T4K: [0, 2], T6K: [208]}[t]
+    offs = {T8_0: [0], T4_0: [0], T4_1: [0, 2], T5_0: [0], T4K: [0, 2], T6K: [208]}[t]
     for i in range(nblocks):
         for o in offs:
             b[i, o:o + 2] = specials[(i + o) % len(specials)]
     return b.reshape(-1)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T4K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0, T4K, T6K])
 def test_dequantize_bit_exact(torch_cuda, t):
     rng = np.random.default_rng(200 + t)
     for nblocks in (1, 3, 17, 1000):
@@ -155,6 +240,7 @@ SHAPES = {
     T6K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T8_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (6, 28672)],
     T4_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (6, 28672)],
+    T5_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (6, 28672)],
 }
 
 
@@ -169,7 +255,7 @@ def _oracle_sums(t, W, xq, n_out, n_in, ncols):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T4K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4K, T6K])
 def test_gemv_block_sums_and_y(torch_cuda, t):
     rng = np.random.default_rng(300 + t)
     at = orc.act_type(t)
@@ -240,7 +326,7 @@ def test_batched_q4_K_extreme_codes(torch_cuda):
 
 def test_gemv_max_row_length(torch_cuda):
     rng = np.random.default_rng(31)
-    for t in (T4K, T6K, T8_0, T4_0):
+    for t in (T4K, T6K, T8_0, T4_0, T5_0):
         n_in = qk.qk_max_n_in(t)
         say("gemv max n_in", t, n_in)
         W = weights(rng, t, 3, n_in)
@@ -254,7 +340,7 @@ def test_gemv_max_row_length(torch_cuda):
 def test_gemv_zero_activation_gives_zero(torch_cuda):
     # rml ZeroActivationsGiveZero
     rng = np.random.default_rng(5)
-    for t in (T4K, T6K, T8_0, T4_0):
+    for t in (T4K, T6K, T8_0, T4_0, T5_0):
         W = weights(rng, t, 8, 1024)
         xq = qk.qk_quantize_act(orc.act_type(t), torch_cuda.zeros((1, 1024), device="cuda"))
         y = host(qk.qk_gemv(t, dev(torch_cuda, W), 8, 1024, xq, 1))
@@ -295,7 +381,8 @@ def test_graph_capture_replays_match_eager(torch_cuda):
     torch = torch_cuda
     rng = np.random.default_rng(9)
     cases = [(T4K, 64, 11008, 1), (T4K, 300, 4096, 1), (T6K, 70, 4096, 1), (T8_0, 50, 4096, 1),
-             (T4_0, 33, 1024, 1), (T4K, 200, 4096, 16), (T4K, 90, 2048, 64)]
+             (T4_0, 33, 1024, 1), (T5_0, 41, 4096, 1), (T4K, 200, 4096, 16),
+             (T4K, 90, 2048, 64)]
     bufs = []
     for t, n_out, n_in, nc in cases:
         W = dev(torch, weights(rng, t, n_out, n_in))
@@ -371,6 +458,12 @@ def test_full_q4_0_and_q4_K_4096x4096(torch_cuda):
     _check_full(torch_cuda, T4_0, d["W_q4_0"], 4096, 4096, d["x"][None, :], what="Q4_0 4096^2")
     say("full Q4_K 4096x4096")
     _check_full(torch_cuda, T4K, d["W_q4_K"], 4096, 4096, d["x"][None, :], what="Q4_K 4096^2")
+
+
+def test_full_q5_0_4096x4096(torch_cuda):
+    d = synth.q5_0_gemv_4096x4096()
+    say("full Q5_0 4096x4096")
+    _check_full(torch_cuda, T5_0, d["W"], 4096, 4096, d["x"][None, :], what="Q5_0 4096^2")
 
 
 def test_full_ffn_7b(torch_cuda):
