@@ -44,7 +44,8 @@ CSRC = os.path.join(ROOT, "quantized_gemv_quantize_amd", "csrc")
 # these files are unchanged since the counters were taken
 KERNEL_SOURCES = {"gemv": ["qk_gemv.hip", "qk_device.h", "qk_internal.h"],
                   "gemm": ["qk_gemm.hip", "qk_device.h", "qk_internal.h"],
-                  "dequant": ["qk_dequant.hip", "qk_device.h", "qk_internal.h"]}
+                  "dequant": ["qk_dequant.hip", "qk_device.h", "qk_internal.h"],
+                  "quantize_row": ["qk_quantize.hip", "qk_device.h", "qk_internal.h"]}
 METRIC = "quantized GEMV weight GB/s and % of HBM peak (Q4_K/Q6_K/Q8_0, batch 1)"
 
 
@@ -59,6 +60,7 @@ def log(*a):
 
 def workloads(qk):
     T4K, T6K, T40, T80 = qk.QK_TYPE_Q4_K, qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q8_0
+    T50 = qk.QK_TYPE_Q5_0
     T8K = qk.QK_TYPE_Q8_K
     return {
         "q4_K_decode_4096x11008": {
@@ -67,6 +69,8 @@ def workloads(qk):
             "gemvs": [("W_q4_K", T4K, 4096, 4096, "x")], "acts": {"x": (T8K, 4096, 1)}},
         "q4_0_4096x4096": {
             "gemvs": [("W_q4_0", T40, 4096, 4096, "x")], "acts": {"x": (T80, 4096, 1)}},
+        "q5_0_4096x4096": {
+            "gemvs": [("W", T50, 4096, 4096, "x")], "acts": {"x": (T80, 4096, 1)}},
         "ffn_7b_q4_K_q6_K": {
             "gemvs": [("gate", T4K, 11008, 4096, "x"), ("up", T4K, 11008, 4096, "x"),
                       ("down", T6K, 4096, 11008, "x2")],
@@ -82,6 +86,9 @@ def workloads(qk):
         # qk_dequantize_row of the whole Q6_K head matrix to f32 (no activations)
         "q6_K_dequantize_32000x4096": {
             "gemvs": [("W", T6K, 32000, 4096, None)], "acts": {}, "dequant": True},
+        # qk_quantize_row of an f32 weight matrix to Q4_0 blocks (no activations)
+        "q4_0_quantize_row_4096x11008": {
+            "gemvs": [("W_f32", T40, 4096, 11008, None)], "acts": {}, "quantize_row": True},
     }
 
 
@@ -101,6 +108,10 @@ def host_inputs(name, qk):
         return {"W": d["W"], "X": d["X"]}
     if name == "q8_0_256x1024":
         return synth.q8_0_gemv_256x1024()
+    if name == "q5_0_4096x4096":
+        return synth.q5_0_gemv_4096x4096()
+    if name == "q4_0_quantize_row_4096x11008":
+        return synth.f32_weights_4096x11008()
     raise KeyError(name)
 
 
@@ -126,6 +137,8 @@ def gpu_copy_like(torch, w_type, n_out, n_in, gen):
         w[:, :, 208:210] = f16(1e-4, 1e-3)
     elif w_type == synth.Q4_0:
         w[:, :, 0:2] = f16(1e-3, 4e-3)
+    elif w_type == synth.Q5_0:
+        w[:, :, 0:2] = f16(5e-4, 2e-3)
     else:
         raise ValueError("GPU copies are drawn for block-byte weight formats only")
     return w.reshape(n_out, nb * bb)
@@ -148,6 +161,13 @@ def cpu_baseline(name, wl, inputs, seconds):
                 sample_rows[wname] = rows
                 orc.dequantize(wt, W[:rows], rows * n_in)
                 done_bytes += rows * W.shape[1] + 4 * rows * n_in
+        if wl.get("quantize_row"):
+            for wname, wt, n_out, n_in, _ in wl["gemvs"]:
+                W = inputs[wname]
+                rows = min(n_out, max(1, int(4e6 // n_in)))
+                sample_rows[wname] = rows
+                b = orc.quantize(wt, W[:rows])
+                done_bytes += 4 * rows * n_in + b.size
         for key, (at, n, ncols) in wl["acts"].items():
             x = inputs[key] if inputs[key].ndim == 2 else inputs[key][None, :]
             xq = orc.quantize(at, x[:ncols])
@@ -165,13 +185,21 @@ def cpu_baseline(name, wl, inputs, seconds):
     dt = time.perf_counter() - t0
     desc = ", ".join(f"{k}: first {r} rows" for k, r in sample_rows.items())
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{desc}; {'dequantize' if wl.get('dequant') else 'quantize + GEMV'} repeated "
+            "sample": f"{desc}; {_kind(wl)} repeated "
                       f"{reps}x in {dt:.1f} s, single thread"}
+
+
+def _kind(wl):
+    if wl.get("dequant"):
+        return "dequantize"
+    return "weight quantize" if wl.get("quantize_row") else "quantize + GEMV"
 
 
 def kernel_family(workload):
     if workload.startswith("q4_K_batched"):
         return "gemm"
+    if "quantize_row" in workload:
+        return "quantize_row"
     return "dequant" if "dequantize" in workload else "gemv"
 
 
@@ -208,11 +236,12 @@ def recorded_traffic(workload):
 
 def algorithmic_bytes(wl, qk):
     """Weights + activation blocks + f32 outputs of the GEMV launches of one step
-    (for a dequantize workload: the blocks read plus the f32 values written)."""
+    (for a dequantize workload: the blocks read plus the f32 values written; for a
+    weight-quantize workload: the f32 values read plus the blocks written)."""
     total = 0
     for _, wt, n_out, n_in, akey in wl["gemvs"]:
-        if wl.get("dequant"):
-            total += qk.qk_row_bytes(wt, n_in) * n_out + 4 * n_out * n_in  # read blocks, write f32
+        if wl.get("dequant") or wl.get("quantize_row"):
+            total += qk.qk_row_bytes(wt, n_in) * n_out + 4 * n_out * n_in
             continue
         at, n, ncols = wl["acts"][akey]
         total += qk.qk_row_bytes(wt, n_in) * n_out + qk.qk_row_bytes(at, n) * ncols + 4 * n_out * ncols
@@ -233,7 +262,7 @@ def _is_calib(name):
 
 
 def _is_family(name, family):
-    """Library kernels of one family: gemv_*, gemm_* or dequant_* (not quantize)."""
+    """Library kernels of one family: gemv_*, gemm_*, dequant_* or quantize_row_*."""
     return "qk::" in name and f"{family}_" in name
 
 
@@ -364,14 +393,21 @@ def main():
         inputs["W"] = qk.qk_quantize_act(qk.QK_TYPE_Q8_0, Wf).cpu().numpy()
 
     step_w_bytes = sum(qk.qk_row_bytes(t, n_in) * n_out for _, t, n_out, n_in, _ in wl["gemvs"])
-    copies = max(1, -(-ROTATE_BYTES // step_w_bytes))
+    quant_row = bool(wl.get("quantize_row"))
+    # the rotated inputs: weight blocks, or the f32 weights a weight-quantize step reads
+    resident = (sum(4 * n_out * n_in for _, _, n_out, n_in, _ in wl["gemvs"]) if quant_row
+                else step_w_bytes)
+    copies = max(1, -(-ROTATE_BYTES // resident))
     dev_w = []  # per copy: list of weight tensors, one per GEMV
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
     for c in range(copies):
         mats = []
         for wname, wt, n_out, n_in, _ in wl["gemvs"]:
-            if c == 0 or wt == qk.QK_TYPE_Q8_0:
+            if quant_row and c > 0:
+                # f32 weights N(0, 0.02), as synth's draw, from the seeded generator
+                mats.append(torch.randn((n_out, n_in), device="cuda", generator=gen) * 0.02)
+            elif c == 0 or wt == qk.QK_TYPE_Q8_0:
                 src = torch.from_numpy(np.ascontiguousarray(inputs[wname])).cuda()
                 mats.append(src if c == 0 else src.clone())
             else:
@@ -386,6 +422,9 @@ def main():
     if wl.get("dequant"):
         ys = [torch.empty((n_out * n_in,), dtype=torch.float32, device="cuda")
               for _, _, n_out, n_in, _ in wl["gemvs"]]
+    elif quant_row:
+        ys = [torch.empty((qk.qk_row_bytes(wt, n_in) * n_out,), dtype=torch.uint8, device="cuda")
+              for _, wt, n_out, n_in, _ in wl["gemvs"]]
     else:
         ys = [torch.empty((ncols_of(wl, akey), n_out), dtype=torch.float32, device="cuda")
               for _, _, n_out, _, akey in wl["gemvs"]]
@@ -400,10 +439,13 @@ def main():
         for key, (at, xf, xq) in acts.items():
             qk.qk_quantize_act(at, xf, xq)
         for g, (wname, wt, n_out, n_in, akey) in enumerate(wl["gemvs"]):
-            if wl.get("dequant"):
+            if wl.get("dequant") or quant_row:
                 if evs is not None:
                     evs[g][0].record(stream)
-                qk.qk_dequantize_row(wt, mats[g], n_out * n_in, ys[g])
+                if quant_row:
+                    qk.qk_quantize_row(wt, mats[g], ys[g])
+                else:
+                    qk.qk_dequantize_row(wt, mats[g], n_out * n_in, ys[g])
                 if evs is not None:
                     evs[g][1].record(stream)
                 continue
@@ -440,8 +482,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed_ms = t_start.elapsed_time(t_stop)
-    # weight bytes per step; a dequantize workload counts the blocks read plus the f32 written
-    value_bytes = algorithmic_bytes(wl, qk) if wl.get("dequant") else step_w_bytes
+    # weight bytes per step; a dequantize workload counts the blocks read plus the f32
+    # written, a weight-quantize workload the f32 read plus the blocks written
+    value_bytes = algorithmic_bytes(wl, qk) if (wl.get("dequant") or quant_row) else step_w_bytes
     value = value_bytes * args.steps / (elapsed_ms / 1e3) / 1e9
 
     # Region B - the same K steps launched one by one; each GEMV launch records

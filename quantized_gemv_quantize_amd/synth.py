@@ -128,6 +128,12 @@ def q5_0_gemv_4096x4096():
     return {"W": q5_0_blocks(rng, 4096, 4096), "x": gaussian(rng, (4096,))}
 
 
+def f32_weights_4096x11008():
+    """f32 weights N(0, 0.02) [4096, 11008], to be quantized to GGUF blocks."""
+    rng = np.random.default_rng(7)
+    return {"W_f32": gaussian(rng, (4096, 11008), 0.02)}
+
+
 def q4_K_batched_14336x4096():
     """Q4_K 14336x4096 with 64 token columns X[64, 4096] (16-column case = first 16)."""
     rng = np.random.default_rng(4)

@@ -192,7 +192,7 @@ def test_quantize_row_page_hex_example_14(torch_cuda):
 def test_quantize_row_full_4096x11008(torch_cuda):
     # a whole weight matrix quantized in one call, as a model loader would
     rng = np.random.default_rng(512)
-    Wf = synth.gaussian(rng, (4096, 11008), 0.02)
+    Wf = synth.f32_weights_4096x11008()["W_f32"]
     Wd = dev(torch_cuda, Wf)
     for t in (T4_0, T4_1, T5_0, T8_0):
         say("quantize_row full", t)
