@@ -51,6 +51,8 @@ def lib():
         L.orc_vec_dot.argtypes = [i32, p, p, i64, p, p]
         L.orc_gemv.restype = i32
         L.orc_gemv.argtypes = [i32, p, i64, i64, p, i64, p, p]
+        L.orc_swiglu.restype = i32
+        L.orc_swiglu.argtypes = [p, p, i64, p]
         _lib = L
     return _lib
 
@@ -152,3 +154,13 @@ def gemv(wt, W, n_out, n_in, xq, ncols=1):
     _check(lib().orc_gemv(wt, _ptr(_u8(W)), n_out, n_in, _ptr(_u8(xq)), ncols, _ptr(y),
                           _ptr(l1)), "gemv")
     return y, l1
+
+
+def swiglu(g, u):
+    """h = silu(g) * u in f64 from f32 g and u of the same shape."""
+    g32 = np.ascontiguousarray(g, dtype=np.float32)
+    u32 = np.ascontiguousarray(u, dtype=np.float32)
+    assert g32.shape == u32.shape
+    h = np.zeros(g32.shape, dtype=np.float64)
+    _check(lib().orc_swiglu(_ptr(g32), _ptr(u32), g32.size, _ptr(h)), "swiglu")
+    return h

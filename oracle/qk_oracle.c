@@ -646,3 +646,19 @@ int orc_gemv(int wt, const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_
   }
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------- */
+/* The gated activation between an FFN's gate / up and down projections.      */
+/* The pages stop at the products; the 7B-shape layers that the FFN workload   */
+/* follows combine them as SwiGLU: h = silu(g) * u with silu(v) = v * sigmoid(v) */
+/* = v / (1 + e^-v).  Evaluated in double from the f32 gate and up outputs.    */
+/* ------------------------------------------------------------------------- */
+
+int orc_swiglu(const float* g, const float* u, int64_t n, double* h) {
+  if (n < 0) return ORC_BAD_SHAPE;
+  for (int64_t i = 0; i < n; ++i) {
+    double v = (double)g[i];
+    h[i] = v / (1.0 + exp(-v)) * (double)u[i];
+  }
+  return ORC_OK;
+}

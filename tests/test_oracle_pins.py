@@ -672,3 +672,35 @@ def test_gemv_is_vec_dot_per_row_and_column():
             for r_ in range(n_out):
                 v, s = o.vec_dot(t, W[rb * r_:rb * (r_ + 1)], xq[c], n_in)
                 assert y[c, r_] == F32(v) and l1[c, r_] == s
+
+
+# --------------------------------------------------------------------------
+# SwiGLU epilogue of the FFN step (not on the pages: silu(g) * u, silu(v) =
+# v * sigmoid(v)); pinned by closed forms of the logistic function.
+# --------------------------------------------------------------------------
+
+def test_swiglu_closed_forms():
+    ln3 = math.log(3.0)
+    g = np.array([0.0, ln3, -ln3, 50.0, -50.0, 2.0, -2.0, 1e-3], dtype=np.float32)
+    u = np.ones_like(g)
+    h = o.swiglu(g, u)
+    gd = g.astype(np.float64)
+    assert h[0] == 0.0
+    # sigmoid(ln 3) = 3/4 with slope 3/16 there; g holds ln 3 rounded to f32
+    d1 = gd[1] - ln3
+    assert abs(h[1] - gd[1] * (0.75 + 0.1875 * d1)) <= 1e-14
+    assert abs(h[2] - gd[2] * (0.25 - 0.1875 * d1)) <= 1e-14
+    assert abs(h[3] - 50.0) <= 1e-15 * 50 and abs(h[4]) < 1e-19                     # tails
+    # odd part: silu(v) - silu(-v) = v exactly in the reals
+    assert abs((h[5] - h[6]) - gd[5]) <= 1e-15
+    assert abs(h[7] - gd[7] * (0.5 + gd[7] / 4)) <= 1e-12                           # slope 1/2 at 0
+    # linear in u, sign follows u
+    u2 = np.array([2, -3, 0.5, 1, 1, -1, 4, 1], dtype=np.float32)
+    h2 = o.swiglu(g, u2)
+    assert np.allclose(h2, h * u2.astype(np.float64), rtol=1e-15, atol=0)
+
+
+def test_swiglu_large_negative_gate_is_zero_not_nan():
+    g = np.array([-1e30, -3.4e38, -89.0], dtype=np.float32)
+    h = o.swiglu(g, np.full(3, 7.0, np.float32))
+    assert np.all(np.isfinite(h)) and np.all(np.abs(h) < 1e-30)
