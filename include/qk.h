@@ -48,7 +48,13 @@ extern "C" {
 #define QK_E_ALIGN 4  /* a base pointer is not 16-byte aligned */
 #define QK_E_NULL 5   /* a required pointer is NULL */
 #define QK_E_DEVICE 6 /* the HIP runtime reported an error while enqueueing */
-#define QK_E_LIMIT 7  /* the activation row does not fit the kernels' LDS budget */
+#define QK_E_LIMIT 7  /* the activation row does not fit the kernels' LDS budget, or
+                         more activation columns than a call takes */
+#define QK_E_ARG 8    /* an argument outside its documented set of values */
+
+/* Epilogues of qk_gemv_pair. */
+#define QK_EPI_NONE 0
+#define QK_EPI_SWIGLU 1
 
 /* Elements per block (32 or 256) and bytes per block (Q4_0 18, Q4_1 20, Q5_0 22,
  * Q8_0 34, Q4_K 144, Q6_K 210, Q8_K 292) of a type, 0 for an unknown id.  Geometry
@@ -171,6 +177,29 @@ int qk_gemv_block_sums(int w_type, const void* W, int64_t n_out, int64_t n_in,
  */
 int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
                   int64_t ncols, float* y, void* stream, void* ev_start, void* ev_stop);
+
+/*
+ * qk_gemv_pair - the gate and up projections of an FFN layer in one launch: two
+ * GEMVs of the same shape over the same activation columns, y1 = W1 x and
+ * y2 = W2 x.  Each row is computed in both matrices from one load of the
+ * activation operands (rml "Kernels and references": one activation row feeding
+ * several weight rows).
+ *   w_type    QK_TYPE_Q4_K (else QK_E_TYPE); x blocks are Q8_K.
+ *   W1, W2    n_out rows of qk_row_bytes(w_type, n_in) bytes each, device.
+ *   n_out, n_in, xq, ncols   as qk_gemv; ncols <= 65535 (else QK_E_LIMIT).
+ *   epilogue  QK_EPI_NONE: out is f32 [ncols][2][n_out], y1 then y2 per column.
+ *             QK_EPI_SWIGLU: out is f32 [ncols][n_out], silu(y1) * y2 with
+ *             silu(v) = v / (1 + e^-v) in f32: the gated activation that the down
+ *             projection of the layer consumes (the pages stop at the products;
+ *             this is the SwiGLU form of the 7B-shape layers).
+ *             Any other value: QK_E_ARG.
+ * Every column runs the one-column GEMV kernels' arithmetic (same integer sums,
+ * float steps and summation order), so with ncols = 1 QK_EPI_NONE returns what
+ * qk_gemv returns bit for bit; with more columns qk_gemv uses the matrix cores and
+ * the two agree to within rounding.  Errors otherwise as qk_gemv.
+ */
+int qk_gemv_pair(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
+                 const void* xq, int64_t ncols, int epilogue, float* out, void* stream);
 
 #ifdef __cplusplus
 }

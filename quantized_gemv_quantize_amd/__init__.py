@@ -18,6 +18,8 @@ QK_TYPE_Q8_K = 15
 WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_K, QK_TYPE_Q6_K)
 DEQUANT_TYPES = WEIGHT_TYPES + (QK_TYPE_Q4_1,)
 QUANT_ROW_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q4_1, QK_TYPE_Q5_0)
+QK_EPI_NONE = 0
+QK_EPI_SWIGLU = 1
 TYPE_NAMES = {QK_TYPE_Q4_0: "Q4_0", QK_TYPE_Q4_1: "Q4_1", QK_TYPE_Q5_0: "Q5_0",
               QK_TYPE_Q8_0: "Q8_0", QK_TYPE_Q4_K: "Q4_K", QK_TYPE_Q6_K: "Q6_K",
               QK_TYPE_Q8_K: "Q8_K"}
@@ -68,6 +70,8 @@ def lib():
         L.qk_gemv_block_sums.argtypes = [i32, p, i64, i64, p, i64, p, p]
         L.qk_dequantize_row.restype = i32
         L.qk_dequantize_row.argtypes = [i32, p, p, i64, p]
+        L.qk_gemv_pair.restype = i32
+        L.qk_gemv_pair.argtypes = [i32, p, p, i64, i64, p, i64, i32, p, p]
         _lib = L
     return _lib
 
@@ -177,3 +181,16 @@ def qk_dequantize_row(t, src, n, dst=None, stream=None):
     _check(lib().qk_dequantize_row(t, _ptr(src), _ptr(dst), n, _stream(stream)),
            "qk_dequantize_row")
     return dst
+
+
+def qk_gemv_pair(w_type, W1, W2, n_out, n_in, xq, ncols=1, epilogue=QK_EPI_NONE, out=None,
+                 stream=None):
+    """Gate and up projections in one launch: out [ncols, 2, n_out] (y1, y2), or
+    [ncols, n_out] silu(y1) * y2 with epilogue=QK_EPI_SWIGLU."""
+    import torch
+    if out is None:
+        shape = (ncols, n_out) if epilogue == QK_EPI_SWIGLU else (ncols, 2, n_out)
+        out = torch.empty(shape, dtype=torch.float32, device=W1.device)
+    _check(lib().qk_gemv_pair(w_type, _ptr(W1), _ptr(W2), n_out, n_in, _ptr(xq), ncols, epilogue,
+                              _ptr(out), _stream(stream)), "qk_gemv_pair")
+    return out

@@ -133,7 +133,8 @@ const char* qk_status_str(int status) {
     case QK_E_ALIGN: return "a base pointer is not 16-byte aligned";
     case QK_E_NULL: return "a required pointer is NULL";
     case QK_E_DEVICE: return "HIP runtime error while enqueueing";
-    case QK_E_LIMIT: return "activation row exceeds the GEMV LDS budget";
+    case QK_E_LIMIT: return "activation row exceeds the GEMV LDS budget, or too many columns";
+    case QK_E_ARG: return "an argument outside its documented set of values";
     default: return "unknown status";
   }
 }
@@ -187,6 +188,21 @@ int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* 
 int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
                   int64_t ncols, float* y, void* stream, void* ev_start, void* ev_stop) {
   return gemv_impl(w_type, W, n_out, n_in, xq, ncols, y, nullptr, stream, ev_start, ev_stop);
+}
+
+int qk_gemv_pair(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
+                 const void* xq, int64_t ncols, int epilogue, float* out, void* stream) {
+  if (w_type != QK_TYPE_Q4_K) return QK_E_TYPE;
+  if (epilogue != QK_EPI_NONE && epilogue != QK_EPI_SWIGLU) return QK_E_ARG;
+  int rc = check_gemv(w_type, W1, n_out, n_in, xq, ncols, out);
+  if (rc != QK_OK) return rc;
+  if (ncols > 65535) return QK_E_LIMIT;
+  if (n_out == 0 || ncols == 0) return QK_OK;
+  if (W2 == nullptr) return QK_E_NULL;
+  if (!aligned16(W2)) return QK_E_ALIGN;
+  return status_of(qk::launch_gemv_pair(static_cast<const uint8_t*>(W1), static_cast<const uint8_t*>(W2),
+                                        n_out, n_in, static_cast<const uint8_t*>(xq), ncols,
+                                        epilogue == QK_EPI_SWIGLU, out, static_cast<hipStream_t>(stream)));
 }
 
 int qk_gemv_block_sums(int w_type, const void* W, int64_t n_out, int64_t n_in,

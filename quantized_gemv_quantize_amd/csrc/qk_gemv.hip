@@ -629,6 +629,167 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two Q4_K matrices over one activation row: the gate and up projections of an
+// FFN layer.  The wavefront that owns row r computes it in both W1 and W2 from
+// the same activation operands (rml "Kernels and references": one activation load
+// feeding several weight rows, there four rows of one matrix, here one row of
+// each matrix), then writes y1[r] and y2[r], or the gated activation
+// silu(y1[r]) * y2[r] = y1 / (1 + e^-y1) * y2 that the down projection consumes.
+// blockIdx.y is the activation column.
+constexpr int kEpiPair = 0, kEpiSwiglu = 1;
+
+template <int EPI>
+__device__ __forceinline__ void pair_out(float* out, int n_out, int row, float g, float u) {
+  if constexpr (EPI == kEpiSwiglu) {
+    out[row] = g / (1.0f + expf(-g)) * u;
+  } else {
+    out[row] = g;
+    out[n_out + row] = u;
+  }
+}
+
+// Rows of one or two passes: activations in registers (as gemv_q4_K_reg), rows
+// grid-strided.
+template <int NW, int NP, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_reg(
+    const uint8_t* __restrict__ W1, const uint8_t* __restrict__ W2, int n_out, int nb,
+    const uint8_t* __restrict__ xq, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 3, u = lane >> 2;
+  const uint32_t hi_mask = (c & 2) ? 0xFFFFFFFFu : 0u;
+  const int sh = (c & 1) * 16;
+  const int wave = blockIdx.x * NW + wave_id();
+  const int nwaves = gridDim.x * NW;
+  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+  xq += static_cast<size_t>(blockIdx.y) * nb * kQ8_KBytes;
+  out += static_cast<size_t>(blockIdx.y) * (EPI == kEpiSwiglu ? 1 : 2) * n_out;
+
+  uint4 A[NP][4];
+  int2 S2[NP];
+  float DX[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint8_t* a = xq + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ8_KBytes);
+    DX[p] = *reinterpret_cast<const float*>(a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[p][i] = load_a4<uint4>(a + 4 + 64 * c + 16 * i);
+    const uint2 bs = load_a4<uint2>(a + 260 + 8 * c);
+    S2[p] = make_int2(sext16_lo(bs.x) + sext16_hi(bs.x), sext16_lo(bs.y) + sext16_hi(bs.y));
+  }
+
+  for (int row = wave; row < n_out; row += nwaves) {
+    uint4 H[2][NP], Q0[2][NP], Q1[2][NP];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t* wrow = (m ? W2 : W1) + static_cast<size_t>(row) * rb;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ4_KBytes);
+        H[m][p] = *reinterpret_cast<const uint4*>(q);
+        Q0[m][p] = *reinterpret_cast<const uint4*>(q + 16 + 32 * c);
+        Q1[m][p] = *reinterpret_cast<const uint4*>(q + 32 + 32 * c);
+      }
+    }
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (p * 16 + u >= nb) continue;  // uniform over the 4 lanes of a superblock
+        const int2 part = q4K_chunk(Q0[m][p], Q1[m][p], H[m][p], A[p][0], A[p][1], A[p][2],
+                                    A[p][3], S2[p], hi_mask, sh);
+        const int sq = quad_sum(part.x);
+        const int sm = quad_sum(part.y);
+        const uint32_t dd = H[m][p].x;
+        const float cb = (DX[p] * f16_to_f32(dd & 0xFFFF)) * static_cast<float>(sq) -
+                         (DX[p] * f16_to_f32(dd >> 16)) * static_cast<float>(sm);
+        acc[m] += (c == 0) ? cb : 0.0f;
+      }
+    }
+    const float g = wave_sum(acc[0]);
+    const float v = wave_sum(acc[1]);
+    if (lane == 0) pair_out<EPI>(out, n_out, row, g, v);
+  }
+}
+
+// Longer rows: the activation row staged in LDS once per workgroup (as
+// gemv_q4_K_kernel), one row of each matrix per wavefront.
+template <int NW, int UNR, int EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_kernel(
+    const uint8_t* __restrict__ W1, const uint8_t* __restrict__ W2, int n_out, int nb,
+    const uint8_t* __restrict__ xq, float* __restrict__ out) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * NW + wave_id();
+  const int c = lane & 3, u = lane >> 2;
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+  const size_t roff = static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 15) >> 4;
+  xq += static_cast<size_t>(blockIdx.y) * nb * kQ8_KBytes;
+  out += static_cast<size_t>(blockIdx.y) * (EPI == kEpiSwiglu ? 1 : 2) * n_out;
+
+  uint4 H[2][UNR], Q0[2][UNR], Q1[2][UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t* wrow = (m ? W2 : W1) + roff;
+#pragma unroll
+      for (int j = 0; j < UNR; ++j) {
+        const int sb = min((p0 + j) * 16 + u, nb - 1);
+        const uint8_t* p = wrow + static_cast<uint32_t>(sb * kQ4_KBytes);
+        H[m][j] = *reinterpret_cast<const uint4*>(p);
+        Q0[m][j] = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
+        Q1[m][j] = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
+      }
+    }
+  };
+  ImageQ8K st;
+  image_load_q8K<NW * 64>(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  image_place_q8K<NW * 64>(lds, st, xq, nb);
+  __syncthreads();
+
+  const int sh = (c & 1) * 16;
+  const uint32_t hi_mask = (c & 2) ? 0xFFFFFFFFu : 0u;
+  float acc[2] = {0.0f, 0.0f};
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = (p0 + j) * 16 + u;
+      if (!row_ok || sb >= nb) continue;  // uniform over the 4 lanes of a superblock
+      const uint8_t* blk = lds + sb * kQ8_KBytes;
+      const uint8_t* ap = blk + 4 + 64 * c;
+      const uint4 a0 = lds_a4<uint4>(ap);
+      const uint4 a1 = lds_a4<uint4>(ap + 16);
+      const uint4 a2 = lds_a4<uint4>(ap + 32);
+      const uint4 a3 = lds_a4<uint4>(ap + 48);
+      const uint2 bsw = lds_a4<uint2>(blk + 260 + 8 * c);
+      const int2 asum = make_int2(sext16_lo(bsw.x) + sext16_hi(bsw.x), sext16_lo(bsw.y) + sext16_hi(bsw.y));
+      const float dx = lds_a4<float>(blk);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint4 h = H[m][j];
+        const int2 part = q4K_chunk(Q0[m][j], Q1[m][j], h, a0, a1, a2, a3, asum, hi_mask, sh);
+        const int sq = quad_sum(part.x);
+        const int sm = quad_sum(part.y);
+        const float cb = (dx * f16_to_f32(h.x & 0xFFFF)) * static_cast<float>(sq) -
+                         (dx * f16_to_f32(h.x >> 16)) * static_cast<float>(sm);
+        acc[m] += (c == 0) ? cb : 0.0f;
+      }
+    }
+  }
+  if (row_ok) {
+    const float g = wave_sum(acc[0]);
+    const float v = wave_sum(acc[1]);
+    if (lane == 0) pair_out<EPI>(out, n_out, row, g, v);
+  }
+}
+
 // Q6_K x Q8_K, register-resident activations.  Lane (u, p = h*2 + k) of pass P
 // covers l in [16k, 16k+16) of half h of superblock P*16 + u for the four groups
 // g: activation pieces 8h + 2g + k, 16-element sub-blocks 8h + 2g + k.
@@ -904,6 +1065,32 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
   }
 #undef QK_ROWS
 #undef QK_LDS
+}
+
+template <int EPI>
+hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
+                           const uint8_t* xq, int64_t ncols, float* out, hipStream_t s) {
+  const int nb = static_cast<int>(n_in / 256);
+  const int n = static_cast<int>(n_out);
+  const int passes = (nb + 15) / 16;
+  if (passes <= 2) {
+    const int64_t waves = n_out < kMaxWaves ? n_out : kMaxWaves;
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));
+    if (passes == 1) gemv_q4_K_pair_reg<4, 1, EPI><<<grid, 256, 0, s>>>(W1, W2, n, nb, xq, out);
+    else gemv_q4_K_pair_reg<4, 2, EPI><<<grid, 256, 0, s>>>(W1, W2, n, nb, xq, out);
+  } else {
+    const dim3 grid(static_cast<unsigned>((n_out + kWaves - 1) / kWaves), static_cast<unsigned>(ncols));
+    const int64_t lds = gemv_lds_bytes(kQ4_K, n_in);
+    gemv_q4_K_pair_kernel<kWaves, 3, EPI><<<grid, kWaves * 64, lds, s>>>(W1, W2, n, nb, xq, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_pair(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
+                            const uint8_t* xq, int64_t ncols, int swiglu, float* out, hipStream_t s) {
+  if (n_out <= 0 || ncols <= 0) return hipSuccess;
+  return swiglu ? launch_pair_epi<kEpiSwiglu>(W1, W2, n_out, n_in, xq, ncols, out, s)
+                : launch_pair_epi<kEpiPair>(W1, W2, n_out, n_in, xq, ncols, out, s);
 }
 
 }  // namespace qk

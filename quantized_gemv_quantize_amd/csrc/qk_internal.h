@@ -36,6 +36,11 @@ constexpr int64_t kGemmMaxCols = 64;
 
 // Bytes of dynamic LDS a GEMV over rows of n_in elements needs.
 int64_t gemv_lds_bytes(int w_type, int64_t n_in);
+
+// Q4_K W1 and W2 over the same Q8_K activation columns (ncols <= 65535): out is
+// [ncols][2][n_out] (y1 then y2) or, with swiglu, [ncols][n_out] silu(y1) * y2.
+hipError_t launch_gemv_pair(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
+                            const uint8_t* xq, int64_t ncols, int swiglu, float* out, hipStream_t s);
 constexpr int64_t kMaxLdsBytes = 65536;
 
 hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t nblocks,

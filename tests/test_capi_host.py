@@ -136,6 +136,25 @@ def test_gemv_validation():
                    None) == 4
 
 
+def test_gemv_pair_validation():
+    f = "qk_gemv_pair"
+    T4K = qk.QK_TYPE_Q4_K
+    assert _status(f, qk.QK_TYPE_Q6_K, GOOD, GOOD, 4, 256, GOOD, 1, 0, GOOD, None) == 1  # Q4_K only
+    assert _status(f, T4K, GOOD, GOOD, 4, 256, GOOD, 1, 2, GOOD, None) == 8     # epilogue
+    assert _status(f, T4K, GOOD, GOOD, 4, 255, GOOD, 1, 0, GOOD, None) == 3
+    assert _status(f, T4K, GOOD, GOOD, -1, 256, GOOD, 1, 1, GOOD, None) == 3
+    assert _status(f, T4K, GOOD, GOOD, 4, 256, GOOD, 65536, 1, GOOD, None) == 7  # columns
+    big = qk.qk_max_n_in(T4K) + 256
+    assert _status(f, T4K, GOOD, GOOD, 4, big, GOOD, 1, 1, GOOD, None) == 7
+    assert _status(f, T4K, GOOD, None, 4, 256, GOOD, 1, 1, GOOD, None) == 5
+    assert _status(f, T4K, None, GOOD, 4, 256, GOOD, 1, 1, GOOD, None) == 5
+    assert _status(f, T4K, GOOD, GOOD, 4, 256, GOOD, 1, 1, None, None) == 5
+    assert _status(f, T4K, GOOD, ODD, 4, 256, GOOD, 1, 1, GOOD, None) == 4
+    assert _status(f, T4K, GOOD, GOOD, 4, 256, ODD, 1, 0, GOOD, None) == 4
+    assert _status(f, T4K, GOOD, GOOD, 0, 256, GOOD, 1, 1, GOOD, None) == 0     # no-op
+    assert _status(f, T4K, None, None, 4, 256, None, 0, 0, None, None) == 0     # no-op
+
+
 def test_dequantize_validation():
     f = "qk_dequantize_row"
     assert _status(f, qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, None) == 1   # activation-only type
@@ -148,7 +167,7 @@ def test_dequantize_validation():
 
 
 def test_status_strings():
-    for s in (0, 1, 3, 4, 5, 6, 7):
+    for s in (0, 1, 3, 4, 5, 6, 7, 8):
         assert qk.status_str(s) and qk.status_str(s) != "unknown status"
     assert qk.status_str(42) == "unknown status"
 

@@ -395,20 +395,27 @@ def test_graph_capture_replays_match_eager(torch_cuda):
     for t, n_out, n_in, nc, W, x, at, xq, y in bufs:
         qk.qk_quantize_act(at, x, xq)
         want.append(qk.qk_gemv(t, W, n_out, n_in, xq, nc).clone())
+    # gate / up pair with the SwiGLU epilogue on the first Q4_K case's activations
+    W2p = dev(torch, weights(rng, T4K, 64, 11008))
+    hp = torch.empty((1, 64), dtype=torch.float32, device="cuda")
+    want_h = qk.qk_gemv_pair(T4K, bufs[0][4], W2p, 64, 11008, bufs[0][7], 1, qk.QK_EPI_SWIGLU).clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for t, n_out, n_in, nc, W, x, at, xq, y in bufs:
             qk.qk_quantize_act(at, x, xq)
             qk.qk_gemv(t, W, n_out, n_in, xq, nc, y)
+        qk.qk_gemv_pair(T4K, bufs[0][4], W2p, 64, 11008, bufs[0][7], 1, qk.QK_EPI_SWIGLU, hp)
     for rep in range(4):
         for b in bufs:
             b[8].fill_(float("nan"))
             b[7].zero_()
+        hp.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for (t, n_out, n_in, nc, W, x, at, xq, y), w in zip(bufs, want):
             assert torch.equal(y, w), (rep, t, n_out, n_in, nc)
+        assert torch.equal(hp, want_h), rep
 
 
 def test_native_library_is_the_one_loaded(torch_cuda):
@@ -416,6 +423,100 @@ def test_native_library_is_the_one_loaded(torch_cuda):
     assert os.path.realpath(qk.LIB_PATH) in maps
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+# ---------------------------------------------------------------------------
+# qk_gemv_pair: gate and up in one launch, optional SwiGLU epilogue
+# ---------------------------------------------------------------------------
+
+SILU_SLOPE = 1.0998  # max |d/dv v*sigmoid(v)|
+
+
+def silu64(v):
+    v = v.astype(np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+def assert_swiglu(h_gpu, g_o, u_o, l1g, l1u, what):
+    """|h_gpu - silu(g)u| within what the R12 bounds on g and u allow, plus a few
+    f32 roundings of the epilogue itself."""
+    h_o = orc.swiglu(g_o, u_o)
+    dg, du = Y_TOL * l1g, Y_TOL * l1u
+    bound = (SILU_SLOPE * (np.abs(u_o) + du) * dg + (np.abs(silu64(g_o)) + SILU_SLOPE * dg) * du
+             + 8 * 2.0 ** -24 * np.abs(h_o) + 1e-30)
+    err = np.abs(h_gpu.astype(np.float64) - h_o)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} outputs beyond the bound (worst {np.max(err / bound):.3g})"
+
+
+PAIR_SHAPES = [(1, 256), (7, 4096), (130, 4096), (33, 8192), (9, 11008), (5, 28672)]
+
+
+@pytest.mark.parametrize("n_out,n_in", PAIR_SHAPES)
+def test_gemv_pair_and_swiglu(torch_cuda, n_out, n_in):
+    rng = np.random.default_rng(600 + n_out + n_in)
+    for ncols in (1, 3):
+        say("gemv_pair", n_out, n_in, ncols)
+        W1 = synth.q4_K_blocks(rng, n_out, n_in)
+        W2 = synth.q4_K_blocks(rng, n_out, n_in)
+        X = rng.standard_normal((ncols, n_in)).astype(np.float32)
+        xq = orc.quantize(T8K, X)
+        W1d, W2d, xd = dev(torch_cuda, W1), dev(torch_cuda, W2), dev(torch_cuda, xq)
+        pair = host(qk.qk_gemv_pair(T4K, W1d, W2d, n_out, n_in, xd, ncols))
+        g_o, l1g = orc.gemv(T4K, W1, n_out, n_in, xq, ncols)
+        u_o, l1u = orc.gemv(T4K, W2, n_out, n_in, xq, ncols)
+        assert_y(pair[:, 0], g_o, l1g, f"pair y1 {n_out}x{n_in} ncols {ncols}")
+        assert_y(pair[:, 1], u_o, l1u, f"pair y2 {n_out}x{n_in} ncols {ncols}")
+        if ncols == 1:  # the one-column GEMV kernels' own arithmetic
+            assert np.array_equal(pair[:, 0], host(qk.qk_gemv(T4K, W1d, n_out, n_in, xd, 1)))
+            assert np.array_equal(pair[:, 1], host(qk.qk_gemv(T4K, W2d, n_out, n_in, xd, 1)))
+        h = host(qk.qk_gemv_pair(T4K, W1d, W2d, n_out, n_in, xd, ncols, qk.QK_EPI_SWIGLU))
+        assert h.shape == (ncols, n_out)
+        assert_swiglu(h, g_o, u_o, l1g, l1u, f"swiglu {n_out}x{n_in} ncols {ncols}")
+
+
+def test_swiglu_extreme_gates(torch_cuda):
+    # gates far into both tails: e^-g overflows to inf (h -> -0) or vanishes (h -> g u)
+    say("swiglu extreme gates")
+    rng = np.random.default_rng(610)
+    n_out, n_in = 64, 512
+    W1 = synth.q4_K_blocks(rng, n_out, n_in, d_range=(0.5, 2.0))   # large |g|
+    W2 = synth.q4_K_blocks(rng, n_out, n_in)
+    X = rng.standard_normal((1, n_in)).astype(np.float32) * 40
+    xq = orc.quantize(T8K, X)
+    h = host(qk.qk_gemv_pair(T4K, dev(torch_cuda, W1), dev(torch_cuda, W2), n_out, n_in,
+                             dev(torch_cuda, xq), 1, qk.QK_EPI_SWIGLU))
+    g_o, l1g = orc.gemv(T4K, W1, n_out, n_in, xq, 1)
+    u_o, l1u = orc.gemv(T4K, W2, n_out, n_in, xq, 1)
+    assert np.abs(g_o).max() > 200  # the tails are reached
+    assert np.all(np.isfinite(h))
+    assert_swiglu(h, g_o, u_o, l1g, l1u, "swiglu extreme gates")
+
+
+def test_ffn_swiglu_step_7b(torch_cuda):
+    # the FFN decode step as the library runs it: quantize x, gate + up with the
+    # SwiGLU epilogue, quantize h on the GPU, down projection.  Each stage is
+    # checked against the oracle on the GPU's own input to that stage.
+    torch = torch_cuda
+    d = synth.ffn_7b()
+    say("FFN step 7B: gate/up pair")
+    x = d["x"][None, :]
+    xq = qk.qk_quantize_act(T8K, dev(torch, x))
+    assert np.array_equal(host(xq), orc.quantize(T8K, x))
+    h = qk.qk_gemv_pair(T4K, dev(torch, d["gate"]), dev(torch, d["up"]), 11008, 4096, xq, 1,
+                        qk.QK_EPI_SWIGLU)
+    xq_h = host(xq)
+    g_o, l1g = orc.gemv(T4K, d["gate"], 11008, 4096, xq_h, 1)
+    u_o, l1u = orc.gemv(T4K, d["up"], 11008, 4096, xq_h, 1)
+    h_host = host(h)
+    assert_swiglu(h_host, g_o, u_o, l1g, l1u, "FFN h")
+    say("FFN step 7B: quantize h, down")
+    hq = qk.qk_quantize_act(T8K, h)
+    hq_o = orc.quantize(T8K, h_host)
+    assert np.array_equal(host(hq), hq_o)
+    y = host(qk.qk_gemv(T6K, dev(torch, d["down"]), 4096, 11008, hq, 1))
+    y_o, l1 = orc.gemv(T6K, d["down"], 4096, 11008, hq_o, 1)
+    assert_y(y, y_o, l1, "FFN down")
 
 
 # ---------------------------------------------------------------------------
