@@ -75,6 +75,12 @@ def workloads(qk):
             "gemvs": [("gate", T4K, 11008, 4096, "x"), ("up", T4K, 11008, 4096, "x"),
                       ("down", T6K, 4096, 11008, "x2")],
             "acts": {"x": (T8K, 4096, 1), "x2": (T8K, 11008, 1)}},
+        # the FFN decode step as one layer runs it: quantize x, gate + up in one
+        # qk_gemv_pair launch with the SwiGLU epilogue (h), quantize h, down
+        "ffn_7b_swiglu": {
+            "gemvs": [("gate", T4K, 11008, 4096, "x"), ("up", T4K, 11008, 4096, "x"),
+                      ("down", T6K, 4096, 11008, "h")],
+            "acts": {"x": (T8K, 4096, 1), "h": (T8K, 11008, 1)}, "swiglu_pair": True},
         "q6_K_head_32000x4096": {
             "gemvs": [("W", T6K, 32000, 4096, "x")], "acts": {"x": (T8K, 4096, 1)}},
         "q8_0_256x1024": {
@@ -99,8 +105,10 @@ def host_inputs(name, qk):
         return synth.q4_K_decode_4096x11008()
     if name in ("q4_K_4096x4096", "q4_0_4096x4096"):
         return synth.q4_gemv_4096x4096()
-    if name == "ffn_7b_q4_K_q6_K":
-        return synth.ffn_7b()
+    if name in ("ffn_7b_q4_K_q6_K", "ffn_7b_swiglu"):
+        d = synth.ffn_7b()
+        d["h"] = d["x2"]  # initial contents of the gated activation buffer
+        return d
     if name in ("q6_K_head_32000x4096", "q6_K_dequantize_32000x4096"):
         return synth.q6_K_head_32000x4096()
     if name.startswith("q4_K_batched"):
@@ -168,6 +176,24 @@ def cpu_baseline(name, wl, inputs, seconds):
                 sample_rows[wname] = rows
                 b = orc.quantize(wt, W[:rows])
                 done_bytes += 4 * rows * n_in + b.size
+        if wl.get("swiglu_pair"):
+            # gate / up rows with the SwiGLU epilogue; down rows against the
+            # quantized stand-in activation (the full h needs every gate row)
+            (gn, gt, g_out, g_in, _), (un, _, _, _, _), (dn, dt, d_out, d_in, _) = wl["gemvs"]
+            xq = orc.quantize(orc.Q8_K, inputs["x"][None, :])
+            rows = min(g_out, max(1, int(4e6 // g_in)))
+            g, _ = orc.gemv(gt, inputs[gn][:rows], rows, g_in, xq, 1)
+            u, _ = orc.gemv(gt, inputs[un][:rows], rows, g_in, xq, 1)
+            orc.swiglu(g, u)
+            hq = orc.quantize(orc.Q8_K, inputs["h"][None, :])
+            rows_d = min(d_out, max(1, int(4e6 // d_in)))
+            orc.gemv(dt, inputs[dn][:rows_d], rows_d, d_in, hq, 1)
+            sample_rows.update({gn: rows, un: rows, dn: rows_d})
+            done_bytes += 2 * rows * inputs[gn].shape[1] + rows_d * inputs[dn].shape[1]
+            reps += 1
+            if time.perf_counter() >= t_end:
+                break
+            continue
         for key, (at, n, ncols) in wl["acts"].items():
             x = inputs[key] if inputs[key].ndim == 2 else inputs[key][None, :]
             xq = orc.quantize(at, x[:ncols])
@@ -192,6 +218,8 @@ def cpu_baseline(name, wl, inputs, seconds):
 def _kind(wl):
     if wl.get("dequant"):
         return "dequantize"
+    if wl.get("swiglu_pair"):
+        return "quantize x + gate/up + SwiGLU + quantize h + down"
     return "weight quantize" if wl.get("quantize_row") else "quantize + GEMV"
 
 
@@ -237,8 +265,14 @@ def recorded_traffic(workload):
 def algorithmic_bytes(wl, qk):
     """Weights + activation blocks + f32 outputs of the GEMV launches of one step
     (for a dequantize workload: the blocks read plus the f32 values written; for a
-    weight-quantize workload: the f32 values read plus the blocks written)."""
+    weight-quantize workload: the f32 values read plus the blocks written; the
+    gate / up pair reads its activation row once and writes one f32 per row)."""
     total = 0
+    if wl.get("swiglu_pair"):
+        (_, gt, g_out, g_in, gk), _, (_, dt, d_out, d_in, dk) = wl["gemvs"]
+        return (2 * qk.qk_row_bytes(gt, g_in) * g_out + qk.qk_row_bytes(wl["acts"][gk][0], g_in)
+                + 4 * g_out + qk.qk_row_bytes(dt, d_in) * d_out
+                + qk.qk_row_bytes(wl["acts"][dk][0], d_in) + 4 * d_out)
     for _, wt, n_out, n_in, akey in wl["gemvs"]:
         if wl.get("dequant") or wl.get("quantize_row"):
             total += qk.qk_row_bytes(wt, n_in) * n_out + 4 * n_out * n_in
@@ -319,7 +353,7 @@ def summarize_pmc(fdir, wdir, workload):
     the calibration copy kernel (CALIB_BYTES read + CALIB_BYTES written)."""
     import quantized_gemv_quantize_amd as qk  # constants only; the library is not loaded
     wl = workloads(qk)[workload]
-    n_g = len(wl["gemvs"])
+    n_g = 2 if wl.get("swiglu_pair") else len(wl["gemvs"])  # library kernel launches per step
     out = {}
     for tag, d in (("FETCH_SIZE", fdir), ("WRITE_SIZE", wdir)):
         m = _counter_means(d)
@@ -432,10 +466,29 @@ def main():
     log(f"[bench] {copies} weight copies x {step_w_bytes / 1e6:.2f} MB resident; "
         f"warmup {args.warmup}, steps {args.steps}")
 
-    n_g = len(wl["gemvs"])
+    swiglu = bool(wl.get("swiglu_pair"))
+    timed_names = ["gate_up", "down"] if swiglu else [gv[0] for gv in wl["gemvs"]]
+    n_g = len(timed_names)
+
+    def recorded(evs, g, launch):
+        if evs is not None:
+            evs[g][0].record(stream)
+        launch()
+        if evs is not None:
+            evs[g][1].record(stream)
 
     def step(k, evs=None):
         mats = dev_w[k % copies]
+        if swiglu:
+            (_, gt, g_out, g_in, _), _, (_, dt, d_out, d_in, _) = wl["gemvs"]
+            at, xf, xq = acts["x"]
+            _, h, hq = acts["h"]
+            qk.qk_quantize_act(at, xf, xq)
+            recorded(evs, 0, lambda: qk.qk_gemv_pair(gt, mats[0], mats[1], g_out, g_in, xq, 1,
+                                                     qk.QK_EPI_SWIGLU, h))
+            qk.qk_quantize_act(acts["h"][0], h, hq)
+            recorded(evs, 1, lambda: qk.qk_gemv(dt, mats[2], d_out, d_in, hq, 1, ys[2]))
+            return
         for key, (at, xf, xq) in acts.items():
             qk.qk_quantize_act(at, xf, xq)
         for g, (wname, wt, n_out, n_in, akey) in enumerate(wl["gemvs"]):
@@ -529,7 +582,7 @@ def main():
 
     alg_bytes = algorithmic_bytes(wl, qk)
     achieved = alg_bytes / (gemv_ms_mean / 1e3) / 1e9
-    per_kernel_us = {wl["gemvs"][g][0]: {"mean": round(float(kern_ms[:, g].mean() * 1e3), 3),
+    per_kernel_us = {timed_names[g]: {"mean": round(float(kern_ms[:, g].mean() * 1e3), 3),
                                           "p10": round(float(np.percentile(kern_ms[:, g], 10) * 1e3), 3),
                                           "p50": round(float(np.percentile(kern_ms[:, g], 50) * 1e3), 3),
                                           "p90": round(float(np.percentile(kern_ms[:, g], 90) * 1e3), 3)}
@@ -585,8 +638,11 @@ def main():
         },
         "cpu_baseline": cpu,
         "detail": {"gemv_kernel_us_per_step": round(float(gemv_ms_mean * 1e3), 3),
-                   "kernel_timing": "HIP events of the kernel launches, steps run back to back "
-                                    "behind a stream hold" + ("" if backlog else " (hold ended early)"),
+                   "kernel_timing": ("events recorded on the launch stream around each kernel"
+                                     if (swiglu or wl.get("dequant") or quant_row) else
+                                     "HIP events of the kernel launches") +
+                                    ", steps run back to back behind a stream hold" +
+                                    ("" if backlog else " (hold ended early)"),
                    "traffic_unit": "bytes per step (FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
                    "eager_us_per_step": round(eager_ms / args.steps * 1e3, 3),
                    "gemv_kernel_us": per_kernel_us,

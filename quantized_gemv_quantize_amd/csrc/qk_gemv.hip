@@ -1074,7 +1074,10 @@ hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, 
   const int n = static_cast<int>(n_out);
   const int passes = (nb + 15) / 16;
   if (passes <= 2) {
-    const int64_t waves = n_out < kMaxWaves ? n_out : kMaxWaves;
+    // a wavefront has two rows' loads in flight, so half the single-GEMV count
+    // (2048 measured best on the 11008 x 4096 gate / up pair; 4096 and 8192 slower)
+    constexpr int64_t kPairWaves = kMaxWaves / 2;
+    const int64_t waves = n_out < kPairWaves ? n_out : kPairWaves;
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));
     if (passes == 1) gemv_q4_K_pair_reg<4, 1, EPI><<<grid, 256, 0, s>>>(W1, W2, n, nb, xq, out);
     else gemv_q4_K_pair_reg<4, 2, EPI><<<grid, 256, 0, s>>>(W1, W2, n, nb, xq, out);
