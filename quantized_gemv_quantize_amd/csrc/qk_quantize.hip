@@ -87,21 +87,31 @@ __global__ __launch_bounds__(256) void quantize_q8_K_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // Weight quantizers Q4_0, Q4_1, Q5_0 (codeloopback Examples 5, 7, 8).  8 lanes per
-// 32-element block, lane p holding elements 4p .. 4p+3.  The sequential reference
-// scans elements in order and replaces its candidate only on a strictly better
-// value, so every reduction below keeps (value, index) and prefers the lower index
-// on ties (this decides signed zeros and equal magnitudes exactly as the scan).
+// 32-element block.  The sequential reference scans elements in order and replaces
+// its candidate only on a strictly better value, so every reduction below keeps
+// (value, index) and prefers the lower index on ties (this decides signed zeros and
+// equal magnitudes exactly as the scan).
+//
+// Lane p of a block holds elements e0(p) .. e0(p) + 3 with e0 = 4p for p < 4 and
+// 44 - 4p for p >= 4 (lanes 4..7 hold 28, 24, 20, 16): byte k of the packed nibbles
+// pairs element k with element k + 16, and with this order the lane holding the
+// upper half of lane p's bytes is lane 7 - p, which the DPP half-row mirror reaches.
+// All exchanges are DPP moves inside the 8 lanes (quad swaps, then the mirror).
+// Each group of 8 lanes quantizes kRowUnroll blocks, the loads of all of them
+// issued first; the blocks of one load instruction are consecutive.
+constexpr int kRowUnroll = 4;  // 4 measured best (8: slower)
 
-// The 8 lanes of a block exchange through ds_bpermute (width 8).
-template <typename T>
-__device__ __forceinline__ T xor8(T v, int m) {
-  return __shfl_xor(v, m, 8);
+__device__ __forceinline__ int lane_e0(int part) { return part < 4 ? 4 * part : 44 - 4 * part; }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
 struct Pick {
   float key;  // compared value (|x| for the signed max, x for min / max)
   float val;  // value kept (x)
-  int idx;    // element index, 32 when the lane has no candidate
+  int idx;    // element index
 };
 
 // better(a, b): a beats b under comparison C (a strict improvement, or equal with
@@ -112,17 +122,28 @@ __device__ __forceinline__ bool better(const Pick& a, const Pick& b) {
   return strictly || (a.key == b.key && a.idx < b.idx);
 }
 
+template <bool kMax, int CTRL>
+__device__ __forceinline__ Pick pick_step(Pick p) {
+  Pick o;
+  o.key = __int_as_float(dpp_i<CTRL>(__float_as_int(p.key)));
+  o.val = __int_as_float(dpp_i<CTRL>(__float_as_int(p.val)));
+  o.idx = dpp_i<CTRL>(p.idx);
+  return better<kMax>(o, p) ? o : p;
+}
+
+// Best of the 8 lanes of a block, in every lane: quad swaps [1,0,3,2] and
+// [2,3,0,1], then the half-row mirror joins the two quads.
 template <bool kMax>
 __device__ __forceinline__ Pick reduce8(Pick p) {
-#pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    Pick o;
-    o.key = xor8(p.key, m);
-    o.val = xor8(p.val, m);
-    o.idx = xor8(p.idx, m);
-    if (better<kMax>(o, p)) p = o;
-  }
-  return p;
+  p = pick_step<kMax, 0xB1>(p);
+  p = pick_step<kMax, 0x4E>(p);
+  return pick_step<kMax, 0x141>(p);
+}
+
+__device__ __forceinline__ uint32_t or8(uint32_t v) {
+  v |= static_cast<uint32_t>(dpp_i<0xB1>(static_cast<int>(v)));
+  v |= static_cast<uint32_t>(dpp_i<0x4E>(static_cast<int>(v)));
+  return v | static_cast<uint32_t>(dpp_i<0x141>(static_cast<int>(v)));
 }
 
 constexpr int kFmtQ4_0 = 0, kFmtQ4_1 = 1, kFmtQ5_0 = 2;
@@ -138,38 +159,30 @@ __device__ __forceinline__ int trunc_sat(float f) {
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256) void quantize_row_kernel(const float* __restrict__ x,
-                                                           uint8_t* __restrict__ dst,
-                                                           int64_t nblocks) {
+__device__ __forceinline__ void quantize_block(float4 v4, int part, bool valid, uint8_t* ob) {
 #pragma clang fp contract(off)
-  constexpr int kBytes = (FMT == kFmtQ4_0) ? kQ4_0Bytes : (FMT == kFmtQ4_1) ? kQ4_1Bytes : kQ5_0Bytes;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t b = t >> 3;  // the 8 lanes of a block are all in or all out of range
-  const int part = threadIdx.x & 7;
-  const bool valid = b < nblocks;
-  float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (valid) v4 = *reinterpret_cast<const float4*>(x + b * 32 + part * 4);
   const float v[4] = {v4.x, v4.y, v4.z, v4.w};
-
+  const int e0 = lane_e0(part);
   float d, id, mn = 0.0f;
   if constexpr (FMT == kFmtQ4_1) {
-    // min and max, each the first occurrence of its value (reference: strict < / >)
-    Pick lo{FLT_MAX, FLT_MAX, 32}, hi{-FLT_MAX, -FLT_MAX, 32};
+    // min and max, each the first occurrence of its value (strict < / >)
+    Pick lo{v[0], v[0], e0}, hi{v[0], v[0], e0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (v[i] < lo.key) lo = Pick{v[i], v[i], 4 * part + i};
-      if (v[i] > hi.key) hi = Pick{v[i], v[i], 4 * part + i};
+    for (int i = 1; i < 4; ++i) {
+      if (v[i] < lo.key) lo = Pick{v[i], v[i], e0 + i};
+      if (v[i] > hi.key) hi = Pick{v[i], v[i], e0 + i};
     }
     lo = reduce8<false>(lo);
     hi = reduce8<true>(hi);
     mn = lo.val;
     d = (hi.val - mn) / 15.0f;
   } else {
-    // the first element of largest magnitude, with its sign
+    // the first element of largest magnitude, with its sign (from 0: an all-zero
+    // block keeps max = 0)
     Pick m{0.0f, 0.0f, 32};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (m.key < fabsf(v[i])) m = Pick{fabsf(v[i]), v[i], 4 * part + i};
+      if (m.key < fabsf(v[i])) m = Pick{fabsf(v[i]), v[i], e0 + i};
     }
     m = reduce8<true>(m);
     d = m.val / ((FMT == kFmtQ4_0) ? -8.0f : -16.0f);
@@ -187,16 +200,14 @@ __global__ __launch_bounds__(256) void quantize_row_kernel(const float* __restri
   }
   const uint32_t nib = (c[0] & 15) | ((c[1] & 15) << 8) | ((c[2] & 15) << 16) |
                        (static_cast<uint32_t>(c[3] & 15) << 24);
-  const uint32_t upper = xor8(nib, 4);  // elements 16 + 4p .. (lanes p < 4)
+  const uint32_t upper = static_cast<uint32_t>(dpp_i<0x141>(static_cast<int>(nib)));  // lane 7 - p
   uint32_t qh = 0;
   if constexpr (FMT == kFmtQ5_0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qh |= ((static_cast<uint32_t>(c[i]) >> 4) & 1u) << (4 * part + i);
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) qh |= xor8(qh, m);
+    for (int i = 0; i < 4; ++i) qh |= ((static_cast<uint32_t>(c[i]) >> 4) & 1u) << (e0 + i);
+    qh = or8(qh);
   }
   if (!valid) return;
-  uint8_t* ob = dst + b * kBytes;
   constexpr int kQs = (FMT == kFmtQ4_0) ? 2 : (FMT == kFmtQ4_1) ? 4 : 6;
   if (part < 4) store_u2(ob + kQs + 4 * part, nib | (upper << 4));
   if (part == 0) {
@@ -206,17 +217,43 @@ __global__ __launch_bounds__(256) void quantize_row_kernel(const float* __restri
   }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_row_kernel(const float* __restrict__ x,
+                                                           uint8_t* __restrict__ dst,
+                                                           int64_t nblocks) {
+  constexpr int kBytes = (FMT == kFmtQ4_0) ? kQ4_0Bytes : (FMT == kFmtQ4_1) ? kQ4_1Bytes : kQ5_0Bytes;
+  const int lane = threadIdx.x & 63;
+  const int part = lane & 7, grp = lane >> 3;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int64_t base = wave * (8 * kRowUnroll) + grp;  // block of unroll step 0
+  float4 v[kRowUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    const int64_t b = base + 8 * u;
+    v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (b < nblocks) v[u] = *reinterpret_cast<const float4*>(x + b * 32 + lane_e0(part));
+  }
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) {
+    const int64_t b = base + 8 * u;
+    // every lane takes part in the exchanges; only whole blocks in range store
+    quantize_block<FMT>(v[u], part, b < nblocks, dst + b * kBytes);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_row(int type, const float* x, uint8_t* dst, int64_t nblocks,
                                hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
+  // 4 wavefronts per workgroup, 8 * kRowUnroll blocks per wavefront
+  const unsigned rgrid = static_cast<unsigned>((nblocks + 32 * kRowUnroll - 1) / (32 * kRowUnroll));
   switch (type) {
     case kQ8_0: quantize_q8_0_kernel<<<grid, 256, 0, s>>>(x, dst, nblocks); break;
-    case kQ4_0: quantize_row_kernel<kFmtQ4_0><<<grid, 256, 0, s>>>(x, dst, nblocks); break;
-    case kQ4_1: quantize_row_kernel<kFmtQ4_1><<<grid, 256, 0, s>>>(x, dst, nblocks); break;
-    case kQ5_0: quantize_row_kernel<kFmtQ5_0><<<grid, 256, 0, s>>>(x, dst, nblocks); break;
+    case kQ4_0: quantize_row_kernel<kFmtQ4_0><<<rgrid, 256, 0, s>>>(x, dst, nblocks); break;
+    case kQ4_1: quantize_row_kernel<kFmtQ4_1><<<rgrid, 256, 0, s>>>(x, dst, nblocks); break;
+    case kQ5_0: quantize_row_kernel<kFmtQ5_0><<<rgrid, 256, 0, s>>>(x, dst, nblocks); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
