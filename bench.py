@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix-core peak (5.0 POP/s)
 ROTATE_BYTES = 512 * 1024 * 1024
 CALIB_BYTES = 256 * 1024 * 1024  # the copy kernel reads and writes this much per dispatch
 CSRC = os.path.join(ROOT, "quantized_gemv_quantize_amd", "csrc")
@@ -648,6 +649,13 @@ def main():
                    "gemv_kernel_us": per_kernel_us,
                    "algorithmic_bytes_per_step_gemv": alg_bytes},
     }
+    if kernel_family(args.workload) == "gemm":
+        # the batched path is also a contraction: 2 int8 ops per weight and column
+        # (multiply, add), against the dense int8 matrix-core peak
+        ops = sum(2 * n_out * n_in * ncols_of(wl, akey) for _, _, n_out, n_in, akey in wl["gemvs"])
+        tops = ops / (gemv_ms_mean / 1e3) / 1e12
+        out["detail"]["int8_tops"] = round(tops, 2)
+        out["detail"]["int8_frac_of_dense_peak"] = round(tops / INT8_PEAK_TOPS, 4)
     print(json.dumps(out), flush=True)
 
 
