@@ -347,6 +347,30 @@ def test_gemv_zero_activation_gives_zero(torch_cuda):
         assert not y.any()
 
 
+def test_empty_calls_touch_nothing(torch_cuda):
+    # zero rows, zero columns or zero elements: QK_OK, nothing launched, buffers intact
+    torch = torch_cuda
+    say("empty calls")
+    L = qk.lib()
+    import ctypes
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    W = torch.zeros(4 * 144, dtype=torch.uint8, device="cuda")
+    xq = torch.zeros(292, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(256, dtype=torch.float32, device="cuda")
+    y = torch.full((16,), 7.0, dtype=torch.float32, device="cuda")
+    blk = torch.full((64,), 0xAB, dtype=torch.uint8, device="cuda")
+    assert L.qk_gemv(T4K, p(W), 0, 256, p(xq), 1, p(y), st) == 0
+    assert L.qk_gemv(T4K, p(W), 4, 256, p(xq), 0, p(y), st) == 0
+    assert L.qk_gemv_block_sums(T6K, p(W), 0, 256, p(xq), 1, p(y), st) == 0
+    assert L.qk_gemv_pair(T4K, p(W), p(W), 0, 256, p(xq), 1, 1, p(y), st) == 0
+    assert L.qk_quantize_act(T8K, p(x), p(blk), 256, 0, st) == 0
+    assert L.qk_quantize_row(T4_0, p(x), p(blk), 0, st) == 0
+    assert L.qk_dequantize_row(T4K, p(W), p(y), 0, st) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0) and torch.all(blk == 0xAB)
+
+
 def test_gemv_rejects_misaligned_view(torch_cuda):
     rng = np.random.default_rng(6)
     W = dev(torch_cuda, weights(rng, T4K, 4, 512))
