@@ -213,7 +213,21 @@ def cpu_baseline(name, wl, inputs, seconds):
     desc = ", ".join(f"{k}: first {r} rows" for k, r in sample_rows.items())
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{desc}; {_kind(wl)} repeated "
-                      f"{reps}x in {dt:.1f} s, single thread"}
+                      f"{reps}x in {dt:.1f} s, single thread on {_host_cpu()}"}
+
+
+def _host_cpu():
+    """CPU model and logical CPU count of the host running the oracle."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model} ({os.cpu_count()} logical CPUs visible)"
 
 
 def _kind(wl):
