@@ -125,8 +125,9 @@ struct Prefetch {
 // offsets of its pieces relative to the stage's first superblock, and where they
 // go in the LDS stage buffer.  A stage starting at superblock b adds b * 144 (W)
 // or b * 292 (activations).  Pieces of superblocks past the row end (the last
-// stage when KSP does not divide the superblock count) re-read the stage's last
-// valid superblock instead; they are never used.
+// stage when KSP does not divide the superblock count, and the stages the
+// straight-line loop runs past the end) re-read the row's last superblock; they
+// are never used.
 template <class C>
 struct StageMap {
   size_t wsrc[C::kWPerThread];     // row * row_bytes + sub * 144 + piece * 16
@@ -308,24 +309,27 @@ __global__ __launch_bounds__(C::kThreads) void gemm_q4_K_mfma(const uint8_t* __r
 
   // Global loads run two stages ahead of the multiply: two register sets
   // alternate (the loop is unrolled by two so each set has a fixed name), and
-  // each stage is written to LDS one stage ahead of its use.
+  // each stage is written to LDS one stage ahead of its use.  The body is
+  // straight-line: loads of stages past the end re-read the row's last superblock
+  // (stage_load clamps) and those stages multiply nothing, so no load sits under a
+  // condition and the compiler's wait counts cover only the older register set.
   const int nstage = (nb + KSP - 1) / KSP;
+  const int nstage2 = (nstage + 1) & ~1;
   const StageMap<C> map(row0, n_out, wrow, ncols, xrow);
+  uint8_t* even = lds;               // stages 0, 2, 4, ...
+  uint8_t* odd = lds + C::kBytes;    // stages 1, 3, 5, ...
   Prefetch<C> pa = stage_load<C>(map, W, xq, nb, 0);
-  Prefetch<C> pb = stage_load<C>(map, W, xq, nb, min(KSP, (nstage - 1) * KSP));
-  stage_store<C>(map, pa, lds);
+  Prefetch<C> pb = stage_load<C>(map, W, xq, nb, KSP);
+  stage_store<C>(map, pa, even);
   __syncthreads();
-  for (int s = 0; s < nstage; s += 2) {
-    uint8_t* even = lds + (s & 1) * C::kBytes;        // holds stage s
-    uint8_t* odd = lds + ((s + 1) & 1) * C::kBytes;   // receives stage s + 1
-    if (s + 2 < nstage) pa = stage_load<C>(map, W, xq, nb, (s + 2) * KSP);
+  for (int s = 0; s < nstage2; s += 2) {
+    pa = stage_load<C>(map, W, xq, nb, (s + 2) * KSP);
     compute(even, s);
-    if (s + 1 < nstage) stage_store<C>(map, pb, odd);
+    stage_store<C>(map, pb, odd);
     __syncthreads();
-    if (s + 1 >= nstage) break;
-    if (s + 3 < nstage) pb = stage_load<C>(map, W, xq, nb, (s + 3) * KSP);
+    pb = stage_load<C>(map, W, xq, nb, (s + 3) * KSP);
     compute(odd, s + 1);
-    if (s + 2 < nstage) stage_store<C>(map, pa, even);
+    stage_store<C>(map, pa, even);
     __syncthreads();
   }
 
@@ -399,10 +403,11 @@ hipError_t launch_gemm_q4K(const uint8_t* W, int64_t n_out, int64_t n_in, const 
                            hipEvent_t e1) {
   const int nb = static_cast<int>(n_in / 256);
   const int n = static_cast<int>(n_out), nc = static_cast<int>(ncols);
-  // measured on 14336 x 4096 (graph replay): 16 columns 13.1 us; 32 columns 16.3 us
-  // (Cfg<2,1,1> with two row tiles: 19.3); 64 columns 22.6 us (Cfg<4,2,1>: 27.8).
-  // Shapes of 16 wavefronts that need more than 128 registers spill and are slower.
-  if (nc <= 16) return launch_cfg<Cfg<1, 1, 2>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+  // measured on 14336 x 4096 (graph replay): 16 columns 12.2 us (two row tiles:
+  // 13.3); 32 columns 16.3 us (Cfg<2,1,1> with two row tiles: 19.3); 64 columns
+  // 22.6 us (Cfg<4,2,1>: 27.8).  Shapes of 16 wavefronts that need more than 128
+  // registers spill and are slower.
+  if (nc <= 16) return launch_cfg<Cfg<1, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
   if (nc <= 32) return launch_cfg<Cfg<2, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
   if (nc <= 64) return launch_cfg<Cfg<4, 4, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
   return hipErrorInvalidValue;
