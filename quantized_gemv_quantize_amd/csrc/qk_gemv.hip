@@ -632,9 +632,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
 // ---------------------------------------------------------------------------
 // Two Q4_K matrices over one activation row: the gate and up projections of an
 // FFN layer.  The wavefront that owns row r computes it in both W1 and W2 from
-// the same activation operands (rml "Kernels and references": one activation load
-// feeding several weight rows, there four rows of one matrix, here one row of
-// each matrix), then writes y1[r] and y2[r], or the gated activation
+// the same activation operands (candle formats page, "实测：一次点积": vec_dot_4
+// takes one activation row against four weight rows with the activation loaded
+// once; here one row of each matrix), then writes y1[r] and y2[r], or the gated activation
 // silu(y1[r]) * y2[r] = y1 / (1 + e^-y1) * y2 that the down projection consumes.
 // blockIdx.y is the activation column.
 constexpr int kEpiPair = 0, kEpiSwiglu = 1;
