@@ -485,13 +485,6 @@ def main():
     timed_names = ["gate_up", "down"] if swiglu else [gv[0] for gv in wl["gemvs"]]
     n_g = len(timed_names)
 
-    def recorded(evs, g, launch):
-        if evs is not None:
-            evs[g][0].record(stream)
-        launch()
-        if evs is not None:
-            evs[g][1].record(stream)
-
     def step(k, evs=None):
         mats = dev_w[k % copies]
         if swiglu:
@@ -499,10 +492,16 @@ def main():
             at, xf, xq = acts["x"]
             _, h, hq = acts["h"]
             qk.qk_quantize_act(at, xf, xq)
-            recorded(evs, 0, lambda: qk.qk_gemv_pair(gt, mats[0], mats[1], g_out, g_in, xq, 1,
-                                                     qk.QK_EPI_SWIGLU, h))
+            if evs is None:
+                qk.qk_gemv_pair(gt, mats[0], mats[1], g_out, g_in, xq, 1, qk.QK_EPI_SWIGLU, h)
+            else:
+                qk.qk_gemv_pair_timed(gt, mats[0], mats[1], g_out, g_in, xq, 1, qk.QK_EPI_SWIGLU, h,
+                                      evs[0][0], evs[0][1])
             qk.qk_quantize_act(acts["h"][0], h, hq)
-            recorded(evs, 1, lambda: qk.qk_gemv(dt, mats[2], d_out, d_in, hq, 1, ys[2]))
+            if evs is None:
+                qk.qk_gemv(dt, mats[2], d_out, d_in, hq, 1, ys[2])
+            else:
+                qk.qk_gemv_timed(dt, mats[2], d_out, d_in, hq, 1, ys[2], evs[1][0], evs[1][1])
             return
         for key, (at, xf, xq) in acts.items():
             qk.qk_quantize_act(at, xf, xq)
@@ -576,7 +575,7 @@ def main():
     s1.record(stream)
     torch.cuda.synchronize()
     cycles_per_ms = 1_000_000 / max(s0.elapsed_time(s1), 1e-3)
-    hold_ms = 4.0 * enqueue_ms_per_step * args.steps + 10.0  # profilers slow the enqueue
+    hold_ms = 10.0 * enqueue_ms_per_step * args.steps + 20.0  # profilers slow the enqueue
     e_start = torch.cuda.Event(enable_timing=True)
     e_stop = torch.cuda.Event(enable_timing=True)
     hold_done = torch.cuda.Event()
@@ -594,6 +593,45 @@ def main():
 
     kern_ms = np.array([[e0.elapsed_time(e1) for e0, e1 in per] for per in ev])  # [steps, n_g]
     gemv_ms_mean = kern_ms.sum(axis=1).mean()
+
+    # Region C - the read-stream ceiling: the library's read-only probe kernel over
+    # the same weight tensors (same rotation, one launch per tensor, launch-recorded
+    # events, back to back behind a stream hold), i.e. what HBM gives a launch that
+    # reads the same bytes and does nothing else.
+    ceiling = None
+    if not (wl.get("dequant") or quant_row):
+        nbytes = [m.numel() // 16 * 16 for m in dev_w[0]]
+        pouts = [torch.empty(((nb_ + 2047) // 2048,), dtype=torch.int32, device="cuda")
+                 for nb_ in nbytes]
+        pev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in nbytes] for _ in range(args.steps)]
+        for per in pev:
+            for e0, e1 in per:
+                e0.record(stream)
+                e1.record(stream)
+        for k in range(args.warmup):
+            for g, nb_ in enumerate(nbytes):
+                qk.qk_read_probe(dev_w[k % copies][g], nb_, pouts[g])
+        torch.cuda.synchronize()
+        hold2 = torch.cuda.Event()
+        torch.cuda._sleep(int(cycles_per_ms * hold_ms))
+        hold2.record(stream)
+        for k in range(args.steps):
+            for g, nb_ in enumerate(nbytes):
+                e0, e1 = pev[k][g]
+                qk.qk_read_probe(dev_w[(args.warmup + k) % copies][g], nb_, pouts[g], e0, e1)
+        backlog2 = not hold2.query()
+        torch.cuda.synchronize()
+        probe_ms = np.array([[e0.elapsed_time(e1) for e0, e1 in per] for per in pev]).sum(axis=1).mean()
+        ceiling = {"kernel": "qk_read_probe (loads of the same weight bytes only; one launch per "
+                             "weight tensor, launch-recorded events, back to back)" +
+                             ("" if backlog2 else " (hold ended early)"),
+                   "us_per_step": round(float(probe_ms * 1e3), 3),
+                   "weight_GBps": round(sum(nbytes) / (probe_ms / 1e3) / 1e9, 1),
+                   "frac_of_hbm_peak": round(sum(nbytes) / (probe_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "gemv_frac_of_ceiling": round(float(probe_ms / gemv_ms_mean), 4)}
+        log(f"[bench] read-stream ceiling {ceiling['us_per_step']} us/step "
+            f"({ceiling['weight_GBps']} GB/s); GEMV at {ceiling['gemv_frac_of_ceiling']:.3f} of it")
 
     alg_bytes = algorithmic_bytes(wl, qk)
     achieved = alg_bytes / (gemv_ms_mean / 1e3) / 1e9
@@ -654,14 +692,15 @@ def main():
         "cpu_baseline": cpu,
         "detail": {"gemv_kernel_us_per_step": round(float(gemv_ms_mean * 1e3), 3),
                    "kernel_timing": ("events recorded on the launch stream around each kernel"
-                                     if (swiglu or wl.get("dequant") or quant_row) else
+                                     if (wl.get("dequant") or quant_row) else
                                      "HIP events of the kernel launches") +
                                     ", steps run back to back behind a stream hold" +
                                     ("" if backlog else " (hold ended early)"),
                    "traffic_unit": "bytes per step (FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
                    "eager_us_per_step": round(eager_ms / args.steps * 1e3, 3),
                    "gemv_kernel_us": per_kernel_us,
-                   "algorithmic_bytes_per_step_gemv": alg_bytes},
+                   "algorithmic_bytes_per_step_gemv": alg_bytes,
+                   "read_stream_ceiling": ceiling},
     }
     if kernel_family(args.workload) == "gemm":
         # the batched path is also a contraction: 2 int8 ops per weight and column

@@ -201,6 +201,29 @@ int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const 
 int qk_gemv_pair(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
                  const void* xq, int64_t ncols, int epilogue, float* out, void* stream);
 
+/* qk_gemv_pair_timed - qk_gemv_pair whose single kernel launch records ev_start and
+ * ev_stop itself, as qk_gemv_timed.  Arguments and errors otherwise as qk_gemv_pair. */
+int qk_gemv_pair_timed(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
+                       const void* xq, int64_t ncols, int epilogue, float* out, void* stream,
+                       void* ev_start, void* ev_stop);
+
+/*
+ * qk_read_probe - measurement probe, not part of the method: a kernel that only
+ * reads `bytes` bytes of device memory, timed like the GEMV, gives the HBM read
+ * bandwidth one launch of that size reaches on the machine (start-up and drain
+ * included).  A GEMV's weight bandwidth is reported against it as well as against
+ * the vendor peak.
+ *   src       device buffer, 16-byte aligned, `bytes` readable bytes.
+ *   bytes     > 0 and a multiple of 16 (else QK_E_SHAPE).
+ *   out       device uint32 [ceil(bytes / 2048)], 16-byte aligned: word g is the
+ *             XOR of the 32-bit little-endian words of bytes [2048 g, 2048 g + 2048)
+ *             (the last group only up to `bytes`), so a test can check the read.
+ *   stream, ev_start, ev_stop   as qk_gemv_timed (either event may be NULL).
+ * QK_E_NULL for a NULL src or out, QK_E_ALIGN for a misaligned one.
+ */
+int qk_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream, void* ev_start,
+                  void* ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,6 +72,10 @@ def lib():
         L.qk_dequantize_row.argtypes = [i32, p, p, i64, p]
         L.qk_gemv_pair.restype = i32
         L.qk_gemv_pair.argtypes = [i32, p, p, i64, i64, p, i64, i32, p, p]
+        L.qk_gemv_pair_timed.restype = i32
+        L.qk_gemv_pair_timed.argtypes = [i32, p, p, i64, i64, p, i64, i32, p, p, p, p]
+        L.qk_read_probe.restype = i32
+        L.qk_read_probe.argtypes = [p, i64, p, p, p, p]
         _lib = L
     return _lib
 
@@ -193,4 +197,29 @@ def qk_gemv_pair(w_type, W1, W2, n_out, n_in, xq, ncols=1, epilogue=QK_EPI_NONE,
         out = torch.empty(shape, dtype=torch.float32, device=W1.device)
     _check(lib().qk_gemv_pair(w_type, _ptr(W1), _ptr(W2), n_out, n_in, _ptr(xq), ncols, epilogue,
                               _ptr(out), _stream(stream)), "qk_gemv_pair")
+    return out
+
+
+def qk_gemv_pair_timed(w_type, W1, W2, n_out, n_in, xq, ncols, epilogue, out, ev_start, ev_stop,
+                       stream=None):
+    """qk_gemv_pair with an event pair recorded by its kernel launch."""
+    e0 = ctypes.c_void_p(ev_start.cuda_event) if ev_start is not None else None
+    e1 = ctypes.c_void_p(ev_stop.cuda_event) if ev_stop is not None else None
+    _check(lib().qk_gemv_pair_timed(w_type, _ptr(W1), _ptr(W2), n_out, n_in, _ptr(xq), ncols,
+                                    epilogue, _ptr(out), _stream(stream), e0, e1),
+           "qk_gemv_pair_timed")
+    return out
+
+
+def qk_read_probe(src, nbytes, out=None, ev_start=None, ev_stop=None, stream=None):
+    """Read-stream probe over the first nbytes of src (device): returns out, uint32
+    [ceil(nbytes / 2048)], the XOR of each 2048-byte group's 32-bit words.  The
+    events (torch.cuda.Event(enable_timing=True)) are recorded by the launch."""
+    import torch
+    if out is None:
+        out = torch.empty(((max(nbytes, 0) + 2047) // 2048,), dtype=torch.int32, device=src.device)
+    e0 = ctypes.c_void_p(ev_start.cuda_event) if ev_start is not None else None
+    e1 = ctypes.c_void_p(ev_stop.cuda_event) if ev_stop is not None else None
+    _check(lib().qk_read_probe(_ptr(src), nbytes, _ptr(out), _stream(stream), e0, e1),
+           "qk_read_probe")
     return out

@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqk.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["qk_capi.hip", "qk_quantize.hip", "qk_gemv.hip", "qk_gemm.hip", "qk_dequant.hip"]
+SOURCES = ["qk_capi.hip", "qk_quantize.hip", "qk_gemv.hip", "qk_gemm.hip", "qk_dequant.hip",
+           "qk_probe.hip"]
 ARCH = "gfx950"
 
 

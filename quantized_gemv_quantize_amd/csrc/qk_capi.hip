@@ -190,8 +190,9 @@ int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const 
   return gemv_impl(w_type, W, n_out, n_in, xq, ncols, y, nullptr, stream, ev_start, ev_stop);
 }
 
-int qk_gemv_pair(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
-                 const void* xq, int64_t ncols, int epilogue, float* out, void* stream) {
+int qk_gemv_pair_timed(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
+                       const void* xq, int64_t ncols, int epilogue, float* out, void* stream,
+                       void* ev_start, void* ev_stop) {
   if (w_type != QK_TYPE_Q4_K) return QK_E_TYPE;
   if (epilogue != QK_EPI_NONE && epilogue != QK_EPI_SWIGLU) return QK_E_ARG;
   int rc = check_gemv(w_type, W1, n_out, n_in, xq, ncols, out);
@@ -202,7 +203,15 @@ int qk_gemv_pair(int w_type, const void* W1, const void* W2, int64_t n_out, int6
   if (!aligned16(W2)) return QK_E_ALIGN;
   return status_of(qk::launch_gemv_pair(static_cast<const uint8_t*>(W1), static_cast<const uint8_t*>(W2),
                                         n_out, n_in, static_cast<const uint8_t*>(xq), ncols,
-                                        epilogue == QK_EPI_SWIGLU, out, static_cast<hipStream_t>(stream)));
+                                        epilogue == QK_EPI_SWIGLU, out, static_cast<hipStream_t>(stream),
+                                        static_cast<hipEvent_t>(ev_start),
+                                        static_cast<hipEvent_t>(ev_stop)));
+}
+
+int qk_gemv_pair(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
+                 const void* xq, int64_t ncols, int epilogue, float* out, void* stream) {
+  return qk_gemv_pair_timed(w_type, W1, W2, n_out, n_in, xq, ncols, epilogue, out, stream, nullptr,
+                            nullptr);
 }
 
 int qk_gemv_block_sums(int w_type, const void* W, int64_t n_out, int64_t n_in,
@@ -220,6 +229,17 @@ int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* st
   if (!aligned16(src) || !aligned16(dst)) return QK_E_ALIGN;
   return status_of(qk::launch_dequantize(type, static_cast<const uint8_t*>(src), dst, n / be,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int qk_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream, void* ev_start,
+                  void* ev_stop) {
+  if (bytes <= 0 || bytes % 16 != 0) return QK_E_SHAPE;
+  if (src == nullptr || out == nullptr) return QK_E_NULL;
+  if (!aligned16(src) || !aligned16(out)) return QK_E_ALIGN;
+  return status_of(qk::launch_read_probe(static_cast<const uint8_t*>(src), bytes, out,
+                                         static_cast<hipStream_t>(stream),
+                                         static_cast<hipEvent_t>(ev_start),
+                                         static_cast<hipEvent_t>(ev_stop)));
 }
 
 }  // extern "C"

@@ -1067,9 +1067,22 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
 #undef QK_LDS
 }
 
+// One launch, with the caller's start / stop events recorded by the launch itself
+// when either is non-null (HIP extended launch).
+template <typename K, typename... Args>
+void launch_ev(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+               Args... args) {
+  if (e0 != nullptr || e1 != nullptr) {
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), s, e0, e1, 0, args...);
+  } else {
+    kernel<<<grid, block, lds, s>>>(args...);
+  }
+}
+
 template <int EPI>
 hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
-                           const uint8_t* xq, int64_t ncols, float* out, hipStream_t s) {
+                           const uint8_t* xq, int64_t ncols, float* out, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1) {
   const int nb = static_cast<int>(n_in / 256);
   const int n = static_cast<int>(n_out);
   const int passes = (nb + 15) / 16;
@@ -1079,21 +1092,23 @@ hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, 
     constexpr int64_t kPairWaves = kMaxWaves / 2;
     const int64_t waves = n_out < kPairWaves ? n_out : kPairWaves;
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));
-    if (passes == 1) gemv_q4_K_pair_reg<4, 1, EPI><<<grid, 256, 0, s>>>(W1, W2, n, nb, xq, out);
-    else gemv_q4_K_pair_reg<4, 2, EPI><<<grid, 256, 0, s>>>(W1, W2, n, nb, xq, out);
+    if (passes == 1) launch_ev(gemv_q4_K_pair_reg<4, 1, EPI>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
+    else launch_ev(gemv_q4_K_pair_reg<4, 2, EPI>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
   } else {
     const dim3 grid(static_cast<unsigned>((n_out + kWaves - 1) / kWaves), static_cast<unsigned>(ncols));
     const int64_t lds = gemv_lds_bytes(kQ4_K, n_in);
-    gemv_q4_K_pair_kernel<kWaves, 3, EPI><<<grid, kWaves * 64, lds, s>>>(W1, W2, n, nb, xq, out);
+    launch_ev(gemv_q4_K_pair_kernel<kWaves, 3, EPI>, grid, dim3(kWaves * 64), static_cast<size_t>(lds), s, e0, e1,
+              W1, W2, n, nb, xq, out);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_pair(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
-                            const uint8_t* xq, int64_t ncols, int swiglu, float* out, hipStream_t s) {
+                            const uint8_t* xq, int64_t ncols, int swiglu, float* out, hipStream_t s,
+                            hipEvent_t e0, hipEvent_t e1) {
   if (n_out <= 0 || ncols <= 0) return hipSuccess;
-  return swiglu ? launch_pair_epi<kEpiSwiglu>(W1, W2, n_out, n_in, xq, ncols, out, s)
-                : launch_pair_epi<kEpiPair>(W1, W2, n_out, n_in, xq, ncols, out, s);
+  return swiglu ? launch_pair_epi<kEpiSwiglu>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1)
+                : launch_pair_epi<kEpiPair>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1);
 }
 
 }  // namespace qk

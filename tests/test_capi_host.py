@@ -10,6 +10,8 @@ import os
 import re
 import subprocess
 
+import pytest
+
 import quantized_gemv_quantize_amd as qk
 from golden_io import rows
 
@@ -136,23 +138,38 @@ def test_gemv_validation():
                    None) == 4
 
 
-def test_gemv_pair_validation():
-    f = "qk_gemv_pair"
+@pytest.mark.parametrize("f", ["qk_gemv_pair", "qk_gemv_pair_timed"])
+def test_gemv_pair_validation(f):
     T4K = qk.QK_TYPE_Q4_K
-    assert _status(f, qk.QK_TYPE_Q6_K, GOOD, GOOD, 4, 256, GOOD, 1, 0, GOOD, None) == 1  # Q4_K only
-    assert _status(f, T4K, GOOD, GOOD, 4, 256, GOOD, 1, 2, GOOD, None) == 8     # epilogue
-    assert _status(f, T4K, GOOD, GOOD, 4, 255, GOOD, 1, 0, GOOD, None) == 3
-    assert _status(f, T4K, GOOD, GOOD, -1, 256, GOOD, 1, 1, GOOD, None) == 3
-    assert _status(f, T4K, GOOD, GOOD, 4, 256, GOOD, 65536, 1, GOOD, None) == 7  # columns
+    ev = (None, None) if f.endswith("_timed") else ()
+
+    def st(*a):
+        return _status(f, *a, *ev)
+    assert st(qk.QK_TYPE_Q6_K, GOOD, GOOD, 4, 256, GOOD, 1, 0, GOOD, None) == 1  # Q4_K only
+    assert st(T4K, GOOD, GOOD, 4, 256, GOOD, 1, 2, GOOD, None) == 8     # epilogue
+    assert st(T4K, GOOD, GOOD, 4, 255, GOOD, 1, 0, GOOD, None) == 3
+    assert st(T4K, GOOD, GOOD, -1, 256, GOOD, 1, 1, GOOD, None) == 3
+    assert st(T4K, GOOD, GOOD, 4, 256, GOOD, 65536, 1, GOOD, None) == 7  # columns
     big = qk.qk_max_n_in(T4K) + 256
-    assert _status(f, T4K, GOOD, GOOD, 4, big, GOOD, 1, 1, GOOD, None) == 7
-    assert _status(f, T4K, GOOD, None, 4, 256, GOOD, 1, 1, GOOD, None) == 5
-    assert _status(f, T4K, None, GOOD, 4, 256, GOOD, 1, 1, GOOD, None) == 5
-    assert _status(f, T4K, GOOD, GOOD, 4, 256, GOOD, 1, 1, None, None) == 5
-    assert _status(f, T4K, GOOD, ODD, 4, 256, GOOD, 1, 1, GOOD, None) == 4
-    assert _status(f, T4K, GOOD, GOOD, 4, 256, ODD, 1, 0, GOOD, None) == 4
-    assert _status(f, T4K, GOOD, GOOD, 0, 256, GOOD, 1, 1, GOOD, None) == 0     # no-op
-    assert _status(f, T4K, None, None, 4, 256, None, 0, 0, None, None) == 0     # no-op
+    assert st(T4K, GOOD, GOOD, 4, big, GOOD, 1, 1, GOOD, None) == 7
+    assert st(T4K, GOOD, None, 4, 256, GOOD, 1, 1, GOOD, None) == 5
+    assert st(T4K, None, GOOD, 4, 256, GOOD, 1, 1, GOOD, None) == 5
+    assert st(T4K, GOOD, GOOD, 4, 256, GOOD, 1, 1, None, None) == 5
+    assert st(T4K, GOOD, ODD, 4, 256, GOOD, 1, 1, GOOD, None) == 4
+    assert st(T4K, GOOD, GOOD, 4, 256, ODD, 1, 0, GOOD, None) == 4
+    assert st(T4K, GOOD, GOOD, 0, 256, GOOD, 1, 1, GOOD, None) == 0     # no-op
+    assert st(T4K, None, None, 4, 256, None, 0, 0, None, None) == 0     # no-op
+
+
+def test_read_probe_validation():
+    f = "qk_read_probe"
+    assert _status(f, GOOD, 0, GOOD, None, None, None) == 3
+    assert _status(f, GOOD, -16, GOOD, None, None, None) == 3
+    assert _status(f, GOOD, 24, GOOD, None, None, None) == 3      # not whole 16-byte units
+    assert _status(f, None, 4096, GOOD, None, None, None) == 5
+    assert _status(f, GOOD, 4096, None, None, None, None) == 5
+    assert _status(f, ODD, 4096, GOOD, None, None, None) == 4
+    assert _status(f, GOOD, 4096, ODD, None, None, None) == 4
 
 
 def test_dequantize_validation():

@@ -399,6 +399,39 @@ def test_gemv_timed_matches_untimed(torch_cuda):
     assert torch_cuda.equal(y0, y1)
 
 
+def test_gemv_pair_timed_matches_untimed(torch_cuda):
+    rng = np.random.default_rng(9)
+    for n_in in (4096, 11008):  # the register kernel and the LDS kernel
+        W1 = dev(torch_cuda, synth.q4_K_blocks(rng, 64, n_in))
+        W2 = dev(torch_cuda, synth.q4_K_blocks(rng, 64, n_in))
+        xq = qk.qk_quantize_act(T8K, dev(torch_cuda, rng.standard_normal((2, n_in)).astype(np.float32)))
+        for epi in (qk.QK_EPI_NONE, qk.QK_EPI_SWIGLU):
+            say("gemv_pair_timed", n_in, epi)
+            out0 = qk.qk_gemv_pair(T4K, W1, W2, 64, n_in, xq, 2, epi)
+            e0 = torch_cuda.cuda.Event(enable_timing=True)
+            e1 = torch_cuda.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            out1 = torch_cuda.empty_like(out0)
+            qk.qk_gemv_pair_timed(T4K, W1, W2, 64, n_in, xq, 2, epi, out1, e0, e1)
+            e1.synchronize()
+            assert e0.elapsed_time(e1) > 0
+            assert torch_cuda.equal(out0, out1)
+
+
+@pytest.mark.parametrize("nbytes", [16, 2048, 5 * 2048 + 7 * 16, 25_362_432])
+def test_read_probe_xor_of_each_group(torch_cuda, nbytes):
+    say("read_probe", nbytes)
+    rng = np.random.default_rng(10)
+    buf = rng.integers(0, 256, size=nbytes + 4096, dtype=np.uint8)  # bytes past nbytes must not count
+    out = host(qk.qk_read_probe(dev(torch_cuda, buf), nbytes)).view(np.uint32)
+    ng = (nbytes + 2047) // 2048
+    words = np.zeros(ng * 512, dtype=np.uint32)
+    words[:nbytes // 4] = buf[:nbytes].view("<u4")
+    assert out.shape == (ng,)
+    assert np.array_equal(out, np.bitwise_xor.reduce(words.reshape(ng, 512), axis=1))
+
+
 def test_graph_capture_replays_match_eager(torch_cuda):
     # quantize + GEMV captured into a HIP graph; several replays, with eager work
     # and synchronizations between them, must each equal the eager result.
