@@ -48,8 +48,9 @@ extern "C" {
 #define QK_E_ALIGN 4  /* a base pointer is not 16-byte aligned */
 #define QK_E_NULL 5   /* a required pointer is NULL */
 #define QK_E_DEVICE 6 /* the HIP runtime reported an error while enqueueing */
-#define QK_E_LIMIT 7  /* the activation row does not fit the kernels' LDS budget, or
-                         more activation columns than a call takes */
+#define QK_E_LIMIT 7  /* the activation row does not fit the kernels' LDS budget, more
+                         activation columns than a call takes, or more work than one
+                         kernel launch addresses (2^32 - 1 work-items) */
 #define QK_E_ARG 8    /* an argument outside its documented set of values */
 
 /* Epilogues of qk_gemv_pair. */

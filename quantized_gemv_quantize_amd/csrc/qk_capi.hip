@@ -25,7 +25,12 @@ bool is_act(int t) { return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q8_K; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int status_of(hipError_t e) { return e == hipSuccess ? QK_OK : QK_E_DEVICE; }
+// A launch beyond the 32-bit work-item count (refused by the launchers before
+// anything is enqueued) is a size limit; any other runtime error is QK_E_DEVICE.
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return QK_OK;
+  return e == hipErrorInvalidConfiguration ? QK_E_LIMIT : QK_E_DEVICE;
+}
 
 // Common checks of a GEMV call; `out` is y or sums.
 int check_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
@@ -61,7 +66,7 @@ int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void
       hipEvent_t e1 = (c + nc == ncols) ? static_cast<hipEvent_t>(ev1) : nullptr;
       const hipError_t e = qk::launch_gemm_q4K(static_cast<const uint8_t*>(W), n_out, n_in, xc, nc,
                                                yc, sc, s, e0, e1);
-      if (e != hipSuccess) return QK_E_DEVICE;
+      if (e != hipSuccess) return status_of(e);
     }
     return QK_OK;
   }
@@ -73,7 +78,7 @@ int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void
     hipEvent_t e1 = (c == ncols - 1) ? static_cast<hipEvent_t>(ev1) : nullptr;
     const hipError_t e = qk::launch_gemv(w_type, static_cast<const uint8_t*>(W), n_out, n_in, xc,
                                          yc, sc, s, e0, e1);
-    if (e != hipSuccess) return QK_E_DEVICE;
+    if (e != hipSuccess) return status_of(e);
   }
   return QK_OK;
 }
@@ -133,7 +138,7 @@ const char* qk_status_str(int status) {
     case QK_E_ALIGN: return "a base pointer is not 16-byte aligned";
     case QK_E_NULL: return "a required pointer is NULL";
     case QK_E_DEVICE: return "HIP runtime error while enqueueing";
-    case QK_E_LIMIT: return "activation row exceeds the GEMV LDS budget, or too many columns";
+    case QK_E_LIMIT: return "a size beyond the kernels' limits (LDS budget, columns, one launch)";
     case QK_E_ARG: return "an argument outside its documented set of values";
     default: return "unknown status";
   }

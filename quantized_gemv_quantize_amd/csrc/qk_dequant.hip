@@ -202,37 +202,18 @@ __global__ __launch_bounds__(256) void dequant_q6_K_kernel(const uint8_t* __rest
 hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t nblocks,
                              hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
+  // 32-element formats: 8 lanes per block; K-quants: kSB superblocks per wavefront
+  const bool small = type == kQ8_0 || type == kQ4_0 || type == kQ4_1 || type == kQ5_0;
+  unsigned grid = 0;
+  if (!launch_grid(small ? (nblocks * 8 + 255) / 256 : (nblocks + 4 * kSB - 1) / (4 * kSB), 256, &grid))
+    return hipErrorInvalidConfiguration;
   switch (type) {
-    case kQ8_0: {
-      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
-      dequant_q8_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
-      break;
-    }
-    case kQ4_0: {
-      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
-      dequant_q4_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
-      break;
-    }
-    case kQ4_1: {
-      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
-      dequant_q4_1_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
-      break;
-    }
-    case kQ5_0: {
-      const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
-      dequant_q5_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
-      break;
-    }
-    case kQ4_K: {
-      const unsigned grid = static_cast<unsigned>((nblocks + 4 * kSB - 1) / (4 * kSB));
-      dequant_q4_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
-      break;
-    }
-    case kQ6_K: {
-      const unsigned grid = static_cast<unsigned>((nblocks + 4 * kSB - 1) / (4 * kSB));
-      dequant_q6_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks);
-      break;
-    }
+    case kQ8_0: dequant_q8_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ4_0: dequant_q4_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ4_1: dequant_q4_1_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ5_0: dequant_q5_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ4_K: dequant_q4_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ6_K: dequant_q6_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     default:
       return hipErrorInvalidValue;
   }

@@ -371,13 +371,14 @@ template <class C, bool SUMS>
 hipError_t launch_kernel(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, float* y,
                          int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   auto k = gemm_q4_K_mfma<C, SUMS>;
-  const unsigned grid = static_cast<unsigned>((n_out + C::kRows - 1) / C::kRows);
+  unsigned grid = 0;
+  if (!launch_grid((n_out + C::kRows - 1) / C::kRows, C::kThreads, &grid)) return hipErrorInvalidConfiguration;
   constexpr size_t lds = 2 * C::kBytes;
   if constexpr (lds > 65536) {
-    // above the default dynamic LDS limit: raise it once for this kernel
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       static_cast<int>(lds));
+    // above the default dynamic LDS limit: raise it for this kernel on the current
+    // device (set on every launch: the library keeps no per-device state)
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (attr != hipSuccess) return attr;
   }
   if (e0 != nullptr || e1 != nullptr) {

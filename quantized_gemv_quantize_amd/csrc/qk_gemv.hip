@@ -973,7 +973,8 @@ template <int NW, typename K>
 hipError_t launch(K kernel, int64_t n_out, int64_t lds_bytes, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1, const uint8_t* W, int nb, const uint8_t* xq, float* y,
                   int32_t* sums) {
-  const unsigned grid = static_cast<unsigned>((n_out + NW - 1) / NW);
+  unsigned grid = 0;
+  if (!launch_grid((n_out + NW - 1) / NW, NW * 64, &grid)) return hipErrorInvalidConfiguration;
   const int n = static_cast<int>(n_out);
   if (e0 != nullptr || e1 != nullptr) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), static_cast<uint32_t>(lds_bytes),
@@ -990,7 +991,8 @@ hipError_t launch_rows(K kernel, int64_t n_out, int rpw, int max_waves, hipStrea
                        float* y, int32_t* sums) {
   const int64_t groups = (n_out + rpw - 1) / rpw;
   const int64_t waves = groups < max_waves ? groups : max_waves;
-  const unsigned grid = static_cast<unsigned>((waves + NW - 1) / NW);
+  unsigned grid = 0;
+  if (!launch_grid((waves + NW - 1) / NW, NW * 64, &grid)) return hipErrorInvalidConfiguration;
   const int n = static_cast<int>(n_out);
   if (e0 != nullptr || e1 != nullptr) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), 0, s, e0, e1, 0, W, n, nb, xq, y, sums);
@@ -1091,11 +1093,13 @@ hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, 
     // (2048 measured best on the 11008 x 4096 gate / up pair; 4096 and 8192 slower)
     constexpr int64_t kPairWaves = kMaxWaves / 2;
     const int64_t waves = n_out < kPairWaves ? n_out : kPairWaves;
-    const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));  // <= 512
     if (passes == 1) launch_ev(gemv_q4_K_pair_reg<4, 1, EPI>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
     else launch_ev(gemv_q4_K_pair_reg<4, 2, EPI>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
   } else {
-    const dim3 grid(static_cast<unsigned>((n_out + kWaves - 1) / kWaves), static_cast<unsigned>(ncols));
+    unsigned gx = 0;
+    if (!launch_grid((n_out + kWaves - 1) / kWaves, kWaves * 64, &gx)) return hipErrorInvalidConfiguration;
+    const dim3 grid(gx, static_cast<unsigned>(ncols));
     const int64_t lds = gemv_lds_bytes(kQ4_K, n_in);
     launch_ev(gemv_q4_K_pair_kernel<kWaves, 3, EPI>, grid, dim3(kWaves * 64), static_cast<size_t>(lds), s, e0, e1,
               W1, W2, n, nb, xq, out);

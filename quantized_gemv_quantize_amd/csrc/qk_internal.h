@@ -9,6 +9,16 @@ namespace qk {
 
 enum WType : int { kQ4_0 = 2, kQ4_1 = 3, kQ5_0 = 6, kQ8_0 = 8, kQ4_K = 12, kQ6_K = 14, kQ8_K = 15 };
 
+// The work-items of one launch are counted in 32 bits (the dispatch packet's grid
+// size).  Launchers size their grids through launch_grid and refuse a larger launch
+// with hipErrorInvalidConfiguration, which the C ABI reports as QK_E_LIMIT.
+constexpr int64_t kMaxLaunchItems = 0xFFFFFFFFll;
+inline bool launch_grid(int64_t blocks, int threads_per_block, unsigned* grid) {
+  if (blocks < 0 || blocks > kMaxLaunchItems / threads_per_block) return false;
+  *grid = static_cast<unsigned>(blocks);
+  return true;
+}
+
 // Activation quantization of `nblocks` consecutive blocks (any number of columns
 // laid end to end: blocks of consecutive columns are contiguous).
 hipError_t launch_quantize(int act_type, const float* x, uint8_t* xq, int64_t nblocks,

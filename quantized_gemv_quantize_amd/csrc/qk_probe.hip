@@ -50,14 +50,14 @@ hipError_t launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* out, h
                              hipEvent_t e1) {
   const int64_t n16 = bytes / 16;
   const int64_t ngroups = (n16 + 127) / 128;
-  const int64_t grid = (ngroups + kProbeThreads / 64 - 1) / (kProbeThreads / 64);
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  unsigned grid = 0;
+  if (!launch_grid((ngroups + kProbeThreads / 64 - 1) / (kProbeThreads / 64), kProbeThreads, &grid))
+    return hipErrorInvalidConfiguration;
   const uint4* p = reinterpret_cast<const uint4*>(src);
   if (e0 != nullptr || e1 != nullptr) {
-    hipExtLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(grid)), dim3(kProbeThreads), 0, s, e0, e1, 0,
-                          p, n16, ngroups, out);
+    hipExtLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(kProbeThreads), 0, s, e0, e1, 0, p, n16, ngroups, out);
   } else {
-    read_probe_kernel<<<static_cast<unsigned>(grid), kProbeThreads, 0, s>>>(p, n16, ngroups, out);
+    read_probe_kernel<<<grid, kProbeThreads, 0, s>>>(p, n16, ngroups, out);
   }
   return hipGetLastError();
 }

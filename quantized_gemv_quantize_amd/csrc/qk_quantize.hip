@@ -246,14 +246,17 @@ __global__ __launch_bounds__(256) void quantize_row_kernel(const float* __restri
 hipError_t launch_quantize_row(int type, const float* x, uint8_t* dst, int64_t nblocks,
                                hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
-  const unsigned grid = static_cast<unsigned>((nblocks * 8 + 255) / 256);
-  // 4 wavefronts per workgroup, 8 * kRowUnroll blocks per wavefront
-  const unsigned rgrid = static_cast<unsigned>((nblocks + 32 * kRowUnroll - 1) / (32 * kRowUnroll));
+  // Q8_0: 8 lanes per block; the others: 4 wavefronts per workgroup, 8 * kRowUnroll
+  // blocks per wavefront
+  unsigned grid = 0;
+  if (!launch_grid(type == kQ8_0 ? (nblocks * 8 + 255) / 256 : (nblocks + 32 * kRowUnroll - 1) / (32 * kRowUnroll),
+                   256, &grid))
+    return hipErrorInvalidConfiguration;
   switch (type) {
     case kQ8_0: quantize_q8_0_kernel<<<grid, 256, 0, s>>>(x, dst, nblocks); break;
-    case kQ4_0: quantize_row_kernel<kFmtQ4_0><<<rgrid, 256, 0, s>>>(x, dst, nblocks); break;
-    case kQ4_1: quantize_row_kernel<kFmtQ4_1><<<rgrid, 256, 0, s>>>(x, dst, nblocks); break;
-    case kQ5_0: quantize_row_kernel<kFmtQ5_0><<<rgrid, 256, 0, s>>>(x, dst, nblocks); break;
+    case kQ4_0: quantize_row_kernel<kFmtQ4_0><<<grid, 256, 0, s>>>(x, dst, nblocks); break;
+    case kQ4_1: quantize_row_kernel<kFmtQ4_1><<<grid, 256, 0, s>>>(x, dst, nblocks); break;
+    case kQ5_0: quantize_row_kernel<kFmtQ5_0><<<grid, 256, 0, s>>>(x, dst, nblocks); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -262,12 +265,13 @@ hipError_t launch_quantize_row(int type, const float* x, uint8_t* dst, int64_t n
 hipError_t launch_quantize(int act_type, const float* x, uint8_t* xq, int64_t nblocks,
                            hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
+  // Q8_0: 8 lanes per block; Q8_K: one wavefront per block
+  unsigned grid = 0;
+  if (!launch_grid(act_type == kQ8_0 ? (nblocks * 8 + 255) / 256 : (nblocks + 3) / 4, 256, &grid))
+    return hipErrorInvalidConfiguration;
   if (act_type == kQ8_0) {
-    const int64_t threads = nblocks * 8;
-    const unsigned grid = static_cast<unsigned>((threads + 255) / 256);
     quantize_q8_0_kernel<<<grid, 256, 0, s>>>(x, xq, nblocks);
   } else {
-    const unsigned grid = static_cast<unsigned>((nblocks + 3) / 4);
     quantize_q8_K_kernel<<<grid, 256, 0, s>>>(x, xq, nblocks);
   }
   return hipGetLastError();

@@ -183,6 +183,22 @@ def test_dequantize_validation():
     assert _status(f, qk.QK_TYPE_Q4_0, GOOD, GOOD, 0, None) == 0
 
 
+def test_launch_size_limit():
+    # sizes whose grid would exceed one launch's 32-bit work-item count are refused
+    # with QK_E_LIMIT before any HIP call (the fake pointers are never touched)
+    big = 1 << 40
+    assert _status("qk_dequantize_row", qk.QK_TYPE_Q8_0, GOOD, GOOD, big, None) == 7
+    assert _status("qk_dequantize_row", qk.QK_TYPE_Q6_K, GOOD, GOOD, big, None) == 7
+    assert _status("qk_quantize_row", qk.QK_TYPE_Q4_0, GOOD, GOOD, big, None) == 7
+    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, 1 << 27, None) == 7
+    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_0, GOOD, GOOD, 32, 1 << 30, None) == 7
+    assert _status("qk_read_probe", GOOD, big, GOOD, None, None, None) == 7
+    # one wavefront per row (rows beyond one pass): 2^26 rows of 64 lanes is the limit
+    assert _status("qk_gemv", qk.QK_TYPE_Q4_K, GOOD, 1 << 27, 11008, GOOD, 1, GOOD, None) == 7
+    # the batched kernel: 64 rows per 512-thread workgroup
+    assert _status("qk_gemv", qk.QK_TYPE_Q4_K, GOOD, (1 << 31) - 1, 4096, GOOD, 16, GOOD, None) == 7
+
+
 def test_status_strings():
     for s in (0, 1, 3, 4, 5, 6, 7, 8):
         assert qk.status_str(s) and qk.status_str(s) != "unknown status"

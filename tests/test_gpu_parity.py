@@ -491,7 +491,8 @@ SILU_SLOPE = 1.0998  # max |d/dv v*sigmoid(v)|
 
 def silu64(v):
     v = v.astype(np.float64)
-    return v / (1.0 + np.exp(-v))
+    with np.errstate(over="ignore"):  # e^-v = inf for very negative v gives the limit 0
+        return v / (1.0 + np.exp(-v))
 
 
 def assert_swiglu(h_gpu, g_o, u_o, l1g, l1u, what):
