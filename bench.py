@@ -12,7 +12,10 @@ Prints ONE JSON line on stdout (details on stderr):
              (HIP events recorded by the kernel launches themselves, on the
              launch stream) against the 8 TB/s HBM peak
   cpu_baseline  the scalar C oracle on the host, single thread, on a bounded
-             sample of the same workload
+             sample of the same workload (all_cores: the same sample on every
+             usable host core at once)
+  detail.read_stream_ceiling  qk_read_probe over the same weight tensors: the
+             bandwidth a launch that only reads those bytes reaches on the machine
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 Profiling helpers (no GPU use; they read rocprofv3 CSV output):
@@ -153,30 +156,35 @@ def gpu_copy_like(torch, w_type, n_out, n_in, gen):
     return w.reshape(n_out, nb * bb)
 
 
-def cpu_baseline(name, wl, inputs, seconds):
-    """The scalar C oracle (single thread) on a bounded sample of the workload:
-    the first rows of each GEMV, repeated until `seconds` have passed."""
+def cpu_baseline(name, wl, inputs, seconds, seconds_all=5.0):
+    """The scalar C oracle on a bounded sample of the workload: the first rows of
+    each GEMV, repeated until `seconds` have passed on one thread; then the same
+    sample on every usable host core at once (one thread each, the C calls release
+    the GIL) for `seconds_all`, reported beside it."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from oracle import oracle as orc
-    t_end = time.perf_counter() + seconds
-    done_bytes = 0
-    reps = 0
     sample_rows = {}
-    t0 = time.perf_counter()
-    while True:
+
+    def one_rep():
+        """One pass over the sample; returns the bytes it covers."""
+        done = 0
         if wl.get("dequant"):
             for wname, wt, n_out, n_in, _ in wl["gemvs"]:
                 W = inputs[wname]
                 rows = min(n_out, max(1, int(4e6 // n_in)))
                 sample_rows[wname] = rows
                 orc.dequantize(wt, W[:rows], rows * n_in)
-                done_bytes += rows * W.shape[1] + 4 * rows * n_in
+                done += rows * W.shape[1] + 4 * rows * n_in
+            return done
         if wl.get("quantize_row"):
             for wname, wt, n_out, n_in, _ in wl["gemvs"]:
                 W = inputs[wname]
                 rows = min(n_out, max(1, int(4e6 // n_in)))
                 sample_rows[wname] = rows
                 b = orc.quantize(wt, W[:rows])
-                done_bytes += 4 * rows * n_in + b.size
+                done += 4 * rows * n_in + b.size
+            return done
         if wl.get("swiglu_pair"):
             # gate / up rows with the SwiGLU epilogue; down rows against the
             # quantized stand-in activation (the full h needs every gate row)
@@ -190,11 +198,7 @@ def cpu_baseline(name, wl, inputs, seconds):
             rows_d = min(d_out, max(1, int(4e6 // d_in)))
             orc.gemv(dt, inputs[dn][:rows_d], rows_d, d_in, hq, 1)
             sample_rows.update({gn: rows, un: rows, dn: rows_d})
-            done_bytes += 2 * rows * inputs[gn].shape[1] + rows_d * inputs[dn].shape[1]
-            reps += 1
-            if time.perf_counter() >= t_end:
-                break
-            continue
+            return 2 * rows * inputs[gn].shape[1] + rows_d * inputs[dn].shape[1]
         for key, (at, n, ncols) in wl["acts"].items():
             x = inputs[key] if inputs[key].ndim == 2 else inputs[key][None, :]
             xq = orc.quantize(at, x[:ncols])
@@ -205,15 +209,35 @@ def cpu_baseline(name, wl, inputs, seconds):
                 rows = min(n_out, max(1, int(4e6 // n_in)))  # about 4 M weights per GEMV
                 sample_rows[wname] = rows
                 orc.gemv(wt, W[:rows], rows, n_in, xq, ncols)
-                done_bytes += rows * W.shape[1]
-        reps += 1
-        if time.perf_counter() >= t_end:
-            break
+                done += rows * W.shape[1]
+        return done
+
+    def run_for(budget):
+        t_end = time.perf_counter() + budget
+        done, reps = 0, 0
+        while True:
+            done += one_rep()
+            reps += 1
+            if time.perf_counter() >= t_end:
+                return done, reps
+
+    t0 = time.perf_counter()
+    done_bytes, reps = run_for(seconds)
     dt = time.perf_counter() - t0
     desc = ", ".join(f"{k}: first {r} rows" for k, r in sample_rows.items())
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{desc}; {_kind(wl)} repeated "
-                      f"{reps}x in {dt:.1f} s, single thread on {_host_cpu()}"}
+    out = {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{desc}; {_kind(wl)} repeated "
+                     f"{reps}x in {dt:.1f} s, single thread on {_host_cpu()}"}
+    if seconds_all > 0:
+        nthreads = min(len(os.sched_getaffinity(0)), 16)  # the host share of one GPU
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            res = list(ex.map(lambda _: run_for(seconds_all), range(nthreads)))
+        dt_all = time.perf_counter() - t0
+        out["all_cores"] = {"value": round(sum(r[0] for r in res) / dt_all / 1e9, 4), "cores": nthreads,
+                            "sample": f"the same sample on {nthreads} threads at once, "
+                                      f"{sum(r[1] for r in res)} passes in {dt_all:.1f} s"}
+    return out
 
 
 def _host_cpu():
