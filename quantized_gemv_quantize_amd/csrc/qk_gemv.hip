@@ -1079,14 +1079,16 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
       const int passes = (nb + 15) / 16;
       if (passes == 1) return S ? QK_ROWS((gemv_q4_K_reg<4, 1, 1, true>)) : QK_ROWS((gemv_q4_K_reg<4, 1, 1, false>));
       if (passes == 2) return S ? QK_ROWS((gemv_q4_K_reg<4, 2, 1, true>)) : QK_ROWS((gemv_q4_K_reg<4, 2, 1, false>));
-      return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 3, true>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 3, false>));
+      if (passes == 3) return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 3, true>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 3, false>));
+      return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 4, true>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 4, false>));
     }
     case kQ6_K: {
       const int nb = static_cast<int>(n_in / 256);
       const int passes = (nb + 15) / 16;
       if (passes == 1) return S ? QK_ROWS((gemv_q6_K_reg<4, 1, true>)) : QK_ROWS((gemv_q6_K_reg<4, 1, false>));
       if (passes == 2) return S ? QK_ROWS((gemv_q6_K_reg<4, 2, true>)) : QK_ROWS((gemv_q6_K_reg<4, 2, false>));
-      return S ? QK_LDS((gemv_q6_K_kernel<kWaves, 3, true>)) : QK_LDS((gemv_q6_K_kernel<kWaves, 3, false>));
+      if (passes == 3) return S ? QK_LDS((gemv_q6_K_kernel<kWaves, 3, true>)) : QK_LDS((gemv_q6_K_kernel<kWaves, 3, false>));
+      return S ? QK_LDS((gemv_q6_K_kernel<kWaves, 4, true>)) : QK_LDS((gemv_q6_K_kernel<kWaves, 4, false>));
     }
     case kQ8_0: {
       const int nb = static_cast<int>(n_in / 32);
