@@ -37,6 +37,19 @@ def test_library_exports_every_declared_function():
     assert set(names) <= exported
 
 
+def test_c_host_program_links_the_library_and_the_oracle():
+    # tests/c/abi_check (built by __graft_entry__.build()) resolves libqk.so and the
+    # oracle in-tree through its rpaths; running it needs a GPU (a gpu test does)
+    exe = os.path.join(ROOT, "tests", "c", "abi_check")
+    if not os.path.exists(exe):
+        pytest.skip("tests/c/abi_check is not built")
+    out = subprocess.run(["ldd", exe], capture_output=True, text=True, check=True).stdout
+    libs = {line.split("=>")[0].strip(): line.split("=>")[1].split("(")[0].strip()
+            for line in out.splitlines() if "=>" in line}
+    assert os.path.realpath(libs["libqk.so"]) == os.path.realpath(qk.LIB_PATH)
+    assert os.path.realpath(libs["liboracle.so"]) == os.path.join(ROOT, "oracle", "liboracle.so")
+
+
 def test_library_is_built_for_gfx950_only():
     # the offload bundle ids embedded in the library name every device target
     data = open(qk.LIB_PATH, "rb").read()

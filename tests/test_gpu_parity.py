@@ -269,8 +269,11 @@ def test_gemv_block_sums_and_y(torch_cuda, t):
             # activation blocks from the GPU quantizer equal the oracle's
             assert np.array_equal(host(qk.qk_quantize_act(at, dev(torch_cuda, X))), xq)
             sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xd, ncols))
-            want = _oracle_sums(t, W, xq, n_out, n_in, ncols)
-            assert np.array_equal(sums, want.reshape(sums.shape)), (t, n_out, n_in, ncols)
+            want = _oracle_sums(t, W, xq, n_out, n_in, ncols).reshape(sums.shape)
+            bad = np.argwhere(sums != want)
+            assert bad.size == 0, (f"type {t} {n_out}x{n_in} ncols {ncols}: {len(bad)} sums differ, "
+                                   f"first [column, row, block, k] {bad[:4].tolist()}: "
+                                   f"got {sums[tuple(bad[0])]}, want {want[tuple(bad[0])]}")
             y = host(qk.qk_gemv(t, Wd, n_out, n_in, xd, ncols))
             y_o, l1 = orc.gemv(t, W, n_out, n_in, xq, ncols)
             assert_y(y, y_o, l1, f"type {t} {n_out}x{n_in} ncols {ncols}")
@@ -430,6 +433,18 @@ def test_read_probe_xor_of_each_group(torch_cuda, nbytes):
     words[:nbytes // 4] = buf[:nbytes].view("<u4")
     assert out.shape == (ng,)
     assert np.array_equal(out, np.bitwise_xor.reduce(words.reshape(ng, 512), axis=1))
+
+
+def test_c_abi_from_a_host_program(torch_cuda):
+    # the C ABI without Python or torch: a host program allocates with the HIP
+    # runtime, calls include/qk.h and checks every result against the C oracle
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "abi_check")
+    assert os.path.exists(exe), "tests/c/abi_check is not built (run __graft_entry__.build())"
+    say("c abi_check")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_check ok" in r.stdout
 
 
 def test_graph_capture_replays_match_eager(torch_cuda):
