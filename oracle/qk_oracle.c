@@ -19,7 +19,7 @@
 /* Type table.                                                                */
 /* [candle] GgmlDType table: block elements / block bytes                    */
 /*   Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q8_0 32/34, Q4K 256/144,            */
-/*   Q6K 256/210, Q8K 256/292.                                                */
+/*   Q5K 256/176, Q6K 256/210, Q8K 256/292.                                   */
 /* [sipllm] Design, "type_nbytes(t, n) = n / block_size * type_size".        */
 /* ------------------------------------------------------------------------- */
 
@@ -31,6 +31,7 @@ int64_t orc_block_elems(int type) {
     case ORC_Q8_0:
       return 32;
     case ORC_Q4_K:
+    case ORC_Q5_K:
     case ORC_Q6_K:
     case ORC_Q8_K:
       return 256;
@@ -46,6 +47,7 @@ int64_t orc_block_bytes(int type) {
     case ORC_Q5_0: return 22;
     case ORC_Q8_0: return 34;
     case ORC_Q4_K: return 144;
+    case ORC_Q5_K: return 176;
     case ORC_Q6_K: return 210;
     case ORC_Q8_K: return 292;
     default: return 0;
@@ -70,6 +72,7 @@ int orc_act_type(int weight_type) {
     case ORC_Q8_0:
       return ORC_Q8_0;
     case ORC_Q4_K:
+    case ORC_Q5_K:
     case ORC_Q6_K:
       return ORC_Q8_K;
     default:
@@ -392,6 +395,25 @@ static int orc_q4_K_code(const uint8_t* blk, int e) {
   return (p < 32) ? (qs[32 * c + p] & 0x0F) : (qs[32 * c + p - 32] >> 4);
 }
 
+/* Q5_K ([candle] GgmlDType table: 256 elements in 176 bytes; 块结构 prose:
+ * like Q4K it carries an f16 d and dmin and eight 32-element sub-blocks whose
+ * scale and min are 6-bit integers, value d * sc_j * q - dmin * m_j).  176 bytes
+ * leave, after d, dmin, the 12 bytes of eight 6-bit (scale, min) pairs and the
+ * 128 bytes of low nibbles, 32 bytes: one fifth bit per element.  The pages give
+ * neither the field order nor which bit belongs to which element; this takes the
+ * GGUF arrangement (parity unpinned): d f16 @0, dmin f16 @2, scales[12] @4 packed
+ * as Q4_K's, qh[32] @16, qs[128] @48.  Element e, chunk c = e / 64, p = e % 64:
+ * low 4 bits as Q4_K's (qs[32c + p % 32], low nibble for p < 32, else high),
+ * bit 4 = bit (2c + (p >= 32)) of qh[p % 32]. */
+static int orc_q5_K_code(const uint8_t* blk, int e) {
+  const uint8_t* qh = blk + 16;
+  const uint8_t* qs = blk + 48;
+  int c = e / 64, p = e % 64;
+  int low4 = (p < 32) ? (qs[32 * c + p] & 0x0F) : (qs[32 * c + p - 32] >> 4);
+  int bit4 = (qh[p % 32] >> (2 * c + (p >= 32 ? 1 : 0))) & 1;
+  return low4 | (bit4 << 4);
+}
+
 /* Q6_K ([candle] BlockQ6K: ql[128] @0 low 4 bits, qh[64] @128 high 2 bits,
  * scales int8[16] @192, d f16 @208; 16-element sub-block j has value
  * d * sc[j] * (q - 32)).  The pages do not give which ql nibble and which qh
@@ -454,6 +476,17 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
         }
         break;
       }
+      case ORC_Q5_K: { /* as Q4_K with the 5-bit code */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        float dmin = orc_f16_to_f32(orc_get_u16(blk + 2));
+        for (int e = 0; e < 256; ++e) {
+          int sc, m;
+          orc_q4_K_scale_min(blk + 4, e / 32, &sc, &m);
+          int q = orc_q5_K_code(blk, e);
+          y[e] = d * (float)sc * (float)q - dmin * (float)m;
+        }
+        break;
+      }
       case ORC_Q6_K: { /* [candle] BlockQ6K: d * sc[j] * (q - 32) */
         float d = orc_f16_to_f32(orc_get_u16(blk + 208));
         const int8_t* sc = (const int8_t*)(blk + 192);
@@ -481,8 +514,8 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
 /* element as VecDotRef does; only the block scales are float).              */
 /* ------------------------------------------------------------------------- */
 
-/* Integer quantities kept per weight block: one s for Q8_0, Q4_0, Q6_K; the
- * pair (S_q, S_m) for Q4_K (scale sum and min sum). */
+/* Integer quantities kept per weight block: one s for Q8_0, Q4_0, Q5_0, Q6_K;
+ * the pair (S_q, S_m) for Q4_K and Q5_K (scale sum and min sum). */
 int64_t orc_sums_per_block(int weight_type) {
   switch (weight_type) {
     case ORC_Q8_0:
@@ -491,6 +524,7 @@ int64_t orc_sums_per_block(int weight_type) {
     case ORC_Q6_K:
       return 1;
     case ORC_Q4_K:
+    case ORC_Q5_K:
       return 2;
     default:
       return 0;
@@ -518,7 +552,8 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
       out[0] = s;
       return ORC_OK;
     }
-    case ORC_Q4_K: {
+    case ORC_Q4_K:
+    case ORC_Q5_K: {
       /* S_q = sum_j sc_j * (sum_{e in j} q_e a_e);  S_m = sum_j m_j * (sum_{e in j} a_e).
        * [rml]: the sub-block min term is min * sum(a); the reference sums it
        * element by element, the kernels take sum(a) over 32 activations as two
@@ -530,7 +565,8 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
         orc_q4_K_scale_min(wb + 4, j, &sc, &m);
         int32_t s = 0, sa = 0;
         for (int e = 32 * j; e < 32 * j + 32; ++e) {
-          s += (int32_t)orc_q4_K_code(wb, e) * (int32_t)(int8_t)a[e];
+          int q = (wt == ORC_Q4_K) ? orc_q4_K_code(wb, e) : orc_q5_K_code(wb, e);
+          s += (int32_t)q * (int32_t)(int8_t)a[e];
           sa += (int32_t)(int8_t)a[e];
         }
         sq += sc * s;
@@ -564,7 +600,7 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
 
 /* The one float step per block ([rml] "Kernels and references": kernels and
  * references share it).  Q8_0/Q4_0: c = s * (dw * dx) with both f16 scales
- * ([cl] Example 10 step 2).  Q4_K: c = (dx*d) * S_q - (dx*dmin) * S_m.
+ * ([cl] Example 10 step 2).  Q4_K, Q5_K: c = (dx*d) * S_q - (dx*dmin) * S_m.
  * Q6_K: c = (dx*d) * S.  dx of Q8_K is f32 ([candle] BlockQ8K). */
 static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s) {
   switch (wt) {
@@ -575,7 +611,8 @@ static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const
       float dx = orc_f16_to_f32(orc_get_u16(xb));
       return (float)s[0] * (dw * dx);
     }
-    case ORC_Q4_K: {
+    case ORC_Q4_K:
+    case ORC_Q5_K: {
       float dx = orc_get_f32(xb);
       float d = orc_f16_to_f32(orc_get_u16(wb));
       float dmin = orc_f16_to_f32(orc_get_u16(wb + 2));

@@ -24,6 +24,11 @@
  *   rule); the scale rule taken is the Q8_0 one over 256 elements.
  *   Q6_K ql/qh bit arrangement: parity unpinned (the pages give only the field
  *   roles); the GGUF arrangement is assumed.
+ *   Q5_K field order and fifth-bit arrangement: parity unpinned (the pages give
+ *   its size and that it shares Q4K's d, dmin and 6-bit scales and mins); the
+ *   GGUF arrangement is assumed.  With every fifth bit clear it reduces to the
+ *   pinned Q4_K decoder; vec_dot Q5_KxQ8_K is pinned by brute force against its
+ *   dequant definition, as the other K-quants are.
  *   quantize / dequantize Q4_1 and Q5_0, vec_dot Q5_0xQ8_0: pinned by the [cl]
  *   Example 7, 8, 12 and 14 printed values and bytes, plus brute force.  Q4_1
  *   has no dot product here: its activation format (Q8_1) is only named on the
@@ -45,6 +50,7 @@ extern "C" {
 #define ORC_Q5_0 6
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
 #define ORC_Q6_K 14
 #define ORC_Q8_K 15
 

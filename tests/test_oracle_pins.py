@@ -25,7 +25,7 @@ F32 = np.float32
 def test_type_table_matches_printed_geometry():
     # candle "量化格式" GgmlDType table; codeloopback lesson format table.
     ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
-           "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
+           "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
     for name, gid, elems, nbytes, bpw in rows("type_table.txt"):
         t = ids[name]
         assert t == int(gid)
@@ -44,6 +44,7 @@ def test_row_bytes_whole_blocks_no_padding():
     assert o.row_bytes(o.Q4_0, 100) == 0
     assert o.row_bytes(o.Q4_K, 11008) == 43 * 144
     assert o.row_bytes(o.Q6_K, 11008) == 43 * 210
+    assert o.row_bytes(o.Q5_K, 11008) == 43 * 176
     assert o.row_bytes(o.Q4_K, 4096 + 32) == 0
     assert o.row_bytes(99, 256) == 0
 
@@ -54,6 +55,7 @@ def test_pairing_table():
     assert o.act_type(o.Q8_0) == o.Q8_0
     assert o.act_type(o.Q4_K) == o.Q8_K
     assert o.act_type(o.Q6_K) == o.Q8_K
+    assert o.act_type(o.Q5_K) == o.Q8_K
     assert o.act_type(o.Q8_K) == -1
     assert o.act_type(3) == -1
 
@@ -502,6 +504,84 @@ def test_q6_K_structure_invariants():
 
 
 # --------------------------------------------------------------------------
+# Q5_K: the pages give its size and that it shares Q4K's d, dmin and 6-bit
+# (scale, min) pairs; field order and fifth-bit arrangement are not on the pages
+# (parity unpinned).  Pinned: the reduction to the pinned Q4_K decoder when no
+# fifth bit is set, and structure any arrangement of the fifth bits satisfies.
+# --------------------------------------------------------------------------
+
+def _q5k_block(rng):
+    b = rng.integers(0, 256, 176, dtype=np.uint8)
+    b[0:2] = np.frombuffer(np.float16(rng.uniform(0.01, 0.1)).tobytes(), np.uint8)
+    b[2:4] = np.frombuffer(np.float16(rng.uniform(0.01, 0.1)).tobytes(), np.uint8)
+    return b
+
+
+def test_q5_K_without_fifth_bits_is_q4_K():
+    # candle 块结构: Q5K is Q4K's (d, dmin, 6-bit scales and mins, 4-bit low codes)
+    # plus one more bit per code.  With every fifth bit clear, each element must be
+    # the Q4_K element of the block made of the same d, dmin, scales and nibbles.
+    rng = np.random.default_rng(13)
+    for _ in range(20):
+        b = _q5k_block(rng)
+        b[16:48] = 0
+        q4 = np.concatenate([b[0:16], b[48:176]])
+        assert np.array_equal(o.dequantize(o.Q5_K, b, 256), o.dequantize(o.Q4_K, q4, 256))
+
+
+def test_q5_K_each_fifth_bit_is_one_element():
+    # 256 fifth bits for 256 elements: every qh bit controls exactly one element,
+    # every element exactly one bit, and setting it adds 16 to that element's code:
+    # seen through dmin = 0, the value moves from d*sc*q to d*sc*(q + 16).
+    rng = np.random.default_rng(14)
+    b = _q5k_block(rng)
+    b[2:4] = 0  # dmin = 0: the value is d * sc * q, exact in f32
+    b[4:16] = 0x21  # scale 33 in sub-blocks 0-3, 1 in sub-blocks 4-7
+    b[16:48] = 0
+    y0 = o.dequantize(o.Q5_K, b, 256).astype(np.float64)
+    d = float(np.frombuffer(b[0:2].tobytes(), np.float16)[0])
+    owner = {}
+    for k in range(32):
+        for bit in range(8):
+            bb = b.copy()
+            bb[16 + k] |= 1 << bit
+            y1 = o.dequantize(o.Q5_K, bb, 256).astype(np.float64)
+            ch = np.nonzero(y1 != y0)[0]
+            assert len(ch) == 1, (k, bit)
+            e = int(ch[0])
+            assert e not in owner
+            owner[e] = (k, bit)
+            sc = 33 if e < 128 else 1
+            assert y1[e] - y0[e] == d * sc * 16
+    assert len(owner) == 256
+    # fifth bits of consecutive elements of one 32-element sub-block share a bit
+    # position and run over consecutive qh bytes (the Q4_K nibble order, one bit plane
+    # per sub-block)
+    for j in range(8):
+        bits = {owner[e][1] for e in range(32 * j, 32 * j + 32)}
+        assert len(bits) == 1
+        assert [owner[e][0] for e in range(32 * j, 32 * j + 32)] == list(range(32))
+
+
+def test_q5_K_codes_span_0_to_31():
+    # A 5-bit code: with d = 1, dmin = 0 and every scale 1, the values are the codes,
+    # all of 0..31 reachable; all-ones low nibbles and fifth bits give 31.
+    b = np.zeros(176, dtype=np.uint8)
+    b[0:2] = np.frombuffer(np.float16(1.0).tobytes(), np.uint8)
+    b[4:8] = 1
+    b[12:16] = 1
+    b[16:48] = 0xFF
+    b[48:176] = 0xFF
+    assert np.array_equal(o.dequantize(o.Q5_K, b, 256), np.full(256, 31, np.float32))
+    rng = np.random.default_rng(15)
+    b[16:48] = rng.integers(0, 256, 32)
+    b[48:176] = rng.integers(0, 256, 128)
+    y = o.dequantize(o.Q5_K, b, 256)
+    assert np.all(y == np.round(y)) and y.min() >= 0 and y.max() <= 31
+    assert len(set(y.tolist())) > 24
+
+
+# --------------------------------------------------------------------------
 # VecDot: brute force against the dequantized values, and the seeded examples
 # --------------------------------------------------------------------------
 
@@ -511,7 +591,7 @@ def _random_weights(t, nblocks, rng):
     h = lambda lo, hi: np.frombuffer(rng.uniform(lo, hi, nblocks).astype(np.float16).tobytes(), np.uint8).reshape(nblocks, 2)
     if t in (o.Q8_0, o.Q4_0, o.Q5_0):
         w[:, 0:2] = h(0.001, 0.05)
-    elif t == o.Q4_K:
+    elif t in (o.Q4_K, o.Q5_K):
         w[:, 0:2] = h(1e-3, 1e-2)
         w[:, 2:4] = h(1e-3, 1e-2)
     elif t == o.Q6_K:
@@ -531,7 +611,7 @@ def _act_parts(at, xq, n):
     return np.repeat(d, 256), blk[:, 4:260].view(np.int8).astype(np.int64).reshape(-1)
 
 
-@pytest.mark.parametrize("t", [o.Q8_0, o.Q4_0, o.Q5_0, o.Q4_K, o.Q6_K])
+@pytest.mark.parametrize("t", [o.Q8_0, o.Q4_0, o.Q5_0, o.Q4_K, o.Q5_K, o.Q6_K])
 def test_vec_dot_brute_force(t):
     rng = np.random.default_rng(100 + t)
     at = o.act_type(t)
@@ -550,14 +630,14 @@ def test_vec_dot_brute_force(t):
         f16 = lambda a, off: a[:, off:off + 2].copy().view(np.float16).astype(np.float64)[:, 0]
         if t in (o.Q8_0, o.Q4_0, o.Q5_0):
             exact = np.sum(sums[:, 0] * f16(wb, 0) * dx[::32])
-        elif t == o.Q4_K:
+        elif t in (o.Q4_K, o.Q5_K):
             exact = np.sum(dx[::256] * (f16(wb, 0) * sums[:, 0] - f16(wb, 2) * sums[:, 1]))
         else:
             exact = np.sum(dx[::256] * f16(wb, 208) * sums[:, 0])
         scale = np.abs(terms).sum()
-        # Q8_0, Q4_0, Q5_0, Q6_K decoded values are exact in f32; Q4_K's d*sc*q - dmin*m
-        # rounds once per element.
-        tol = 1e-12 if t != o.Q4_K else 1e-7
+        # Q8_0, Q4_0, Q5_0, Q6_K decoded values are exact in f32; the K-quants with a
+        # min (d*sc*q - dmin*m) round once per element.
+        tol = 1e-12 if t not in (o.Q4_K, o.Q5_K) else 1e-7
         assert abs(exact - brute) <= tol * scale, (t, n, exact, brute)
         y, l1 = o.vec_dot(t, w, xq, n)
         nbk = n // o.block_elems(t)
@@ -661,7 +741,7 @@ def test_gemv_is_vec_dot_per_row_and_column():
     # sipllm matmul_quant: y[o] = VecDot(row o, x) for each output row; every
     # activation column is independent.
     rng = np.random.default_rng(21)
-    for t in (o.Q8_0, o.Q4_0, o.Q4_K, o.Q6_K):
+    for t in (o.Q8_0, o.Q4_0, o.Q4_K, o.Q5_K, o.Q6_K):
         n_out, n_in, ncols = 5, 512, 3
         W = _random_weights(t, n_out * n_in // o.block_elems(t), rng)
         X = rng.standard_normal((ncols, n_in)).astype(np.float32)
