@@ -64,11 +64,13 @@ def log(*a):
 
 def workloads(qk):
     T4K, T6K, T40, T80 = qk.QK_TYPE_Q4_K, qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q8_0
-    T50 = qk.QK_TYPE_Q5_0
+    T50, T5K = qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_K
     T8K = qk.QK_TYPE_Q8_K
     return {
         "q4_K_decode_4096x11008": {
             "gemvs": [("W", T4K, 4096, 11008, "x")], "acts": {"x": (T8K, 11008, 1)}},
+        "q5_K_decode_4096x11008": {
+            "gemvs": [("W", T5K, 4096, 11008, "x")], "acts": {"x": (T8K, 11008, 1)}},
         "q4_K_4096x4096": {
             "gemvs": [("W_q4_K", T4K, 4096, 4096, "x")], "acts": {"x": (T8K, 4096, 1)}},
         "q4_0_4096x4096": {
@@ -107,6 +109,8 @@ def host_inputs(name, qk):
     from quantized_gemv_quantize_amd import synth
     if name == "q4_K_decode_4096x11008":
         return synth.q4_K_decode_4096x11008()
+    if name == "q5_K_decode_4096x11008":
+        return synth.q5_K_decode_4096x11008()
     if name in ("q4_K_4096x4096", "q4_0_4096x4096"):
         return synth.q4_gemv_4096x4096()
     if name in ("ffn_7b_q4_K_q6_K", "ffn_7b_swiglu"):
@@ -140,7 +144,7 @@ def gpu_copy_like(torch, w_type, n_out, n_in, gen):
         v = torch.rand((n_out, nb), device="cuda", generator=gen, dtype=torch.float64) * (hi - lo) + lo
         return v.to(torch.float16).view(torch.uint8).reshape(n_out, nb, 2)
 
-    if w_type == synth.Q4_K:
+    if w_type in (synth.Q4_K, synth.Q5_K):
         w[:, :, 0:2] = f16(1e-4, 1e-3)
         w[:, :, 2:4] = f16(1e-4, 1e-3)
     elif w_type == synth.Q6_K:

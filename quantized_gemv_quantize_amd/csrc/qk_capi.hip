@@ -13,7 +13,7 @@ namespace {
 // Weight formats with a GEMV (a paired activation type).
 bool is_weight(int t) {
   return t == QK_TYPE_Q4_0 || t == QK_TYPE_Q5_0 || t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_K ||
-         t == QK_TYPE_Q6_K;
+         t == QK_TYPE_Q5_K || t == QK_TYPE_Q6_K;
 }
 // Weight formats qk_dequantize_row expands.
 bool is_dequant(int t) { return is_weight(t) || t == QK_TYPE_Q4_1; }
@@ -53,7 +53,7 @@ int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void
   const int at = qk_act_type(w_type);
   const int64_t xrow = qk_row_bytes(at, n_in);
   const int64_t nb = n_in / qk_block_elems(w_type);
-  const int k = (w_type == QK_TYPE_Q4_K) ? 2 : 1;
+  const int k = (w_type == QK_TYPE_Q4_K || w_type == QK_TYPE_Q5_K) ? 2 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_type == QK_TYPE_Q4_K && ncols > 1) {
     // several columns: one pass over W per group of up to 64 columns (matrix cores)
@@ -94,6 +94,7 @@ int64_t qk_block_elems(int type) {
     case QK_TYPE_Q5_0:
     case QK_TYPE_Q8_0: return 32;
     case QK_TYPE_Q4_K:
+    case QK_TYPE_Q5_K:
     case QK_TYPE_Q6_K:
     case QK_TYPE_Q8_K: return 256;
     default: return 0;
@@ -107,6 +108,7 @@ int64_t qk_block_bytes(int type) {
     case QK_TYPE_Q5_0: return 22;
     case QK_TYPE_Q8_0: return 34;
     case QK_TYPE_Q4_K: return 144;
+    case QK_TYPE_Q5_K: return 176;
     case QK_TYPE_Q6_K: return 210;
     case QK_TYPE_Q8_K: return 292;
     default: return 0;
@@ -125,6 +127,7 @@ int qk_act_type(int weight_type) {
     case QK_TYPE_Q5_0:
     case QK_TYPE_Q8_0: return QK_TYPE_Q8_0;
     case QK_TYPE_Q4_K:
+    case QK_TYPE_Q5_K:
     case QK_TYPE_Q6_K: return QK_TYPE_Q8_K;
     default: return -1;
   }

@@ -8,6 +8,8 @@
 //   Q5_0  d * (q - 16), low nibbles as Q4_0, bit 4 from qh (codeloopback Example 8)
 //   Q4_K  d * sc_j * q - dmin * m_j for 32-element sub-block j (scales per
 //         get_scale_min_k4, rml element-200 trace)
+//   Q5_K  the same with a 5-bit q: element 64c + p takes bit 2c + (p >= 32) of
+//         qh[p % 32] as bit 4 (GGUF arrangement; the pages give the field roles)
 //   Q6_K  d * sc_j * (q - 32) for 16-element sub-block j; q = 4 bits from ql and
 //         2 bits from qh in the GGUF arrangement (the pages give only the roles)
 // Each product is exact in f32 (at most 23 significant bits), so the order of
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(256) void dequant_q5_0_kernel(const uint8_t* __rest
   *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(lo | fifth, d, 16);
 }
 
-// Q4_K and Q6_K: one wavefront per kSB consecutive superblocks, lane l -> elements
+// Q4_K, Q5_K and Q6_K: one wavefront per kSB consecutive superblocks, lane l -> elements
 // 4l..4l+3 of each; every load of the kSB superblocks is issued before the first
 // store, and fewer, longer wavefronts keep the dispatcher out of the way.
 constexpr int kSB = 4;
@@ -115,8 +117,11 @@ constexpr int kSB = 4;
 struct Q4KPart {
   uint4 h;      // d, dmin, scales[12]
   uint32_t w;   // the 4 qs bytes holding this lane's 4 nibbles
+  uint32_t qh;  // Q5_K: the 4 qh bytes holding this lane's fifth bits
 };
 
+// Q5 selects Q5_K (176-byte superblocks: qh[32] at byte 16, qs at byte 48).
+template <int Q5>
 __global__ __launch_bounds__(256) void dequant_q4_K_kernel(const uint8_t* __restrict__ src,
                                                            float* __restrict__ dst,
                                                            int64_t nblocks) {
@@ -127,12 +132,14 @@ __global__ __launch_bounds__(256) void dequant_q4_K_kernel(const uint8_t* __rest
   const int j = e0 >> 5;   // sub-block
   const int c = e0 >> 6;   // 64-element chunk
   const int p = e0 & 63;   // position in the chunk
+  constexpr int kBytes = Q5 ? kQ5_KBytes : kQ4_KBytes, kQs = Q5 ? 48 : 16;
   Q4KPart v[kSB];
 #pragma unroll
   for (int k = 0; k < kSB; ++k) {
-    const uint8_t* blk = src + min(b0 + k, nblocks - 1) * kQ4_KBytes;
+    const uint8_t* blk = src + min(b0 + k, nblocks - 1) * kBytes;
     v[k].h = *reinterpret_cast<const uint4*>(blk);
-    v[k].w = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * c + (p & 31));
+    v[k].w = *reinterpret_cast<const uint32_t*>(blk + kQs + 32 * c + (p & 31));
+    v[k].qh = Q5 ? *reinterpret_cast<const uint32_t*>(blk + 16 + (p & 31)) : 0u;
   }
 #pragma unroll
   for (int k = 0; k < kSB; ++k) {
@@ -148,7 +155,8 @@ __global__ __launch_bounds__(256) void dequant_q4_K_kernel(const uint8_t* __rest
     const int sh = 8 * (j & 3);
     const float sc = static_cast<float>((scw >> sh) & 0xFF);
     const float mn = static_cast<float>((mw >> sh) & 0xFF);
-    const uint32_t q = (p < 32) ? (v[k].w & kLo4) : ((v[k].w >> 4) & kLo4);
+    uint32_t q = (p < 32) ? (v[k].w & kLo4) : ((v[k].w >> 4) & kLo4);
+    if constexpr (Q5 != 0) q |= ((v[k].qh >> (2 * c + (p >= 32 ? 1 : 0))) & 0x01010101u) << 4;
     const float dsc = d * sc;
     const float dm = dmin * mn;
     float4 o;
@@ -212,7 +220,8 @@ hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t n
     case kQ4_0: dequant_q4_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ4_1: dequant_q4_1_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ5_0: dequant_q5_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
-    case kQ4_K: dequant_q4_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ4_K: dequant_q4_K_kernel<0><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ5_K: dequant_q4_K_kernel<1><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ6_K: dequant_q6_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     default:
       return hipErrorInvalidValue;

@@ -6,6 +6,9 @@
 //   Q4_1  20 B: d f16 @0, m f16 @2, qs u8[16] @4 (nibbles as Q4_0)
 //   Q5_0  22 B: d f16 @0, qh u32 @2 (bit e: bit 4 of element e), qs u8[16] @6
 //   Q4_K 144 B: d f16 @0, dmin f16 @2, scales u8[12] @4, qs u8[128] @16
+//   Q5_K 176 B: d f16 @0, dmin f16 @2, scales u8[12] @4 (as Q4_K), qh u8[32] @16,
+//               qs u8[128] @48 (the pages give the size and field roles; the
+//               order and bit arrangement are GGUF's)
 //   Q6_K 210 B: ql u8[128] @0, qh u8[64] @128, scales int8[16] @192, d f16 @208
 //   Q8_K 292 B: d f32 @0, qs int8[256] @4, bsums int16[16] @260
 #pragma once
@@ -20,6 +23,7 @@ constexpr int kQ4_0Bytes = 18;
 constexpr int kQ4_1Bytes = 20;
 constexpr int kQ5_0Bytes = 22;
 constexpr int kQ4_KBytes = 144;
+constexpr int kQ5_KBytes = 176;
 constexpr int kQ6_KBytes = 210;
 constexpr int kQ8_KBytes = 292;
 

@@ -8,14 +8,15 @@
 // block step uses floats:
 //   Q8_0, Q4_0, Q5_0  c = s * (d_w * d_x)  (Q5_0: codeloopback Example 8's 5-bit
 //               codes, bit 4 from qh, paired with Q8_0 per candle's VecDotType)
-//   Q4_K        c = (d_x * d) * S_q - (d_x * dmin) * S_m,
+//   Q4_K, Q5_K  c = (d_x * d) * S_q - (d_x * dmin) * S_m,
 //               S_q = sum_j sc_j s_j, S_m = sum_j m_j (bsum_2j + bsum_2j+1)
+//               (Q5_K: the same with 5-bit codes, bit 4 from qh)
 //   Q6_K        c = (d_x * d) * S,  S = sum_j sc_j sum_e (q_e - 32) a_e
 // y[row] is the f32 sum of c over the row's blocks.
 //
 // Mapping on the GPU (all kernels):
 //  - one wavefront per output row; its lanes cover a span of consecutive blocks
-//    (Q4_K, Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
+//    (Q4_K, Q5_K, Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
 //    Q8_0, Q4_0, Q5_0: 1 lane per 32-element block, 64 blocks per pass);
 //  - rows of one or two passes keep the activation blocks a lane needs in
 //    registers, loaded once per wavefront and reused over grid-strided rows;
@@ -177,10 +178,28 @@ __device__ __forceinline__ T load_a4(const uint8_t* p) {  // 4-byte aligned fiel
   return v;
 }
 
+// S_q and S_m partials of chunk c (sub-blocks 2c, 2c+1) from its two sub-block
+// code sums slo, shi and activation sums asum: get_scale_min_k4 for all four
+// sub-blocks of a group at once: sub-blocks 0-3 take the low 6 bits of scale bytes
+// 0-3 / 4-7; sub-blocks 4-7 take the low / high nibble of bytes 8-11 and the top 2
+// bits of bytes 0-3 / 4-7.  hi_mask is all ones for chunks 2 and 3 (sub-blocks
+// 4-7), zero otherwise, so the scale words are selected with bit operations
+// instead of a divergent branch; sh = 16 (c & 1) picks the byte pair.
+__device__ __forceinline__ int2 q4K_scale_mins(int slo, int shi, const uint4& h, int2 asum,
+                                               uint32_t hi_mask, int sh) {
+  const uint32_t sc_a = h.y & 0x3F3F3F3Fu;
+  const uint32_t m_a = h.z & 0x3F3F3F3Fu;
+  const uint32_t sc_b = (h.w & kLo4) | ((h.y >> 2) & kHi2);
+  const uint32_t m_b = ((h.w >> 4) & kLo4) | ((h.z >> 2) & kHi2);
+  const uint32_t scw = (sc_b & hi_mask) | (sc_a & ~hi_mask);
+  const uint32_t mw = (m_b & hi_mask) | (m_a & ~hi_mask);
+  const int sc_lo = __builtin_amdgcn_ubfe(scw, sh, 8), sc_hi = __builtin_amdgcn_ubfe(scw, sh + 8, 8);
+  const int m_lo = __builtin_amdgcn_ubfe(mw, sh, 8), m_hi = __builtin_amdgcn_ubfe(mw, sh + 8, 8);
+  return make_int2(mad24(sc_lo, slo, __mul24(sc_hi, shi)), mad24(m_lo, asum.x, __mul24(m_hi, asum.y)));
+}
+
 // Exact integer part of one Q4_K superblock for chunk c (sub-blocks 2c, 2c+1):
 // returns this lane's S_q and S_m partial sums (before the quad reduction).
-// hi_mask is all ones for chunks 2 and 3 (sub-blocks 4-7), zero otherwise, so the
-// scale words are selected with bit operations instead of a divergent branch.
 __device__ __forceinline__ int2 q4K_chunk(const uint4& q0, const uint4& q1, const uint4& h,
                                           const uint4& a0, const uint4& a1, const uint4& a2,
                                           const uint4& a3, int2 asum, uint32_t hi_mask, int sh) {
@@ -201,19 +220,33 @@ __device__ __forceinline__ int2 q4K_chunk(const uint4& q0, const uint4& q1, cons
   shi = dot4((q1.y >> 4) & kLo4, a3.y, shi);
   shi = dot4((q1.z >> 4) & kLo4, a3.z, shi);
   shi = dot4((q1.w >> 4) & kLo4, a3.w, shi);
-  // get_scale_min_k4 for all four sub-blocks of a group at once: sub-blocks 0-3
-  // take the low 6 bits of scale bytes 0-3 / 4-7; sub-blocks 4-7 take the low /
-  // high nibble of bytes 8-11 and the top 2 bits of bytes 0-3 / 4-7.
-  const uint32_t sc_a = h.y & 0x3F3F3F3Fu;
-  const uint32_t m_a = h.z & 0x3F3F3F3Fu;
-  const uint32_t sc_b = (h.w & kLo4) | ((h.y >> 2) & kHi2);
-  const uint32_t m_b = ((h.w >> 4) & kLo4) | ((h.z >> 2) & kHi2);
-  const uint32_t scw = (sc_b & hi_mask) | (sc_a & ~hi_mask);
-  const uint32_t mw = (m_b & hi_mask) | (m_a & ~hi_mask);
-  const int sc_lo = __builtin_amdgcn_ubfe(scw, sh, 8), sc_hi = __builtin_amdgcn_ubfe(scw, sh + 8, 8);
-  const int m_lo = __builtin_amdgcn_ubfe(mw, sh, 8), m_hi = __builtin_amdgcn_ubfe(mw, sh + 8, 8);
-  return make_int2(mad24(sc_lo, slo, __mul24(sc_hi, shi)), mad24(m_lo, asum.x, __mul24(m_hi, asum.y)));
+  return q4K_scale_mins(slo, shi, h, asum, hi_mask, sh);
 }
+
+// Q5_K chunk c: the Q4_K nibbles plus, for element 64c + p, bit 2c (p < 32) or
+// 2c + 1 (p >= 32) of qh byte p % 32 as bit 4.  qh0 / qh1 are qh bytes 0-15 /
+// 16-31, already shifted right by 2c, so bits 0 and 1 of each byte are this
+// chunk's two fifth bits.  Codes stay below 32, so the signed dot is exact.
+__device__ __forceinline__ int2 q5K_chunk(const uint4& q0, const uint4& q1, const uint4& qh0,
+                                          const uint4& qh1, const uint4& h, const uint4& a0,
+                                          const uint4& a1, const uint4& a2, const uint4& a3,
+                                          int2 asum, uint32_t hi_mask, int sh) {
+  const uint32_t ql[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const uint32_t qh[8] = {qh0.x, qh0.y, qh0.z, qh0.w, qh1.x, qh1.y, qh1.z, qh1.w};
+  const uint32_t al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const uint32_t ah[8] = {a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+  int slo = 0, shi = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t lo = (ql[k] & kLo4) | ((qh[k] & kOnes) << 4);
+    const uint32_t hi = ((ql[k] >> 4) & kLo4) | ((qh[k] & (kOnes << 1)) << 3);
+    slo = dot4(lo, al[k], slo);
+    shi = dot4(hi, ah[k], shi);
+  }
+  return q4K_scale_mins(slo, shi, h, asum, hi_mask, sh);
+}
+
+
 
 // Image staging of a Q8_K activation row: the row's bytes are copied to LDS
 // unchanged (16-byte chunks: one dwordx4 load and one ds_write_b128 each), so the
@@ -273,8 +306,20 @@ __device__ __forceinline__ T lds_a4(const uint8_t* p) {  // 4-byte aligned LDS f
 // ---------------------------------------------------------------------------
 // Q4_K x Q8_K.  Lane (u = lane >> 2, c = lane & 3) of pass `it` handles 64-element
 // chunk c of superblock it*16 + u: qs[32c .. 32c+31] hold sub-block 2c in their low
-// nibbles and sub-block 2c+1 in their high nibbles.
-template <int NW, int UNR, bool SUMS>
+// nibbles and sub-block 2c+1 in their high nibbles.  Q5 selects Q5_K: 176-byte
+// superblocks whose qs start at byte 48, and every lane also loads the 32 qh bytes
+// (bytes 16-47) for the fifth bits of its chunk.
+template <int Q5>
+struct KQuant4 {
+  static constexpr int kBytes = Q5 ? kQ5_KBytes : kQ4_KBytes;
+  static constexpr int kQs = Q5 ? 48 : 16;
+};
+
+__device__ __forceinline__ uint4 shr4(const uint4& v, int n) {
+  return make_uint4(v.x >> n, v.y >> n, v.z >> n, v.w >> n);
+}
+
+template <int NW, int UNR, bool SUMS, int Q5 = 0>
 __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
@@ -283,21 +328,26 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
   const int row = blockIdx.x * NW + wave_id();
   const int c = lane & 3, u = lane >> 2;
   const bool row_ok = row < n_out;
-  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+  using F = KQuant4<Q5>;
+  const size_t rb = static_cast<size_t>(nb) * F::kBytes;
   const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
   const int passes = (nb + 15) >> 4;
 
-  uint4 H[UNR], Q0[UNR], Q1[UNR];
+  uint4 H[UNR], Q0[UNR], Q1[UNR], QH0[Q5 ? UNR : 1], QH1[Q5 ? UNR : 1];
   // Unconditional loads (superblock index clamped): the same number of loads in
   // every lane lets the compiler wait for pass j's data only.
   auto issue = [&](int p0) {
 #pragma unroll
     for (int j = 0; j < UNR; ++j) {
       const int sb = min((p0 + j) * 16 + u, nb - 1);
-      const uint8_t* p = wrow + static_cast<uint32_t>(sb * kQ4_KBytes);
+      const uint8_t* p = wrow + static_cast<uint32_t>(sb * F::kBytes);
       H[j] = *reinterpret_cast<const uint4*>(p);
-      Q0[j] = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
-      Q1[j] = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
+      Q0[j] = *reinterpret_cast<const uint4*>(p + F::kQs + 32 * c);
+      Q1[j] = *reinterpret_cast<const uint4*>(p + F::kQs + 16 + 32 * c);
+      if constexpr (Q5 != 0) {
+        QH0[j] = *reinterpret_cast<const uint4*>(p + 16);
+        QH1[j] = *reinterpret_cast<const uint4*>(p + 32);
+      }
     }
   };
   ImageQ8K st;
@@ -328,7 +378,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
       const int2 asum = make_int2(sext16_lo(bsw.x) + sext16_hi(bsw.x), sext16_lo(bsw.y) + sext16_hi(bsw.y));
       const float dx = lds_a4<float>(blk);
       const uint4 h = H[j];
-      const int2 part = q4K_chunk(Q0[j], Q1[j], h, a0, a1, a2, a3, asum, hi_mask, sh);
+      int2 part;
+      if constexpr (Q5 != 0) {
+        part = q5K_chunk(Q0[j], Q1[j], shr4(QH0[j], 2 * c), shr4(QH1[j], 2 * c), h, a0, a1, a2, a3, asum,
+                         hi_mask, sh);
+      } else {
+        part = q4K_chunk(Q0[j], Q1[j], h, a0, a1, a2, a3, asum, hi_mask, sh);
+      }
       const int sq = quad_sum(part.x);
       const int sm = quad_sum(part.y);
       const float cb = (dx * f16_to_f32(h.x & 0xFFFF)) * static_cast<float>(sq) -
@@ -604,7 +660,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_0_kernel(
 // activation codes, sums and scale of the blocks it covers in every pass of a
 // row, then the wavefront walks its rows (RPW at a time, strided by the grid)
 // reusing those registers: no LDS, no workgroup barrier.
-template <int NW, int NP, int RPW, bool SUMS>
+template <int NW, int NP, int RPW, bool SUMS, int Q5 = 0>
 __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
     const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
     float* __restrict__ y, int32_t* __restrict__ sums) {
@@ -614,7 +670,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
   const int sh = (c & 1) * 16;
   const int wave = blockIdx.x * NW + wave_id();
   const int nwaves = gridDim.x * NW;
-  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+  using F = KQuant4<Q5>;
+  const size_t rb = static_cast<size_t>(nb) * F::kBytes;
 
   uint4 A[NP][4];
   int2 S2[NP];
@@ -630,16 +687,20 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
   }
 
   for (int r0 = wave * RPW; r0 < n_out; r0 += nwaves * RPW) {
-    uint4 H[RPW][NP], Q0[RPW][NP], Q1[RPW][NP];
+    uint4 H[RPW][NP], Q0[RPW][NP], Q1[RPW][NP], QH0[RPW][Q5 ? NP : 1], QH1[RPW][Q5 ? NP : 1];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const uint8_t* wrow = W + static_cast<size_t>(min(r0 + r, n_out - 1)) * rb;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ4_KBytes);
+        const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * F::kBytes);
         H[r][p] = *reinterpret_cast<const uint4*>(q);
-        Q0[r][p] = *reinterpret_cast<const uint4*>(q + 16 + 32 * c);
-        Q1[r][p] = *reinterpret_cast<const uint4*>(q + 32 + 32 * c);
+        Q0[r][p] = *reinterpret_cast<const uint4*>(q + F::kQs + 32 * c);
+        Q1[r][p] = *reinterpret_cast<const uint4*>(q + F::kQs + 16 + 32 * c);
+        if constexpr (Q5 != 0) {
+          QH0[r][p] = *reinterpret_cast<const uint4*>(q + 16);
+          QH1[r][p] = *reinterpret_cast<const uint4*>(q + 32);
+        }
       }
     }
 #pragma unroll
@@ -651,8 +712,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
       for (int p = 0; p < NP; ++p) {
         const int sb = p * 16 + u;
         if (sb >= nb) continue;  // uniform over the 4 lanes of a superblock
-        const int2 part = q4K_chunk(Q0[r][p], Q1[r][p], H[r][p], A[p][0], A[p][1], A[p][2], A[p][3],
-                                    S2[p], hi_mask, sh);
+        int2 part;
+        if constexpr (Q5 != 0) {
+          part = q5K_chunk(Q0[r][p], Q1[r][p], shr4(QH0[r][p], 2 * c), shr4(QH1[r][p], 2 * c), H[r][p],
+                           A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask, sh);
+        } else {
+          part = q4K_chunk(Q0[r][p], Q1[r][p], H[r][p], A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask,
+                           sh);
+        }
         const int sq = quad_sum(part.x);
         const int sm = quad_sum(part.y);
         const uint32_t dd = H[r][p].x;
@@ -1051,6 +1118,7 @@ hipError_t launch_rows(K kernel, int64_t n_out, int rpw, int max_waves, hipStrea
 int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
   switch (w_type) {
     case kQ4_K:
+    case kQ5_K:
     case kQ6_K: return align16(n_in / 256 * kQ8_KBytes);
     case kQ8_0:
     case kQ4_0:
@@ -1081,6 +1149,14 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
       if (passes == 2) return S ? QK_ROWS((gemv_q4_K_reg<4, 2, 1, true>)) : QK_ROWS((gemv_q4_K_reg<4, 2, 1, false>));
       if (passes == 3) return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 3, true>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 3, false>));
       return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 4, true>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 4, false>));
+    }
+    case kQ5_K: {
+      const int nb = static_cast<int>(n_in / 256);
+      const int passes = (nb + 15) / 16;
+      if (passes == 1) return S ? QK_ROWS((gemv_q4_K_reg<4, 1, 1, true, 1>)) : QK_ROWS((gemv_q4_K_reg<4, 1, 1, false, 1>));
+      if (passes == 2) return S ? QK_ROWS((gemv_q4_K_reg<4, 2, 1, true, 1>)) : QK_ROWS((gemv_q4_K_reg<4, 2, 1, false, 1>));
+      if (passes == 3) return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 3, true, 1>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 3, false, 1>));
+      return S ? QK_LDS((gemv_q4_K_kernel<kWaves, 4, true, 1>)) : QK_LDS((gemv_q4_K_kernel<kWaves, 4, false, 1>));
     }
     case kQ6_K: {
       const int nb = static_cast<int>(n_in / 256);

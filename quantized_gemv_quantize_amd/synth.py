@@ -7,14 +7,15 @@ and to the HIP library; the benchmark uses them for its weight copies.
 
 Recipes (one numpy default_rng(seed) per workload, drawn in the order listed):
   f16 fields "U[a, b]": f64 uniform draw, rounded to f16 (numpy, RNE).
-  "uniform bytes": every byte iid U{0..255}, so Q4_K's 6-bit scales/mins and the
-  nibbles are uniform; Q6_K scales int8 U{-64..63} inclusive.
+  "uniform bytes": every byte iid U{0..255}, so Q4_K's and Q5_K's 6-bit
+  scales/mins, nibbles and fifth bits are uniform; Q6_K scales int8 U{-64..63}
+  inclusive.
 """
 import numpy as np
 
-Q4_0, Q4_1, Q5_0, Q8_0, Q4_K, Q6_K, Q8_K = 2, 3, 6, 8, 12, 14, 15
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q8_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q8_K: 292}
+Q4_0, Q4_1, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 8, 12, 13, 14, 15
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q8_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q8_K: 292}
 
 
 def uniform_bytes(rng, shape):
@@ -69,6 +70,15 @@ def q4_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
     return b.reshape(n_out, nb * 144)
 
 
+def q5_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
+    """Q5_K rows: f16 d, dmin ~ U[d_range]; 12 scale, 32 qh and 128 qs bytes uniform."""
+    nb = n_in // 256
+    b = uniform_bytes(rng, (n_out, nb, 176))
+    b[:, :, 0:2] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    b[:, :, 2:4] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 176)
+
+
 def q6_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
     """Q6_K rows: ql/qh bytes uniform, int8 scales ~ U{-64..63}, f16 d ~ U[d_range]."""
     nb = n_in // 256
@@ -80,7 +90,7 @@ def q6_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
 
 def weight_blocks(rng, t, n_out, n_in):
     return {Q4_0: q4_0_blocks, Q4_1: q4_1_blocks, Q5_0: q5_0_blocks, Q4_K: q4_K_blocks,
-            Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
+            Q5_K: q5_K_blocks, Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
 
 
 def gaussian(rng, shape, std=1.0):
@@ -144,6 +154,12 @@ def q4_K_decode_4096x11008(seed=5):
     """Q4_K decode GEMV, 4096 rows x 11008 columns (43 superblocks per row); x[11008]."""
     rng = np.random.default_rng(seed)
     return {"W": q4_K_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
+
+
+def q5_K_decode_4096x11008(seed=8):
+    """Q5_K decode GEMV, 4096 rows x 11008 columns (43 superblocks per row); x[11008]."""
+    rng = np.random.default_rng(seed)
+    return {"W": q5_K_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
 
 
 def random_copies(t, n_out, n_in, count, seed):

@@ -67,7 +67,7 @@ std::vector<uint8_t> weights(int type, int64_t n_out, int64_t n_in) {
   for (auto& b : w) b = static_cast<uint8_t>(next_u64() >> 56);
   for (int64_t i = 0; i < nb; ++i) {
     uint8_t* blk = w.data() + i * bb;
-    if (type == QK_TYPE_Q4_K) {
+    if (type == QK_TYPE_Q4_K || type == QK_TYPE_Q5_K) {
       put_f16(blk, 1e-4, 1e-3);
       put_f16(blk + 2, 1e-4, 1e-3);
     } else if (type == QK_TYPE_Q6_K) {
@@ -189,7 +189,7 @@ int main() {
     std::printf("no GPU visible\n");
     return 2;
   }
-  const int types[] = {QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_K, QK_TYPE_Q6_K};
+  const int types[] = {QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_K, QK_TYPE_Q5_K, QK_TYPE_Q6_K};
   for (int t : types) {
     // one column (GEMV kernels) and three (Q4_K: the matrix-core path), ragged rows,
     // rows of two passes and of three (the LDS-staged kernels)
@@ -205,6 +205,6 @@ int main() {
     return 1;
   }
   std::printf("abi_check ok: quantize_act, gemv, gemv_block_sums, dequantize_row for Q8_0, Q4_0, Q5_0, "
-              "Q4_K, Q6_K and quantize_row for Q8_0, Q4_0, Q4_1, Q5_0 match the oracle\n");
+              "Q4_K, Q5_K, Q6_K and quantize_row for Q8_0, Q4_0, Q4_1, Q5_0 match the oracle\n");
   return 0;
 }

@@ -59,8 +59,8 @@ def test_library_is_built_for_gfx950_only():
 
 def test_geometry_matches_type_table():
     ids = {"Q4_0": qk.QK_TYPE_Q4_0, "Q4_1": qk.QK_TYPE_Q4_1, "Q5_0": qk.QK_TYPE_Q5_0,
-           "Q8_0": qk.QK_TYPE_Q8_0, "Q4_K": qk.QK_TYPE_Q4_K, "Q6_K": qk.QK_TYPE_Q6_K,
-           "Q8_K": qk.QK_TYPE_Q8_K}
+           "Q8_0": qk.QK_TYPE_Q8_0, "Q4_K": qk.QK_TYPE_Q4_K, "Q5_K": qk.QK_TYPE_Q5_K,
+           "Q6_K": qk.QK_TYPE_Q6_K, "Q8_K": qk.QK_TYPE_Q8_K}
     for name, gid, elems, nbytes, _ in rows("type_table.txt"):
         assert ids[name] == int(gid)
         assert qk.qk_block_elems(ids[name]) == int(elems)
@@ -68,6 +68,7 @@ def test_geometry_matches_type_table():
     assert qk.qk_row_bytes(qk.QK_TYPE_Q8_0, 4096) == 4352
     assert qk.qk_row_bytes(qk.QK_TYPE_Q4_K, 11008) == 6192
     assert qk.qk_row_bytes(qk.QK_TYPE_Q6_K, 11008) == 9030
+    assert qk.qk_row_bytes(qk.QK_TYPE_Q5_K, 11008) == 7568
     assert qk.qk_row_bytes(qk.QK_TYPE_Q4_0, 100) == 0
     assert qk.qk_row_bytes(99, 256) == 0
     assert qk.qk_row_bytes(qk.QK_TYPE_Q5_0, 4096) == 2816
@@ -80,6 +81,7 @@ def test_pairing():
     assert qk.qk_act_type(qk.QK_TYPE_Q8_0) == qk.QK_TYPE_Q8_0
     assert qk.qk_act_type(qk.QK_TYPE_Q4_K) == qk.QK_TYPE_Q8_K
     assert qk.qk_act_type(qk.QK_TYPE_Q6_K) == qk.QK_TYPE_Q8_K
+    assert qk.qk_act_type(qk.QK_TYPE_Q5_K) == qk.QK_TYPE_Q8_K
     assert qk.qk_act_type(qk.QK_TYPE_Q5_0) == qk.QK_TYPE_Q8_0
     assert qk.qk_act_type(qk.QK_TYPE_Q8_K) == -1
     assert qk.qk_act_type(qk.QK_TYPE_Q4_1) == -1   # its partner Q8_1 is only named

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 T8_0, T4_0, T4K, T6K, T8K = (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q4_K,
                              qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q8_K)
-T4_1, T5_0 = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_0
+T4_1, T5_0, T5K = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_K
 Y_TOL = 1e-5
 
 
@@ -212,14 +212,14 @@ def _edge_scale_blocks(t, rng, nblocks):
     b = weights(rng, t, 1, n).reshape(nblocks, -1).copy()
     specials = np.array([0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF, 0x3C00, 0xBC00, 0x0000],
                         dtype=np.uint16).view(np.uint8).reshape(-1, 2)
-    offs = {T8_0: [0], T4_0: [0], T4_1: [0, 2], T5_0: [0], T4K: [0, 2], T6K: [208]}[t]
+    offs = {T8_0: [0], T4_0: [0], T4_1: [0, 2], T5_0: [0], T4K: [0, 2], T5K: [0, 2], T6K: [208]}[t]
     for i in range(nblocks):
         for o in offs:
             b[i, o:o + 2] = specials[(i + o) % len(specials)]
     return b.reshape(-1)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0, T4K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0, T4K, T5K, T6K])
 def test_dequantize_bit_exact(torch_cuda, t):
     rng = np.random.default_rng(200 + t)
     for nblocks in (1, 3, 17, 1000):
@@ -238,6 +238,7 @@ def test_dequantize_bit_exact(torch_cuda, t):
 SHAPES = {
     T4K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T6K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
+    T5K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T8_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
     T4_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
     T5_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
@@ -255,7 +256,7 @@ def _oracle_sums(t, W, xq, n_out, n_in, ncols):
     return np.stack(out)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4K, T5K, T6K])
 def test_gemv_block_sums_and_y(torch_cuda, t):
     rng = np.random.default_rng(300 + t)
     at = orc.act_type(t)
@@ -329,7 +330,7 @@ def test_batched_q4_K_extreme_codes(torch_cuda):
 
 def test_gemv_max_row_length(torch_cuda):
     rng = np.random.default_rng(31)
-    for t in (T4K, T6K, T8_0, T4_0, T5_0):
+    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0):
         n_in = qk.qk_max_n_in(t)
         say("gemv max n_in", t, n_in)
         W = weights(rng, t, 3, n_in)
@@ -343,7 +344,7 @@ def test_gemv_max_row_length(torch_cuda):
 def test_gemv_zero_activation_gives_zero(torch_cuda):
     # rml ZeroActivationsGiveZero
     rng = np.random.default_rng(5)
-    for t in (T4K, T6K, T8_0, T4_0, T5_0):
+    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0):
         W = weights(rng, t, 8, 1024)
         xq = qk.qk_quantize_act(orc.act_type(t), torch_cuda.zeros((1, 1024), device="cuda"))
         y = host(qk.qk_gemv(t, dev(torch_cuda, W), 8, 1024, xq, 1))
@@ -454,7 +455,7 @@ def test_graph_capture_replays_match_eager(torch_cuda):
     rng = np.random.default_rng(9)
     cases = [(T4K, 64, 11008, 1), (T4K, 300, 4096, 1), (T6K, 70, 4096, 1), (T8_0, 50, 4096, 1),
              (T4_0, 33, 1024, 1), (T5_0, 41, 4096, 1), (T4K, 200, 4096, 16),
-             (T4K, 90, 2048, 64)]
+             (T4K, 90, 2048, 64), (T5K, 57, 11008, 1), (T5K, 40, 4096, 3)]
     bufs = []
     for t, n_out, n_in, nc in cases:
         W = dev(torch, weights(rng, t, n_out, n_in))
@@ -672,6 +673,37 @@ def test_full_q4_K_batched_14336x4096(torch_cuda, ncols):
     rows = np.unique(np.concatenate([np.arange(64), rng.integers(0, 14336, 192), [14335]]))
     _check_full(torch_cuda, T4K, d["W"], 14336, 4096, d["X"][:ncols], rows=rows,
                 what=f"Q4_K batched {ncols}")
+
+
+def test_full_q5_K_decode_4096x11008(torch_cuda):
+    d = synth.q5_K_decode_4096x11008()
+    say("full Q5_K 4096x11008")
+    _check_full(torch_cuda, T5K, d["W"], 4096, 11008, d["x"][None, :], what="Q5_K 4096x11008")
+
+
+def test_q5_K_extreme_codes(torch_cuda):
+    # every code 31 (all nibbles and fifth bits set) and largest 6-bit scales and
+    # mins against activations of +-127: the largest |S_q| and |S_m| the format
+    # can produce, computed exactly.
+    rng = np.random.default_rng(55)
+    n_out, n_in = 19, 11008
+    W = weights(rng, T5K, n_out, n_in).reshape(n_out, -1, 176).copy()
+    W[:, :, 4:16] = 0xFF
+    W[:, :, 16:176] = 0xFF
+    W[::2, :, 16:48] = 0x00  # half the rows: fifth bits clear (codes 15)
+    W = W.reshape(n_out, -1)
+    X = np.where(rng.random((2, n_in)) < 0.5, 127.0, -127.0).astype(np.float32)
+    X[1] = 127.0
+    xq = orc.quantize(orc.Q8_K, X)
+    Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+    for ncols in (1, 2):
+        say("Q5_K extreme codes", ncols)
+        sums = host(qk.qk_gemv_block_sums(T5K, Wd, n_out, n_in, xd, ncols))
+        want = _oracle_sums(T5K, W, xq, n_out, n_in, ncols).reshape(sums.shape)
+        assert np.array_equal(sums, want)
+        y = host(qk.qk_gemv(T5K, Wd, n_out, n_in, xd, ncols))
+        y_o, l1 = orc.gemv(T5K, W, n_out, n_in, xq, ncols)
+        assert_y(y, y_o, l1, "Q5_K extreme codes")
 
 
 def test_full_q4_K_decode_4096x11008(torch_cuda):
