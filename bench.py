@@ -10,7 +10,8 @@ Prints ONE JSON line on stdout (details on stderr):
   value      whole-job weight GB/s = steps * weight bytes per step / elapsed
   roofline   the GEMV kernels: algorithmic bytes per launch / mean kernel duration
              (HIP events recorded by the kernel launches themselves, on the
-             launch stream) against the 8 TB/s HBM peak
+             launch stream; the quantize launches of the step record theirs too,
+             reported as detail.quantize_kernel_us) against the 8 TB/s HBM peak
   cpu_baseline  the scalar C oracle on the host, single thread, on a bounded
              sample of the same workload (all_cores: the same sample on every
              usable host core at once)
@@ -512,27 +513,35 @@ def main():
     swiglu = bool(wl.get("swiglu_pair"))
     timed_names = ["gate_up", "down"] if swiglu else [gv[0] for gv in wl["gemvs"]]
     n_g = len(timed_names)
+    quant_names = list(acts)  # one activation quantize per key (x, then h for the FFN step)
+    n_q = len(quant_names)
 
-    def step(k, evs=None):
+    def quantize(i, at, xf, xq, qevs):
+        if qevs is None:
+            qk.qk_quantize_act(at, xf, xq)
+        else:
+            qk.qk_quantize_act_timed(at, xf, xq, qevs[i][0], qevs[i][1])
+
+    def step(k, evs=None, qevs=None):
         mats = dev_w[k % copies]
         if swiglu:
             (_, gt, g_out, g_in, _), _, (_, dt, d_out, d_in, _) = wl["gemvs"]
             at, xf, xq = acts["x"]
             _, h, hq = acts["h"]
-            qk.qk_quantize_act(at, xf, xq)
+            quantize(0, at, xf, xq, qevs)
             if evs is None:
                 qk.qk_gemv_pair(gt, mats[0], mats[1], g_out, g_in, xq, 1, qk.QK_EPI_SWIGLU, h)
             else:
                 qk.qk_gemv_pair_timed(gt, mats[0], mats[1], g_out, g_in, xq, 1, qk.QK_EPI_SWIGLU, h,
                                       evs[0][0], evs[0][1])
-            qk.qk_quantize_act(acts["h"][0], h, hq)
+            quantize(1, acts["h"][0], h, hq, qevs)
             if evs is None:
                 qk.qk_gemv(dt, mats[2], d_out, d_in, hq, 1, ys[2])
             else:
                 qk.qk_gemv_timed(dt, mats[2], d_out, d_in, hq, 1, ys[2], evs[1][0], evs[1][1])
             return
-        for key, (at, xf, xq) in acts.items():
-            qk.qk_quantize_act(at, xf, xq)
+        for i, (at, xf, xq) in enumerate(acts.values()):
+            quantize(i, at, xf, xq, qevs)
         for g, (wname, wt, n_out, n_in, akey) in enumerate(wl["gemvs"]):
             if wl.get("dequant") or quant_row:
                 if evs is not None:
@@ -582,13 +591,19 @@ def main():
     value_bytes = algorithmic_bytes(wl, qk) if (wl.get("dequant") or quant_row) else step_w_bytes
     value = value_bytes * args.steps / (elapsed_ms / 1e3) / 1e9
 
-    # Region B - the same K steps launched one by one; each GEMV launch records
-    # a start / stop event pair with its own kernel timestamps (HIP extended
-    # launch), giving kernel durations free of enqueue gaps.  torch creates the
-    # underlying events on their first record.
+    # Region B - the same K steps launched one by one; every kernel launch of the
+    # step (the activation quantize as well as the GEMV) records a start / stop
+    # event pair with its own kernel timestamps (HIP extended launch), giving
+    # kernel durations free of enqueue gaps.  Timing every kernel the same way
+    # matters: a launch-recorded start event on a kernel whose predecessor was
+    # launched without events also takes in part of the boundary between the two
+    # (about 1.7 us here), which rocprofv3's dispatch timestamps do not show.
+    # torch creates the underlying events on their first record.
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_g)] for _ in range(args.steps)]
-    for per in ev:
+    qev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_q)] for _ in range(args.steps)]
+    for per in ev + qev:
         for e0, e1 in per:
             e0.record(stream)
             e1.record(stream)
@@ -611,7 +626,7 @@ def main():
     hold_done.record(stream)
     e_start.record(stream)
     for k in range(args.steps):
-        step(args.warmup + k, ev[k])
+        step(args.warmup + k, ev[k], qev[k])
     e_stop.record(stream)
     backlog = not hold_done.query()  # still spinning: every step was queued in time
     torch.cuda.synchronize()
@@ -621,6 +636,8 @@ def main():
 
     kern_ms = np.array([[e0.elapsed_time(e1) for e0, e1 in per] for per in ev])  # [steps, n_g]
     gemv_ms_mean = kern_ms.sum(axis=1).mean()
+    quant_ms = (np.array([[e0.elapsed_time(e1) for e0, e1 in per] for per in qev])
+                if n_q else np.zeros((args.steps, 0)))  # [steps, n_q]
 
     # Region C - the read-stream ceiling: the library's read-only probe kernel over
     # the same weight tensors (same rotation, one launch per tensor, launch-recorded
@@ -663,11 +680,14 @@ def main():
 
     alg_bytes = algorithmic_bytes(wl, qk)
     achieved = alg_bytes / (gemv_ms_mean / 1e3) / 1e9
-    per_kernel_us = {timed_names[g]: {"mean": round(float(kern_ms[:, g].mean() * 1e3), 3),
-                                          "p10": round(float(np.percentile(kern_ms[:, g], 10) * 1e3), 3),
-                                          "p50": round(float(np.percentile(kern_ms[:, g], 50) * 1e3), 3),
-                                          "p90": round(float(np.percentile(kern_ms[:, g], 90) * 1e3), 3)}
-                     for g in range(n_g)}
+    def stats_us(col):
+        return {"mean": round(float(col.mean() * 1e3), 3),
+                "p10": round(float(np.percentile(col, 10) * 1e3), 3),
+                "p50": round(float(np.percentile(col, 50) * 1e3), 3),
+                "p90": round(float(np.percentile(col, 90) * 1e3), 3)}
+
+    per_kernel_us = {timed_names[g]: stats_us(kern_ms[:, g]) for g in range(n_g)}
+    quant_kernel_us = {quant_names[i]: stats_us(quant_ms[:, i]) for i in range(n_q)}
     log(f"[bench] graph replay {elapsed_ms:.3f} ms over {args.steps} steps "
         f"({elapsed_ms / args.steps * 1e3:.2f} us/step, host wall {wall * 1e3:.1f} ms); "
         f"eager {eager_ms / args.steps * 1e3:.2f} us/step; GEMV kernel time per step "
@@ -721,12 +741,14 @@ def main():
         "detail": {"gemv_kernel_us_per_step": round(float(gemv_ms_mean * 1e3), 3),
                    "kernel_timing": ("events recorded on the launch stream around each kernel"
                                      if (wl.get("dequant") or quant_row) else
-                                     "HIP events of the kernel launches") +
+                                     "HIP events recorded by every kernel launch of the step "
+                                     "(activation quantize and GEMV)") +
                                     ", steps run back to back behind a stream hold" +
                                     ("" if backlog else " (hold ended early)"),
                    "traffic_unit": "bytes per step (FETCH_SIZE + WRITE_SIZE, copy-kernel scaled)",
                    "eager_us_per_step": round(eager_ms / args.steps * 1e3, 3),
                    "gemv_kernel_us": per_kernel_us,
+                   "quantize_kernel_us": quant_kernel_us or None,
                    "algorithmic_bytes_per_step_gemv": alg_bytes,
                    "read_stream_ceiling": ceiling},
     }

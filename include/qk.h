@@ -103,6 +103,13 @@ int64_t qk_max_n_in(int weight_type);
 int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
                     void* stream);
 
+/* qk_quantize_act_timed - qk_quantize_act whose kernel launch records ev_start and
+ * ev_stop itself (hipEvent_t, either may be NULL), as qk_gemv_timed: timing every
+ * kernel of a step the same way keeps the per-kernel durations comparable.
+ * Arguments and errors otherwise as qk_quantize_act. */
+int qk_quantize_act_timed(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
+                          void* stream, void* ev_start, void* ev_stop);
+
 /*
  * qk_quantize_row - quantize f32 weights into GGUF blocks (quantize_row_*_ref).
  *   type      QK_TYPE_Q8_0, Q4_0, Q4_1 or Q5_0 (else QK_E_TYPE).

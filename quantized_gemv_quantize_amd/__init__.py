@@ -61,6 +61,8 @@ def lib():
         L.qk_max_n_in.argtypes = [i32]
         L.qk_quantize_act.restype = i32
         L.qk_quantize_act.argtypes = [i32, p, p, i64, i64, p]
+        L.qk_quantize_act_timed.restype = i32
+        L.qk_quantize_act_timed.argtypes = [i32, p, p, i64, i64, p, p, p]
         L.qk_quantize_row.restype = i32
         L.qk_quantize_row.argtypes = [i32, p, p, i64, p]
         L.qk_gemv.restype = i32
@@ -131,6 +133,18 @@ def qk_quantize_act(act_type, x, xq=None, stream=None):
                          device=x.device)
     _check(lib().qk_quantize_act(act_type, _ptr(x), _ptr(xq), n, ncols, _stream(stream)),
            "qk_quantize_act")
+    return xq
+
+
+def qk_quantize_act_timed(act_type, x, xq, ev_start, ev_stop, stream=None):
+    """qk_quantize_act whose kernel launch records the torch.cuda.Event(enable_timing=True)
+    pair itself (either may be None)."""
+    n = x.shape[-1]
+    ncols = x.numel() // n if n else 0
+    e0 = ctypes.c_void_p(ev_start.cuda_event) if ev_start is not None else None
+    e1 = ctypes.c_void_p(ev_stop.cuda_event) if ev_stop is not None else None
+    _check(lib().qk_quantize_act_timed(act_type, _ptr(x), _ptr(xq), n, ncols, _stream(stream), e0, e1),
+           "qk_quantize_act_timed")
     return xq
 
 

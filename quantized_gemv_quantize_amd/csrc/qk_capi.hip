@@ -165,8 +165,8 @@ int64_t qk_max_n_in(int weight_type) {
   return best;
 }
 
-int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
-                    void* stream) {
+int qk_quantize_act_timed(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
+                          void* stream, void* ev_start, void* ev_stop) {
   if (!is_act(act_type)) return QK_E_TYPE;
   const int64_t be = qk_block_elems(act_type);
   if (n <= 0 || n % be != 0 || ncols < 0) return QK_E_SHAPE;
@@ -175,7 +175,13 @@ int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t n
   if (!aligned16(x) || !aligned16(xq)) return QK_E_ALIGN;
   const int64_t nblocks = n / be * ncols;
   return status_of(qk::launch_quantize(act_type, x, static_cast<uint8_t*>(xq), nblocks,
-                                       static_cast<hipStream_t>(stream)));
+                                       static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
+                                       static_cast<hipEvent_t>(ev_stop)));
+}
+
+int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
+                    void* stream) {
+  return qk_quantize_act_timed(act_type, x, xq, n, ncols, stream, nullptr, nullptr);
 }
 
 int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream) {

@@ -20,9 +20,10 @@ inline bool launch_grid(int64_t blocks, int threads_per_block, unsigned* grid) {
 }
 
 // Activation quantization of `nblocks` consecutive blocks (any number of columns
-// laid end to end: blocks of consecutive columns are contiguous).
+// laid end to end: blocks of consecutive columns are contiguous).  Non-null events
+// are recorded by the launch itself (start / end of the kernel).
 hipError_t launch_quantize(int act_type, const float* x, uint8_t* xq, int64_t nblocks,
-                           hipStream_t s);
+                           hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 // Weight quantization (quantize_row_*_ref) of `nblocks` 32-element blocks of
 // type Q8_0, Q4_0, Q4_1 or Q5_0.

@@ -16,6 +16,7 @@
 //
 // The weight quantizers Q4_0, Q4_1 and Q5_0 (quantize_row_*_ref) follow below.
 #include <float.h>
+#include <hip/hip_ext.h>
 #include <limits.h>
 
 #include "qk_device.h"
@@ -263,16 +264,17 @@ hipError_t launch_quantize_row(int type, const float* x, uint8_t* dst, int64_t n
 }
 
 hipError_t launch_quantize(int act_type, const float* x, uint8_t* xq, int64_t nblocks,
-                           hipStream_t s) {
+                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (nblocks <= 0) return hipSuccess;
   // Q8_0: 8 lanes per block; Q8_K: one wavefront per block
   unsigned grid = 0;
   if (!launch_grid(act_type == kQ8_0 ? (nblocks * 8 + 255) / 256 : (nblocks + 3) / 4, 256, &grid))
     return hipErrorInvalidConfiguration;
-  if (act_type == kQ8_0) {
-    quantize_q8_0_kernel<<<grid, 256, 0, s>>>(x, xq, nblocks);
+  auto* kernel = act_type == kQ8_0 ? quantize_q8_0_kernel : quantize_q8_K_kernel;
+  if (e0 != nullptr || e1 != nullptr) {
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, e0, e1, 0, x, xq, nblocks);
   } else {
-    quantize_q8_K_kernel<<<grid, 256, 0, s>>>(x, xq, nblocks);
+    kernel<<<grid, 256, 0, s>>>(x, xq, nblocks);
   }
   return hipGetLastError();
 }

@@ -104,15 +104,18 @@ def _status(fn, *args):
     return getattr(qk.lib(), fn)(*args)
 
 
-def test_quantize_validation():
-    assert _status("qk_quantize_act", qk.QK_TYPE_Q4_K, GOOD, GOOD, 256, 1, None) == 1  # weight type
-    assert _status("qk_quantize_act", 99, GOOD, GOOD, 256, 1, None) == 1
-    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_0, GOOD, GOOD, 33, 1, None) == 3
-    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_K, GOOD, GOOD, 0, 1, None) == 3
-    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, -1, None) == 3
-    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_K, None, GOOD, 256, 1, None) == 5
-    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_K, GOOD, ODD, 256, 1, None) == 4
-    assert _status("qk_quantize_act", qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, 0, None) == 0  # no-op
+@pytest.mark.parametrize("timed", [False, True])
+def test_quantize_validation(timed):
+    def st(*a):
+        return _status("qk_quantize_act_timed", *a, None, None) if timed else _status("qk_quantize_act", *a)
+    assert st(qk.QK_TYPE_Q4_K, GOOD, GOOD, 256, 1, None) == 1  # weight type
+    assert st(99, GOOD, GOOD, 256, 1, None) == 1
+    assert st(qk.QK_TYPE_Q8_0, GOOD, GOOD, 33, 1, None) == 3
+    assert st(qk.QK_TYPE_Q8_K, GOOD, GOOD, 0, 1, None) == 3
+    assert st(qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, -1, None) == 3
+    assert st(qk.QK_TYPE_Q8_K, None, GOOD, 256, 1, None) == 5
+    assert st(qk.QK_TYPE_Q8_K, GOOD, ODD, 256, 1, None) == 4
+    assert st(qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, 0, None) == 0  # no-op
 
 
 def test_quantize_row_validation():

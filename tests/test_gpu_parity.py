@@ -403,6 +403,23 @@ def test_gemv_timed_matches_untimed(torch_cuda):
     assert torch_cuda.equal(y0, y1)
 
 
+def test_quantize_act_timed_matches_untimed(torch_cuda):
+    rng = np.random.default_rng(14)
+    for act, n, ncols in ((T8K, 11008, 1), (T8_0, 4096, 3)):
+        say("quantize_act_timed", act, n, ncols)
+        x = dev(torch_cuda, rng.standard_normal((ncols, n)).astype(np.float32))
+        want = host(qk.qk_quantize_act(act, x))
+        xq = torch_cuda.zeros((ncols, qk.qk_row_bytes(act, n)), dtype=torch_cuda.uint8, device="cuda")
+        e0 = torch_cuda.cuda.Event(enable_timing=True)
+        e1 = torch_cuda.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()
+        qk.qk_quantize_act_timed(act, x, xq, e0, e1)
+        torch_cuda.cuda.synchronize()
+        assert np.array_equal(host(xq), want)
+        assert e0.elapsed_time(e1) > 0
+
+
 def test_gemv_pair_timed_matches_untimed(torch_cuda):
     rng = np.random.default_rng(9)
     for n_in in (4096, 11008):  # the register kernel and the LDS kernel
