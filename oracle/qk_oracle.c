@@ -18,7 +18,7 @@
 /* ------------------------------------------------------------------------- */
 /* Type table.                                                                */
 /* [candle] GgmlDType table: block elements / block bytes                    */
-/*   Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q8_0 32/34, Q4K 256/144,            */
+/*   Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q5_1 32/24, Q8_0 32/34, Q4K 256/144,*/
 /*   Q5K 256/176, Q6K 256/210, Q8K 256/292.                                   */
 /* [sipllm] Design, "type_nbytes(t, n) = n / block_size * type_size".        */
 /* ------------------------------------------------------------------------- */
@@ -28,6 +28,7 @@ int64_t orc_block_elems(int type) {
     case ORC_Q4_0:
     case ORC_Q4_1:
     case ORC_Q5_0:
+    case ORC_Q5_1:
     case ORC_Q8_0:
       return 32;
     case ORC_Q4_K:
@@ -45,6 +46,7 @@ int64_t orc_block_bytes(int type) {
     case ORC_Q4_0: return 18;
     case ORC_Q4_1: return 20;
     case ORC_Q5_0: return 22;
+    case ORC_Q5_1: return 24;
     case ORC_Q8_0: return 34;
     case ORC_Q4_K: return 144;
     case ORC_Q5_K: return 176;
@@ -366,6 +368,18 @@ static int orc_q5_0_code(const uint8_t* blk, int e) {
   return (low4 | (bit4 << 4)) - 16;
 }
 
+/* Q5_1 ([candle] GgmlDType table: 32 elements in 24 bytes; 块结构 prose: the _1
+ * types add an f16 min m to the _0 block): d f16 @0, m f16 @2, qh u32 @4, qs[16]
+ * @8 (GGUF order; the pages do not give it).  Code as Q5_0's (low 4 bits ordered
+ * as Q4_0, bit 4 = bit e of qh), unsigned 0..31, value code * d + m as Q4_1. */
+static int orc_q5_1_code(const uint8_t* blk, int e) {
+  const uint8_t* qs = blk + 8;
+  uint32_t qh = (uint32_t)blk[4] | ((uint32_t)blk[5] << 8) | ((uint32_t)blk[6] << 16) |
+                ((uint32_t)blk[7] << 24);
+  int low4 = (e < 16) ? (qs[e] & 0x0F) : (qs[e - 16] >> 4);
+  return low4 | (int)(((qh >> e) & 1u) << 4);
+}
+
 /* Q4_K sub-block (scale, min) pair, get_scale_min_k4:
  * [candle] 块结构: "the first 4 sub-blocks' scale and min are the low 6 bits of
  * the first 8 bytes; the last 4 keep their low 4 bits in the last 4 bytes and
@@ -458,6 +472,12 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
         float d = orc_f16_to_f32(orc_get_u16(blk));
         float m = orc_f16_to_f32(orc_get_u16(blk + 2));
         for (int e = 0; e < 32; ++e) y[e] = (float)orc_q4_1_code(blk, e) * d + m;
+        break;
+      }
+      case ORC_Q5_1: { /* as Q4_1 with the 5-bit code: value = code * d + m */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        float m = orc_f16_to_f32(orc_get_u16(blk + 2));
+        for (int e = 0; e < 32; ++e) y[e] = (float)orc_q5_1_code(blk, e) * d + m;
         break;
       }
       case ORC_Q5_0: { /* [cl] Example 8: value = (code - 16) * d */

@@ -24,6 +24,9 @@
  *   rule); the scale rule taken is the Q8_0 one over 256 elements.
  *   Q6_K ql/qh bit arrangement: parity unpinned (the pages give only the field
  *   roles); the GGUF arrangement is assumed.
+ *   dequantize Q5_1: the pages give its size (24 bytes) and that the _1 types add
+ *   an f16 min to the _0 layout; the field order (d, m, qh, qs) is GGUF's.  With no
+ *   fifth bit set it reduces to the pinned Q4_1 decoder; dequantize only, as Q4_1.
  *   Q5_K field order and fifth-bit arrangement: parity unpinned (the pages give
  *   its size and that it shares Q4K's d, dmin and 6-bit scales and mins); the
  *   GGUF arrangement is assumed.  With every fifth bit clear it reduces to the
@@ -48,6 +51,7 @@ extern "C" {
 #define ORC_Q4_0 2
 #define ORC_Q4_1 3
 #define ORC_Q5_0 6
+#define ORC_Q5_1 7
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13

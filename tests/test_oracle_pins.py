@@ -24,7 +24,7 @@ F32 = np.float32
 
 def test_type_table_matches_printed_geometry():
     # candle "量化格式" GgmlDType table; codeloopback lesson format table.
-    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
+    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q5_1": o.Q5_1, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
            "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
     for name, gid, elems, nbytes, bpw in rows("type_table.txt"):
         t = ids[name]
@@ -501,6 +501,40 @@ def test_q6_K_structure_invariants():
     # q = 0 everywhere: value = -32 * d * sc
     sc = bb[192:208].view(np.int8).astype(np.float32)
     assert np.array_equal(o.dequantize(o.Q6_K, bb, 256), np.repeat(F32(-32) * d * sc, 16))
+
+
+# --------------------------------------------------------------------------
+# Q5_1 (dequantize only): size from candle's table, "the _1 types add an f16 min"
+# from its block prose; field order not on the pages (parity unpinned beyond the
+# reduction to the pinned Q4_1 decoder and the fifth-bit structure).
+# --------------------------------------------------------------------------
+
+def test_q5_1_without_fifth_bits_is_q4_1():
+    rng = np.random.default_rng(71)
+    for _ in range(50):
+        b = rng.integers(0, 256, 24, dtype=np.uint8)
+        b[0:2] = np.frombuffer(np.float16(rng.uniform(1e-3, 4e-3)).tobytes(), np.uint8)
+        b[2:4] = np.frombuffer(np.float16(rng.uniform(-0.03, 0.03)).tobytes(), np.uint8)
+        b[4:8] = 0
+        q41 = np.concatenate([b[0:4], b[8:24]])
+        assert np.array_equal(o.dequantize(o.Q5_1, b, 32), o.dequantize(o.Q4_1, q41, 32))
+
+
+def test_q5_1_fifth_bit_e_is_element_e():
+    # bit e of qh is bit 4 of element e, as in Q5_0 (codeloopback Example 8's qh
+    # string pins that arrangement for Q5_0); with m = 0 it adds exactly 16 d.
+    rng = np.random.default_rng(72)
+    b = rng.integers(0, 256, 24, dtype=np.uint8)
+    b[0:2] = np.frombuffer(np.float16(0.25).tobytes(), np.uint8)
+    b[2:4] = 0
+    b[4:8] = 0
+    y0 = o.dequantize(o.Q5_1, b, 32).astype(np.float64)
+    for e in range(32):
+        bb = b.copy()
+        bb[4 + e // 8] |= 1 << (e % 8)
+        y1 = o.dequantize(o.Q5_1, bb, 32).astype(np.float64)
+        assert list(np.nonzero(y1 != y0)[0]) == [e]
+        assert y1[e] - y0[e] == 16 * 0.25
 
 
 # --------------------------------------------------------------------------
