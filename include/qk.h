@@ -39,6 +39,7 @@ extern "C" {
 #define QK_TYPE_Q4_0 2
 #define QK_TYPE_Q4_1 3
 #define QK_TYPE_Q5_0 6
+#define QK_TYPE_Q5_1 7
 #define QK_TYPE_Q8_0 8
 #define QK_TYPE_Q4_K 12
 #define QK_TYPE_Q5_K 13
@@ -62,7 +63,7 @@ extern "C" {
 #define QK_EPI_SWIGLU 1
 
 /* Elements per block (32 or 256) and bytes per block (Q4_0 18, Q4_1 20, Q5_0 22,
- * Q8_0 34, Q4_K 144, Q5_K 176, Q6_K 210, Q8_K 292) of a type, 0 for an unknown id.  Geometry
+ * Q5_1 24, Q8_0 34, Q4_K 144, Q5_K 176, Q6_K 210, Q8_K 292) of a type, 0 for an unknown id.  Geometry
  * from the candle formats page, "GgmlDType" table. */
 int64_t qk_block_elems(int type);
 int64_t qk_block_bytes(int type);
@@ -74,8 +75,8 @@ int64_t qk_row_bytes(int type, int64_t n);
 
 /* Activation type a weight type is multiplied against (candle "VecDotType" table;
  * codeloopback Example 11): Q4_0, Q5_0, Q8_0 -> Q8_0; Q4_K, Q5_K, Q6_K -> Q8_K; -1
- * otherwise (Q4_1 pairs with Q8_1, a format the sources only name, so Q4_1 is a
- * quantize / dequantize type here and has no GEMV). */
+ * otherwise (Q4_1 and Q5_1 pair with Q8_1, a format the sources only name, so they
+ * are quantize / dequantize types here and have no GEMV). */
 int qk_act_type(int weight_type);
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -161,16 +162,19 @@ int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* 
 
 /*
  * qk_dequantize_row - expand n elements (whole blocks) of a weight type to f32.
- *   type      QK_TYPE_Q8_0, Q4_0, Q4_1, Q5_0, Q4_K, Q5_K or Q6_K (Q8_K is an
+ *   type      QK_TYPE_Q8_0, Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q5_K or Q6_K (Q8_K is an
  *             activation-only format and is refused with QK_E_TYPE, as sipllm's
  *             dequantize_row refuses it).
  *   src       n / block blocks, device.  A whole matrix is n = n_out * n_in.
  *   dst       out: f32 [n], device.
  *   n         >= 0, a multiple of the block size; 0 enqueues nothing.
  * Values (rml DequantizeRow; candle block table; codeloopback Examples 7, 8): Q8_0
- * d*q; Q4_0 d*(q-8); Q4_1 q*d + m; Q5_0 d*(q-16); Q4_K and Q5_K d*sc_j*q - dmin*m_j;
- * Q6_K d*sc_j*(q-32).  Each product is exact in f32 (at most one rounding, in the
- * final addition of Q4_1, Q4_K and Q5_K), so the result is bit-exact.
+ * d*q; Q4_0 d*(q-8); Q4_1 and Q5_1 q*d + m; Q5_0 d*(q-16); Q4_K and Q5_K
+ * d*sc_j*q - dmin*m_j; Q6_K d*sc_j*(q-32).  Each product is exact in f32 (at most
+ * one rounding, in the final addition of Q4_1, Q5_1, Q4_K and Q5_K), so the result
+ * is bit-exact.
+ * Q5_1 (24 B): d f16 @0, m f16 @2, qh u32 @4, qs[16] @8 (the _1 types add an f16 min
+ * to the _0 block; the order is GGUF's); code as Q5_0's, unsigned 0..31.
  * Q5_K (176 B): d f16 @0, dmin f16 @2, scales[12] @4 packed as Q4_K's, qh[32] @16,
  * qs[128] @48; element e = 64c + p: low 4 bits as Q4_K's (qs[32c + p % 32], low
  * nibble for p < 32, else high), bit 4 = bit 2c + (p >= 32) of qh[p % 32].

@@ -16,7 +16,7 @@ bool is_weight(int t) {
          t == QK_TYPE_Q5_K || t == QK_TYPE_Q6_K;
 }
 // Weight formats qk_dequantize_row expands.
-bool is_dequant(int t) { return is_weight(t) || t == QK_TYPE_Q4_1; }
+bool is_dequant(int t) { return is_weight(t) || t == QK_TYPE_Q4_1 || t == QK_TYPE_Q5_1; }
 // Weight formats qk_quantize_row writes.
 bool is_quant_row(int t) {
   return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_0 || t == QK_TYPE_Q4_1 || t == QK_TYPE_Q5_0;
@@ -92,6 +92,7 @@ int64_t qk_block_elems(int type) {
     case QK_TYPE_Q4_0:
     case QK_TYPE_Q4_1:
     case QK_TYPE_Q5_0:
+    case QK_TYPE_Q5_1:
     case QK_TYPE_Q8_0: return 32;
     case QK_TYPE_Q4_K:
     case QK_TYPE_Q5_K:
@@ -106,6 +107,7 @@ int64_t qk_block_bytes(int type) {
     case QK_TYPE_Q4_0: return 18;
     case QK_TYPE_Q4_1: return 20;
     case QK_TYPE_Q5_0: return 22;
+    case QK_TYPE_Q5_1: return 24;
     case QK_TYPE_Q8_0: return 34;
     case QK_TYPE_Q4_K: return 144;
     case QK_TYPE_Q5_K: return 176;

@@ -6,6 +6,7 @@
 //   Q4_0  d * (q - 8); byte j: element j in the low nibble, element j+16 in the high
 //   Q4_1  q * d + m, nibbles as Q4_0 (codeloopback Example 7)
 //   Q5_0  d * (q - 16), low nibbles as Q4_0, bit 4 from qh (codeloopback Example 8)
+//   Q5_1  q * d + m, q as Q5_0's code (the _1 block adds an f16 min to the _0 one)
 //   Q4_K  d * sc_j * q - dmin * m_j for 32-element sub-block j (scales per
 //         get_scale_min_k4, rml element-200 trace)
 //   Q5_K  the same with a 5-bit q: element 64c + p takes bit 2c + (p >= 32) of
@@ -107,6 +108,29 @@ __global__ __launch_bounds__(256) void dequant_q5_0_kernel(const uint8_t* __rest
   // four bits -> bit 4 of four bytes: multiplying by 0x204081 copies bit i to bit 8i
   const uint32_t fifth = ((((qh >> (4 * part)) & 0xF) * 0x00204081u) & 0x01010101u) << 4;
   *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(lo | fifth, d, 16);
+}
+
+// Q5_1: Q5_0's codes (unsigned) with Q4_1's value q * d + m; d, m, qh in the first 8
+// bytes (4-byte aligned: 24-byte blocks from a 16-byte aligned base).
+__global__ __launch_bounds__(256) void dequant_q5_1_kernel(const uint8_t* __restrict__ src,
+                                                           float* __restrict__ dst,
+                                                           int64_t nblocks) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t b = t >> 3;
+  if (b >= nblocks) return;
+  const int part = threadIdx.x & 7;
+  const uint8_t* blk = src + b * kQ5_1Bytes;
+  const uint2 dmq = *reinterpret_cast<const uint2*>(blk);  // d, m, qh
+  const float d = f16_to_f32(dmq.x & 0xFFFF), m = f16_to_f32(dmq.x >> 16);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(blk + 8 + 4 * (part & 3));
+  const uint32_t lo = (part < 4) ? (w & kLo4) : ((w >> 4) & kLo4);
+  const uint32_t q = lo | (((((dmq.y >> (4 * part)) & 0xF) * 0x00204081u) & 0x01010101u) << 4);
+  float4 o;
+  o.x = static_cast<float>(q & 0xFF) * d + m;
+  o.y = static_cast<float>((q >> 8) & 0xFF) * d + m;
+  o.z = static_cast<float>((q >> 16) & 0xFF) * d + m;
+  o.w = static_cast<float>(q >> 24) * d + m;
+  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = o;
 }
 
 // Q4_K, Q5_K and Q6_K: one wavefront per kSB consecutive superblocks, lane l -> elements
@@ -211,7 +235,7 @@ hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t n
                              hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   // 32-element formats: 8 lanes per block; K-quants: kSB superblocks per wavefront
-  const bool small = type == kQ8_0 || type == kQ4_0 || type == kQ4_1 || type == kQ5_0;
+  const bool small = type == kQ8_0 || type == kQ4_0 || type == kQ4_1 || type == kQ5_0 || type == kQ5_1;
   unsigned grid = 0;
   if (!launch_grid(small ? (nblocks * 8 + 255) / 256 : (nblocks + 4 * kSB - 1) / (4 * kSB), 256, &grid))
     return hipErrorInvalidConfiguration;
@@ -220,6 +244,7 @@ hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t n
     case kQ4_0: dequant_q4_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ4_1: dequant_q4_1_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ5_0: dequant_q5_0_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ5_1: dequant_q5_1_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ4_K: dequant_q4_K_kernel<0><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ5_K: dequant_q4_K_kernel<1><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ6_K: dequant_q6_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;

@@ -5,6 +5,7 @@
 //   Q4_0  18 B: d f16 @0, qs u8[16] @2 (byte j: element j low nibble, j+16 high)
 //   Q4_1  20 B: d f16 @0, m f16 @2, qs u8[16] @4 (nibbles as Q4_0)
 //   Q5_0  22 B: d f16 @0, qh u32 @2 (bit e: bit 4 of element e), qs u8[16] @6
+//   Q5_1  24 B: d f16 @0, m f16 @2, qh u32 @4, qs u8[16] @8 (GGUF order)
 //   Q4_K 144 B: d f16 @0, dmin f16 @2, scales u8[12] @4, qs u8[128] @16
 //   Q5_K 176 B: d f16 @0, dmin f16 @2, scales u8[12] @4 (as Q4_K), qh u8[32] @16,
 //               qs u8[128] @48 (the pages give the size and field roles; the
@@ -22,6 +23,7 @@ constexpr int kQ8_0Bytes = 34;
 constexpr int kQ4_0Bytes = 18;
 constexpr int kQ4_1Bytes = 20;
 constexpr int kQ5_0Bytes = 22;
+constexpr int kQ5_1Bytes = 24;
 constexpr int kQ4_KBytes = 144;
 constexpr int kQ5_KBytes = 176;
 constexpr int kQ6_KBytes = 210;

@@ -13,9 +13,11 @@ Recipes (one numpy default_rng(seed) per workload, drawn in the order listed):
 """
 import numpy as np
 
-Q4_0, Q4_1, Q5_0, Q8_0, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 8, 12, 13, 14, 15
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q8_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q8_K: 292}
+Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 7, 8, 12, 13, 14, 15
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256,
+               Q8_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210,
+               Q8_K: 292}
 
 
 def uniform_bytes(rng, shape):
@@ -51,6 +53,15 @@ def q4_1_blocks(rng, n_out, n_in, d_range=(1e-3, 4e-3), m_range=(-0.03, -0.005))
     b[:, :, 0:2] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
     b[:, :, 2:4] = _f16_bytes(rng.uniform(*m_range, size=(n_out, nb)))
     return b.reshape(n_out, nb * 20)
+
+
+def q5_1_blocks(rng, n_out, n_in, d_range=(5e-4, 2e-3), m_range=(-0.03, -0.005)):
+    """Q5_1 rows: f16 d ~ U[d_range], f16 m ~ U[m_range]; the 4 qh and 16 qs bytes uniform."""
+    nb = n_in // 32
+    b = uniform_bytes(rng, (n_out, nb, 24))
+    b[:, :, 0:2] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    b[:, :, 2:4] = _f16_bytes(rng.uniform(*m_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 24)
 
 
 def q5_0_blocks(rng, n_out, n_in, d_range=(5e-4, 2e-3)):
@@ -89,8 +100,8 @@ def q6_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
 
 
 def weight_blocks(rng, t, n_out, n_in):
-    return {Q4_0: q4_0_blocks, Q4_1: q4_1_blocks, Q5_0: q5_0_blocks, Q4_K: q4_K_blocks,
-            Q5_K: q5_K_blocks, Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
+    return {Q4_0: q4_0_blocks, Q4_1: q4_1_blocks, Q5_0: q5_0_blocks, Q5_1: q5_1_blocks,
+            Q4_K: q4_K_blocks, Q5_K: q5_K_blocks, Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
 
 
 def gaussian(rng, shape, std=1.0):

@@ -58,7 +58,7 @@ def test_library_is_built_for_gfx950_only():
 
 
 def test_geometry_matches_type_table():
-    ids = {"Q4_0": qk.QK_TYPE_Q4_0, "Q4_1": qk.QK_TYPE_Q4_1, "Q5_0": qk.QK_TYPE_Q5_0,
+    ids = {"Q4_0": qk.QK_TYPE_Q4_0, "Q4_1": qk.QK_TYPE_Q4_1, "Q5_0": qk.QK_TYPE_Q5_0, "Q5_1": qk.QK_TYPE_Q5_1,
            "Q8_0": qk.QK_TYPE_Q8_0, "Q4_K": qk.QK_TYPE_Q4_K, "Q5_K": qk.QK_TYPE_Q5_K,
            "Q6_K": qk.QK_TYPE_Q6_K, "Q8_K": qk.QK_TYPE_Q8_K}
     for name, gid, elems, nbytes, _ in rows("type_table.txt"):
@@ -73,7 +73,7 @@ def test_geometry_matches_type_table():
     assert qk.qk_row_bytes(99, 256) == 0
     assert qk.qk_row_bytes(qk.QK_TYPE_Q5_0, 4096) == 2816
     assert qk.qk_row_bytes(qk.QK_TYPE_Q4_1, 4096) == 2560
-    assert qk.qk_block_elems(7) == 0
+    assert qk.qk_block_elems(9) == 0  # Q8_1: named on the pages, never laid out
 
 
 def test_pairing():
@@ -85,6 +85,7 @@ def test_pairing():
     assert qk.qk_act_type(qk.QK_TYPE_Q5_0) == qk.QK_TYPE_Q8_0
     assert qk.qk_act_type(qk.QK_TYPE_Q8_K) == -1
     assert qk.qk_act_type(qk.QK_TYPE_Q4_1) == -1   # its partner Q8_1 is only named
+    assert qk.qk_act_type(qk.QK_TYPE_Q5_1) == -1
 
 
 def test_max_n_in_covers_llm_shapes():
@@ -136,6 +137,7 @@ def test_gemv_validation():
     f = "qk_gemv"
     assert _status(f, qk.QK_TYPE_Q8_K, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
     assert _status(f, qk.QK_TYPE_Q4_1, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
+    assert _status(f, qk.QK_TYPE_Q5_1, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1  # no GEMV
     assert _status(f, 5, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
     assert _status(f, qk.QK_TYPE_Q4_K, GOOD, 4, 255, GOOD, 1, GOOD, None) == 3
     assert _status(f, qk.QK_TYPE_Q4_K, GOOD, 4, 0, GOOD, 1, GOOD, None) == 3
@@ -193,7 +195,7 @@ def test_read_probe_validation():
 def test_dequantize_validation():
     f = "qk_dequantize_row"
     assert _status(f, qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, None) == 1   # activation-only type
-    assert _status(f, 7, GOOD, GOOD, 32, None) == 1
+    assert _status(f, 9, GOOD, GOOD, 32, None) == 1   # Q8_1: never laid out on the pages
     assert _status(f, qk.QK_TYPE_Q4_0, GOOD, GOOD, 48, None) == 3
     assert _status(f, qk.QK_TYPE_Q4_0, GOOD, GOOD, -32, None) == 3
     assert _status(f, qk.QK_TYPE_Q4_0, None, GOOD, 32, None) == 5

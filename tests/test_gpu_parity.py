@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 T8_0, T4_0, T4K, T6K, T8K = (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q4_K,
                              qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q8_K)
-T4_1, T5_0, T5K = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_K
+T4_1, T5_0, T5_1, T5K = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_1, qk.QK_TYPE_Q5_K
 Y_TOL = 1e-5
 
 
@@ -212,14 +212,15 @@ def _edge_scale_blocks(t, rng, nblocks):
     b = weights(rng, t, 1, n).reshape(nblocks, -1).copy()
     specials = np.array([0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF, 0x3C00, 0xBC00, 0x0000],
                         dtype=np.uint16).view(np.uint8).reshape(-1, 2)
-    offs = {T8_0: [0], T4_0: [0], T4_1: [0, 2], T5_0: [0], T4K: [0, 2], T5K: [0, 2], T6K: [208]}[t]
+    offs = {T8_0: [0], T4_0: [0], T4_1: [0, 2], T5_0: [0], T5_1: [0, 2], T4K: [0, 2], T5K: [0, 2],
+            T6K: [208]}[t]
     for i in range(nblocks):
         for o in offs:
             b[i, o:o + 2] = specials[(i + o) % len(specials)]
     return b.reshape(-1)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0, T4K, T5K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0, T5_1, T4K, T5K, T6K])
 def test_dequantize_bit_exact(torch_cuda, t):
     rng = np.random.default_rng(200 + t)
     for nblocks in (1, 3, 17, 1000):
