@@ -211,7 +211,7 @@ int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const 
  * y2 = W2 x.  Each row is computed in both matrices from one load of the
  * activation operands (candle formats page, "实测：一次点积": vec_dot_4, one
  * activation row against several weight rows with the activation loaded once).
- *   w_type    QK_TYPE_Q4_K (else QK_E_TYPE); x blocks are Q8_K.
+ *   w_type    QK_TYPE_Q4_K or QK_TYPE_Q5_K (else QK_E_TYPE); x blocks are Q8_K.
  *   W1, W2    n_out rows of qk_row_bytes(w_type, n_in) bytes each, device.
  *   n_out, n_in, xq, ncols   as qk_gemv; ncols <= 65535 (else QK_E_LIMIT).
  *   epilogue  QK_EPI_NONE: out is f32 [ncols][2][n_out], y1 then y2 per column.

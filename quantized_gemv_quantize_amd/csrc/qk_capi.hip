@@ -209,7 +209,7 @@ int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const 
 int qk_gemv_pair_timed(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
                        const void* xq, int64_t ncols, int epilogue, float* out, void* stream,
                        void* ev_start, void* ev_stop) {
-  if (w_type != QK_TYPE_Q4_K) return QK_E_TYPE;
+  if (w_type != QK_TYPE_Q4_K && w_type != QK_TYPE_Q5_K) return QK_E_TYPE;
   if (epilogue != QK_EPI_NONE && epilogue != QK_EPI_SWIGLU) return QK_E_ARG;
   int rc = check_gemv(w_type, W1, n_out, n_in, xq, ncols, out);
   if (rc != QK_OK) return rc;
@@ -217,7 +217,7 @@ int qk_gemv_pair_timed(int w_type, const void* W1, const void* W2, int64_t n_out
   if (n_out == 0 || ncols == 0) return QK_OK;
   if (W2 == nullptr) return QK_E_NULL;
   if (!aligned16(W2)) return QK_E_ALIGN;
-  return status_of(qk::launch_gemv_pair(static_cast<const uint8_t*>(W1), static_cast<const uint8_t*>(W2),
+  return status_of(qk::launch_gemv_pair(w_type, static_cast<const uint8_t*>(W1), static_cast<const uint8_t*>(W2),
                                         n_out, n_in, static_cast<const uint8_t*>(xq), ncols,
                                         epilogue == QK_EPI_SWIGLU, out, static_cast<hipStream_t>(stream),
                                         static_cast<hipEvent_t>(ev_start),

@@ -741,8 +741,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
 }
 
 // ---------------------------------------------------------------------------
-// Two Q4_K matrices over one activation row: the gate and up projections of an
-// FFN layer.  The wavefront that owns row r computes it in both W1 and W2 from
+// Two Q4_K matrices (or, with the Q5 flag, two Q5_K matrices) over one activation
+// row: the gate and up projections of an FFN layer.  The wavefront that owns row r
+// computes it in both W1 and W2 from
 // the same activation operands (candle formats page, "实测：一次点积": vec_dot_4
 // takes one activation row against four weight rows with the activation loaded
 // once; here one row of each matrix), then writes y1[r] and y2[r], or the gated activation
@@ -762,7 +763,7 @@ __device__ __forceinline__ void pair_out(float* out, int n_out, int row, float g
 
 // Rows of one or two passes: activations in registers (as gemv_q4_K_reg), rows
 // grid-strided.
-template <int NW, int NP, int EPI>
+template <int NW, int NP, int EPI, int Q5 = 0>
 __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_reg(
     const uint8_t* __restrict__ W1, const uint8_t* __restrict__ W2, int n_out, int nb,
     const uint8_t* __restrict__ xq, float* __restrict__ out) {
@@ -772,7 +773,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_reg(
   const int sh = (c & 1) * 16;
   const int wave = blockIdx.x * NW + wave_id();
   const int nwaves = gridDim.x * NW;
-  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+  using F = KQuant4<Q5>;
+  const size_t rb = static_cast<size_t>(nb) * F::kBytes;
   xq += static_cast<size_t>(blockIdx.y) * nb * kQ8_KBytes;
   out += static_cast<size_t>(blockIdx.y) * (EPI == kEpiSwiglu ? 1 : 2) * n_out;
 
@@ -790,16 +792,20 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_reg(
   }
 
   for (int row = wave; row < n_out; row += nwaves) {
-    uint4 H[2][NP], Q0[2][NP], Q1[2][NP];
+    uint4 H[2][NP], Q0[2][NP], Q1[2][NP], QH0[2][Q5 ? NP : 1], QH1[2][Q5 ? NP : 1];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const uint8_t* wrow = (m ? W2 : W1) + static_cast<size_t>(row) * rb;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * kQ4_KBytes);
+        const uint8_t* q = wrow + static_cast<uint32_t>(min(p * 16 + u, nb - 1) * F::kBytes);
         H[m][p] = *reinterpret_cast<const uint4*>(q);
-        Q0[m][p] = *reinterpret_cast<const uint4*>(q + 16 + 32 * c);
-        Q1[m][p] = *reinterpret_cast<const uint4*>(q + 32 + 32 * c);
+        Q0[m][p] = *reinterpret_cast<const uint4*>(q + F::kQs + 32 * c);
+        Q1[m][p] = *reinterpret_cast<const uint4*>(q + F::kQs + 16 + 32 * c);
+        if constexpr (Q5 != 0) {
+          QH0[m][p] = *reinterpret_cast<const uint4*>(q + 16);
+          QH1[m][p] = *reinterpret_cast<const uint4*>(q + 32);
+        }
       }
     }
     float acc[2] = {0.0f, 0.0f};
@@ -808,8 +814,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_reg(
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (p * 16 + u >= nb) continue;  // uniform over the 4 lanes of a superblock
-        const int2 part = q4K_chunk(Q0[m][p], Q1[m][p], H[m][p], A[p][0], A[p][1], A[p][2],
-                                    A[p][3], S2[p], hi_mask, sh);
+        int2 part;
+        if constexpr (Q5 != 0) {
+          part = q5K_chunk(Q0[m][p], Q1[m][p], shr4(QH0[m][p], 2 * c), shr4(QH1[m][p], 2 * c), H[m][p],
+                           A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask, sh);
+        } else {
+          part = q4K_chunk(Q0[m][p], Q1[m][p], H[m][p], A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask,
+                           sh);
+        }
         const int sq = quad_sum(part.x);
         const int sm = quad_sum(part.y);
         const uint32_t dd = H[m][p].x;
@@ -826,7 +838,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_reg(
 
 // Longer rows: the activation row staged in LDS once per workgroup (as
 // gemv_q4_K_kernel), one row of each matrix per wavefront.
-template <int NW, int UNR, int EPI>
+template <int NW, int UNR, int EPI, int Q5 = 0>
 __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_kernel(
     const uint8_t* __restrict__ W1, const uint8_t* __restrict__ W2, int n_out, int nb,
     const uint8_t* __restrict__ xq, float* __restrict__ out) {
@@ -835,13 +847,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_kernel(
   const int row = blockIdx.x * NW + wave_id();
   const int c = lane & 3, u = lane >> 2;
   const bool row_ok = row < n_out;
-  const size_t rb = static_cast<size_t>(nb) * kQ4_KBytes;
+  using F = KQuant4<Q5>;
+  const size_t rb = static_cast<size_t>(nb) * F::kBytes;
   const size_t roff = static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
   const int passes = (nb + 15) >> 4;
   xq += static_cast<size_t>(blockIdx.y) * nb * kQ8_KBytes;
   out += static_cast<size_t>(blockIdx.y) * (EPI == kEpiSwiglu ? 1 : 2) * n_out;
 
-  uint4 H[2][UNR], Q0[2][UNR], Q1[2][UNR];
+  uint4 H[2][UNR], Q0[2][UNR], Q1[2][UNR], QH0[2][Q5 ? UNR : 1], QH1[2][Q5 ? UNR : 1];
   auto issue = [&](int p0) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -849,10 +862,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_kernel(
 #pragma unroll
       for (int j = 0; j < UNR; ++j) {
         const int sb = min((p0 + j) * 16 + u, nb - 1);
-        const uint8_t* p = wrow + static_cast<uint32_t>(sb * kQ4_KBytes);
+        const uint8_t* p = wrow + static_cast<uint32_t>(sb * F::kBytes);
         H[m][j] = *reinterpret_cast<const uint4*>(p);
-        Q0[m][j] = *reinterpret_cast<const uint4*>(p + 16 + 32 * c);
-        Q1[m][j] = *reinterpret_cast<const uint4*>(p + 32 + 32 * c);
+        Q0[m][j] = *reinterpret_cast<const uint4*>(p + F::kQs + 32 * c);
+        Q1[m][j] = *reinterpret_cast<const uint4*>(p + F::kQs + 16 + 32 * c);
+        if constexpr (Q5 != 0) {
+          QH0[m][j] = *reinterpret_cast<const uint4*>(p + 16);
+          QH1[m][j] = *reinterpret_cast<const uint4*>(p + 32);
+        }
       }
     }
   };
@@ -885,7 +902,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_kernel(
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const uint4 h = H[m][j];
-        const int2 part = q4K_chunk(Q0[m][j], Q1[m][j], h, a0, a1, a2, a3, asum, hi_mask, sh);
+        int2 part;
+        if constexpr (Q5 != 0) {
+          part = q5K_chunk(Q0[m][j], Q1[m][j], shr4(QH0[m][j], 2 * c), shr4(QH1[m][j], 2 * c), h, a0, a1, a2,
+                           a3, asum, hi_mask, sh);
+        } else {
+          part = q4K_chunk(Q0[m][j], Q1[m][j], h, a0, a1, a2, a3, asum, hi_mask, sh);
+        }
         const int sq = quad_sum(part.x);
         const int sm = quad_sum(part.y);
         const float cb = (dx * f16_to_f32(h.x & 0xFFFF)) * static_cast<float>(sq) -
@@ -1209,7 +1232,7 @@ void launch_ev(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEv
   }
 }
 
-template <int EPI>
+template <int EPI, int Q5>
 hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
                            const uint8_t* xq, int64_t ncols, float* out, hipStream_t s, hipEvent_t e0,
                            hipEvent_t e1) {
@@ -1222,25 +1245,30 @@ hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, 
     constexpr int64_t kPairWaves = kMaxWaves / 2;
     const int64_t waves = n_out < kPairWaves ? n_out : kPairWaves;
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));  // <= 512
-    if (passes == 1) launch_ev(gemv_q4_K_pair_reg<4, 1, EPI>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
-    else launch_ev(gemv_q4_K_pair_reg<4, 2, EPI>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
+    if (passes == 1) launch_ev(gemv_q4_K_pair_reg<4, 1, EPI, Q5>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
+    else launch_ev(gemv_q4_K_pair_reg<4, 2, EPI, Q5>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
   } else {
     unsigned gx = 0;
     if (!launch_grid((n_out + kWaves - 1) / kWaves, kWaves * 64, &gx)) return hipErrorInvalidConfiguration;
     const dim3 grid(gx, static_cast<unsigned>(ncols));
     const int64_t lds = gemv_lds_bytes(kQ4_K, n_in);
-    launch_ev(gemv_q4_K_pair_kernel<kWaves, 3, EPI>, grid, dim3(kWaves * 64), static_cast<size_t>(lds), s, e0, e1,
+    launch_ev(gemv_q4_K_pair_kernel<kWaves, 3, EPI, Q5>, grid, dim3(kWaves * 64), static_cast<size_t>(lds), s, e0, e1,
               W1, W2, n, nb, xq, out);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_pair(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
+hipError_t launch_gemv_pair(int w_type, const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
                             const uint8_t* xq, int64_t ncols, int swiglu, float* out, hipStream_t s,
                             hipEvent_t e0, hipEvent_t e1) {
   if (n_out <= 0 || ncols <= 0) return hipSuccess;
-  return swiglu ? launch_pair_epi<kEpiSwiglu>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1)
-                : launch_pair_epi<kEpiPair>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1);
+  if (w_type == kQ5_K) {
+    return swiglu ? launch_pair_epi<kEpiSwiglu, 1>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1)
+                  : launch_pair_epi<kEpiPair, 1>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1);
+  }
+  if (w_type != kQ4_K) return hipErrorInvalidValue;
+  return swiglu ? launch_pair_epi<kEpiSwiglu, 0>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1)
+                : launch_pair_epi<kEpiPair, 0>(W1, W2, n_out, n_in, xq, ncols, out, s, e0, e1);
 }
 
 }  // namespace qk

@@ -51,7 +51,7 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in);
 // Q4_K W1 and W2 over the same Q8_K activation columns (ncols <= 65535): out is
 // [ncols][2][n_out] (y1 then y2) or, with swiglu, [ncols][n_out] silu(y1) * y2.
 // ev_start / ev_stop as launch_gemv (one launch).
-hipError_t launch_gemv_pair(const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
+hipError_t launch_gemv_pair(int w_type, const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
                             const uint8_t* xq, int64_t ncols, int swiglu, float* out, hipStream_t s,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 constexpr int64_t kMaxLdsBytes = 65536;

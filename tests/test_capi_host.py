@@ -165,7 +165,7 @@ def test_gemv_pair_validation(f):
 
     def st(*a):
         return _status(f, *a, *ev)
-    assert st(qk.QK_TYPE_Q6_K, GOOD, GOOD, 4, 256, GOOD, 1, 0, GOOD, None) == 1  # Q4_K only
+    assert st(qk.QK_TYPE_Q6_K, GOOD, GOOD, 4, 256, GOOD, 1, 0, GOOD, None) == 1  # Q4_K / Q5_K only
     assert st(T4K, GOOD, GOOD, 4, 256, GOOD, 1, 2, GOOD, None) == 8     # epilogue
     assert st(T4K, GOOD, GOOD, 4, 255, GOOD, 1, 0, GOOD, None) == 3
     assert st(T4K, GOOD, GOOD, -1, 256, GOOD, 1, 1, GOOD, None) == 3

@@ -544,25 +544,26 @@ def assert_swiglu(h_gpu, g_o, u_o, l1g, l1u, what):
 PAIR_SHAPES = [(1, 256), (7, 4096), (130, 4096), (33, 8192), (9, 11008), (5, 28672)]
 
 
+@pytest.mark.parametrize("t", [T4K, T5K])
 @pytest.mark.parametrize("n_out,n_in", PAIR_SHAPES)
-def test_gemv_pair_and_swiglu(torch_cuda, n_out, n_in):
-    rng = np.random.default_rng(600 + n_out + n_in)
+def test_gemv_pair_and_swiglu(torch_cuda, n_out, n_in, t):
+    rng = np.random.default_rng(600 + n_out + n_in + t)
     for ncols in (1, 3):
-        say("gemv_pair", n_out, n_in, ncols)
-        W1 = synth.q4_K_blocks(rng, n_out, n_in)
-        W2 = synth.q4_K_blocks(rng, n_out, n_in)
+        say("gemv_pair", t, n_out, n_in, ncols)
+        W1 = synth.weight_blocks(rng, t, n_out, n_in)
+        W2 = synth.weight_blocks(rng, t, n_out, n_in)
         X = rng.standard_normal((ncols, n_in)).astype(np.float32)
         xq = orc.quantize(T8K, X)
         W1d, W2d, xd = dev(torch_cuda, W1), dev(torch_cuda, W2), dev(torch_cuda, xq)
-        pair = host(qk.qk_gemv_pair(T4K, W1d, W2d, n_out, n_in, xd, ncols))
-        g_o, l1g = orc.gemv(T4K, W1, n_out, n_in, xq, ncols)
-        u_o, l1u = orc.gemv(T4K, W2, n_out, n_in, xq, ncols)
+        pair = host(qk.qk_gemv_pair(t, W1d, W2d, n_out, n_in, xd, ncols))
+        g_o, l1g = orc.gemv(t, W1, n_out, n_in, xq, ncols)
+        u_o, l1u = orc.gemv(t, W2, n_out, n_in, xq, ncols)
         assert_y(pair[:, 0], g_o, l1g, f"pair y1 {n_out}x{n_in} ncols {ncols}")
         assert_y(pair[:, 1], u_o, l1u, f"pair y2 {n_out}x{n_in} ncols {ncols}")
         if ncols == 1:  # the one-column GEMV kernels' own arithmetic
-            assert np.array_equal(pair[:, 0], host(qk.qk_gemv(T4K, W1d, n_out, n_in, xd, 1)))
-            assert np.array_equal(pair[:, 1], host(qk.qk_gemv(T4K, W2d, n_out, n_in, xd, 1)))
-        h = host(qk.qk_gemv_pair(T4K, W1d, W2d, n_out, n_in, xd, ncols, qk.QK_EPI_SWIGLU))
+            assert np.array_equal(pair[:, 0], host(qk.qk_gemv(t, W1d, n_out, n_in, xd, 1)))
+            assert np.array_equal(pair[:, 1], host(qk.qk_gemv(t, W2d, n_out, n_in, xd, 1)))
+        h = host(qk.qk_gemv_pair(t, W1d, W2d, n_out, n_in, xd, ncols, qk.QK_EPI_SWIGLU))
         assert h.shape == (ncols, n_out)
         assert_swiglu(h, g_o, u_o, l1g, l1u, f"swiglu {n_out}x{n_in} ncols {ncols}")
 
