@@ -88,6 +88,11 @@ def workloads(qk):
             "gemvs": [("gate", T4K, 11008, 4096, "x"), ("up", T4K, 11008, 4096, "x"),
                       ("down", T6K, 4096, 11008, "h")],
             "acts": {"x": (T8K, 4096, 1), "h": (T8K, 11008, 1)}, "swiglu_pair": True},
+        # the same step with Q5_K gate / up (the Q5_K_M layout of these layers)
+        "ffn_7b_q5_K_swiglu": {
+            "gemvs": [("gate", T5K, 11008, 4096, "x"), ("up", T5K, 11008, 4096, "x"),
+                      ("down", T6K, 4096, 11008, "h")],
+            "acts": {"x": (T8K, 4096, 1), "h": (T8K, 11008, 1)}, "swiglu_pair": True},
         "q6_K_head_32000x4096": {
             "gemvs": [("W", T6K, 32000, 4096, "x")], "acts": {"x": (T8K, 4096, 1)}},
         "q8_0_256x1024": {
@@ -114,8 +119,8 @@ def host_inputs(name, qk):
         return synth.q5_K_decode_4096x11008()
     if name in ("q4_K_4096x4096", "q4_0_4096x4096"):
         return synth.q4_gemv_4096x4096()
-    if name in ("ffn_7b_q4_K_q6_K", "ffn_7b_swiglu"):
-        d = synth.ffn_7b()
+    if name in ("ffn_7b_q4_K_q6_K", "ffn_7b_swiglu", "ffn_7b_q5_K_swiglu"):
+        d = synth.ffn_7b_q5_K() if name == "ffn_7b_q5_K_swiglu" else synth.ffn_7b()
         d["h"] = d["x2"]  # initial contents of the gated activation buffer
         return d
     if name in ("q6_K_head_32000x4096", "q6_K_dequantize_32000x4096"):

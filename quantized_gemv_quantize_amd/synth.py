@@ -137,6 +137,17 @@ def ffn_7b():
             "x2": gaussian(rng, (11008,))}
 
 
+def ffn_7b_q5_K():
+    """7B-shape FFN as a Q5_K_M file stores it: gate, up Q5_K 11008x4096; down Q6_K
+    4096x11008; x[4096], x2[11008]."""
+    rng = np.random.default_rng(9)
+    gate = q5_K_blocks(rng, 11008, 4096)
+    up = q5_K_blocks(rng, 11008, 4096)
+    down = q6_K_blocks(rng, 4096, 11008)
+    return {"gate": gate, "up": up, "down": down, "x": gaussian(rng, (4096,)),
+            "x2": gaussian(rng, (11008,))}
+
+
 def q6_K_head_32000x4096():
     """Q6_K output head 32000x4096; x[4096]."""
     rng = np.random.default_rng(3)

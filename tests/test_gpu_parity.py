@@ -586,21 +586,23 @@ def test_swiglu_extreme_gates(torch_cuda):
     assert_swiglu(h, g_o, u_o, l1g, l1u, "swiglu extreme gates")
 
 
-def test_ffn_swiglu_step_7b(torch_cuda):
+@pytest.mark.parametrize("gt", [T4K, T5K])
+def test_ffn_swiglu_step_7b(torch_cuda, gt):
     # the FFN decode step as the library runs it: quantize x, gate + up with the
     # SwiGLU epilogue, quantize h on the GPU, down projection.  Each stage is
-    # checked against the oracle on the GPU's own input to that stage.
+    # checked against the oracle on the GPU's own input to that stage.  Gate / up
+    # are Q4_K (Q4_K_M layout) or Q5_K (Q5_K_M layout); down is Q6_K in both.
     torch = torch_cuda
-    d = synth.ffn_7b()
-    say("FFN step 7B: gate/up pair")
+    d = synth.ffn_7b() if gt == T4K else synth.ffn_7b_q5_K()
+    say("FFN step 7B: gate/up pair", gt)
     x = d["x"][None, :]
     xq = qk.qk_quantize_act(T8K, dev(torch, x))
     assert np.array_equal(host(xq), orc.quantize(T8K, x))
-    h = qk.qk_gemv_pair(T4K, dev(torch, d["gate"]), dev(torch, d["up"]), 11008, 4096, xq, 1,
+    h = qk.qk_gemv_pair(gt, dev(torch, d["gate"]), dev(torch, d["up"]), 11008, 4096, xq, 1,
                         qk.QK_EPI_SWIGLU)
     xq_h = host(xq)
-    g_o, l1g = orc.gemv(T4K, d["gate"], 11008, 4096, xq_h, 1)
-    u_o, l1u = orc.gemv(T4K, d["up"], 11008, 4096, xq_h, 1)
+    g_o, l1g = orc.gemv(gt, d["gate"], 11008, 4096, xq_h, 1)
+    u_o, l1u = orc.gemv(gt, d["up"], 11008, 4096, xq_h, 1)
     h_host = host(h)
     assert_swiglu(h_host, g_o, u_o, l1g, l1u, "FFN h")
     say("FFN step 7B: quantize h, down")
