@@ -222,8 +222,8 @@ int qk_gemv_timed(int w_type, const void* W, int64_t n_out, int64_t n_in, const 
  *             Any other value: QK_E_ARG.
  * Every column runs the one-column GEMV kernels' arithmetic (same integer sums,
  * float steps and summation order), so with ncols = 1 QK_EPI_NONE returns what
- * qk_gemv returns bit for bit; with more columns qk_gemv uses the matrix cores and
- * the two agree to within rounding.  Errors otherwise as qk_gemv.
+ * qk_gemv returns bit for bit; with more Q4_K columns qk_gemv uses the matrix cores
+ * and the two agree to within rounding.  Errors otherwise as qk_gemv.
  */
 int qk_gemv_pair(int w_type, const void* W1, const void* W2, int64_t n_out, int64_t n_in,
                  const void* xq, int64_t ncols, int epilogue, float* out, void* stream);
