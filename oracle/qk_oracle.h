@@ -20,8 +20,9 @@
  *   get_scale_min_k4 prose, plus brute force.
  *   vec_dot Q4_KxQ8_K / Q6_KxQ8_K: pinned by brute force against the dequant
  *   definitions and by the bsums identity.
- *   quantize_q8_K: invariants only (the pages give its layout, not its scale
- *   rule); the scale rule taken is the Q8_0 one over 256 elements.
+ *   quantize_q8_K: the pages give its layout, and for its scale rule only the
+ *   round-trip statistics of [candle] "往返误差"; the rule taken is the Q8_0 one
+ *   over 256 elements, pinned by those statistics and by invariants.
  *   Q6_K ql/qh bit arrangement: parity unpinned (the pages give only the field
  *   roles); the GGUF arrangement is assumed.
  *   dequantize Q5_1: the pages give its size (24 bytes) and that the _1 types add

@@ -504,6 +504,46 @@ def test_q6_K_structure_invariants():
 
 
 # --------------------------------------------------------------------------
+# Round-trip statistics printed on the candle formats page ("往返误差"): the only
+# numbers the pages give that depend on the Q8_K scale rule (its bytes are never
+# printed).  Quantize + dequantize of 262144 N(0,1) values (and the same with one
+# value per 256 scaled by 20) must reproduce the printed rel RMSE within the
+# sampling spread of a different draw (1 % of the value for N(0,1), 3 % with
+# outliers; measured over seeds 0-5: 0.3 % and 1.6 %) and max |err| within 25 %.
+# This fixes each rule's resolution (block size, levels, round to nearest), not its
+# last bit.  Planted in the Q8_K rule, each of these fails: a divisor of 128 (the
+# extreme value saturates at 127, so max |err| is a whole step), 63 or 255,
+# truncation instead of rounding, an amax over the first 32 values only.
+# --------------------------------------------------------------------------
+
+def _roundtrip(t, x):
+    if t == o.Q8_K:
+        b = o.quantize(o.Q8_K, x.reshape(-1, 256)).reshape(-1, 292)
+        d = b[:, 0:4].copy().view(np.float32)[:, 0]
+        y = (b[:, 4:260].view(np.int8).astype(np.float32) * d[:, None]).reshape(-1)
+    else:
+        y = o.dequantize(t, o.quantize(t, x), x.size)
+    e = y.astype(np.float64) - x.astype(np.float64)
+    return 100 * math.sqrt(np.mean(e ** 2) / np.mean(x.astype(np.float64) ** 2)), float(np.max(np.abs(e)))
+
+
+@pytest.mark.parametrize("row", rows("candle_roundtrip.txt", sep="|"), ids=lambda r: r[0])
+def test_candle_roundtrip_statistics(row):
+    name, rmse, maxerr, rmse_o, _ = row
+    t = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q8_0": o.Q8_0, "Q8_K": o.Q8_K}[name]
+    rng = np.random.default_rng(2025)
+    x = rng.standard_normal(262144).astype(np.float32)
+    got, gmax = _roundtrip(t, x)
+    assert abs(got - float(rmse)) <= 0.01 * float(rmse), (name, got)
+    assert abs(gmax - float(maxerr)) <= 0.25 * float(maxerr), (name, gmax)
+    if rmse_o != "-":
+        xo = x.copy().reshape(-1, 256)
+        xo[np.arange(xo.shape[0]), rng.integers(0, 256, xo.shape[0])] *= np.float32(20)
+        got_o, _ = _roundtrip(t, xo.reshape(-1))
+        assert abs(got_o - float(rmse_o)) <= 0.03 * float(rmse_o), (name, got_o)
+
+
+# --------------------------------------------------------------------------
 # Q5_1 (dequantize only): size from candle's table, "the _1 types add an f16 min"
 # from its block prose; field order not on the pages (parity unpinned beyond the
 # reduction to the pinned Q4_1 decoder and the fifth-bit structure).
