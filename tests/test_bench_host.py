@@ -26,6 +26,11 @@ def test_algorithmic_bytes_of_the_workloads():
     # gate + up pair (x read once, one f32 per row) and the Q6_K down projection
     ffn = 2 * 25_362_432 + 4_672 + 4 * 11008 + 36_986_880 + 12_556 + 4 * 4096
     assert bench.algorithmic_bytes(wls["ffn_7b_swiglu"], qk) == ffn
+    # Q5_K 4096 x 11008: 43 superblocks of 176 B per row
+    assert bench.algorithmic_bytes(wls["q5_K_decode_4096x11008"], qk) == 4096 * 43 * 176 + 12_556 + 16_384
+    # the same FFN step with Q5_K gate / up (11008 rows of 16 superblocks of 176 B each)
+    ffn5 = 2 * 11008 * 16 * 176 + 4_672 + 4 * 11008 + 36_986_880 + 12_556 + 4 * 4096
+    assert bench.algorithmic_bytes(wls["ffn_7b_q5_K_swiglu"], qk) == ffn5
     # 64 columns: activations 64 x 4,672 B, outputs 64 x 14336 f32
     assert bench.algorithmic_bytes(wls["q4_K_batched_14336x4096_n64"], qk) == \
         33_030_144 + 64 * 4_672 + 4 * 64 * 14336
@@ -34,6 +39,8 @@ def test_algorithmic_bytes_of_the_workloads():
 def test_kernel_families():
     assert bench.kernel_family("q4_K_decode_4096x11008") == "gemv"
     assert bench.kernel_family("ffn_7b_swiglu") == "gemv"
+    assert bench.kernel_family("ffn_7b_q5_K_swiglu") == "gemv"
+    assert bench.kernel_family("q5_K_decode_4096x11008") == "gemv"
     assert bench.kernel_family("q4_K_batched_14336x4096_n16") == "gemm"
     assert bench.kernel_family("q6_K_dequantize_32000x4096") == "dequant"
     assert bench.kernel_family("q4_0_quantize_row_4096x11008") == "quantize_row"
