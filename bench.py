@@ -52,6 +52,15 @@ KERNEL_SOURCES = {"gemv": ["qk_gemv.hip", "qk_device.h", "qk_internal.h"],
                   "dequant": ["qk_dequant.hip", "qk_device.h", "qk_internal.h"],
                   "quantize_row": ["qk_quantize.hip", "qk_device.h", "qk_internal.h"]}
 METRIC = "quantized GEMV weight GB/s and % of HBM peak (Q4_K/Q6_K/Q8_0, batch 1)"
+# The pages' own figures for these dot products (candle formats page, "实测：一次点积"):
+# one 4096-element row against one activation row on one M2 Max CPU core, the row
+# cache-resident, fastest of 9 batches; weight GB/s = row bytes / time.  Context for
+# the bench line only: another machine, another memory level, another workload.
+PAGES_CONTEXT = {
+    "Q4_K": "Q4K x Q8K vec_dot 99.9 ns per 4096-element row (2304 B): 23.1 GB/s, one M2 Max core, cache-resident",
+    "Q6_K": "Q6K x Q8K vec_dot 152.3 ns per 4096-element row (3360 B): 22.1 GB/s, one M2 Max core, cache-resident",
+    "Q8_0": "Q8_0 x Q8_0 vec_dot 121.9 ns per 4096-element row (4352 B): 35.7 GB/s, one M2 Max core, cache-resident",
+}
 
 
 def log(*a):
@@ -755,7 +764,9 @@ def main():
                    "gemv_kernel_us": per_kernel_us,
                    "quantize_kernel_us": quant_kernel_us or None,
                    "algorithmic_bytes_per_step_gemv": alg_bytes,
-                   "read_stream_ceiling": ceiling},
+                   "read_stream_ceiling": ceiling,
+                   "pages_context": {k: v for k, v in PAGES_CONTEXT.items()
+                                     if any(qk.TYPE_NAMES[t] == k for _, t, _, _, _ in wl["gemvs"])} or None},
     }
     if kernel_family(args.workload) == "gemm":
         # the batched path is also a contraction: 2 int8 ops per weight and column
