@@ -139,7 +139,9 @@ def block_sums(wt, w_row, xq_row, n):
 
 
 def vec_dot(wt, w_row, xq_row, n):
-    """(f32 result, sum |c_b| in f64) of one weight row against one act row."""
+    """(f32 result, tolerance scale in f64) of one weight row against one act row: the
+    sum over blocks of the absolute float terms of each block step (|c_b| for the
+    one-term formats; |scale term| + |min term| for Q4_K and Q5_K)."""
     y = np.zeros(1, dtype=np.float32)
     l1 = np.zeros(1, dtype=np.float64)
     _check(lib().orc_vec_dot(wt, _ptr(_u8(w_row)), _ptr(_u8(xq_row)), n, _ptr(y), _ptr(l1)),
@@ -148,7 +150,8 @@ def vec_dot(wt, w_row, xq_row, n):
 
 
 def gemv(wt, W, n_out, n_in, xq, ncols=1):
-    """y [ncols, n_out] f32 and l1 [ncols, n_out] f64 (sum |c_b| per output)."""
+    """y [ncols, n_out] f32 and l1 [ncols, n_out] f64 (the vec_dot tolerance scale per
+    output)."""
     y = np.zeros((ncols, n_out), dtype=np.float32)
     l1 = np.zeros((ncols, n_out), dtype=np.float64)
     _check(lib().orc_gemv(wt, _ptr(_u8(W)), n_out, n_in, _ptr(_u8(xq)), ncols, _ptr(y),

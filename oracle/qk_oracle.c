@@ -648,6 +648,19 @@ static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const
   }
 }
 
+/* The magnitude a block contributes to the tolerance scale: the sum of the
+ * absolute values of the float terms its step adds ([cl] Example 10 measures
+ * error against the sum of |a*b| over the terms).  One term for Q8_0, Q4_0,
+ * Q5_0 and Q6_K; for Q4_K and Q5_K the scale term (dx*d)*S_q and the min term
+ * (dx*dmin)*S_m, which can cancel in c while each is rounded on its own. */
+static double orc_block_l1(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s, float c) {
+  if (wt != ORC_Q4_K && wt != ORC_Q5_K) return fabs((double)c);
+  float dx = orc_get_f32(xb);
+  float d = orc_f16_to_f32(orc_get_u16(wb));
+  float dmin = orc_f16_to_f32(orc_get_u16(wb + 2));
+  return fabs((double)((dx * d) * (float)s[0])) + fabs((double)((dx * dmin) * (float)s[1]));
+}
+
 int orc_block_sums(int wt, const uint8_t* w, const uint8_t* xq, int64_t n, int32_t* sums) {
   int at = orc_act_type(wt);
   if (at < 0) return ORC_BAD_PAIR;
@@ -663,8 +676,10 @@ int orc_block_sums(int wt, const uint8_t* w, const uint8_t* xq, int64_t n, int32
 
 /* VecDot(weight, w, x, n): y = sum over blocks of the float step, accumulated
  * in f32 in block order ([cl] Example 10: `sumf += ...`).  l1 (optional)
- * receives sum |c_b| in f64, the scale the output tolerance is taken against
- * ([cl] Example 10 reports error against the sum of |a*b|). */
+ * receives, in f64, the sum over blocks of the absolute float terms of each step
+ * (|c_b| for the one-term formats, |scale term| + |min term| for Q4_K and Q5_K):
+ * the scale the output tolerance is taken against ([cl] Example 10 reports error
+ * against the sum of |a*b|). */
 int orc_vec_dot(int wt, const uint8_t* w, const uint8_t* xq, int64_t n, float* out, double* l1) {
   int at = orc_act_type(wt);
   if (at < 0) return ORC_BAD_PAIR;
@@ -678,7 +693,7 @@ int orc_vec_dot(int wt, const uint8_t* w, const uint8_t* xq, int64_t n, float* o
     if (rc != ORC_OK) return rc;
     float c = orc_block_float(wt, w + bw * b, xq + bx * b, s);
     sumf += c;
-    sabs += fabs((double)c);
+    sabs += orc_block_l1(wt, w + bw * b, xq + bx * b, s, c);
   }
   *out = sumf;
   if (l1) *l1 = sabs;

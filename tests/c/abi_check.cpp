@@ -4,7 +4,8 @@
 // infrastructure) on the same inputs.
 //
 // Bars: activation blocks, per-block int32 sums, dequantized values and weight
-// blocks bit-exact; y within 1e-5 * sum_b |c_b| per output.
+// blocks bit-exact; y within 1e-5 * L per output, L the oracle's sum of the absolute
+// float terms of the block steps (orc_gemv's l1).
 // Inputs: splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
 // generators", 2014) drives random block bytes, f16 scales drawn uniformly in the
 // workloads' ranges, and activations uniform in [-2, 2).
