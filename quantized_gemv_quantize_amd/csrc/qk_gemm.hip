@@ -404,13 +404,30 @@ hipError_t launch_gemm_q4K(const uint8_t* W, int64_t n_out, int64_t n_in, const 
                            hipEvent_t e1) {
   const int nb = static_cast<int>(n_in / 256);
   const int n = static_cast<int>(n_out), nc = static_cast<int>(ncols);
-  // measured on 14336 x 4096 (graph replay): 16 columns 12.2 us (two row tiles:
-  // 13.3); 32 columns 16.3 us (Cfg<2,1,1> with two row tiles: 19.3); 64 columns
-  // 22.6 us (Cfg<4,2,1>: 27.8).  Shapes of 16 wavefronts that need more than 128
-  // registers spill and are slower.
-  if (nc <= 16) return launch_cfg<Cfg<1, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-  if (nc <= 32) return launch_cfg<Cfg<2, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-  if (nc <= 64) return launch_cfg<Cfg<4, 4, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+  // 64-row workgroups (RT = 4) share each staged activation tile over four row
+  // tiles, measured best on 14336 x 4096 (graph replay: 16 columns 12.2 us, two row
+  // tiles 13.3; 32 columns 16.3 us, Cfg<2,1,1> with two row tiles 19.3; 64 columns
+  // 22.6 us, Cfg<4,2,1> 27.8).  Few rows leave most CUs idle at 64 rows per
+  // workgroup (4096 rows: 64 workgroups for 256 CUs), so matrices with at most 128
+  // (16 columns) or 64 (32, 64 columns) such groups use 16-row workgroups with four
+  // superblocks per stage instead (launch-recorded events: 4096 x 11008 at 16 / 32 /
+  // 64 columns 25.9 / 35.9 / 52.4 -> 15.7 / 21.4 / 33.6 us; 4096 x 4096 13.0 / 16.9 /
+  // 23.8 -> 9.1 / 11.5 / 16.8 us; at 11008 or more rows the 64-row shapes stay
+  // faster).  Shapes of 16 wavefronts that need more than 128 registers spill and
+  // are slower.
+  const int64_t groups64 = (n_out + 63) / 64;
+  if (nc <= 16) {
+    if (groups64 <= 128) return launch_cfg<Cfg<1, 1, 4, 1>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+    return launch_cfg<Cfg<1, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+  }
+  if (nc <= 32) {
+    if (groups64 <= 64) return launch_cfg<Cfg<2, 1, 4, 1>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+    return launch_cfg<Cfg<2, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+  }
+  if (nc <= 64) {
+    if (groups64 <= 64) return launch_cfg<Cfg<4, 2, 4, 1>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+    return launch_cfg<Cfg<4, 4, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
+  }
   return hipErrorInvalidValue;
 }
 
