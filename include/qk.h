@@ -150,9 +150,13 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
  * "Quantized dot products"; the Q4_K / Q5_K min term taken from the activation bsums), then
  * one f32 step with the block scales; y is the f32 sum of those steps.  The
  * summation order differs from a sequential loop, so y matches a sequential f32
- * evaluation to within rounding, not bit for bit.  Q4_K with ncols > 1 runs on the
- * int8 matrix cores, up to 64 columns per launch (same per-block integers, y equal
- * to within rounding); every other case runs the one-column kernels per column.
+ * evaluation to within rounding, not bit for bit.  Several columns: Q4_K at 2
+ * columns (3 up to 8192 rows) and Q5_K in groups of up to 4 columns run a GEMV
+ * kernel that reads W once for all its columns (each column's arithmetic as the
+ * one-column kernel's); Q4_K otherwise runs on the int8 matrix cores, up to 64
+ * columns per launch (same per-block integers, y equal to within rounding); every
+ * other case, and rows too long for the shared activation buffer, runs the
+ * one-column kernels per column.
  * Errors: QK_E_TYPE; QK_E_SHAPE (n_in not whole blocks, a negative count, or
  * n_out above INT32_MAX); QK_E_LIMIT (n_in above qk_max_n_in, or a launch beyond
  * 2^32 - 1 work-items); QK_E_NULL / QK_E_ALIGN for W, xq, y; QK_E_DEVICE.

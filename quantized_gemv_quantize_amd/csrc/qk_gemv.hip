@@ -406,6 +406,138 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Q4_K / Q5_K x Q8_K for NC = 2..4 activation columns (a small batch): the LDS
+// kernel above with each weight superblock loaded and unpacked once and its codes
+// multiplied against every column's activations, the NC Q8_K rows staged one after
+// another in LDS (images `img` bytes apart).  W is read once per call instead of
+// once per column.  The integer sums and float steps per column are the
+// one-column kernel's, in the same order.
+template <int Q5>
+__device__ __forceinline__ void kq_codes(const uint4& q0, const uint4& q1, const uint4& qh0, const uint4& qh1,
+                                         uint32_t (&lo)[8], uint32_t (&hi)[8]) {
+  const uint32_t ql[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const uint32_t qh[8] = {qh0.x, qh0.y, qh0.z, qh0.w, qh1.x, qh1.y, qh1.z, qh1.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    lo[k] = ql[k] & kLo4;
+    hi[k] = (ql[k] >> 4) & kLo4;
+    if constexpr (Q5 != 0) {
+      lo[k] |= (qh[k] & kOnes) << 4;
+      hi[k] |= (qh[k] & (kOnes << 1)) << 3;
+    }
+  }
+}
+
+template <int NW, int UNR, int NC, bool SUMS, int Q5>
+__global__ __launch_bounds__(NW * 64) void gemv_q4_K_cols(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * NW + wave_id();
+  const int c = lane & 3, u = lane >> 2;
+  const bool row_ok = row < n_out;
+  using F = KQuant4<Q5>;
+  const size_t rb = static_cast<size_t>(nb) * F::kBytes;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 15) >> 4;
+  const int xrow = nb * kQ8_KBytes;          // bytes of one column's Q8_K row
+  const int img = (xrow + 15) & ~15;         // its LDS image, 16-byte aligned
+
+  uint4 H[UNR], Q0[UNR], Q1[UNR], QH0[Q5 ? UNR : 1], QH1[Q5 ? UNR : 1];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = min((p0 + j) * 16 + u, nb - 1);
+      const uint8_t* p = wrow + static_cast<uint32_t>(sb * F::kBytes);
+      H[j] = *reinterpret_cast<const uint4*>(p);
+      Q0[j] = *reinterpret_cast<const uint4*>(p + F::kQs + 32 * c);
+      Q1[j] = *reinterpret_cast<const uint4*>(p + F::kQs + 16 + 32 * c);
+      if constexpr (Q5 != 0) {
+        QH0[j] = *reinterpret_cast<const uint4*>(p + 16);
+        QH1[j] = *reinterpret_cast<const uint4*>(p + 32);
+      }
+    }
+  };
+  ImageQ8K st;
+  image_load_q8K<NW * 64>(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  image_place_q8K<NW * 64>(lds, st, xq, nb);
+#pragma unroll
+  for (int col = 1; col < NC; ++col) {
+    const uint8_t* xc = xq + static_cast<uint32_t>(col * xrow);
+    ImageQ8K sc;
+    image_load_q8K<NW * 64>(sc, xc, nb);
+    image_place_q8K<NW * 64>(lds + col * img, sc, xc, nb);
+  }
+  __syncthreads();
+
+  const int sh = (c & 1) * 16;
+  const uint32_t hi_mask = (c & 2) ? 0xFFFFFFFFu : 0u;
+  float acc[NC];
+#pragma unroll
+  for (int col = 0; col < NC; ++col) acc[col] = 0.0f;
+
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = (p0 + j) * 16 + u;
+      if (!row_ok || sb >= nb) continue;  // uniform over the 4 lanes of a superblock
+      uint32_t lo[8], hi[8];
+      if constexpr (Q5 != 0) {
+        kq_codes<1>(Q0[j], Q1[j], shr4(QH0[j], 2 * c), shr4(QH1[j], 2 * c), lo, hi);
+      } else {
+        kq_codes<0>(Q0[j], Q1[j], Q0[j], Q1[j], lo, hi);
+      }
+      const uint4 h = H[j];
+      const float d = f16_to_f32(h.x & 0xFFFF), dmin = f16_to_f32(h.x >> 16);
+#pragma unroll
+      for (int col = 0; col < NC; ++col) {
+        const uint8_t* blk = lds + col * img + sb * kQ8_KBytes;
+        const uint8_t* ap = blk + 4 + 64 * c;
+        const uint4 a0 = lds_a4<uint4>(ap);
+        const uint4 a1 = lds_a4<uint4>(ap + 16);
+        const uint4 a2 = lds_a4<uint4>(ap + 32);
+        const uint4 a3 = lds_a4<uint4>(ap + 48);
+        const uint2 bsw = lds_a4<uint2>(blk + 260 + 8 * c);
+        const int2 asum = make_int2(sext16_lo(bsw.x) + sext16_hi(bsw.x), sext16_lo(bsw.y) + sext16_hi(bsw.y));
+        const float dx = lds_a4<float>(blk);
+        const uint32_t al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const uint32_t ah[8] = {a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+        int slo = 0, shi = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          slo = dot4(lo[k], al[k], slo);
+          shi = dot4(hi[k], ah[k], shi);
+        }
+        const int2 part = q4K_scale_mins(slo, shi, h, asum, hi_mask, sh);
+        const int sq = quad_sum(part.x);
+        const int sm = quad_sum(part.y);
+        const float cb = (dx * d) * static_cast<float>(sq) - (dx * dmin) * static_cast<float>(sm);
+        acc[col] += (c == 0) ? cb : 0.0f;
+        if constexpr (SUMS) {
+          if (c == 0) {
+            int32_t* o = sums + ((static_cast<size_t>(col) * n_out + row) * nb + sb) * 2;
+            o[0] = sq;
+            o[1] = sm;
+          }
+        }
+      }
+    }
+  }
+  if (row_ok) {
+#pragma unroll
+    for (int col = 0; col < NC; ++col) {
+      const float total = wave_sum(acc[col]);
+      if (lane == 0 && y != nullptr) y[static_cast<size_t>(col) * n_out + row] = total;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Q6_K x Q8_K.  Lane (u = lane >> 2, p = lane & 3 -> half h = p >> 1, k = p & 1) of
 // pass `it` handles, in superblock it*16 + u, positions l in [16k, 16k+16) of half
 // h for all four groups g: elements 128h + 32g + l, sub-blocks 8h + 2g + k.
@@ -1155,6 +1287,44 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
 // wavefronts the register-resident kernels launch (grid-strided over rows).
 constexpr int kWaves = 4;
 constexpr int kMaxWaves = 4096;
+
+bool gemv_cols_fits(int w_type, int64_t n_in, int64_t ncols) {
+  if ((w_type != kQ4_K && w_type != kQ5_K) || ncols < 2 || ncols > kGemvMaxCols) return false;
+  return ncols * align16(n_in / 256 * kQ8_KBytes) <= kMaxLdsBytes;
+}
+
+namespace {
+template <int NC, bool S, int Q5>
+hipError_t launch_cols_nc(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, float* y, int32_t* sums,
+                          hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const int64_t lds = NC * align16(static_cast<int64_t>(nb) * kQ8_KBytes);
+  const int passes = (nb + 15) / 16;
+  if (passes == 1) return launch<kWaves>(gemv_q4_K_cols<kWaves, 1, NC, S, Q5>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  if (passes == 2) return launch<kWaves>(gemv_q4_K_cols<kWaves, 2, NC, S, Q5>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  return launch<kWaves>(gemv_q4_K_cols<kWaves, 3, NC, S, Q5>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+}
+template <bool S, int Q5>
+hipError_t launch_cols_s(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, int64_t ncols, float* y,
+                         int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (ncols == 2) return launch_cols_nc<2, S, Q5>(W, n_out, nb, xq, y, sums, s, e0, e1);
+  if (ncols == 3) return launch_cols_nc<3, S, Q5>(W, n_out, nb, xq, y, sums, s, e0, e1);
+  return launch_cols_nc<4, S, Q5>(W, n_out, nb, xq, y, sums, s, e0, e1);
+}
+}  // namespace
+
+hipError_t launch_gemv_cols(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_t* xq,
+                            int64_t ncols, float* y, int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (!gemv_cols_fits(w_type, n_in, ncols)) return hipErrorInvalidValue;
+  if (n_out <= 0) return hipSuccess;
+  const int nb = static_cast<int>(n_in / 256);
+  const bool S = sums != nullptr;
+  if (w_type == kQ5_K) {
+    return S ? launch_cols_s<true, 1>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1)
+             : launch_cols_s<false, 1>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
+  }
+  return S ? launch_cols_s<true, 0>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1)
+           : launch_cols_s<false, 0>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
+}
 
 hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in,
                        const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,

@@ -284,12 +284,16 @@ def test_gemv_block_sums_and_y(torch_cuda, t):
 
 
 # Q4_K with several activation columns runs on the matrix cores (16-token tiles,
-# up to 64 columns per pass): ragged row counts, every tile count and the
-# column counts around each tile and pass boundary.
+# up to 64 columns per pass), or for 2 (3) columns on the multi-column GEMV
+# kernel: ragged row counts, every tile count and the column counts around each
+# tile, pass and kernel boundary.
 BATCHED = [(1, 256, 2), (17, 512, 16), (33, 1024, 17), (45, 4096, 33), (70, 2304, 48),
            (31, 11008, 64), (50, 768, 65), (21, 4352, 130), (129, 256, 7),
            # past the row counts that switch to 64-row workgroups, ragged
-           (8300, 256, 9), (4200, 256, 24), (4160, 256, 40)]
+           (8300, 256, 9), (4200, 256, 24), (4160, 256, 40),
+           # small batches: the multi-column GEMV kernel (2 columns; 3 up to 8192
+           # rows) and, past 8192 rows, the matrix cores at 3 columns
+           (37, 2304, 3), (8300, 256, 3), (4100, 11008, 2)]
 
 
 @pytest.mark.parametrize("n_out,n_in,ncols", BATCHED)
