@@ -637,6 +637,120 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Q6_K x Q8_K for NC = 2..4 activation columns: the kernel above with each
+// superblock's 6-bit codes and signed scales built once and dotted against every
+// column's Q8_K row, the rows staged one after another in LDS (`img` bytes
+// apart) as in gemv_q4_K_cols.  Integer sums and float steps per column are the
+// one-column kernel's, in the same order.
+template <int NW, int UNR, int NC, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q6_K_cols(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * NW + wave_id();
+  const int pos = lane & 3, u = lane >> 2;
+  const int hh = pos >> 1, kk = pos & 1;
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kQ6_KBytes;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 15) >> 4;
+  const int xrow = nb * kQ8_KBytes;
+  const int img = (xrow + 15) & ~15;
+
+  uint4 A[UNR], B[UNR], QH[UNR];
+  uint2 SC[UNR];
+  uint32_t D[UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = min((p0 + j) * 16 + u, nb - 1);
+      const uint8_t* p = wrow + static_cast<uint32_t>(sb * kQ6_KBytes);
+      A[j] = load_u2<uint4>(p + 64 * hh + 16 * kk);
+      B[j] = load_u2<uint4>(p + 64 * hh + 32 + 16 * kk);
+      QH[j] = load_u2<uint4>(p + 128 + 32 * hh + 16 * kk);
+      SC[j] = load_u2<uint2>(p + 192 + 8 * hh);
+      D[j] = *reinterpret_cast<const uint16_t*>(p + 208);
+    }
+  };
+  ImageQ8K st;
+  image_load_q8K<NW * 64>(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  image_place_q8K<NW * 64>(lds, st, xq, nb);
+#pragma unroll
+  for (int col = 1; col < NC; ++col) {
+    const uint8_t* xc = xq + static_cast<uint32_t>(col * xrow);
+    ImageQ8K sc;
+    image_load_q8K<NW * 64>(sc, xc, nb);
+    image_place_q8K<NW * 64>(lds + col * img, sc, xc, nb);
+  }
+  __syncthreads();
+
+  float acc[NC];
+#pragma unroll
+  for (int col = 0; col < NC; ++col) acc[col] = 0.0f;
+
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = (p0 + j) * 16 + u;
+      if (!row_ok || sb >= nb) continue;
+      const uint32_t al[4] = {A[j].x, A[j].y, A[j].z, A[j].w};
+      const uint32_t bl[4] = {B[j].x, B[j].y, B[j].z, B[j].w};
+      const uint32_t hl[4] = {QH[j].x, QH[j].y, QH[j].z, QH[j].w};
+      uint32_t q[4][4];  // q[g][i]: codes of group g, dword i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q[0][i] = (al[i] & kLo4) | ((hl[i] << 4) & kHi2);
+        q[1][i] = (bl[i] & kLo4) | ((hl[i] << 2) & kHi2);
+        q[2][i] = ((al[i] >> 4) & kLo4) | (hl[i] & kHi2);
+        q[3][i] = ((bl[i] >> 4) & kLo4) | ((hl[i] >> 2) & kHi2);
+      }
+      const int sc0 = static_cast<int8_t>((SC[j].x >> (8 * kk)) & 0xFF);
+      const int sc1 = static_cast<int8_t>((SC[j].x >> (16 + 8 * kk)) & 0xFF);
+      const int sc2 = static_cast<int8_t>((SC[j].y >> (8 * kk)) & 0xFF);
+      const int sc3 = static_cast<int8_t>((SC[j].y >> (16 + 8 * kk)) & 0xFF);
+      const float d = f16_to_f32(D[j]);
+#pragma unroll
+      for (int col = 0; col < NC; ++col) {
+        const uint8_t* blk = lds + col * img + sb * kQ8_KBytes;
+        int sg[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint4 a = lds_a4<uint4>(blk + 4 + 128 * hh + 32 * g + 16 * kk);
+          sg[g] = dot4(q[g][0], a.x, sg[g]);
+          sg[g] = dot4(q[g][1], a.y, sg[g]);
+          sg[g] = dot4(q[g][2], a.z, sg[g]);
+          sg[g] = dot4(q[g][3], a.w, sg[g]);
+        }
+        const uint4 bw = lds_a4<uint4>(blk + 260 + 16 * hh);  // bsums 8h .. 8h+7
+        const int b0 = 32 * (kk ? sext16_hi(bw.x) : sext16_lo(bw.x));
+        const int b1 = 32 * (kk ? sext16_hi(bw.y) : sext16_lo(bw.y));
+        const int b2 = 32 * (kk ? sext16_hi(bw.z) : sext16_lo(bw.z));
+        const int b3 = 32 * (kk ? sext16_hi(bw.w) : sext16_lo(bw.w));
+        const float dx = lds_a4<float>(blk);
+        const int part = mad24(sc0, sg[0] - b0, mad24(sc1, sg[1] - b1, mad24(sc2, sg[2] - b2, __mul24(sc3, sg[3] - b3))));
+        const int S = quad_sum(part);
+        if (pos == 0) {
+          acc[col] += (dx * d) * static_cast<float>(S);
+          if constexpr (SUMS) sums[(static_cast<size_t>(col) * n_out + row) * nb + sb] = S;
+        }
+      }
+    }
+  }
+  if (row_ok) {
+#pragma unroll
+    for (int col = 0; col < NC; ++col) {
+      const float total = wave_sum(acc[col]);
+      if (lane == 0 && y != nullptr) y[static_cast<size_t>(col) * n_out + row] = total;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Q8_0 x Q8_0 and Q4_0 x Q8_0: lane b of pass `it` handles block it*64 + lane.
 template <int NW, int UNR, bool SUMS>
 __global__ __launch_bounds__(NW * 64) void gemv_q8_0_kernel(
@@ -1289,26 +1403,33 @@ constexpr int kWaves = 4;
 constexpr int kMaxWaves = 4096;
 
 bool gemv_cols_fits(int w_type, int64_t n_in, int64_t ncols) {
-  if ((w_type != kQ4_K && w_type != kQ5_K) || ncols < 2 || ncols > kGemvMaxCols) return false;
+  if ((w_type != kQ4_K && w_type != kQ5_K && w_type != kQ6_K) || ncols < 2 || ncols > kGemvMaxCols) return false;
   return ncols * align16(n_in / 256 * kQ8_KBytes) <= kMaxLdsBytes;
 }
 
 namespace {
-template <int NC, bool S, int Q5>
+// FMT: 0 Q4_K, 1 Q5_K, 2 Q6_K.
+template <int NC, bool S, int FMT>
 hipError_t launch_cols_nc(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, float* y, int32_t* sums,
                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t lds = NC * align16(static_cast<int64_t>(nb) * kQ8_KBytes);
   const int passes = (nb + 15) / 16;
-  if (passes == 1) return launch<kWaves>(gemv_q4_K_cols<kWaves, 1, NC, S, Q5>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
-  if (passes == 2) return launch<kWaves>(gemv_q4_K_cols<kWaves, 2, NC, S, Q5>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
-  return launch<kWaves>(gemv_q4_K_cols<kWaves, 3, NC, S, Q5>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  if constexpr (FMT == 2) {
+    if (passes == 1) return launch<kWaves>(gemv_q6_K_cols<kWaves, 1, NC, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    if (passes == 2) return launch<kWaves>(gemv_q6_K_cols<kWaves, 2, NC, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    return launch<kWaves>(gemv_q6_K_cols<kWaves, 3, NC, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  } else {
+    if (passes == 1) return launch<kWaves>(gemv_q4_K_cols<kWaves, 1, NC, S, FMT>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    if (passes == 2) return launch<kWaves>(gemv_q4_K_cols<kWaves, 2, NC, S, FMT>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+    return launch<kWaves>(gemv_q4_K_cols<kWaves, 3, NC, S, FMT>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  }
 }
-template <bool S, int Q5>
+template <bool S, int FMT>
 hipError_t launch_cols_s(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, int64_t ncols, float* y,
                          int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (ncols == 2) return launch_cols_nc<2, S, Q5>(W, n_out, nb, xq, y, sums, s, e0, e1);
-  if (ncols == 3) return launch_cols_nc<3, S, Q5>(W, n_out, nb, xq, y, sums, s, e0, e1);
-  return launch_cols_nc<4, S, Q5>(W, n_out, nb, xq, y, sums, s, e0, e1);
+  if (ncols == 2) return launch_cols_nc<2, S, FMT>(W, n_out, nb, xq, y, sums, s, e0, e1);
+  if (ncols == 3) return launch_cols_nc<3, S, FMT>(W, n_out, nb, xq, y, sums, s, e0, e1);
+  return launch_cols_nc<4, S, FMT>(W, n_out, nb, xq, y, sums, s, e0, e1);
 }
 }  // namespace
 
@@ -1321,6 +1442,10 @@ hipError_t launch_gemv_cols(int w_type, const uint8_t* W, int64_t n_out, int64_t
   if (w_type == kQ5_K) {
     return S ? launch_cols_s<true, 1>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1)
              : launch_cols_s<false, 1>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
+  }
+  if (w_type == kQ6_K) {
+    return S ? launch_cols_s<true, 2>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1)
+             : launch_cols_s<false, 2>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
   }
   return S ? launch_cols_s<true, 0>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1)
            : launch_cols_s<false, 0>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);

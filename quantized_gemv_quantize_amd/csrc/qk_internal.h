@@ -37,7 +37,7 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
                        const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,
                        hipEvent_t ev_start, hipEvent_t ev_stop);
 
-// Q4_K / Q5_K x Q8_K over 2..kGemvMaxCols activation columns with the weights read
+// Q4_K / Q5_K / Q6_K x Q8_K over 2..kGemvMaxCols activation columns with the weights read
 // once (the one-column kernels' arithmetic per column; the columns' Q8_K rows are
 // staged together in LDS).  gemv_cols_fits says whether a shape qualifies.
 constexpr int64_t kGemvMaxCols = 4;
