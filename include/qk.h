@@ -151,7 +151,7 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
  * one f32 step with the block scales; y is the f32 sum of those steps.  The
  * summation order differs from a sequential loop, so y matches a sequential f32
  * evaluation to within rounding, not bit for bit.  Several columns: Q4_K at 2
- * columns (3 up to 8192 rows), Q5_K and Q6_K in groups of up to 4 columns run a GEMV
+ * columns (3 up to 8192 rows), every other format in groups of up to 4 columns run a GEMV
  * kernel that reads W once for all its columns (each column's arithmetic as the
  * one-column kernel's); Q4_K otherwise runs on the int8 matrix cores, up to 64
  * columns per launch (same per-block integers, y equal to within rounding); every

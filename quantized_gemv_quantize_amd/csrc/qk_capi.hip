@@ -58,11 +58,12 @@ int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void
   // Small batches read W once with the multi-column GEMV kernel: Q4_K at 2 columns,
   // and at 3 when the matrix has at most 8192 rows (beyond, and from 4 columns, the
   // matrix-core kernel is faster: 14336 x 4096 at 3 columns 13.7 against 15.9 us);
-  // Q5_K and Q6_K, which have no matrix-core path, in groups of up to 4 columns.
+  // every other format, which has no matrix-core path, in groups of up to 4 columns.
   const bool small_q4K = w_type == QK_TYPE_Q4_K && (ncols == 2 || (ncols == 3 && n_out <= 8192));
   int64_t group = qk::kGemvMaxCols;  // columns per launch: as many as the LDS holds
   while (group > 1 && !qk::gemv_cols_fits(w_type, n_in, group)) --group;
-  if ((small_q4K || ((w_type == QK_TYPE_Q5_K || w_type == QK_TYPE_Q6_K) && ncols > 1)) && group > 1) {
+  const bool gemv_only = w_type != QK_TYPE_Q4_K;  // formats with no matrix-core path
+  if ((small_q4K || (gemv_only && ncols > 1)) && group > 1) {
     for (int64_t c = 0; c < ncols; c += group) {
       const int64_t nc = (ncols - c < group) ? ncols - c : group;
       const uint8_t* xc = static_cast<const uint8_t*>(xq) + c * xrow;

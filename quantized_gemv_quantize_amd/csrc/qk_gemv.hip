@@ -902,6 +902,115 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_0_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Q8_0, Q4_0 and Q5_0 x Q8_0 for NC = 2..4 activation columns: the LDS kernels
+// above with the NC Q8_0 rows staged one after another (LayoutQ80 regions
+// `L.bytes` apart) and each weight block loaded once.  The lane turns its block's
+// codes into signed bytes once (Q4_0 / Q5_0: the stored value + bias minus the
+// bias, per byte without borrows since every byte is at least 0x80 after the OR),
+// then takes 8 dot4 per column: s = sum (q - bias) a, the same integer as the
+// one-column kernels' sum q a - bias sum a.  FMT: 0 Q8_0, 1 Q4_0, 2 Q5_0.
+template <int NW, int UNR, int NC, int FMT, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q80_cols(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  constexpr int kWB = FMT == 0 ? kQ8_0Bytes : FMT == 1 ? kQ4_0Bytes : kQ5_0Bytes;
+  constexpr int kQs = FMT == 2 ? 6 : 2;             // offset of the code bytes
+  constexpr uint32_t kBias4 = FMT == 2 ? 0x10101010u : 0x08080808u;
+  constexpr int kN = FMT == 0 ? 8 : 4;              // dwords of code bytes
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * NW + wave_id();
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kWB;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 63) >> 6;
+  const int xrow = nb * kQ8_0Bytes;
+
+  ShiftedField<kN> QS[UNR];
+  uint32_t D[UNR], QH[UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = min((p0 + j) * 64 + lane, nb - 1);
+      const uint8_t* p = wrow + static_cast<uint32_t>(b * kWB);
+      D[j] = *reinterpret_cast<const uint16_t*>(p);
+      if constexpr (FMT == 2) QH[j] = load_u2<uint32_t>(p + 2);
+      QS[j] = load_field<kN>(p + kQs);
+    }
+  };
+  const LayoutQ80 L(nb);
+  StagedQ80 st;
+  stage_load_q80<NW * 64>(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  stage_place_q80<NW * 64>(lds, L, st, xq, nb);
+#pragma unroll
+  for (int col = 1; col < NC; ++col) {
+    const uint8_t* xc = xq + static_cast<uint32_t>(col * xrow);
+    StagedQ80 sc;
+    stage_load_q80<NW * 64>(sc, xc, nb);
+    stage_place_q80<NW * 64>(lds + col * L.bytes, L, sc, xc, nb);
+  }
+  __syncthreads();
+
+  float acc[NC];
+#pragma unroll
+  for (int col = 0; col < NC; ++col) acc[col] = 0.0f;
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = (p0 + j) * 64 + lane;
+      if (!row_ok || b >= nb) continue;
+      uint32_t q[8];  // signed codes of elements 4i .. 4i+3
+      if constexpr (FMT == 0) {
+        align_field(QS[j], q);
+      } else {
+        uint32_t w[4];
+        align_field(QS[j], w);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          uint32_t lo = w[k] & kLo4, hi = (w[k] >> 4) & kLo4;
+          if constexpr (FMT == 2) {
+            lo = q5_codes(lo, QH[j], 4 * k);
+            hi = q5_codes(hi, QH[j], 16 + 4 * k);
+          }
+          q[k] = ((lo | 0x80808080u) - kBias4) ^ 0x80808080u;
+          q[4 + k] = ((hi | 0x80808080u) - kBias4) ^ 0x80808080u;
+        }
+      }
+      const float d = f16_to_f32(D[j]);
+#pragma unroll
+      for (int col = 0; col < NC; ++col) {
+        const uint8_t* base = lds + col * L.bytes;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(base + b * LayoutQ80::kStride);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(base + b * LayoutQ80::kStride + 16);
+        const float dx = reinterpret_cast<const float*>(base + L.off_d)[b];
+        int sv = 0;
+        sv = dot4(q[0], a0.x, sv);
+        sv = dot4(q[1], a0.y, sv);
+        sv = dot4(q[2], a0.z, sv);
+        sv = dot4(q[3], a0.w, sv);
+        sv = dot4(q[4], a1.x, sv);
+        sv = dot4(q[5], a1.y, sv);
+        sv = dot4(q[6], a1.z, sv);
+        sv = dot4(q[7], a1.w, sv);
+        acc[col] += static_cast<float>(sv) * (d * dx);
+        if constexpr (SUMS) sums[(static_cast<size_t>(col) * n_out + row) * nb + b] = sv;
+      }
+    }
+  }
+  if (row_ok) {
+#pragma unroll
+    for (int col = 0; col < NC; ++col) {
+      const float total = wave_sum(acc[col]);
+      if (lane == 0 && y != nullptr) y[static_cast<size_t>(col) * n_out + row] = total;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Register-resident activations.  Each lane loads, once per wavefront, the
 // activation codes, sums and scale of the blocks it covers in every pass of a
 // row, then the wavefront walks its rows (RPW at a time, strided by the grid)
@@ -1403,11 +1512,31 @@ constexpr int kWaves = 4;
 constexpr int kMaxWaves = 4096;
 
 bool gemv_cols_fits(int w_type, int64_t n_in, int64_t ncols) {
-  if ((w_type != kQ4_K && w_type != kQ5_K && w_type != kQ6_K) || ncols < 2 || ncols > kGemvMaxCols) return false;
+  if (ncols < 2 || ncols > kGemvMaxCols) return false;
+  if (w_type == kQ8_0 || w_type == kQ4_0 || w_type == kQ5_0) return ncols * LayoutQ80(n_in / 32).bytes <= kMaxLdsBytes;
+  if (w_type != kQ4_K && w_type != kQ5_K && w_type != kQ6_K) return false;
   return ncols * align16(n_in / 256 * kQ8_KBytes) <= kMaxLdsBytes;
 }
 
 namespace {
+// FMT: 0 Q8_0, 1 Q4_0, 2 Q5_0.
+template <int NC, bool S, int FMT>
+hipError_t launch_q80_cols_nc(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, float* y,
+                              int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const int64_t lds = NC * LayoutQ80(nb).bytes;
+  const int passes = (nb + 63) / 64;
+  if (passes == 1) return launch<kWaves>(gemv_q80_cols<kWaves, 1, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  if (passes == 2) return launch<kWaves>(gemv_q80_cols<kWaves, 2, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  return launch<kWaves>(gemv_q80_cols<kWaves, 4, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+}
+template <bool S, int FMT>
+hipError_t launch_q80_cols_s(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, int64_t ncols, float* y,
+                             int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (ncols == 2) return launch_q80_cols_nc<2, S, FMT>(W, n_out, nb, xq, y, sums, s, e0, e1);
+  if (ncols == 3) return launch_q80_cols_nc<3, S, FMT>(W, n_out, nb, xq, y, sums, s, e0, e1);
+  return launch_q80_cols_nc<4, S, FMT>(W, n_out, nb, xq, y, sums, s, e0, e1);
+}
+
 // FMT: 0 Q4_K, 1 Q5_K, 2 Q6_K.
 template <int NC, bool S, int FMT>
 hipError_t launch_cols_nc(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, float* y, int32_t* sums,
@@ -1437,8 +1566,18 @@ hipError_t launch_gemv_cols(int w_type, const uint8_t* W, int64_t n_out, int64_t
                             int64_t ncols, float* y, int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (!gemv_cols_fits(w_type, n_in, ncols)) return hipErrorInvalidValue;
   if (n_out <= 0) return hipSuccess;
-  const int nb = static_cast<int>(n_in / 256);
   const bool S = sums != nullptr;
+  if (w_type == kQ8_0 || w_type == kQ4_0 || w_type == kQ5_0) {
+    const int nb32 = static_cast<int>(n_in / 32);
+    const int f = w_type == kQ8_0 ? 0 : w_type == kQ4_0 ? 1 : 2;
+    if (f == 0) return S ? launch_q80_cols_s<true, 0>(W, n_out, nb32, xq, ncols, y, sums, s, e0, e1)
+                         : launch_q80_cols_s<false, 0>(W, n_out, nb32, xq, ncols, y, sums, s, e0, e1);
+    if (f == 1) return S ? launch_q80_cols_s<true, 1>(W, n_out, nb32, xq, ncols, y, sums, s, e0, e1)
+                         : launch_q80_cols_s<false, 1>(W, n_out, nb32, xq, ncols, y, sums, s, e0, e1);
+    return S ? launch_q80_cols_s<true, 2>(W, n_out, nb32, xq, ncols, y, sums, s, e0, e1)
+             : launch_q80_cols_s<false, 2>(W, n_out, nb32, xq, ncols, y, sums, s, e0, e1);
+  }
+  const int nb = static_cast<int>(n_in / 256);
   if (w_type == kQ5_K) {
     return S ? launch_cols_s<true, 1>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1)
              : launch_cols_s<false, 1>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);

@@ -37,9 +37,10 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
                        const uint8_t* xq, float* y, int32_t* sums, hipStream_t s,
                        hipEvent_t ev_start, hipEvent_t ev_stop);
 
-// Q4_K / Q5_K / Q6_K x Q8_K over 2..kGemvMaxCols activation columns with the weights read
-// once (the one-column kernels' arithmetic per column; the columns' Q8_K rows are
-// staged together in LDS).  gemv_cols_fits says whether a shape qualifies.
+// Q8_0 / Q4_0 / Q5_0 x Q8_0 and Q4_K / Q5_K / Q6_K x Q8_K over 2..kGemvMaxCols
+// activation columns with the weights read once (the one-column kernels' integer
+// sums per column; the columns' activation rows are staged together in LDS).
+// gemv_cols_fits says whether a shape qualifies.
 constexpr int64_t kGemvMaxCols = 4;
 bool gemv_cols_fits(int w_type, int64_t n_in, int64_t ncols);
 hipError_t launch_gemv_cols(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_t* xq,

@@ -481,7 +481,7 @@ def test_graph_capture_replays_match_eager(torch_cuda):
     rng = np.random.default_rng(9)
     cases = [(T4K, 64, 11008, 1), (T4K, 300, 4096, 1), (T6K, 70, 4096, 1), (T8_0, 50, 4096, 1),
              (T4_0, 33, 1024, 1), (T5_0, 41, 4096, 1), (T4K, 200, 4096, 16),
-             (T4K, 90, 2048, 64), (T5K, 57, 11008, 1), (T5K, 40, 4096, 3), (T6K, 48, 4096, 4)]
+             (T4K, 90, 2048, 64), (T5K, 57, 11008, 1), (T5K, 40, 4096, 3), (T6K, 48, 4096, 4), (T5_0, 36, 2048, 3)]
     bufs = []
     for t, n_out, n_in, nc in cases:
         W = dev(torch, weights(rng, t, n_out, n_in))
@@ -735,23 +735,24 @@ def test_q5_K_extreme_codes(torch_cuda):
         assert_y(y, y_o, l1, "Q5_K extreme codes")
 
 
-# Q5_K and Q6_K with several columns: the multi-column GEMV kernel in groups of up
-# to 4 columns (fewer where the rows are too long for 4 activation rows in LDS:
-# 2 at 28672), a ragged last group, one to seven passes per row and the rows past
-# one workgroup.
+# Q8_0, Q4_0, Q5_0, Q5_K and Q6_K with several columns: the multi-column GEMV
+# kernels in groups of up to 4 columns (fewer where the rows are too long for 4
+# activation rows in LDS: Q8_K rows of 28672 take 2; Q8_0 rows of 11008 take 3, of
+# 14336 2, and of 28672 run one column per launch), a ragged last group, one to
+# fourteen passes per row and the rows past one workgroup.
 SMALL_BATCH = [(37, 2304, 2), (129, 4096, 4), (8300, 256, 5), (45, 11008, 9),
                (3, 28672, 3), (50, 768, 7), (70, 14336, 4)]
 
 
-@pytest.mark.parametrize("t", [T5K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T5K, T6K])
 @pytest.mark.parametrize("n_out,n_in,ncols", SMALL_BATCH)
-def test_small_batch_q5_K_q6_K(torch_cuda, t, n_out, n_in, ncols):
+def test_small_batch_gemv_kernels(torch_cuda, t, n_out, n_in, ncols):
     say("small batch", t, n_out, n_in, ncols)
     rng = np.random.default_rng(n_out * 11 + ncols + t)
     W = weights(rng, t, n_out, n_in)
     X = rng.standard_normal((ncols, n_in)).astype(np.float32)
     X[ncols // 2] = 0.0                      # an all-zero column: d = 0, codes 0
-    xq = orc.quantize(T8K, X)
+    xq = orc.quantize(orc.act_type(t), X)
     Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
     sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xd, ncols))
     want = _oracle_sums(t, W, xq, n_out, n_in, ncols).reshape(sums.shape)
@@ -760,6 +761,38 @@ def test_small_batch_q5_K_q6_K(torch_cuda, t, n_out, n_in, ncols):
     y_o, l1 = orc.gemv(t, W, n_out, n_in, xq, ncols)
     assert_y(y, y_o, l1, f"small batch type {t} {n_out}x{n_in} ncols {ncols}")
     assert not y[ncols // 2].any()
+
+
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0])
+def test_q80_family_extreme_codes(torch_cuda, t):
+    # the ends of each code range (Q8_0 -128 / +127, Q4_0 -8 / +7, Q5_0 -16 / +15)
+    # against activations of +-127, one to four columns: the largest block sums
+    # the 32-element formats can produce, and the signed-byte conversion of the
+    # multi-column kernel at both ends.
+    rng = np.random.default_rng(57)
+    n_out, n_in = 21, 4096
+    bb = {T8_0: 34, T4_0: 18, T5_0: 22}[t]
+    W = weights(rng, t, n_out, n_in).reshape(n_out, -1, bb).copy()
+    if t == T8_0:
+        W[0::2, :, 2:] = 0x80
+        W[1::2, :, 2:] = 0x7F
+    else:
+        W[0::2, :, 2:] = 0xFF                # Q5_0: qh set too, code 31
+        W[1::2, :, 2:] = 0x00
+    W = W.reshape(n_out, -1)
+    X = np.where(rng.random((4, n_in)) < 0.5, 127.0, -127.0).astype(np.float32)
+    X[1] = 127.0
+    X[2] = -127.0
+    xq = orc.quantize(orc.Q8_0, X)
+    Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+    for ncols in (1, 2, 3, 4):
+        say("extreme codes", t, ncols)
+        sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xd, ncols))
+        want = _oracle_sums(t, W, xq, n_out, n_in, ncols).reshape(sums.shape)
+        assert np.array_equal(sums, want)
+        y = host(qk.qk_gemv(t, Wd, n_out, n_in, xd, ncols))
+        y_o, l1 = orc.gemv(t, W, n_out, n_in, xq, ncols)
+        assert_y(y, y_o, l1, f"type {t} extreme codes")
 
 
 def test_q6_K_extreme_codes(torch_cuda):
