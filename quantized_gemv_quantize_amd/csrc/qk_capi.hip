@@ -64,8 +64,12 @@ int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void
   while (group > 1 && !qk::gemv_cols_fits(w_type, n_in, group)) --group;
   const bool gemv_only = w_type != QK_TYPE_Q4_K;  // formats with no matrix-core path
   if ((small_q4K || (gemv_only && ncols > 1)) && group > 1) {
-    for (int64_t c = 0; c < ncols; c += group) {
-      const int64_t nc = (ncols - c < group) ? ncols - c : group;
+    // as few launches as the group size allows, their sizes balanced (4 columns that
+    // take at most 3 per launch run as 2 + 2, not 3 + 1: Q4_0 4096 x 11008 21.6
+    // against 22.8 us)
+    const int64_t launches = (ncols + group - 1) / group;
+    for (int64_t c = 0, i = 0; c < ncols; c += ncols / launches + (i < ncols % launches), ++i) {
+      const int64_t nc = ncols / launches + (i < ncols % launches ? 1 : 0);
       const uint8_t* xc = static_cast<const uint8_t*>(xq) + c * xrow;
       float* yc = y ? y + c * n_out : nullptr;
       int32_t* sc = sums ? sums + c * n_out * nb * k : nullptr;
