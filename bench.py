@@ -443,6 +443,95 @@ def summarize_pmc(fdir, wdir, workload):
     print(f"traffic_over_algorithmic: {(fetch + write) / alg:.4f}")
 
 
+# Read-probe variants of the sweep: (kilobytes per wavefront, persistent grid
+# workgroups or 0 for one wavefront per group, non-temporal loads)
+SWEEP_VARIANTS = [(2, 0, 0), (1, 0, 0), (4, 0, 0), (8, 0, 0), (16, 0, 0), (2, 0, 1), (8, 0, 1),
+                  (2, 256, 0), (2, 512, 0), (2, 1024, 0), (2, 2048, 0), (8, 256, 0), (8, 1024, 0),
+                  (16, 256, 0), (16, 512, 0)]
+SWEEP_SIZES = [4_194_304, 8_388_608, 16_777_216, 25_362_432, 33_030_144, 67_108_864, 134_217_728,
+               268_435_456, 536_870_912]
+
+
+def read_sweep(steps, warmup):
+    """Read-only launches of growing size and every probe load pattern: per launch
+    the kernel time from events the launch records itself (launches back to back
+    behind a stream hold, each reading a different copy out of a 2 GiB pool, so no
+    launch finds its bytes in the 256 MB Infinity Cache), then a least-squares fit
+    t = t0 + bytes / BW per pattern over the sizes of 8 MB and up."""
+    import torch
+
+    import quantized_gemv_quantize_amd as qk
+    torch.cuda.set_device(0)
+    pool_bytes = 2 << 30
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    for off in range(0, pool_bytes, 256 << 20):
+        pool[off:off + (256 << 20)].random_(0, 256, generator=gen)
+    outs = torch.empty((pool_bytes // 1024,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(s0.elapsed_time(s1), 1e-3)
+    results = {}
+    for size in SWEEP_SIZES:
+        copies = pool_bytes // size
+        for var in SWEEP_VARIANTS:
+            kb, grid, nt = var
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                e1.record(stream)
+            for k in range(warmup):
+                src = pool[(k % copies) * size:]
+                qk.qk_read_probe_ex(src, size, kb, grid, nt, out=outs)
+            torch.cuda.synchronize()
+            hold = torch.cuda.Event()
+            torch.cuda._sleep(int(cycles_per_ms * (0.05 * steps + 20.0)))
+            hold.record(stream)
+            for k in range(steps):
+                src = pool[((warmup + k) % copies) * size:]
+                qk.qk_read_probe_ex(src, size, kb, grid, nt, out=outs, ev_start=ev[k][0], ev_stop=ev[k][1])
+            held = not hold.query()
+            torch.cuda.synchronize()
+            us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+            results[(size, var)] = (float(np.median(us)), float(np.mean(us)), held)
+        best = min(SWEEP_VARIANTS, key=lambda v: results[(size, v)][0])
+        log(f"[sweep] {size / 1e6:8.2f} MB: best {best} {results[(size, best)][0]:.3f} us "
+            f"({size / results[(size, best)][0] / 1e3 / HBM_PEAK_GBS:.3f} of peak)")
+
+    def name(v):
+        kb, grid, nt = v
+        return f"{kb:2d} KB/wave, " + (f"grid {grid:4d}" if grid else "grid all ") + (", nt" if nt else "    ")
+
+    print("read-only probe launches: median kernel time (us) / fraction of the 8 TB/s HBM peak")
+    print(f"  {'pattern':28s}" + "".join(f"{s / 1e6:>13.1f}" for s in SWEEP_SIZES) + "   fit t0 (us)  BW (GB/s)")
+    fits = {}
+    for v in SWEEP_VARIANTS:
+        xs = np.array([s for s in SWEEP_SIZES if s >= 8_000_000], dtype=np.float64)
+        ts = np.array([results[(s, v)][0] for s in xs.astype(np.int64)])
+        A = np.stack([np.ones_like(xs), xs], axis=1)
+        (t0, inv_bw), *_ = np.linalg.lstsq(A, ts, rcond=None)
+        fits[v] = (float(t0), float(1e-3 / inv_bw))  # GB/s
+        cells = "".join(f"{results[(s, v)][0]:7.2f}/{s / results[(s, v)][0] / 1e3 / HBM_PEAK_GBS:.2f}"
+                        for s in SWEEP_SIZES)
+        print(f"  {name(v):28s}{cells}   {fits[v][0]:8.3f}  {fits[v][1]:9.1f}")
+    held_all = all(r[2] for r in results.values())
+    print(f"all timed launches queued behind the stream hold: {held_all}")
+    print("best pattern per size, and the fitted line's time and fraction at that size:")
+    for s in SWEEP_SIZES:
+        best = min(SWEEP_VARIANTS, key=lambda v: results[(s, v)][0])
+        t_best = results[(s, best)][0]
+        bfit = min(SWEEP_VARIANTS, key=lambda v: fits[v][0] + s / (fits[v][1] * 1e3))
+        t_fit = fits[bfit][0] + s / (fits[bfit][1] * 1e3)
+        print(f"  {s:>11d} B: {name(best)} {t_best:8.3f} us = {s / t_best / 1e3 / HBM_PEAK_GBS:.3f} of peak; "
+              f"fitted line {t_fit:8.3f} us = {s / t_fit / 1e3 / HBM_PEAK_GBS:.3f} ({name(bfit)})")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,12 +544,17 @@ def main():
                     help="also run a plain 256 MiB read + write kernel (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="time read-only probe launches over sizes and load patterns (no workload)")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return
+    if args.read_sweep:
+        read_sweep(args.steps, args.warmup)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

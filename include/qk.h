@@ -255,6 +255,24 @@ int qk_gemv_pair_timed(int w_type, const void* W1, const void* W2, int64_t n_out
 int qk_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream, void* ev_start,
                   void* ev_stop);
 
+/*
+ * qk_read_probe_ex - qk_read_probe with its load pattern as arguments, so a sweep
+ * can look for the fastest way one launch reads a given number of bytes.
+ *   kb_per_wave   1, 2, 4, 8 or 16: each wavefront reads one group of that many
+ *                 kilobytes (kb_per_wave 16-byte loads per lane, all issued before
+ *                 any use); out word g is the XOR of the 32-bit words of group g,
+ *                 out holds ceil(bytes / (1024 kb_per_wave)) words.
+ *   grid_blocks   0: one wavefront per group (qk_read_probe); > 0: a persistent grid
+ *                 of that many 256-thread workgroups (at most one per four groups)
+ *                 whose wavefronts stride over the groups.
+ *   nontemporal   0: plain loads; 1: non-temporal (streaming) loads.
+ * QK_E_ARG for any other kb_per_wave, a negative grid_blocks or another
+ * nontemporal value; otherwise as qk_read_probe (qk_read_probe is this call with
+ * 2, 0, 0).
+ */
+int qk_read_probe_ex(const void* src, int64_t bytes, uint32_t* out, int kb_per_wave, int64_t grid_blocks,
+                     int nontemporal, void* stream, void* ev_start, void* ev_stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,8 @@ def lib():
         L.qk_gemv_pair_timed.argtypes = [i32, p, p, i64, i64, p, i64, i32, p, p, p, p]
         L.qk_read_probe.restype = i32
         L.qk_read_probe.argtypes = [p, i64, p, p, p, p]
+        L.qk_read_probe_ex.restype = i32
+        L.qk_read_probe_ex.argtypes = [p, i64, p, i32, i64, i32, p, p, p]
         _lib = L
     return _lib
 
@@ -238,4 +240,19 @@ def qk_read_probe(src, nbytes, out=None, ev_start=None, ev_stop=None, stream=Non
     e1 = ctypes.c_void_p(ev_stop.cuda_event) if ev_stop is not None else None
     _check(lib().qk_read_probe(_ptr(src), nbytes, _ptr(out), _stream(stream), e0, e1),
            "qk_read_probe")
+    return out
+
+
+def qk_read_probe_ex(src, nbytes, kb_per_wave=2, grid_blocks=0, nontemporal=0, out=None, ev_start=None,
+                     ev_stop=None, stream=None):
+    """qk_read_probe with its load pattern as arguments: returns out, uint32
+    [ceil(nbytes / (1024 kb_per_wave))], the XOR of each group's 32-bit words."""
+    import torch
+    gb = 1024 * kb_per_wave
+    if out is None:
+        out = torch.empty(((max(nbytes, 0) + gb - 1) // gb,), dtype=torch.int32, device=src.device)
+    e0 = ctypes.c_void_p(ev_start.cuda_event) if ev_start is not None else None
+    e1 = ctypes.c_void_p(ev_stop.cuda_event) if ev_stop is not None else None
+    _check(lib().qk_read_probe_ex(_ptr(src), nbytes, _ptr(out), kb_per_wave, grid_blocks, nontemporal,
+                                  _stream(stream), e0, e1), "qk_read_probe_ex")
     return out

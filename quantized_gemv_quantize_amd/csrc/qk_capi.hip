@@ -274,15 +274,21 @@ int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* st
                                          static_cast<hipStream_t>(stream)));
 }
 
-int qk_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream, void* ev_start,
-                  void* ev_stop) {
+int qk_read_probe_ex(const void* src, int64_t bytes, uint32_t* out, int kb_per_wave, int64_t grid_blocks,
+                     int nontemporal, void* stream, void* ev_start, void* ev_stop) {
+  if (!qk::read_probe_kb_ok(kb_per_wave) || grid_blocks < 0 || (nontemporal != 0 && nontemporal != 1))
+    return QK_E_ARG;
   if (bytes <= 0 || bytes % 16 != 0) return QK_E_SHAPE;
   if (src == nullptr || out == nullptr) return QK_E_NULL;
   if (!aligned16(src) || !aligned16(out)) return QK_E_ALIGN;
-  return status_of(qk::launch_read_probe(static_cast<const uint8_t*>(src), bytes, out,
-                                         static_cast<hipStream_t>(stream),
-                                         static_cast<hipEvent_t>(ev_start),
-                                         static_cast<hipEvent_t>(ev_stop)));
+  return status_of(qk::launch_read_probe(static_cast<const uint8_t*>(src), bytes, out, kb_per_wave, grid_blocks,
+                                         nontemporal, static_cast<hipStream_t>(stream),
+                                         static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)));
+}
+
+int qk_read_probe(const void* src, int64_t bytes, uint32_t* out, void* stream, void* ev_start,
+                  void* ev_stop) {
+  return qk_read_probe_ex(src, bytes, out, 2, 0, 0, stream, ev_start, ev_stop);
 }
 
 }  // extern "C"

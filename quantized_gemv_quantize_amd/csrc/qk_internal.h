@@ -69,9 +69,12 @@ constexpr int64_t kMaxLdsBytes = 65536;
 hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t nblocks,
                              hipStream_t s);
 
-// Read-stream probe over `bytes` (a multiple of 16) bytes: one XOR word per
-// 2048-byte group into out.  ev_start / ev_stop as launch_gemv.
-hipError_t launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* out, hipStream_t s,
-                             hipEvent_t ev_start, hipEvent_t ev_stop);
+// Read-stream probe over `bytes` (a multiple of 16) bytes: one XOR word per group
+// of kb kilobytes (kb in 1, 2, 4, 8, 16) into out; grid_blocks > 0 launches a
+// persistent grid of that many 4-wavefront workgroups, 0 one wavefront per group;
+// nontemporal selects streaming loads.  ev_start / ev_stop as launch_gemv.
+bool read_probe_kb_ok(int kb);
+hipError_t launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* out, int kb, int64_t grid_blocks,
+                             int nontemporal, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace qk

@@ -192,6 +192,17 @@ def test_read_probe_validation():
     assert _status(f, GOOD, 4096, ODD, None, None, None) == 4
 
 
+def test_read_probe_ex_validation():
+    f = "qk_read_probe_ex"
+    for kb in (0, 3, 32, -1):
+        assert _status(f, GOOD, 4096, GOOD, kb, 0, 0, None, None, None) == 8
+    assert _status(f, GOOD, 4096, GOOD, 2, -1, 0, None, None, None) == 8
+    assert _status(f, GOOD, 4096, GOOD, 2, 0, 2, None, None, None) == 8
+    assert _status(f, GOOD, 24, GOOD, 2, 0, 0, None, None, None) == 3
+    assert _status(f, None, 4096, GOOD, 2, 0, 0, None, None, None) == 5
+    assert _status(f, GOOD, 4096, ODD, 16, 256, 1, None, None, None) == 4
+
+
 def test_dequantize_validation():
     f = "qk_dequantize_row"
     assert _status(f, qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, None) == 1   # activation-only type

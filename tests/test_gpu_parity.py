@@ -462,6 +462,24 @@ def test_read_probe_xor_of_each_group(torch_cuda, nbytes):
     assert np.array_equal(out, np.bitwise_xor.reduce(words.reshape(ng, 512), axis=1))
 
 
+@pytest.mark.parametrize("kb,grid,nt", [(1, 0, 0), (4, 0, 1), (8, 0, 0), (16, 0, 0), (2, 3, 0), (4, 256, 1),
+                                         (16, 1, 0)])
+def test_read_probe_ex_xor_of_each_group(torch_cuda, kb, grid, nt):
+    # every load pattern of the probe reads exactly the bytes asked for: the XOR of
+    # each kb-kilobyte group (a persistent grid of `grid` workgroups strides over them)
+    for nbytes in (16, 1024 * kb * 37 + 7 * 16, 3_000_000):
+        say("read_probe_ex", kb, grid, nt, nbytes)
+        rng = np.random.default_rng(11)
+        buf = rng.integers(0, 256, size=nbytes + 4096, dtype=np.uint8)
+        out = host(qk.qk_read_probe_ex(dev(torch_cuda, buf), nbytes, kb, grid, nt)).view(np.uint32)
+        gw = 256 * kb
+        ng = (nbytes + 4 * gw - 1) // (4 * gw)
+        words = np.zeros(ng * gw, dtype=np.uint32)
+        words[:nbytes // 4] = buf[:nbytes].view("<u4")
+        assert out.shape == (ng,)
+        assert np.array_equal(out, np.bitwise_xor.reduce(words.reshape(ng, gw), axis=1))
+
+
 def test_c_abi_from_a_host_program(torch_cuda):
     # the C ABI without Python or torch: a host program allocates with the HIP
     # runtime, calls include/qk.h and checks every result against the C oracle

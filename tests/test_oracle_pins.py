@@ -23,15 +23,25 @@ F32 = np.float32
 # --------------------------------------------------------------------------
 
 def test_type_table_matches_printed_geometry():
-    # candle "量化格式" GgmlDType table; codeloopback lesson format table.
+    # candle "量化格式" GgmlDType table; codeloopback lesson format table.  Elements,
+    # bytes and bits per weight are printed there; the id column is a reading (the
+    # pages say the ids follow ggml's enum without printing them), so it is checked
+    # for consistency with the oracle's constants only, not as a pin.
     ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q5_1": o.Q5_1, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
            "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
     for name, gid, elems, nbytes, bpw in rows("type_table.txt"):
         t = ids[name]
-        assert t == int(gid)
         assert o.block_elems(t) == int(elems)
         assert o.block_bytes(t) == int(nbytes)
         assert f"{o.block_bytes(t) * 8 / o.block_elems(t):.4f}" == bpw
+
+
+def test_type_ids_reading_is_consistent():
+    # reading, not a pin: the GGUF enum values used as ids (type_table.txt header)
+    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q5_1": o.Q5_1, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
+           "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
+    for name, gid, _, _, _ in rows("type_table.txt"):
+        assert ids[name] == int(gid)
 
 
 def test_row_bytes_whole_blocks_no_padding():
@@ -360,6 +370,57 @@ def test_q8_K_layout_invariants():
     assert np.all(err <= (amax / 254 * (1 + 1e-5))[:, None])
     y = o.dequantize(o.Q8_K, b, x.size).reshape(-1, 256)
     assert np.array_equal(y, (qs.astype(np.float32) * d[:, None]).astype(np.float32))
+
+
+def _q8_K_fields(b):
+    b = b.reshape(-1, 292)
+    return (b[:, 0:4].tobytes(), b[:, 4:260].view(np.int8).astype(np.int32),
+            b[:, 260:292].copy().view("<i2").astype(np.int32))
+
+
+def test_q8_K_exact_ties_round_away_from_zero():
+    # codeloopback "Building Q8_0 and Q4_0 Like ggml", Example 2 prints roundf(2.5) = 3
+    # and roundf(-2.5) = -3: a scaled value halfway between two codes goes away from
+    # zero.  In a Q8_K block whose largest magnitude is 127 the scale is 127 / 127 =
+    # 1 exactly and 1/d = 1, so x itself is the scaled value and each k + 1/2 is an
+    # exact tie.  Worked by hand: codes 127, 3, -3, 1, -1, 5, -5, 127, -127, 2, -2,
+    # 0 elsewhere; d's four bytes are f32 1.0 (00 00 80 3F); bsums[0] is the sum of
+    # those codes (129 + ...), the other fifteen 0.  Round-half-even would give 2, -2,
+    # 0, 0, 4, -4, 126, -126, 2, -2.
+    x = np.zeros(256, np.float32)
+    vals = [127.0, 2.5, -2.5, 0.5, -0.5, 4.5, -4.5, 126.5, -126.5, 1.5, -1.5]
+    x[:len(vals)] = vals
+    d, qs, bsums = _q8_K_fields(o.quantize(o.Q8_K, x))
+    want = [127, 3, -3, 1, -1, 5, -5, 127, -127, 2, -2]
+    assert d == bytes([0x00, 0x00, 0x80, 0x3F])
+    assert qs[0, :len(want)].tolist() == want and not qs[0, len(want):].any()
+    assert bsums[0].tolist() == [sum(want)] + [0] * 15
+    # the same ties in the second block of a row, mirrored, with another block first
+    x2 = np.concatenate([np.linspace(-1, 1, 256, dtype=np.float32), -x])
+    d2, qs2, bs2 = _q8_K_fields(o.quantize(o.Q8_K, x2))
+    assert d2[4:8] == bytes([0x00, 0x00, 0x80, 0x3F])
+    assert qs2[1, :len(want)].tolist() == [-w for w in want]
+    assert bs2[1].tolist() == [-sum(want)] + [0] * 15
+
+
+def test_q8_K_scale_is_stored_as_f32():
+    # candle "量化格式", section "块结构": BlockQ8K's d is an f32 (BlockQ8_0's an f16).
+    # A block whose largest magnitude is 1 has d = fl32(1/127), worked by hand:
+    # 1/127 = 2^-7 * 128/127 = 2^-7 * (1 + 1/127), 23-bit fraction round(2^23 / 127) =
+    # round(66052.03) = 66052 = 0x10204, biased exponent 120 -> bits 0x3C010204, bytes
+    # 04 02 01 3C.  Rounded to f16 first it would be 2^-7 * (1 + 8/1024) = 0x3C010000.
+    # 1/d = 2^30 / 8454660 = 127 + 4/8454660 rounds to 127 exactly in f32 (half an ulp
+    # at 127 is 2^-17), so the codes are x * 127 rounded: 1 -> 127, 0.5 -> 63.5 -> 64
+    # (a tie, away from zero), -0.25 -> -31.75 -> -32, 0.125 -> 15.875 -> 16.
+    x = np.zeros(256, np.float32)
+    x[:4] = [1.0, 0.5, -0.25, 0.125]
+    d, qs, bsums = _q8_K_fields(o.quantize(o.Q8_K, x))
+    assert d == bytes([0x04, 0x02, 0x01, 0x3C])
+    assert qs[0, :4].tolist() == [127, 64, -32, 16] and not qs[0, 4:].any()
+    assert bsums[0].tolist() == [127 + 64 - 32 + 16] + [0] * 15
+    # dequantized through the stored f32 d: 64 * d = 64 * 8454660 * 2^-30 exactly
+    y = o.dequantize(o.Q8_K, o.quantize(o.Q8_K, x), 256)
+    assert y[1] == np.float32(8454660 * 2.0 ** -24)
 
 
 # --------------------------------------------------------------------------
