@@ -12,13 +12,15 @@ SRC = os.path.join(HERE, "qk_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(extra_flags=()):
+def build(extra_flags=(), lib=LIB):
+    """Compile the oracle into `lib` (the in-tree liboracle.so by default; the
+    sanitizer test builds an instrumented copy elsewhere)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
            "-fno-fast-math", "-Wall", "-Wextra", "-Werror", *extra_flags,
-           "-o", LIB + ".tmp", SRC, "-lm"]
+           "-o", lib + ".tmp", SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -26,7 +26,10 @@ TYPE_NAMES = {QK_TYPE_Q4_0: "Q4_0", QK_TYPE_Q4_1: "Q4_1", QK_TYPE_Q5_0: "Q5_0", 
               QK_TYPE_Q8_0: "Q8_0", QK_TYPE_Q4_K: "Q4_K", QK_TYPE_Q5_K: "Q5_K", QK_TYPE_Q6_K: "Q6_K",
               QK_TYPE_Q8_K: "Q8_K"}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqk.so")
+# the in-tree build; QK_LIB_PATH names another build of the same sources (the
+# host-sanitizer test runs the host-side checks against one)
+DEFAULT_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqk.so")
+LIB_PATH = os.environ.get("QK_LIB_PATH") or DEFAULT_LIB_PATH
 
 _lib = None
 

@@ -34,8 +34,8 @@ COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function"]
 
 
-def _compile(src, extra):
-    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src, extra, obj_dir=OBJ_DIR):
+    obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -43,18 +43,20 @@ def _compile(src, extra):
     return obj
 
 
-def build(extra=(), verbose=False):
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(extra=(), verbose=False, lib=LIB, obj_dir=OBJ_DIR, link_extra=()):
+    """Compile every source and link `lib` (the in-tree libqk.so by default; a
+    host-sanitizer test build passes its own paths and flags)."""
+    os.makedirs(obj_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        objs = list(ex.map(lambda s: _compile(s, list(extra), obj_dir), SOURCES))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", lib + ".tmp", *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
     if verbose:
-        print(LIB)
-    return LIB
+        print(lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -372,7 +372,8 @@ hipError_t launch_kernel(const uint8_t* W, int n_out, int nb, const uint8_t* xq,
                          int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   auto k = gemm_q4_K_mfma<C, SUMS>;
   unsigned grid = 0;
-  if (!launch_grid((n_out + C::kRows - 1) / C::kRows, C::kThreads, &grid)) return hipErrorInvalidConfiguration;
+  if (!launch_grid((static_cast<int64_t>(n_out) + C::kRows - 1) / C::kRows, C::kThreads, &grid))
+    return hipErrorInvalidConfiguration;
   constexpr size_t lds = 2 * C::kBytes;
   if constexpr (lds > 65536) {
     // above the default dynamic LDS limit: raise it for this kernel on the current

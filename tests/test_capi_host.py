@@ -46,7 +46,7 @@ def test_c_host_program_links_the_library_and_the_oracle():
     out = subprocess.run(["ldd", exe], capture_output=True, text=True, check=True).stdout
     libs = {line.split("=>")[0].strip(): line.split("=>")[1].split("(")[0].strip()
             for line in out.splitlines() if "=>" in line}
-    assert os.path.realpath(libs["libqk.so"]) == os.path.realpath(qk.LIB_PATH)
+    assert os.path.realpath(libs["libqk.so"]) == os.path.realpath(qk.DEFAULT_LIB_PATH)
     assert os.path.realpath(libs["liboracle.so"]) == os.path.join(ROOT, "oracle", "liboracle.so")
 
 
