@@ -51,6 +51,8 @@ def lib():
         L.orc_vec_dot.argtypes = [i32, p, p, i64, p, p]
         L.orc_gemv.restype = i32
         L.orc_gemv.argtypes = [i32, p, i64, i64, p, i64, p, p]
+        L.orc_gemv_block_sums.restype = i32
+        L.orc_gemv_block_sums.argtypes = [i32, p, i64, i64, p, i64, p]
         L.orc_swiglu.restype = i32
         L.orc_swiglu.argtypes = [p, p, i64, p]
         _lib = L
@@ -147,6 +149,15 @@ def vec_dot(wt, w_row, xq_row, n):
     _check(lib().orc_vec_dot(wt, _ptr(_u8(w_row)), _ptr(_u8(xq_row)), n, _ptr(y), _ptr(l1)),
            "vec_dot")
     return float(y[0]), float(l1[0])
+
+
+def gemv_block_sums(wt, W, n_out, n_in, xq, ncols=1):
+    """block_sums of every (column, row): shape [ncols, n_out, n_in/block, k]."""
+    k = int(lib().orc_sums_per_block(wt))
+    out = np.zeros((ncols, n_out, n_in // block_elems(wt), k), dtype=np.int32)
+    _check(lib().orc_gemv_block_sums(wt, _ptr(_u8(W)), n_out, n_in, _ptr(_u8(xq)), ncols, _ptr(out)),
+           "gemv_block_sums")
+    return out
 
 
 def gemv(wt, W, n_out, n_in, xq, ncols=1):

@@ -719,6 +719,24 @@ int orc_gemv(int wt, const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_
   return ORC_OK;
 }
 
+/* The per-block integer sums of a whole GEMV: orc_block_sums for every (column,
+ * row), laid out [ncols][n_out][n_in / block][sums per block]. */
+int orc_gemv_block_sums(int wt, const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_t* xq,
+                        int64_t ncols, int32_t* sums) {
+  int at = orc_act_type(wt);
+  if (at < 0) return ORC_BAD_PAIR;
+  int64_t rw = orc_row_bytes(wt, n_in), rx = orc_row_bytes(at, n_in);
+  if (rw == 0 || n_out < 0 || ncols < 0) return ORC_BAD_SHAPE;
+  int64_t per_row = (n_in / orc_block_elems(wt)) * orc_sums_per_block(wt);
+  for (int64_t c = 0; c < ncols; ++c) {
+    for (int64_t r = 0; r < n_out; ++r) {
+      int rc = orc_block_sums(wt, W + rw * r, xq + rx * c, n_in, sums + (c * n_out + r) * per_row);
+      if (rc != ORC_OK) return rc;
+    }
+  }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* The gated activation between an FFN's gate / up and down projections.      */
 /* The pages stop at the products; the 7B-shape layers that the FFN workload   */

@@ -89,6 +89,8 @@ int orc_vec_dot(int weight_type, const uint8_t* w, const uint8_t* xq, int64_t n,
                 float* out, double* l1);
 int orc_gemv(int weight_type, const uint8_t* W, int64_t n_out, int64_t n_in,
              const uint8_t* xq, int64_t ncols, float* y, double* l1);
+int orc_gemv_block_sums(int weight_type, const uint8_t* W, int64_t n_out, int64_t n_in,
+                        const uint8_t* xq, int64_t ncols, int32_t* sums);
 int orc_swiglu(const float* g, const float* u, int64_t n, double* h);
 
 #ifdef __cplusplus

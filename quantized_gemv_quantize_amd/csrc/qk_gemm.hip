@@ -1,40 +1,56 @@
 // qk_gemm.hip - batched Q4_K x Q8_K product (2..64 activation columns per launch)
-// on the gfx950 int8 matrix cores.
+// on the gfx950 matrix cores.
 //
 // Same method as the GEMV (rml "Quantized dot products"; candle formats page,
 // BlockQ4K / BlockQ8K): for every (token t, row r, superblock b) the exact int32
 //   S_q = sum_j sc_j * s_j,  s_j = sum_{e in sub-block j} q_e a_e   (32 elements)
-//   S_m = sum_j m_j * sum_{e in j} a_e
-// and y[t][r] accumulates (dx * d) * S_q - (dx * dmin) * S_m in f32.  With many tokens
-// the code products are a dense contraction, so they run on MFMA
-// (v_mfma_i32_16x16x64_i8, K = one 64-element chunk = two sub-blocks):
-//   - the 6-bit scale goes into the weight operand, split as sc = 8 * (sc >> 3) +
-//     (sc & 7): the bytes q * (sc & 7) and q * (sc >> 3) are at most 105, so both
-//     are int8 operands, and S_q = 8 * Q_hi + Q_lo where Q_hi, Q_lo accumulate
-//     over the superblock's four chunks inside the matrix core (exact int32);
-//   - S_m is the same contraction against m_j repeated over sub-block j (m <= 63).
-// Three MFMAs per chunk and tile, no per-sub-block integer work on the VALU.
+//   S_m = sum_j m_j * B_j,   B_j = sum_{e in j} a_e = bsum_{2j} + bsum_{2j+1}
+// (candle 块结构: BlockQ8K carries the 16-element code sums so that the min term needs
+// no pass over the codes), and y[t][r] accumulates dx * (d * S_q - dmin * S_m) in f32.
+// With many tokens the code products are a dense contraction, so they run on MFMA:
+//   - S_q: v_mfma_i32_16x16x64_i8 with the 6-bit scale folded into the weight
+//     operand, split as sc = 8 * (sc >> 3) + (sc & 7): the bytes q * (sc & 7) and
+//     q * (sc >> 3) are at most 105, so both are int8 operands and S_q = 8 * Q_hi +
+//     Q_lo, where Q_hi and Q_lo accumulate over the superblock inside the matrix core
+//     (exact int32).  Two MFMAs per 64 elements and 16 x 16 tile.
+//   - S_m: one v_mfma_f32_16x16x32_bf16 per superblock and tile from the bsums.  B_j
+//     lies in [-4064, 4064]; it is split as B_j = 64 * Bh + Bl with Bl = B_j & 63, and
+//     64 * Bh (a multiple of 64 below 2^13) and Bl (below 64) are exact bf16 values,
+//     as is m_j <= 63.  The 16 products m_j * (64 Bh_j) and m_j * Bl_j are exact in f32
+//     and so is every partial sum (|S_m| < 2^21 < 2^24), so the f32 result is S_m
+//     exactly.
 // Operand layout (checked on the hardware): A = activations, lane l holds token
-// l % 16 and k-slot group l / 16; B = weights, lane l holds row l % 16 and the same
-// k-slot group; D[token][row] lands in lane row + 16 * (token / 4), element
-// token % 4, so the four outputs of a lane share one weight row and its scales.
-// In chunk c, lane group g holds bytes 0-7 = elements 64c + 8g .. +7 of sub-block
-// 2c (low nibbles of qs[32c + 8g .. +7]) and bytes 8-15 = elements 64c + 32 + 8g
-// .. +7 of sub-block 2c+1 (high nibbles of the same bytes).  The same byte of A and
-// of B always meets the same k slot, so this grouping gives the full sum.
+// l % 16 and k-slot group g = l / 16 (16 bytes, or 8 bf16); B = weights, lane l
+// holds row l % 16 and the same k-slot group; D[token][row] lands in lane row +
+// 16 * (token / 4), element token % 4, so the four outputs of a lane share one
+// weight row and its scales.  Lane group g of a row holds qs bytes 16g .. 16g+15
+// (chunk g / 2) and 64 + 16g .. 64 + 16g + 15 (chunk 2 + g / 2); their low and high
+// nibbles are four runs of 16 consecutive elements, one sub-block each: with
+// c = g / 2 and p = 16 (g % 2), MFMA i = 0, 1, 2, 3 takes elements 64c + p, 64c + 32
+// + p, 64(c + 2) + p and 64(c + 2) + 32 + p onwards (sub-blocks 2c, 2c + 1, 2c + 4,
+// 2c + 5), so each operand carries one scale factor and its activation bytes are
+// 16 consecutive codes of the Q8_K block.
 //
-// Data movement: a workgroup owns RT 16-row tiles and all columns.  Per stage it
-// copies KSP superblocks of those rows (whole 144-byte blocks) and of every
-// activation column (256 codes + d) from HBM / L2 into LDS with contiguous 16-byte
-// loads; the loads run two stages ahead of the multiply and each stage is written
-// to LDS one stage ahead of its use (two buffers).  The workgroup has
-// RT x (NT / TW) x KSP wavefronts: a row tile, a group of TW token tiles and one
-// superblock of the stage each; the KSP partial sums of an output are added in
-// LDS at the end, always in the same order.  A wavefront that holds all token
-// tiles (TW = NT) builds each scaled weight operand once per superblock.  LDS row strides are 8 bytes more
-// than a multiple of 16, so the 16 rows (tokens) that a wavefront reads at one
-// offset fall in different bank pairs.
+// Data movement.  A workgroup owns R rows (R a multiple of 8, chosen so that about
+// one workgroup runs per CU) and all tokens.  Its compute wavefronts (RT 16-row
+// tiles x KS, each of the KS taking a contiguous range of every chunk's
+// superblocks) stream their own rows' 144-byte superblocks from HBM into
+// registers, P superblocks in flight.  The loads are coalesced: four consecutive
+// lanes read one row's 16-byte header (a dword each) and 2 x 64 contiguous qs
+// bytes, so a quad of lanes touches one cache line per instruction; ds_bpermute
+// then moves each row's bytes to the four lanes of the MFMA layout (loading lane
+// 4r + g -> MFMA lane 16g + r).  No weight byte is stored in LDS.
+// Four staging wavefronts copy the activations into LDS in chunks of KC
+// superblocks x all tokens (two buffers, one chunk ahead), token-major with a
+// 272-byte stride (coalesced 16-byte writes, and the MFMA's 16-byte reads of 8
+// consecutive tokens fall in distinct banks), each (superblock, 16-token tile)
+// followed by the bf16 digits of B_j for the S_m MFMA and the 16 scales dx.  They
+// issue no weight loads, so their in-order memory counter never waits behind the
+// weight stream; both roles meet only at the chunk barriers.  The K-split partial
+// sums of an output are added in LDS at the end, in split order.
 #include <hip/hip_ext.h>
+
+#include <type_traits>
 
 #include "qk_device.h"
 #include "qk_internal.h"
@@ -43,42 +59,21 @@ namespace qk {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));  // register-friendly 16 bytes
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr uint32_t kLo4 = 0x0F0F0F0Fu;
 constexpr uint32_t kHi2 = 0x30303030u;
-constexpr int kAStride = 264;   // LDS bytes per staged activation column (256 codes + pad)
 
-__device__ __forceinline__ v4i as_v4i(uint2 lo, uint2 hi) {
-  v4i r;
-  r[0] = static_cast<int>(lo.x);
-  r[1] = static_cast<int>(lo.y);
-  r[2] = static_cast<int>(hi.x);
-  r[3] = static_cast<int>(hi.y);
-  return r;
-}
-// Byte j of x in both 16-bit halves (v_perm_b32; selector 12 gives a zero byte).
-__device__ __forceinline__ uint32_t bcast16(uint32_t x, uint32_t j) {
-  return __builtin_amdgcn_perm(x, x, j * 0x00010001u + 0x0C000C00u);
-}
-// Each byte of x times the small factor s held in both halves of s2 (packed 16-bit
-// multiply): every product stays below 256 (codes <= 15, factor <= 7), so no
-// byte carries into its neighbour.
-__device__ __forceinline__ uint32_t mul_bytes(uint32_t x, uint32_t s2) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) * __builtin_bit_cast(u16x2, s2));
-}
-// 16 bytes to / from LDS at an 8-byte aligned address (rows padded to 8 bytes).
-__device__ __forceinline__ void lds_store16(uint8_t* p, u4 v) {
-  uint2* q = reinterpret_cast<uint2*>(__builtin_assume_aligned(p, 8));
-  q[0] = make_uint2(v[0], v[1]);
-  q[1] = make_uint2(v[2], v[3]);
-}
-__device__ __forceinline__ uint4 lds_load16(const uint8_t* p) {
-  const uint2* q = reinterpret_cast<const uint2*>(__builtin_assume_aligned(p, 8));
-  const uint2 a = q[0], b = q[1];
-  return make_uint4(a.x, a.y, b.x, b.y);
-}
+// LDS image of one (superblock, 16-token tile).
+constexpr int kTokStride = 272;              // 256 codes + 16: conflict-free operand reads
+constexpr int kDigOff = 16 * kTokStride;     // digits: lanes 0-15 64 * Bh_j, lanes 16-31 Bl_j (8 bf16)
+constexpr int kDxOff = kDigOff + 512;        // 16 f32 scales dx
+constexpr int kBT = kDxOff + 64;             // 4928 bytes
+constexpr int kZeroBytes = 512;              // the digit operand of lanes 32..63 (all zero)
+
 // 16 bytes at a 4-byte aligned global address (Q8_K codes start 4 bytes into the block)
 __device__ __forceinline__ u4 load_a4x4(const uint8_t* p) {
   const uint32_t* p4 = reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(p, 4));
@@ -86,316 +81,407 @@ __device__ __forceinline__ u4 load_a4x4(const uint8_t* p) {
   __builtin_memcpy(&v, p4, 16);
   return v;
 }
+// Each byte of x times the small factor held in both halves of s2 (packed 16-bit
+// multiply): every product stays below 256 (codes <= 15, factor <= 7), so no byte
+// carries into its neighbour.
+__device__ __forceinline__ int mul_bytes(uint32_t x, uint32_t s2) {
+  return static_cast<int>(
+      __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) * __builtin_bit_cast(u16x2, s2)));
+}
+// bf16 bits of a float that bf16 holds exactly (its low 16 bits are zero).
+__device__ __forceinline__ uint32_t bf16_hi(float f) { return __float_as_uint(f) >> 16; }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
 
-// Launch shape and stage geometry: NT 16-column tiles, TW tiles per wavefront,
-// KSP superblocks per stage, RT 16-row tiles per workgroup.
-template <int NT_, int TW_, int KSP_, int RT_ = 2>
+// Launch shape: NT 16-token tiles, RT 16-row tiles per workgroup, KS compute
+// wavefronts per row tile splitting the superblocks, P superblocks of weights in
+// flight per compute wavefront; SW staging wavefronts copy the activations.
+template <int NT_, int RT_, int KS_, int P_, int SW_ = 4>
 struct Cfg {
-  static constexpr int NT = NT_, TW = TW_, KSP = KSP_, RT = RT_;
-  static constexpr int kRows = 16 * RT;                // rows per workgroup
-  static constexpr int kTG = NT / TW;                  // token-tile groups
-  static constexpr int kWaves = RT * kTG * KSP;
+  static constexpr int NT = NT_, RT = RT_, KS = KS_, P = P_, SW = SW_;
+  static constexpr int KC = 16 / NT;            // superblocks per LDS chunk
+  static constexpr int QC = KC / KS;            // superblocks per wavefront and chunk
+  static constexpr int B = P > QC ? P : QC;     // superblocks per loop iteration
+  static constexpr int kCW = RT * KS;           // compute wavefronts
+  static constexpr int kWaves = kCW + SW;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kTok = 16 * NT;
-  static constexpr int kWStride = KSP * kQ4_KBytes + 8;  // bytes per staged weight row
-  static constexpr int kWBytes = kRows * kWStride;
-  static constexpr int kABytes = KSP * kTok * kAStride;
-  static constexpr int kDBytes = KSP * kTok * 4;
-  static constexpr int kBytes = kWBytes + kABytes + kDBytes;  // one stage buffer
-  static constexpr int kWPieces = kRows * KSP * 9;            // 16-byte pieces
-  static constexpr int kWPerThread = (kWPieces + kThreads - 1) / kThreads;
-  static constexpr int kAPieces = KSP * kTok * 16;
-  static constexpr int kAPerThread = kAPieces / kThreads;
-  static constexpr int kRedBytes = (KSP - 1) * RT * kTG * TW * 4 * 64 * 4;  // partial sums
-  static_assert(NT % TW == 0, "token tiles split evenly over wavefronts");
-  static_assert(kAPieces % kThreads == 0, "activation pieces split evenly");
-  static_assert(KSP * kTok <= kThreads, "one thread per staged scale");
-  static_assert(kBytes % 16 == 0, "stage buffers stay 16-byte aligned");
-  static_assert(kRedBytes <= 2 * kBytes, "the final reduction fits the stage buffers");
+  static constexpr int kST = 64 * SW;           // staging threads
+  static constexpr int kChunk = KC * NT * kBT;  // 78,848 bytes
+  static constexpr int kLds = kZeroBytes + 2 * kChunk;
+  static constexpr int kPieces = KC * NT * 256;  // 16-byte code pieces per chunk
+  static constexpr int kPPT = kPieces / kST;
+  static constexpr int kPairs = KC * NT * 16;    // (superblock, token) pairs per chunk
+  static constexpr int kRedBytes = (KS - 1) * RT * NT * 4 * 64 * 4;
+  static_assert(KC % KS == 0 && QC >= 1, "whole superblocks per wavefront and chunk");
+  static_assert(B % QC == 0 && B % P == 0, "whole chunks and whole weight rings per iteration");
+  static_assert(kST == 256 && kPieces % kST == 0, "piece k of a staging thread is image k");
+  static_assert(kPairs == kST, "one staging thread per (superblock, token) pair");
+  static_assert(kRedBytes <= 2 * kChunk, "the K-split reduction fits the chunk buffers");
+  static_assert(kLds <= 160 * 1024, "one workgroup's LDS fits a CU");
 };
 
+// One chunk's activation bytes in flight, per thread.
 template <class C>
-struct Prefetch {
-  u4 w[C::kWPerThread];
-  u4 a[C::kAPerThread];
+struct Stage {
+  u4 code[C::kPPT];
+  u4 bs0, bs1;  // the 16 bsums of this thread's (superblock, token) pair
   float dx;
 };
 
-// What each thread copies in every stage, fixed for the whole kernel: the byte
-// offsets of its pieces relative to the stage's first superblock, and where they
-// go in the LDS stage buffer.  A stage starting at superblock b adds b * 144 (W)
-// or b * 292 (activations).  Pieces of superblocks past the row end (the last
-// stage when KSP does not divide the superblock count, and the stages the
-// straight-line loop runs past the end) re-read the row's last superblock; they
-// are never used.
+// What each staging thread copies, fixed for the whole kernel.  Piece k of staging
+// thread i (i = 0 .. 255) is piece j = i % 16 of token n = (i / 16) % 16 of image k
+// (image = (superblock, tile) pair, k = sb * NT + t), so the image and the
+// superblock part of the address are compile-time / wave-uniform and only the
+// token part is per lane.  Superblocks past the row end are clamped to the last
+// one (valid memory, never used).
 template <class C>
 struct StageMap {
-  size_t wsrc[C::kWPerThread];     // row * row_bytes + sub * 144 + piece * 16
-  int wsub[C::kWPerThread];        // superblock of the stage the piece belongs to
-  int wdst[C::kWPerThread];        // LDS offset, -1 for threads without a piece
-  uint32_t asrc[C::kAPerThread];   // column * xrow + sub * 292 + 4 + piece * 16
-  int asub[C::kAPerThread];
-  uint32_t dsrc;
-  int dsub;
+  uint32_t src[C::kPPT];  // token * xrow + 4 + 16 j (per lane)
+  uint32_t dst;           // n * kTokStride + 16 j; image k adds k * kBT
+  uint32_t psrc;          // the thread's (superblock, token) pair
+  int psb;
+  uint32_t pimg;          // LDS offset of the pair's (superblock, tile) image
+  int ptok;               // the pair's token inside its tile
 
-  __device__ __forceinline__ StageMap(int row0, int n_out, size_t wrow, int ncols, uint32_t xrow) {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ StageMap(int sid, int ncols, uint32_t xrow) {
+    const int n = (sid >> 4) & 15, j = sid & 15;
 #pragma unroll
-    for (int k = 0; k < C::kWPerThread; ++k) {
-      const int p0 = tid + C::kThreads * k;
-      const int p = min(p0, C::kWPieces - 1);
-      const int row = p / (9 * C::KSP), rem = p % (9 * C::KSP);
-      wsrc[k] = static_cast<size_t>(min(row0 + row, n_out - 1)) * wrow + rem * 16;
-      wsub[k] = rem / 9;
-      wdst[k] = (p0 < C::kWPieces) ? row * C::kWStride + rem * 16 : -1;
+    for (int k = 0; k < C::kPPT; ++k) {
+      const int tok = min(16 * (k % C::NT) + n, ncols - 1);
+      src[k] = static_cast<uint32_t>(tok) * xrow + 4 + 16 * j;
     }
-#pragma unroll
-    for (int k = 0; k < C::kAPerThread; ++k) {
-      const int p = tid + C::kThreads * k;
-      const int piece = p & 15, col = (p >> 4) % C::kTok, kk = (p >> 4) / C::kTok;
-      asrc[k] = static_cast<uint32_t>(min(col, ncols - 1)) * xrow + kk * kQ8_KBytes + 4 + piece * 16;
-      asub[k] = kk;
-    }
-    const int t = min(tid, C::KSP * C::kTok - 1);
-    dsrc = static_cast<uint32_t>(min(t % C::kTok, ncols - 1)) * xrow + (t / C::kTok) * kQ8_KBytes;
-    dsub = t / C::kTok;
+    dst = n * kTokStride + 16 * j;
+    const int tok = sid % (16 * C::NT);
+    psrc = static_cast<uint32_t>(min(tok, ncols - 1)) * xrow;
+    psb = sid / (16 * C::NT);
+    pimg = (psb * C::NT + tok / 16) * kBT;
+    ptok = tok % 16;
   }
 };
 
-// Global -> registers for the stage starting at superblock b.  Offsets only
-// grow: a piece of a superblock past the row end steps back after b's offset is
-// added, never below its own row's start.
 template <class C>
-__device__ __forceinline__ Prefetch<C> stage_load(const StageMap<C>& m, const uint8_t* __restrict__ W,
-                                                  const uint8_t* __restrict__ xq, int nb, int b) {
-  const int last = nb - 1 - b;  // last superblock of this stage inside the row (>= 0)
-  Prefetch<C> pf;
+__device__ __forceinline__ void stage_load(Stage<C>& st, const StageMap<C>& m, const uint8_t* __restrict__ xq,
+                                           int nb, int b0) {
 #pragma unroll
-  for (int k = 0; k < C::kWPerThread; ++k) {
-    const size_t back = static_cast<size_t>(max(m.wsub[k] - last, 0)) * kQ4_KBytes;
-    pf.w[k] = *reinterpret_cast<const u4*>(W + (m.wsrc[k] + static_cast<size_t>(b) * kQ4_KBytes - back));
+  for (int k = 0; k < C::kPPT; ++k) {
+    const uint8_t* base = xq + static_cast<uint32_t>(min(b0 + k / C::NT, nb - 1)) * kQ8_KBytes;  // scalar
+    st.code[k] = load_a4x4(base + m.src[k]);
   }
-#pragma unroll
-  for (int k = 0; k < C::kAPerThread; ++k) {
-    const uint32_t back = static_cast<uint32_t>(max(m.asub[k] - last, 0)) * kQ8_KBytes;
-    pf.a[k] = load_a4x4(xq + (m.asrc[k] + static_cast<uint32_t>(b * kQ8_KBytes) - back));
-  }
-  {
-    const uint32_t back = static_cast<uint32_t>(max(m.dsub - last, 0)) * kQ8_KBytes;
-    pf.dx = *reinterpret_cast<const float*>(xq + (m.dsrc + static_cast<uint32_t>(b * kQ8_KBytes) - back));
-  }
-  return pf;
+  const uint8_t* p = xq + m.psrc + static_cast<uint32_t>(min(b0 + m.psb, nb - 1)) * kQ8_KBytes;
+  st.dx = *reinterpret_cast<const float*>(p);
+  st.bs0 = load_a4x4(p + 260);
+  st.bs1 = load_a4x4(p + 276);
 }
 
-// Registers -> LDS stage buffer.
 template <class C>
-__device__ __forceinline__ void stage_store(const StageMap<C>& m, const Prefetch<C>& pf, uint8_t* lds) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void stage_store(const Stage<C>& st, const StageMap<C>& m, uint8_t* buf) {
 #pragma unroll
-  for (int k = 0; k < C::kWPerThread; ++k) {
-    if (m.wdst[k] >= 0) lds_store16(lds + m.wdst[k], pf.w[k]);
-  }
+  for (int k = 0; k < C::kPPT; ++k) *reinterpret_cast<u4*>(buf + m.dst + k * kBT) = st.code[k];
+  {
+    // B_j = bsum_{2j} + bsum_{2j+1}, split into the bf16 digits 64 * Bh_j and Bl_j
+    const uint32_t w[8] = {st.bs0[0], st.bs0[1], st.bs0[2], st.bs0[3],
+                           st.bs1[0], st.bs1[1], st.bs1[2], st.bs1[3]};
+    float hi[8], lo[8];
 #pragma unroll
-  for (int k = 0; k < C::kAPerThread; ++k) {
-    const int p = tid + C::kThreads * k;
-    const int piece = p & 15, colk = p >> 4;  // colk = sub * kTok + col
-    lds_store16(lds + C::kWBytes + colk * kAStride + piece * 16, pf.a[k]);
+    for (int j = 0; j < 8; ++j) {
+      const int B = static_cast<int>(static_cast<int16_t>(w[j] & 0xFFFFu)) + (static_cast<int>(w[j]) >> 16);
+      const int bl = B & 63;
+      hi[j] = static_cast<float>(B - bl);
+      lo[j] = static_cast<float>(bl);
+    }
+    u4 h4, l4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h4[e] = pack_bf16(hi[2 * e], hi[2 * e + 1]);
+      l4[e] = pack_bf16(lo[2 * e], lo[2 * e + 1]);
+    }
+    uint8_t* img = buf + m.pimg;
+    *reinterpret_cast<u4*>(img + kDigOff + m.ptok * 16) = h4;        // lanes 0-15
+    *reinterpret_cast<u4*>(img + kDigOff + 256 + m.ptok * 16) = l4;  // lanes 16-31
+    *reinterpret_cast<float*>(img + kDxOff + m.ptok * 4) = st.dx;
   }
-  if (tid < C::KSP * C::kTok) *reinterpret_cast<float*>(lds + C::kWBytes + C::kABytes + tid * 4) = pf.dx;
+}
+
+// The four scaled weight operand pairs, d, dmin and the bf16 mins of one superblock
+// for the lane's row and k-slot group g (sub-blocks 2c, 2c + 1, 2c + 4, 2c + 5 with
+// c = g / 2; sel0 / sel1 pick byte 2c / 2c + 1 of a scale word into both 16-bit
+// halves).
+struct WOps {
+  v4i lo[4], hi[4];
+  bf16x8 m;
+  float d, dmin;
+};
+
+__device__ __forceinline__ WOps build_wops(const u4& h, const u4& qa, const u4& qb, uint32_t sel0,
+                                           uint32_t sel1) {
+  WOps o;
+  // 6-bit scales and mins of the 8 sub-blocks (get_scale_min_k4 on whole words)
+  const uint32_t sc_a = h[1] & 0x3F3F3F3Fu, m_a = h[2] & 0x3F3F3F3Fu;
+  const uint32_t sc_b = (h[3] & kLo4) | ((h[1] >> 2) & kHi2);
+  const uint32_t m_b = ((h[3] >> 4) & kLo4) | ((h[2] >> 2) & kHi2);
+  const uint32_t l3a = sc_a & 0x07070707u, h3a = (sc_a >> 3) & 0x07070707u;
+  const uint32_t l3b = sc_b & 0x07070707u, h3b = (sc_b >> 3) & 0x07070707u;
+  const uint32_t s_l[4] = {__builtin_amdgcn_perm(l3a, l3a, sel0), __builtin_amdgcn_perm(l3a, l3a, sel1),
+                           __builtin_amdgcn_perm(l3b, l3b, sel0), __builtin_amdgcn_perm(l3b, l3b, sel1)};
+  const uint32_t s_h[4] = {__builtin_amdgcn_perm(h3a, h3a, sel0), __builtin_amdgcn_perm(h3a, h3a, sel1),
+                           __builtin_amdgcn_perm(h3b, h3b, sel0), __builtin_amdgcn_perm(h3b, h3b, sel1)};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t q4[4] = {qa[e] & kLo4, (qa[e] >> 4) & kLo4, qb[e] & kLo4, (qb[e] >> 4) & kLo4};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o.lo[i][e] = mul_bytes(q4[i], s_l[i]);
+      o.hi[i][e] = mul_bytes(q4[i], s_h[i]);
+    }
+  }
+  u4 mw;
+  mw[0] = pack_bf16(static_cast<float>(m_a & 0xFF), static_cast<float>((m_a >> 8) & 0xFF));
+  mw[1] = pack_bf16(static_cast<float>((m_a >> 16) & 0xFF), static_cast<float>(m_a >> 24));
+  mw[2] = pack_bf16(static_cast<float>(m_b & 0xFF), static_cast<float>((m_b >> 8) & 0xFF));
+  mw[3] = pack_bf16(static_cast<float>((m_b >> 16) & 0xFF), static_cast<float>(m_b >> 24));
+  o.m = __builtin_bit_cast(bf16x8, mw);
+  o.d = f16_to_f32(h[0] & 0xFFFFu);
+  o.dmin = f16_to_f32(h[0] >> 16);
+  return o;
+}
+
+// One superblock of weights as loaded (coalesced layout): lane 4r + q holds header
+// dword q and qs bytes 16q .. 16q+15 and 64 + 16q .. 64 + 16q + 15 of row r.
+struct WRaw {
+  uint32_t hd;
+  u4 qa, qb;
+};
+
+__device__ __forceinline__ uint32_t from_lane(int byte_addr, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(byte_addr, static_cast<int>(v)));
 }
 
 template <class C, bool SUMS>
-__global__ __launch_bounds__(C::kThreads) void gemm_q4_K_mfma(const uint8_t* __restrict__ W, int n_out,
-                                                              int nb, const uint8_t* __restrict__ xq,
-                                                              int ncols, float* __restrict__ y,
+__global__ __launch_bounds__(C::kThreads) void gemm_q4_K_mfma(const uint8_t* __restrict__ W, int n_out, int nb,
+                                                              const uint8_t* __restrict__ xq, int ncols,
+                                                              int rows_wg, float* __restrict__ y,
                                                               int32_t* __restrict__ sums) {
-  constexpr int TW = C::TW, KSP = C::KSP;
+  constexpr int NT = C::NT, KC = C::KC, KS = C::KS, QC = C::QC, P = C::P, B = C::B;
   extern __shared__ __align__(16) uint8_t lds[];
+  uint8_t* const zero = lds;
+  uint8_t* const buf0 = lds + kZeroBytes;
+  uint8_t* const buf1 = buf0 + C::kChunk;
 
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int n = lane & 15;  // weight row in the tile; token in the A operand
   const int g = lane >> 4;  // k-slot group; the lane's outputs are tokens 4g .. 4g+3
   const int w = wave_id();
-  const int rt = w % C::RT;               // row tile
-  const int tg = (w / C::RT) % C::kTG;   // token-tile group
-  const int kh = (w / C::RT) / C::kTG;   // superblock of the stage
-  const int row0 = blockIdx.x * C::kRows;
-  const int row = row0 + 16 * rt + n;
-  const size_t wrow = static_cast<size_t>(nb) * kQ4_KBytes;
+  const uint32_t wrow = static_cast<uint32_t>(nb) * kQ4_KBytes;
   const uint32_t xrow = static_cast<uint32_t>(nb) * kQ8_KBytes;
+  const int nchunk = (nb + KC - 1) / KC;
+  const int qpad = (nchunk * QC + B - 1) / B * B;  // whole loop iterations
+  const int nbarrier = qpad / QC;                  // chunk ends of the compute loop
 
-  float acc[TW][4];
-#pragma unroll
-  for (int t = 0; t < TW; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-
-  // multiply the stage in LDS buffer `cur` (stage index s)
-  auto compute = [&](const uint8_t* cur, int s) {
-    const int b = s * KSP + kh;
-    if (b >= nb) return;
-    const uint8_t* wl = cur + (16 * rt + n) * C::kWStride + kh * kQ4_KBytes;
-    const uint4 h = lds_load16(wl);
-    // 6-bit scales and mins of the 8 sub-blocks (get_scale_min_k4)
-    const uint32_t sc_a = h.y & 0x3F3F3F3Fu, m_a = h.z & 0x3F3F3F3Fu;
-    const uint32_t sc_b = (h.w & kLo4) | ((h.y >> 2) & kHi2);
-    const uint32_t m_b = ((h.w >> 4) & kLo4) | ((h.z >> 2) & kHi2);
-    // B operands per 64-element chunk c (bytes 0-7: sub-block 2c, low nibbles;
-    // bytes 8-15: sub-block 2c+1, high nibbles): the codes times the low three
-    // and the high three bits of the sub-block's scale, and the min repeated.
-    const uint32_t l3a = sc_a & 0x07070707u, h3a = (sc_a >> 3) & 0x07070707u;
-    const uint32_t l3b = sc_b & 0x07070707u, h3b = (sc_b >> 3) & 0x07070707u;
-    v4i bl[4], bh[4], mB[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint2 q = *reinterpret_cast<const uint2*>(wl + 16 + 32 * c + 8 * g);
-      const uint32_t lo0 = q.x & kLo4, lo1 = q.y & kLo4;
-      const uint32_t hi0 = (q.x >> 4) & kLo4, hi1 = (q.y >> 4) & kLo4;
-      const uint32_t l3 = (c < 2) ? l3a : l3b, h3 = (c < 2) ? h3a : h3b;
-      const uint32_t j0 = 2 * (c & 1), j1 = j0 + 1;  // byte of sub-blocks 2c, 2c+1
-      const uint32_t sl0 = bcast16(l3, j0), sl1 = bcast16(l3, j1);
-      const uint32_t sh0 = bcast16(h3, j0), sh1 = bcast16(h3, j1);
-      bl[c][0] = static_cast<int>(mul_bytes(lo0, sl0));
-      bl[c][1] = static_cast<int>(mul_bytes(lo1, sl0));
-      bl[c][2] = static_cast<int>(mul_bytes(hi0, sl1));
-      bl[c][3] = static_cast<int>(mul_bytes(hi1, sl1));
-      bh[c][0] = static_cast<int>(mul_bytes(lo0, sh0));
-      bh[c][1] = static_cast<int>(mul_bytes(lo1, sh0));
-      bh[c][2] = static_cast<int>(mul_bytes(hi0, sh1));
-      bh[c][3] = static_cast<int>(mul_bytes(hi1, sh1));
-      const uint32_t mw = (c < 2) ? m_a : m_b;
-      const uint32_t m0 = __builtin_amdgcn_perm(mw, mw, 0x01010101u * j0);
-      const uint32_t m1 = __builtin_amdgcn_perm(mw, mw, 0x01010101u * j1);
-      mB[c][0] = static_cast<int>(m0);
-      mB[c][1] = static_cast<int>(m0);
-      mB[c][2] = static_cast<int>(m1);
-      mB[c][3] = static_cast<int>(m1);
+  if (w >= C::kCW) {
+    // Staging wavefronts: they issue no weight loads, so their waits cover only the
+    // activation bytes.  Chunk 0 goes to buffer 0 before the first barrier; after
+    // barrier c (the compute wavefronts are then on chunk c) chunk c + 1 goes to
+    // the other buffer, whose last reader was chunk c - 1.  The barrier count
+    // matches the compute wavefronts' (chunk ends, then the K-split reduction).
+    const int sid = tid - 64 * C::kCW;
+    const StageMap<C> map(sid, ncols, xrow);
+    Stage<C> st;
+    stage_load<C>(st, map, xq, nb, 0);
+    if (sid < kZeroBytes / 16) *reinterpret_cast<u4*>(zero + sid * 16) = u4{0u, 0u, 0u, 0u};
+    stage_store<C>(st, map, buf0);
+    __syncthreads();
+    for (int c = 0; c < nbarrier; ++c) {
+      stage_load<C>(st, map, xq, nb, (c + 1) * KC);
+      stage_store<C>(st, map, (c & 1) ? buf0 : buf1);
+      __syncthreads();
     }
-    const float d = f16_to_f32(h.x & 0xFFFF);
-    const float dmin = f16_to_f32(h.x >> 16);
+    if constexpr (!SUMS && KS > 1) __syncthreads();
+    return;
+  }
 
+  const int rt = w % C::RT;  // row tile
+  const int ks = w / C::RT;  // K split
+  const int row0 = blockIdx.x * rows_wg;
+  const int row_end = min(row0 + rows_wg, n_out);
+  const int row = row0 + 16 * rt + n;
+  // Weights: the workgroup's rows start at a wave-uniform address; the loading
+  // layout's lane 4r + q reads row r of the tile (rows past the workgroup's end
+  // read its last row: valid memory, never stored) at a 32-bit lane offset.
+  const uint8_t* const Wwg = W + static_cast<size_t>(row0) * wrow;
+  const uint32_t lw_hd = static_cast<uint32_t>(min(16 * rt + (lane >> 2), row_end - row0 - 1)) * wrow + 4 * (lane & 3);
+  const uint32_t lw_qs = lw_hd + 12 * (lane & 3) + 16;  // qs bytes 16 q .. 16 q + 15
+  // MFMA lane (n, g) takes row n's bytes from loading lane 4n + g; the header from
+  // lanes 4n .. 4n + 3
+  const int src_lane = 4 * (4 * n + g);
+  const int src_hdr = 16 * n;
+  const uint32_t sel0 = 0x0C000C00u + 0x00010001u * static_cast<uint32_t>(g & 2);
+  const uint32_t sel1 = sel0 + 0x00010001u;
+  // LDS: the wavefront multiplies superblocks ks * QC .. ks * QC + QC - 1 of each
+  // chunk.  A operand of lane (token n, g): codes 64c + 16 (g % 2) + {0, 32, 128,
+  // 160} of the token's row, c = g / 2; the digit operand of lanes 32..63 is the
+  // zero area.
+  const uint32_t wave_img = static_cast<uint32_t>(ks * QC * NT * kBT);
+  const uint32_t a_lane = wave_img + n * kTokStride + 64 * (g >> 1) + 16 * (g & 1);
+  const uint32_t dig_lane = wave_img + kDigOff + lane * 16;
+  const uint32_t zero_lane = static_cast<uint32_t>(lane - 32) * 16;
+  const uint32_t dx_lane = wave_img + kDxOff + g * 16;
+
+  // the wavefront's superblock sequence: in chunk c, b = c * KC + ks * QC + j
+  auto sb_of = [&](int q) { return (q / QC) * KC + ks * QC + (q % QC); };
+
+  // a ring of P weight slots (superblocks past the row end are clamped; their
+  // products get zero scales)
+  WRaw ring[P];
+  auto wload = [&](WRaw& r, int q) {
+    const uint8_t* base = Wwg + static_cast<uint32_t>(min(sb_of(q), nb - 1)) * kQ4_KBytes;  // scalar
+    r.hd = *reinterpret_cast<const uint32_t*>(base + lw_hd);
+    r.qa = *reinterpret_cast<const u4*>(base + lw_qs);
+    r.qb = *reinterpret_cast<const u4*>(base + lw_qs + 64);
+  };
+
+  // At most two superblocks of weights are requested before the first barrier (the
+  // staging wavefronts' activation reads then meet a shorter queue), the rest of
+  // the ring right after it.
+  constexpr int kEarly = P < 2 ? P : 2;
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      const int tt = tg * TW + t;  // token tile
-      const uint8_t* al = cur + C::kWBytes + (kh * C::kTok + 16 * tt + n) * kAStride;
-      const float4 dx4 = *reinterpret_cast<const float4*>(cur + C::kWBytes + C::kABytes +
-                                                          (kh * C::kTok + 16 * tt + 4 * g) * 4);
-      const float dx[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
-      v4i ql = {0, 0, 0, 0}, qh = {0, 0, 0, 0}, sm = {0, 0, 0, 0};
+  for (int s = 0; s < kEarly; ++s) wload(ring[s], s);
+  __syncthreads();
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint2 alo = *reinterpret_cast<const uint2*>(al + 64 * c + 8 * g);
-        const uint2 ahi = *reinterpret_cast<const uint2*>(al + 64 * c + 32 + 8 * g);
-        const v4i a = as_v4i(alo, ahi);
-        ql = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bl[c], ql, 0, 0, 0);
-        qh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bh[c], qh, 0, 0, 0);
-        sm = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, mB[c], sm, 0, 0, 0);
-      }
+  for (int s = kEarly; s < P; ++s) wload(ring[s], s);
+
+  float acc[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[t][e] = 0.0f;
+
+  // multiply the wavefront's superblock jj of the chunk in `cur` (superblock b)
+  auto multiply = [&](const WOps& o, const uint8_t* cur, int jj, int b) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int img = (jj * NT + t) * kBT;
+      v4i ql = {0, 0, 0, 0}, qh = {0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int sq = (qh[i] << 3) + ql[i];  // sc = 8 * (sc >> 3) + (sc & 7)
-        acc[t][i] += (dx[i] * d) * static_cast<float>(sq) - (dx[i] * dmin) * static_cast<float>(sm[i]);
+        const v4i a = *reinterpret_cast<const v4i*>(cur + a_lane + img + 32 * (i & 1) + 128 * (i >> 1));
+        ql = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, o.lo[i], ql, 0, 0, 0);
+        qh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, o.hi[i], qh, 0, 0, 0);
+      }
+      const bf16x8 dg = *reinterpret_cast<const bf16x8*>(g < 2 ? cur + dig_lane + img : zero + zero_lane);
+      const v4f sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dg, o.m, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      const v4f dx = *reinterpret_cast<const v4f*>(cur + dx_lane + img);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sq = (qh[e] << 3) + ql[e];  // sc = 8 * (sc >> 3) + (sc & 7)
+        const float v = fmaf(-o.dmin, sm[e], o.d * static_cast<float>(sq));
+        acc[t][e] = fmaf(dx[e], v, acc[t][e]);
         if constexpr (SUMS) {
-          const int tk = 16 * tt + 4 * g + i;
-          if (row < n_out && tk < ncols) {
-            int32_t* o = sums + ((static_cast<size_t>(tk) * n_out + row) * nb + b) * 2;
-            o[0] = sq;
-            o[1] = sm[i];
+          const int tk = 16 * t + 4 * g + e;
+          if (b < nb && row < row_end && tk < ncols) {
+            int32_t* out = sums + ((static_cast<size_t>(tk) * n_out + row) * nb + b) * 2;
+            out[0] = sq;
+            out[1] = static_cast<int>(sm[e]);
           }
         }
       }
     }
   };
 
-  // Global loads run two stages ahead of the multiply: two register sets
-  // alternate (the loop is unrolled by two so each set has a fixed name), and
-  // each stage is written to LDS one stage ahead of its use.  The body is
-  // straight-line: loads of stages past the end re-read the row's last superblock
-  // (stage_load clamps) and those stages multiply nothing, so no load sits under a
-  // condition and the compiler's wait counts cover only the older register set.
-  const int nstage = (nb + KSP - 1) / KSP;
-  const int nstage2 = (nstage + 1) & ~1;
-  const StageMap<C> map(row0, n_out, wrow, ncols, xrow);
-  uint8_t* even = lds;               // stages 0, 2, 4, ...
-  uint8_t* odd = lds + C::kBytes;    // stages 1, 3, 5, ...
-  Prefetch<C> pa = stage_load<C>(map, W, xq, nb, 0);
-  Prefetch<C> pb = stage_load<C>(map, W, xq, nb, KSP);
-  stage_store<C>(map, pa, even);
-  __syncthreads();
-  for (int s = 0; s < nstage2; s += 2) {
-    pa = stage_load<C>(map, W, xq, nb, (s + 2) * KSP);
-    compute(even, s);
-    stage_store<C>(map, pb, odd);
-    __syncthreads();
-    pb = stage_load<C>(map, W, xq, nb, (s + 3) * KSP);
-    compute(odd, s + 1);
-    stage_store<C>(map, pa, even);
-    __syncthreads();
-  }
+  // B superblocks per iteration; the slot of step j is j % P.  `more` is false on
+  // the last iteration, which requests no weights past the wavefront's sequence.
+  auto iteration = [&](int q0, auto more) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int q = q0 + j;
+      const int cc = q / QC, jj = j % QC;  // q0 is a multiple of QC
+      const int b = cc * KC + ks * QC + jj;
+      WRaw& r = ring[j % P];
+      u4 h, qa, qb;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[k] = from_lane(src_hdr + 4 * k, r.hd);
+        qa[k] = from_lane(src_lane, r.qa[k]);
+        qb[k] = from_lane(src_lane, r.qb[k]);
+      }
+      if (decltype(more)::value || j < B - P) wload(r, q + P);
+      WOps o = build_wops(h, qa, qb, sel0, sel1);
+      if (b < nb) multiply(o, (cc & 1) ? buf1 : buf0, jj, b);
+      if (jj == QC - 1) __syncthreads();  // end of chunk cc: chunk cc + 1 is staged
+    }
+  };
+  int q0 = 0;
+  for (; q0 + B < qpad; q0 += B) iteration(q0, std::true_type{});
+  iteration(q0, std::false_type{});
 
   if constexpr (!SUMS) {
-    if constexpr (KSP > 1) {
-      // wavefronts of superblocks 1 .. KSP-1 hand their partial sums to those of
-      // superblock 0, which add them in superblock order
-      float* red = reinterpret_cast<float*>(lds);
-      const int slot = (rt * C::kTG + tg) * TW;
-      constexpr int kPer = C::RT * C::kTG * TW;  // slots per superblock of the stage
-      if (kh > 0) {
+    if constexpr (KS > 1) {
+      // K-split wavefronts 1 .. KS-1 hand their partial sums to wavefront 0 of the
+      // row tile, which adds them in split order
+      float* red = reinterpret_cast<float*>(buf0);
+      if (ks > 0) {
 #pragma unroll
-        for (int t = 0; t < TW; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[(((kh - 1) * kPer + slot + t) * 4 + i) * 64 + lane] = acc[t][i];
+          for (int e = 0; e < 4; ++e) red[((((ks - 1) * C::RT + rt) * NT + t) * 4 + e) * 64 + lane] = acc[t][e];
       }
       __syncthreads();
-      if (kh > 0) return;
+      if (ks > 0) return;
 #pragma unroll
-      for (int k = 1; k < KSP; ++k)
+      for (int k = 1; k < KS; ++k)
 #pragma unroll
-        for (int t = 0; t < TW; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][i] += red[(((k - 1) * kPer + slot + t) * 4 + i) * 64 + lane];
+          for (int e = 0; e < 4; ++e) acc[t][e] += red[((((k - 1) * C::RT + rt) * NT + t) * 4 + e) * 64 + lane];
     }
-    if (row < n_out) {
+    if (row < row_end) {
 #pragma unroll
-      for (int t = 0; t < TW; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tk = 16 * (tg * TW + t) + 4 * g + i;
-          if (tk < ncols) y[static_cast<size_t>(tk) * n_out + row] = acc[t][i];
+        for (int e = 0; e < 4; ++e) {
+          const int tk = 16 * t + 4 * g + e;
+          if (tk < ncols) y[static_cast<size_t>(tk) * n_out + row] = acc[t][e];
         }
     }
   }
 }
 
 template <class C, bool SUMS>
-hipError_t launch_kernel(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, float* y,
+hipError_t launch_kernel(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, int rows_wg, float* y,
                          int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   auto k = gemm_q4_K_mfma<C, SUMS>;
   unsigned grid = 0;
-  if (!launch_grid((static_cast<int64_t>(n_out) + C::kRows - 1) / C::kRows, C::kThreads, &grid))
+  if (!launch_grid((static_cast<int64_t>(n_out) + rows_wg - 1) / rows_wg, C::kThreads, &grid))
     return hipErrorInvalidConfiguration;
-  constexpr size_t lds = 2 * C::kBytes;
-  if constexpr (lds > 65536) {
-    // above the default dynamic LDS limit: raise it for this kernel on the current
-    // device (set on every launch: the library keeps no per-device state)
-    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (attr != hipSuccess) return attr;
-  }
+  constexpr size_t lds = C::kLds;
+  // above the default dynamic LDS limit: raise it for this kernel on the current
+  // device (set on every launch: the library keeps no per-device state)
+  const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
   if (e0 != nullptr || e1 != nullptr) {
-    hipExtLaunchKernelGGL(k, dim3(grid), dim3(C::kThreads), lds, s, e0, e1, 0, W, n_out, nb, xq, ncols, y,
+    hipExtLaunchKernelGGL(k, dim3(grid), dim3(C::kThreads), lds, s, e0, e1, 0, W, n_out, nb, xq, ncols, rows_wg, y,
                           sums);
   } else {
-    k<<<grid, C::kThreads, lds, s>>>(W, n_out, nb, xq, ncols, y, sums);
+    k<<<grid, C::kThreads, lds, s>>>(W, n_out, nb, xq, ncols, rows_wg, y, sums);
   }
   return hipGetLastError();
 }
 
 template <class C>
-hipError_t launch_cfg(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, float* y,
+hipError_t launch_cfg(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, int rows_wg, float* y,
                       int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (sums != nullptr) return launch_kernel<C, true>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
-  return launch_kernel<C, false>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
+  if (sums != nullptr) return launch_kernel<C, true>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
+  return launch_kernel<C, false>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
+}
+
+template <int NT, int KS1, int KS2, int KS4, int P>
+hipError_t launch_nt(int rt, const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, int rows_wg,
+                     float* y, int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (rt == 1) return launch_cfg<Cfg<NT, 1, KS1, P>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
+  if (rt == 2) return launch_cfg<Cfg<NT, 2, KS2, P>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
+  return launch_cfg<Cfg<NT, 4, KS4, P>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
 }
 
 }  // namespace
@@ -403,33 +489,23 @@ hipError_t launch_cfg(const uint8_t* W, int n_out, int nb, const uint8_t* xq, in
 hipError_t launch_gemm_q4K(const uint8_t* W, int64_t n_out, int64_t n_in, const uint8_t* xq,
                            int64_t ncols, float* y, int32_t* sums, hipStream_t s, hipEvent_t e0,
                            hipEvent_t e1) {
+  if (ncols < 1 || ncols > kGemmMaxCols) return hipErrorInvalidValue;
   const int nb = static_cast<int>(n_in / 256);
   const int n = static_cast<int>(n_out), nc = static_cast<int>(ncols);
-  // 64-row workgroups (RT = 4) share each staged activation tile over four row
-  // tiles, measured best on 14336 x 4096 (graph replay: 16 columns 12.2 us, two row
-  // tiles 13.3; 32 columns 16.3 us, Cfg<2,1,1> with two row tiles 19.3; 64 columns
-  // 22.6 us, Cfg<4,2,1> 27.8).  Few rows leave most CUs idle at 64 rows per
-  // workgroup (4096 rows: 64 workgroups for 256 CUs), so matrices with at most 128
-  // (16 columns) or 64 (32, 64 columns) such groups use 16-row workgroups with four
-  // superblocks per stage instead (launch-recorded events: 4096 x 11008 at 16 / 32 /
-  // 64 columns 25.9 / 35.9 / 52.4 -> 15.7 / 21.4 / 33.6 us; 4096 x 4096 13.0 / 16.9 /
-  // 23.8 -> 9.1 / 11.5 / 16.8 us; at 11008 or more rows the 64-row shapes stay
-  // faster).  Shapes of 16 wavefronts that need more than 128 registers spill and
-  // are slower.
-  const int64_t groups64 = (n_out + 63) / 64;
-  if (nc <= 16) {
-    if (groups64 <= 128) return launch_cfg<Cfg<1, 1, 4, 1>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-    return launch_cfg<Cfg<1, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-  }
-  if (nc <= 32) {
-    if (groups64 <= 64) return launch_cfg<Cfg<2, 1, 4, 1>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-    return launch_cfg<Cfg<2, 1, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-  }
-  if (nc <= 64) {
-    if (groups64 <= 64) return launch_cfg<Cfg<4, 2, 4, 1>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-    return launch_cfg<Cfg<4, 4, 2, 4>>(W, n, nb, xq, nc, y, sums, s, e0, e1);
-  }
-  return hipErrorInvalidValue;
+  // Rows per workgroup: a multiple of 8 that spreads the rows over about 256
+  // workgroups (one per CU: 14336 rows -> 56, 4096 -> 16), at most 64; the row
+  // tiles of a workgroup cover them (a last tile may hold fewer than 16 rows).
+  const int64_t r0 = 8 * ((n_out + 2047) / 2048);
+  const int rt = r0 <= 16 ? 1 : (r0 <= 32 ? 2 : 4);
+  const int rows_wg = static_cast<int>(r0 < 16 * rt ? r0 : 16 * rt);
+  // 8 compute wavefronts per workgroup (4 for 32 or more tokens on one row tile),
+  // splitting each row tile's superblocks, plus 4 staging wavefronts; 2 (up to 16
+  // tokens) or 4 superblocks of weights in flight per compute wavefront (measured
+  // on 14336 x 4096: 16 tokens 11.8 us with 2 against 12.6 with 4 and 13.5 with 8;
+  // 64 tokens 20.7 us with 4 against 22.1 with 2 and 22.6 with 8)
+  if (nc <= 16) return launch_nt<1, 8, 4, 2, 2>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
+  if (nc <= 32) return launch_nt<2, 8, 4, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
+  return launch_nt<4, 4, 4, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
 }
 
 }  // namespace qk

@@ -248,15 +248,35 @@ SHAPES = {
 }
 
 
+def _row_chunks(n_out):
+    """Row ranges that split a matrix over the host's threads (the C oracle's
+    calls release the GIL, so large full-size cases run on every core)."""
+    parts = min(n_out, 4 * _THREADS)
+    edges = np.linspace(0, n_out, parts + 1).astype(np.int64)
+    return [(int(a), int(b)) for a, b in zip(edges[:-1], edges[1:]) if b > a]
+
+
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def _oracle_sums(t, W, xq, n_out, n_in, ncols):
-    at = orc.act_type(t)
-    rb, xb = orc.row_bytes(t, n_in), orc.row_bytes(at, n_in)
-    Wf, xf = W.reshape(-1), xq.reshape(-1)
-    out = []
-    for c in range(ncols):
-        out.append(np.stack([orc.block_sums(t, Wf[r * rb:(r + 1) * rb], xf[c * xb:(c + 1) * xb], n_in)
-                             for r in range(n_out)]))
-    return np.stack(out)
+    """Per-block integer sums of every (column, row): [ncols, n_out, blocks, k]."""
+    from concurrent.futures import ThreadPoolExecutor
+    W2 = W.reshape(n_out, -1)
+    with ThreadPoolExecutor(_THREADS) as ex:
+        parts = list(ex.map(lambda rr: orc.gemv_block_sums(t, W2[rr[0]:rr[1]], rr[1] - rr[0], n_in, xq, ncols),
+                            _row_chunks(n_out)))
+    return np.concatenate(parts, axis=1)
+
+
+def _oracle_gemv(t, W, n_out, n_in, xq, ncols):
+    """orc.gemv over all rows, split over the host's threads: (y, l1) [ncols, n_out]."""
+    from concurrent.futures import ThreadPoolExecutor
+    W2 = W.reshape(n_out, -1)
+    with ThreadPoolExecutor(_THREADS) as ex:
+        parts = list(ex.map(lambda rr: orc.gemv(t, W2[rr[0]:rr[1]], rr[1] - rr[0], n_in, xq, ncols),
+                            _row_chunks(n_out)))
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
 
 
 @pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4K, T5K, T6K])
@@ -290,7 +310,7 @@ def test_gemv_block_sums_and_y(torch_cuda, t):
 BATCHED = [(1, 256, 2), (17, 512, 16), (33, 1024, 17), (45, 4096, 33), (70, 2304, 48),
            (31, 11008, 64), (50, 768, 65), (21, 4352, 130), (129, 256, 7),
            # past the row counts that switch to 64-row workgroups, ragged
-           (8300, 256, 9), (4200, 256, 24), (4160, 256, 40),
+           (8300, 256, 9), (4200, 256, 24), (4160, 256, 40), (8300, 1024, 40), (2100, 2560, 64),
            # small batches: the multi-column GEMV kernel (2 columns; 3 up to 8192
            # rows) and, past 8192 rows, the matrix cores at 3 columns
            (37, 2304, 3), (8300, 256, 3), (4100, 11008, 2)]
@@ -309,7 +329,7 @@ def test_batched_q4_K_block_sums_and_y(torch_cuda, n_out, n_in, ncols):
     want = _oracle_sums(T4K, W, xq, n_out, n_in, ncols)
     assert np.array_equal(sums, want.reshape(sums.shape))
     y = host(qk.qk_gemv(T4K, Wd, n_out, n_in, xd, ncols))
-    y_o, l1 = orc.gemv(T4K, W, n_out, n_in, xq, ncols)
+    y_o, l1 = _oracle_gemv(T4K, W, n_out, n_in, xq, ncols)
     assert_y(y, y_o, l1, f"batched Q4_K {n_out}x{n_in} ncols {ncols}")
     assert not y[ncols // 2].any()
 
@@ -644,8 +664,9 @@ def test_ffn_swiglu_step_7b(torch_cuda, gt):
 # Full-size workloads, in the launch configuration the benchmark times.
 # ---------------------------------------------------------------------------
 
-def _check_full(torch, t, W, n_out, n_in, X, rows=None, what=""):
-    """GEMV over the full matrix on the GPU; oracle on `rows` (all if None)."""
+def _check_full(torch, t, W, n_out, n_in, X, what=""):
+    """GEMV over the full matrix on the GPU, every output and every per-block sum
+    against the oracle."""
     at = orc.act_type(t)
     ncols = X.shape[0]
     xq_gpu = qk.qk_quantize_act(at, dev(torch, X))
@@ -653,14 +674,11 @@ def _check_full(torch, t, W, n_out, n_in, X, rows=None, what=""):
     assert np.array_equal(host(xq_gpu), xq), what
     Wd = dev(torch, W)
     y = host(qk.qk_gemv(t, Wd, n_out, n_in, xq_gpu, ncols))
-    sel = np.arange(n_out) if rows is None else np.asarray(rows)
-    Wsel = W.reshape(n_out, -1)[sel]
-    y_o, l1 = orc.gemv(t, Wsel, len(sel), n_in, xq, ncols)
-    assert_y(y[:, sel], y_o, l1, what)
+    y_o, l1 = _oracle_gemv(t, W, n_out, n_in, xq, ncols)
+    assert_y(y, y_o, l1, what)
     sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xq_gpu, ncols))
-    pick = sel[:: max(1, len(sel) // 64)]
-    want = _oracle_sums(t, W.reshape(n_out, -1)[pick], xq, len(pick), n_in, ncols)
-    assert np.array_equal(sums[:, pick], want.reshape(sums[:, pick].shape)), what
+    want = _oracle_sums(t, W, xq, n_out, n_in, ncols)
+    assert np.array_equal(sums, want.reshape(sums.shape)), what
     return y
 
 
@@ -716,10 +734,7 @@ def test_full_q6_K_head_and_dequantize(torch_cuda):
 def test_full_q4_K_batched_14336x4096(torch_cuda, ncols):
     d = synth.q4_K_batched_14336x4096()
     say("full Q4_K batched 14336x4096", ncols)
-    rng = np.random.default_rng(44)
-    rows = np.unique(np.concatenate([np.arange(64), rng.integers(0, 14336, 192), [14335]]))
-    _check_full(torch_cuda, T4K, d["W"], 14336, 4096, d["X"][:ncols], rows=rows,
-                what=f"Q4_K batched {ncols}")
+    _check_full(torch_cuda, T4K, d["W"], 14336, 4096, d["X"][:ncols], what=f"Q4_K batched {ncols}")
 
 
 def test_full_q5_K_decode_4096x11008(torch_cuda):
@@ -845,8 +860,7 @@ def test_q4_K_batched_4096x11008(torch_cuda, ncols):
     rng = np.random.default_rng(45)
     X = rng.standard_normal((ncols, 11008)).astype(np.float32)
     say("batched Q4_K 4096x11008", ncols)
-    rows = np.unique(np.concatenate([np.arange(32), rng.integers(0, 4096, 96), [4095]]))
-    _check_full(torch_cuda, T4K, d["W"], 4096, 11008, X, rows=rows, what=f"Q4_K 4096x11008 x {ncols}")
+    _check_full(torch_cuda, T4K, d["W"], 4096, 11008, X, what=f"Q4_K 4096x11008 x {ncols}")
 
 
 def test_full_q4_K_decode_4096x11008(torch_cuda):
