@@ -11,7 +11,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 7, 8, 12, 13, 14, 15
+Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q8_1, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 7, 8, 9, 12, 13, 14, 15
 
 _lib = None
 
@@ -37,7 +37,7 @@ def lib():
         L.orc_f32_to_f16.restype = ctypes.c_uint16
         L.orc_f32_to_f16.argtypes = [ctypes.c_float]
         for name in ("orc_quantize_q8_0", "orc_quantize_q8_K", "orc_quantize_q4_0",
-                     "orc_quantize_q4_1", "orc_quantize_q5_0"):
+                     "orc_quantize_q4_1", "orc_quantize_q5_0", "orc_quantize_q8_1"):
             f = getattr(L, name)
             f.restype = i32
             f.argtypes = [p, p, i64]
@@ -105,14 +105,14 @@ def f32_to_f16(f):
 
 
 def quantize(t, x):
-    """Quantize a float32 array (last axis n) to blocks of type t (Q8_0, Q8_K, Q4_0,
-    Q4_1, Q5_0)."""
+    """Quantize a float32 array (last axis n) to blocks of type t (Q8_0, Q8_1, Q8_K,
+    Q4_0, Q4_1, Q5_0)."""
     x = _f32(x)
     n = x.shape[-1]
     rows = x.reshape(-1, n)
     fn = {Q8_0: lib().orc_quantize_q8_0, Q8_K: lib().orc_quantize_q8_K,
           Q4_0: lib().orc_quantize_q4_0, Q4_1: lib().orc_quantize_q4_1,
-          Q5_0: lib().orc_quantize_q5_0}[t]
+          Q5_0: lib().orc_quantize_q5_0, Q8_1: lib().orc_quantize_q8_1}[t]
     rb = row_bytes(t, n)
     if rb == 0:
         raise OracleError(f"n={n} is not whole blocks of type {t}")

@@ -30,6 +30,7 @@ int64_t orc_block_elems(int type) {
     case ORC_Q5_0:
     case ORC_Q5_1:
     case ORC_Q8_0:
+    case ORC_Q8_1:
       return 32;
     case ORC_Q4_K:
     case ORC_Q5_K:
@@ -48,6 +49,7 @@ int64_t orc_block_bytes(int type) {
     case ORC_Q5_0: return 22;
     case ORC_Q5_1: return 24;
     case ORC_Q8_0: return 34;
+    case ORC_Q8_1: return 36; /* reading: d f16, s f16, 32 int8 codes */
     case ORC_Q4_K: return 144;
     case ORC_Q5_K: return 176;
     case ORC_Q6_K: return 210;
@@ -64,15 +66,18 @@ int64_t orc_row_bytes(int type, int64_t n) {
 }
 
 /* Weight -> activation pairing: [candle] VecDotType table (Q4_0, Q5_0, Q8_0
- * pair with Q8_0; the K-quants with Q8K); [cl] Example 11; [rml] "Quantized
- * dot products".  Q4_1 pairs with Q8_1, which the pages only name: no pairing
- * here. */
+ * pair with Q8_0; Q4_1, Q5_1 with Q8_1; the K-quants with Q8K); [cl] Example 11;
+ * [rml] "Quantized dot products".  Q8_1 is an activation format only ([candle]
+ * 块结构: it never appears in a GGUF file), so it has no pairing as a weight. */
 int orc_act_type(int weight_type) {
   switch (weight_type) {
     case ORC_Q4_0:
     case ORC_Q5_0:
     case ORC_Q8_0:
       return ORC_Q8_0;
+    case ORC_Q4_1:
+    case ORC_Q5_1:
+      return ORC_Q8_1;
     case ORC_Q4_K:
     case ORC_Q5_K:
     case ORC_Q6_K:
@@ -209,6 +214,31 @@ int orc_quantize_q8_0(const float* x, uint8_t* out, int64_t n) {
     float id = (d != 0.0f) ? 1.0f / d : 0.0f;
     orc_put_u16(ob, orc_f32_to_f16(d));
     for (int j = 0; j < 32; ++j) ob[2 + j] = (uint8_t)orc_code_q8(xb[j] * id);
+  }
+  return ORC_OK;
+}
+
+/* quantize_row_q8_1 (reading; [candle] VecDotType table names BlockQ8_1 as the
+ * activation block of the _1 types, 块结构 says the _1 blocks add one f16 to the _0
+ * layout): d and the codes exactly as quantize_row_q8_0 above, then
+ * s = sum of the 32 codes times the unrounded f32 d, stored as f16.  Block bytes:
+ * d f16 at 0, s f16 at 2, codes at 4. */
+int orc_quantize_q8_1(const float* x, uint8_t* out, int64_t n) {
+  if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float* xb = x + 32 * b;
+    uint8_t* ob = out + 36 * b;
+    float amax = orc_amax(xb, 32);
+    float d = amax / 127.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    int sum = 0;
+    for (int j = 0; j < 32; ++j) {
+      int8_t q = orc_code_q8(xb[j] * id);
+      ob[4 + j] = (uint8_t)q;
+      sum += q;
+    }
+    orc_put_u16(ob, orc_f32_to_f16(d));
+    orc_put_u16(ob + 2, orc_f32_to_f16((float)sum * d));
   }
   return ORC_OK;
 }
@@ -516,6 +546,11 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
         }
         break;
       }
+      case ORC_Q8_1: { /* d * q, as Q8_0 (test helper: activations) */
+        float d = orc_f16_to_f32(orc_get_u16(blk));
+        for (int j = 0; j < 32; ++j) y[j] = (float)(int8_t)blk[4 + j] * d;
+        break;
+      }
       case ORC_Q8_K: { /* [candle] BlockQ8K: d * q (test helper: activations) */
         float d = orc_get_f32(blk);
         for (int j = 0; j < 256; ++j) y[j] = d * (float)(int8_t)blk[4 + j];
@@ -534,13 +569,15 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
 /* element as VecDotRef does; only the block scales are float).              */
 /* ------------------------------------------------------------------------- */
 
-/* Integer quantities kept per weight block: one s for Q8_0, Q4_0, Q5_0, Q6_K;
- * the pair (S_q, S_m) for Q4_K and Q5_K (scale sum and min sum). */
+/* Integer quantities kept per weight block: one s for Q8_0, Q4_0, Q5_0, Q4_1,
+ * Q5_1, Q6_K; the pair (S_q, S_m) for Q4_K and Q5_K (scale sum and min sum). */
 int64_t orc_sums_per_block(int weight_type) {
   switch (weight_type) {
     case ORC_Q8_0:
     case ORC_Q4_0:
     case ORC_Q5_0:
+    case ORC_Q4_1:
+    case ORC_Q5_1:
     case ORC_Q6_K:
       return 1;
     case ORC_Q4_K:
@@ -569,6 +606,17 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
     case ORC_Q5_0: { /* as Q4_0, with the 5-bit code (minus 16) of each element */
       int32_t s = 0;
       for (int e = 0; e < 32; ++e) s += (int32_t)orc_q5_0_code(wb, e) * (int32_t)(int8_t)xb[2 + e];
+      out[0] = s;
+      return ORC_OK;
+    }
+    case ORC_Q4_1:
+    case ORC_Q5_1: { /* s = sum of code x a over the 32 elements (codes 0..15 / 0..31,
+                      * unsigned: the minimum is added by the float step) */
+      int32_t s = 0;
+      for (int e = 0; e < 32; ++e) {
+        int q = (wt == ORC_Q4_1) ? orc_q4_1_code(wb, e) : orc_q5_1_code(wb, e);
+        s += (int32_t)q * (int32_t)(int8_t)xb[4 + e];
+      }
       out[0] = s;
       return ORC_OK;
     }
@@ -620,7 +668,10 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
 
 /* The one float step per block ([rml] "Kernels and references": kernels and
  * references share it).  Q8_0/Q4_0: c = s * (dw * dx) with both f16 scales
- * ([cl] Example 10 step 2).  Q4_K, Q5_K: c = (dx*d) * S_q - (dx*dmin) * S_m.
+ * ([cl] Example 10 step 2).  Q4_1, Q5_1 against Q8_1: every weight value is
+ * code * dw + mw and every activation dx * a, so the block's sum is
+ * dw dx sum(code a) + mw dx sum(a) = s * (dw * dx) + mw * sx, with sx the Q8_1
+ * block's stored f16 dx * sum(a).  Q4_K, Q5_K: c = (dx*d) * S_q - (dx*dmin) * S_m.
  * Q6_K: c = (dx*d) * S.  dx of Q8_K is f32 ([candle] BlockQ8K). */
 static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s) {
   switch (wt) {
@@ -630,6 +681,14 @@ static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const
       float dw = orc_f16_to_f32(orc_get_u16(wb));
       float dx = orc_f16_to_f32(orc_get_u16(xb));
       return (float)s[0] * (dw * dx);
+    }
+    case ORC_Q4_1:
+    case ORC_Q5_1: {
+      float dw = orc_f16_to_f32(orc_get_u16(wb));
+      float mw = orc_f16_to_f32(orc_get_u16(wb + 2));
+      float dx = orc_f16_to_f32(orc_get_u16(xb));
+      float sx = orc_f16_to_f32(orc_get_u16(xb + 2));
+      return (float)s[0] * (dw * dx) + mw * sx;
     }
     case ORC_Q4_K:
     case ORC_Q5_K: {
@@ -651,9 +710,18 @@ static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const
 /* The magnitude a block contributes to the tolerance scale: the sum of the
  * absolute values of the float terms its step adds ([cl] Example 10 measures
  * error against the sum of |a*b| over the terms).  One term for Q8_0, Q4_0,
- * Q5_0 and Q6_K; for Q4_K and Q5_K the scale term (dx*d)*S_q and the min term
- * (dx*dmin)*S_m, which can cancel in c while each is rounded on its own. */
+ * Q5_0 and Q6_K; for Q4_1 and Q5_1 the code term s*(dw*dx) and the minimum term
+ * mw*sx; for Q4_K and Q5_K the scale term (dx*d)*S_q and the min term
+ * (dx*dmin)*S_m.  Two-term steps can cancel in c while each term is rounded on
+ * its own. */
 static double orc_block_l1(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s, float c) {
+  if (wt == ORC_Q4_1 || wt == ORC_Q5_1) {
+    float dw = orc_f16_to_f32(orc_get_u16(wb));
+    float mw = orc_f16_to_f32(orc_get_u16(wb + 2));
+    float dx = orc_f16_to_f32(orc_get_u16(xb));
+    float sx = orc_f16_to_f32(orc_get_u16(xb + 2));
+    return fabs((double)((float)s[0] * (dw * dx))) + fabs((double)(mw * sx));
+  }
   if (wt != ORC_Q4_K && wt != ORC_Q5_K) return fabs((double)c);
   float dx = orc_get_f32(xb);
   float d = orc_f16_to_f32(orc_get_u16(wb));

@@ -34,9 +34,15 @@
  *   pinned Q4_K decoder; vec_dot Q5_KxQ8_K is pinned by brute force against its
  *   dequant definition, as the other K-quants are.
  *   quantize / dequantize Q4_1 and Q5_0, vec_dot Q5_0xQ8_0: pinned by the [cl]
- *   Example 7, 8, 12 and 14 printed values and bytes, plus brute force.  Q4_1
- *   has no dot product here: its activation format (Q8_1) is only named on the
- *   pages, so it is a dequantize / quantize format only.
+ *   Example 7, 8, 12 and 14 printed values and bytes, plus brute force.
+ *   quantize_q8_1 and vec_dot Q4_1xQ8_1 / Q5_1xQ8_1: [candle] names BlockQ8_1 as
+ *   the activation format of the _1 types (VecDotType table) without printing its
+ *   layout.  The reading taken: d f16 @0, s f16 @2, 32 int8 codes @4 (36 bytes);
+ *   d and the codes follow the Q8_0 rule, s = f16(d * sum of codes) with the
+ *   unrounded f32 d, the sum the weight minimum's term needs (as BlockQ8K's bsums
+ *   serve Q4K's min term).  Codes and d are pinned by the printed Q8_0 bytes; s by
+ *   a hand-worked block; the dot product by f64 brute force over the pinned Q4_1
+ *   decoder within the bound of s's f16 rounding, and its integer sum exactly.
  */
 #ifndef QK_ORACLE_H
 #define QK_ORACLE_H
@@ -54,6 +60,7 @@ extern "C" {
 #define ORC_Q5_0 6
 #define ORC_Q5_1 7
 #define ORC_Q8_0 8
+#define ORC_Q8_1 9
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
 #define ORC_Q6_K 14
@@ -79,6 +86,7 @@ int orc_quantize_q8_K(const float* x, uint8_t* out, int64_t n);
 int orc_quantize_q4_0(const float* x, uint8_t* out, int64_t n);
 int orc_quantize_q4_1(const float* x, uint8_t* out, int64_t n);
 int orc_quantize_q5_0(const float* x, uint8_t* out, int64_t n);
+int orc_quantize_q8_1(const float* x, uint8_t* out, int64_t n);
 
 int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n);
 

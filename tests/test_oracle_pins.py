@@ -67,7 +67,11 @@ def test_pairing_table():
     assert o.act_type(o.Q6_K) == o.Q8_K
     assert o.act_type(o.Q5_K) == o.Q8_K
     assert o.act_type(o.Q8_K) == -1
-    assert o.act_type(3) == -1
+    # the same table pairs Q4_1 and Q5_1 with BlockQ8_1, an activation-only block
+    assert o.act_type(o.Q4_1) == o.Q8_1
+    assert o.act_type(o.Q5_1) == o.Q8_1
+    assert o.act_type(o.Q8_1) == -1
+    assert o.act_type(4) == -1
 
 
 # --------------------------------------------------------------------------
@@ -636,6 +640,102 @@ def test_q5_1_fifth_bit_e_is_element_e():
         y1 = o.dequantize(o.Q5_1, bb, 32).astype(np.float64)
         assert list(np.nonzero(y1 != y0)[0]) == [e]
         assert y1[e] - y0[e] == 16 * 0.25
+
+
+# --------------------------------------------------------------------------
+# Q8_1 and the Q4_1 / Q5_1 dot products.  candle "量化格式", VecDotType table:
+# Q4_1 and Q5_1 pair with BlockQ8_1, whose layout the pages do not print.  Reading:
+# d f16 @0, s f16 @2, 32 int8 codes @4; d and the codes by the Q8_0 rule (pinned
+# below by the printed Q8_0 bytes), s = f16(sum of codes * the unrounded f32 d).
+# --------------------------------------------------------------------------
+
+def _q8_1_fields(b):
+    return (b[0:2].tobytes().hex(), b[2:4].tobytes().hex(), [int(c) for c in b[4:36].view(np.int8)])
+
+
+def test_q8_1_d_and_codes_are_the_printed_q8_0_bytes():
+    kv = keyvals("q8_0_blocks.txt")
+    assert o.block_elems(o.Q8_1) == 32 and o.block_bytes(o.Q8_1) == 36
+    # codeloopback Example 2's block: the printed Q8_0 hex is d (2 bytes) + 32 codes
+    b = o.quantize(o.Q8_1, _cl_inputs(32))
+    assert b[0:2].tobytes().hex() + b[4:].tobytes().hex() == kv["cl_ex2.hex"]
+    # candle's Q8_0 block
+    d, _, codes = _q8_1_fields(o.quantize(o.Q8_1, (np.arange(32, dtype=np.float32) - F32(15.5)) / F32(10)))
+    assert d == kv["candle.d_bytes_hex"]
+    assert codes == [int(c) for c in kv["candle.qs"].split()]
+
+
+def test_q8_1_sum_field_hand_worked():
+    # amax 127: d = 1 exactly, codes are roundf(x) (ties away from zero, codeloopback
+    # Example 2), s = f16(sum).  127 + 3 - 3 + 1 = 128 = 2^7: f16 0x5800.
+    x = np.zeros(32, np.float32)
+    x[:4] = [127.0, 2.5, -2.5, 1.4]
+    d, s_, codes = _q8_1_fields(o.quantize(o.Q8_1, x))
+    assert d == "003c" and codes[:4] == [127, 3, -3, 1] and s_ == "0058"
+    # -127 - 100 = -227 = -1.7734375 * 2^7: sign, exponent 22, fraction 792: 0xdb18.
+    x[:4] = [-127.0, -100.0, 0.0, 0.0]
+    assert _q8_1_fields(o.quantize(o.Q8_1, x))[1] == "18db"
+    # amax 1: d = fl32(1/127) = 0.0078740157; codes 127, -127, 16 (0.125 * 127 =
+    # 15.875), 1 (0.0078125 * 127 = 0.99); sum 17.  17 * d = 0.13385826 lies between
+    # the f16 neighbours 0x3048 = 0.13378906 and 0x3049 = 0.13391113, nearer 0x3049.
+    # With d first rounded to f16 (0.0078735352) the product, 0.13385010, would be
+    # nearer 0x3048: the sum is scaled by the unrounded d.
+    x[:4] = [1.0, -1.0, 0.125, 0.0078125]
+    d, s_, codes = _q8_1_fields(o.quantize(o.Q8_1, x))
+    assert codes[:4] == [127, -127, 16, 1] and sum(codes) == 17
+    assert s_ == "4930"
+    assert o.quantize(o.Q8_1, np.zeros(32, np.float32)).tobytes() == bytes(36)
+
+
+def _blocks_with_min(t, nblocks, rng, zero_min=False):
+    nb = o.block_bytes(t)
+    w = rng.integers(0, 256, (nblocks, nb), dtype=np.uint8)
+    w[:, 0:2] = np.frombuffer(rng.uniform(1e-3, 4e-3, nblocks).astype(np.float16).tobytes(), np.uint8).reshape(-1, 2)
+    m = np.zeros(nblocks) if zero_min else rng.uniform(-0.05, 0.05, nblocks)
+    w[:, 2:4] = np.frombuffer(m.astype(np.float16).tobytes(), np.uint8).reshape(-1, 2)
+    return w.reshape(-1)
+
+
+@pytest.mark.parametrize("t", [o.Q4_1, o.Q5_1])
+def test_q4_1_q5_1_block_sums_are_exact(t):
+    # with m = 0 every decoded value is code * d exactly (code < 32, d f16), so the
+    # codes come back from the dequantizer (pinned by codeloopback Examples 7 and 14
+    # for Q4_1) and the block's integer is their dot product with the Q8_1 codes.
+    rng = np.random.default_rng(80 + t)
+    n = 256
+    w = _blocks_with_min(t, n // 32, rng, zero_min=True)
+    xq = o.quantize(o.Q8_1, rng.standard_normal(n).astype(np.float32))
+    d = np.repeat(w.reshape(-1, o.block_bytes(t))[:, 0:2].copy().view(np.float16).astype(np.float64)[:, 0], 32)
+    q = o.dequantize(t, w, n).astype(np.float64) / d
+    assert np.array_equal(q, np.round(q)) and q.min() >= 0 and q.max() < (16 if t == o.Q4_1 else 32)
+    a = xq.reshape(-1, 36)[:, 4:].view(np.int8).astype(np.int64).reshape(-1)
+    want = (q.astype(np.int64) * a).reshape(-1, 32).sum(axis=1)
+    assert np.array_equal(o.block_sums(t, w, xq, n)[:, 0], want)
+
+
+@pytest.mark.parametrize("t", [o.Q4_1, o.Q5_1])
+def test_q4_1_q5_1_vec_dot_brute_force(t):
+    # sum over elements of (code d_w + m_w) (d_x a), in f64 from the dequantized
+    # values.  The oracle's minimum term uses the stored s = f16(d_x32 sum a), where
+    # d_x32 is the unrounded scale that the dequantizer sees rounded to f16: the two
+    # differ by at most 2^-10 |m_w d_x sum a| per block (two f16 roundings); the
+    # rest is f32 rounding of the block steps and their sum.
+    rng = np.random.default_rng(90 + t)
+    for nblk in (1, 8, 96):
+        n = 32 * nblk
+        w = _blocks_with_min(t, nblk, rng)
+        x = rng.standard_normal(n).astype(np.float32)
+        xq = o.quantize(o.Q8_1, x)
+        xb = xq.reshape(-1, 36)
+        dx = xb[:, 0:2].copy().view(np.float16).astype(np.float64)[:, 0]
+        a = xb[:, 4:].view(np.int8).astype(np.int64)
+        brute = np.sum(o.dequantize(t, w, n).astype(np.float64) * np.repeat(dx, 32) * a.reshape(-1))
+        mw = w.reshape(nblk, -1)[:, 2:4].copy().view(np.float16).astype(np.float64)[:, 0]
+        bound = np.sum(np.abs(mw * dx * a.sum(axis=1))) * 2.0 ** -10 * 1.01
+        y, l1 = o.vec_dot(t, w, xq, n)
+        assert abs(y - brute) <= bound + 2 * nblk * 2.0 ** -23 * l1 + 1e-30, (t, n, y, brute)
+        # dropping the minimum term, or taking it with the wrong sign, is far outside
+        assert np.sum(np.abs(mw * dx * a.sum(axis=1))) > 50 * bound
 
 
 # --------------------------------------------------------------------------
