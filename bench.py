@@ -75,12 +75,18 @@ def log(*a):
 def workloads(qk):
     T4K, T6K, T40, T80 = qk.QK_TYPE_Q4_K, qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q8_0
     T50, T5K = qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_K
+    T41, T51, T81 = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_1, qk.QK_TYPE_Q8_1
     T8K = qk.QK_TYPE_Q8_K
     return {
         "q4_K_decode_4096x11008": {
             "gemvs": [("W", T4K, 4096, 11008, "x")], "acts": {"x": (T8K, 11008, 1)}},
         "q5_K_decode_4096x11008": {
             "gemvs": [("W", T5K, 4096, 11008, "x")], "acts": {"x": (T8K, 11008, 1)}},
+        # the _1 weight formats against Q8_1 activations (candle VecDotType table)
+        "q4_1_decode_4096x11008": {
+            "gemvs": [("W", T41, 4096, 11008, "x")], "acts": {"x": (T81, 11008, 1)}},
+        "q5_1_decode_4096x11008": {
+            "gemvs": [("W", T51, 4096, 11008, "x")], "acts": {"x": (T81, 11008, 1)}},
         "q4_K_4096x4096": {
             "gemvs": [("W_q4_K", T4K, 4096, 4096, "x")], "acts": {"x": (T8K, 4096, 1)}},
         "q4_0_4096x4096": {
@@ -126,6 +132,10 @@ def host_inputs(name, qk):
         return synth.q4_K_decode_4096x11008()
     if name == "q5_K_decode_4096x11008":
         return synth.q5_K_decode_4096x11008()
+    if name == "q4_1_decode_4096x11008":
+        return synth.q4_1_decode_4096x11008()
+    if name == "q5_1_decode_4096x11008":
+        return synth.q5_1_decode_4096x11008()
     if name in ("q4_K_4096x4096", "q4_0_4096x4096"):
         return synth.q4_gemv_4096x4096()
     if name in ("ffn_7b_q4_K_q6_K", "ffn_7b_swiglu", "ffn_7b_q5_K_swiglu"):
@@ -170,6 +180,9 @@ def gpu_copy_like(torch, w_type, n_out, n_in, gen):
         w[:, :, 0:2] = f16(1e-3, 4e-3)
     elif w_type == synth.Q5_0:
         w[:, :, 0:2] = f16(5e-4, 2e-3)
+    elif w_type in (synth.Q4_1, synth.Q5_1):
+        w[:, :, 0:2] = f16(1e-3, 4e-3) if w_type == synth.Q4_1 else f16(5e-4, 2e-3)
+        w[:, :, 2:4] = f16(-0.03, -0.005)
     else:
         raise ValueError("GPU copies are drawn for block-byte weight formats only")
     return w.reshape(n_out, nb * bb)

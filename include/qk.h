@@ -2,17 +2,19 @@
  * qk.h - C ABI of libqk.so, the MI355X (gfx950) block-quantized GEMV library.
  *
  * The library computes y = W x where W is stored row-major as whole ggml blocks
- * (Q8_0, Q4_0, Q5_0, Q4_K, Q5_K or Q6_K, byte-exact GGUF layouts) and x is quantized once per
- * call into int8 activation blocks (Q8_0 or Q8_K) aligned with W's blocks.  Every
+ * (Q8_0, Q4_0, Q5_0, Q4_1, Q5_1, Q4_K, Q5_K or Q6_K, byte-exact GGUF layouts) and x is
+ * quantized once per call into int8 activation blocks (Q8_0, Q8_1 or Q8_K) aligned
+ * with W's blocks.  Every
  * product inside a block is an exact int32 sum; only the block scales are float.
  * Sources (page title, section):
  *   "Quantization" (rml): type table, DequantizeRow, VecDot and its pairing.
  *   "Quantization" (sipllm): dequantize_row(t, src, dst, n), matmul_quant layout.
  *   "Building Q8_0 and Q4_0 Like ggml" (codeloopback): Q8_0/Q4_0 bytes, Examples 1-11.
  *   "量化格式" (candle formats): type table, BlockQ4K/Q6K/Q8K fields, VecDotType.
- * Q5_K and Q6_K: the pages give their size and the role of each field, not which
- * bit belongs to which element; the GGUF arrangement is implemented (stated below
- * at qk_dequantize_row).
+ * Q5_1, Q5_K and Q6_K: the pages give their size and the role of each field, not
+ * which bit belongs to which element; the GGUF arrangement is implemented (stated
+ * below at qk_dequantize_row).  Q8_1: the pages name it as the activation block of
+ * the _1 types without its layout; the reading is stated at qk_quantize_act.
  *
  * Conventions shared by every call:
  *  - Types are ggml's ids, as a GGUF tensor record stores them.
@@ -41,6 +43,7 @@ extern "C" {
 #define QK_TYPE_Q5_0 6
 #define QK_TYPE_Q5_1 7
 #define QK_TYPE_Q8_0 8
+#define QK_TYPE_Q8_1 9
 #define QK_TYPE_Q4_K 12
 #define QK_TYPE_Q5_K 13
 #define QK_TYPE_Q6_K 14
@@ -63,8 +66,9 @@ extern "C" {
 #define QK_EPI_SWIGLU 1
 
 /* Elements per block (32 or 256) and bytes per block (Q4_0 18, Q4_1 20, Q5_0 22,
- * Q5_1 24, Q8_0 34, Q4_K 144, Q5_K 176, Q6_K 210, Q8_K 292) of a type, 0 for an unknown id.  Geometry
- * from the candle formats page, "GgmlDType" table. */
+ * Q5_1 24, Q8_0 34, Q8_1 36, Q4_K 144, Q5_K 176, Q6_K 210, Q8_K 292) of a type, 0 for an
+ * unknown id.  Geometry from the candle formats page, "GgmlDType" table (Q8_1's 36
+ * bytes are the reading stated at qk_quantize_act). */
 int64_t qk_block_elems(int type);
 int64_t qk_block_bytes(int type);
 
@@ -74,9 +78,8 @@ int64_t qk_block_bytes(int type);
 int64_t qk_row_bytes(int type, int64_t n);
 
 /* Activation type a weight type is multiplied against (candle "VecDotType" table;
- * codeloopback Example 11): Q4_0, Q5_0, Q8_0 -> Q8_0; Q4_K, Q5_K, Q6_K -> Q8_K; -1
- * otherwise (Q4_1 and Q5_1 pair with Q8_1, a format the sources only name, so they
- * are quantize / dequantize types here and have no GEMV). */
+ * codeloopback Example 11): Q4_0, Q5_0, Q8_0 -> Q8_0; Q4_1, Q5_1 -> Q8_1; Q4_K, Q5_K,
+ * Q6_K -> Q8_K; -1 otherwise (including the activation-only Q8_1 and Q8_K). */
 int qk_act_type(int weight_type);
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -88,7 +91,7 @@ int64_t qk_max_n_in(int weight_type);
 
 /*
  * qk_quantize_act - quantize float activations into int8 blocks, once per call.
- *   act_type  QK_TYPE_Q8_0 or QK_TYPE_Q8_K (else QK_E_TYPE).
+ *   act_type  QK_TYPE_Q8_0, QK_TYPE_Q8_1 or QK_TYPE_Q8_K (else QK_E_TYPE).
  *   x         f32 [ncols][n], row-major, device.
  *   xq        out: [ncols][n / block] blocks, ncols * qk_row_bytes(act_type, n) bytes.
  *   n         elements per column, a positive multiple of the block size.
@@ -98,7 +101,10 @@ int64_t qk_max_n_in(int weight_type);
  * is 0; code = roundf(x * id), halves away from zero, NaN -> 0, saturated to int8.
  * Q8_0 stores d as f16 (round to nearest even, subnormals kept, overflow -> inf)
  * then 32 codes (34 bytes).  Q8_K stores d as f32, 256 codes and 16 int16 bsums,
- * each the sum of 16 consecutive codes (292 bytes; candle BlockQ8K).
+ * each the sum of 16 consecutive codes (292 bytes; candle BlockQ8K).  Q8_1 (36 bytes;
+ * candle names BlockQ8_1 as the activation block of Q4_1 and Q5_1 without printing
+ * it, so this layout is a reading): f16 d, f16 s = (sum of the 32 codes) * d with the
+ * unrounded f32 d, rounded to f16, then the 32 codes as Q8_0's.
  * Results are bit-exact to that definition.
  */
 int qk_quantize_act(int act_type, const float* x, void* xq, int64_t n, int64_t ncols,
@@ -137,7 +143,7 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
 
 /*
  * qk_gemv - y = W x for quantized W and already-quantized activations.
- *   w_type    QK_TYPE_Q8_0, Q4_0, Q5_0, Q4_K, Q5_K or Q6_K (else QK_E_TYPE).
+ *   w_type    QK_TYPE_Q8_0, Q4_0, Q5_0, Q4_1, Q5_1, Q4_K, Q5_K or Q6_K (else QK_E_TYPE).
  *   W         n_out rows of qk_row_bytes(w_type, n_in) bytes, contiguous, row-major
  *             (sipllm matmul_quant layout), device.
  *   n_out     output rows, >= 0.
@@ -148,10 +154,11 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
  *   y         out: f32 [ncols][n_out], device.
  * For every (row, block): the exact int32 sums of code products (VecDot, rml
  * "Quantized dot products"; the Q4_K / Q5_K min term taken from the activation bsums), then
- * one f32 step with the block scales; y is the f32 sum of those steps.  The
+ * one f32 step with the block scales; y is the f32 sum of those steps.  Q4_1 and Q5_1:
+ * s * (d_w * d_x) + m_w * s_x, with s_x the Q8_1 block's f16 sum field.  The
  * summation order differs from a sequential loop, so y matches a sequential f32
  * evaluation to within rounding, not bit for bit.  Several columns: Q4_K at 2
- * columns (3 up to 8192 rows), every other format in groups of up to 4 columns run a GEMV
+ * columns (3 up to 8192 rows), Q8_0, Q4_0, Q5_0, Q5_K and Q6_K in groups of up to 4 columns run a GEMV
  * kernel that reads W once for all its columns (each column's arithmetic as the
  * one-column kernel's); Q4_K otherwise runs on the int8 matrix cores, up to 64
  * columns per launch (same per-block integers, y equal to within rounding); every
@@ -193,7 +200,7 @@ int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* st
  * compute instead of y.  For checking exactness; not needed to use the library.
  *   sums      out: int32 [ncols][n_out][n_in / block][k]; k = 2 for Q4_K, Q5_K (the scale
  *             sum S_q = sum_j sc_j s_j and the min sum S_m = sum_j m_j sum(a_j)),
- *             k = 1 otherwise (Q8_0, Q4_0, Q5_0: the block's code-product sum; Q6_K:
+ *             k = 1 otherwise (Q8_0, Q4_0, Q5_0, Q4_1, Q5_1: the block's code-product sum; Q6_K:
  *             S = sum_j sc_j sum (q - 32) a).
  * Other arguments and errors as qk_gemv.
  */

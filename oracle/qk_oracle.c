@@ -221,8 +221,8 @@ int orc_quantize_q8_0(const float* x, uint8_t* out, int64_t n) {
 /* quantize_row_q8_1 (reading; [candle] VecDotType table names BlockQ8_1 as the
  * activation block of the _1 types, 块结构 says the _1 blocks add one f16 to the _0
  * layout): d and the codes exactly as quantize_row_q8_0 above, then
- * s = sum of the 32 codes times the unrounded f32 d, stored as f16.  Block bytes:
- * d f16 at 0, s f16 at 2, codes at 4. */
+ * s = sum of the 32 codes times the unrounded f32 d, stored as f16 (a NaN product,
+ * from an infinite d, as 0x7E00).  Block bytes: d f16 at 0, s f16 at 2, codes at 4. */
 int orc_quantize_q8_1(const float* x, uint8_t* out, int64_t n) {
   if (n < 0 || n % 32 != 0) return ORC_BAD_SHAPE;
   for (int64_t b = 0; b < n / 32; ++b) {
@@ -238,7 +238,11 @@ int orc_quantize_q8_1(const float* x, uint8_t* out, int64_t n) {
       sum += q;
     }
     orc_put_u16(ob, orc_f32_to_f16(d));
-    orc_put_u16(ob + 2, orc_f32_to_f16((float)sum * d));
+    /* d is infinite only for a block holding an infinity; its codes are then all 0
+     * and the product is NaN, stored as the quiet NaN 0x7E00 whatever sign the
+     * host's NaN carries. */
+    float p = (float)sum * d;
+    orc_put_u16(ob + 2, isnan(p) ? (uint16_t)0x7E00 : orc_f32_to_f16(p));
   }
   return ORC_OK;
 }

@@ -13,18 +13,20 @@ QK_TYPE_Q4_1 = 3
 QK_TYPE_Q5_0 = 6
 QK_TYPE_Q5_1 = 7
 QK_TYPE_Q8_0 = 8
+QK_TYPE_Q8_1 = 9
 QK_TYPE_Q4_K = 12
 QK_TYPE_Q5_K = 13
 QK_TYPE_Q6_K = 14
 QK_TYPE_Q8_K = 15
-WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_K, QK_TYPE_Q5_K, QK_TYPE_Q6_K)
-DEQUANT_TYPES = WEIGHT_TYPES + (QK_TYPE_Q4_1, QK_TYPE_Q5_1)
+WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_1, QK_TYPE_Q5_1, QK_TYPE_Q4_K,
+                QK_TYPE_Q5_K, QK_TYPE_Q6_K)
+DEQUANT_TYPES = WEIGHT_TYPES
 QUANT_ROW_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q4_1, QK_TYPE_Q5_0)
 QK_EPI_NONE = 0
 QK_EPI_SWIGLU = 1
 TYPE_NAMES = {QK_TYPE_Q4_0: "Q4_0", QK_TYPE_Q4_1: "Q4_1", QK_TYPE_Q5_0: "Q5_0", QK_TYPE_Q5_1: "Q5_1",
               QK_TYPE_Q8_0: "Q8_0", QK_TYPE_Q4_K: "Q4_K", QK_TYPE_Q5_K: "Q5_K", QK_TYPE_Q6_K: "Q6_K",
-              QK_TYPE_Q8_K: "Q8_K"}
+              QK_TYPE_Q8_1: "Q8_1", QK_TYPE_Q8_K: "Q8_K"}
 
 # the in-tree build; QK_LIB_PATH names another build of the same sources (the
 # host-sanitizer test runs the host-side checks against one)

@@ -12,16 +12,16 @@ namespace {
 
 // Weight formats with a GEMV (a paired activation type).
 bool is_weight(int t) {
-  return t == QK_TYPE_Q4_0 || t == QK_TYPE_Q5_0 || t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_K ||
-         t == QK_TYPE_Q5_K || t == QK_TYPE_Q6_K;
+  return t == QK_TYPE_Q4_0 || t == QK_TYPE_Q5_0 || t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_1 ||
+         t == QK_TYPE_Q5_1 || t == QK_TYPE_Q4_K || t == QK_TYPE_Q5_K || t == QK_TYPE_Q6_K;
 }
-// Weight formats qk_dequantize_row expands.
-bool is_dequant(int t) { return is_weight(t) || t == QK_TYPE_Q4_1 || t == QK_TYPE_Q5_1; }
+// Weight formats qk_dequantize_row expands (every GEMV weight format).
+bool is_dequant(int t) { return is_weight(t); }
 // Weight formats qk_quantize_row writes.
 bool is_quant_row(int t) {
   return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_0 || t == QK_TYPE_Q4_1 || t == QK_TYPE_Q5_0;
 }
-bool is_act(int t) { return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q8_K; }
+bool is_act(int t) { return t == QK_TYPE_Q8_0 || t == QK_TYPE_Q8_1 || t == QK_TYPE_Q8_K; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -120,7 +120,8 @@ int64_t qk_block_elems(int type) {
     case QK_TYPE_Q4_1:
     case QK_TYPE_Q5_0:
     case QK_TYPE_Q5_1:
-    case QK_TYPE_Q8_0: return 32;
+    case QK_TYPE_Q8_0:
+    case QK_TYPE_Q8_1: return 32;
     case QK_TYPE_Q4_K:
     case QK_TYPE_Q5_K:
     case QK_TYPE_Q6_K:
@@ -136,6 +137,7 @@ int64_t qk_block_bytes(int type) {
     case QK_TYPE_Q5_0: return 22;
     case QK_TYPE_Q5_1: return 24;
     case QK_TYPE_Q8_0: return 34;
+    case QK_TYPE_Q8_1: return 36;
     case QK_TYPE_Q4_K: return 144;
     case QK_TYPE_Q5_K: return 176;
     case QK_TYPE_Q6_K: return 210;
@@ -155,6 +157,8 @@ int qk_act_type(int weight_type) {
     case QK_TYPE_Q4_0:
     case QK_TYPE_Q5_0:
     case QK_TYPE_Q8_0: return QK_TYPE_Q8_0;
+    case QK_TYPE_Q4_1:
+    case QK_TYPE_Q5_1: return QK_TYPE_Q8_1;
     case QK_TYPE_Q4_K:
     case QK_TYPE_Q5_K:
     case QK_TYPE_Q6_K: return QK_TYPE_Q8_K;

@@ -24,6 +24,7 @@ constexpr int kQ4_0Bytes = 18;
 constexpr int kQ4_1Bytes = 20;
 constexpr int kQ5_0Bytes = 22;
 constexpr int kQ5_1Bytes = 24;
+constexpr int kQ8_1Bytes = 36;
 constexpr int kQ4_KBytes = 144;
 constexpr int kQ5_KBytes = 176;
 constexpr int kQ6_KBytes = 210;
@@ -43,8 +44,13 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
 }
 
 // f32 -> binary16 bits, round to nearest even, subnormals kept, overflow to inf
-// (v_cvt_f16_f32 with the kernel's default rounding and f16 denormal modes).
+// (v_cvt_f16_f32 with the kernel's default rounding and f16 denormal modes).  The
+// argument is an f32 value already rounded: the empty asm hides how it was computed,
+// because the backend otherwise merges a product feeding this conversion into one
+// mixed-precision multiply (v_fma_mix) rounded once to f16, a different value near
+// f16 ties.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  asm volatile("" : "+v"(f));
   _Float16 h = static_cast<_Float16>(f);
   uint16_t b;
   __builtin_memcpy(&b, &h, 2);
@@ -101,6 +107,12 @@ __device__ __forceinline__ float wave_sum(float v) {
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31)) +
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47)) +
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over groups of 8 lanes (returned in every lane of the group, exact int32).
+__device__ __forceinline__ int sum8(int v) {
+  v = quad_sum(v);
+  return v + __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
 }
 
 // Largest value over groups of 8 lanes (returned in every lane of the group).

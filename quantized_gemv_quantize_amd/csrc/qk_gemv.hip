@@ -12,12 +12,13 @@
 //               S_q = sum_j sc_j s_j, S_m = sum_j m_j (bsum_2j + bsum_2j+1)
 //               (Q5_K: the same with 5-bit codes, bit 4 from qh)
 //   Q6_K        c = (d_x * d) * S,  S = sum_j sc_j sum_e (q_e - 32) a_e
+//   Q4_1, Q5_1  against Q8_1: c = s * (d_w * d_x) + m_w * s_x, s = sum code a
 // y[row] is the f32 sum of c over the row's blocks.
 //
 // Mapping on the GPU (all kernels):
 //  - one wavefront per output row; its lanes cover a span of consecutive blocks
 //    (Q4_K, Q5_K, Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
-//    Q8_0, Q4_0, Q5_0: 1 lane per 32-element block, 64 blocks per pass);
+//    Q8_0, Q4_0, Q5_0, Q4_1, Q5_1: 1 lane per 32-element block, 64 blocks per pass);
 //  - rows of one or two passes keep the activation blocks a lane needs in
 //    registers, loaded once per wavefront and reused over grid-strided rows;
 //  - longer rows share the activation row through LDS: every lane issues the
@@ -902,6 +903,151 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_0_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Q4_1 and Q5_1 x Q8_1 (candle formats page, VecDotType table: the _1 weight types
+// pair with BlockQ8_1).  Weight value = code * d_w + m_w with unsigned codes, the
+// activation d_x * a, so a block contributes
+//   c = s * (d_w * d_x) + m_w * s_x,   s = sum code * a (exact int32),
+// with s_x the Q8_1 block's stored f16 d_x * sum a.  Blocks of 20 / 24 bytes keep
+// every field 4-byte aligned (Q4_1: d, m, qs[16] at 4; Q5_1: d, m, qh at 4, qs at
+// 8), so each lane loads its block with one dword and one dwordx4 (plus the qh dword).
+// The Q8_1 row is staged into LDS as the Q8_0 row is: codes at a 48-byte stride,
+// then d_x and s_x as f32 per block.
+struct LayoutQ81 {
+  static constexpr int kStride = 48;
+  int64_t off_d, off_s, bytes;
+  __host__ __device__ explicit LayoutQ81(int64_t nb) {
+    off_d = nb * kStride;
+    off_s = off_d + 4 * nb;
+    bytes = align16(off_s + 4 * nb);
+  }
+};
+
+struct StagedQ81 {
+  uint4 piece[kPieces];
+  uint32_t small[kSmall];  // d | s << 16
+};
+
+// Q8_1 block i (36 bytes): pieces 0, 1 = codes at 4 and 20; small unit = d, s at 0.
+template <int NT>
+__device__ __forceinline__ void stage_load_q81(StagedQ81& st, const uint8_t* __restrict__ xq, int nb) {
+  const int np = nb * 2;
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, np - 1);
+    st.piece[i] = load_a4<uint4>(xq + static_cast<uint32_t>((u >> 1) * kQ8_1Bytes + 4 + 16 * (u & 1)));
+  }
+#pragma unroll
+  for (int i = 0; i < kSmall; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, nb - 1);
+    st.small[i] = load_a4<uint32_t>(xq + static_cast<uint32_t>(u * kQ8_1Bytes));
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void stage_place_q81(uint8_t* lds, const LayoutQ81& L, const StagedQ81& st,
+                                                const uint8_t* __restrict__ xq, int nb) {
+  const int np = nb * 2;
+  float* dA = reinterpret_cast<float*>(lds + L.off_d);
+  float* sA = reinterpret_cast<float*>(lds + L.off_s);
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, np - 1);
+    *reinterpret_cast<uint4*>(lds + (u >> 1) * LayoutQ81::kStride + 16 * (u & 1)) = st.piece[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kSmall; ++i) {
+    const int u = min(static_cast<int>(threadIdx.x) + i * NT, nb - 1);
+    dA[u] = f16_to_f32(st.small[i] & 0xFFFFu);
+    sA[u] = f16_to_f32(st.small[i] >> 16);
+  }
+  for (int u = static_cast<int>(threadIdx.x) + kPieces * NT; u < np; u += NT) {
+    *reinterpret_cast<uint4*>(lds + (u >> 1) * LayoutQ81::kStride + 16 * (u & 1)) =
+        load_a4<uint4>(xq + (u >> 1) * kQ8_1Bytes + 4 + 16 * (u & 1));
+  }
+  for (int u = static_cast<int>(threadIdx.x) + kSmall * NT; u < nb; u += NT) {
+    const uint32_t ds = load_a4<uint32_t>(xq + u * kQ8_1Bytes);
+    dA[u] = f16_to_f32(ds & 0xFFFFu);
+    sA[u] = f16_to_f32(ds >> 16);
+  }
+}
+
+template <int NW, int UNR, bool Q5, bool SUMS>
+__global__ __launch_bounds__(NW * 64) void gemv_q4_1_kernel(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  constexpr int kWB = Q5 ? kQ5_1Bytes : kQ4_1Bytes;
+  constexpr int kQs = Q5 ? 8 : 4;  // offset of the 16 nibble bytes
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * NW + wave_id();
+  const bool row_ok = row < n_out;
+  const size_t rb = static_cast<size_t>(nb) * kWB;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 63) >> 6;
+
+  uint4 QS[UNR];
+  uint32_t DM[UNR], QH[UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = min((p0 + j) * 64 + lane, nb - 1);
+      const uint8_t* p = wrow + static_cast<uint32_t>(b * kWB);
+      DM[j] = load_a4<uint32_t>(p);
+      if constexpr (Q5) QH[j] = load_a4<uint32_t>(p + 4);
+      QS[j] = load_a4<uint4>(p + kQs);
+    }
+  };
+  const LayoutQ81 L(nb);
+  StagedQ81 st;
+  stage_load_q81<NW * 64>(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  stage_place_q81<NW * 64>(lds, L, st, xq, nb);
+  __syncthreads();
+
+  const float* dA = reinterpret_cast<const float*>(lds + L.off_d);
+  const float* sA = reinterpret_cast<const float*>(lds + L.off_s);
+  float acc = 0.0f;
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int b = (p0 + j) * 64 + lane;
+      if (!row_ok || b >= nb) continue;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ81::kStride);       // elements 0-15
+      const uint4 a1 = *reinterpret_cast<const uint4*>(lds + b * LayoutQ81::kStride + 16);  // 16-31
+      const uint4 q = QS[j];
+      uint32_t lo[4] = {q.x & kLo4, q.y & kLo4, q.z & kLo4, q.w & kLo4};
+      uint32_t hi[4] = {(q.x >> 4) & kLo4, (q.y >> 4) & kLo4, (q.z >> 4) & kLo4, (q.w >> 4) & kLo4};
+      if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lo[k] = q5_codes(lo[k], QH[j], 4 * k);
+          hi[k] = q5_codes(hi[k], QH[j], 16 + 4 * k);
+        }
+      }
+      int sv = 0;  // codes are at most 31: the signed byte dot is exact
+      sv = dot4(lo[0], a0.x, sv);
+      sv = dot4(lo[1], a0.y, sv);
+      sv = dot4(lo[2], a0.z, sv);
+      sv = dot4(lo[3], a0.w, sv);
+      sv = dot4(hi[0], a1.x, sv);
+      sv = dot4(hi[1], a1.y, sv);
+      sv = dot4(hi[2], a1.z, sv);
+      sv = dot4(hi[3], a1.w, sv);
+      const float dw = f16_to_f32(DM[j] & 0xFFFFu), mw = f16_to_f32(DM[j] >> 16);
+      acc += static_cast<float>(sv) * (dw * dA[b]) + mw * sA[b];
+      if constexpr (SUMS) sums[static_cast<size_t>(row) * nb + b] = sv;
+    }
+  }
+  if (row_ok) {
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Q8_0, Q4_0 and Q5_0 x Q8_0 for NC = 2..4 activation columns: the LDS kernels
 // above with the NC Q8_0 rows staged one after another (LayoutQ80 regions
 // `L.bytes` apart) and each weight block loaded once.  The lane turns its block's
@@ -1501,6 +1647,8 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
     case kQ8_0:
     case kQ4_0:
     case kQ5_0: return LayoutQ80(n_in / 32).bytes;
+    case kQ4_1:
+    case kQ5_1: return LayoutQ81(n_in / 32).bytes;
     default: return -1;
   }
 }
@@ -1646,6 +1794,21 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
       if (passes == 2) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, false>));
       if (passes <= 4) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 4, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 4, true, false>));
       return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 8, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 8, true, false>));
+    }
+    case kQ4_1:
+    case kQ5_1: {
+      const int nb = static_cast<int>(n_in / 32);
+      const int passes = (nb + 63) / 64;
+      if (w_type == kQ4_1) {
+        if (passes == 1) return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 1, false, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 1, false, false>));
+        if (passes == 2) return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 2, false, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 2, false, false>));
+        if (passes <= 4) return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 4, false, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 4, false, false>));
+        return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 8, false, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 8, false, false>));
+      }
+      if (passes == 1) return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 1, true, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 1, true, false>));
+      if (passes == 2) return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 2, true, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 2, true, false>));
+      if (passes <= 4) return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 4, true, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 4, true, false>));
+      return S ? QK_LDS((gemv_q4_1_kernel<kWaves, 8, true, true>)) : QK_LDS((gemv_q4_1_kernel<kWaves, 8, true, false>));
     }
     default:
       return hipErrorInvalidValue;

@@ -1,4 +1,4 @@
-// qk_quantize.hip - activation quantization kernels (Q8_0 and Q8_K) for gfx950.
+// qk_quantize.hip - activation quantization kernels (Q8_0, Q8_1 and Q8_K) for gfx950.
 //
 // Definition (codeloopback "Building Q8_0 and Q4_0 Like ggml", Example 2; candle
 // formats page, BlockQ8_0::from_float and the "一些边界值" edge table):
@@ -7,6 +7,9 @@
 //   id   = 1 / d, or 0 when d is 0;
 //   code = roundf(x * id): halves away from zero, NaN -> 0, saturated to int8.
 // Q8_0 keeps d as f16 (RNE, subnormals kept, overflow -> inf) before 32 codes.
+// Q8_1 (the activation block candle's VecDotType table pairs with Q4_1 and Q5_1;
+// its layout is not printed, so this is a reading): f16 d, then f16 s = d * sum of
+// the block's codes (the sum the weight minimum's term needs), then 32 codes.
 // Q8_K (candle BlockQ8K) keeps d as f32, then 256 codes, then 16 int16 bsums,
 // each the sum of 16 consecutive codes.  The pages give no scale rule of its own
 // for Q8_K; the Q8_0 rule is applied over its 256 elements.
@@ -62,6 +65,36 @@ __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restr
   uint8_t* ob = xq + b * kQ8_0Bytes;
   store_u2(ob + 2 + part * 4, packed);
   if (part == 0) *reinterpret_cast<uint16_t*>(ob) = f32_to_f16_bits(d);
+}
+
+// Q8_1: the Q8_0 block with s = f16(d * sum of the 32 codes) after d (d unrounded
+// f32 in that product; a NaN product, from an infinite d, stored as 0x7E00), codes at
+// byte 4.  8 lanes per block as Q8_0.
+__global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float* __restrict__ x,
+                                                            uint8_t* __restrict__ xq,
+                                                            int64_t nblocks) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t b = t >> 3;
+  const int part = threadIdx.x & 7;
+  const bool valid = b < nblocks;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (valid) v = *reinterpret_cast<const float4*>(x + b * 32 + part * 4);
+  const float amax = max8(abs_max4(v));
+  const float d = amax / 127.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const int c0 = code_q8(v.x * id), c1 = code_q8(v.y * id);
+  const int c2 = code_q8(v.z * id), c3 = code_q8(v.w * id);
+  const int sum = sum8(c0 + c1 + c2 + c3);  // every lane of the block takes part
+  if (!valid) return;
+  uint8_t* ob = xq + b * kQ8_1Bytes;
+  *reinterpret_cast<uint32_t*>(ob + 4 + part * 4) = pack4(c0, c1, c2, c3);
+  if (part == 0) {
+    // an infinite d (a block holding an infinity) has every code 0: the NaN product
+    // is stored as the quiet NaN 0x7E00
+    const float p = static_cast<float>(sum) * d;
+    const uint32_t s_bits = (p != p) ? 0x7E00u : static_cast<uint32_t>(f32_to_f16_bits(p));
+    *reinterpret_cast<uint32_t*>(ob) = static_cast<uint32_t>(f32_to_f16_bits(d)) | (s_bits << 16);
+  }
 }
 
 // One wavefront per 256-element block, 4 consecutive elements per lane.
@@ -266,11 +299,12 @@ hipError_t launch_quantize_row(int type, const float* x, uint8_t* dst, int64_t n
 hipError_t launch_quantize(int act_type, const float* x, uint8_t* xq, int64_t nblocks,
                            hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (nblocks <= 0) return hipSuccess;
-  // Q8_0: 8 lanes per block; Q8_K: one wavefront per block
+  // Q8_0, Q8_1: 8 lanes per block; Q8_K: one wavefront per block
+  const bool q8K = act_type == kQ8_K;
   unsigned grid = 0;
-  if (!launch_grid(act_type == kQ8_0 ? (nblocks * 8 + 255) / 256 : (nblocks + 3) / 4, 256, &grid))
+  if (!launch_grid(q8K ? (nblocks + 3) / 4 : (nblocks * 8 + 255) / 256, 256, &grid))
     return hipErrorInvalidConfiguration;
-  auto* kernel = act_type == kQ8_0 ? quantize_q8_0_kernel : quantize_q8_K_kernel;
+  auto* kernel = q8K ? quantize_q8_K_kernel : act_type == kQ8_1 ? quantize_q8_1_kernel : quantize_q8_0_kernel;
   if (e0 != nullptr || e1 != nullptr) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, e0, e1, 0, x, xq, nblocks);
   } else {

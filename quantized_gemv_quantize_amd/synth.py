@@ -178,6 +178,18 @@ def q4_K_decode_4096x11008(seed=5):
     return {"W": q4_K_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
 
 
+def q4_1_decode_4096x11008(seed=9):
+    """Q4_1 GEMV, 4096 rows x 11008 columns (344 blocks per row, Q8_1 activations); x[11008]."""
+    rng = np.random.default_rng(seed)
+    return {"W": q4_1_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
+
+
+def q5_1_decode_4096x11008(seed=10):
+    """Q5_1 GEMV, 4096 rows x 11008 columns (344 blocks per row, Q8_1 activations); x[11008]."""
+    rng = np.random.default_rng(seed)
+    return {"W": q5_1_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
+
+
 def q5_K_decode_4096x11008(seed=8):
     """Q5_K decode GEMV, 4096 rows x 11008 columns (43 superblocks per row); x[11008]."""
     rng = np.random.default_rng(seed)

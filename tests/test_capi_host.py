@@ -73,7 +73,11 @@ def test_geometry_matches_type_table():
     assert qk.qk_row_bytes(99, 256) == 0
     assert qk.qk_row_bytes(qk.QK_TYPE_Q5_0, 4096) == 2816
     assert qk.qk_row_bytes(qk.QK_TYPE_Q4_1, 4096) == 2560
-    assert qk.qk_block_elems(9) == 0  # Q8_1: named on the pages, never laid out
+    # Q8_1: named on the pages, never laid out; 36 bytes is the reading (f16 d, f16 s,
+    # 32 codes) that the oracle's layout takes too
+    assert qk.qk_block_elems(qk.QK_TYPE_Q8_1) == 32 and qk.qk_block_bytes(qk.QK_TYPE_Q8_1) == 36
+    assert qk.qk_row_bytes(qk.QK_TYPE_Q8_1, 4096) == 4608
+    assert qk.qk_block_elems(10) == 0
 
 
 def test_pairing():
@@ -84,8 +88,9 @@ def test_pairing():
     assert qk.qk_act_type(qk.QK_TYPE_Q5_K) == qk.QK_TYPE_Q8_K
     assert qk.qk_act_type(qk.QK_TYPE_Q5_0) == qk.QK_TYPE_Q8_0
     assert qk.qk_act_type(qk.QK_TYPE_Q8_K) == -1
-    assert qk.qk_act_type(qk.QK_TYPE_Q4_1) == -1   # its partner Q8_1 is only named
-    assert qk.qk_act_type(qk.QK_TYPE_Q5_1) == -1
+    assert qk.qk_act_type(qk.QK_TYPE_Q4_1) == qk.QK_TYPE_Q8_1
+    assert qk.qk_act_type(qk.QK_TYPE_Q5_1) == qk.QK_TYPE_Q8_1
+    assert qk.qk_act_type(qk.QK_TYPE_Q8_1) == -1
 
 
 def test_max_n_in_covers_llm_shapes():
@@ -93,7 +98,7 @@ def test_max_n_in_covers_llm_shapes():
         m = qk.qk_max_n_in(t)
         assert m >= 28672 and m % qk.qk_block_elems(t) == 0
     assert qk.qk_max_n_in(qk.QK_TYPE_Q8_K) == 0
-    assert qk.qk_max_n_in(qk.QK_TYPE_Q4_1) == 0
+    assert qk.qk_max_n_in(qk.QK_TYPE_Q8_1) == 0
 
 
 P = ctypes.c_void_p
@@ -112,6 +117,8 @@ def test_quantize_validation(timed):
     assert st(qk.QK_TYPE_Q4_K, GOOD, GOOD, 256, 1, None) == 1  # weight type
     assert st(99, GOOD, GOOD, 256, 1, None) == 1
     assert st(qk.QK_TYPE_Q8_0, GOOD, GOOD, 33, 1, None) == 3
+    assert st(qk.QK_TYPE_Q8_1, GOOD, GOOD, 48, 1, None) == 3
+    assert st(qk.QK_TYPE_Q8_1, GOOD, ODD, 32, 1, None) == 4
     assert st(qk.QK_TYPE_Q8_K, GOOD, GOOD, 0, 1, None) == 3
     assert st(qk.QK_TYPE_Q8_K, GOOD, GOOD, 256, -1, None) == 3
     assert st(qk.QK_TYPE_Q8_K, None, GOOD, 256, 1, None) == 5
@@ -136,8 +143,9 @@ def test_quantize_row_validation():
 def test_gemv_validation():
     f = "qk_gemv"
     assert _status(f, qk.QK_TYPE_Q8_K, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
-    assert _status(f, qk.QK_TYPE_Q4_1, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
-    assert _status(f, qk.QK_TYPE_Q5_1, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1  # no GEMV
+    assert _status(f, qk.QK_TYPE_Q8_1, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1  # activation only
+    assert _status(f, qk.QK_TYPE_Q4_1, GOOD, 4, 48, GOOD, 1, GOOD, None) == 3
+    assert _status(f, qk.QK_TYPE_Q5_1, GOOD, 4, 256, GOOD, 1, ODD, None) == 4
     assert _status(f, 5, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
     assert _status(f, qk.QK_TYPE_Q4_K, GOOD, 4, 255, GOOD, 1, GOOD, None) == 3
     assert _status(f, qk.QK_TYPE_Q4_K, GOOD, 4, 0, GOOD, 1, GOOD, None) == 3

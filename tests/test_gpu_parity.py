@@ -27,6 +27,7 @@ pytestmark = pytest.mark.gpu
 T8_0, T4_0, T4K, T6K, T8K = (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q4_K,
                              qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q8_K)
 T4_1, T5_0, T5_1, T5K = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_1, qk.QK_TYPE_Q5_K
+T8_1 = qk.QK_TYPE_Q8_1
 Y_TOL = 1e-5
 
 
@@ -97,7 +98,7 @@ def _special_rows(n, rng):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("act", [T8_0, T8K])
+@pytest.mark.parametrize("act", [T8_0, T8_1, T8K])
 @pytest.mark.parametrize("n", [256, 4096, 11008])
 def test_quantize_act_bit_exact(torch_cuda, act, n):
     say("quantize", act, n)
@@ -115,7 +116,7 @@ def test_quantize_act_many_columns(torch_cuda):
     say("quantize many columns")
     rng = np.random.default_rng(7)
     X = rng.standard_normal((64, 4096)).astype(np.float32)
-    for act in (T8_0, T8K):
+    for act in (T8_0, T8_1, T8K):
         assert np.array_equal(host(qk.qk_quantize_act(act, dev(torch_cuda, X))),
                               orc.quantize(act, X))
 
@@ -245,6 +246,8 @@ SHAPES = {
     T8_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
     T4_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
     T5_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
+    T4_1: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
+    T5_1: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
 }
 
 
@@ -279,7 +282,7 @@ def _oracle_gemv(t, W, n_out, n_in, xq, ncols):
     return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4K, T5K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4_1, T5_1, T4K, T5K, T6K])
 def test_gemv_block_sums_and_y(torch_cuda, t):
     rng = np.random.default_rng(300 + t)
     at = orc.act_type(t)
@@ -359,7 +362,7 @@ def test_batched_q4_K_extreme_codes(torch_cuda):
 
 def test_gemv_max_row_length(torch_cuda):
     rng = np.random.default_rng(31)
-    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0):
+    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0, T4_1, T5_1):
         n_in = qk.qk_max_n_in(t)
         say("gemv max n_in", t, n_in)
         W = weights(rng, t, 3, n_in)
@@ -373,7 +376,7 @@ def test_gemv_max_row_length(torch_cuda):
 def test_gemv_zero_activation_gives_zero(torch_cuda):
     # rml ZeroActivationsGiveZero
     rng = np.random.default_rng(5)
-    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0):
+    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0, T4_1, T5_1):
         W = weights(rng, t, 8, 1024)
         xq = qk.qk_quantize_act(orc.act_type(t), torch_cuda.zeros((1, 1024), device="cuda"))
         y = host(qk.qk_gemv(t, dev(torch_cuda, W), 8, 1024, xq, 1))
@@ -777,7 +780,7 @@ SMALL_BATCH = [(37, 2304, 2), (129, 4096, 4), (8300, 256, 5), (45, 11008, 9),
                (3, 28672, 3), (50, 768, 7), (70, 14336, 4)]
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T5K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4_1, T5_1, T5K, T6K])
 @pytest.mark.parametrize("n_out,n_in,ncols", SMALL_BATCH)
 def test_small_batch_gemv_kernels(torch_cuda, t, n_out, n_in, ncols):
     say("small batch", t, n_out, n_in, ncols)
@@ -828,6 +831,35 @@ def test_q80_family_extreme_codes(torch_cuda, t):
         assert_y(y, y_o, l1, f"type {t} extreme codes")
 
 
+@pytest.mark.parametrize("t", [T4_1, T5_1])
+def test_q4_1_q5_1_extreme_codes(torch_cuda, t):
+    # the ends of each code range (Q4_1 0 / 15, Q5_1 0 / 31) against activations of
+    # +-127, with negative and positive minimums: the largest block sums these
+    # formats produce, and the minimum term against the Q8_1 sum field at its ends.
+    rng = np.random.default_rng(58)
+    n_out, n_in = 22, 4096
+    bb = {T4_1: 20, T5_1: 24}[t]
+    W = weights(rng, t, n_out, n_in).reshape(n_out, -1, bb).copy()
+    W[0::2, :, 4:] = 0xFF                    # Q5_1: qh set too, code 31
+    W[1::2, :, 4:] = 0x00
+    W[2::4, :, 2:4] = np.frombuffer(np.float16(0.02).tobytes(), np.uint8)
+    W = W.reshape(n_out, -1)
+    X = np.where(rng.random((3, n_in)) < 0.5, 127.0, -127.0).astype(np.float32)
+    X[1] = 127.0
+    X[2] = -127.0
+    xq = orc.quantize(T8_1, X)
+    assert np.array_equal(host(qk.qk_quantize_act(T8_1, dev(torch_cuda, X))), xq)
+    Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+    for ncols in (1, 3):
+        say("Q4_1 / Q5_1 extreme codes", t, ncols)
+        sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xd, ncols))
+        want = _oracle_sums(t, W, xq, n_out, n_in, ncols).reshape(sums.shape)
+        assert np.array_equal(sums, want)
+        y = host(qk.qk_gemv(t, Wd, n_out, n_in, xd, ncols))
+        y_o, l1 = orc.gemv(t, W, n_out, n_in, xq, ncols)
+        assert_y(y, y_o, l1, f"type {t} extreme codes")
+
+
 def test_q6_K_extreme_codes(torch_cuda):
     # codes 63 and 0 (q - 32 = 31 and -32) with scales +127 and -128 against
     # activations of +-127: the largest |S| the format can produce, exactly.
@@ -861,6 +893,12 @@ def test_q4_K_batched_4096x11008(torch_cuda, ncols):
     X = rng.standard_normal((ncols, 11008)).astype(np.float32)
     say("batched Q4_K 4096x11008", ncols)
     _check_full(torch_cuda, T4K, d["W"], 4096, 11008, X, what=f"Q4_K 4096x11008 x {ncols}")
+
+
+def test_full_q4_1_and_q5_1_decode_4096x11008(torch_cuda):
+    for t, d in ((T4_1, synth.q4_1_decode_4096x11008()), (T5_1, synth.q5_1_decode_4096x11008())):
+        say("full", qk.TYPE_NAMES[t], "4096x11008")
+        _check_full(torch_cuda, t, d["W"], 4096, 11008, d["x"][None, :], what=f"{qk.TYPE_NAMES[t]} 4096x11008")
 
 
 def test_full_q4_K_decode_4096x11008(torch_cuda):

@@ -685,6 +685,11 @@ def test_q8_1_sum_field_hand_worked():
     assert codes[:4] == [127, -127, 16, 1] and sum(codes) == 17
     assert s_ == "4930"
     assert o.quantize(o.Q8_1, np.zeros(32, np.float32)).tobytes() == bytes(36)
+    # an infinity: d = inf (f16 0x7c00), every code 0 (finite * 0, and inf * 0 = NaN
+    # coded 0), so s = 0 * inf, stored as the quiet NaN 0x7e00
+    x[:4] = [np.inf, 1.0, -2.0, 0.0]
+    d, s_, codes = _q8_1_fields(o.quantize(o.Q8_1, x))
+    assert d == "007c" and not any(codes) and s_ == "007e"
 
 
 def _blocks_with_min(t, nblocks, rng, zero_min=False):
