@@ -11,7 +11,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q8_1, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 7, 8, 9, 12, 13, 14, 15
+Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q8_1, Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15
 
 _lib = None
 

@@ -18,8 +18,8 @@
 /* ------------------------------------------------------------------------- */
 /* Type table.                                                                */
 /* [candle] GgmlDType table: block elements / block bytes                    */
-/*   Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q5_1 32/24, Q8_0 32/34, Q4K 256/144,*/
-/*   Q5K 256/176, Q6K 256/210, Q8K 256/292.                                   */
+/*   Q4_0 32/18, Q4_1 32/20, Q5_0 32/22, Q5_1 32/24, Q8_0 32/34, Q2K 256/84, */
+/*   Q3K 256/110, Q4K 256/144, Q5K 256/176, Q6K 256/210, Q8K 256/292.         */
 /* [sipllm] Design, "type_nbytes(t, n) = n / block_size * type_size".        */
 /* ------------------------------------------------------------------------- */
 
@@ -32,6 +32,8 @@ int64_t orc_block_elems(int type) {
     case ORC_Q8_0:
     case ORC_Q8_1:
       return 32;
+    case ORC_Q2_K:
+    case ORC_Q3_K:
     case ORC_Q4_K:
     case ORC_Q5_K:
     case ORC_Q6_K:
@@ -50,6 +52,8 @@ int64_t orc_block_bytes(int type) {
     case ORC_Q5_1: return 24;
     case ORC_Q8_0: return 34;
     case ORC_Q8_1: return 36; /* reading: d f16, s f16, 32 int8 codes */
+    case ORC_Q2_K: return 84;
+    case ORC_Q3_K: return 110;
     case ORC_Q4_K: return 144;
     case ORC_Q5_K: return 176;
     case ORC_Q6_K: return 210;
@@ -78,6 +82,8 @@ int orc_act_type(int weight_type) {
     case ORC_Q4_1:
     case ORC_Q5_1:
       return ORC_Q8_1;
+    case ORC_Q2_K:
+    case ORC_Q3_K:
     case ORC_Q4_K:
     case ORC_Q5_K:
     case ORC_Q6_K:
@@ -414,6 +420,44 @@ static int orc_q5_1_code(const uint8_t* blk, int e) {
   return low4 | (int)(((qh >> e) & 1u) << 4);
 }
 
+/* Q2_K (parity unpinned: the pages give 256 elements in 84 bytes and that the
+ * K-quants carry small integer sub-block scales times an f16 d; the field order and
+ * bit arrangement are GGUF's, assumed here): scales[16] @0, qs[64] @16, d f16 @80,
+ * dmin f16 @82.  Sub-block j is elements 16j .. 16j+15; scales[j] holds its scale in
+ * the low nibble and its min in the high nibble.  Element e: half h = e / 128,
+ * r = e % 128, group g = r / 32, l = r % 32; its code (0..3) is bits 2g, 2g+1 of
+ * qs[32h + l].  Value d * sc_j * code - dmin * m_j, as Q4_K's with 2-bit codes. */
+static int orc_q2_K_code(const uint8_t* blk, int e) {
+  int h = e / 128, r = e % 128, g = r / 32, l = r % 32;
+  return (blk[16 + 32 * h + l] >> (2 * g)) & 3;
+}
+
+static void orc_q2_K_scale_min(const uint8_t* blk, int j, int* sc, int* m) {
+  *sc = blk[j] & 0x0F;
+  *m = blk[j] >> 4;
+}
+
+/* Q3_K (parity unpinned as Q2_K: 256 elements in 110 bytes; GGUF arrangement):
+ * hmask[32] @0, qs[64] @32, scales[12] @96, d f16 @108.  Element e (h, r, g, l as
+ * Q2_K): low 2 bits are bits 2g, 2g+1 of qs[32h + l], bit 2 is bit 4h + g of
+ * hmask[l]; the 3-bit code means code - 4 (-4..3).  Sub-block j (16 elements) has a
+ * 6-bit scale meaning scale - 32: its low 4 bits are the low nibble of scales[j]
+ * (j < 8) or the high nibble of scales[j - 8] (j >= 8), its high 2 bits are bits
+ * 2(j/4), 2(j/4)+1 of scales[8 + j % 4].  Value d * (scale - 32) * (code - 4). */
+static int orc_q3_K_code(const uint8_t* blk, int e) {
+  int h = e / 128, r = e % 128, g = r / 32, l = r % 32;
+  int low2 = (blk[32 + 32 * h + l] >> (2 * g)) & 3;
+  int hbit = (blk[l] >> (4 * h + g)) & 1;
+  return (low2 | (hbit << 2)) - 4;
+}
+
+static int orc_q3_K_scale(const uint8_t* blk, int j) {
+  const uint8_t* s = blk + 96;
+  int low4 = (j < 8) ? (s[j] & 0x0F) : (s[j - 8] >> 4);
+  int high2 = (s[8 + j % 4] >> (2 * (j / 4))) & 3;
+  return (low4 | (high2 << 4)) - 32;
+}
+
 /* Q4_K sub-block (scale, min) pair, get_scale_min_k4:
  * [candle] 块结构: "the first 4 sub-blocks' scale and min are the low 6 bits of
  * the first 8 bytes; the last 4 keep their low 4 bits in the last 4 bytes and
@@ -519,6 +563,22 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
         for (int e = 0; e < 32; ++e) y[e] = (float)orc_q5_0_code(blk, e) * d;
         break;
       }
+      case ORC_Q2_K: { /* d * sc_j * q - dmin * m_j, 16-element j (reading above) */
+        float d = orc_f16_to_f32(orc_get_u16(blk + 80));
+        float dmin = orc_f16_to_f32(orc_get_u16(blk + 82));
+        for (int e = 0; e < 256; ++e) {
+          int sc, m;
+          orc_q2_K_scale_min(blk, e / 16, &sc, &m);
+          y[e] = d * (float)sc * (float)orc_q2_K_code(blk, e) - dmin * (float)m;
+        }
+        break;
+      }
+      case ORC_Q3_K: { /* d * (scale_j - 32) * (code - 4), 16-element j */
+        float d = orc_f16_to_f32(orc_get_u16(blk + 108));
+        for (int e = 0; e < 256; ++e)
+          y[e] = d * (float)orc_q3_K_scale(blk, e / 16) * (float)orc_q3_K_code(blk, e);
+        break;
+      }
       case ORC_Q4_K: { /* [rml] trace: x = d * scale * q - dmin * min */
         float d = orc_f16_to_f32(orc_get_u16(blk));
         float dmin = orc_f16_to_f32(orc_get_u16(blk + 2));
@@ -574,7 +634,8 @@ int orc_dequantize(int type, const uint8_t* src, float* dst, int64_t n) {
 /* ------------------------------------------------------------------------- */
 
 /* Integer quantities kept per weight block: one s for Q8_0, Q4_0, Q5_0, Q4_1,
- * Q5_1, Q6_K; the pair (S_q, S_m) for Q4_K and Q5_K (scale sum and min sum). */
+ * Q5_1, Q3_K, Q6_K; the pair (S_q, S_m) for Q2_K, Q4_K and Q5_K (scale sum and min
+ * sum). */
 int64_t orc_sums_per_block(int weight_type) {
   switch (weight_type) {
     case ORC_Q8_0:
@@ -582,8 +643,10 @@ int64_t orc_sums_per_block(int weight_type) {
     case ORC_Q5_0:
     case ORC_Q4_1:
     case ORC_Q5_1:
+    case ORC_Q3_K:
     case ORC_Q6_K:
       return 1;
+    case ORC_Q2_K:
     case ORC_Q4_K:
     case ORC_Q5_K:
       return 2;
@@ -652,6 +715,41 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
       out[1] = sm;
       return ORC_OK;
     }
+    case ORC_Q2_K: {
+      /* S_q = sum_j sc_j (sum_{e in j} q_e a_e), S_m = sum_j m_j (sum_{e in j} a_e) over
+       * the 16-element sub-blocks; sum a over one sub-block is one stored bsum of the
+       * Q8_K block ([candle] 块结构: bsums serve the min term).  Both routes are
+       * computed and must agree. */
+      const uint8_t* a = xb + 4;
+      int32_t sq = 0, sm = 0, sm_bsums = 0;
+      for (int j = 0; j < 16; ++j) {
+        int sc, m;
+        orc_q2_K_scale_min(wb, j, &sc, &m);
+        int32_t s = 0, sa = 0;
+        for (int e = 16 * j; e < 16 * j + 16; ++e) {
+          s += (int32_t)orc_q2_K_code(wb, e) * (int32_t)(int8_t)a[e];
+          sa += (int32_t)(int8_t)a[e];
+        }
+        sq += sc * s;
+        sm += m * sa;
+        sm_bsums += m * (int32_t)orc_get_i16(xb + 260 + 2 * j);
+      }
+      if (sm != sm_bsums) return ORC_INCONSISTENT;
+      out[0] = sq;
+      out[1] = sm;
+      return ORC_OK;
+    }
+    case ORC_Q3_K: { /* S = sum_j (scale_j - 32) * sum_{e in j} (code_e - 4) a_e */
+      const uint8_t* a = xb + 4;
+      int32_t S = 0;
+      for (int j = 0; j < 16; ++j) {
+        int32_t s = 0;
+        for (int e = 16 * j; e < 16 * j + 16; ++e) s += (int32_t)orc_q3_K_code(wb, e) * (int32_t)(int8_t)a[e];
+        S += (int32_t)orc_q3_K_scale(wb, j) * s;
+      }
+      out[0] = S;
+      return ORC_OK;
+    }
     case ORC_Q6_K: { /* S = sum_j sc_j * sum_{e in j} (q_e - 32) a_e, 16-element j */
       const uint8_t* a = xb + 4;
       const int8_t* sc = (const int8_t*)(wb + 192);
@@ -676,6 +774,7 @@ static int orc_block_ints(int wt, const uint8_t* wb, const uint8_t* xb, int32_t*
  * code * dw + mw and every activation dx * a, so the block's sum is
  * dw dx sum(code a) + mw dx sum(a) = s * (dw * dx) + mw * sx, with sx the Q8_1
  * block's stored f16 dx * sum(a).  Q4_K, Q5_K: c = (dx*d) * S_q - (dx*dmin) * S_m.
+ * Q2_K as Q4_K, Q3_K as Q6_K (each with its own d / dmin offsets).
  * Q6_K: c = (dx*d) * S.  dx of Q8_K is f32 ([candle] BlockQ8K). */
 static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s) {
   switch (wt) {
@@ -706,6 +805,17 @@ static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const
       float d = orc_f16_to_f32(orc_get_u16(wb + 208));
       return (dx * d) * (float)s[0];
     }
+    case ORC_Q2_K: { /* as Q4_K, d and dmin at bytes 80 and 82 */
+      float dx = orc_get_f32(xb);
+      float d = orc_f16_to_f32(orc_get_u16(wb + 80));
+      float dmin = orc_f16_to_f32(orc_get_u16(wb + 82));
+      return (dx * d) * (float)s[0] - (dx * dmin) * (float)s[1];
+    }
+    case ORC_Q3_K: { /* as Q6_K, d at byte 108 */
+      float dx = orc_get_f32(xb);
+      float d = orc_f16_to_f32(orc_get_u16(wb + 108));
+      return (dx * d) * (float)s[0];
+    }
     default:
       return NAN;
   }
@@ -714,8 +824,8 @@ static float orc_block_float(int wt, const uint8_t* wb, const uint8_t* xb, const
 /* The magnitude a block contributes to the tolerance scale: the sum of the
  * absolute values of the float terms its step adds ([cl] Example 10 measures
  * error against the sum of |a*b| over the terms).  One term for Q8_0, Q4_0,
- * Q5_0 and Q6_K; for Q4_1 and Q5_1 the code term s*(dw*dx) and the minimum term
- * mw*sx; for Q4_K and Q5_K the scale term (dx*d)*S_q and the min term
+ * Q5_0, Q3_K and Q6_K; for Q4_1 and Q5_1 the code term s*(dw*dx) and the minimum
+ * term mw*sx; for Q2_K, Q4_K and Q5_K the scale term (dx*d)*S_q and the min term
  * (dx*dmin)*S_m.  Two-term steps can cancel in c while each term is rounded on
  * its own. */
 static double orc_block_l1(int wt, const uint8_t* wb, const uint8_t* xb, const int32_t* s, float c) {
@@ -726,10 +836,11 @@ static double orc_block_l1(int wt, const uint8_t* wb, const uint8_t* xb, const i
     float sx = orc_f16_to_f32(orc_get_u16(xb + 2));
     return fabs((double)((float)s[0] * (dw * dx))) + fabs((double)(mw * sx));
   }
-  if (wt != ORC_Q4_K && wt != ORC_Q5_K) return fabs((double)c);
+  if (wt != ORC_Q4_K && wt != ORC_Q5_K && wt != ORC_Q2_K) return fabs((double)c);
+  int off = (wt == ORC_Q2_K) ? 80 : 0; /* d, dmin */
   float dx = orc_get_f32(xb);
-  float d = orc_f16_to_f32(orc_get_u16(wb));
-  float dmin = orc_f16_to_f32(orc_get_u16(wb + 2));
+  float d = orc_f16_to_f32(orc_get_u16(wb + off));
+  float dmin = orc_f16_to_f32(orc_get_u16(wb + off + 2));
   return fabs((double)((dx * d) * (float)s[0])) + fabs((double)((dx * dmin) * (float)s[1]));
 }
 

@@ -43,6 +43,14 @@
  *   serve Q4K's min term).  Codes and d are pinned by the printed Q8_0 bytes; s by
  *   a hand-worked block; the dot product by f64 brute force over the pinned Q4_1
  *   decoder within the bound of s's f16 rounding, and its integer sum exactly.
+ *   Q2_K and Q3_K: parity unpinned.  The pages give their size (84 and 110 bytes
+ *   per 256 elements, [candle] GgmlDType table), that they are K-quants (16-element
+ *   sub-blocks with small integer scales times the f16 d, [rml] summary) and that
+ *   dequantize_row handles them ([sipllm] Per-format dequant), not their field
+ *   order or bit arrangement; the GGUF arrangement is assumed (stated at the
+ *   decoders).  Pinned: sizes, structure any arrangement of those fields has (each
+ *   code bit moves one element, each scale field one 16-element sub-block), and the
+ *   dot products by f64 brute force against the dequantizer.
  */
 #ifndef QK_ORACLE_H
 #define QK_ORACLE_H
@@ -61,6 +69,8 @@ extern "C" {
 #define ORC_Q5_1 7
 #define ORC_Q8_0 8
 #define ORC_Q8_1 9
+#define ORC_Q2_K 10
+#define ORC_Q3_K 11
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
 #define ORC_Q6_K 14

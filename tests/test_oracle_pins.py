@@ -27,8 +27,8 @@ def test_type_table_matches_printed_geometry():
     # bytes and bits per weight are printed there; the id column is a reading (the
     # pages say the ids follow ggml's enum without printing them), so it is checked
     # for consistency with the oracle's constants only, not as a pin.
-    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q5_1": o.Q5_1, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
-           "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
+    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q5_1": o.Q5_1, "Q8_0": o.Q8_0, "Q2_K": o.Q2_K,
+           "Q3_K": o.Q3_K, "Q4_K": o.Q4_K, "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
     for name, gid, elems, nbytes, bpw in rows("type_table.txt"):
         t = ids[name]
         assert o.block_elems(t) == int(elems)
@@ -38,8 +38,8 @@ def test_type_table_matches_printed_geometry():
 
 def test_type_ids_reading_is_consistent():
     # reading, not a pin: the GGUF enum values used as ids (type_table.txt header)
-    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q5_1": o.Q5_1, "Q8_0": o.Q8_0, "Q4_K": o.Q4_K,
-           "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
+    ids = {"Q4_0": o.Q4_0, "Q4_1": o.Q4_1, "Q5_0": o.Q5_0, "Q5_1": o.Q5_1, "Q8_0": o.Q8_0, "Q2_K": o.Q2_K,
+           "Q3_K": o.Q3_K, "Q4_K": o.Q4_K, "Q5_K": o.Q5_K, "Q6_K": o.Q6_K, "Q8_K": o.Q8_K}
     for name, gid, _, _, _ in rows("type_table.txt"):
         assert ids[name] == int(gid)
 
@@ -66,6 +66,8 @@ def test_pairing_table():
     assert o.act_type(o.Q4_K) == o.Q8_K
     assert o.act_type(o.Q6_K) == o.Q8_K
     assert o.act_type(o.Q5_K) == o.Q8_K
+    assert o.act_type(o.Q2_K) == o.Q8_K   # "Q2K 到 Q6K" -> BlockQ8K
+    assert o.act_type(o.Q3_K) == o.Q8_K
     assert o.act_type(o.Q8_K) == -1
     # the same table pairs Q4_1 and Q5_1 with BlockQ8_1, an activation-only block
     assert o.act_type(o.Q4_1) == o.Q8_1
@@ -569,6 +571,106 @@ def test_q6_K_structure_invariants():
 
 
 # --------------------------------------------------------------------------
+# Q2_K and Q3_K: the pages give their size (candle GgmlDType table: 84 and 110
+# bytes per 256 elements), that the K-quants split a superblock into 16 sub-blocks
+# of 16 (or 8 of 32) whose small integer scales multiply the f16 d (rml summary,
+# candle 块结构 prose), and that Q2K..Q6K pair with BlockQ8K; the field order and
+# bit arrangement are GGUF's (parity unpinned).  Pinned here: structure any
+# arrangement of those fields has.
+# --------------------------------------------------------------------------
+
+def _field_owners(t, b, fields):
+    """For each (byte, mask) field: the elements a flip of it changes."""
+    y0 = o.dequantize(t, b, 256)
+    out = []
+    for k, mask in fields:
+        bb = b.copy()
+        bb[k] ^= mask
+        out.append(np.nonzero(o.dequantize(t, bb, 256) != y0)[0])
+    return y0, out
+
+
+def test_q2_K_structure_invariants():
+    rng = np.random.default_rng(12)
+    b = rng.integers(0, 256, 84, dtype=np.uint8)
+    b[0:16] = rng.integers(1, 16, 16) | (rng.integers(1, 16, 16) << 4)   # sc, m nonzero
+    b[80:82] = np.frombuffer(np.float16(0.5).tobytes(), np.uint8)
+    b[82:84] = np.frombuffer(np.float16(0.25).tobytes(), np.uint8)
+    # the 256 two-bit code fields of the 64 code bytes: each moves exactly one
+    # element, and each element is moved by exactly one
+    y0, owners = _field_owners(o.Q2_K, b, [(16 + k, 3 << (2 * f)) for k in range(64) for f in range(4)])
+    assert all(len(c) == 1 for c in owners)
+    assert sorted(int(c[0]) for c in owners) == list(range(256))
+    # each scale byte's nibbles act on exactly one run of 16 consecutive elements,
+    # the 16 runs tile the superblock (every code 1, so the scale shows everywhere)
+    b1 = b.copy()
+    b1[16:80] = 0x55
+    _, sc_owners = _field_owners(o.Q2_K, b1, [(j, 0x0F) for j in range(16)])
+    _, m_owners = _field_owners(o.Q2_K, b1, [(j, 0xF0) for j in range(16)])
+    runs = sorted(tuple(c) for c in sc_owners)
+    assert runs == [tuple(range(16 * j, 16 * j + 16)) for j in range(16)]
+    assert all(np.array_equal(a, c) for a, c in zip(sc_owners, m_owners))
+    # codes 0: value -dmin * m of the element's sub-block; codes 3: 3 d sc - dmin m
+    for fill, mult in ((0x00, 0), (0xFF, 3)):
+        bb = b.copy()
+        bb[16:80] = fill
+        y = o.dequantize(o.Q2_K, bb, 256)
+        vals = sorted(set(np.round(y.astype(np.float64), 6)))
+        want = sorted(set(np.round([mult * 0.5 * (s & 15) - 0.25 * (s >> 4) for s in b[0:16]], 6)))
+        assert vals == want
+
+
+def test_q3_K_structure_invariants():
+    rng = np.random.default_rng(13)
+    b = rng.integers(0, 256, 110, dtype=np.uint8)
+    b[108:110] = np.frombuffer(np.float16(0.5).tobytes(), np.uint8)
+    # no sub-block scale of 32 (a zero multiplier would hide its elements)
+    while any(o.dequantize(o.Q3_K, b, 256)[16 * j:16 * j + 16].tolist() == [0.0] * 16 for j in range(16)):
+        b[96:108] = rng.integers(0, 256, 12, dtype=np.uint8)
+    # two-bit code fields of qs and the single hmask bits: each moves exactly one
+    # element; both families cover all 256 elements once
+    _, lo = _field_owners(o.Q3_K, b, [(32 + k, 3 << (2 * f)) for k in range(64) for f in range(4)])
+    _, hi = _field_owners(o.Q3_K, b, [(k, 1 << f) for k in range(32) for f in range(8)])
+    assert all(len(c) == 1 for c in lo + hi)
+    assert sorted(int(c[0]) for c in lo) == list(range(256))
+    assert sorted(int(c[0]) for c in hi) == list(range(256))
+    # the high code bit is worth 4 steps of the element's scale
+    y0 = o.dequantize(o.Q3_K, b, 256).astype(np.float64)
+    for k, f in ((0, 0), (5, 3), (31, 7)):
+        bb = b.copy()
+        bb[k] ^= 1 << f
+        y1 = o.dequantize(o.Q3_K, bb, 256).astype(np.float64)
+        e = int(np.nonzero(y1 != y0)[0][0])
+        lowbb = b.copy()
+        # the same element's low field moved by one step, for the step size
+        step = None
+        for kk in range(64):
+            for ff in range(4):
+                c = lowbb.copy()
+                c[32 + kk] ^= 1 << (2 * ff)
+                yc = o.dequantize(o.Q3_K, c, 256).astype(np.float64)
+                if yc[e] != y0[e]:
+                    step = abs(yc[e] - y0[e])
+        assert abs(abs(y1[e] - y0[e]) - 4 * step) == 0
+    # the 96 scale bits: each acts on exactly one run of 16 consecutive elements, each
+    # run is acted on by exactly 6 bits
+    _, sc = _field_owners(o.Q3_K, b, [(96 + k, 1 << f) for k in range(12) for f in range(8)])
+    runs = {}
+    for c in sc:
+        assert len(c) >= 1
+        j = int(c[0]) // 16
+        assert set(int(x) for x in c) <= set(range(16 * j, 16 * j + 16))
+        runs[j] = runs.get(j, 0) + 1
+    assert runs == {j: 6 for j in range(16)}
+    # every code at its middle value (low bits 0, high bit set) or every scale at its
+    # middle value gives zero: codes and scales are offset by half their range
+    bb = b.copy()
+    bb[32:96] = 0
+    bb[0:32] = 0xFF
+    assert not o.dequantize(o.Q3_K, bb, 256).any()
+
+
+# --------------------------------------------------------------------------
 # Round-trip statistics printed on the candle formats page ("往返误差"): the only
 # numbers the pages give that depend on the Q8_K scale rule (its bytes are never
 # printed).  Quantize + dequantize of 262144 N(0,1) values (and the same with one
@@ -837,6 +939,11 @@ def _random_weights(t, nblocks, rng):
     elif t == o.Q6_K:
         w[:, 192:208] = rng.integers(-64, 64, (nblocks, 16)).astype(np.int8).view(np.uint8)
         w[:, 208:210] = h(1e-3, 1e-2)
+    elif t == o.Q2_K:
+        w[:, 80:82] = h(1e-3, 1e-2)
+        w[:, 82:84] = h(1e-3, 1e-2)
+    elif t == o.Q3_K:
+        w[:, 108:110] = h(1e-3, 1e-2)
     return w.reshape(-1)
 
 
@@ -851,7 +958,7 @@ def _act_parts(at, xq, n):
     return np.repeat(d, 256), blk[:, 4:260].view(np.int8).astype(np.int64).reshape(-1)
 
 
-@pytest.mark.parametrize("t", [o.Q8_0, o.Q4_0, o.Q5_0, o.Q4_K, o.Q5_K, o.Q6_K])
+@pytest.mark.parametrize("t", [o.Q8_0, o.Q4_0, o.Q5_0, o.Q4_K, o.Q5_K, o.Q6_K, o.Q2_K, o.Q3_K])
 def test_vec_dot_brute_force(t):
     rng = np.random.default_rng(100 + t)
     at = o.act_type(t)
@@ -870,14 +977,15 @@ def test_vec_dot_brute_force(t):
         f16 = lambda a, off: a[:, off:off + 2].copy().view(np.float16).astype(np.float64)[:, 0]
         if t in (o.Q8_0, o.Q4_0, o.Q5_0):
             exact = np.sum(sums[:, 0] * f16(wb, 0) * dx[::32])
-        elif t in (o.Q4_K, o.Q5_K):
-            exact = np.sum(dx[::256] * (f16(wb, 0) * sums[:, 0] - f16(wb, 2) * sums[:, 1]))
+        elif t in (o.Q4_K, o.Q5_K, o.Q2_K):
+            off = 80 if t == o.Q2_K else 0
+            exact = np.sum(dx[::256] * (f16(wb, off) * sums[:, 0] - f16(wb, off + 2) * sums[:, 1]))
         else:
-            exact = np.sum(dx[::256] * f16(wb, 208) * sums[:, 0])
+            exact = np.sum(dx[::256] * f16(wb, 108 if t == o.Q3_K else 208) * sums[:, 0])
         scale = np.abs(terms).sum()
-        # Q8_0, Q4_0, Q5_0, Q6_K decoded values are exact in f32; the K-quants with a
-        # min (d*sc*q - dmin*m) round once per element.
-        tol = 1e-12 if t not in (o.Q4_K, o.Q5_K) else 1e-7
+        # Q8_0, Q4_0, Q5_0, Q3_K, Q6_K decoded values are exact in f32; the K-quants
+        # with a min (d*sc*q - dmin*m) round once per element.
+        tol = 1e-12 if t not in (o.Q4_K, o.Q5_K, o.Q2_K) else 1e-7
         assert abs(exact - brute) <= tol * scale, (t, n, exact, brute)
         y, l1 = o.vec_dot(t, w, xq, n)
         nbk = n // o.block_elems(t)
