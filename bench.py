@@ -76,6 +76,7 @@ def workloads(qk):
     T4K, T6K, T40, T80 = qk.QK_TYPE_Q4_K, qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q8_0
     T50, T5K = qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_K
     T41, T51, T81 = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_1, qk.QK_TYPE_Q8_1
+    T2K, T3K = qk.QK_TYPE_Q2_K, qk.QK_TYPE_Q3_K
     T8K = qk.QK_TYPE_Q8_K
     return {
         "q4_K_decode_4096x11008": {
@@ -87,6 +88,11 @@ def workloads(qk):
             "gemvs": [("W", T41, 4096, 11008, "x")], "acts": {"x": (T81, 11008, 1)}},
         "q5_1_decode_4096x11008": {
             "gemvs": [("W", T51, 4096, 11008, "x")], "acts": {"x": (T81, 11008, 1)}},
+        # the 2- and 3-bit K-quants (GGUF arrangement) against Q8_K
+        "q2_K_decode_4096x11008": {
+            "gemvs": [("W", T2K, 4096, 11008, "x")], "acts": {"x": (T8K, 11008, 1)}},
+        "q3_K_decode_4096x11008": {
+            "gemvs": [("W", T3K, 4096, 11008, "x")], "acts": {"x": (T8K, 11008, 1)}},
         "q4_K_4096x4096": {
             "gemvs": [("W_q4_K", T4K, 4096, 4096, "x")], "acts": {"x": (T8K, 4096, 1)}},
         "q4_0_4096x4096": {
@@ -132,6 +138,10 @@ def host_inputs(name, qk):
         return synth.q4_K_decode_4096x11008()
     if name == "q5_K_decode_4096x11008":
         return synth.q5_K_decode_4096x11008()
+    if name == "q2_K_decode_4096x11008":
+        return synth.q2_K_decode_4096x11008()
+    if name == "q3_K_decode_4096x11008":
+        return synth.q3_K_decode_4096x11008()
     if name == "q4_1_decode_4096x11008":
         return synth.q4_1_decode_4096x11008()
     if name == "q5_1_decode_4096x11008":
@@ -180,6 +190,11 @@ def gpu_copy_like(torch, w_type, n_out, n_in, gen):
         w[:, :, 0:2] = f16(1e-3, 4e-3)
     elif w_type == synth.Q5_0:
         w[:, :, 0:2] = f16(5e-4, 2e-3)
+    elif w_type == synth.Q2_K:
+        w[:, :, 80:82] = f16(1e-4, 1e-3)
+        w[:, :, 82:84] = f16(1e-4, 1e-3)
+    elif w_type == synth.Q3_K:
+        w[:, :, 108:110] = f16(1e-4, 1e-3)
     elif w_type in (synth.Q4_1, synth.Q5_1):
         w[:, :, 0:2] = f16(1e-3, 4e-3) if w_type == synth.Q4_1 else f16(5e-4, 2e-3)
         w[:, :, 2:4] = f16(-0.03, -0.005)

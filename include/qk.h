@@ -2,7 +2,7 @@
  * qk.h - C ABI of libqk.so, the MI355X (gfx950) block-quantized GEMV library.
  *
  * The library computes y = W x where W is stored row-major as whole ggml blocks
- * (Q8_0, Q4_0, Q5_0, Q4_1, Q5_1, Q4_K, Q5_K or Q6_K, byte-exact GGUF layouts) and x is
+ * (Q8_0, Q4_0, Q5_0, Q4_1, Q5_1, Q2_K, Q3_K, Q4_K, Q5_K or Q6_K, byte-exact GGUF layouts) and x is
  * quantized once per call into int8 activation blocks (Q8_0, Q8_1 or Q8_K) aligned
  * with W's blocks.  Every
  * product inside a block is an exact int32 sum; only the block scales are float.
@@ -12,8 +12,9 @@
  *   "Building Q8_0 and Q4_0 Like ggml" (codeloopback): Q8_0/Q4_0 bytes, Examples 1-11.
  *   "量化格式" (candle formats): type table, BlockQ4K/Q6K/Q8K fields, VecDotType.
  * Q5_1, Q5_K and Q6_K: the pages give their size and the role of each field, not
- * which bit belongs to which element; the GGUF arrangement is implemented (stated
- * below at qk_dequantize_row).  Q8_1: the pages name it as the activation block of
+ * which bit belongs to which element; Q2_K and Q3_K: the pages give their size only.
+ * For all five the GGUF arrangement is implemented (stated below at
+ * qk_dequantize_row).  Q8_1: the pages name it as the activation block of
  * the _1 types without its layout; the reading is stated at qk_quantize_act.
  *
  * Conventions shared by every call:
@@ -44,6 +45,8 @@ extern "C" {
 #define QK_TYPE_Q5_1 7
 #define QK_TYPE_Q8_0 8
 #define QK_TYPE_Q8_1 9
+#define QK_TYPE_Q2_K 10
+#define QK_TYPE_Q3_K 11
 #define QK_TYPE_Q4_K 12
 #define QK_TYPE_Q5_K 13
 #define QK_TYPE_Q6_K 14
@@ -66,7 +69,7 @@ extern "C" {
 #define QK_EPI_SWIGLU 1
 
 /* Elements per block (32 or 256) and bytes per block (Q4_0 18, Q4_1 20, Q5_0 22,
- * Q5_1 24, Q8_0 34, Q8_1 36, Q4_K 144, Q5_K 176, Q6_K 210, Q8_K 292) of a type, 0 for an
+ * Q5_1 24, Q8_0 34, Q8_1 36, Q2_K 84, Q3_K 110, Q4_K 144, Q5_K 176, Q6_K 210, Q8_K 292) of a type, 0 for an
  * unknown id.  Geometry from the candle formats page, "GgmlDType" table (Q8_1's 36
  * bytes are the reading stated at qk_quantize_act). */
 int64_t qk_block_elems(int type);
@@ -78,8 +81,8 @@ int64_t qk_block_bytes(int type);
 int64_t qk_row_bytes(int type, int64_t n);
 
 /* Activation type a weight type is multiplied against (candle "VecDotType" table;
- * codeloopback Example 11): Q4_0, Q5_0, Q8_0 -> Q8_0; Q4_1, Q5_1 -> Q8_1; Q4_K, Q5_K,
- * Q6_K -> Q8_K; -1 otherwise (including the activation-only Q8_1 and Q8_K). */
+ * codeloopback Example 11): Q4_0, Q5_0, Q8_0 -> Q8_0; Q4_1, Q5_1 -> Q8_1; Q2_K, Q3_K,
+ * Q4_K, Q5_K, Q6_K -> Q8_K; -1 otherwise (including the activation-only Q8_1 and Q8_K). */
 int qk_act_type(int weight_type);
 
 /* Human-readable text of a status code (static storage, never NULL). */
@@ -143,7 +146,8 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
 
 /*
  * qk_gemv - y = W x for quantized W and already-quantized activations.
- *   w_type    QK_TYPE_Q8_0, Q4_0, Q5_0, Q4_1, Q5_1, Q4_K, Q5_K or Q6_K (else QK_E_TYPE).
+ *   w_type    QK_TYPE_Q8_0, Q4_0, Q5_0, Q4_1, Q5_1, Q2_K, Q3_K, Q4_K, Q5_K or Q6_K
+ *             (else QK_E_TYPE).
  *   W         n_out rows of qk_row_bytes(w_type, n_in) bytes, contiguous, row-major
  *             (sipllm matmul_quant layout), device.
  *   n_out     output rows, >= 0.
@@ -155,7 +159,8 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
  * For every (row, block): the exact int32 sums of code products (VecDot, rml
  * "Quantized dot products"; the Q4_K / Q5_K min term taken from the activation bsums), then
  * one f32 step with the block scales; y is the f32 sum of those steps.  Q4_1 and Q5_1:
- * s * (d_w * d_x) + m_w * s_x, with s_x the Q8_1 block's f16 sum field.  The
+ * s * (d_w * d_x) + m_w * s_x, with s_x the Q8_1 block's f16 sum field.  Q2_K as
+ * Q4_K over 16-element sub-blocks; Q3_K as Q6_K with codes - 4 and scales - 32.  The
  * summation order differs from a sequential loop, so y matches a sequential f32
  * evaluation to within rounding, not bit for bit.  Several columns: Q4_K at 2
  * columns (3 up to 8192 rows), Q8_0, Q4_0, Q5_0, Q5_K and Q6_K in groups of up to 4 columns run a GEMV
@@ -173,22 +178,30 @@ int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* 
 
 /*
  * qk_dequantize_row - expand n elements (whole blocks) of a weight type to f32.
- *   type      QK_TYPE_Q8_0, Q4_0, Q4_1, Q5_0, Q5_1, Q4_K, Q5_K or Q6_K (Q8_K is an
- *             activation-only format and is refused with QK_E_TYPE, as sipllm's
- *             dequantize_row refuses it).
+ *   type      QK_TYPE_Q8_0, Q4_0, Q4_1, Q5_0, Q5_1, Q2_K, Q3_K, Q4_K, Q5_K or Q6_K
+ *             (Q8_1 and Q8_K are activation-only formats and are refused with
+ *             QK_E_TYPE, as sipllm's dequantize_row refuses them).
  *   src       n / block blocks, device.  A whole matrix is n = n_out * n_in.
  *   dst       out: f32 [n], device.
  *   n         >= 0, a multiple of the block size; 0 enqueues nothing.
  * Values (rml DequantizeRow; candle block table; codeloopback Examples 7, 8): Q8_0
- * d*q; Q4_0 d*(q-8); Q4_1 and Q5_1 q*d + m; Q5_0 d*(q-16); Q4_K and Q5_K
- * d*sc_j*q - dmin*m_j; Q6_K d*sc_j*(q-32).  Each product is exact in f32 (at most
- * one rounding, in the final addition of Q4_1, Q5_1, Q4_K and Q5_K), so the result
+ * d*q; Q4_0 d*(q-8); Q4_1 and Q5_1 q*d + m; Q5_0 d*(q-16); Q2_K, Q4_K and Q5_K
+ * d*sc_j*q - dmin*m_j; Q3_K d*(sc_j-32)*(q-4); Q6_K d*sc_j*(q-32).  Each product is
+ * exact in f32 (at most one rounding, in the final addition of Q4_1, Q5_1, Q2_K, Q4_K
+ * and Q5_K), so the result
  * is bit-exact.
  * Q5_1 (24 B): d f16 @0, m f16 @2, qh u32 @4, qs[16] @8 (the _1 types add an f16 min
  * to the _0 block; the order is GGUF's); code as Q5_0's, unsigned 0..31.
  * Q5_K (176 B): d f16 @0, dmin f16 @2, scales[12] @4 packed as Q4_K's, qh[32] @16,
  * qs[128] @48; element e = 64c + p: low 4 bits as Q4_K's (qs[32c + p % 32], low
  * nibble for p < 32, else high), bit 4 = bit 2c + (p >= 32) of qh[p % 32].
+ * Q2_K (84 B): scales[16] @0 (sub-block j of 16 elements: scale = low nibble, min =
+ * high nibble), qs[64] @16, d f16 @80, dmin f16 @82; element e, h = e / 128,
+ * r = e % 128, g = r / 32, l = r % 32: code (qs[32h + l] >> 2g) & 3.
+ * Q3_K (110 B): hmask[32] @0, qs[64] @32, scales[12] @96, d f16 @108; element e (h,
+ * g, l as Q2_K): low 2 bits (qs[32h + l] >> 2g) & 3, bit 2 = bit 4h + g of hmask[l];
+ * sub-block j's 6-bit scale: low 4 bits the low nibble of scales[j] (j < 8) or the
+ * high nibble of scales[j - 8], high 2 bits (scales[8 + j % 4] >> 2(j / 4)) & 3.
  * Q6_K (210 B): ql[128] @0, qh[64] @128, int8 scales[16] @192, d f16 @208; element
  * e, h = e / 128, r = e % 128, g = r / 32, l = r % 32: low 4 bits the low (g < 2)
  * or high nibble of ql[64h + l + 32 (g & 1)], high 2 bits (qh[32h + l] >> 2g) & 3.
@@ -198,9 +211,9 @@ int qk_dequantize_row(int type, const void* src, float* dst, int64_t n, void* st
 /*
  * qk_gemv_block_sums - the same GEMV kernels, storing the per-block integers they
  * compute instead of y.  For checking exactness; not needed to use the library.
- *   sums      out: int32 [ncols][n_out][n_in / block][k]; k = 2 for Q4_K, Q5_K (the scale
+ *   sums      out: int32 [ncols][n_out][n_in / block][k]; k = 2 for Q2_K, Q4_K, Q5_K (the scale
  *             sum S_q = sum_j sc_j s_j and the min sum S_m = sum_j m_j sum(a_j)),
- *             k = 1 otherwise (Q8_0, Q4_0, Q5_0, Q4_1, Q5_1: the block's code-product sum; Q6_K:
+ *             k = 1 otherwise (Q8_0, Q4_0, Q5_0, Q4_1, Q5_1: the block's code-product sum; Q3_K, Q6_K:
  *             S = sum_j sc_j sum (q - 32) a).
  * Other arguments and errors as qk_gemv.
  */

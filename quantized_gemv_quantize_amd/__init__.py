@@ -14,19 +14,21 @@ QK_TYPE_Q5_0 = 6
 QK_TYPE_Q5_1 = 7
 QK_TYPE_Q8_0 = 8
 QK_TYPE_Q8_1 = 9
+QK_TYPE_Q2_K = 10
+QK_TYPE_Q3_K = 11
 QK_TYPE_Q4_K = 12
 QK_TYPE_Q5_K = 13
 QK_TYPE_Q6_K = 14
 QK_TYPE_Q8_K = 15
-WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_1, QK_TYPE_Q5_1, QK_TYPE_Q4_K,
-                QK_TYPE_Q5_K, QK_TYPE_Q6_K)
+WEIGHT_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_1, QK_TYPE_Q5_1, QK_TYPE_Q2_K,
+                QK_TYPE_Q3_K, QK_TYPE_Q4_K, QK_TYPE_Q5_K, QK_TYPE_Q6_K)
 DEQUANT_TYPES = WEIGHT_TYPES
 QUANT_ROW_TYPES = (QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q4_1, QK_TYPE_Q5_0)
 QK_EPI_NONE = 0
 QK_EPI_SWIGLU = 1
 TYPE_NAMES = {QK_TYPE_Q4_0: "Q4_0", QK_TYPE_Q4_1: "Q4_1", QK_TYPE_Q5_0: "Q5_0", QK_TYPE_Q5_1: "Q5_1",
               QK_TYPE_Q8_0: "Q8_0", QK_TYPE_Q4_K: "Q4_K", QK_TYPE_Q5_K: "Q5_K", QK_TYPE_Q6_K: "Q6_K",
-              QK_TYPE_Q8_1: "Q8_1", QK_TYPE_Q8_K: "Q8_K"}
+              QK_TYPE_Q8_1: "Q8_1", QK_TYPE_Q2_K: "Q2_K", QK_TYPE_Q3_K: "Q3_K", QK_TYPE_Q8_K: "Q8_K"}
 
 # the in-tree build; QK_LIB_PATH names another build of the same sources (the
 # host-sanitizer test runs the host-side checks against one)
@@ -191,7 +193,7 @@ def qk_gemv_timed(w_type, W, n_out, n_in, xq, ncols, y, ev_start, ev_stop, strea
 def qk_gemv_block_sums(w_type, W, n_out, n_in, xq, ncols=1, sums=None, stream=None):
     """Per-block int32 sums [ncols, n_out, n_in/block, k] of the GEMV kernels."""
     import torch
-    k = 2 if w_type in (QK_TYPE_Q4_K, QK_TYPE_Q5_K) else 1
+    k = 2 if w_type in (QK_TYPE_Q2_K, QK_TYPE_Q4_K, QK_TYPE_Q5_K) else 1
     nb = n_in // qk_block_elems(w_type) if qk_block_elems(w_type) else 0
     if sums is None:
         sums = torch.empty((ncols, n_out, nb, k), dtype=torch.int32, device=W.device)

@@ -13,7 +13,8 @@ namespace {
 // Weight formats with a GEMV (a paired activation type).
 bool is_weight(int t) {
   return t == QK_TYPE_Q4_0 || t == QK_TYPE_Q5_0 || t == QK_TYPE_Q8_0 || t == QK_TYPE_Q4_1 ||
-         t == QK_TYPE_Q5_1 || t == QK_TYPE_Q4_K || t == QK_TYPE_Q5_K || t == QK_TYPE_Q6_K;
+         t == QK_TYPE_Q5_1 || t == QK_TYPE_Q2_K || t == QK_TYPE_Q3_K || t == QK_TYPE_Q4_K ||
+         t == QK_TYPE_Q5_K || t == QK_TYPE_Q6_K;
 }
 // Weight formats qk_dequantize_row expands (every GEMV weight format).
 bool is_dequant(int t) { return is_weight(t); }
@@ -53,7 +54,7 @@ int gemv_impl(int w_type, const void* W, int64_t n_out, int64_t n_in, const void
   const int at = qk_act_type(w_type);
   const int64_t xrow = qk_row_bytes(at, n_in);
   const int64_t nb = n_in / qk_block_elems(w_type);
-  const int k = (w_type == QK_TYPE_Q4_K || w_type == QK_TYPE_Q5_K) ? 2 : 1;
+  const int k = (w_type == QK_TYPE_Q2_K || w_type == QK_TYPE_Q4_K || w_type == QK_TYPE_Q5_K) ? 2 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Small batches read W once with the multi-column GEMV kernel: Q4_K at 2 columns,
   // and at 3 when the matrix has at most 8192 rows (beyond, and from 4 columns, the
@@ -122,6 +123,8 @@ int64_t qk_block_elems(int type) {
     case QK_TYPE_Q5_1:
     case QK_TYPE_Q8_0:
     case QK_TYPE_Q8_1: return 32;
+    case QK_TYPE_Q2_K:
+    case QK_TYPE_Q3_K:
     case QK_TYPE_Q4_K:
     case QK_TYPE_Q5_K:
     case QK_TYPE_Q6_K:
@@ -138,6 +141,8 @@ int64_t qk_block_bytes(int type) {
     case QK_TYPE_Q5_1: return 24;
     case QK_TYPE_Q8_0: return 34;
     case QK_TYPE_Q8_1: return 36;
+    case QK_TYPE_Q2_K: return 84;
+    case QK_TYPE_Q3_K: return 110;
     case QK_TYPE_Q4_K: return 144;
     case QK_TYPE_Q5_K: return 176;
     case QK_TYPE_Q6_K: return 210;
@@ -159,6 +164,8 @@ int qk_act_type(int weight_type) {
     case QK_TYPE_Q8_0: return QK_TYPE_Q8_0;
     case QK_TYPE_Q4_1:
     case QK_TYPE_Q5_1: return QK_TYPE_Q8_1;
+    case QK_TYPE_Q2_K:
+    case QK_TYPE_Q3_K:
     case QK_TYPE_Q4_K:
     case QK_TYPE_Q5_K:
     case QK_TYPE_Q6_K: return QK_TYPE_Q8_K;

@@ -13,6 +13,8 @@
 //         qh[p % 32] as bit 4 (GGUF arrangement; the pages give the field roles)
 //   Q6_K  d * sc_j * (q - 32) for 16-element sub-block j; q = 4 bits from ql and
 //         2 bits from qh in the GGUF arrangement (the pages give only the roles)
+//   Q2_K  d * sc_j * q - dmin * m_j, Q3_K d * (sc_j - 32) * (q - 4), 16-element j
+//         (GGUF arrangement; the pages give only the sizes)
 // Each product is exact in f32 (at most 23 significant bits), so the order of
 // multiplication and any FMA contraction leave the result unchanged.
 //
@@ -229,6 +231,67 @@ __global__ __launch_bounds__(256) void dequant_q6_K_kernel(const uint8_t* __rest
   }
 }
 
+// Q2_K and Q3_K (GGUF arrangement; the pages give their sizes only): lane takes 4
+// consecutive elements e0 .. e0 + 3 of one 16-element sub-block j = e0 / 16, half
+// h = e0 / 128, group g = (e0 % 128) / 32, l = e0 % 32: 2 code bits at bits 2g of
+// qs[32h + l .. +3].  Q2_K (84 B): d * (scales[j] & 15) * q - dmin * (scales[j] >> 4),
+// d, dmin at bytes 80, 82.  Q3_K (110 B, 2-byte aligned): bit 2 of the code from
+// bit 4h + g of hmask[l], value d * (scale_j - 32) * (code - 4), scale_j's low 4 bits
+// from byte j (j < 8) or the high nibble of byte j - 8, its high 2 bits from bits
+// 2(j/4) of byte 8 + j % 4 of scales[12] at 96; d at byte 108.
+struct Q23Part {
+  uint32_t q, m;  // code bytes (qs) and, for Q3_K, hmask bytes of this lane's 4 elements
+  uint32_t d;     // Q2_K: d | dmin << 16; Q3_K: d
+  uint32_t sc;    // Q2_K: scales[j]; Q3_K: the unsigned 6-bit scale of sub-block j
+};
+
+template <int Q3>
+__global__ __launch_bounds__(256) void dequant_q23_K_kernel(const uint8_t* __restrict__ src,
+                                                            float* __restrict__ dst,
+                                                            int64_t nblocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kSB;
+  if (b0 >= nblocks) return;
+  const int e0 = 4 * lane;
+  const int j = e0 >> 4, h = e0 >> 7, g = (e0 & 127) >> 5, l = e0 & 31;
+  constexpr int kBytes = Q3 ? kQ3_KBytes : kQ2_KBytes;
+  Q23Part v[kSB];
+#pragma unroll
+  for (int k = 0; k < kSB; ++k) {
+    const uint8_t* blk = src + min(b0 + k, nblocks - 1) * kBytes;
+    if constexpr (Q3 != 0) {
+      v[k].q = load_u2<uint32_t>(blk + 32 + 32 * h + l);
+      v[k].m = load_u2<uint32_t>(blk + l);
+      v[k].d = *reinterpret_cast<const uint16_t*>(blk + 108);
+      const int low4 = (j < 8) ? (blk[96 + j] & 15) : (blk[96 + j - 8] >> 4);
+      v[k].sc = static_cast<uint32_t>(low4 | (((blk[104 + (j & 3)] >> (2 * (j >> 2))) & 3) << 4));
+    } else {
+      v[k].q = *reinterpret_cast<const uint32_t*>(blk + 16 + 32 * h + l);
+      v[k].m = 0u;
+      v[k].d = *reinterpret_cast<const uint32_t*>(blk + 80);
+      v[k].sc = blk[j];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kSB; ++k) {
+    if (b0 + k >= nblocks) break;  // uniform over the wavefront
+    uint32_t q = (v[k].q >> (2 * g)) & 0x03030303u;
+    float4 o;
+    if constexpr (Q3 != 0) {
+      q |= ((v[k].m >> (4 * h + g)) & 0x01010101u) << 2;
+      o = scale_bytes_signed(q, f16_to_f32(v[k].d) * static_cast<float>(static_cast<int>(v[k].sc) - 32), 4);
+    } else {
+      const float dsc = f16_to_f32(v[k].d & 0xFFFF) * static_cast<float>(v[k].sc & 15);
+      const float dm = f16_to_f32(v[k].d >> 16) * static_cast<float>(v[k].sc >> 4);
+      o.x = dsc * static_cast<float>(q & 0xFF) - dm;
+      o.y = dsc * static_cast<float>((q >> 8) & 0xFF) - dm;
+      o.z = dsc * static_cast<float>((q >> 16) & 0xFF) - dm;
+      o.w = dsc * static_cast<float>(q >> 24) - dm;
+    }
+    *reinterpret_cast<float4*>(dst + (b0 + k) * 256 + e0) = o;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t nblocks,
@@ -248,6 +311,8 @@ hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t n
     case kQ4_K: dequant_q4_K_kernel<0><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ5_K: dequant_q4_K_kernel<1><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     case kQ6_K: dequant_q6_K_kernel<<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ2_K: dequant_q23_K_kernel<0><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
+    case kQ3_K: dequant_q23_K_kernel<1><<<grid, 256, 0, s>>>(src, dst, nblocks); break;
     default:
       return hipErrorInvalidValue;
   }

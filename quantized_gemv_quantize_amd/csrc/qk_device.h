@@ -25,6 +25,8 @@ constexpr int kQ4_1Bytes = 20;
 constexpr int kQ5_0Bytes = 22;
 constexpr int kQ5_1Bytes = 24;
 constexpr int kQ8_1Bytes = 36;
+constexpr int kQ2_KBytes = 84;
+constexpr int kQ3_KBytes = 110;
 constexpr int kQ4_KBytes = 144;
 constexpr int kQ5_KBytes = 176;
 constexpr int kQ6_KBytes = 210;

@@ -13,11 +13,13 @@
 //               (Q5_K: the same with 5-bit codes, bit 4 from qh)
 //   Q6_K        c = (d_x * d) * S,  S = sum_j sc_j sum_e (q_e - 32) a_e
 //   Q4_1, Q5_1  against Q8_1: c = s * (d_w * d_x) + m_w * s_x, s = sum code a
+//   Q2_K        as Q4_K over 16-element sub-blocks (2-bit codes, 4-bit scale / min)
+//   Q3_K        c = (d_x * d) * S,  S = sum_j (sc_j - 32) sum_e (q_e - 4) a_e
 // y[row] is the f32 sum of c over the row's blocks.
 //
 // Mapping on the GPU (all kernels):
 //  - one wavefront per output row; its lanes cover a span of consecutive blocks
-//    (Q4_K, Q5_K, Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
+//    (Q2_K .. Q6_K: 4 lanes per 256-element superblock, 16 superblocks per pass;
 //    Q8_0, Q4_0, Q5_0, Q4_1, Q5_1: 1 lane per 32-element block, 64 blocks per pass);
 //  - rows of one or two passes keep the activation blocks a lane needs in
 //    registers, loaded once per wavefront and reused over grid-strided rows;
@@ -397,6 +399,169 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
           o[0] = sq;
           o[1] = sm;
         }
+      }
+    }
+  }
+  if (row_ok) {
+    const float total = wave_sum(acc);
+    if (lane == 0 && y != nullptr) y[row] = total;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q2_K and Q3_K x Q8_K (GGUF arrangement; the pages give only their sizes and that
+// they are K-quants paired with Q8K).  Sub-blocks of 16 elements; element
+// e = 128h + 32g + l has its 2 low code bits at bits 2g of qs[32h + l].
+//   Q2_K (84 B: scales[16] @0, qs @16, d @80, dmin @82): code 0..3, scales[j] =
+//        scale | min << 4;  c = (d_x d) S_q - (d_x dmin) S_m with
+//        S_q = sum_j sc_j sum q a, S_m = sum_j m_j bsum_j (one Q8_K bsum per sub-block).
+//   Q3_K (110 B: hmask @0, qs @32, scales[12] @96, d @108): bit 2 of the code is bit
+//        4h + g of hmask[l]; value (code - 4) (scale_j - 32), the 6-bit scale split
+//        into a low nibble (byte j, or the high nibble of byte j - 8) and 2 high bits
+//        (bits 2(j/4) of byte 8 + j % 4);  c = (d_x d) S,
+//        S = sum_j (scale_j - 32) (sum code a - 4 bsum_j), codes taken unsigned 0..7.
+// Lane (u = lane >> 2, c = lane & 3) of a pass takes elements 64c .. 64c + 63 of
+// superblock 16 pass + u: sub-blocks 4c .. 4c + 3, half h = c >> 1, shift groups
+// 2(c & 1) and 2(c & 1) + 1, the 32 qs bytes of half h.  Q3_K blocks are only
+// 2-byte aligned; every load stays inside its block.
+template <int Q3>
+struct KQuant23 {
+  static constexpr int kBytes = Q3 ? kQ3_KBytes : kQ2_KBytes;
+  static constexpr int kQs = Q3 ? 32 : 16;
+};
+
+struct Q23Loads {
+  uint4 q0, q1;    // qs bytes 32h .. 32h + 31 of the lane's half
+  uint4 m0, m1;    // Q3_K: hmask bytes 0-31
+  uint32_t sc;     // Q2_K: scales[4c .. 4c+3]; Q3_K: scale bytes 96-99
+  uint32_t sc1;    // Q3_K: scale bytes 100-103
+  uint32_t sc2;    // Q3_K: scale bytes 104-107
+  uint32_t d;      // Q2_K: d | dmin << 16; Q3_K: d
+};
+
+template <int Q3>
+__device__ __forceinline__ void q23_load(Q23Loads& v, const uint8_t* p, int c) {
+  using F = KQuant23<Q3>;
+  const int h = c >> 1;
+  if constexpr (Q3 != 0) {
+    v.q0 = load_u2<uint4>(p + F::kQs + 32 * h);
+    v.q1 = load_u2<uint4>(p + F::kQs + 32 * h + 16);
+    v.m0 = load_u2<uint4>(p);
+    v.m1 = load_u2<uint4>(p + 16);
+    const uint2 s01 = load_u2<uint2>(p + 96);
+    v.sc = s01.x;
+    v.sc1 = s01.y;
+    v.sc2 = load_u2<uint32_t>(p + 104);
+    v.d = *reinterpret_cast<const uint16_t*>(p + 108);
+  } else {
+    v.q0 = load_a4<uint4>(p + F::kQs + 32 * h);
+    v.q1 = load_a4<uint4>(p + F::kQs + 32 * h + 16);
+    v.sc = load_a4<uint32_t>(p + 4 * c);
+    v.d = load_a4<uint32_t>(p + 80);
+  }
+}
+
+// This lane's exact integer partials of one superblock: Q2_K (S_q, S_m), Q3_K (S, 0).
+template <int Q3>
+__device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk, int c) {
+  const uint8_t* ap = ablk + 4 + 64 * c;
+  const uint4 a[4] = {lds_a4<uint4>(ap), lds_a4<uint4>(ap + 16), lds_a4<uint4>(ap + 32), lds_a4<uint4>(ap + 48)};
+  const uint2 bsw = lds_a4<uint2>(ablk + 260 + 8 * c);  // bsums 4c .. 4c+3
+  const int bs[4] = {sext16_lo(bsw.x), sext16_hi(bsw.x), sext16_lo(bsw.y), sext16_hi(bsw.y)};
+  const int h = c >> 1, g0 = 2 * (c & 1);
+  uint32_t scw;  // byte k: the unsigned scale of sub-block 4c + k
+  if constexpr (Q3 != 0) {
+    const uint32_t low = (((c & 1) ? v.sc1 : v.sc) >> (4 * (c >> 1))) & kLo4;
+    scw = low | (((v.sc2 >> (2 * c)) & 0x03030303u) << 4);
+  } else {
+    scw = v.sc;
+  }
+  int sq = 0, sm = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 q = (k & 1) ? v.q1 : v.q0;  // bytes l = 16 (k & 1) .. + 15
+    const int sh = 2 * (g0 + (k >> 1));
+    uint32_t w[4] = {(q.x >> sh) & 0x03030303u, (q.y >> sh) & 0x03030303u, (q.z >> sh) & 0x03030303u,
+                     (q.w >> sh) & 0x03030303u};
+    if constexpr (Q3 != 0) {
+      const uint4 m = (k & 1) ? v.m1 : v.m0;
+      const int hb = 4 * h + g0 + (k >> 1);
+      w[0] |= ((m.x >> hb) & kOnes) << 2;
+      w[1] |= ((m.y >> hb) & kOnes) << 2;
+      w[2] |= ((m.z >> hb) & kOnes) << 2;
+      w[3] |= ((m.w >> hb) & kOnes) << 2;
+    }
+    int s = 0;
+    s = dot4(w[0], a[k].x, s);
+    s = dot4(w[1], a[k].y, s);
+    s = dot4(w[2], a[k].z, s);
+    s = dot4(w[3], a[k].w, s);
+    const int scb = static_cast<int>((scw >> (8 * k)) & 0xFFu);
+    if constexpr (Q3 != 0) {
+      sq = mad24(scb - 32, s - 4 * bs[k], sq);
+    } else {
+      sq = mad24(scb & 15, s, sq);
+      sm = mad24(scb >> 4, bs[k], sm);
+    }
+  }
+  return make_int2(sq, sm);
+}
+
+template <int NW, int UNR, bool SUMS, int Q3>
+__global__ __launch_bounds__(NW * 64) void gemv_q23_K_kernel(
+    const uint8_t* __restrict__ W, int n_out, int nb, const uint8_t* __restrict__ xq,
+    float* __restrict__ y, int32_t* __restrict__ sums) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * NW + wave_id();
+  const int c = lane & 3, u = lane >> 2;
+  const bool row_ok = row < n_out;
+  using F = KQuant23<Q3>;
+  const size_t rb = static_cast<size_t>(nb) * F::kBytes;
+  const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
+  const int passes = (nb + 15) >> 4;
+
+  Q23Loads V[UNR];
+  auto issue = [&](int p0) {
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = min((p0 + j) * 16 + u, nb - 1);
+      q23_load<Q3>(V[j], wrow + static_cast<uint32_t>(sb * F::kBytes), c);
+    }
+  };
+  ImageQ8K st;
+  image_load_q8K<NW * 64>(st, xq, nb);
+  sched_fence();
+  issue(0);
+  sched_fence();
+  image_place_q8K<NW * 64>(lds, st, xq, nb);
+  __syncthreads();
+
+  float acc = 0.0f;
+  for (int p0 = 0; p0 < passes; p0 += UNR) {
+    if (p0 > 0) issue(p0);
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+      const int sb = (p0 + j) * 16 + u;
+      if (!row_ok || sb >= nb) continue;  // uniform over the 4 lanes of a superblock
+      const uint8_t* ablk = lds + sb * kQ8_KBytes;
+      const int2 part = q23_chunk<Q3>(V[j], ablk, c);
+      const int sq = quad_sum(part.x);
+      const float dx = lds_a4<float>(ablk);
+      float cb;
+      if constexpr (Q3 != 0) {
+        cb = (dx * f16_to_f32(V[j].d)) * static_cast<float>(sq);
+      } else {
+        const int sm = quad_sum(part.y);
+        cb = (dx * f16_to_f32(V[j].d & 0xFFFF)) * static_cast<float>(sq) -
+             (dx * f16_to_f32(V[j].d >> 16)) * static_cast<float>(sm);
+        if constexpr (SUMS) {
+          if (c == 0) sums[(static_cast<size_t>(row) * nb + sb) * 2 + 1] = sm;
+        }
+      }
+      acc += (c == 0) ? cb : 0.0f;
+      if constexpr (SUMS) {
+        if (c == 0) sums[(static_cast<size_t>(row) * nb + sb) * (Q3 ? 1 : 2)] = sq;
       }
     }
   }
@@ -1641,6 +1806,8 @@ hipError_t launch_rows(K kernel, int64_t n_out, int rpw, int max_waves, hipStrea
 
 int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
   switch (w_type) {
+    case kQ2_K:
+    case kQ3_K:
     case kQ4_K:
     case kQ5_K:
     case kQ6_K: return align16(n_in / 256 * kQ8_KBytes);
@@ -1794,6 +1961,21 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
       if (passes == 2) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, false>));
       if (passes <= 4) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 4, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 4, true, false>));
       return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 8, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 8, true, false>));
+    }
+    case kQ2_K:
+    case kQ3_K: {
+      const int nb = static_cast<int>(n_in / 256);
+      const int passes = (nb + 15) / 16;
+      if (w_type == kQ2_K) {
+        if (passes == 1) return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 1, true, 0>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 1, false, 0>));
+        if (passes == 2) return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 2, true, 0>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 2, false, 0>));
+        if (passes == 3) return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 3, true, 0>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 3, false, 0>));
+        return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 4, true, 0>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 4, false, 0>));
+      }
+      if (passes == 1) return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 1, true, 1>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 1, false, 1>));
+      if (passes == 2) return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 2, true, 1>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 2, false, 1>));
+      if (passes == 3) return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 3, true, 1>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 3, false, 1>));
+      return S ? QK_LDS((gemv_q23_K_kernel<kWaves, 4, true, 1>)) : QK_LDS((gemv_q23_K_kernel<kWaves, 4, false, 1>));
     }
     case kQ4_1:
     case kQ5_1: {

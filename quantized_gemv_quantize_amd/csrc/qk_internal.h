@@ -7,7 +7,7 @@
 
 namespace qk {
 
-enum WType : int { kQ4_0 = 2, kQ4_1 = 3, kQ5_0 = 6, kQ5_1 = 7, kQ8_0 = 8, kQ8_1 = 9, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14, kQ8_K = 15 };
+enum WType : int { kQ4_0 = 2, kQ4_1 = 3, kQ5_0 = 6, kQ5_1 = 7, kQ8_0 = 8, kQ8_1 = 9, kQ2_K = 10, kQ3_K = 11, kQ4_K = 12, kQ5_K = 13, kQ6_K = 14, kQ8_K = 15 };
 
 // The work-items of one launch are counted in 32 bits (the dispatch packet's grid
 // size).  Launchers size their grids through launch_grid and refuse a larger launch

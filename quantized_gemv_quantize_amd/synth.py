@@ -13,11 +13,12 @@ Recipes (one numpy default_rng(seed) per workload, drawn in the order listed):
 """
 import numpy as np
 
-Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q4_K, Q5_K, Q6_K, Q8_K = 2, 3, 6, 7, 8, 12, 13, 14, 15
-BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256,
-               Q8_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210,
-               Q8_K: 292}
+Q4_0, Q4_1, Q5_0, Q5_1, Q8_0, Q8_1 = 2, 3, 6, 7, 8, 9
+Q2_K, Q3_K, Q4_K, Q5_K, Q6_K, Q8_K = 10, 11, 12, 13, 14, 15
+BLOCK_ELEMS = {Q4_0: 32, Q4_1: 32, Q5_0: 32, Q5_1: 32, Q8_0: 32, Q8_1: 32, Q2_K: 256, Q3_K: 256,
+               Q4_K: 256, Q5_K: 256, Q6_K: 256, Q8_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q5_0: 22, Q5_1: 24, Q8_0: 34, Q8_1: 36, Q2_K: 84, Q3_K: 110,
+               Q4_K: 144, Q5_K: 176, Q6_K: 210, Q8_K: 292}
 
 
 def uniform_bytes(rng, shape):
@@ -99,9 +100,27 @@ def q6_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
     return b.reshape(n_out, nb * 210)
 
 
+def q2_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
+    """Q2_K rows: 16 scale bytes and 64 qs bytes uniform, f16 d, dmin ~ U[d_range]."""
+    nb = n_in // 256
+    b = uniform_bytes(rng, (n_out, nb, 84))
+    b[:, :, 80:82] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    b[:, :, 82:84] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 84)
+
+
+def q3_K_blocks(rng, n_out, n_in, d_range=(1e-4, 1e-3)):
+    """Q3_K rows: hmask, qs and scale bytes uniform, f16 d ~ U[d_range]."""
+    nb = n_in // 256
+    b = uniform_bytes(rng, (n_out, nb, 110))
+    b[:, :, 108:110] = _f16_bytes(rng.uniform(*d_range, size=(n_out, nb)))
+    return b.reshape(n_out, nb * 110)
+
+
 def weight_blocks(rng, t, n_out, n_in):
     return {Q4_0: q4_0_blocks, Q4_1: q4_1_blocks, Q5_0: q5_0_blocks, Q5_1: q5_1_blocks,
-            Q4_K: q4_K_blocks, Q5_K: q5_K_blocks, Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
+            Q2_K: q2_K_blocks, Q3_K: q3_K_blocks, Q4_K: q4_K_blocks, Q5_K: q5_K_blocks,
+            Q6_K: q6_K_blocks}[t](rng, n_out, n_in)
 
 
 def gaussian(rng, shape, std=1.0):
@@ -188,6 +207,18 @@ def q5_1_decode_4096x11008(seed=10):
     """Q5_1 GEMV, 4096 rows x 11008 columns (344 blocks per row, Q8_1 activations); x[11008]."""
     rng = np.random.default_rng(seed)
     return {"W": q5_1_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
+
+
+def q2_K_decode_4096x11008(seed=11):
+    """Q2_K decode GEMV, 4096 rows x 11008 columns (43 superblocks per row); x[11008]."""
+    rng = np.random.default_rng(seed)
+    return {"W": q2_K_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
+
+
+def q3_K_decode_4096x11008(seed=12):
+    """Q3_K decode GEMV, 4096 rows x 11008 columns (43 superblocks per row); x[11008]."""
+    rng = np.random.default_rng(seed)
+    return {"W": q3_K_blocks(rng, 4096, 11008), "x": gaussian(rng, (11008,))}
 
 
 def q5_K_decode_4096x11008(seed=8):

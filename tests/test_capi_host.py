@@ -59,7 +59,8 @@ def test_library_is_built_for_gfx950_only():
 
 def test_geometry_matches_type_table():
     ids = {"Q4_0": qk.QK_TYPE_Q4_0, "Q4_1": qk.QK_TYPE_Q4_1, "Q5_0": qk.QK_TYPE_Q5_0, "Q5_1": qk.QK_TYPE_Q5_1,
-           "Q8_0": qk.QK_TYPE_Q8_0, "Q4_K": qk.QK_TYPE_Q4_K, "Q5_K": qk.QK_TYPE_Q5_K,
+           "Q8_0": qk.QK_TYPE_Q8_0, "Q2_K": qk.QK_TYPE_Q2_K, "Q3_K": qk.QK_TYPE_Q3_K,
+           "Q4_K": qk.QK_TYPE_Q4_K, "Q5_K": qk.QK_TYPE_Q5_K,
            "Q6_K": qk.QK_TYPE_Q6_K, "Q8_K": qk.QK_TYPE_Q8_K}
     for name, gid, elems, nbytes, _ in rows("type_table.txt"):
         assert ids[name] == int(gid)
@@ -77,7 +78,7 @@ def test_geometry_matches_type_table():
     # 32 codes) that the oracle's layout takes too
     assert qk.qk_block_elems(qk.QK_TYPE_Q8_1) == 32 and qk.qk_block_bytes(qk.QK_TYPE_Q8_1) == 36
     assert qk.qk_row_bytes(qk.QK_TYPE_Q8_1, 4096) == 4608
-    assert qk.qk_block_elems(10) == 0
+    assert qk.qk_block_elems(16) == 0
 
 
 def test_pairing():
@@ -91,6 +92,8 @@ def test_pairing():
     assert qk.qk_act_type(qk.QK_TYPE_Q4_1) == qk.QK_TYPE_Q8_1
     assert qk.qk_act_type(qk.QK_TYPE_Q5_1) == qk.QK_TYPE_Q8_1
     assert qk.qk_act_type(qk.QK_TYPE_Q8_1) == -1
+    assert qk.qk_act_type(qk.QK_TYPE_Q2_K) == qk.QK_TYPE_Q8_K
+    assert qk.qk_act_type(qk.QK_TYPE_Q3_K) == qk.QK_TYPE_Q8_K
 
 
 def test_max_n_in_covers_llm_shapes():

@@ -28,6 +28,7 @@ T8_0, T4_0, T4K, T6K, T8K = (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q4_K,
                              qk.QK_TYPE_Q6_K, qk.QK_TYPE_Q8_K)
 T4_1, T5_0, T5_1, T5K = qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q5_0, qk.QK_TYPE_Q5_1, qk.QK_TYPE_Q5_K
 T8_1 = qk.QK_TYPE_Q8_1
+T2K, T3K = qk.QK_TYPE_Q2_K, qk.QK_TYPE_Q3_K
 Y_TOL = 1e-5
 
 
@@ -216,14 +217,14 @@ def _edge_scale_blocks(t, rng, nblocks):
     specials = np.array([0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF, 0x3C00, 0xBC00, 0x0000],
                         dtype=np.uint16).view(np.uint8).reshape(-1, 2)
     offs = {T8_0: [0], T4_0: [0], T4_1: [0, 2], T5_0: [0], T5_1: [0, 2], T4K: [0, 2], T5K: [0, 2],
-            T6K: [208]}[t]
+            T6K: [208], T2K: [80, 82], T3K: [108]}[t]
     for i in range(nblocks):
         for o in offs:
             b[i, o:o + 2] = specials[(i + o) % len(specials)]
     return b.reshape(-1)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0, T5_1, T4K, T5K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T4_1, T5_0, T5_1, T2K, T3K, T4K, T5K, T6K])
 def test_dequantize_bit_exact(torch_cuda, t):
     rng = np.random.default_rng(200 + t)
     for nblocks in (1, 3, 17, 1000):
@@ -243,6 +244,8 @@ SHAPES = {
     T4K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T6K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T5K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
+    T2K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
+    T3K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T8_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
     T4_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
     T5_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
@@ -282,7 +285,7 @@ def _oracle_gemv(t, W, n_out, n_in, xq, ncols):
     return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4_1, T5_1, T4K, T5K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4_1, T5_1, T2K, T3K, T4K, T5K, T6K])
 def test_gemv_block_sums_and_y(torch_cuda, t):
     rng = np.random.default_rng(300 + t)
     at = orc.act_type(t)
@@ -362,7 +365,7 @@ def test_batched_q4_K_extreme_codes(torch_cuda):
 
 def test_gemv_max_row_length(torch_cuda):
     rng = np.random.default_rng(31)
-    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0, T4_1, T5_1):
+    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0, T4_1, T5_1, T2K, T3K):
         n_in = qk.qk_max_n_in(t)
         say("gemv max n_in", t, n_in)
         W = weights(rng, t, 3, n_in)
@@ -376,7 +379,7 @@ def test_gemv_max_row_length(torch_cuda):
 def test_gemv_zero_activation_gives_zero(torch_cuda):
     # rml ZeroActivationsGiveZero
     rng = np.random.default_rng(5)
-    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0, T4_1, T5_1):
+    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0, T4_1, T5_1, T2K, T3K):
         W = weights(rng, t, 8, 1024)
         xq = qk.qk_quantize_act(orc.act_type(t), torch_cuda.zeros((1, 1024), device="cuda"))
         y = host(qk.qk_gemv(t, dev(torch_cuda, W), 8, 1024, xq, 1))
@@ -780,7 +783,7 @@ SMALL_BATCH = [(37, 2304, 2), (129, 4096, 4), (8300, 256, 5), (45, 11008, 9),
                (3, 28672, 3), (50, 768, 7), (70, 14336, 4)]
 
 
-@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4_1, T5_1, T5K, T6K])
+@pytest.mark.parametrize("t", [T8_0, T4_0, T5_0, T4_1, T5_1, T2K, T3K, T5K, T6K])
 @pytest.mark.parametrize("n_out,n_in,ncols", SMALL_BATCH)
 def test_small_batch_gemv_kernels(torch_cuda, t, n_out, n_in, ncols):
     say("small batch", t, n_out, n_in, ncols)
@@ -860,6 +863,40 @@ def test_q4_1_q5_1_extreme_codes(torch_cuda, t):
         assert_y(y, y_o, l1, f"type {t} extreme codes")
 
 
+@pytest.mark.parametrize("t", [T2K, T3K])
+def test_q2_K_q3_K_extreme_codes(torch_cuda, t):
+    # codes at both ends (Q2_K 0 / 3, Q3_K -4 / +3), the largest scales and mins (Q2_K
+    # nibbles 15; Q3_K scale fields 0 and 63, i.e. -32 and +31) against activations of
+    # +-127: the largest |S| these formats produce, exactly.
+    rng = np.random.default_rng(59)
+    n_out, n_in = 24, 11008
+    bb = {T2K: 84, T3K: 110}[t]
+    W = weights(rng, t, n_out, n_in).reshape(n_out, -1, bb).copy()
+    if t == T2K:
+        W[:, :, 0:16] = 0xFF                 # scale 15, min 15
+        W[0::2, :, 16:80] = 0xFF             # code 3
+        W[1::2, :, 16:80] = 0x00             # code 0
+    else:
+        W[0::2, :, 0:96] = 0xFF              # code 7 - 4 = +3
+        W[1::2, :, 0:96] = 0x00              # code -4
+        W[0::4, :, 96:108] = 0xFF            # scale 63 - 32 = +31
+        W[1::4, :, 96:108] = 0x00            # scale -32
+    W = W.reshape(n_out, -1)
+    X = np.where(rng.random((3, n_in)) < 0.5, 127.0, -127.0).astype(np.float32)
+    X[1] = 127.0
+    X[2] = -127.0
+    xq = orc.quantize(orc.Q8_K, X)
+    Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+    for ncols in (1, 3):
+        say("Q2_K / Q3_K extreme codes", t, ncols)
+        sums = host(qk.qk_gemv_block_sums(t, Wd, n_out, n_in, xd, ncols))
+        want = _oracle_sums(t, W, xq, n_out, n_in, ncols).reshape(sums.shape)
+        assert np.array_equal(sums, want)
+        y = host(qk.qk_gemv(t, Wd, n_out, n_in, xd, ncols))
+        y_o, l1 = orc.gemv(t, W, n_out, n_in, xq, ncols)
+        assert_y(y, y_o, l1, f"type {t} extreme codes")
+
+
 def test_q6_K_extreme_codes(torch_cuda):
     # codes 63 and 0 (q - 32 = 31 and -32) with scales +127 and -128 against
     # activations of +-127: the largest |S| the format can produce, exactly.
@@ -893,6 +930,12 @@ def test_q4_K_batched_4096x11008(torch_cuda, ncols):
     X = rng.standard_normal((ncols, 11008)).astype(np.float32)
     say("batched Q4_K 4096x11008", ncols)
     _check_full(torch_cuda, T4K, d["W"], 4096, 11008, X, what=f"Q4_K 4096x11008 x {ncols}")
+
+
+def test_full_q2_K_and_q3_K_decode_4096x11008(torch_cuda):
+    for t, d in ((T2K, synth.q2_K_decode_4096x11008()), (T3K, synth.q3_K_decode_4096x11008())):
+        say("full", qk.TYPE_NAMES[t], "4096x11008")
+        _check_full(torch_cuda, t, d["W"], 4096, 11008, d["x"][None, :], what=f"{qk.TYPE_NAMES[t]} 4096x11008")
 
 
 def test_full_q4_1_and_q5_1_decode_4096x11008(torch_cuda):
