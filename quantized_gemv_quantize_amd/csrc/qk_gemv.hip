@@ -1769,12 +1769,23 @@ __global__ __launch_bounds__(NW * 64) void gemv_q80_reg(
   }
 }
 
+// Dynamic LDS above 64 KB has to be allowed for the kernel on the current device;
+// set on every such launch (the library keeps no per-device state).
+template <typename K>
+hipError_t allow_lds(K kernel, int64_t lds_bytes) {
+  if (lds_bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(lds_bytes));
+}
+
 template <int NW, typename K>
 hipError_t launch(K kernel, int64_t n_out, int64_t lds_bytes, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1, const uint8_t* W, int nb, const uint8_t* xq, float* y,
                   int32_t* sums) {
   unsigned grid = 0;
   if (!launch_grid((n_out + NW - 1) / NW, NW * 64, &grid)) return hipErrorInvalidConfiguration;
+  const hipError_t attr = allow_lds(kernel, lds_bytes);
+  if (attr != hipSuccess) return attr;
   const int n = static_cast<int>(n_out);
   if (e0 != nullptr || e1 != nullptr) {
     hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), static_cast<uint32_t>(lds_bytes),
@@ -1828,9 +1839,9 @@ constexpr int kMaxWaves = 4096;
 
 bool gemv_cols_fits(int w_type, int64_t n_in, int64_t ncols) {
   if (ncols < 2 || ncols > kGemvMaxCols) return false;
-  if (w_type == kQ8_0 || w_type == kQ4_0 || w_type == kQ5_0) return ncols * LayoutQ80(n_in / 32).bytes <= kMaxLdsBytes;
+  if (w_type == kQ8_0 || w_type == kQ4_0 || w_type == kQ5_0) return ncols * LayoutQ80(n_in / 32).bytes <= kColsLdsBytes;
   if (w_type != kQ4_K && w_type != kQ5_K && w_type != kQ6_K) return false;
-  return ncols * align16(n_in / 256 * kQ8_KBytes) <= kMaxLdsBytes;
+  return ncols * align16(n_in / 256 * kQ8_KBytes) <= kColsLdsBytes;
 }
 
 namespace {
@@ -2031,6 +2042,8 @@ hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, 
     if (!launch_grid((n_out + kWaves - 1) / kWaves, kWaves * 64, &gx)) return hipErrorInvalidConfiguration;
     const dim3 grid(gx, static_cast<unsigned>(ncols));
     const int64_t lds = gemv_lds_bytes(kQ4_K, n_in);
+    const hipError_t attr = allow_lds(gemv_q4_K_pair_kernel<kWaves, 3, EPI, Q5>, lds);
+    if (attr != hipSuccess) return attr;
     launch_ev(gemv_q4_K_pair_kernel<kWaves, 3, EPI, Q5>, grid, dim3(kWaves * 64), static_cast<size_t>(lds), s, e0, e1,
               W1, W2, n, nb, xq, out);
   }

@@ -64,7 +64,14 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in);
 hipError_t launch_gemv_pair(int w_type, const uint8_t* W1, const uint8_t* W2, int64_t n_out, int64_t n_in,
                             const uint8_t* xq, int64_t ncols, int swiglu, float* out, hipStream_t s,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
-constexpr int64_t kMaxLdsBytes = 65536;
+// LDS one workgroup may address on gfx950: all 160 KB of a CU (the device reports
+// it as sharedMemPerBlock).  The longest activation row a one-column GEMV stages;
+// launches above 64 KB opt in per kernel (hipFuncAttributeMaxDynamicSharedMemorySize).
+constexpr int64_t kMaxLdsBytes = 163840;
+// LDS budget of the multi-column GEMV kernels' column groups: at most 64 KB, so
+// that two 4-wavefront workgroups still share a CU; longer groups run fewer columns
+// per launch (the measured trade-off of those kernels).
+constexpr int64_t kColsLdsBytes = 65536;
 
 hipError_t launch_dequantize(int type, const uint8_t* src, float* dst, int64_t nblocks,
                              hipStream_t s);

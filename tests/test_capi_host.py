@@ -100,6 +100,8 @@ def test_max_n_in_covers_llm_shapes():
     for t in qk.WEIGHT_TYPES:
         m = qk.qk_max_n_in(t)
         assert m >= 28672 and m % qk.qk_block_elems(t) == 0
+    # one workgroup stages up to 160 KB of activation blocks: 561 Q8_K blocks
+    assert qk.qk_max_n_in(qk.QK_TYPE_Q4_K) == 561 * 256
     assert qk.qk_max_n_in(qk.QK_TYPE_Q8_K) == 0
     assert qk.qk_max_n_in(qk.QK_TYPE_Q8_1) == 0
 

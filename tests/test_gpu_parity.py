@@ -376,6 +376,54 @@ def test_gemv_max_row_length(torch_cuda):
         assert_y(y, y_o, l1, f"type {t} max n_in {n_in}")
 
 
+def test_lds_budget_matches_device(torch_cuda):
+    # the one-column kernels stage rows up to 160 KB of activation blocks in one
+    # workgroup's LDS: the device must let a workgroup address that much
+    props = torch_cuda.cuda.get_device_properties(0)
+    say("sharedMemPerBlock", props.shared_memory_per_block)
+    assert props.shared_memory_per_block >= 163840
+    n = qk.qk_max_n_in(T4K)
+    assert n // 256 * 292 <= 163840 < (n // 256 + 1) * 292
+
+
+def test_long_rows_beyond_64KB_lds(torch_cuda):
+    # rows whose activation blocks need more than 64 KB of LDS: the launches opt in
+    # to the larger dynamic LDS; every path that takes such rows (one column, column
+    # groups falling back to one column per launch, the matrix-core kernel over a
+    # long K, the gate / up pair) against the oracle
+    rng = np.random.default_rng(33)
+    n_in = qk.qk_max_n_in(T4K)
+    assert n_in // 256 * 292 > 65536
+    n_out = 37
+    W = weights(rng, T4K, n_out, n_in)
+    X = rng.standard_normal((16, n_in)).astype(np.float32)
+    xq = orc.quantize(orc.Q8_K, X)
+    Wd, xd = dev(torch_cuda, W), dev(torch_cuda, xq)
+    for ncols in (1, 3, 16):
+        say("long rows Q4_K", n_in, ncols)
+        sums = host(qk.qk_gemv_block_sums(T4K, Wd, n_out, n_in, xd, ncols))
+        assert np.array_equal(sums, _oracle_sums(T4K, W, xq[:ncols], n_out, n_in, ncols).reshape(sums.shape))
+        y = host(qk.qk_gemv(T4K, Wd, n_out, n_in, xd, ncols))
+        y_o, l1 = orc.gemv(T4K, W, n_out, n_in, xq[:ncols], ncols)
+        assert_y(y, y_o, l1, f"Q4_K n_in {n_in} ncols {ncols}")
+    say("long rows pair", n_in)
+    W2 = weights(rng, T4K, n_out, n_in)
+    out = host(qk.qk_gemv_pair(T4K, Wd, dev(torch_cuda, W2), n_out, n_in, xd, 1, qk.QK_EPI_NONE))
+    y1, l1a = orc.gemv(T4K, W, n_out, n_in, xq[:1], 1)
+    y2, l1b = orc.gemv(T4K, W2, n_out, n_in, xq[:1], 1)
+    assert_y(out.reshape(2, n_out)[0], y1[0], l1a[0], "pair y1 long rows")
+    assert_y(out.reshape(2, n_out)[1], y2[0], l1b[0], "pair y2 long rows")
+    for t in (T8_0, T4_1, T6K):
+        n_t = qk.qk_max_n_in(t)
+        say("long rows", t, n_t)
+        Wt = weights(rng, t, 5, n_t)
+        Xt = rng.standard_normal((2, n_t)).astype(np.float32)
+        xt = orc.quantize(orc.act_type(t), Xt)
+        y = host(qk.qk_gemv(t, dev(torch_cuda, Wt), 5, n_t, dev(torch_cuda, xt), 2))
+        y_o, l1 = orc.gemv(t, Wt, 5, n_t, xt, 2)
+        assert_y(y, y_o, l1, f"type {t} n_in {n_t} ncols 2")
+
+
 def test_gemv_zero_activation_gives_zero(torch_cuda):
     # rml ZeroActivationsGiveZero
     rng = np.random.default_rng(5)
