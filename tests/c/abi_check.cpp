@@ -73,6 +73,14 @@ std::vector<uint8_t> weights(int type, int64_t n_out, int64_t n_in) {
       put_f16(blk + 2, 1e-4, 1e-3);
     } else if (type == QK_TYPE_Q6_K) {
       put_f16(blk + 208, 1e-4, 1e-3);
+    } else if (type == QK_TYPE_Q2_K) {
+      put_f16(blk + 80, 1e-4, 1e-3);
+      put_f16(blk + 82, 1e-4, 1e-3);
+    } else if (type == QK_TYPE_Q3_K) {
+      put_f16(blk + 108, 1e-4, 1e-3);
+    } else if (type == QK_TYPE_Q4_1 || type == QK_TYPE_Q5_1) {
+      put_f16(blk, 1e-3, 4e-3);
+      put_f16(blk + 2, -0.03, -0.005);
     } else {
       put_f16(blk, 1e-3, 4e-3);
     }
@@ -116,8 +124,9 @@ int check_type(int type, int64_t n_out, int64_t n_in, int64_t ncols) {
 
   // activation blocks
   std::vector<uint8_t> xq_o(static_cast<size_t>(xbytes));
-  const int qrc = at == QK_TYPE_Q8_0 ? orc_quantize_q8_0(x.data(), xq_o.data(), n_in * ncols)
-                                     : orc_quantize_q8_K(x.data(), xq_o.data(), n_in * ncols);
+  const int qrc = at == QK_TYPE_Q8_0   ? orc_quantize_q8_0(x.data(), xq_o.data(), n_in * ncols)
+                  : at == QK_TYPE_Q8_1 ? orc_quantize_q8_1(x.data(), xq_o.data(), n_in * ncols)
+                                       : orc_quantize_q8_K(x.data(), xq_o.data(), n_in * ncols);
   if (qrc != ORC_OK || std::memcmp(xq.data(), xq_o.data(), xq.size()) != 0) {
     std::snprintf(what, sizeof what, "type %d: activation blocks differ from the oracle", type);
     fail(what);
@@ -190,7 +199,8 @@ int main() {
     std::printf("no GPU visible\n");
     return 2;
   }
-  const int types[] = {QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_K, QK_TYPE_Q5_K, QK_TYPE_Q6_K};
+  const int types[] = {QK_TYPE_Q8_0, QK_TYPE_Q4_0, QK_TYPE_Q5_0, QK_TYPE_Q4_1, QK_TYPE_Q5_1,
+                       QK_TYPE_Q2_K, QK_TYPE_Q3_K, QK_TYPE_Q4_K, QK_TYPE_Q5_K, QK_TYPE_Q6_K};
   for (int t : types) {
     // one column (GEMV kernels) and three (Q4_K: the matrix-core path), ragged rows,
     // rows of two passes and of three (the LDS-staged kernels)
