@@ -134,4 +134,44 @@ __device__ __forceinline__ float wave_max(float v) {
                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63))));
 }
 
+// ---------------------------------------------------------------------------
+// Activation quantization (codeloopback Example 2's rule; candle BlockQ8K layout),
+// shared by the quantize kernels and the GEMV that quantizes its own x.
+
+// roundf, halves away from zero; NaN -> 0; saturated to int8.
+__device__ __forceinline__ int code_q8(float v) {
+  if (v != v) return 0;
+  float r = roundf(v);
+  r = fminf(fmaxf(r, -128.0f), 127.0f);
+  return static_cast<int>(r);
+}
+
+__device__ __forceinline__ uint32_t pack4(int c0, int c1, int c2, int c3) {
+  return (static_cast<uint32_t>(c0) & 0xFFu) | ((static_cast<uint32_t>(c1) & 0xFFu) << 8) |
+         ((static_cast<uint32_t>(c2) & 0xFFu) << 16) | ((static_cast<uint32_t>(c3) & 0xFFu) << 24);
+}
+
+// Largest |x| of 4 values folded from 0, so NaN never wins (fmaxf returns the
+// other operand) and an all-NaN block gives 0, as the sequential definition does.
+__device__ __forceinline__ float abs_max4(float4 v) {
+  return fmaxf(fmaxf(fmaxf(fmaxf(0.0f, fabsf(v.x)), fabsf(v.y)), fabsf(v.z)), fabsf(v.w));
+}
+
+// One Q8_K block by one wavefront, lane l holding elements 4l .. 4l+3 in v: d = amax
+// / 127 (f32), codes roundf(x / d) via id = 1 / d (0 when d is 0), the 16 int16 code
+// sums, written at ob (global memory or LDS: d @0, codes @4, bsums @260).
+__device__ __forceinline__ void q8K_block(float4 v, int lane, uint8_t* ob) {
+  const float amax = wave_max(abs_max4(v));
+  const float d = amax / 127.0f;
+  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+  const int c0 = code_q8(v.x * id), c1 = code_q8(v.y * id);
+  const int c2 = code_q8(v.z * id), c3 = code_q8(v.w * id);
+  *reinterpret_cast<uint32_t*>(ob + 4 + lane * 4) = pack4(c0, c1, c2, c3);
+  const int s16 = quad_sum(c0 + c1 + c2 + c3);  // 16 codes = 4 lanes
+  if ((lane & 3) == 0) {
+    *reinterpret_cast<int16_t*>(ob + 260 + 2 * (lane >> 2)) = static_cast<int16_t>(s16);
+  }
+  if (lane == 0) *reinterpret_cast<float*>(ob) = d;
+}
+
 }  // namespace qk

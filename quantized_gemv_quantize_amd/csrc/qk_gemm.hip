@@ -96,18 +96,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // Launch shape: NT 16-token tiles, RT 16-row tiles per workgroup, KS compute
 // wavefronts per row tile splitting the superblocks, P superblocks of weights in
-// flight per compute wavefront; SW staging wavefronts copy the activations.
-template <int NT_, int RT_, int KS_, int P_, int SW_ = 4>
+// flight per compute wavefront; SW staging wavefronts copy the activations in
+// chunks of KC superblocks (at most 16 / NT: two chunks fill the LDS).
+template <int NT_, int RT_, int KS_, int P_, int SW_ = 4, int KC_ = 16 / NT_>
 struct Cfg {
   static constexpr int NT = NT_, RT = RT_, KS = KS_, P = P_, SW = SW_;
-  static constexpr int KC = 16 / NT;            // superblocks per LDS chunk
+  static constexpr int KC = KC_;                // superblocks per LDS chunk
   static constexpr int QC = KC / KS;            // superblocks per wavefront and chunk
   static constexpr int B = P > QC ? P : QC;     // superblocks per loop iteration
   static constexpr int kCW = RT * KS;           // compute wavefronts
   static constexpr int kWaves = kCW + SW;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kST = 64 * SW;           // staging threads
-  static constexpr int kChunk = KC * NT * kBT;  // 78,848 bytes
+  static constexpr int kChunk = KC * NT * kBT;  // 78,848 bytes for KC = 16 / NT
   static constexpr int kLds = kZeroBytes + 2 * kChunk;
   static constexpr int kPieces = KC * NT * 256;  // 16-byte code pieces per chunk
   static constexpr int kPPT = kPieces / kST;
@@ -116,7 +117,7 @@ struct Cfg {
   static_assert(KC % KS == 0 && QC >= 1, "whole superblocks per wavefront and chunk");
   static_assert(B % QC == 0 && B % P == 0, "whole chunks and whole weight rings per iteration");
   static_assert(kST == 256 && kPieces % kST == 0, "piece k of a staging thread is image k");
-  static_assert(kPairs == kST, "one staging thread per (superblock, token) pair");
+  static_assert(kPairs <= kST, "at most one (superblock, token) pair per staging thread");
   static_assert(kRedBytes <= 2 * kChunk, "the K-split reduction fits the chunk buffers");
   static_assert(kLds <= 160 * 1024, "one workgroup's LDS fits a CU");
 };
@@ -196,6 +197,7 @@ __device__ __forceinline__ void stage_store(const Stage<C>& st, const StageMap<C
       h4[e] = pack_bf16(hi[2 * e], hi[2 * e + 1]);
       l4[e] = pack_bf16(lo[2 * e], lo[2 * e + 1]);
     }
+    if (m.psb >= C::KC) return;  // smaller chunks: more staging threads than pairs
     uint8_t* img = buf + m.pimg;
     *reinterpret_cast<u4*>(img + kDigOff + m.ptok * 16) = h4;        // lanes 0-15
     *reinterpret_cast<u4*>(img + kDigOff + 256 + m.ptok * 16) = l4;  // lanes 16-31
@@ -476,12 +478,12 @@ hipError_t launch_cfg(const uint8_t* W, int n_out, int nb, const uint8_t* xq, in
   return launch_kernel<C, false>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
 }
 
-template <int NT, int KS1, int KS2, int KS4, int P>
+template <int NT, int KS1, int KS2, int KS4, int P, int KC24 = 16 / NT>
 hipError_t launch_nt(int rt, const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, int rows_wg,
                      float* y, int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (rt == 1) return launch_cfg<Cfg<NT, 1, KS1, P>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
-  if (rt == 2) return launch_cfg<Cfg<NT, 2, KS2, P>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
-  return launch_cfg<Cfg<NT, 4, KS4, P>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
+  if (rt == 2) return launch_cfg<Cfg<NT, 2, KS2, P, 4, KC24>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
+  return launch_cfg<Cfg<NT, 4, KS4, P, 4, KC24>>(W, n_out, nb, xq, ncols, rows_wg, y, sums, s, e0, e1);
 }
 
 }  // namespace
@@ -502,8 +504,13 @@ hipError_t launch_gemm_q4K(const uint8_t* W, int64_t n_out, int64_t n_in, const 
   // splitting each row tile's superblocks, plus 4 staging wavefronts; 2 (up to 16
   // tokens) or 4 superblocks of weights in flight per compute wavefront (measured
   // on 14336 x 4096: 16 tokens 11.8 us with 2 against 12.6 with 4 and 13.5 with 8;
-  // 64 tokens 20.7 us with 4 against 22.1 with 2 and 22.6 with 8)
-  if (nc <= 16) return launch_nt<1, 8, 4, 2, 2>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
+  // 64 tokens 20.7 us with 4 against 22.1 with 2 and 22.6 with 8).  Up to 16
+  // tokens on two or four row tiles the activations go in chunks of 4 superblocks,
+  // so the products start after a quarter of the staging (14336 x 4096: 11.1
+  // against 11.7 us with whole 16-superblock chunks; 2-superblock chunks 12.9);
+  // one row tile keeps 16-superblock chunks and 8 K-split wavefronts (4096 x 11008:
+  // 12.2 against 13.8 us)
+  if (nc <= 16) return launch_nt<1, 8, 4, 2, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
   if (nc <= 32) return launch_nt<2, 8, 4, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
   return launch_nt<4, 4, 4, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
 }

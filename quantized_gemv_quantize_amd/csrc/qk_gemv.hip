@@ -420,10 +420,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
 //        into a low nibble (byte j, or the high nibble of byte j - 8) and 2 high bits
 //        (bits 2(j/4) of byte 8 + j % 4);  c = (d_x d) S,
 //        S = sum_j (scale_j - 32) (sum code a - 4 bsum_j), codes taken unsigned 0..7.
-// Lane (u = lane >> 2, c = lane & 3) of a pass takes elements 64c .. 64c + 63 of
-// superblock 16 pass + u: sub-blocks 4c .. 4c + 3, half h = c >> 1, shift groups
-// 2(c & 1) and 2(c & 1) + 1, the 32 qs bytes of half h.  Q3_K blocks are only
-// 2-byte aligned; every load stays inside its block.
+// Lane (u = lane >> 2, c = lane & 3) of a pass takes superblock 16 pass + u.
+//  - Q2_K: elements 64c .. 64c + 63 (sub-blocks 4c .. 4c + 3, half h = c >> 1, shift
+//    groups 2 (c & 1) and 2 (c & 1) + 1), from the 32 qs bytes of half h, the 4 scale
+//    bytes of its sub-blocks and d / dmin: 84-byte blocks keep every field 4-byte
+//    aligned.
+//  - Q3_K: qs bytes 16c .. 16c + 15 (half h = c >> 1, l = 16 (c & 1) + i), which in
+//    shift group g hold elements 128h + 32g + 16 (c & 1) + i, sub-block 8h + 2g +
+//    (c & 1); with the 16 hmask bytes of its l range each qs and hmask byte goes
+//    through the address unit once or twice per superblock instead of four times
+//    (measured on 4096 x 11008: 7.6 against 9.3 us with the Q2_K mapping, which in
+//    turn is faster for Q2_K: 5.1 against 5.6 us).  The blocks are only 2-byte
+//    aligned; every load stays inside its block.
 template <int Q3>
 struct KQuant23 {
   static constexpr int kBytes = Q3 ? kQ3_KBytes : kQ2_KBytes;
@@ -431,32 +439,27 @@ struct KQuant23 {
 };
 
 struct Q23Loads {
-  uint4 q0, q1;    // qs bytes 32h .. 32h + 31 of the lane's half
-  uint4 m0, m1;    // Q3_K: hmask bytes 0-31
-  uint32_t sc;     // Q2_K: scales[4c .. 4c+3]; Q3_K: scale bytes 96-99
-  uint32_t sc1;    // Q3_K: scale bytes 100-103
-  uint32_t sc2;    // Q3_K: scale bytes 104-107
-  uint32_t d;      // Q2_K: d | dmin << 16; Q3_K: d
+  uint4 q0, q1;   // Q2_K: qs bytes 32h .. 32h + 31; Q3_K: q0 = qs bytes 16c .. 16c + 15
+  uint4 m;        // Q3_K: hmask bytes 16 (c & 1) .. + 15
+  uint2 sc;       // Q2_K: sc.x = scales[4c .. 4c + 3]; Q3_K: scale bytes 96-103
+  uint32_t sc2;   // Q3_K: scale bytes 104-107
+  uint32_t d;     // Q2_K: d | dmin << 16; Q3_K: d
 };
 
 template <int Q3>
 __device__ __forceinline__ void q23_load(Q23Loads& v, const uint8_t* p, int c) {
   using F = KQuant23<Q3>;
-  const int h = c >> 1;
   if constexpr (Q3 != 0) {
-    v.q0 = load_u2<uint4>(p + F::kQs + 32 * h);
-    v.q1 = load_u2<uint4>(p + F::kQs + 32 * h + 16);
-    v.m0 = load_u2<uint4>(p);
-    v.m1 = load_u2<uint4>(p + 16);
-    const uint2 s01 = load_u2<uint2>(p + 96);
-    v.sc = s01.x;
-    v.sc1 = s01.y;
+    v.q0 = load_u2<uint4>(p + F::kQs + 16 * c);
+    v.m = load_u2<uint4>(p + 16 * (c & 1));
+    v.sc = load_u2<uint2>(p + 96);
     v.sc2 = load_u2<uint32_t>(p + 104);
     v.d = *reinterpret_cast<const uint16_t*>(p + 108);
   } else {
+    const int h = c >> 1;
     v.q0 = load_a4<uint4>(p + F::kQs + 32 * h);
     v.q1 = load_a4<uint4>(p + F::kQs + 32 * h + 16);
-    v.sc = load_a4<uint32_t>(p + 4 * c);
+    v.sc.x = load_a4<uint32_t>(p + 4 * c);
     v.d = load_a4<uint32_t>(p + 80);
   }
 }
@@ -464,42 +467,50 @@ __device__ __forceinline__ void q23_load(Q23Loads& v, const uint8_t* p, int c) {
 // This lane's exact integer partials of one superblock: Q2_K (S_q, S_m), Q3_K (S, 0).
 template <int Q3>
 __device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk, int c) {
-  const uint8_t* ap = ablk + 4 + 64 * c;
-  const uint4 a[4] = {lds_a4<uint4>(ap), lds_a4<uint4>(ap + 16), lds_a4<uint4>(ap + 32), lds_a4<uint4>(ap + 48)};
-  const uint2 bsw = lds_a4<uint2>(ablk + 260 + 8 * c);  // bsums 4c .. 4c+3
-  const int bs[4] = {sext16_lo(bsw.x), sext16_hi(bsw.x), sext16_lo(bsw.y), sext16_hi(bsw.y)};
-  const int h = c >> 1, g0 = 2 * (c & 1);
-  uint32_t scw;  // byte k: the unsigned scale of sub-block 4c + k
-  if constexpr (Q3 != 0) {
-    const uint32_t low = (((c & 1) ? v.sc1 : v.sc) >> (4 * (c >> 1))) & kLo4;
-    scw = low | (((v.sc2 >> (2 * c)) & 0x03030303u) << 4);
-  } else {
-    scw = v.sc;
-  }
+  const int h = c >> 1, lh = c & 1;
   int sq = 0, sm = 0;
+  if constexpr (Q3 != 0) {
+    const uint4 bsv = lds_a4<uint4>(ablk + 260 + 16 * h);  // bsums 8h .. 8h + 7
+    const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint4 q = (k & 1) ? v.q1 : v.q0;  // bytes l = 16 (k & 1) .. + 15
-    const int sh = 2 * (g0 + (k >> 1));
-    uint32_t w[4] = {(q.x >> sh) & 0x03030303u, (q.y >> sh) & 0x03030303u, (q.z >> sh) & 0x03030303u,
-                     (q.w >> sh) & 0x03030303u};
-    if constexpr (Q3 != 0) {
-      const uint4 m = (k & 1) ? v.m1 : v.m0;
-      const int hb = 4 * h + g0 + (k >> 1);
-      w[0] |= ((m.x >> hb) & kOnes) << 2;
-      w[1] |= ((m.y >> hb) & kOnes) << 2;
-      w[2] |= ((m.z >> hb) & kOnes) << 2;
-      w[3] |= ((m.w >> hb) & kOnes) << 2;
+    for (int g = 0; g < 4; ++g) {
+      const uint4 a = lds_a4<uint4>(ablk + 4 + 128 * h + 32 * g + 16 * lh);
+      const int bs = lh ? sext16_hi(bw[g]) : sext16_lo(bw[g]);  // sub-block 8h + 2g + lh
+      const int hb = 4 * h + g;
+      const uint32_t w0 = ((v.q0.x >> (2 * g)) & 0x03030303u) | (((v.m.x >> hb) & kOnes) << 2);
+      const uint32_t w1 = ((v.q0.y >> (2 * g)) & 0x03030303u) | (((v.m.y >> hb) & kOnes) << 2);
+      const uint32_t w2 = ((v.q0.z >> (2 * g)) & 0x03030303u) | (((v.m.z >> hb) & kOnes) << 2);
+      const uint32_t w3 = ((v.q0.w >> (2 * g)) & 0x03030303u) | (((v.m.w >> hb) & kOnes) << 2);
+      int s = 0;
+      s = dot4(w0, a.x, s);
+      s = dot4(w1, a.y, s);
+      s = dot4(w2, a.z, s);
+      s = dot4(w3, a.w, s);
+      // 6-bit scale of sub-block j = 8h + 2g + lh: low 4 bits from byte j (h = 0) or
+      // the high nibble of byte j - 8 (h = 1), i.e. byte lh + 2g of bytes 96-103;
+      // high 2 bits from byte 8 + j % 4 of the 12 scale bytes, bits 2 (j / 4)
+      const uint32_t sbyte = __builtin_amdgcn_ubfe((g < 2) ? v.sc.x : v.sc.y, 8 * (lh + 2 * (g & 1)), 8);
+      const int low4 = static_cast<int>((sbyte >> (4 * h)) & 15u);
+      const int high2 = static_cast<int>(
+          __builtin_amdgcn_ubfe(v.sc2, 8 * (lh + 2 * (g & 1)) + 2 * (2 * h + (g >> 1)), 2));
+      sq = mad24((low4 | (high2 << 4)) - 32, s - 4 * bs, sq);
     }
-    int s = 0;
-    s = dot4(w[0], a[k].x, s);
-    s = dot4(w[1], a[k].y, s);
-    s = dot4(w[2], a[k].z, s);
-    s = dot4(w[3], a[k].w, s);
-    const int scb = static_cast<int>((scw >> (8 * k)) & 0xFFu);
-    if constexpr (Q3 != 0) {
-      sq = mad24(scb - 32, s - 4 * bs[k], sq);
-    } else {
+  } else {
+    const uint8_t* ap = ablk + 4 + 64 * c;
+    const uint4 a[4] = {lds_a4<uint4>(ap), lds_a4<uint4>(ap + 16), lds_a4<uint4>(ap + 32), lds_a4<uint4>(ap + 48)};
+    const uint2 bsw = lds_a4<uint2>(ablk + 260 + 8 * c);  // bsums 4c .. 4c+3
+    const int bs[4] = {sext16_lo(bsw.x), sext16_hi(bsw.x), sext16_lo(bsw.y), sext16_hi(bsw.y)};
+    const int g0 = 2 * lh;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 q = (k & 1) ? v.q1 : v.q0;  // bytes l = 16 (k & 1) .. + 15
+      const int sh = 2 * (g0 + (k >> 1));
+      int s = 0;
+      s = dot4((q.x >> sh) & 0x03030303u, a[k].x, s);
+      s = dot4((q.y >> sh) & 0x03030303u, a[k].y, s);
+      s = dot4((q.z >> sh) & 0x03030303u, a[k].z, s);
+      s = dot4((q.w >> sh) & 0x03030303u, a[k].w, s);
+      const int scb = static_cast<int>((v.sc.x >> (8 * k)) & 0xFFu);  // scales[4c + k]
       sq = mad24(scb & 15, s, sq);
       sm = mad24(scb >> 4, bs[k], sm);
     }

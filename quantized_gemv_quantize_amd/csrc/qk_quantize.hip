@@ -28,24 +28,6 @@
 namespace qk {
 namespace {
 
-__device__ __forceinline__ int code_q8(float v) {
-  if (v != v) return 0;
-  float r = roundf(v);
-  r = fminf(fmaxf(r, -128.0f), 127.0f);
-  return static_cast<int>(r);
-}
-
-__device__ __forceinline__ uint32_t pack4(int c0, int c1, int c2, int c3) {
-  return (static_cast<uint32_t>(c0) & 0xFFu) | ((static_cast<uint32_t>(c1) & 0xFFu) << 8) |
-         ((static_cast<uint32_t>(c2) & 0xFFu) << 16) | ((static_cast<uint32_t>(c3) & 0xFFu) << 24);
-}
-
-// Largest |x| of 4 values folded from 0, so NaN never wins (fmaxf returns the
-// other operand) and an all-NaN block gives 0, as the sequential definition does.
-__device__ __forceinline__ float abs_max4(float4 v) {
-  return fmaxf(fmaxf(fmaxf(fmaxf(0.0f, fabsf(v.x)), fabsf(v.y)), fabsf(v.z)), fabsf(v.w));
-}
-
 // 8 lanes per 32-element block, 4 consecutive elements per lane.
 __global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restrict__ x,
                                                             uint8_t* __restrict__ xq,
@@ -105,18 +87,7 @@ __global__ __launch_bounds__(256) void quantize_q8_K_kernel(const float* __restr
   const int64_t b = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (b >= nblocks) return;  // whole wavefront leaves together
   const float4 v = *reinterpret_cast<const float4*>(x + b * 256 + lane * 4);
-  const float amax = wave_max(abs_max4(v));
-  const float d = amax / 127.0f;
-  const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
-  const int c0 = code_q8(v.x * id), c1 = code_q8(v.y * id);
-  const int c2 = code_q8(v.z * id), c3 = code_q8(v.w * id);
-  uint8_t* ob = xq + b * kQ8_KBytes;
-  *reinterpret_cast<uint32_t*>(ob + 4 + lane * 4) = pack4(c0, c1, c2, c3);
-  const int s16 = quad_sum(c0 + c1 + c2 + c3);  // 16 codes = 4 lanes
-  if ((lane & 3) == 0) {
-    *reinterpret_cast<int16_t*>(ob + 260 + 2 * (lane >> 2)) = static_cast<int16_t>(s16);
-  }
-  if (lane == 0) *reinterpret_cast<float*>(ob) = d;
+  q8K_block(v, lane, xq + b * kQ8_KBytes);
 }
 
 // ---------------------------------------------------------------------------
