@@ -449,6 +449,221 @@ __global__ __launch_bounds__(C::kThreads) void gemm_q4_K_mfma(const uint8_t* __r
   }
 }
 
+// ---------------------------------------------------------------------------
+// Up to 16 tokens and rows of at most 16 superblocks (n_in <= 4096): the tokens'
+// activation blocks for the whole row fit one workgroup's LDS (16 images of
+// kBT bytes, 79 KB), so they are staged once, by the compute wavefronts
+// themselves, and every wavefront puts all of its weight loads in flight at
+// kernel start, as the one-column GEMV does.  A workgroup of RT x KS wavefronts
+// owns RT 16-row tiles; wavefront (rt, ks) multiplies superblocks ks * QS ..
+// ks * QS + QS - 1 of tile rt, and the KS partial sums of an output are added in
+// LDS at the end, in split order.  Each thread issues its activation loads
+// before its weight loads; the load counter retires in order, so storing the
+// activations to LDS waits for those loads only.  The products and the float
+// step are the kernel above's.
+template <int RT, int KS, bool SUMS>
+__global__ __launch_bounds__(64 * RT * KS) void gemm_q4_K_res(const uint8_t* __restrict__ W, int n_out, int nb,
+                                                              const uint8_t* __restrict__ xq, int ncols,
+                                                              int rows_wg, float* __restrict__ y,
+                                                              int32_t* __restrict__ sums) {
+  constexpr int NTH = 64 * RT * KS;
+  constexpr int QS = (16 + KS - 1) / KS;       // superblocks per wavefront
+  constexpr int kPPT = (4096 + NTH - 1) / NTH;  // 16-byte code pieces per thread (16 x 16 x 16)
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint8_t* const zero = lds;
+  uint8_t* const img0 = lds + kZeroBytes;       // superblock b's image at img0 + b * kBT
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int w = wave_id();
+  const int rt = w % RT, ks = w / RT;
+  const uint32_t wrow = static_cast<uint32_t>(nb) * kQ4_KBytes;
+  const uint32_t xrow = static_cast<uint32_t>(nb) * kQ8_KBytes;
+  const int row0 = blockIdx.x * rows_wg;
+  const int row_end = min(row0 + rows_wg, n_out);
+  const int row = row0 + 16 * rt + n;
+
+  // activation loads: piece p = (superblock p / 256, token (p / 16) % 16, 16-byte
+  // piece p % 16); one (superblock, token) pair of bsums and scale per thread of
+  // the first 256.  Indices past the row's pieces or the call's tokens are clamped
+  // (the clamped thread stores what the last one stores).
+  const int npieces = nb * 256, npairs = nb * 16;
+  u4 code[kPPT];
+#pragma unroll
+  for (int k = 0; k < kPPT; ++k) {
+    const int pc = min(tid + k * NTH, npieces - 1);
+    const int sb = pc >> 8, tok = min((pc >> 4) & 15, ncols - 1);
+    code[k] = load_a4x4(xq + static_cast<uint32_t>(tok) * xrow + static_cast<uint32_t>(sb) * kQ8_KBytes + 4 +
+                        16 * (pc & 15));
+  }
+  const bool pair_thread = tid < 256;  // whole wavefronts
+  const int pp = min(tid, npairs - 1);
+  const int psb = pp >> 4, ptok = pp & 15;
+  u4 bs0 = u4{0u, 0u, 0u, 0u}, bs1 = u4{0u, 0u, 0u, 0u};
+  float pdx = 0.0f;
+  if (pair_thread) {
+    const uint8_t* p = xq + static_cast<uint32_t>(min(ptok, ncols - 1)) * xrow + static_cast<uint32_t>(psb) * kQ8_KBytes;
+    pdx = *reinterpret_cast<const float*>(p);
+    bs0 = load_a4x4(p + 260);
+    bs1 = load_a4x4(p + 276);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // all of this wavefront's weights (coalesced layout, as the kernel above)
+  const uint8_t* const Wwg = W + static_cast<size_t>(row0) * wrow;
+  const uint32_t lw_hd = static_cast<uint32_t>(min(16 * rt + (lane >> 2), row_end - row0 - 1)) * wrow + 4 * (lane & 3);
+  const uint32_t lw_qs = lw_hd + 12 * (lane & 3) + 16;
+  WRaw ring[QS];
+#pragma unroll
+  for (int i = 0; i < QS; ++i) {
+    const uint8_t* base = Wwg + static_cast<uint32_t>(min(ks * QS + i, nb - 1)) * kQ4_KBytes;
+    ring[i].hd = *reinterpret_cast<const uint32_t*>(base + lw_hd);
+    ring[i].qa = *reinterpret_cast<const u4*>(base + lw_qs);
+    ring[i].qb = *reinterpret_cast<const u4*>(base + lw_qs + 64);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // activations into LDS
+#pragma unroll
+  for (int k = 0; k < kPPT; ++k) {
+    const int pc = min(tid + k * NTH, npieces - 1);
+    *reinterpret_cast<u4*>(img0 + (pc >> 8) * kBT + ((pc >> 4) & 15) * kTokStride + 16 * (pc & 15)) = code[k];
+  }
+  if (pair_thread) {
+    // B_j = bsum_{2j} + bsum_{2j+1}, split into the bf16 digits 64 * Bh_j and Bl_j
+    const uint32_t wd[8] = {bs0[0], bs0[1], bs0[2], bs0[3], bs1[0], bs1[1], bs1[2], bs1[3]};
+    float hi[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int Bj = static_cast<int>(static_cast<int16_t>(wd[j] & 0xFFFFu)) + (static_cast<int>(wd[j]) >> 16);
+      const int bl = Bj & 63;
+      hi[j] = static_cast<float>(Bj - bl);
+      lo[j] = static_cast<float>(bl);
+    }
+    u4 h4, l4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h4[e] = pack_bf16(hi[2 * e], hi[2 * e + 1]);
+      l4[e] = pack_bf16(lo[2 * e], lo[2 * e + 1]);
+    }
+    uint8_t* img = img0 + psb * kBT;
+    *reinterpret_cast<u4*>(img + kDigOff + ptok * 16) = h4;
+    *reinterpret_cast<u4*>(img + kDigOff + 256 + ptok * 16) = l4;
+    *reinterpret_cast<float*>(img + kDxOff + ptok * 4) = pdx;
+  }
+  if (tid < kZeroBytes / 16) *reinterpret_cast<u4*>(zero + tid * 16) = u4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  const int src_lane = 4 * (4 * n + g);
+  const int src_hdr = 16 * n;
+  const uint32_t sel0 = 0x0C000C00u + 0x00010001u * static_cast<uint32_t>(g & 2);
+  const uint32_t sel1 = sel0 + 0x00010001u;
+  const uint32_t a_lane = n * kTokStride + 64 * (g >> 1) + 16 * (g & 1);
+  const uint32_t dig_lane = kDigOff + lane * 16;
+  const uint32_t zero_lane = static_cast<uint32_t>(lane - 32) * 16;
+  const uint32_t dx_lane = kDxOff + g * 16;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < QS; ++i) {
+    const int b = ks * QS + i;
+    const WRaw& r = ring[i];
+    u4 h, qa, qb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      h[k] = from_lane(src_hdr + 4 * k, r.hd);
+      qa[k] = from_lane(src_lane, r.qa[k]);
+      qb[k] = from_lane(src_lane, r.qb[k]);
+    }
+    if (b >= nb) continue;  // wave-uniform
+    const WOps o = build_wops(h, qa, qb, sel0, sel1);
+    const uint8_t* cur = img0 + b * kBT;
+    v4i ql = {0, 0, 0, 0}, qh = {0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const v4i a = *reinterpret_cast<const v4i*>(cur + a_lane + 32 * (m & 1) + 128 * (m >> 1));
+      ql = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, o.lo[m], ql, 0, 0, 0);
+      qh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, o.hi[m], qh, 0, 0, 0);
+    }
+    const bf16x8 dg = *reinterpret_cast<const bf16x8*>(g < 2 ? cur + dig_lane : zero + zero_lane);
+    const v4f sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dg, o.m, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    const v4f dx = *reinterpret_cast<const v4f*>(cur + dx_lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int sq = (qh[e] << 3) + ql[e];  // sc = 8 * (sc >> 3) + (sc & 7)
+      const float v = fmaf(-o.dmin, sm[e], o.d * static_cast<float>(sq));
+      acc[e] = fmaf(dx[e], v, acc[e]);
+      if constexpr (SUMS) {
+        const int tk = 4 * g + e;
+        if (row < row_end && tk < ncols) {
+          int32_t* out = sums + ((static_cast<size_t>(tk) * n_out + row) * nb + b) * 2;
+          out[0] = sq;
+          out[1] = static_cast<int>(sm[e]);
+        }
+      }
+    }
+  }
+
+  if constexpr (!SUMS) {
+    if constexpr (KS > 1) {
+      __syncthreads();  // every wavefront is done with the images
+      float* red = reinterpret_cast<float*>(lds);
+      if (ks > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(((ks - 1) * RT + rt) * 4 + e) * 64 + lane] = acc[e];
+      }
+      __syncthreads();
+      if (ks > 0) return;
+#pragma unroll
+      for (int k = 1; k < KS; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += red[(((k - 1) * RT + rt) * 4 + e) * 64 + lane];
+    }
+    if (row < row_end) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tk = 4 * g + e;
+        if (tk < ncols) y[static_cast<size_t>(tk) * n_out + row] = acc[e];
+      }
+    }
+  }
+}
+
+template <int RT, int KS, bool SUMS>
+hipError_t launch_res_kernel(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, float* y,
+                             int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  auto k = gemm_q4_K_res<RT, KS, SUMS>;
+  constexpr int rows_wg = 16 * RT;
+  unsigned grid = 0;
+  if (!launch_grid((static_cast<int64_t>(n_out) + rows_wg - 1) / rows_wg, 64 * RT * KS, &grid))
+    return hipErrorInvalidConfiguration;
+  // the images of nb superblocks, and room for the K-split partial sums that
+  // replace them at the end (more than the images when nb is small)
+  constexpr size_t kRed = static_cast<size_t>(KS - 1) * RT * 4 * 64 * 4;
+  const size_t images = kZeroBytes + static_cast<size_t>(nb) * kBT;
+  const size_t lds = images > kRed ? images : kRed;
+  if (lds > 65536) {
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (attr != hipSuccess) return attr;
+  }
+  if (e0 != nullptr || e1 != nullptr) {
+    hipExtLaunchKernelGGL(k, dim3(grid), dim3(64 * RT * KS), lds, s, e0, e1, 0, W, n_out, nb, xq, ncols, rows_wg,
+                          y, sums);
+  } else {
+    k<<<grid, 64 * RT * KS, lds, s>>>(W, n_out, nb, xq, ncols, rows_wg, y, sums);
+  }
+  return hipGetLastError();
+}
+
+template <int RT, int KS>
+hipError_t launch_res(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, float* y, int32_t* sums,
+                      hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (sums != nullptr) return launch_res_kernel<RT, KS, true>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
+  return launch_res_kernel<RT, KS, false>(W, n_out, nb, xq, ncols, y, sums, s, e0, e1);
+}
+
 template <class C, bool SUMS>
 hipError_t launch_kernel(const uint8_t* W, int n_out, int nb, const uint8_t* xq, int ncols, int rows_wg, float* y,
                          int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
@@ -510,6 +725,14 @@ hipError_t launch_gemm_q4K(const uint8_t* W, int64_t n_out, int64_t n_in, const 
   // against 11.7 us with whole 16-superblock chunks; 2-superblock chunks 12.9);
   // one row tile keeps 16-superblock chunks and 8 K-split wavefronts (4096 x 11008:
   // 12.2 against 13.8 us)
+  // Up to 16 tokens on short matrices (under 400 16-row tiles, rows of at most 16
+  // superblocks): the LDS-resident kernel, one row tile per workgroup split over
+  // 16 K-split wavefronts (4096 x 4096 at 16 / 8 columns: 6.9 / 5.4 against 7.6 /
+  // 6.0 us).  On taller matrices its products, all after the one staging barrier,
+  // no longer hide under the weight stream (14336 x 4096 at 16 columns: 14.3
+  // against 11.1 us with 4 row tiles per workgroup), and the kernel below wins.
+  if (nc <= 16 && nb <= 16 && (n_out + 15) / 16 < 400)
+    return launch_res<1, 16>(W, n, nb, xq, nc, y, sums, s, e0, e1);
   if (nc <= 16) return launch_nt<1, 8, 4, 2, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
   if (nc <= 32) return launch_nt<2, 8, 4, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
   return launch_nt<4, 4, 4, 2, 4>(rt, W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
