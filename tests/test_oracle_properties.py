@@ -10,7 +10,10 @@ BlockQ8K) without restating its arithmetic:
   - power-of-two scaling: x * 2^k gives the same codes and a scale times 2^k while
     the scale stays a normal number of its storage format;
   - Q8_K bsums are the sums of their 16 codes, codes lie in [-127, 127] and the
-    largest magnitude maps to +-127.
+    largest magnitude maps to +-127;
+  - Q8_1 (the reading of the _1 types' activation block) carries Q8_0's bytes for d
+    and the codes, its sum field changes sign with x, and it lies within its two
+    f16 roundings of the sum of the codes times the stored d.
 Blocks whose largest magnitude is below 127 * 2^-128 are left out of the
 symmetry, fixed-point and range properties: there 1 / d overflows to infinity and the codes
 saturate to the int8 range, -128 included (the reading the C ABI documents).
@@ -119,3 +122,31 @@ def test_q8_K_bsums_range_and_extreme(x):
     if d > 0 and np.isfinite(d):
         i = int(np.argmax(np.abs(x)))
         assert abs(int(c[i])) == 127
+
+
+@SETTINGS
+@given(x=blocks(32))
+def test_q8_1_d_and_codes_are_q8_0s(x):
+    b1 = o.quantize(o.Q8_1, x)
+    b0 = o.quantize(o.Q8_0, x)
+    assert b1[0:2].tobytes() == b0[0:2].tobytes() and b1[4:36].tobytes() == b0[2:34].tobytes()
+
+
+@SETTINGS
+@given(x=blocks(32))
+def test_q8_1_sum_field_sign_and_bound(x):
+    if not finite_id(x):
+        return
+    b = o.quantize(o.Q8_1, x)
+    s = np.frombuffer(b[2:4].tobytes(), np.float16)[0]
+    s_neg = np.frombuffer(o.quantize(o.Q8_1, -x)[2:4].tobytes(), np.float16)[0]
+    d16 = np.float64(np.frombuffer(b[0:2].tobytes(), np.float16)[0])
+    S = int(b[4:36].view(np.int8).astype(np.int64).sum())
+    if not np.isfinite(s) or not np.isfinite(d16):
+        return
+    assert s_neg == -s and (S != 0 or s == 0)
+    # s rounds S * d32 (d32 the unrounded scale, d16 its f16 rounding) twice: to f32,
+    # then to f16; d16 is within 2^-11 of d32 (or 2^-25 below the f16 normal range)
+    s = np.float64(s)
+    bound = abs(S) * (2.0 ** -10 * d16 + 2.0 ** -24) + 2.0 ** -11 * abs(s) + 2.0 ** -24
+    assert abs(s - S * d16) <= bound, (s, S, d16)
