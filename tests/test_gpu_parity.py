@@ -246,11 +246,11 @@ SHAPES = {
     T5K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T2K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
     T3K: [(1, 256), (5, 512), (67, 4096), (9, 4352), (13, 11008), (3, 12544), (6, 28672)],
-    T8_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
-    T4_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
-    T5_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
-    T4_1: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
-    T5_1: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (7, 11008), (6, 28672)],
+    T8_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (4, 10240), (7, 11008), (6, 28672)],
+    T4_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (4, 10240), (7, 11008), (6, 28672)],
+    T5_0: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (4, 10240), (7, 11008), (6, 28672)],
+    T4_1: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (4, 10240), (7, 11008), (6, 28672)],
+    T5_1: [(1, 32), (5, 96), (67, 1024), (9, 2048), (13, 4096), (3, 4128), (4, 10240), (7, 11008), (6, 28672)],
 }
 
 
