@@ -319,7 +319,10 @@ BATCHED = [(1, 256, 2), (17, 512, 16), (33, 1024, 17), (45, 4096, 33), (70, 2304
            (8300, 256, 9), (4200, 256, 24), (4160, 256, 40), (8300, 1024, 40), (2100, 2560, 64),
            # small batches: the multi-column GEMV kernel (2 columns; 3 up to 8192
            # rows) and, past 8192 rows, the matrix cores at 3 columns
-           (37, 2304, 3), (8300, 256, 3), (4100, 11008, 2)]
+           (37, 2304, 3), (8300, 256, 3), (4100, 11008, 2),
+           # up to 16 columns on tall matrices with rows of at most 16 superblocks:
+           # one superblock per wavefront, two to four row tiles per workgroup
+           (7000, 2048, 13), (9001, 4096, 5), (11008, 4096, 16)]
 
 
 @pytest.mark.parametrize("n_out,n_in,ncols", BATCHED)
