@@ -472,29 +472,42 @@ __device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk
   if constexpr (Q3 != 0) {
     const uint4 bsv = lds_a4<uint4>(ablk + 260 + 16 * h);  // bsums 8h .. 8h + 7
     const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
+    // Bit 2 of the code of shift group g is bit 4h + g of the hmask byte: rotating
+    // each hmask word right by 4h - 2 (mod 32) puts bit 4h + g of every byte at bit
+    // g + 2 of the same byte (the bits that wrap around land below bit 2 of byte 0,
+    // which no group reads).
+    const uint32_t rot = h ? 2u : 30u;
+    const uint32_t mq[4] = {__builtin_amdgcn_alignbit(v.m.x, v.m.x, rot), __builtin_amdgcn_alignbit(v.m.y, v.m.y, rot),
+                            __builtin_amdgcn_alignbit(v.m.z, v.m.z, rot), __builtin_amdgcn_alignbit(v.m.w, v.m.w, rot)};
+    const uint32_t qw[4] = {v.q0.x, v.q0.y, v.q0.z, v.q0.w};
+    // 6-bit scales of sub-blocks j = 8h + 2g + lh, g = 0 .. 3: the low 4 bits are
+    // nibble h of scale byte 2g + lh, the high 2 bits are bits 4h + 2 (g >> 1) of
+    // scale byte 8 + 2 (g & 1) + lh.  s01 holds the scales of g = 0, 1 in bytes lh and
+    // 2 + lh, s23 those of g = 2, 3.
+    const uint32_t hs = v.sc2 >> (4 * h);
+    const uint32_t s01 = ((v.sc.x >> (4 * h)) & kLo4) | ((hs & 0x03030303u) << 4);
+    const uint32_t s23 = ((v.sc.y >> (4 * h)) & kLo4) | (((hs >> 2) & 0x03030303u) << 4);
+    int tsum = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint4 a = lds_a4<uint4>(ablk + 4 + 128 * h + 32 * g + 16 * lh);
-      const int bs = lh ? sext16_hi(bw[g]) : sext16_lo(bw[g]);  // sub-block 8h + 2g + lh
-      const int hb = 4 * h + g;
-      const uint32_t w0 = ((v.q0.x >> (2 * g)) & 0x03030303u) | (((v.m.x >> hb) & kOnes) << 2);
-      const uint32_t w1 = ((v.q0.y >> (2 * g)) & 0x03030303u) | (((v.m.y >> hb) & kOnes) << 2);
-      const uint32_t w2 = ((v.q0.z >> (2 * g)) & 0x03030303u) | (((v.m.z >> hb) & kOnes) << 2);
-      const uint32_t w3 = ((v.q0.w >> (2 * g)) & 0x03030303u) | (((v.m.w >> hb) & kOnes) << 2);
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        w[k] = ((qw[k] >> (2 * g)) & 0x03030303u) | ((mq[k] >> g) & 0x04040404u);
+      }
       int s = 0;
-      s = dot4(w0, a.x, s);
-      s = dot4(w1, a.y, s);
-      s = dot4(w2, a.z, s);
-      s = dot4(w3, a.w, s);
-      // 6-bit scale of sub-block j = 8h + 2g + lh: low 4 bits from byte j (h = 0) or
-      // the high nibble of byte j - 8 (h = 1), i.e. byte lh + 2g of bytes 96-103;
-      // high 2 bits from byte 8 + j % 4 of the 12 scale bytes, bits 2 (j / 4)
-      const uint32_t sbyte = __builtin_amdgcn_ubfe((g < 2) ? v.sc.x : v.sc.y, 8 * (lh + 2 * (g & 1)), 8);
-      const int low4 = static_cast<int>((sbyte >> (4 * h)) & 15u);
-      const int high2 = static_cast<int>(
-          __builtin_amdgcn_ubfe(v.sc2, 8 * (lh + 2 * (g & 1)) + 2 * (2 * h + (g >> 1)), 2));
-      sq = mad24((low4 | (high2 << 4)) - 32, s - 4 * bs, sq);
+      s = dot4(w[0], a.x, s);
+      s = dot4(w[1], a.y, s);
+      s = dot4(w[2], a.z, s);
+      s = dot4(w[3], a.w, s);
+      const int bs = static_cast<int>(__builtin_amdgcn_sbfe(bw[g], 16 * lh, 16));  // bsum of sub-block 8h + 2g + lh
+      const int t = mad24(-4, bs, s);                                              // sum (code - 4) a
+      const int scale = static_cast<int>(__builtin_amdgcn_ubfe(g < 2 ? s01 : s23, 8 * (lh + 2 * (g & 1)), 8));
+      sq = mad24(scale, t, sq);
+      tsum += t;
     }
+    sq = mad24(-32, tsum, sq);  // sum_j (scale_j - 32) t_j
   } else {
     const uint8_t* ap = ablk + 4 + 64 * c;
     const uint4 a[4] = {lds_a4<uint4>(ap), lds_a4<uint4>(ap + 16), lds_a4<uint4>(ap + 32), lds_a4<uint4>(ap + 48)};
