@@ -55,6 +55,7 @@ extern "C" {
 /* Status codes returned by every call that can fail. */
 #define QK_OK 0
 #define QK_E_TYPE 1   /* unknown type id, or a type the call does not take */
+#define QK_E_PAIR 2   /* the activation type is not the one the weight type pairs with */
 #define QK_E_SHAPE 3  /* n not a positive multiple of the block size, or a negative count */
 #define QK_E_ALIGN 4  /* a base pointer is not 16-byte aligned */
 #define QK_E_NULL 5   /* a required pointer is NULL */
@@ -175,6 +176,20 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
  */
 int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
             int64_t ncols, float* y, void* stream);
+
+/*
+ * qk_gemv_typed - qk_gemv with the activation blocks' type stated by the caller.
+ * Each weight format is multiplied against one activation format whose blocks line
+ * up with its own, and an unpaired combination has no dot product (rml "Quantized
+ * dot products"; candle "VecDotType" table).
+ *   act_type  the type xq was quantized to; must equal qk_act_type(w_type).
+ *   other arguments as qk_gemv.
+ * Errors: QK_E_TYPE when w_type is not a weight type or act_type not an activation
+ * type; QK_E_PAIR when act_type is not qk_act_type(w_type); then as qk_gemv.  The
+ * checks run on the host before anything is enqueued.
+ */
+int qk_gemv_typed(int w_type, int act_type, const void* W, int64_t n_out, int64_t n_in,
+                  const void* xq, int64_t ncols, float* y, void* stream);
 
 /*
  * qk_dequantize_row - expand n elements (whole blocks) of a weight type to f32.

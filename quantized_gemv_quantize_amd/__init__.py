@@ -75,6 +75,8 @@ def lib():
         L.qk_quantize_row.argtypes = [i32, p, p, i64, p]
         L.qk_gemv.restype = i32
         L.qk_gemv.argtypes = [i32, p, i64, i64, p, i64, p, p]
+        L.qk_gemv_typed.restype = i32
+        L.qk_gemv_typed.argtypes = [i32, i32, p, i64, i64, p, i64, p, p]
         L.qk_gemv_timed.restype = i32
         L.qk_gemv_timed.argtypes = [i32, p, i64, i64, p, i64, p, p, p, p]
         L.qk_gemv_block_sums.restype = i32
@@ -177,6 +179,17 @@ def qk_gemv(w_type, W, n_out, n_in, xq, ncols=1, y=None, stream=None):
         y = torch.empty((ncols, n_out), dtype=torch.float32, device=W.device)
     _check(lib().qk_gemv(w_type, _ptr(W), n_out, n_in, _ptr(xq), ncols, _ptr(y),
                          _stream(stream)), "qk_gemv")
+    return y
+
+
+def qk_gemv_typed(w_type, act_type, W, n_out, n_in, xq, ncols=1, y=None, stream=None):
+    """qk_gemv with the activation type of xq stated: QKError (QK_E_PAIR) when it is
+    not qk_act_type(w_type)."""
+    import torch
+    if y is None:
+        y = torch.empty((ncols, n_out), dtype=torch.float32, device=W.device)
+    _check(lib().qk_gemv_typed(w_type, act_type, _ptr(W), n_out, n_in, _ptr(xq), ncols, _ptr(y),
+                               _stream(stream)), "qk_gemv_typed")
     return y
 
 

@@ -177,6 +177,7 @@ const char* qk_status_str(int status) {
   switch (status) {
     case QK_OK: return "ok";
     case QK_E_TYPE: return "unknown type, or a type this call does not take";
+    case QK_E_PAIR: return "the activation type is not the one the weight type pairs with";
     case QK_E_SHAPE: return "shape is not whole blocks, or a count is negative";
     case QK_E_ALIGN: return "a base pointer is not 16-byte aligned";
     case QK_E_NULL: return "a required pointer is NULL";
@@ -236,6 +237,13 @@ int qk_quantize_row(int type, const float* x, void* dst, int64_t n, void* stream
 
 int qk_gemv(int w_type, const void* W, int64_t n_out, int64_t n_in, const void* xq,
             int64_t ncols, float* y, void* stream) {
+  return gemv_impl(w_type, W, n_out, n_in, xq, ncols, y, nullptr, stream, nullptr, nullptr);
+}
+
+int qk_gemv_typed(int w_type, int act_type, const void* W, int64_t n_out, int64_t n_in,
+                  const void* xq, int64_t ncols, float* y, void* stream) {
+  if (!is_weight(w_type) || !is_act(act_type)) return QK_E_TYPE;
+  if (act_type != qk_act_type(w_type)) return QK_E_PAIR;
   return gemv_impl(w_type, W, n_out, n_in, xq, ncols, y, nullptr, stream, nullptr, nullptr);
 }
 

@@ -97,17 +97,24 @@ int check_type(int type, int64_t n_out, int64_t n_in, int64_t ncols) {
   for (auto& v : x) v = static_cast<float>(4.0 * uniform01() - 2.0);
 
   Dev<uint8_t> dW(wbytes), dxq(xbytes);
-  Dev<float> dx(x.size()), dy(n_out * ncols), dd(n_out * n_in);
+  Dev<float> dx(x.size()), dy(n_out * ncols), dy2(n_out * ncols), dd(n_out * n_in);
   const int64_t k = orc_sums_per_block(type), nb = n_in / qk_block_elems(type);
   Dev<int32_t> ds(ncols * n_out * nb * k);
-  if (!dW.p || !dxq.p || !dx.p || !dy.p || !dd.p || !ds.p) return 2;
+  if (!dW.p || !dxq.p || !dx.p || !dy.p || !dy2.p || !dd.p || !ds.p) return 2;
   HIPCHECK(hipMemcpy(dW.p, W.data(), wbytes, hipMemcpyHostToDevice));
   HIPCHECK(hipMemcpy(dx.p, x.data(), x.size() * 4, hipMemcpyHostToDevice));
 
   int rc = qk_quantize_act(at, dx.p, dxq.p, n_in, ncols, nullptr);
   if (rc == QK_OK) rc = qk_gemv(type, dW.p, n_out, n_in, dxq.p, ncols, dy.p, nullptr);
+  if (rc == QK_OK) rc = qk_gemv_typed(type, at, dW.p, n_out, n_in, dxq.p, ncols, dy2.p, nullptr);
   if (rc == QK_OK) rc = qk_gemv_block_sums(type, dW.p, n_out, n_in, dxq.p, ncols, ds.p, nullptr);
   if (rc == QK_OK) rc = qk_dequantize_row(type, dW.p, dd.p, n_out * n_in, nullptr);
+  // an activation type the weight type does not pair with: refused before any launch
+  const int wrong = at == QK_TYPE_Q8_K ? QK_TYPE_Q8_0 : QK_TYPE_Q8_K;
+  if (qk_gemv_typed(type, wrong, dW.p, n_out, n_in, dxq.p, ncols, dy2.p, nullptr) != QK_E_PAIR) {
+    std::snprintf(what, sizeof what, "type %d: a mismatched activation type was not refused", type);
+    fail(what);
+  }
   if (rc != QK_OK) {
     std::snprintf(what, sizeof what, "type %d: status %d (%s)", type, rc, qk_status_str(rc));
     fail(what);
@@ -119,6 +126,14 @@ int check_type(int type, int64_t n_out, int64_t n_in, int64_t ncols) {
   std::vector<int32_t> sums(static_cast<size_t>(ncols * n_out * nb * k));
   HIPCHECK(hipMemcpy(xq.data(), dxq.p, xbytes, hipMemcpyDeviceToHost));
   HIPCHECK(hipMemcpy(y.data(), dy.p, y.size() * 4, hipMemcpyDeviceToHost));
+  {
+    std::vector<float> y2(y.size());
+    HIPCHECK(hipMemcpy(y2.data(), dy2.p, y2.size() * 4, hipMemcpyDeviceToHost));
+    if (std::memcmp(y.data(), y2.data(), y.size() * 4) != 0) {
+      std::snprintf(what, sizeof what, "type %d: qk_gemv_typed differs from qk_gemv", type);
+      fail(what);
+    }
+  }
   HIPCHECK(hipMemcpy(deq.data(), dd.p, deq.size() * 4, hipMemcpyDeviceToHost));
   HIPCHECK(hipMemcpy(sums.data(), ds.p, sums.size() * 4, hipMemcpyDeviceToHost));
 

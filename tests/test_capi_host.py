@@ -171,6 +171,26 @@ def test_gemv_validation():
                    None) == 4
 
 
+def test_gemv_typed_validation():
+    # every weight type against every activation type: QK_E_PAIR unless it is the
+    # weight type's pairing, which then passes on to qk_gemv (n_out = 0: a no-op)
+    f = "qk_gemv_typed"
+    acts = (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q8_1, qk.QK_TYPE_Q8_K)
+    for w in qk.WEIGHT_TYPES:
+        blk = qk.qk_block_elems(w)
+        for a in acts:
+            want = 0 if a == qk.qk_act_type(w) else 2
+            assert _status(f, w, a, GOOD, 0, blk, GOOD, 1, GOOD, None) == want, (w, a)
+        assert sum(a == qk.qk_act_type(w) for a in acts) == 1
+    assert _status(f, qk.QK_TYPE_Q8_K, qk.QK_TYPE_Q8_K, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
+    assert _status(f, qk.QK_TYPE_Q4_K, qk.QK_TYPE_Q4_K, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
+    assert _status(f, qk.QK_TYPE_Q4_K, 99, GOOD, 4, 256, GOOD, 1, GOOD, None) == 1
+    # after the pairing, qk_gemv's own checks
+    assert _status(f, qk.QK_TYPE_Q4_K, qk.QK_TYPE_Q8_K, GOOD, 4, 255, GOOD, 1, GOOD, None) == 3
+    assert _status(f, qk.QK_TYPE_Q4_0, qk.QK_TYPE_Q8_0, GOOD, 4, 64, GOOD, 1, ODD, None) == 4
+    assert _status(f, qk.QK_TYPE_Q4_1, qk.QK_TYPE_Q8_1, None, 4, 64, GOOD, 1, GOOD, None) == 5
+
+
 @pytest.mark.parametrize("f", ["qk_gemv_pair", "qk_gemv_pair_timed"])
 def test_gemv_pair_validation(f):
     T4K = qk.QK_TYPE_Q4_K
@@ -244,7 +264,7 @@ def test_launch_size_limit():
 
 
 def test_status_strings():
-    for s in (0, 1, 3, 4, 5, 6, 7, 8):
+    for s in (0, 1, 2, 3, 4, 5, 6, 7, 8):
         assert qk.status_str(s) and qk.status_str(s) != "unknown status"
     assert qk.status_str(42) == "unknown status"
 

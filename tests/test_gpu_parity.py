@@ -437,6 +437,28 @@ def test_gemv_zero_activation_gives_zero(torch_cuda):
         assert not y.any()
 
 
+def test_gemv_typed_is_gemv_with_a_pairing_check(torch_cuda):
+    # the stated activation type only adds the pairing check: y is qk_gemv's, bit for
+    # bit, and a mismatched type fails before anything is enqueued (y untouched)
+    rng = np.random.default_rng(17)
+    for t in (T4K, T5K, T6K, T8_0, T4_0, T5_0, T4_1, T5_1, T2K, T3K):
+        say("qk_gemv_typed", t)
+        W = dev(torch_cuda, weights(rng, t, 37, 1024))
+        at = qk.qk_act_type(t)
+        xq = qk.qk_quantize_act(at, torch_cuda.randn((2, 1024), device="cuda"))
+        want = host(qk.qk_gemv(t, W, 37, 1024, xq, 2))
+        got = host(qk.qk_gemv_typed(t, at, W, 37, 1024, xq, 2))
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        y = torch_cuda.full((2, 37), 7.0, device="cuda")
+        for other in (qk.QK_TYPE_Q8_0, qk.QK_TYPE_Q8_1, qk.QK_TYPE_Q8_K):
+            if other == at:
+                continue
+            with pytest.raises(qk.QKError) as e:
+                qk.qk_gemv_typed(t, other, W, 37, 1024, xq, 2, y=y)
+            assert e.value.status == 2
+        assert bool((y == 7.0).all())
+
+
 def test_empty_calls_touch_nothing(torch_cuda):
     # zero rows, zero columns or zero elements: QK_OK, nothing launched, buffers intact
     torch = torch_cuda
