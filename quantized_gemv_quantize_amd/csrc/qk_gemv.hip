@@ -727,6 +727,33 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_cols(
   }
 }
 
+// Codes of one dword of each Q6_K group: low nibbles from the ql words a (groups 0
+// and 2: low / high nibbles) and b (groups 1 and 3), the high 2 bits of group g at
+// bits 2g of each qh byte of h.  h masked to the fields of groups 0 and 2 (bits 0-1,
+// 4-5), and shifted right by 2 and masked to those of groups 1 and 3, lets a single
+// bit-field insert take each code's bits 0-3 from the nibble word and bits 4-7 from
+// the field word: the bits a shift carries in from the neighbouring byte all land in
+// the half the insert discards.
+// (The compiler folds a written-out (x & m) | (y & ~m) back into shifts and masks
+// here, because it knows y's zero bits, so the insert is written as v_bfi_b32.)
+struct Q6Codes {
+  uint32_t q0, q1, q2, q3;
+};
+__device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t x, uint32_t y) {  // (x & mask) | (y & ~mask)
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ Q6Codes q6_codes(uint32_t a, uint32_t b, uint32_t h) {
+  const uint32_t h02 = h & 0x33333333u, h13 = (h >> 2) & 0x33333333u;
+  Q6Codes r;
+  r.q0 = bit_insert(kLo4, a, h02 << 4);
+  r.q1 = bit_insert(kLo4, b, h13 << 4);
+  r.q2 = bit_insert(kLo4, a >> 4, h02);
+  r.q3 = bit_insert(kLo4, b >> 4, h13);
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Q6_K x Q8_K.  Lane (u = lane >> 2, p = lane & 3 -> half h = p >> 1, k = p & 1) of
 // pass `it` handles, in superblock it*16 + u, positions l in [16k, 16k+16) of half
@@ -796,14 +823,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
       int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t q0 = (al[i] & kLo4) | ((hl[i] << 4) & kHi2);
-        const uint32_t q1 = (bl[i] & kLo4) | ((hl[i] << 2) & kHi2);
-        const uint32_t q2 = ((al[i] >> 4) & kLo4) | (hl[i] & kHi2);
-        const uint32_t q3 = ((bl[i] >> 4) & kLo4) | ((hl[i] >> 2) & kHi2);
-        s0 = dot4(q0, a0[i], s0);
-        s1 = dot4(q1, a1[i], s1);
-        s2 = dot4(q2, a2[i], s2);
-        s3 = dot4(q3, a3[i], s3);
+        const Q6Codes q = q6_codes(al[i], bl[i], hl[i]);
+        s0 = dot4(q.q0, a0[i], s0);
+        s1 = dot4(q.q1, a1[i], s1);
+        s2 = dot4(q.q2, a2[i], s2);
+        s3 = dot4(q.q3, a3[i], s3);
       }
       // sub-block scales sc[8h + 2g + k] = byte (2g + k) of the 8 bytes at 192 + 8h
       const int sc0 = static_cast<int8_t>((SC[j].x >> (8 * kk)) & 0xFF);
@@ -894,10 +918,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_cols(
       uint32_t q[4][4];  // q[g][i]: codes of group g, dword i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        q[0][i] = (al[i] & kLo4) | ((hl[i] << 4) & kHi2);
-        q[1][i] = (bl[i] & kLo4) | ((hl[i] << 2) & kHi2);
-        q[2][i] = ((al[i] >> 4) & kLo4) | (hl[i] & kHi2);
-        q[3][i] = ((bl[i] >> 4) & kLo4) | ((hl[i] >> 2) & kHi2);
+        const Q6Codes c6 = q6_codes(al[i], bl[i], hl[i]);
+        q[0][i] = c6.q0;
+        q[1][i] = c6.q1;
+        q[2][i] = c6.q2;
+        q[3][i] = c6.q3;
       }
       const int sc0 = static_cast<int8_t>((SC[j].x >> (8 * kk)) & 0xFF);
       const int sc1 = static_cast<int8_t>((SC[j].x >> (16 + 8 * kk)) & 0xFF);
@@ -1674,10 +1699,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_reg(
         const uint32_t a1 = i == 0 ? A[p][1].x : i == 1 ? A[p][1].y : i == 2 ? A[p][1].z : A[p][1].w;
         const uint32_t a2 = i == 0 ? A[p][2].x : i == 1 ? A[p][2].y : i == 2 ? A[p][2].z : A[p][2].w;
         const uint32_t a3 = i == 0 ? A[p][3].x : i == 1 ? A[p][3].y : i == 2 ? A[p][3].z : A[p][3].w;
-        s0 = dot4((al[i] & kLo4) | ((hl[i] << 4) & kHi2), a0, s0);
-        s1 = dot4((bl[i] & kLo4) | ((hl[i] << 2) & kHi2), a1, s1);
-        s2 = dot4(((al[i] >> 4) & kLo4) | (hl[i] & kHi2), a2, s2);
-        s3 = dot4(((bl[i] >> 4) & kLo4) | ((hl[i] >> 2) & kHi2), a3, s3);
+        const Q6Codes q = q6_codes(al[i], bl[i], hl[i]);
+        s0 = dot4(q.q0, a0, s0);
+        s1 = dot4(q.q1, a1, s1);
+        s2 = dot4(q.q2, a2, s2);
+        s3 = dot4(q.q3, a3, s3);
       }
       const int sc0 = static_cast<int8_t>((SC[p].x >> (8 * kk)) & 0xFF);
       const int sc1 = static_cast<int8_t>((SC[p].x >> (16 + 8 * kk)) & 0xFF);
