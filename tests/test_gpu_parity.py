@@ -322,7 +322,7 @@ BATCHED = [(1, 256, 2), (17, 512, 16), (33, 1024, 17), (45, 4096, 33), (70, 2304
            (37, 2304, 3), (8300, 256, 3), (4100, 11008, 2),
            # up to 16 columns on tall matrices with rows of at most 16 superblocks:
            # one superblock per wavefront, two to four row tiles per workgroup
-           (7000, 2048, 13), (9001, 4096, 5), (11008, 4096, 16)]
+           (7000, 2048, 13), (6500, 4096, 16), (9001, 4096, 5), (11008, 4096, 16)]
 
 
 @pytest.mark.parametrize("n_out,n_in,ncols", BATCHED)
