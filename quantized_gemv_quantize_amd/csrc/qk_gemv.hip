@@ -228,8 +228,9 @@ __device__ __forceinline__ int2 q4K_chunk(const uint4& q0, const uint4& q1, cons
 
 // Q5_K chunk c: the Q4_K nibbles plus, for element 64c + p, bit 2c (p < 32) or
 // 2c + 1 (p >= 32) of qh byte p % 32 as bit 4.  qh0 / qh1 are qh bytes 0-15 /
-// 16-31, already shifted right by 2c, so bits 0 and 1 of each byte are this
-// chunk's two fifth bits.  Codes stay below 32, so the signed dot is exact.
+// 16-31 after rot_q5 (each word rotated right by 2c - 4), so bits 4 and 5 of each
+// byte are this chunk's two fifth bits.  Codes stay below 32, so the signed dot is
+// exact.
 __device__ __forceinline__ int2 q5K_chunk(const uint4& q0, const uint4& q1, const uint4& qh0,
                                           const uint4& qh1, const uint4& h, const uint4& a0,
                                           const uint4& a1, const uint4& a2, const uint4& a3,
@@ -241,8 +242,8 @@ __device__ __forceinline__ int2 q5K_chunk(const uint4& q0, const uint4& q1, cons
   int slo = 0, shi = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const uint32_t lo = (ql[k] & kLo4) | ((qh[k] & kOnes) << 4);
-    const uint32_t hi = ((ql[k] >> 4) & kLo4) | ((qh[k] & (kOnes << 1)) << 3);
+    const uint32_t lo = (ql[k] & kLo4) | (qh[k] & 0x10101010u);
+    const uint32_t hi = ((ql[k] >> 4) & kLo4) | ((qh[k] >> 1) & 0x10101010u);
     slo = dot4(lo, al[k], slo);
     shi = dot4(hi, ah[k], shi);
   }
@@ -318,8 +319,13 @@ struct KQuant4 {
   static constexpr int kQs = Q5 ? 48 : 16;
 };
 
-__device__ __forceinline__ uint4 shr4(const uint4& v, int n) {
-  return make_uint4(v.x >> n, v.y >> n, v.z >> n, v.w >> n);
+// The qh words of Q5_K chunk c rotated right by 2c - 4 (mod 32): bit 2c of every
+// byte lands on bit 4 of the same byte and bit 2c + 1 on bit 5 (the bits that wrap
+// around stay below bit 4 of byte 0).
+__device__ __forceinline__ uint4 rot_q5(const uint4& v, int c) {
+  const uint32_t r = static_cast<uint32_t>(2 * c - 4) & 31u;
+  return make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, r), __builtin_amdgcn_alignbit(v.y, v.y, r),
+                    __builtin_amdgcn_alignbit(v.z, v.z, r), __builtin_amdgcn_alignbit(v.w, v.w, r));
 }
 
 template <int NW, int UNR, bool SUMS, int Q5 = 0>
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
       const uint4 h = H[j];
       int2 part;
       if constexpr (Q5 != 0) {
-        part = q5K_chunk(Q0[j], Q1[j], shr4(QH0[j], 2 * c), shr4(QH1[j], 2 * c), h, a0, a1, a2, a3, asum,
+        part = q5K_chunk(Q0[j], Q1[j], rot_q5(QH0[j], c), rot_q5(QH1[j], c), h, a0, a1, a2, a3, asum,
                          hi_mask, sh);
       } else {
         part = q4K_chunk(Q0[j], Q1[j], h, a0, a1, a2, a3, asum, hi_mask, sh);
@@ -611,9 +617,9 @@ __device__ __forceinline__ void kq_codes(const uint4& q0, const uint4& q1, const
   for (int k = 0; k < 8; ++k) {
     lo[k] = ql[k] & kLo4;
     hi[k] = (ql[k] >> 4) & kLo4;
-    if constexpr (Q5 != 0) {
-      lo[k] |= (qh[k] & kOnes) << 4;
-      hi[k] |= (qh[k] & (kOnes << 1)) << 3;
+    if constexpr (Q5 != 0) {  // qh after rot_q5: fifth bits at bits 4 and 5
+      lo[k] |= qh[k] & 0x10101010u;
+      hi[k] |= (qh[k] >> 1) & 0x10101010u;
     }
   }
 }
@@ -678,7 +684,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_cols(
       if (!row_ok || sb >= nb) continue;  // uniform over the 4 lanes of a superblock
       uint32_t lo[8], hi[8];
       if constexpr (Q5 != 0) {
-        kq_codes<1>(Q0[j], Q1[j], shr4(QH0[j], 2 * c), shr4(QH1[j], 2 * c), lo, hi);
+        kq_codes<1>(Q0[j], Q1[j], rot_q5(QH0[j], c), rot_q5(QH1[j], c), lo, hi);
       } else {
         kq_codes<0>(Q0[j], Q1[j], Q0[j], Q1[j], lo, hi);
       }
@@ -1429,7 +1435,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_reg(
         if (sb >= nb) continue;  // uniform over the 4 lanes of a superblock
         int2 part;
         if constexpr (Q5 != 0) {
-          part = q5K_chunk(Q0[r][p], Q1[r][p], shr4(QH0[r][p], 2 * c), shr4(QH1[r][p], 2 * c), H[r][p],
+          part = q5K_chunk(Q0[r][p], Q1[r][p], rot_q5(QH0[r][p], c), rot_q5(QH1[r][p], c), H[r][p],
                            A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask, sh);
         } else {
           part = q4K_chunk(Q0[r][p], Q1[r][p], H[r][p], A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask,
@@ -1531,7 +1537,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_reg(
         if (p * 16 + u >= nb) continue;  // uniform over the 4 lanes of a superblock
         int2 part;
         if constexpr (Q5 != 0) {
-          part = q5K_chunk(Q0[m][p], Q1[m][p], shr4(QH0[m][p], 2 * c), shr4(QH1[m][p], 2 * c), H[m][p],
+          part = q5K_chunk(Q0[m][p], Q1[m][p], rot_q5(QH0[m][p], c), rot_q5(QH1[m][p], c), H[m][p],
                            A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask, sh);
         } else {
           part = q4K_chunk(Q0[m][p], Q1[m][p], H[m][p], A[p][0], A[p][1], A[p][2], A[p][3], S2[p], hi_mask,
@@ -1619,7 +1625,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_pair_kernel(
         const uint4 h = H[m][j];
         int2 part;
         if constexpr (Q5 != 0) {
-          part = q5K_chunk(Q0[m][j], Q1[m][j], shr4(QH0[m][j], 2 * c), shr4(QH1[m][j], 2 * c), h, a0, a1, a2,
+          part = q5K_chunk(Q0[m][j], Q1[m][j], rot_q5(QH0[m][j], c), rot_q5(QH1[m][j], c), h, a0, a1, a2,
                            a3, asum, hi_mask, sh);
         } else {
           part = q4K_chunk(Q0[m][j], Q1[m][j], h, a0, a1, a2, a3, asum, hi_mask, sh);
