@@ -73,6 +73,7 @@ constexpr int kDigOff = 16 * kTokStride;     // digits: lanes 0-15 64 * Bh_j, la
 constexpr int kDxOff = kDigOff + 512;        // 16 f32 scales dx
 constexpr int kBT = kDxOff + 64;             // 4928 bytes
 constexpr int kZeroBytes = 512;              // the digit operand of lanes 32..63 (all zero)
+constexpr int kTokImg = 304;                 // one token's Q8_K block in a wavefront's LDS region
 
 // 16 bytes at a 4-byte aligned global address (Q8_K codes start 4 bytes into the block)
 __device__ __forceinline__ u4 load_a4x4(const uint8_t* p) {
@@ -638,11 +639,10 @@ __global__ __launch_bounds__(64 * RT * KS) void gemm_q4_K_res(const uint8_t* __r
 // ---------------------------------------------------------------------------
 // Up to 16 tokens, rows of at most 16 superblocks, tall matrices: wavefront k of a
 // 16-wavefront workgroup owns superblock k of the workgroup's RT row tiles.  It
-// loads that superblock's activation blocks of the 16 tokens straight into
-// registers in the MFMA operand layout (the lane's four A pieces, the bf16 digits
-// of B_j and the scales dx of its four output tokens), then the weights of all RT
-// row tiles, so every weight byte is requested at kernel start and no product
-// waits for a staging barrier.  Each lane's RT x 4 products d_x (d S_q - dmin S_m)
+// loads that superblock's activation blocks of the 16 tokens (contiguous 16-byte
+// pieces, through its own LDS region into the MFMA operand layout), then the
+// weights of all RT row tiles, so every weight byte is requested at kernel start
+// and no product waits for a workgroup barrier.  Each lane's RT x 4 products d_x (d S_q - dmin S_m)
 // go to LDS once; after the one barrier each thread adds one output's partials in
 // superblock order.  The products are the kernels' above.
 template <int RT, bool SUMS>
@@ -664,20 +664,24 @@ __global__ __launch_bounds__(1024) void gemm_q4_K_col(const uint8_t* __restrict_
   const int row0 = blockIdx.x * rows_wg;
   const int row_end = min(row0 + rows_wg, n_out);
 
-  // activations: lane (token n, k-slot group g) holds codes 64c + 16 (g % 2) +
-  // {0, 32, 128, 160} onwards of its token's block (c = g / 2), the token's bsums,
-  // and the scales dx of tokens 4g .. 4g + 3 (tokens past the call's are clamped)
+  // activations: the wavefront copies the 16 tokens' blocks of superblock bc into its
+  // own LDS region (tokens past the call's are clamped), each token's 292 bytes at a
+  // 304-byte stride shifted by 12, so that the codes (block bytes 4..259) and both
+  // halves of the bsums start 16-byte aligned.  Piece j = 1..18 of token t is block
+  // bytes 16j - 12 .. 16j + 3, copied with one 16-byte load; consecutive lanes take
+  // consecutive pieces of one token, so a load instruction reads a few whole
+  // 288-byte runs instead of a 32-byte run per token and lane group.  Dword 0 (the
+  // scale dx) goes separately.  Only this wavefront writes and reads the region.
   const uint8_t* const xb = xq + static_cast<uint32_t>(bc) * kQ8_KBytes;  // scalar
-  const uint32_t xt = static_cast<uint32_t>(min(n, ncols - 1)) * xrow;
-  const uint32_t xa = xt + 4 + 64 * (g >> 1) + 16 * (g & 1);
-  v4i a[4];
+  uint8_t* const img = lds + (SUMS ? 0 : nb * kOut * 4) + b * (16 * kTokImg);
+  u4 piece[5];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(v4i, load_a4x4(xb + xa + 32 * (i & 1) + 128 * (i >> 1)));
-  const u4 bs0 = load_a4x4(xb + xt + 260), bs1 = load_a4x4(xb + xt + 276);
-  float dxv[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    dxv[e] = *reinterpret_cast<const float*>(xb + static_cast<uint32_t>(min(4 * g + e, ncols - 1)) * xrow);
+  for (int k = 0; k < 5; ++k) {
+    const int pc = min(lane + 64 * k, 16 * 18 - 1);
+    const int t = pc / 18, j = 1 + pc % 18;
+    piece[k] = load_a4x4(xb + static_cast<uint32_t>(min(t, ncols - 1)) * xrow + 16 * j - 12);
+  }
+  const float dxt = *reinterpret_cast<const float*>(xb + static_cast<uint32_t>(min(n, ncols - 1)) * xrow);
   __builtin_amdgcn_sched_barrier(0);
 
   // weights of superblock bc, coalesced: lane 4r + q of row tile rt reads header
@@ -694,6 +698,28 @@ __global__ __launch_bounds__(1024) void gemm_q4_K_col(const uint8_t* __restrict_
     wr[rt].qb = *reinterpret_cast<const u4*>(Wb + qs + 64);
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  // the activation pieces into the region (the waits cover the activation loads only:
+  // the load counter retires in order), then this lane's operands out of it: the A
+  // pieces of token n (codes 64c + 16 (g % 2) + {0, 32, 128, 160} onwards, c = g / 2),
+  // its bsums, and dx of tokens 4g .. 4g + 3
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int pc = min(lane + 64 * k, 16 * 18 - 1);
+    *reinterpret_cast<u4*>(img + (pc / 18) * kTokImg + 16 * (1 + pc % 18)) = piece[k];
+  }
+  *reinterpret_cast<float*>(img + n * kTokImg + 12) = dxt;  // the 4 lanes of a token store the same value
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint8_t* const timg = img + n * kTokImg;
+  v4i a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a[i] = *reinterpret_cast<const v4i*>(timg + 16 + 64 * (g >> 1) + 16 * (g & 1) + 32 * (i & 1) + 128 * (i >> 1));
+  const u4 bs0 = *reinterpret_cast<const u4*>(timg + 272), bs1 = *reinterpret_cast<const u4*>(timg + 288);
+  float dxv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dxv[e] = *reinterpret_cast<const float*>(img + (4 * g + e) * kTokImg + 12);
 
   // bf16 digits of B_j = bsum_{2j} + bsum_{2j+1}: lanes 0-15 64 * Bh_j, lanes 16-31
   // Bl_j, lanes 32-63 zero (the k-slots that carry no products)
@@ -776,7 +802,8 @@ hipError_t launch_col_kernel(const uint8_t* W, int n_out, int nb, const uint8_t*
   unsigned grid = 0;
   if (!launch_grid((static_cast<int64_t>(n_out) + rows_wg - 1) / rows_wg, 1024, &grid))
     return hipErrorInvalidConfiguration;
-  const size_t lds = SUMS ? 0 : static_cast<size_t>(nb) * RT * 256 * 4;  // the partial sums
+  // the partial sums, then each wavefront's 16 activation blocks
+  const size_t lds = (SUMS ? 0 : static_cast<size_t>(nb) * RT * 256 * 4) + 16 * 16 * kTokImg;
   if (lds > 65536) {
     const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -901,10 +928,12 @@ hipError_t launch_gemm_q4K(const uint8_t* W, int64_t n_out, int64_t n_in, const 
   if (nc <= 16 && nb <= 16 && (n_out + 15) / 16 < 400)
     return launch_res<1, 16>(W, n, nb, xq, nc, y, sums, s, e0, e1);
   // Up to 16 tokens on taller matrices with rows of at most 16 superblocks: one
-  // superblock per wavefront, activations in registers, no staging barrier
-  // (14336 / 11008 / 8192 x 4096 at 16 columns: 10.8 / 9.3 / 7.9 against 11.2 / 10.7
-  // / 8.5 us with the chunked kernel below; staging the activations in LDS instead,
-  // with the one barrier that needs, 13.3 us on 14336 x 4096).
+  // superblock per wavefront, no staging barrier (14336 / 11008 / 8192 x 4096 at 16
+  // columns: 10.3 / 8.9 / 7.2 against 11.2 / 10.7 / 8.5 us with the chunked kernel
+  // below; loading each lane's operand pieces from global memory directly, 10.7 / 9.4
+  // / 7.8 us, its many 32-byte requests stalling the address unit; staging the
+  // activations in LDS for the whole workgroup, with the one barrier that needs,
+  // 13.3 us on 14336 x 4096).
   if (nc <= 16 && nb <= 16 && rt > 1) {
     const int tiles = (rows_wg + 15) / 16;  // 2, 3 or 4
     if (tiles == 2) return launch_col<2>(W, n, nb, xq, nc, rows_wg, y, sums, s, e0, e1);
