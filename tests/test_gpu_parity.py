@@ -322,7 +322,10 @@ BATCHED = [(1, 256, 2), (17, 512, 16), (33, 1024, 17), (45, 4096, 33), (70, 2304
            (37, 2304, 3), (8300, 256, 3), (4100, 11008, 2),
            # up to 16 columns on tall matrices with rows of at most 16 superblocks:
            # one superblock per wavefront, two to four row tiles per workgroup
-           (7000, 2048, 13), (6500, 4096, 16), (9001, 4096, 5), (11008, 4096, 16)]
+           (7000, 2048, 13), (6500, 4096, 16), (9001, 4096, 5), (11008, 4096, 16),
+           # 33 to 64 columns on the same tall matrices: two superblocks per
+           # wavefront (an odd count leaves the last one alone), two to four row tiles
+           (6500, 4096, 33), (9001, 2304, 50), (5000, 768, 47), (11008, 4096, 64)]
 
 
 @pytest.mark.parametrize("n_out,n_in,ncols", BATCHED)
@@ -343,12 +346,12 @@ def test_batched_q4_K_block_sums_and_y(torch_cuda, n_out, n_in, ncols):
     assert not y[ncols // 2].any()
 
 
-def test_batched_q4_K_extreme_codes(torch_cuda):
+@pytest.mark.parametrize("n_out,n_in,ncols", [(40, 1024, 20), (4200, 1024, 64)])
+def test_batched_q4_K_extreme_codes(torch_cuda, n_out, n_in, ncols):
     # every nibble 15, every 6-bit scale and min 63, activations at +-127: the
     # largest integer sums the format allows, on both MFMA products
-    say("batched Q4_K extreme codes")
+    say("batched Q4_K extreme codes", n_out, n_in, ncols)
     rng = np.random.default_rng(77)
-    n_out, n_in, ncols = 40, 1024, 20
     W = synth.q4_K_blocks(rng, n_out, n_in).reshape(n_out, n_in // 256, 144)
     W[:, :, 4:] = 0xFF
     W = W.reshape(n_out, -1)
