@@ -28,6 +28,13 @@ namespace {
 
 constexpr uint32_t kLo4 = 0x0F0F0F0Fu;
 
+// The f32 output is written once and not read back by this kernel: non-temporal
+// stores (32000 x 4096 Q6_K: 121.9 against 127.7 us with ordinary stores).
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_f4(float* p, float4 o) {
+  __builtin_nontemporal_store(f4v{o.x, o.y, o.z, o.w}, reinterpret_cast<f4v*>(p));
+}
+
 __device__ __forceinline__ float4 scale_bytes_signed(uint32_t q, float scale, int offset) {
   return make_float4(scale * static_cast<float>(static_cast<int>(q & 0xFF) - offset),
                      scale * static_cast<float>(static_cast<int>((q >> 8) & 0xFF) - offset),
@@ -51,7 +58,7 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __rest
   o.y = d * static_cast<float>(static_cast<int8_t>((q >> 8) & 0xFF));
   o.z = d * static_cast<float>(static_cast<int8_t>((q >> 16) & 0xFF));
   o.w = d * static_cast<float>(static_cast<int8_t>(q >> 24));
-  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = o;
+  store_f4(dst + b * 32 + 4 * part, o);
 }
 
 // Q4_0: 8 lanes per block; lanes 0-3 take low nibbles (elements 0-15), lanes 4-7
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* __rest
   const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk));
   const uint32_t w = load_u2<uint32_t>(blk + 2 + 4 * (part & 3));
   const uint32_t q = (part < 4) ? (w & kLo4) : ((w >> 4) & kLo4);
-  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(q, d, 8);
+  store_f4(dst + b * 32 + 4 * part, scale_bytes_signed(q, d, 8));
 }
 
 // Q4_1: as Q4_0 with the codes unsigned and a min added: value = q * d + m (the
@@ -89,7 +96,7 @@ __global__ __launch_bounds__(256) void dequant_q4_1_kernel(const uint8_t* __rest
   o.y = static_cast<float>((q >> 8) & 0xFF) * d + m;
   o.z = static_cast<float>((q >> 16) & 0xFF) * d + m;
   o.w = static_cast<float>(q >> 24) * d + m;
-  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = o;
+  store_f4(dst + b * 32 + 4 * part, o);
 }
 
 // Q5_0: the Q4_0 nibbles plus bit e of qh as bit 4 of element e; value d * (q - 16).
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(256) void dequant_q5_0_kernel(const uint8_t* __rest
   const uint32_t lo = (part < 4) ? (w & kLo4) : ((w >> 4) & kLo4);
   // four bits -> bit 4 of four bytes: multiplying by 0x204081 copies bit i to bit 8i
   const uint32_t fifth = ((((qh >> (4 * part)) & 0xF) * 0x00204081u) & 0x01010101u) << 4;
-  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = scale_bytes_signed(lo | fifth, d, 16);
+  store_f4(dst + b * 32 + 4 * part, scale_bytes_signed(lo | fifth, d, 16));
 }
 
 // Q5_1: Q5_0's codes (unsigned) with Q4_1's value q * d + m; d, m, qh in the first 8
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(256) void dequant_q5_1_kernel(const uint8_t* __rest
   o.y = static_cast<float>((q >> 8) & 0xFF) * d + m;
   o.z = static_cast<float>((q >> 16) & 0xFF) * d + m;
   o.w = static_cast<float>(q >> 24) * d + m;
-  *reinterpret_cast<float4*>(dst + b * 32 + 4 * part) = o;
+  store_f4(dst + b * 32 + 4 * part, o);
 }
 
 // Q4_K, Q5_K and Q6_K: one wavefront per kSB consecutive superblocks, lane l -> elements
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(256) void dequant_q4_K_kernel(const uint8_t* __rest
     o.y = dsc * static_cast<float>((q >> 8) & 0xFF) - dm;
     o.z = dsc * static_cast<float>((q >> 16) & 0xFF) - dm;
     o.w = dsc * static_cast<float>(q >> 24) - dm;
-    *reinterpret_cast<float4*>(dst + (b0 + k) * 256 + e0) = o;
+    store_f4(dst + (b0 + k) * 256 + e0, o);
   }
 }
 
@@ -226,8 +233,7 @@ __global__ __launch_bounds__(256) void dequant_q6_K_kernel(const uint8_t* __rest
     const uint32_t lo = (g < 2) ? (v[k].wl & kLo4) : ((v[k].wl >> 4) & kLo4);
     const uint32_t q = lo | (((v[k].wh >> (2 * g)) & 0x03030303u) << 4);
     const float d = f16_to_f32(v[k].dw);
-    *reinterpret_cast<float4*>(dst + (b0 + k) * 256 + e0) =
-        scale_bytes_signed(q, d * static_cast<float>(v[k].sc), 32);
+    store_f4(dst + (b0 + k) * 256 + e0, scale_bytes_signed(q, d * static_cast<float>(v[k].sc), 32));
   }
 }
 
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(256) void dequant_q23_K_kernel(const uint8_t* __res
       o.z = dsc * static_cast<float>((q >> 16) & 0xFF) - dm;
       o.w = dsc * static_cast<float>(q >> 24) - dm;
     }
-    *reinterpret_cast<float4*>(dst + (b0 + k) * 256 + e0) = o;
+    store_f4(dst + (b0 + k) * 256 + e0, o);
   }
 }
 
