@@ -1888,10 +1888,31 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
 }
 
 // Wavefronts (rows) per workgroup of the LDS-staged GEMV launches (4 measured
-// best: 8 and 2 were slower on the 4096 x 11008 Q4_K decode shape), and the most
-// wavefronts the register-resident kernels launch (grid-strided over rows).
+// best: 8 and 2 were slower on the 4096 x 11008 Q4_K decode shape).
 constexpr int kWaves = 4;
-constexpr int kMaxWaves = 4096;
+
+// Compute units of the current device (256 on MI355X), queried once per device.
+int cu_count() {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;  // every thread that races here stores the same value
+  }
+  return cached[dev];
+}
+
+// The register-resident kernels walk the rows with a grid of exactly three
+// 4-wavefront workgroups per compute unit (3072 wavefronts on MI355X).  Measured
+// on the 32000 x 4096 Q6_K output head (launch-recorded events): 18.9 us at three
+// workgroups per CU and at two, 21.4 at four, 20.6 at six, 29.4 at one; counts
+// that do not divide evenly over the CUs were slow (2.5 per CU 21.7, 1.5 per CU
+// 23.4).  On 11008 x 4096 Q4_K: 5.65-5.74 us at three per CU, 5.74-6.01 at four,
+// 6.5-6.6 at two.
+int max_row_waves() { return 3 * 4 * cu_count(); }
 
 bool gemv_cols_fits(int w_type, int64_t n_in, int64_t ncols) {
   if (ncols < 2 || ncols > kGemvMaxCols) return false;
@@ -1978,7 +1999,7 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
   if (n_out <= 0) return hipSuccess;
   const int64_t lds = gemv_lds_bytes(w_type, n_in);
   const bool S = sums != nullptr;
-#define QK_ROWS(kern) launch_rows<4>(kern, n_out, 1, kMaxWaves, s, e0, e1, W, nb, xq, y, sums)
+#define QK_ROWS(kern) launch_rows<4>(kern, n_out, 1, max_row_waves(), s, e0, e1, W, nb, xq, y, sums)
 #define QK_LDS(kern) launch<kWaves>(kern, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
   switch (w_type) {
     case kQ4_K: {
@@ -2094,11 +2115,12 @@ hipError_t launch_pair_epi(const uint8_t* W1, const uint8_t* W2, int64_t n_out, 
   const int n = static_cast<int>(n_out);
   const int passes = (nb + 15) / 16;
   if (passes <= 2) {
-    // a wavefront has two rows' loads in flight, so half the single-GEMV count
-    // (2048 measured best on the 11008 x 4096 gate / up pair; 4096 and 8192 slower)
-    constexpr int64_t kPairWaves = kMaxWaves / 2;
-    const int64_t waves = n_out < kPairWaves ? n_out : kPairWaves;
-    const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));  // <= 512
+    // a wavefront has two rows' loads in flight: two 4-wavefront workgroups per CU
+    // (2048 wavefronts measured best on the 11008 x 4096 gate / up pair; 4096 and
+    // 8192 slower)
+    const int64_t pair_waves = 2 * 4 * cu_count();
+    const int64_t waves = n_out < pair_waves ? n_out : pair_waves;
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4), static_cast<unsigned>(ncols));
     if (passes == 1) launch_ev(gemv_q4_K_pair_reg<4, 1, EPI, Q5>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
     else launch_ev(gemv_q4_K_pair_reg<4, 2, EPI, Q5>, grid, dim3(256), 0, s, e0, e1, W1, W2, n, nb, xq, out);
   } else {
