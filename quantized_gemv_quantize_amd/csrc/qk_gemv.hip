@@ -32,6 +32,8 @@
 //    then one lane applies the float step; the row total is a wavefront sum.
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "qk_device.h"
 #include "qk_internal.h"
 
@@ -1894,15 +1896,15 @@ constexpr int kWaves = 4;
 // Compute units of the current device (256 on MI355X), queried once per device.
 int cu_count() {
   constexpr int kMaxDevices = 64;
-  static int cached[kMaxDevices] = {};
+  static std::atomic<int> cached[kMaxDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;  // every thread that races here stores the same value
+    cached[dev].store(n, std::memory_order_relaxed);  // threads that race here store the same value
   }
-  return cached[dev];
+  return n;
 }
 
 // The register-resident kernels walk the rows with a grid of exactly three
