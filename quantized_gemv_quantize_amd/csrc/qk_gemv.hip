@@ -1889,9 +1889,15 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
   }
 }
 
-// Wavefronts (rows) per workgroup of the LDS-staged GEMV launches (4 measured
-// best: 8 and 2 were slower on the 4096 x 11008 Q4_K decode shape).
+// Wavefronts (rows) per workgroup of the LDS-staged GEMV launches: 4 for the
+// K-quant and _1 kernels (8 and 2 were slower on every 4096 x 11008 shape, e.g. Q4_K
+// decode, Q5_K 7.69 / 9.32 against 7.20 us), 8 for the Q8_0 / Q4_0 / Q5_0 kernels,
+// whose staging (the per-block layout and, for Q4_0 / Q5_0, the activation sums) is
+// then shared by twice the rows: Q4_0 4096 x 11008 8.43 -> 8.03 us, 8192 x 8192
+// 11.12 -> 10.1, 14336 x 4096 11.08 -> 10.18, Q8_0 4096 x 11008 11.02 -> 10.69, Q5_0
+// 14336 x 4096 12.71 -> 11.99, 4096 x 4096 Q4_0 4.60 -> 4.43.
 constexpr int kWaves = 4;
+constexpr int kWaves32 = 8;
 
 // Compute units of the current device (256 on MI355X), queried once per device.
 int cu_count() {
@@ -2003,6 +2009,7 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
   const bool S = sums != nullptr;
 #define QK_ROWS(kern) launch_rows<4>(kern, n_out, 1, max_row_waves(), s, e0, e1, W, nb, xq, y, sums)
 #define QK_LDS(kern) launch<kWaves>(kern, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
+#define QK_LDS8(kern) launch<kWaves32>(kern, n_out, lds, s, e0, e1, W, nb, xq, y, sums)
   switch (w_type) {
     case kQ4_K: {
       const int nb = static_cast<int>(n_in / 256);
@@ -2032,9 +2039,9 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
       const int nb = static_cast<int>(n_in / 32);
       const int passes = (nb + 63) / 64;
       if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, kFmtQ8_0, true>)) : QK_ROWS((gemv_q80_reg<4, 1, kFmtQ8_0, false>));
-      if (passes == 2) return S ? QK_LDS((gemv_q8_0_kernel<kWaves, 2, true>)) : QK_LDS((gemv_q8_0_kernel<kWaves, 2, false>));
-      if (passes <= 4) return S ? QK_LDS((gemv_q8_0_kernel<kWaves, 4, true>)) : QK_LDS((gemv_q8_0_kernel<kWaves, 4, false>));
-      return S ? QK_LDS((gemv_q8_0_kernel<kWaves, 6, true>)) : QK_LDS((gemv_q8_0_kernel<kWaves, 6, false>));
+      if (passes == 2) return S ? QK_LDS8((gemv_q8_0_kernel<kWaves32, 2, true>)) : QK_LDS8((gemv_q8_0_kernel<kWaves32, 2, false>));
+      if (passes <= 4) return S ? QK_LDS8((gemv_q8_0_kernel<kWaves32, 4, true>)) : QK_LDS8((gemv_q8_0_kernel<kWaves32, 4, false>));
+      return S ? QK_LDS8((gemv_q8_0_kernel<kWaves32, 6, true>)) : QK_LDS8((gemv_q8_0_kernel<kWaves32, 6, false>));
     }
     case kQ4_0: {
       // 32-element formats keep all of a row's passes of weight loads in flight up
@@ -2044,19 +2051,19 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
       const int nb = static_cast<int>(n_in / 32);
       const int passes = (nb + 63) / 64;
       if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, kFmtQ4_0, true>)) : QK_ROWS((gemv_q80_reg<4, 1, kFmtQ4_0, false>));
-      if (passes == 2) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, false, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, false, false>));
-      if (passes <= 4) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 4, false, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 4, false, false>));
-      if (passes <= 6) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 6, false, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 6, false, false>));
-      return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 8, false, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 8, false, false>));
+      if (passes == 2) return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 2, false, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 2, false, false>));
+      if (passes <= 4) return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 4, false, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 4, false, false>));
+      if (passes <= 6) return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 6, false, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 6, false, false>));
+      return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 8, false, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 8, false, false>));
     }
     case kQ5_0: {
       const int nb = static_cast<int>(n_in / 32);
       const int passes = (nb + 63) / 64;
       if (passes == 1) return S ? QK_ROWS((gemv_q80_reg<4, 1, kFmtQ5_0, true>)) : QK_ROWS((gemv_q80_reg<4, 1, kFmtQ5_0, false>));
-      if (passes == 2) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 2, true, false>));
-      if (passes <= 4) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 4, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 4, true, false>));
-      if (passes <= 6) return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 6, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 6, true, false>));
-      return S ? QK_LDS((gemv_q4_0_kernel<kWaves, 8, true, true>)) : QK_LDS((gemv_q4_0_kernel<kWaves, 8, true, false>));
+      if (passes == 2) return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 2, true, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 2, true, false>));
+      if (passes <= 4) return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 4, true, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 4, true, false>));
+      if (passes <= 6) return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 6, true, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 6, true, false>));
+      return S ? QK_LDS8((gemv_q4_0_kernel<kWaves32, 8, true, true>)) : QK_LDS8((gemv_q4_0_kernel<kWaves32, 8, true, false>));
     }
     case kQ2_K:
     case kQ3_K: {
@@ -2095,6 +2102,7 @@ hipError_t launch_gemv(int w_type, const uint8_t* W, int64_t n_out, int64_t n_in
   }
 #undef QK_ROWS
 #undef QK_LDS
+#undef QK_LDS8
 }
 
 // One launch, with the caller's start / stop events recorded by the launch itself
