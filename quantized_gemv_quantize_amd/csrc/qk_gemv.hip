@@ -1895,7 +1895,10 @@ int64_t gemv_lds_bytes(int w_type, int64_t n_in) {
 // whose staging (the per-block layout and, for Q4_0 / Q5_0, the activation sums) is
 // then shared by twice the rows: Q4_0 4096 x 11008 8.43 -> 8.03 us, 8192 x 8192
 // 11.12 -> 10.1, 14336 x 4096 11.08 -> 10.18, Q8_0 4096 x 11008 11.02 -> 10.69, Q5_0
-// 14336 x 4096 12.71 -> 11.99, 4096 x 4096 Q4_0 4.60 -> 4.43.
+// 14336 x 4096 12.71 -> 11.99, 4096 x 4096 Q4_0 4.60 -> 4.43.  The same holds for their
+// multi-column kernel (Q4_0 4096 x 11008 at 3 columns 15.4 -> 12.8 us, at 2 11.6 -> 10.6,
+// Q8_0 4096 x 4096 at 4 columns 9.4 -> 8.7), while the K-quant multi-column kernels were
+// slower with 8 (Q4_K 4096 x 11008 at 2 columns 8.42 -> 9.0, Q6_K 12.1 -> 13.1).
 constexpr int kWaves = 4;
 constexpr int kWaves32 = 8;
 
@@ -1936,9 +1939,9 @@ hipError_t launch_q80_cols_nc(const uint8_t* W, int64_t n_out, int nb, const uin
                               int32_t* sums, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t lds = NC * LayoutQ80(nb).bytes;
   const int passes = (nb + 63) / 64;
-  if (passes == 1) return launch<kWaves>(gemv_q80_cols<kWaves, 1, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
-  if (passes == 2) return launch<kWaves>(gemv_q80_cols<kWaves, 2, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
-  return launch<kWaves>(gemv_q80_cols<kWaves, 4, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  if (passes == 1) return launch<kWaves32>(gemv_q80_cols<kWaves32, 1, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  if (passes == 2) return launch<kWaves32>(gemv_q80_cols<kWaves32, 2, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
+  return launch<kWaves32>(gemv_q80_cols<kWaves32, 4, NC, FMT, S>, n_out, lds, s, e0, e1, W, nb, xq, y, sums);
 }
 template <bool S, int FMT>
 hipError_t launch_q80_cols_s(const uint8_t* W, int64_t n_out, int nb, const uint8_t* xq, int64_t ncols, float* y,
