@@ -603,6 +603,36 @@ def test_c_abi_from_a_host_program(torch_cuda):
     assert "abi_check ok" in r.stdout
 
 
+def test_two_streams_concurrently(torch_cuda):
+    # the library keeps no state between calls beyond a per-device cache of the CU
+    # count: calls on two streams at once (different formats, launch shapes and
+    # inputs, outputs in separate buffers) give what each gives alone
+    torch = torch_cuda
+    rng = np.random.default_rng(91)
+    cases = [(T6K, 9000, 4096, 1), (T4K, 4096, 11008, 1), (T4_0, 5000, 4096, 3), (T4K, 3000, 4096, 16)]
+    bufs, want = [], []
+    for t, n_out, n_in, nc in cases:
+        W = dev(torch, weights(rng, t, n_out, n_in))
+        x = dev(torch, rng.standard_normal((nc, n_in)).astype(np.float32))
+        at = qk.qk_act_type(t)
+        xq = qk.qk_quantize_act(at, x)
+        want.append(qk.qk_gemv(t, W, n_out, n_in, xq, nc).clone())
+        bufs.append((t, n_out, n_in, nc, W, x, at))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    outs = [[] for _ in cases]
+    for rep in range(5):
+        for i, (t, n_out, n_in, nc, W, x, at) in enumerate(bufs):
+            with torch.cuda.stream(streams[i % 2]):
+                xq = qk.qk_quantize_act(at, x)
+                outs[i].append(qk.qk_gemv(t, W, n_out, n_in, xq, nc))
+    torch.cuda.synchronize()
+    for i, (t, n_out, n_in, nc, *_rest) in enumerate(bufs):
+        say("two streams", t, n_out, n_in, nc)
+        for y in outs[i]:
+            assert torch.equal(y.view(torch.int32), want[i].view(torch.int32)), (t, n_out, n_in, nc)
+
+
 def test_graph_capture_replays_match_eager(torch_cuda):
     # quantize + GEMV captured into a HIP graph; several replays, with eager work
     # and synchronizations between them, must each equal the eager result.
@@ -610,7 +640,9 @@ def test_graph_capture_replays_match_eager(torch_cuda):
     rng = np.random.default_rng(9)
     cases = [(T4K, 64, 11008, 1), (T4K, 300, 4096, 1), (T6K, 70, 4096, 1), (T8_0, 50, 4096, 1),
              (T4_0, 33, 1024, 1), (T5_0, 41, 4096, 1), (T4K, 200, 4096, 16),
-             (T4K, 90, 2048, 64), (T5K, 57, 11008, 1), (T5K, 40, 4096, 3), (T6K, 48, 4096, 4), (T5_0, 36, 2048, 3)]
+             (T4K, 90, 2048, 64), (T5K, 57, 11008, 1), (T5K, 40, 4096, 3), (T6K, 48, 4096, 4), (T5_0, 36, 2048, 3),
+             # more rows than the row-walking grid has wavefronts: each walks several
+             (T6K, 7000, 4096, 1), (T4K, 6500, 2048, 1), (T8_0, 5000, 1024, 1)]
     bufs = []
     for t, n_out, n_in, nc in cases:
         W = dev(torch, weights(rng, t, n_out, n_in))
