@@ -439,7 +439,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
 //    through the address unit once or twice per superblock instead of four times
 //    (measured on 4096 x 11008: 7.6 against 9.3 us with the Q2_K mapping, which in
 //    turn is faster for Q2_K: 5.1 against 5.6 us).  The blocks are only 2-byte
-//    aligned; every load stays inside its block.
+//    aligned: the fields are read as 4-byte aligned dwords and shifted into place
+//    (q23_load).
 template <int Q3>
 struct KQuant23 {
   static constexpr int kBytes = Q3 ? kQ3_KBytes : kQ2_KBytes;
@@ -447,21 +448,41 @@ struct KQuant23 {
 };
 
 struct Q23Loads {
-  uint4 q0, q1;   // Q2_K: qs bytes 32h .. 32h + 31; Q3_K: q0 = qs bytes 16c .. 16c + 15
-  uint4 m;        // Q3_K: hmask bytes 16 (c & 1) .. + 15
-  uint2 sc;       // Q2_K: sc.x = scales[4c .. 4c + 3]; Q3_K: scale bytes 96-103
-  uint32_t sc2;   // Q3_K: scale bytes 104-107
+  uint4 q0, q1;   // Q2_K: qs bytes 32h .. 32h + 31; Q3_K: q0 = the aligned words at or below qs bytes 16c ..
+  uint4 m;        // Q3_K: the 4-byte aligned words at or below hmask bytes 16 (c & 1) ..
+  uint2 sc;       // Q2_K: sc.x = scales[4c .. 4c + 3]; Q3_K: sc.x = aligned scale word c
+  uint32_t sc2;   // Q3_K: shift of the aligned words (0 or 16 bits)
   uint32_t d;     // Q2_K: d | dmin << 16; Q3_K: d
 };
+
+// Lane K's value in every lane of its group of 4 (DPP quad_perm [K,K,K,K]).
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, K * 0x55, 0xF, 0xF, false);
+}
 
 template <int Q3>
 __device__ __forceinline__ void q23_load(Q23Loads& v, const uint8_t* p, int c) {
   using F = KQuant23<Q3>;
   if constexpr (Q3 != 0) {
-    v.q0 = load_u2<uint4>(p + F::kQs + 16 * c);
-    v.m = load_u2<uint4>(p + 16 * (c & 1));
-    v.sc = load_u2<uint2>(p + 96);
-    v.sc2 = load_u2<uint32_t>(p + 104);
+    // Every field starts a multiple of 4 bytes into the 110-byte block, and the block
+    // itself is only 2-byte aligned.  Loads at 2-byte aligned addresses take a slow
+    // path (Q3_K 4096 x 11008 with the products removed: 5.67 us, 4.62 with the same
+    // loads 4-byte aligned), so each lane reads 4-byte aligned words from pa, the
+    // aligned address at or just below the block (sh = 0 or 16 bits of shift), and
+    // q23_chunk shifts them into place.  The lane loads its 16 qs bytes and its 16
+    // hmask bytes as dwordx4 from pa, plus dword c of the 16 bytes at pa + 96 (the
+    // scales); the word after each dwordx4 and the other scale words come from the
+    // other lanes of the quad, which hold the same block.  All words lie inside the
+    // block, except that a block at 2 mod 4 also reads the 2 bytes before it (the
+    // previous block's; the first block of W is 16-byte aligned) and that with sh = 0
+    // lane 3 re-reads scale word 2 (its word 3 would end past the block).
+    const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 2u) * 8u;
+    const uint8_t* pa = p - (sh >> 3);
+    v.q0 = load_a4<uint4>(pa + F::kQs + 16 * c);
+    v.m = load_a4<uint4>(pa + 16 * (c & 1));
+    v.sc.x = load_a4<uint32_t>(pa + 96 + 4 * ((sh == 0 && c == 3) ? 2 : c));
+    v.sc2 = sh;
     v.d = *reinterpret_cast<const uint16_t*>(p + 108);
   } else {
     const int h = c >> 1;
@@ -480,21 +501,36 @@ __device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk
   if constexpr (Q3 != 0) {
     const uint4 bsv = lds_a4<uint4>(ablk + 260 + 16 * h);  // bsums 8h .. 8h + 7
     const uint32_t bw[4] = {bsv.x, bsv.y, bsv.z, bsv.w};
+    // the block's fields from the 4-byte aligned words of q23_load: the scale words
+    // from the quad's four lanes, the word after this lane's qs bytes from lane c + 1
+    // (lane 3: scale word 0), the word after its hmask bytes from lane c + 1 (hmask
+    // bytes 16 ..) or lane 0 (qs bytes 0 ..)
+    const uint32_t sh = v.sc2;
+    const uint32_t w0 = quad_bcast<0>(v.sc.x), w1 = quad_bcast<1>(v.sc.x);
+    const uint32_t w2 = quad_bcast<2>(v.sc.x), w3 = quad_bcast<3>(v.sc.x);
+    const uint32_t qnext = __builtin_amdgcn_update_dpp(0u, v.q0.x, 0xF9, 0xF, 0xF, false);  // [1,2,3,3]
+    const uint32_t qn = (c == 3) ? w0 : qnext;
+    const uint32_t mn = __builtin_amdgcn_update_dpp(0u, (c & 1) ? v.m.x : v.q0.x, 0x31, 0xF, 0xF, false);  // [1,0,3,0]
+    const uint32_t qw[4] = {__builtin_amdgcn_alignbit(v.q0.y, v.q0.x, sh), __builtin_amdgcn_alignbit(v.q0.z, v.q0.y, sh),
+                            __builtin_amdgcn_alignbit(v.q0.w, v.q0.z, sh), __builtin_amdgcn_alignbit(qn, v.q0.w, sh)};
+    const uint4 mraw = make_uint4(__builtin_amdgcn_alignbit(v.m.y, v.m.x, sh), __builtin_amdgcn_alignbit(v.m.z, v.m.y, sh),
+                                  __builtin_amdgcn_alignbit(v.m.w, v.m.z, sh), __builtin_amdgcn_alignbit(mn, v.m.w, sh));
+    const uint2 scw = make_uint2(__builtin_amdgcn_alignbit(w1, w0, sh), __builtin_amdgcn_alignbit(w2, w1, sh));
+    const uint32_t sc2w = __builtin_amdgcn_alignbit(w3, w2, sh);
     // Bit 2 of the code of shift group g is bit 4h + g of the hmask byte: rotating
     // each hmask word right by 4h - 2 (mod 32) puts bit 4h + g of every byte at bit
     // g + 2 of the same byte (the bits that wrap around land below bit 2 of byte 0,
     // which no group reads).
     const uint32_t rot = h ? 2u : 30u;
-    const uint32_t mq[4] = {__builtin_amdgcn_alignbit(v.m.x, v.m.x, rot), __builtin_amdgcn_alignbit(v.m.y, v.m.y, rot),
-                            __builtin_amdgcn_alignbit(v.m.z, v.m.z, rot), __builtin_amdgcn_alignbit(v.m.w, v.m.w, rot)};
-    const uint32_t qw[4] = {v.q0.x, v.q0.y, v.q0.z, v.q0.w};
+    const uint32_t mq[4] = {__builtin_amdgcn_alignbit(mraw.x, mraw.x, rot), __builtin_amdgcn_alignbit(mraw.y, mraw.y, rot),
+                            __builtin_amdgcn_alignbit(mraw.z, mraw.z, rot), __builtin_amdgcn_alignbit(mraw.w, mraw.w, rot)};
     // 6-bit scales of sub-blocks j = 8h + 2g + lh, g = 0 .. 3: the low 4 bits are
     // nibble h of scale byte 2g + lh, the high 2 bits are bits 4h + 2 (g >> 1) of
     // scale byte 8 + 2 (g & 1) + lh.  s01 holds the scales of g = 0, 1 in bytes lh and
     // 2 + lh, s23 those of g = 2, 3.
-    const uint32_t hs = v.sc2 >> (4 * h);
-    const uint32_t s01 = ((v.sc.x >> (4 * h)) & kLo4) | ((hs & 0x03030303u) << 4);
-    const uint32_t s23 = ((v.sc.y >> (4 * h)) & kLo4) | (((hs >> 2) & 0x03030303u) << 4);
+    const uint32_t hs = sc2w >> (4 * h);
+    const uint32_t s01 = ((scw.x >> (4 * h)) & kLo4) | ((hs & 0x03030303u) << 4);
+    const uint32_t s23 = ((scw.y >> (4 * h)) & kLo4) | (((hs >> 2) & 0x03030303u) << 4);
     int tsum = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
