@@ -458,7 +458,7 @@ struct Q23Loads {
 // Lane K's value in every lane of its group of 4 (DPP quad_perm [K,K,K,K]).
 template <int K>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
-  return __builtin_amdgcn_update_dpp(0u, v, K * 0x55, 0xF, 0xF, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), K * 0x55, 0xF, 0xF, false));
 }
 
 template <int Q3>
@@ -508,9 +508,9 @@ __device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk
     const uint32_t sh = v.sc2;
     const uint32_t w0 = quad_bcast<0>(v.sc.x), w1 = quad_bcast<1>(v.sc.x);
     const uint32_t w2 = quad_bcast<2>(v.sc.x), w3 = quad_bcast<3>(v.sc.x);
-    const uint32_t qnext = __builtin_amdgcn_update_dpp(0u, v.q0.x, 0xF9, 0xF, 0xF, false);  // [1,2,3,3]
+    const uint32_t qnext = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v.q0.x), 0xF9, 0xF, 0xF, false));  // [1,2,3,3]
     const uint32_t qn = (c == 3) ? w0 : qnext;
-    const uint32_t mn = __builtin_amdgcn_update_dpp(0u, (c & 1) ? v.m.x : v.q0.x, 0x31, 0xF, 0xF, false);  // [1,0,3,0]
+    const uint32_t mn = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>((c & 1) ? v.m.x : v.q0.x), 0x31, 0xF, 0xF, false));  // [1,0,3,0]
     const uint32_t qw[4] = {__builtin_amdgcn_alignbit(v.q0.y, v.q0.x, sh), __builtin_amdgcn_alignbit(v.q0.z, v.q0.y, sh),
                             __builtin_amdgcn_alignbit(v.q0.w, v.q0.z, sh), __builtin_amdgcn_alignbit(qn, v.q0.w, sh)};
     const uint4 mraw = make_uint4(__builtin_amdgcn_alignbit(v.m.y, v.m.x, sh), __builtin_amdgcn_alignbit(v.m.z, v.m.y, sh),
@@ -527,11 +527,12 @@ __device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk
     // 6-bit scales of sub-blocks j = 8h + 2g + lh, g = 0 .. 3: the low 4 bits are
     // nibble h of scale byte 2g + lh, the high 2 bits are bits 4h + 2 (g >> 1) of
     // scale byte 8 + 2 (g & 1) + lh.  s01 holds the scales of g = 0, 1 in bytes lh and
-    // 2 + lh, s23 those of g = 2, 3.
-    const uint32_t hs = sc2w >> (4 * h);
+    // 2 + lh, s23 those of g = 2, 3, each with its bit 5 flipped (the xor flips the
+    // upper bit of both 2-bit fields of every byte): a 6-bit s with bit 5 flipped,
+    // read as a signed 6-bit field, is s - 32.
+    const uint32_t hs = (sc2w >> (4 * h)) ^ 0x0A0A0A0Au;
     const uint32_t s01 = ((scw.x >> (4 * h)) & kLo4) | ((hs & 0x03030303u) << 4);
     const uint32_t s23 = ((scw.y >> (4 * h)) & kLo4) | (((hs >> 2) & 0x03030303u) << 4);
-    int tsum = 0;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint4 a = lds_a4<uint4>(ablk + 4 + 128 * h + 32 * g + 16 * lh);
@@ -540,18 +541,15 @@ __device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk
       for (int k = 0; k < 4; ++k) {
         w[k] = ((qw[k] >> (2 * g)) & 0x03030303u) | ((mq[k] >> g) & 0x04040404u);
       }
-      int s = 0;
-      s = dot4(w[0], a.x, s);
-      s = dot4(w[1], a.y, s);
-      s = dot4(w[2], a.z, s);
-      s = dot4(w[3], a.w, s);
       const int bs = static_cast<int>(__builtin_amdgcn_sbfe(bw[g], 16 * lh, 16));  // bsum of sub-block 8h + 2g + lh
-      const int t = mad24(-4, bs, s);                                              // sum (code - 4) a
-      const int scale = static_cast<int>(__builtin_amdgcn_ubfe(g < 2 ? s01 : s23, 8 * (lh + 2 * (g & 1)), 8));
-      sq = mad24(scale, t, sq);
-      tsum += t;
+      int t = __mul24(bs, -4);  // sum (code - 4) a, the codes taken unsigned
+      t = dot4(w[0], a.x, t);
+      t = dot4(w[1], a.y, t);
+      t = dot4(w[2], a.z, t);
+      t = dot4(w[3], a.w, t);
+      const int scale = static_cast<int>(__builtin_amdgcn_sbfe(g < 2 ? s01 : s23, 8 * (lh + 2 * (g & 1)), 6));
+      sq = mad24(scale, t, sq);  // (scale_j - 32) t_j
     }
-    sq = mad24(-32, tsum, sq);  // sum_j (scale_j - 32) t_j
   } else {
     const uint8_t* ap = ablk + 4 + 64 * c;
     const uint4 a[4] = {lds_a4<uint4>(ap), lds_a4<uint4>(ap + 16), lds_a4<uint4>(ap + 32), lds_a4<uint4>(ap + 48)};
