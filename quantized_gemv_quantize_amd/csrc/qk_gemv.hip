@@ -88,6 +88,9 @@ struct StagedQ80 {
 };
 
 __device__ __forceinline__ int sext16_lo(uint32_t v) { return static_cast<int16_t>(v & 0xFFFF); }
+// Signed 16-bit half `hi` (0 or 1) and signed byte at bit `off` of v, one v_bfe_i32 each.
+__device__ __forceinline__ int sbfe16(uint32_t v, int hi) { return static_cast<int>(__builtin_amdgcn_sbfe(v, 16 * hi, 16)); }
+__device__ __forceinline__ int sbfe8(uint32_t v, int off) { return static_cast<int>(__builtin_amdgcn_sbfe(v, off, 8)); }
 __device__ __forceinline__ int sext16_hi(uint32_t v) { return static_cast<int16_t>(v >> 16); }
 
 // Q8_0 block i (34 bytes): pieces 0, 1 = codes at 2 and 18; small unit = f16 d at 0.
@@ -850,10 +853,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) a[g] = lds_a4<uint4>(blk + 4 + 128 * hh + 32 * g + 16 * kk);
       const uint4 bw = lds_a4<uint4>(blk + 260 + 16 * hh);  // bsums 8h .. 8h+7
-      const int4 bs = make_int4(32 * (kk ? sext16_hi(bw.x) : sext16_lo(bw.x)),
-                                32 * (kk ? sext16_hi(bw.y) : sext16_lo(bw.y)),
-                                32 * (kk ? sext16_hi(bw.z) : sext16_lo(bw.z)),
-                                32 * (kk ? sext16_hi(bw.w) : sext16_lo(bw.w)));
+      // q is stored as 0..63: each sub-block's sum (q - 32) a starts at -32 bsum
+      const int4 bs = make_int4(__mul24(sbfe16(bw.x, kk), -32), __mul24(sbfe16(bw.y, kk), -32),
+                                __mul24(sbfe16(bw.z, kk), -32), __mul24(sbfe16(bw.w, kk), -32));
       const float dx = lds_a4<float>(blk);
       const uint32_t al[4] = {A[j].x, A[j].y, A[j].z, A[j].w};
       const uint32_t bl[4] = {B[j].x, B[j].y, B[j].z, B[j].w};
@@ -862,7 +864,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
       const uint32_t a1[4] = {a[1].x, a[1].y, a[1].z, a[1].w};
       const uint32_t a2[4] = {a[2].x, a[2].y, a[2].z, a[2].w};
       const uint32_t a3[4] = {a[3].x, a[3].y, a[3].z, a[3].w};
-      int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+      int s0 = bs.x, s1 = bs.y, s2 = bs.z, s3 = bs.w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const Q6Codes q = q6_codes(al[i], bl[i], hl[i]);
@@ -872,12 +874,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_q6_K_kernel(
         s3 = dot4(q.q3, a3[i], s3);
       }
       // sub-block scales sc[8h + 2g + k] = byte (2g + k) of the 8 bytes at 192 + 8h
-      const int sc0 = static_cast<int8_t>((SC[j].x >> (8 * kk)) & 0xFF);
-      const int sc1 = static_cast<int8_t>((SC[j].x >> (16 + 8 * kk)) & 0xFF);
-      const int sc2 = static_cast<int8_t>((SC[j].y >> (8 * kk)) & 0xFF);
-      const int sc3 = static_cast<int8_t>((SC[j].y >> (16 + 8 * kk)) & 0xFF);
-      // q is stored as 0..63; sum (q - 32) a = sum q a - 32 * bsum
-      const int part = mad24(sc0, s0 - bs.x, mad24(sc1, s1 - bs.y, mad24(sc2, s2 - bs.z, __mul24(sc3, s3 - bs.w))));
+      const int sc0 = sbfe8(SC[j].x, 8 * kk), sc1 = sbfe8(SC[j].x, 16 + 8 * kk);
+      const int sc2 = sbfe8(SC[j].y, 8 * kk), sc3 = sbfe8(SC[j].y, 16 + 8 * kk);
+      const int part = mad24(sc0, s0, mad24(sc1, s1, mad24(sc2, s2, __mul24(sc3, s3))));
       const int S = quad_sum(part);
       if (pos == 0) {
         const float d = f16_to_f32(D[j]);
