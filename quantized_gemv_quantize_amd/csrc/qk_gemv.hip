@@ -312,6 +312,37 @@ __device__ __forceinline__ T lds_a4(const uint8_t* p) {  // 4-byte aligned LDS f
   return v;
 }
 
+// Lane K's value in every lane of its group of 4 (DPP quad_perm [K,K,K,K]).
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), K * 0x55, 0xF, 0xF, false));
+}
+
+// The four lanes of a quad hold one K-quant superblock, and each needs all of its
+// 16-byte header (d, dmin, scales) and, for Q5_K, all 32 qh bytes.  In the LDS kernel
+// below lane c loads only header dword c and qh bytes 16 + 8c .. 23 + 8c, and the
+// rest comes from the other lanes by DPP: four loads of the same bytes per quad cost
+// address-unit time, a broadcast one VALU instruction.  (4096 x 14336 Q5_K: 8.91 ->
+// 8.55-8.60 us, Q4_K 7.48-7.49 -> 7.35-7.39, 4096 x 11008 Q4_K 6.21-6.27 -> 6.17-6.18.
+// The register-resident row-walking kernels measured 2-3 % slower with the same
+// change, the gate / up pair kernel of Q5_K 13 % slower, and keep full loads.)
+// Callers keep all four lanes of a quad active wherever these run.
+__device__ __forceinline__ uint32_t load_head(const uint8_t* p, int c) {
+  return *reinterpret_cast<const uint32_t*>(p + 4 * c);
+}
+__device__ __forceinline__ uint4 head_of(uint32_t w) {
+  return make_uint4(quad_bcast<0>(w), quad_bcast<1>(w), quad_bcast<2>(w), quad_bcast<3>(w));
+}
+__device__ __forceinline__ uint2 load_qh(const uint8_t* p, int c) {
+  return *reinterpret_cast<const uint2*>(p + 16 + 8 * c);
+}
+__device__ __forceinline__ uint4 qh_lo(uint2 v) {  // qh bytes 0 .. 15
+  return make_uint4(quad_bcast<0>(v.x), quad_bcast<0>(v.y), quad_bcast<1>(v.x), quad_bcast<1>(v.y));
+}
+__device__ __forceinline__ uint4 qh_hi(uint2 v) {  // qh bytes 16 .. 31
+  return make_uint4(quad_bcast<2>(v.x), quad_bcast<2>(v.y), quad_bcast<3>(v.x), quad_bcast<3>(v.y));
+}
+
 // ---------------------------------------------------------------------------
 // Q4_K x Q8_K.  Lane (u = lane >> 2, c = lane & 3) of pass `it` handles 64-element
 // chunk c of superblock it*16 + u: qs[32c .. 32c+31] hold sub-block 2c in their low
@@ -347,7 +378,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
   const uint8_t* wrow = W + static_cast<size_t>(row_ok ? row : n_out - 1) * rb;
   const int passes = (nb + 15) >> 4;
 
-  uint4 H[UNR], Q0[UNR], Q1[UNR], QH0[Q5 ? UNR : 1], QH1[Q5 ? UNR : 1];
+  uint32_t H[UNR];
+  uint4 Q0[UNR], Q1[UNR];
+  uint2 QH[Q5 ? UNR : 1];
   // Unconditional loads (superblock index clamped): the same number of loads in
   // every lane lets the compiler wait for pass j's data only.
   auto issue = [&](int p0) {
@@ -355,12 +388,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
     for (int j = 0; j < UNR; ++j) {
       const int sb = min((p0 + j) * 16 + u, nb - 1);
       const uint8_t* p = wrow + static_cast<uint32_t>(sb * F::kBytes);
-      H[j] = *reinterpret_cast<const uint4*>(p);
+      H[j] = load_head(p, c);
       Q0[j] = *reinterpret_cast<const uint4*>(p + F::kQs + 32 * c);
       Q1[j] = *reinterpret_cast<const uint4*>(p + F::kQs + 16 + 32 * c);
       if constexpr (Q5 != 0) {
-        QH0[j] = *reinterpret_cast<const uint4*>(p + 16);
-        QH1[j] = *reinterpret_cast<const uint4*>(p + 32);
+        QH[j] = load_qh(p, c);
       }
     }
   };
@@ -391,10 +423,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_q4_K_kernel(
       const uint2 bsw = lds_a4<uint2>(blk + 260 + 8 * c);  // bsums 4c .. 4c+3
       const int2 asum = make_int2(sext16_lo(bsw.x) + sext16_hi(bsw.x), sext16_lo(bsw.y) + sext16_hi(bsw.y));
       const float dx = lds_a4<float>(blk);
-      const uint4 h = H[j];
+      const uint4 h = head_of(H[j]);
       int2 part;
       if constexpr (Q5 != 0) {
-        part = q5K_chunk(Q0[j], Q1[j], rot_q5(QH0[j], c), rot_q5(QH1[j], c), h, a0, a1, a2, a3, asum,
+        part = q5K_chunk(Q0[j], Q1[j], rot_q5(qh_lo(QH[j]), c), rot_q5(qh_hi(QH[j]), c), h, a0, a1, a2, a3, asum,
                          hi_mask, sh);
       } else {
         part = q4K_chunk(Q0[j], Q1[j], h, a0, a1, a2, a3, asum, hi_mask, sh);
@@ -457,12 +489,6 @@ struct Q23Loads {
   uint32_t sc2;   // Q3_K: shift of the aligned words (0 or 16 bits)
   uint32_t d;     // Q2_K: d | dmin << 16; Q3_K: d
 };
-
-// Lane K's value in every lane of its group of 4 (DPP quad_perm [K,K,K,K]).
-template <int K>
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), K * 0x55, 0xF, 0xF, false));
-}
 
 template <int Q3>
 __device__ __forceinline__ void q23_load(Q23Loads& v, const uint8_t* p, int c) {
