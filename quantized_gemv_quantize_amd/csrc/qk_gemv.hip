@@ -317,6 +317,11 @@ template <int K>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), K * 0x55, 0xF, 0xF, false));
 }
+// DPP quad_perm with the control word P: lane i of each quad takes lane (P >> 2i) & 3.
+template <int P>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), P, 0xF, 0xF, false));
+}
 
 // The four lanes of a quad hold one K-quant superblock, and each needs all of its
 // 16-byte header (d, dmin, scales) and, for Q5_K, all 32 qh bytes.  In the LDS kernel
@@ -483,7 +488,7 @@ struct KQuant23 {
 };
 
 struct Q23Loads {
-  uint4 q0, q1;   // Q2_K: qs bytes 32h .. 32h + 31; Q3_K: q0 = the aligned words at or below qs bytes 16c ..
+  uint4 q0;       // Q2_K: qs bytes 16c .. 16c + 15; Q3_K: the aligned words at or below qs bytes 16c ..
   uint4 m;        // Q3_K: the 4-byte aligned words at or below hmask bytes 16 (c & 1) ..
   uint2 sc;       // Q2_K: sc.x = scales[4c .. 4c + 3]; Q3_K: sc.x = aligned scale word c
   uint32_t sc2;   // Q3_K: shift of the aligned words (0 or 16 bits)
@@ -514,9 +519,7 @@ __device__ __forceinline__ void q23_load(Q23Loads& v, const uint8_t* p, int c) {
     v.sc2 = sh;
     v.d = *reinterpret_cast<const uint16_t*>(p + 108);
   } else {
-    const int h = c >> 1;
-    v.q0 = load_a4<uint4>(p + F::kQs + 32 * h);
-    v.q1 = load_a4<uint4>(p + F::kQs + 32 * h + 16);
+    v.q0 = load_a4<uint4>(p + F::kQs + 16 * c);  // qs bytes 16c .. 16c + 15
     v.sc.x = load_a4<uint32_t>(p + 4 * c);
     v.d = load_a4<uint32_t>(p + 80);
   }
@@ -585,9 +588,17 @@ __device__ __forceinline__ int2 q23_chunk(const Q23Loads& v, const uint8_t* ablk
     const uint2 bsw = lds_a4<uint2>(ablk + 260 + 8 * c);  // bsums 4c .. 4c+3
     const int bs[4] = {sext16_lo(bsw.x), sext16_hi(bsw.x), sext16_lo(bsw.y), sext16_hi(bsw.y)};
     const int g0 = 2 * lh;
+    // The lane's half takes qs bytes 32h .. 32h + 31, loaded by lanes 2h and 2h + 1 of
+    // the quad (one 16-byte load per lane instead of two; DPP quad_perm [0,0,2,2] and
+    // [1,1,3,3]): 11008 x 4096 5.46 -> 5.31 us, 4096 x 14336 6.26-6.39 -> 6.05,
+    // 4096 x 11008 unchanged at 5.16.
+    const uint4 qa = make_uint4(quad_perm<0xA0>(v.q0.x), quad_perm<0xA0>(v.q0.y), quad_perm<0xA0>(v.q0.z),
+                                quad_perm<0xA0>(v.q0.w));
+    const uint4 qb = make_uint4(quad_perm<0xF5>(v.q0.x), quad_perm<0xF5>(v.q0.y), quad_perm<0xF5>(v.q0.z),
+                                quad_perm<0xF5>(v.q0.w));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint4 q = (k & 1) ? v.q1 : v.q0;  // bytes l = 16 (k & 1) .. + 15
+      const uint4 q = (k & 1) ? qb : qa;  // bytes l = 16 (k & 1) .. + 15
       const int sh = 2 * (g0 + (k >> 1));
       int s = 0;
       s = dot4((q.x >> sh) & 0x03030303u, a[k].x, s);
